@@ -1,0 +1,37 @@
+"""fp64 CPU oracle for the DFlash draft-body forward -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package. The HIP library never calls it and shares no code with it.
+
+Contents:
+  plan.py  -- the seeded anchor plan (integer; bit-exact spec).
+  body.py  -- context projection, dual-source block attention, the draft body,
+              and a brute-force dense-mask attention used to pin the gathered form.
+
+Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
+  build_plan             pinned by invariants the pages fix (determinism, equal
+                         sample id -> equal anchors, anchors from valid windows,
+                         loss mask excludes the anchor and invalid positions) and
+                         by brute-force top-N selection; the exact SplitMix64
+                         constants are "parity unpinned" (the pages print no
+                         known-answer vector).
+  rms_norm, silu, rope   pinned by closed forms and identities.
+  block_attention        pinned by the brute-force dense-mask attention and by
+                         closed-form special cases.
+  body_forward           pinned by composition of the above plus the pages'
+                         invariants; whole-body values beyond that are
+                         "parity unpinned" (the pages print no worked example).
+"""
+from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
+from .body import (
+    rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
+    dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
+    concat_target_states,
+)
+
+__all__ = [
+    "splitmix64", "build_plan", "eligible_anchors", "row_key", "position_key",
+    "rms_norm", "silu", "rope", "rope_inv_freq", "ctx_proj", "ctx_kv", "block_attention",
+    "dense_mask_attention", "block_attn_call", "body_forward", "body_forward_dense",
+    "concat_target_states",
+]
