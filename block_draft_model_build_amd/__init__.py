@@ -1,0 +1,206 @@
+"""Python binding of libdflash: the DFlash draft-body forward on MI355X (gfx950).
+
+Argument marshalling only. Every call goes to the C ABI declared in
+include/dflash.h; all computation runs in the library's HIP kernels. Tensors
+are torch tensors used as device buffers (their data pointers are passed);
+the stream defaults to torch's current stream on the tensor's device.
+
+The names mirror the C entry points:
+  dflash_build_plan, dflash_ctx_proj, dflash_block_attn, dflash_body_forward,
+  dflash_workspace_size, dflash_check_config, dflash_status_string.
+
+If libdflash.so is missing it is built in-tree with hipcc on first import; if
+that fails, importing this package raises ImportError. There is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+
+DFLASH_OK, DFLASH_ERR_INVALID_ARG, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP = range(5)
+DFLASH_F32, DFLASH_BF16 = 0, 1
+
+EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_block_attn", "dflash_body_forward",
+            "dflash_workspace_size", "dflash_check_config", "dflash_status_string")
+
+
+class DFlashConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("intermediate", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("num_target_layers", ctypes.c_int32), ("target_hidden", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float)]
+
+
+_LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+
+
+class DFlashLayerWeights(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in _LAYER_FIELDS]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {dflash_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                            ctypes.c_size_t)
+    CFG = ctypes.POINTER(DFlashConfig)
+    lib.dflash_build_plan.argtypes = [P, I32, I32, P, I64, U64, I32, I32, P, P, P, P, P, P, P]
+    lib.dflash_build_plan.restype = ctypes.c_int
+    lib.dflash_ctx_proj.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, I64, I64, P, SZ, P]
+    lib.dflash_ctx_proj.restype = ctypes.c_int
+    lib.dflash_block_attn.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, SZ, P]
+    lib.dflash_block_attn.restype = ctypes.c_int
+    lib.dflash_body_forward.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, SZ, P]
+    lib.dflash_body_forward.restype = ctypes.c_int
+    lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
+    lib.dflash_workspace_size.restype = ctypes.c_size_t
+    lib.dflash_check_config.argtypes = [CFG]
+    lib.dflash_check_config.restype = ctypes.c_int
+    lib.dflash_status_string.argtypes = [ctypes.c_int]
+    lib.dflash_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+try:
+    _lib = _load()
+except Exception as exc:  # noqa: BLE001 - surface any build/load failure as ImportError
+    raise ImportError(f"libdflash is not available ({LIB_PATH}): {exc}") from exc
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+# ----------------------------------------------------------------- marshalling helpers
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def make_config(hidden, num_q_heads, num_kv_heads, head_dim, intermediate, num_layers,
+                num_target_layers, target_hidden, block_size, dtype, rope_theta=1e6,
+                rms_eps=1e-6) -> DFlashConfig:
+    dt = {"f32": DFLASH_F32, "bf16": DFLASH_BF16}.get(dtype, dtype)
+    return DFlashConfig(hidden, num_q_heads, num_kv_heads, head_dim, intermediate, num_layers,
+                        num_target_layers, target_hidden, block_size, int(dt), float(rope_theta),
+                        float(rms_eps))
+
+
+def config_from_workload(w) -> DFlashConfig:
+    """Config from a workload description (attributes named as in DFlashConfig)."""
+    return make_config(w.hidden, w.num_q_heads, w.num_kv_heads, w.head_dim, w.intermediate,
+                       w.num_layers, w.num_target_layers, w.target_hidden, w.block_size, w.dtype,
+                       w.rope_theta, w.rms_eps)
+
+
+def _layers(layers: Sequence[Dict[str, object]]):
+    arr = (DFlashLayerWeights * len(layers))()
+    for i, L in enumerate(layers):
+        for f in _LAYER_FIELDS:
+            setattr(arr[i], f, _ptr(L.get(f)) if isinstance(L, dict) else _ptr(getattr(L, f)))
+    return arr
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _check(fn, status):
+    if status != DFLASH_OK:
+        raise DFlashError(fn, status)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+# ----------------------------------------------------------------- entry points
+def dflash_status_string(status: int) -> str:
+    return _lib.dflash_status_string(int(status)).decode()
+
+
+def dflash_check_config(cfg: DFlashConfig) -> int:
+    return _lib.dflash_check_config(ctypes.byref(cfg))
+
+
+def dflash_workspace_size(cfg: DFlashConfig, num_blocks: int, ctx_rows: int) -> int:
+    return _lib.dflash_workspace_size(ctypes.byref(cfg), int(num_blocks), int(ctx_rows))
+
+
+def dflash_build_plan(mask, sample_ids, step: int, seed: int, anchors_per_row: int, block_size: int,
+                      anchors, positions, valid, loss_mask, num_anchors, block_ctx_base=None,
+                      stream=None) -> None:
+    B, S = mask.shape
+    s = _lib.dflash_build_plan(_ptr(mask), B, S, _ptr(sample_ids), int(step),
+                               int(seed) & ((1 << 64) - 1), int(anchors_per_row), int(block_size),
+                               _ptr(anchors), _ptr(positions), _ptr(valid), _ptr(loss_mask),
+                               _ptr(num_anchors), _ptr(block_ctx_base), _stream(stream, mask))
+    _check("dflash_build_plan", s)
+
+
+def dflash_ctx_proj(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
+                    num_rows: int, positions, w_proj, layers, ctx_k: List, ctx_v: List,
+                    ctx_total: int, row_offset: int, workspace, stream=None) -> None:
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_ctx_proj(ctypes.byref(cfg), _ptr(target_states), int(ts_row_stride),
+                             int(ts_layer_stride), int(num_rows), _ptr(positions), _ptr(w_proj), lw,
+                             ck, cv, int(ctx_total), int(row_offset), wp, wb,
+                             _stream(stream, target_states))
+    _check("dflash_ctx_proj", s)
+
+
+def dflash_block_attn(cfg: DFlashConfig, num_blocks: int, q, k_blk, v_blk, ctx_k, ctx_v,
+                      ctx_total: int, block_ctx_base, block_anchor, block_valid, out, workspace,
+                      stream=None) -> None:
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_block_attn(ctypes.byref(cfg), int(num_blocks), _ptr(q), _ptr(k_blk), _ptr(v_blk),
+                               _ptr(ctx_k), _ptr(ctx_v), int(ctx_total), _ptr(block_ctx_base),
+                               _ptr(block_anchor), _ptr(block_valid), _ptr(out), wp, wb,
+                               _stream(stream, q))
+    _check("dflash_block_attn", s)
+
+
+def dflash_body_forward(cfg: DFlashConfig, num_blocks: int, block_embeds, layers, ctx_k: List,
+                        ctx_v: List, ctx_total: int, block_ctx_base, block_anchor, block_valid, out,
+                        workspace, stream=None) -> None:
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_body_forward(ctypes.byref(cfg), int(num_blocks), _ptr(block_embeds), lw, ck, cv,
+                                 int(ctx_total), _ptr(block_ctx_base), _ptr(block_anchor),
+                                 _ptr(block_valid), _ptr(out), wp, wb, _stream(stream, block_embeds))
+    _check("dflash_body_forward", s)

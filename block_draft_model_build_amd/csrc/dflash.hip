@@ -1,0 +1,342 @@
+// libdflash entry points: argument checks, workspace carving and launch
+// sequencing for the context projection, the dual-source block attention and
+// the draft body. All arithmetic happens in the kernels of gemm.h,
+// attention.h and the RMSNorm kernel below.
+#include <string.h>
+
+#include "attention.h"
+#include "common.h"
+#include "gemm.h"
+#include "internal.h"
+
+namespace dflash {
+
+// Large tiles for the big context GEMMs, 128x128 tiles (one 32-row MFMA strip
+// per wave) when the row count is small.
+using BigTile = TileCfg<256, 256, 2, 2>;
+using MidTile = TileCfg<128, 128, 4, 1>;
+static_assert(BigTile::WN == 128 && MidTile::WN == 128, "gate/up interleave and RoPE pairing assume WN = 128");
+
+template <typename T, class AL, class BL, class EP>
+static hipError_t gemm(int M, int N, int K, const AL& al, const BL& bl, const EP& ep, hipStream_t st) {
+    if (M >= 2048 && N % 256 == 0) return launch_gemm<T, BigTile>(M, N, K, al, bl, ep, st);
+    return launch_gemm<T, MidTile>(M, N, K, al, bl, ep, st);
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// out[row] = x / sqrt(mean(x^2) + eps) * w, x read as fp32; optionally copies
+// x into the fp32 residual stream (first layer: embeddings -> h).
+template <typename TIN, typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in, float* __restrict__ hcopy,
+                                                      const T* __restrict__ w, T* __restrict__ out, int H,
+                                                      float eps) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const TIN* x = in + row * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        float v = to_f32(x[i]);
+        ss += v * v;
+    }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += 256) {
+        float v = to_f32(x[i]);
+        if (hcopy) hcopy[row * H + i] = v;
+        out[row * H + i] = from_f32<T>(v * r * to_f32(w[i]));
+    }
+}
+
+// ------------------------------------------------------------------ attention launch
+template <typename T, int D, int QC>
+static hipError_t attn_launch_t(const dflash_config& c, const AttnArgs<T>& a, int nb, hipStream_t st) {
+    const int items_max = c.num_kv_heads * (attn_target_splits(c, nb) + nb);
+    hipLaunchKernelGGL((block_attn_kernel<T, D, QC>), dim3(items_max), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, QC>), dim3(nb, c.num_kv_heads), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t attn_launch(const dflash_config& c, const AttnArgs<T>& a, int nb, hipStream_t st) {
+    constexpr int D = 256 / (int)sizeof(T);
+    if (attn_qcols(c) == 32) return attn_launch_t<T, D, 32>(c, a, nb, st);
+    return attn_launch_t<T, D, 64>(c, a, nb, st);
+}
+
+template <typename T>
+static AttnArgs<T> attn_args(const dflash_config& c, int nb, const T* q, int64_t q_ld, const T* kb,
+                             const T* vb, int64_t kv_ld, const T* ck, const T* cv, int64_t ctx_total,
+                             const int64_t* base, const int32_t* anchor, const uint8_t* valid, T* out,
+                             int64_t out_ld, char* ws, const Workspace& w) {
+    AttnArgs<T> a;
+    a.q = q; a.q_ld = q_ld; a.kb = kb; a.vb = vb; a.kv_ld = kv_ld;
+    a.ck = ck; a.cv = cv; a.ctx_total = ctx_total;
+    a.base = base; a.anchor = anchor; a.valid = valid;
+    a.out = out; a.out_ld = out_ld;
+    a.nb = nb; a.bs = c.block_size; a.hq = c.num_q_heads; a.hkv = c.num_kv_heads;
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)c.head_dim));
+    a.item_start = reinterpret_cast<const int*>(ws + w.item_start);
+    a.chunk = reinterpret_cast<const int*>(ws + w.chunk);
+    a.part_o = reinterpret_cast<float*>(ws + w.part_o);
+    a.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+    a.rt = make_rope_turns(c);
+    return a;
+}
+
+static hipError_t attn_schedule(const dflash_config& c, int nb, const int64_t* base, const int32_t* anchor,
+                                int64_t ctx_total, char* ws, const Workspace& w, hipStream_t st) {
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, base, anchor, nb, ctx_total,
+                       attn_target_splits(c, nb), reinterpret_cast<int*>(ws + w.item_start),
+                       reinterpret_cast<int*>(ws + w.chunk));
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ typed bodies
+template <typename T>
+static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, int64_t ls, int64_t rows,
+                             const int32_t* positions, const T* w_proj, const dflash_layer_weights* layers,
+                             void* const* ck, void* const* cv, int64_t ctx_total, int64_t row_offset,
+                             char* ws, hipStream_t st) {
+    const Workspace w = workspace_layout(c, 0, rows);
+    T* C = reinterpret_cast<T*>(ws + w.c);
+    const int H = c.hidden, K = c.num_target_layers * c.target_hidden;
+    const int M = (int)rows;
+    hipError_t e = gemm<T>(M, H, K, AStacked<T>{ts, rs, ls, c.target_hidden}, BPlain<T>{w_proj, K},
+                           EpStore<T>{C, H}, st);
+    if (e != hipSuccess) return e;
+    BCtxKV<T> b{};
+    EpCtxKV<T> ep{};
+    for (int l = 0; l < c.num_layers; ++l) {
+        b.wk[l] = static_cast<const T*>(layers[l].wk);
+        b.wv[l] = static_cast<const T*>(layers[l].wv);
+        ep.ck[l] = static_cast<T*>(ck[l]);
+        ep.cv[l] = static_cast<T*>(cv[l]);
+    }
+    b.hkvd = c.num_kv_heads * c.head_dim;
+    b.ld = H;
+    ep.positions = positions;
+    ep.ctx_total = ctx_total;
+    ep.row_offset = row_offset;
+    ep.hkv = c.num_kv_heads;
+    ep.rt = make_rope_turns(c);
+    const int N = c.num_layers * 2 * c.num_kv_heads * c.head_dim;
+    // The RoPE epilogue needs registers the 256x256 tile does not have left.
+    return launch_gemm<T, MidTile>(M, N, H, APlain<T>{C, H}, b, ep, st);
+}
+
+template <typename T>
+static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dflash_layer_weights* layers,
+                         void* const* ck, void* const* cv, int64_t ctx_total, const int64_t* base,
+                         const int32_t* anchor, const uint8_t* valid, T* out, char* ws, hipStream_t st) {
+    const Workspace w = workspace_layout(c, nb, 0);
+    const int R = nb * c.block_size, H = c.hidden, D = c.head_dim;
+    const int nq = c.num_q_heads * D, nk = c.num_kv_heads * D, nqkv = nq + 2 * nk, I = c.intermediate;
+    float* h = reinterpret_cast<float*>(ws + w.h);
+    T* x = reinterpret_cast<T*>(ws + w.x);
+    T* qkv = reinterpret_cast<T*>(ws + w.qkv);
+    T* att = reinterpret_cast<T*>(ws + w.att);
+    T* u = reinterpret_cast<T*>(ws + w.u);
+    hipError_t e = attn_schedule(c, nb, base, anchor, ctx_total, ws, w, st);
+    if (e != hipSuccess) return e;
+    for (int l = 0; l < c.num_layers; ++l) {
+        const dflash_layer_weights& L = layers[l];
+        if (l == 0)
+            hipLaunchKernelGGL((rmsnorm_kernel<T, T>), dim3(R), dim3(256), 0, st, emb, h,
+                               static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
+        else
+            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
+                               static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = gemm<T>(R, nqkv, H, APlain<T>{x, H},
+                    BQKV<T>{static_cast<const T*>(L.wq), static_cast<const T*>(L.wk),
+                            static_cast<const T*>(L.wv), nq, nk, H},
+                    EpStore<T>{qkv, nqkv}, st);
+        if (e != hipSuccess) return e;
+        AttnArgs<T> a = attn_args<T>(c, nb, qkv, nqkv, qkv + nq, qkv + nq + nk, nqkv,
+                                     static_cast<const T*>(ck[l]), static_cast<const T*>(cv[l]), ctx_total,
+                                     base, anchor, valid, att, nq, ws, w);
+        if ((e = attn_launch<T>(c, a, nb, st)) != hipSuccess) return e;
+        e = gemm<T>(R, H, nq, APlain<T>{att, nq}, BPlain<T>{static_cast<const T*>(L.wo), nq},
+                    EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0}, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
+                           static_cast<const T*>(L.mlp_norm), x, H, c.rms_eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = gemm<T>(R, 2 * I, H, APlain<T>{x, H},
+                    BGateUp<T, 128>{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), H},
+                    EpSwiGLU<T>{u, I}, st);
+        if (e != hipSuccess) return e;
+        const bool last = l + 1 == c.num_layers;
+        e = gemm<T>(R, H, I, APlain<T>{u, I}, BPlain<T>{static_cast<const T*>(L.w_down), I},
+                    EpResidual<T>{h, H, last ? out : nullptr, valid, anchor, c.block_size}, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------------ checks
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dflash_status check_config(const dflash_config* c) {
+    if (c == nullptr) return DFLASH_ERR_INVALID_ARG;
+    if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_INVALID_ARG;
+    if (c->hidden <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
+        c->intermediate <= 0 || c->num_layers <= 0 || c->num_target_layers <= 0 || c->target_hidden <= 0 ||
+        c->block_size <= 0 || !(c->rope_theta > 0.0) || !(c->rms_eps >= 0.f))
+        return DFLASH_ERR_INVALID_ARG;
+    if (c->num_q_heads % c->num_kv_heads != 0) return DFLASH_ERR_INVALID_ARG;
+    const int eb = elem_bytes(*c), bk = 128 / eb;
+    if (c->head_dim * eb != 256) return DFLASH_ERR_UNSUPPORTED;
+    if (c->block_size * (c->num_q_heads / c->num_kv_heads) > 64) return DFLASH_ERR_UNSUPPORTED;
+    if (c->num_layers > kMaxLayers) return DFLASH_ERR_UNSUPPORTED;
+    if (c->hidden % 128 != 0 || c->intermediate % 64 != 0 || c->target_hidden % bk != 0) return DFLASH_ERR_UNSUPPORTED;
+    if (((int64_t)c->num_q_heads + 2 * c->num_kv_heads) * c->head_dim % 128 != 0) return DFLASH_ERR_UNSUPPORTED;
+    if ((int64_t)c->num_target_layers * c->target_hidden > INT32_MAX / 2) return DFLASH_ERR_UNSUPPORTED;
+    return DFLASH_OK;
+}
+
+}  // namespace dflash
+
+using namespace dflash;
+
+extern "C" dflash_status dflash_check_config(const dflash_config* cfg) { return check_config(cfg); }
+
+extern "C" const char* dflash_status_string(dflash_status s) {
+    switch (s) {
+        case DFLASH_OK: return "ok";
+        case DFLASH_ERR_INVALID_ARG: return "invalid argument";
+        case DFLASH_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case DFLASH_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case DFLASH_ERR_HIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+extern "C" size_t dflash_workspace_size(const dflash_config* cfg, int32_t num_blocks, int64_t ctx_rows) {
+    if (check_config(cfg) != DFLASH_OK || num_blocks < 0 || ctx_rows < 0) return 0;
+    return workspace_layout(*cfg, num_blocks, ctx_rows).total;
+}
+
+static dflash_status ws_check(const dflash_config* c, int nb, int64_t rows, void* ws, size_t bytes) {
+    const size_t need = workspace_layout(*c, nb, rows).total;
+    if (ws == nullptr || bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DFLASH_ERR_WORKSPACE;
+    return DFLASH_OK;
+}
+
+extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* target_states,
+                                         int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                         const int32_t* positions, const void* w_proj,
+                                         const dflash_layer_weights* layers, void* const* ctx_k,
+                                         void* const* ctx_v, int64_t ctx_total, int64_t row_offset,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (num_rows < 0 || ctx_total < 0 || row_offset < 0 || row_offset + num_rows > ctx_total)
+        return DFLASH_ERR_INVALID_ARG;
+    if (num_rows > INT32_MAX / 2) return DFLASH_ERR_UNSUPPORTED;
+    if (num_rows == 0) return DFLASH_OK;
+    const int64_t vec = 16 / elem_bytes(*cfg);
+    if (target_states == nullptr || positions == nullptr || w_proj == nullptr || layers == nullptr ||
+        ctx_k == nullptr || ctx_v == nullptr || !aligned16(target_states) || !aligned16(w_proj) ||
+        ts_row_stride <= 0 || ts_layer_stride < 0 || ts_row_stride % vec != 0 || ts_layer_stride % vec != 0)
+        return DFLASH_ERR_INVALID_ARG;
+    for (int l = 0; l < cfg->num_layers; ++l)
+        if (layers[l].wk == nullptr || layers[l].wv == nullptr || ctx_k[l] == nullptr || ctx_v[l] == nullptr ||
+            !aligned16(layers[l].wk) || !aligned16(layers[l].wv))
+            return DFLASH_ERR_INVALID_ARG;
+    if ((s = ws_check(cfg, 0, num_rows, workspace, workspace_bytes)) != DFLASH_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e;
+    if (cfg->dtype == DFLASH_BF16)
+        e = ctx_proj_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
+                               num_rows, positions, static_cast<const __bf16*>(w_proj), layers, ctx_k, ctx_v,
+                               ctx_total, row_offset, ws, st);
+    else
+        e = ctx_proj_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
+                              num_rows, positions, static_cast<const float*>(w_proj), layers, ctx_k, ctx_v,
+                              ctx_total, row_offset, ws, st);
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_block_attn(const dflash_config* cfg, int32_t num_blocks, const void* q,
+                                           const void* k_blk, const void* v_blk, const void* ctx_k,
+                                           const void* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
+                                           const int32_t* block_anchor, const uint8_t* block_valid, void* out,
+                                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (num_blocks < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2) return DFLASH_ERR_UNSUPPORTED;
+    if (num_blocks == 0) return DFLASH_OK;
+    if (q == nullptr || k_blk == nullptr || v_blk == nullptr || block_ctx_base == nullptr ||
+        block_anchor == nullptr || block_valid == nullptr || out == nullptr ||
+        (ctx_total > 0 && (ctx_k == nullptr || ctx_v == nullptr)) || !aligned16(ctx_k) || !aligned16(ctx_v))
+        return DFLASH_ERR_INVALID_ARG;
+    if ((s = ws_check(cfg, num_blocks, 0, workspace, workspace_bytes)) != DFLASH_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    const Workspace w = workspace_layout(*cfg, num_blocks, 0);
+    const int64_t nq = (int64_t)cfg->num_q_heads * cfg->head_dim, nk = (int64_t)cfg->num_kv_heads * cfg->head_dim;
+    hipError_t e = attn_schedule(*cfg, num_blocks, block_ctx_base, block_anchor, ctx_total, ws, w, st);
+    if (e == hipSuccess) {
+        if (cfg->dtype == DFLASH_BF16) {
+            using T = __bf16;
+            e = attn_launch<T>(*cfg,
+                               attn_args<T>(*cfg, num_blocks, static_cast<const T*>(q), nq, static_cast<const T*>(k_blk),
+                                            static_cast<const T*>(v_blk), nk, static_cast<const T*>(ctx_k),
+                                            static_cast<const T*>(ctx_v), ctx_total, block_ctx_base, block_anchor,
+                                            block_valid, static_cast<T*>(out), nq, ws, w),
+                               num_blocks, st);
+        } else {
+            using T = float;
+            e = attn_launch<T>(*cfg,
+                               attn_args<T>(*cfg, num_blocks, static_cast<const T*>(q), nq, static_cast<const T*>(k_blk),
+                                            static_cast<const T*>(v_blk), nk, static_cast<const T*>(ctx_k),
+                                            static_cast<const T*>(ctx_v), ctx_total, block_ctx_base, block_anchor,
+                                            block_valid, static_cast<T*>(out), nq, ws, w),
+                               num_blocks, st);
+        }
+    }
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t num_blocks, const void* block_embeds,
+                                             const dflash_layer_weights* layers, void* const* ctx_k,
+                                             void* const* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
+                                             const int32_t* block_anchor, const uint8_t* block_valid, void* out,
+                                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (num_blocks < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2) return DFLASH_ERR_UNSUPPORTED;
+    if (num_blocks == 0) return DFLASH_OK;
+    if (block_embeds == nullptr || layers == nullptr || ctx_k == nullptr || ctx_v == nullptr ||
+        block_ctx_base == nullptr || block_anchor == nullptr || block_valid == nullptr || out == nullptr)
+        return DFLASH_ERR_INVALID_ARG;
+    for (int l = 0; l < cfg->num_layers; ++l) {
+        const dflash_layer_weights& L = layers[l];
+        const void* ptrs[9] = {L.attn_norm, L.wq, L.wk, L.wv, L.wo, L.mlp_norm, L.w_gate, L.w_up, L.w_down};
+        for (const void* p : ptrs)
+            if (p == nullptr || !aligned16(p)) return DFLASH_ERR_INVALID_ARG;
+        if ((ctx_total > 0 && (ctx_k[l] == nullptr || ctx_v[l] == nullptr)) || !aligned16(ctx_k[l]) ||
+            !aligned16(ctx_v[l]))
+            return DFLASH_ERR_INVALID_ARG;
+    }
+    if ((s = ws_check(cfg, num_blocks, 0, workspace, workspace_bytes)) != DFLASH_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e;
+    if (cfg->dtype == DFLASH_BF16)
+        e = body_t<__bf16>(*cfg, num_blocks, static_cast<const __bf16*>(block_embeds), layers, ctx_k, ctx_v,
+                           ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<__bf16*>(out), ws, st);
+    else
+        e = body_t<float>(*cfg, num_blocks, static_cast<const float*>(block_embeds), layers, ctx_k, ctx_v,
+                          ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<float*>(out), ws, st);
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}

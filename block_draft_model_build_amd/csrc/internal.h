@@ -1,0 +1,71 @@
+// Host-side helpers shared by the libdflash translation units.
+#pragma once
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dflash.h"
+#include "common.h"
+
+namespace dflash {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int elem_bytes(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
+
+// Keys per split target for the attention scheduler; see attn_schedule_kernel.
+inline int attn_target_splits(const dflash_config& c, int nb) {
+    int t = (2048 + c.num_kv_heads - 1) / c.num_kv_heads;
+    return nb > t ? nb : t;
+}
+
+inline int attn_qcols(const dflash_config& c) {
+    return c.block_size * (c.num_q_heads / c.num_kv_heads) <= 32 ? 32 : 64;
+}
+
+// Workspace layout (every region 256-byte aligned):
+//   attention scheduler: item_start [nb+1] i32, chunk i32
+//   attention partials:  part_o [items_max][QC][D] f32, part_ml [items_max][QC][2] f32
+//   body: h [R][H] f32, x [R][H], qkv [R][(Hq+2Hkv)D], att [R][Hq D], u [R][I]   (dtype)
+//   ctx_proj: C [ctx_rows][H] (dtype); shares the body's space (calls are stream-ordered).
+struct Workspace {
+    size_t item_start, chunk, part_o, part_ml, h, x, qkv, att, u, c, total;
+};
+
+inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_rows) {
+    Workspace w{};
+    const size_t A = 256, eb = (size_t)elem_bytes(c);
+    const size_t R = (size_t)nb * (size_t)c.block_size;
+    const size_t H = (size_t)c.hidden, D = (size_t)c.head_dim;
+    const size_t qc = (size_t)attn_qcols(c);
+    const size_t items = (size_t)c.num_kv_heads * (size_t)(attn_target_splits(c, nb) + nb);
+    size_t off = 0;
+    w.item_start = off; off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
+    w.chunk = off;      off = align_up(off + sizeof(int), A);
+    w.part_o = off;     off = align_up(off + sizeof(float) * items * qc * D, A);
+    w.part_ml = off;    off = align_up(off + sizeof(float) * items * qc * 2, A);
+    const size_t shared0 = off;
+    w.h = off;          off = align_up(off + sizeof(float) * R * H, A);
+    w.x = off;          off = align_up(off + eb * R * H, A);
+    w.qkv = off;        off = align_up(off + eb * R * (size_t)(c.num_q_heads + 2 * c.num_kv_heads) * D, A);
+    w.att = off;        off = align_up(off + eb * R * (size_t)c.num_q_heads * D, A);
+    w.u = off;          off = align_up(off + eb * R * (size_t)c.intermediate, A);
+    const size_t body_end = off;
+    w.c = shared0;
+    const size_t c_end = align_up(shared0 + eb * (size_t)ctx_rows * H, A);
+    w.total = body_end > c_end ? body_end : c_end;
+    return w;
+}
+
+inline RopeTurns make_rope_turns(const dflash_config& c) {
+    RopeTurns rt{};
+    const int half = c.head_dim / 2;
+    for (int i = 0; i < half && i < 64; ++i)
+        rt.turns[i] = pow(c.rope_theta, -2.0 * (double)i / (double)c.head_dim) / (2.0 * M_PI);
+    return rt;
+}
+
+dflash_status check_config(const dflash_config* c);
+
+}  // namespace dflash

@@ -1,0 +1,226 @@
+/*
+ * libdflash -- the DFlash draft-body forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is stated on three pages:
+ *   [P1] angelspec documentation, "DFlash" (sections "How it works", "Configuration");
+ *   [P2] NeMo RL design docs, "DFlash Draft Body" (section "How It Works", steps 1-4, "Scope");
+ *   [P3] cooking-agi deep dive, "DFlash: drafting, verification, and speed"
+ *        (section "One DFlash generation cycle").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are HIP device pointers; "host" pointers are read
+ *     during the call only. The library never allocates device memory and never
+ *     frees caller memory; scratch space comes from the caller's workspace
+ *     (size: dflash_workspace_size).
+ *   - Asynchronous calls enqueue kernels on `hip_stream` (a hipStream_t; NULL is
+ *     the null stream) and return before they finish. Every argument that can be
+ *     checked on the host is checked before anything is enqueued: a call that
+ *     returns an error has enqueued nothing. Kernel faults surface at the
+ *     caller's next synchronisation. A failed launch returns DFLASH_ERR_HIP.
+ *   - Matrices are row-major. Weights use the Linear layout [out, in]: y = x W^T.
+ *   - dtype DFLASH_BF16: every tensor argument (activations, weights, caches and
+ *     outputs) is bfloat16; arithmetic accumulates in fp32 and the residual
+ *     stream of the body is fp32. dtype DFLASH_F32: every tensor is fp32.
+ *   - Shape envelope (DFLASH_ERR_UNSUPPORTED outside it): head_dim 64 or 128;
+ *     num_q_heads a multiple of num_kv_heads; block_size * (num_q_heads /
+ *     num_kv_heads) <= 64; hidden, intermediate and num_q_heads*head_dim
+ *     multiples of 256 (bf16) / 128 (fp32)... see dflash_check_config; target
+ *     hidden a multiple of 64 elements (bf16) or 32 (fp32); num_layers <= 16.
+ *   - Calls on one stream are ordered; the library keeps no state between calls
+ *     and is safe to call from several threads on different streams with
+ *     different workspaces.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dflash_status {
+    DFLASH_OK = 0,
+    DFLASH_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shape */
+    DFLASH_ERR_UNSUPPORTED = 2,   /* valid, but outside the shapes the kernels implement */
+    DFLASH_ERR_WORKSPACE = 3,     /* workspace missing, too small or misaligned */
+    DFLASH_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} dflash_status;
+
+typedef enum dflash_dtype { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Draft-model dimensions ([P1] "Configuration": hidden_size, num_hidden_layers,
+ * num_target_layers, target_hidden_size, rope_theta; [P1] "How it works":
+ * block_size; [P2] step 2: a block is one anchor plus gamma = block_size - 1
+ * draft positions). rms_eps is not on the pages; 1e-6 is the usual value. */
+typedef struct dflash_config {
+    int32_t hidden;             /* H: draft hidden size */
+    int32_t num_q_heads;        /* Hq */
+    int32_t num_kv_heads;       /* Hkv; query head h reads KV head h / (Hq/Hkv) */
+    int32_t head_dim;           /* D */
+    int32_t intermediate;       /* I: SwiGLU width */
+    int32_t num_layers;         /* draft decoder layers */
+    int32_t num_target_layers;  /* L_t: target layers concatenated as context */
+    int32_t target_hidden;      /* H_t */
+    int32_t block_size;         /* bs = 1 + gamma */
+    int32_t dtype;              /* dflash_dtype */
+    double rope_theta;
+    float rms_eps;
+} dflash_config;
+
+/* One draft decoder layer's weights (device pointers, dtype of the config).
+ * attn_norm, mlp_norm: [H]; wq: [Hq*D, H]; wk, wv: [Hkv*D, H]; wo: [H, Hq*D];
+ * w_gate, w_up: [I, H]; w_down: [H, I]. */
+typedef struct dflash_layer_weights {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} dflash_layer_weights;
+
+/*
+ * dflash_build_plan -- choose anchors and the per-position masks on the device.
+ * [P2] step 1: an anchor is a valid position; the same mask, sample ids,
+ * optimizer step and seed give the same plan; rows with equal sample ids get
+ * equal anchors; a row with no valid window contributes no draft loss.
+ * [P2] step 2: block n of row b covers positions anchor + k, k = 0..bs-1.
+ * [P2] step 4: loss_mask leaves out the anchor and invalid positions.
+ * [P1] "How it works", anchor sampling: anchors are sampled across the sequence.
+ *
+ * The sampler (the pages fix its properties, not its form): with SplitMix64
+ * mix(), row key = mix(mix(mix(seed) ^ sample_id) ^ step) (64-bit two's
+ * complement), key(a) = mix(row key ^ a). Position a is eligible when
+ * mask[a] and mask[a+1] are nonzero (0 <= a <= S-2). The min(N, #eligible)
+ * eligible positions with the smallest (key, a) are the anchors, stored in
+ * ascending order, padded with -1.
+ *
+ *   mask        device u8  [batch, seq_len]          (nonzero = valid)
+ *   sample_ids  device i64 [batch]
+ *   anchors     device i32 [batch, N]                (out; -1 = empty slot)
+ *   positions   device i32 [batch, N, block_size]    (out; anchor + k, -1 for empty slots)
+ *   valid       device u8  [batch, N, block_size]    (out; anchor+k < S and mask[anchor+k])
+ *   loss_mask   device u8  [batch, N, block_size]    (out; valid and k >= 1)
+ *   num_anchors device i32 [batch]                   (out)
+ *   block_ctx_base device i64 [batch, N] or NULL     (out; b * seq_len, the first
+ *               context row of each block's sequence when the context rows of the
+ *               batch are stored back to back)
+ * Errors: INVALID_ARG for negative sizes, block_size < 1 or a null required
+ * pointer when batch*N > 0. Deterministic: outputs are a pure function of
+ * (mask, sample_ids, step, seed, N, block_size).
+ */
+dflash_status dflash_build_plan(const uint8_t *mask, int32_t batch, int32_t seq_len,
+                                const int64_t *sample_ids, int64_t step, uint64_t seed,
+                                int32_t anchors_per_row, int32_t block_size,
+                                int32_t *anchors, int32_t *positions, uint8_t *valid,
+                                uint8_t *loss_mask, int32_t *num_anchors,
+                                int64_t *block_ctx_base, void *hip_stream);
+
+/*
+ * dflash_ctx_proj -- project target hidden states into every draft layer's
+ * context K/V cache. [P1] "How it works", dual-source KV context: the target's
+ * multi-layer hidden states are projected (W_proj) into the attention key/value
+ * space; [P1] "Configuration": the layers in target_layer_ids, concatenated in
+ * that order; [P3] "One DFlash generation cycle": target features enter every
+ * draft layer's K/V.
+ *
+ *   C = X W_proj^T                        X [num_rows, L_t*H_t], C [num_rows, H]
+ *   ctx_k[l][g][row_offset + r][:] = RoPE((C Wk_l^T)[r, g*D:(g+1)*D], positions[r])
+ *   ctx_v[l][g][row_offset + r][:] = (C Wv_l^T)[r, g*D:(g+1)*D]
+ *
+ *   target_states  device; element (r, k) of X is at
+ *                  target_states[r*ts_row_stride + (k / H_t)*ts_layer_stride + k % H_t],
+ *                  so both a concatenated [rows, L_t*H_t] buffer (row stride L_t*H_t,
+ *                  layer stride H_t) and per-layer slabs [L_t, rows, H_t] (row stride
+ *                  H_t, layer stride rows*H_t) are read in place. Strides are in
+ *                  elements and must be multiples of 8 (bf16) / 4 (fp32).
+ *   positions      device i32 [num_rows]: RoPE position of each row, in [0, ctx_total).
+ *   w_proj         device [H, L_t*H_t]
+ *   layers         host array [num_layers]; only wk and wv are read.
+ *   ctx_k, ctx_v   host arrays [num_layers] of device caches [Hkv][ctx_total][D]
+ *                  (head-major); rows [row_offset, row_offset + num_rows) are written.
+ * RoPE pairs dimension i with i + D/2 at angle position * rope_theta^(-2i/D).
+ * Errors: INVALID_ARG when row_offset + num_rows > ctx_total or a pointer is null;
+ * WORKSPACE when workspace_bytes < dflash_workspace_size(cfg, 0, num_rows).
+ */
+dflash_status dflash_ctx_proj(const dflash_config *cfg, const void *target_states,
+                              int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                              const int32_t *positions, const void *w_proj,
+                              const dflash_layer_weights *layers, void *const *ctx_k,
+                              void *const *ctx_v, int64_t ctx_total, int64_t row_offset,
+                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * dflash_block_attn -- one layer's dual-source block attention.
+ * [P2] step 3: a block reads the target prefix before its anchor and all
+ * positions of its own block, never another block; outputs are produced for
+ * block positions only. [P1] "How it works": attended together with the draft
+ * tokens' own K/V. [P3] "One DFlash generation cycle": a block must not read
+ * target features that contain its future.
+ *
+ * For block n with anchor a = block_anchor[n] and base = block_ctx_base[n], query
+ * row k (position a + k) of head h attends, with softmax(q k^T / sqrt(D)), to
+ *   ctx_k/ctx_v[g][base + j] for 0 <= j < a        (prefix, strictly before the anchor)
+ *   k_blk/v_blk rows n*bs + k', k' = 0..bs-1        (its whole block, both directions)
+ * where g = h / (Hq/Hkv). q and k_blk arrive un-rotated and are rotated at a + k.
+ *
+ *   q              device [nb*bs, Hq*D]
+ *   k_blk, v_blk   device [nb*bs, Hkv*D]
+ *   ctx_k, ctx_v   device [Hkv][ctx_total][D], K already rotated at its positions
+ *   block_ctx_base device i64 [nb]; block_anchor device i32 [nb] (-1: empty block)
+ *   block_valid    device u8 [nb*bs]
+ *   out            device [nb*bs, Hq*D]; rows with block_valid == 0 and all rows of
+ *                  empty blocks are written as exact zeros.
+ * Anchors and bases are clamped on the device so that base + a <= ctx_total.
+ * Errors: INVALID_ARG for null pointers or nb < 0; WORKSPACE when workspace_bytes <
+ * dflash_workspace_size(cfg, nb, 0).
+ */
+dflash_status dflash_block_attn(const dflash_config *cfg, int32_t num_blocks, const void *q,
+                                const void *k_blk, const void *v_blk, const void *ctx_k,
+                                const void *ctx_v, int64_t ctx_total,
+                                const int64_t *block_ctx_base, const int32_t *block_anchor,
+                                const uint8_t *block_valid, void *out, void *workspace,
+                                size_t workspace_bytes, void *hip_stream);
+
+/*
+ * dflash_body_forward -- the draft body: all num_layers draft decoder layers over
+ * the blocks. [P2] step 3: the body runs the block embeddings through the draft
+ * decoder layers, each block reading the prefix before its anchor and its own
+ * block; step 4: one hidden state per block position, zero for invalid
+ * positions; "Scope": no vocabulary logits, no loss.
+ *
+ * Per layer l, with h the fp32 residual stream (h = block_embeds at the start):
+ *   x = RMSNorm(h) * attn_norm;  q, k, v = x Wq^T, x Wk^T, x Wv^T
+ *   h += DualSourceAttention(q, k, v, ctx_k[l], ctx_v[l]) Wo^T   (as dflash_block_attn)
+ *   y = RMSNorm(h) * mlp_norm;   h += (SiLU(y Wg^T) * (y Wu^T)) Wd^T
+ * out = h (cast to the config dtype) on valid rows, exact zero on rows with
+ * block_valid == 0 and on every row of an empty block (anchor -1). Invalid rows
+ * still take part in their block's attention in every layer.
+ *
+ *   block_embeds   device [nb*bs, H] (caller-supplied embedding per block position)
+ *   layers         host array [num_layers]
+ *   ctx_k, ctx_v   host arrays [num_layers] of device [Hkv][ctx_total][D]
+ *   out            device [nb*bs, H]
+ * Errors: as dflash_block_attn; WORKSPACE below dflash_workspace_size(cfg, nb, 0).
+ */
+dflash_status dflash_body_forward(const dflash_config *cfg, int32_t num_blocks,
+                                  const void *block_embeds, const dflash_layer_weights *layers,
+                                  void *const *ctx_k, void *const *ctx_v, int64_t ctx_total,
+                                  const int64_t *block_ctx_base, const int32_t *block_anchor,
+                                  const uint8_t *block_valid, void *out, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
+ * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one
+ * buffer of this size serves all of them; 256-byte aligned). Returns 0 for an
+ * invalid or unsupported config. */
+size_t dflash_workspace_size(const dflash_config *cfg, int32_t num_blocks, int64_t ctx_rows);
+
+/* Checks a config against the shape envelope without touching the GPU. */
+dflash_status dflash_check_config(const dflash_config *cfg);
+
+/* Static text for a status code. */
+const char *dflash_status_string(dflash_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

@@ -1,0 +1,132 @@
+"""dflash_block_attn vs the oracle's dual-source attention (NeMo RL "DFlash Draft
+Body", How It Works, step 3; angelspec "DFlash", How it works, dual-source KV
+context), from tiny fp32 cases to the long-context and ragged-cache shapes."""
+import numpy as np
+import pytest
+import torch
+
+import block_draft_model_build_amd as d
+import oracle
+from dflash_synth import WORKLOADS, Rng, random_attention_inputs, scaled
+from tests.helpers import BF16_TOL, F32_TOL, compare, np64, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, bases, anchors, valid, ctx_total, seed, check_blocks=None):
+    dev = "cuda"
+    nb, bs = len(anchors), w.block_size
+    cfg = d.config_from_workload(w)
+    rng = Rng(seed, dev)
+    q, k, v, ck, cv = random_attention_inputs(rng, nb, bs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                              ctx_total, w.torch_dtype)
+    base_t = torch.tensor(bases, dtype=torch.int64, device=dev)
+    anc_t = torch.tensor(anchors, dtype=torch.int32, device=dev)
+    val_t = torch.tensor(np.asarray(valid, np.uint8).reshape(-1), dtype=torch.uint8, device=dev)
+    out = torch.full((nb * bs, w.num_q_heads * w.head_dim), float("nan"), dtype=w.torch_dtype, device=dev)
+    ws = workspace(d, cfg, nb, 0, dev)
+    d.dflash_block_attn(cfg, nb, q, k, v, ck, cv, ctx_total, base_t, anc_t, val_t, out, ws)
+    torch.cuda.synchronize()
+    blocks = list(range(nb)) if check_blocks is None else list(check_blocks)
+    tol = F32_TOL if w.dtype == "f32" else BF16_TOL
+    val = np.asarray(valid, np.uint8).reshape(nb, bs)
+    for n in blocks:
+        rows = slice(n * bs, (n + 1) * bs)
+        a = int(anchors[n])
+        b0 = int(bases[n])
+        lo, hi = (b0, b0 + max(a, 0))
+        ref = oracle.block_attn_call(np64(q[rows]), np64(k[rows]), np64(v[rows]), np64(ck[:, lo:hi]),
+                                     np64(cv[:, lo:hi]), [0], [a], val[n], bs, w.num_q_heads,
+                                     w.num_kv_heads, w.head_dim, w.rope_theta)
+        got = out[rows]
+        compare(got, ref, tol, f"block {n} (anchor {a})")
+        zero_rows = (val[n] == 0) | (a < 0)
+        if zero_rows.any():
+            assert (got[torch.from_numpy(zero_rows).to(dev)].float() == 0).all()
+    return out
+
+
+def test_tiny_fp32():
+    w = WORKLOADS["c1"]
+    valid = np.ones((4, 8), np.uint8)
+    valid[3, 3:] = 0
+    _run(w, [0, 0, 0, 0], [21, 89, 95, 125], valid, 128, seed=1)
+
+
+def test_fp32_edge_anchors():
+    w = WORKLOADS["c1"]
+    anchors = [0, 1, 127, -1, 64, 300]           # 300 exceeds the context: clamped to 128
+    valid = np.ones((6, 8), np.uint8)
+    valid[2, 1:] = 0
+    _run(w, [0] * 6, anchors, valid, 128, seed=2, check_blocks=[0, 1, 2, 3, 4])
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 2), (8, 8)])
+def test_bf16_ragged(hq, hkv):
+    w = scaled(WORKLOADS["c2"], num_q_heads=hq, num_kv_heads=hkv, hidden=1024, block_size=16 if hq // hkv <= 4 else 8)
+    S = 700
+    anchors = [0, 1, 33, 128, 129, 698, -1, 511, 300]
+    bases = [0, S, 0, S, 0, S, 0, S, 0]
+    valid = np.ones((len(anchors), w.block_size), np.uint8)
+    valid[5, 2:] = 0
+    valid[2, 7] = 0
+    _run(w, bases, anchors, valid, 2 * S, seed=3)
+
+
+def test_bf16_split_prefixes():
+    # Few blocks with long prefixes: each prefix is split over several work items
+    # and merged by the combine step.
+    w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
+    S = 6000
+    _run(w, [0, S, 0], [5999, 3001, 700], np.ones((3, 16), np.uint8), 2 * S, seed=4)
+
+
+def test_ragged_cache_requests():
+    # Inference shape: 64 requests, prefixes 1024..16384 packed back to back.
+    w = WORKLOADS["c5"]
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1024, 16385, size=64)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    check = [0, 1, int(np.argmax(lens)), int(np.argmin(lens)), 63]
+    _run(w, offs[:-1].tolist(), lens.tolist(), np.ones((64, 16), np.uint8), int(offs[-1]), seed=5,
+         check_blocks=check)
+
+
+def test_long_context_blocks():
+    # Long-context shape: one 32768-row sequence, 512 anchors from the plan.
+    w = WORKLOADS["c4"]
+    S, N = 32768, 512
+    anchors, _, valid, _, _ = oracle.build_plan(np.ones((1, S), np.uint8), [0], 0, 0, N, 16)
+    a = anchors[0].tolist()
+    check = [0, 1, 255, 510, 511]
+    _run(w, [0] * N, a, valid[0], S, seed=6, check_blocks=check)
+
+
+def test_deterministic_and_information_boundary():
+    w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
+    dev = "cuda"
+    cfg = d.config_from_workload(w)
+    S, nb, bs = 3000, 4, 16
+    rng = Rng(7, dev)
+    q, k, v, ck, cv = random_attention_inputs(rng, nb, bs, 8, 2, 128, 2 * S, torch.bfloat16)
+    bases = torch.tensor([0, 0, S, S], dtype=torch.int64, device=dev)
+    anchors = torch.tensor([1500, 2999, 700, 2500], dtype=torch.int32, device=dev)
+    valid = torch.ones(nb * bs, dtype=torch.uint8, device=dev)
+    ws = workspace(d, cfg, nb, 0, dev)
+
+    def run(q, k, v, ck, cv):
+        out = torch.empty((nb * bs, 8 * 128), dtype=torch.bfloat16, device=dev)
+        d.dflash_block_attn(cfg, nb, q, k, v, ck, cv, 2 * S, bases, anchors, valid, out, ws)
+        torch.cuda.synchronize()
+        return out
+
+    ref = run(q, k, v, ck, cv)
+    assert torch.equal(ref, run(q, k, v, ck, cv))
+    ck2, cv2, k2, v2 = ck.clone(), cv.clone(), k.clone(), v.clone()
+    ck2[:, 1500:S] += 3.0                # block 0 (base 0, anchor 1500) may not read these
+    cv2[:, 1500:S] -= 2.0
+    ck2[:, S:] = float("nan")            # another sequence
+    k2[bs:] = float("nan")               # other blocks
+    v2[bs:] = float("nan")
+    out = run(q, k2, v2, ck2, cv2)
+    assert torch.equal(out[:bs], ref[:bs])

@@ -1,0 +1,172 @@
+"""Context projection and the full draft body on the GPU vs the oracle
+(angelspec "DFlash", How it works and Configuration; NeMo RL "DFlash Draft
+Body", How It Works, steps 1-4), from the tiny fp32 workload to sampled
+blocks of the full-size bf16 workloads, plus the pages' invariants."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_draft_model_build_amd as d
+import oracle
+from dflash_synth import WORKLOADS, make_inference_inputs, make_training_inputs, scaled
+from tests.helpers import (TrainingRun, compare, layers64, np64, oracle_cfg, oracle_training_blocks,
+                           tol_for, workspace)
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _c1_seed():
+    with open(os.path.join(HERE, "golden", "c1_plan.json")) as f:
+        return json.load(f)["seed"]
+
+
+def _check_plan(run):
+    w = run.w
+    ref = oracle.build_plan(run.inp["mask"].cpu().numpy(), run.inp["sample_ids"].cpu().numpy(),
+                            run.inp["step"], run.inp["plan_seed"], w.anchors_per_row, w.block_size)
+    assert np.array_equal(run.anchors.cpu().numpy(), ref[0])
+    assert np.array_equal(run.valid.cpu().numpy(), ref[2])
+    return ref
+
+
+def _check_ctx(run, rows):
+    """Context K/V of the given cache rows vs the oracle (computed for those rows only)."""
+    w, inp = run.w, run.inp
+    S = w.seq_len
+    layers = layers64(inp["layers"])
+    X = oracle.concat_target_states(np64(inp["states"][:, rows]))
+    C = oracle.ctx_proj(X, np64(inp["w_proj"]))
+    ck, cv = oracle.ctx_kv(C, layers, np.asarray(rows) % S, w.num_kv_heads, w.head_dim, w.rope_theta)
+    tol = tol_for(w)
+    for l in range(w.num_layers):
+        compare(run.ctx_k[l][:, rows], ck[l], tol, f"ctx_k layer {l}")
+        compare(run.ctx_v[l][:, rows], cv[l], tol, f"ctx_v layer {l}")
+
+
+def test_tiny_fp32_end_to_end():
+    w = WORKLOADS["c1"]
+    inp = make_training_inputs(w, "cuda", plan_seed=_c1_seed())
+    run = TrainingRun(d, w, inp).run()
+    anchors, _, valid, _, _ = _check_plan(run)
+    assert anchors.max() >= w.seq_len - w.block_size + 1          # one block overflows the end
+    _check_ctx(run, np.arange(w.seq_len))
+    ref = oracle_training_blocks(w, inp, anchors, valid, range(w.num_blocks))
+    compare(run.out, ref, tol_for(w), "body")
+    zero = torch.from_numpy(valid.reshape(-1) == 0).cuda()
+    assert zero.any() and (run.out[zero] == 0).all()
+
+
+SMALL_BF16 = scaled(WORKLOADS["c3"], batch=2, seq_len=300, num_target_layers=2, target_hidden=128,
+                    hidden=256, num_q_heads=4, num_kv_heads=2, intermediate=512, num_layers=2,
+                    block_size=16, anchors_per_row=6, seed=77)
+
+
+def test_small_bf16_multilayer_ragged():
+    w = SMALL_BF16
+    mask = torch.ones((2, 300), dtype=torch.uint8, device="cuda")
+    mask[1, 250:] = 0                                             # short second row
+    mask[0, 100:110] = 0
+    inp = make_training_inputs(w, "cuda", plan_seed=3, mask=mask)
+    run = TrainingRun(d, w, inp).run()
+    anchors, _, valid, _, _ = _check_plan(run)
+    _check_ctx(run, np.arange(2 * w.seq_len))
+    ref = oracle_training_blocks(w, inp, anchors, valid, range(w.num_blocks))
+    compare(run.out, ref, tol_for(w), "body")
+
+
+def test_concat_and_stacked_layouts_agree():
+    w = SMALL_BF16
+    inp = make_training_inputs(w, "cuda")
+    run = TrainingRun(d, w, inp)
+    run.ctx_proj()
+    k1 = [t.clone() for t in run.ctx_k]
+    X = torch.cat([inp["states"][i] for i in range(w.num_target_layers)], dim=-1).contiguous()
+    Kt = w.num_target_layers * w.target_hidden
+    d.dflash_ctx_proj(run.cfg, X, Kt, w.target_hidden, run.T, run.ctx_pos, inp["w_proj"], inp["layers"],
+                      run.ctx_k, run.ctx_v, run.T, 0, run.ws)
+    torch.cuda.synchronize()
+    for a, b in zip(k1, run.ctx_k):
+        assert torch.equal(a, b)
+
+
+def test_one_layer_bf16_full_size():
+    w = WORKLOADS["c2"]
+    inp = make_training_inputs(w, "cuda")
+    run = TrainingRun(d, w, inp).run()
+    anchors, _, valid, _, _ = _check_plan(run)
+    _check_ctx(run, np.array([0, 1, 2047, 2048, 5000, 8191]))
+    ref = oracle_training_blocks(w, inp, anchors, valid, range(w.num_blocks))
+    compare(run.out, ref, tol_for(w), "body (all 1024 rows)")
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_five_layer_full_size_sampled(name):
+    w = WORKLOADS[name]
+    inp = make_training_inputs(w, "cuda")
+    run = TrainingRun(d, w, inp).run()
+    anchors, _, valid, _, _ = _check_plan(run)
+    flat = anchors.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    blocks = sorted(set(order[:3].tolist()))                      # smallest anchors (cheap prefixes)
+    bs = w.block_size
+    rows = np.concatenate([np.arange(n * bs, (n + 1) * bs) for n in blocks])
+    ref = oracle_training_blocks(w, inp, anchors, valid, blocks)
+    compare(run.out[torch.from_numpy(rows).cuda()], ref, tol_for(w), f"{name} sampled blocks {blocks}")
+    _check_ctx(run, np.array([0, 3, w.seq_len - 1, w.batch * w.seq_len - 1]))
+    # Every row of the full output is finite and invalid rows are exactly zero.
+    assert torch.isfinite(run.out.float()).all()
+    zero = torch.from_numpy(valid.reshape(-1) == 0).cuda()
+    assert (run.out[zero] == 0).all()
+
+
+def test_ragged_cache_body_sampled():
+    w = WORKLOADS["c5"]
+    inp = make_inference_inputs(w, "cuda")
+    cfg = d.config_from_workload(w)
+    out = torch.empty((w.num_blocks * w.block_size, w.hidden), dtype=torch.bfloat16, device="cuda")
+    ws = workspace(d, cfg, w.num_blocks, 0, "cuda")
+    d.dflash_body_forward(cfg, w.num_blocks, inp["emb"], inp["layers"], inp["ctx_k"], inp["ctx_v"],
+                          inp["total"], inp["block_ctx_base"], inp["block_anchor"], inp["block_valid"],
+                          out, ws)
+    torch.cuda.synchronize()
+    lens = inp["lengths"].cpu().numpy()
+    offs = inp["offsets"].cpu().numpy()
+    layers = layers64(inp["layers"])
+    bs = w.block_size
+    for r in [int(np.argmin(lens)), int(np.argmax(lens)), 7]:
+        lo, hi = int(offs[r]), int(offs[r + 1])
+        ck = [np64(k[:, lo:hi]) for k in inp["ctx_k"]]
+        cv = [np64(v[:, lo:hi]) for v in inp["ctx_v"]]
+        ref = oracle.body_forward(np64(inp["emb"][r * bs:(r + 1) * bs]), layers, ck, cv, [0],
+                                  [int(lens[r])], np.ones(bs, np.uint8), oracle_cfg(w))
+        compare(out[r * bs:(r + 1) * bs], ref, tol_for(w), f"request {r} (prefix {lens[r]})")
+
+
+def test_body_invariants_bit_exact():
+    w = SMALL_BF16
+    inp = make_training_inputs(w, "cuda", plan_seed=5)
+    run = TrainingRun(d, w, inp).run()
+    ref = run.out.clone()
+    run.body()
+    torch.cuda.synchronize()
+    assert torch.equal(run.out, ref)                              # deterministic
+    anchors = run.anchors.cpu().numpy().reshape(-1)
+    n = int(np.argmin(np.where(anchors >= 0, anchors, 1 << 30)))   # block with the smallest anchor
+    a = int(anchors[n])
+    b = n // w.anchors_per_row
+    S, bs = w.seq_len, w.block_size
+    for l in range(w.num_layers):                                 # context at or after the anchor
+        run.ctx_k[l][:, b * S + a: (b + 1) * S] += 5.0
+        run.ctx_v[l][:, b * S + a: (b + 1) * S] = float("nan")
+    emb = inp["emb"]
+    saved = emb.clone()
+    emb[: n * bs] = float("nan")                                  # every other block's embeddings
+    emb[(n + 1) * bs:] = float("nan")
+    run.body()
+    torch.cuda.synchronize()
+    assert torch.equal(run.out[n * bs:(n + 1) * bs], ref[n * bs:(n + 1) * bs])
+    emb.copy_(saved)

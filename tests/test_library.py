@@ -1,0 +1,118 @@
+"""Host-side checks of libdflash that need no GPU: the library loads, exports
+every symbol include/dflash.h declares, sizes workspaces, and rejects bad
+arguments before enqueueing anything (only failing calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_draft_model_build_amd as d
+from dflash_synth import WORKLOADS, scaled
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared()
+    assert set(declared) == set(d.EXPORTED)
+    lib = ctypes.CDLL(d.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_config_checks():
+    for w in WORKLOADS.values():
+        assert d.dflash_check_config(d.config_from_workload(w)) == d.DFLASH_OK
+    c3 = WORKLOADS["c3"]
+    bad = [
+        (dict(head_dim=64), d.DFLASH_ERR_UNSUPPORTED),          # bf16 rows must be 256 bytes
+        (dict(num_q_heads=30), d.DFLASH_ERR_INVALID_ARG),       # not a multiple of kv heads
+        (dict(block_size=17), d.DFLASH_ERR_UNSUPPORTED),        # bs * G > 64
+        (dict(block_size=0), d.DFLASH_ERR_INVALID_ARG),
+        (dict(hidden=4000), d.DFLASH_ERR_UNSUPPORTED),
+        (dict(num_layers=17), d.DFLASH_ERR_UNSUPPORTED),
+        (dict(rope_theta=0.0), d.DFLASH_ERR_INVALID_ARG),
+    ]
+    for change, status in bad:
+        assert d.dflash_check_config(d.config_from_workload(scaled(c3, **change))) == status, change
+    assert d.dflash_workspace_size(d.config_from_workload(scaled(c3, head_dim=64)), 4, 4) == 0
+
+
+def test_workspace_size_grows_with_work():
+    c = d.config_from_workload(WORKLOADS["c3"])
+    a = d.dflash_workspace_size(c, 64, 0)
+    b = d.dflash_workspace_size(c, 256, 0)
+    e = d.dflash_workspace_size(c, 256, 32768)
+    assert 0 < a < b <= e
+    assert a % 256 == 0 and b % 256 == 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert d.dflash_status_string(s)
+    assert "workspace" in d.dflash_status_string(d.DFLASH_ERR_WORKSPACE)
+
+
+def _lib():
+    return d.library()
+
+
+def test_rejects_bad_arguments_before_launch():
+    lib = _lib()
+    cfg = d.config_from_workload(WORKLOADS["c2"])
+    fake = 1 << 20                               # 16-byte-aligned non-null value; never dereferenced
+    P = ctypes.c_void_p
+    # plan: negative sizes, missing outputs
+    assert lib.dflash_build_plan(P(fake), -1, 10, P(fake), 0, 0, 4, 4, P(fake), P(fake), P(fake),
+                                 P(fake), P(fake), None, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_build_plan(P(fake), 2, 10, P(fake), 0, 0, 4, 0, P(fake), P(fake), P(fake),
+                                 P(fake), P(fake), None, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_build_plan(P(fake), 2, 10, None, 0, 0, 4, 4, P(fake), P(fake), P(fake),
+                                 P(fake), P(fake), None, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_build_plan(None, 0, 10, None, 0, 0, 4, 4, None, None, None, None, None, None,
+                                 None) == d.DFLASH_OK                       # empty batch: no-op
+    # attention: null output, workspace too small or misaligned
+    args = [ctypes.byref(cfg), 4, P(fake), P(fake), P(fake), P(fake), P(fake), 100, P(fake),
+            P(fake), P(fake)]
+    assert lib.dflash_block_attn(*args, None, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_block_attn(*args, P(fake), P(fake), 16, None) == d.DFLASH_ERR_WORKSPACE
+    assert lib.dflash_block_attn(*args, P(fake), P(fake + 16), 1 << 40, None) == d.DFLASH_ERR_WORKSPACE
+    assert lib.dflash_block_attn(*args, P(fake), None, 1 << 40, None) == d.DFLASH_ERR_WORKSPACE
+    misaligned = [ctypes.byref(cfg), 4, P(fake), P(fake), P(fake), P(fake + 2), P(fake), 100,
+                  P(fake), P(fake), P(fake)]
+    assert lib.dflash_block_attn(*misaligned, P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    # ctx projection: rows past the cache, bad strides
+    lw = (d.DFlashLayerWeights * 1)()
+    for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
+        setattr(lw[0], f, fake)
+    ptrs = (ctypes.c_void_p * 1)(fake)
+    assert lib.dflash_ctx_proj(ctypes.byref(cfg), P(fake), 20480, 4096, 100, P(fake), P(fake), lw,
+                               ptrs, ptrs, 50, 0, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_proj(ctypes.byref(cfg), P(fake), 20481, 4096, 10, P(fake), P(fake), lw,
+                               ptrs, ptrs, 50, 0, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_proj(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), P(fake), lw,
+                               ptrs, ptrs, 50, 0, P(fake), 1024, None) == d.DFLASH_ERR_WORKSPACE
+    # body: a null weight
+    lw[0].w_up = None
+    assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
+                                   P(fake), P(fake), P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    # unsupported config is reported before anything else
+    bad = d.config_from_workload(scaled(WORKLOADS["c2"], head_dim=64))
+    assert lib.dflash_body_forward(ctypes.byref(bad), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
+                                   P(fake), P(fake), P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_UNSUPPORTED
+
+
+def test_product_path_does_not_reach_the_oracle():
+    pkg = os.path.join(ROOT, "block_draft_model_build_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
