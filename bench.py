@@ -1,0 +1,325 @@
+"""Benchmark of the DFlash draft-body forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+  training-shaped workloads: anchor plan -> context projection (W_proj and every
+  layer's context K/V) -> draft body (all layers);
+  inference-shaped workload (ragged prefixes, cached context K/V): draft body.
+
+Prints one JSON line. `value` is block positions per second (every block slot
+counted). The roofline object describes the kernel with the largest share of
+the step time, timed live with HIP events recorded by the library around each
+of its launches on the launch stream; the cpu_baseline object is the fp64
+oracle timed on this host on a bounded sample of the same workload.
+
+    python bench.py [--workload c3] [--steps 10] [--warmup 3] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft block-positions/sec for 5-layer DFlash body forward; % bf16 MFMA / HBM roofline"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # dense MI355X matrix peaks
+PEAK_HBM_GBS = 8000.0
+
+DESCR = {
+    "c1": "tiny fp32 single-layer body: batch 1, target seq 128, 2x256 target layers -> 256, 4/2 heads x 64, block 8, 4 anchors",
+    "c2": "one draft layer, bf16: batch 4, target seq 2048, 5x4096 target layers -> 4096, 32/8 heads x 128, block 16, 16 anchors/row",
+    "c3": "full 5-layer draft body, bf16: batch 8, target seq 4096, 5x4096 target layers -> 4096, 32/8 heads x 128, SwiGLU 12288, block 16, 32 anchors/row",
+    "c4": "long-context 5-layer body, bf16: batch 1, target seq 32768, 512 anchors, block 16",
+    "c5": "inference drafting, bf16: 64 requests, prefixes U{1024..16384} with cached per-layer context K/V, one block of 16 per request, 5 layers",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- GPU runner
+class Runner:
+    def __init__(self, d, w, device="cuda"):
+        import torch
+        from dflash_synth import make_inference_inputs, make_training_inputs
+        self.d, self.w, self.torch = d, w, torch
+        self.cfg = d.config_from_workload(w)
+        bs, H = w.block_size, w.hidden
+        if w.inference:
+            self.inp = make_inference_inputs(w, device)
+            self.T = self.inp["total"]
+            self.base, self.anchor = self.inp["block_ctx_base"], self.inp["block_anchor"]
+            self.valid = self.inp["block_valid"]
+            self.ctx_k, self.ctx_v = self.inp["ctx_k"], self.inp["ctx_v"]
+            ctx_rows = 0
+        else:
+            self.inp = make_training_inputs(w, device)
+            B, S, N = w.batch, w.seq_len, w.anchors_per_row
+            self.T = B * S
+            self.anchors = torch.empty((B, N), dtype=torch.int32, device=device)
+            self.positions = torch.empty((B, N, bs), dtype=torch.int32, device=device)
+            self.valid3 = torch.empty((B, N, bs), dtype=torch.uint8, device=device)
+            self.loss_mask = torch.empty((B, N, bs), dtype=torch.uint8, device=device)
+            self.num = torch.empty((B,), dtype=torch.int32, device=device)
+            self.base = torch.empty((B * N,), dtype=torch.int64, device=device)
+            self.anchor = self.anchors.view(-1)
+            self.valid = self.valid3.view(-1)
+            self.ctx_pos = torch.arange(S, dtype=torch.int32, device=device).repeat(B)
+            self.ctx_k = [torch.empty((w.num_kv_heads, self.T, w.head_dim), dtype=w.torch_dtype, device=device)
+                          for _ in range(w.num_layers)]
+            self.ctx_v = [torch.empty_like(k) for k in self.ctx_k]
+            ctx_rows = self.T
+        self.out = torch.empty((w.num_blocks * bs, H), dtype=w.torch_dtype, device=device)
+        self.ws = torch.empty(d.dflash_workspace_size(self.cfg, w.num_blocks, ctx_rows), dtype=torch.uint8,
+                              device=device)
+
+    def step(self):
+        d, w, i = self.d, self.w, self.inp
+        if not w.inference:
+            d.dflash_build_plan(i["mask"], i["sample_ids"], i["step"], i["plan_seed"], w.anchors_per_row,
+                                w.block_size, self.anchors, self.positions, self.valid3, self.loss_mask,
+                                self.num, self.base)
+            d.dflash_ctx_proj(self.cfg, i["states"], w.target_hidden, self.T * w.target_hidden, self.T,
+                              self.ctx_pos, i["w_proj"], i["layers"], self.ctx_k, self.ctx_v, self.T, 0,
+                              self.ws)
+        d.dflash_body_forward(self.cfg, w.num_blocks, i["emb"], i["layers"], self.ctx_k, self.ctx_v, self.T,
+                              self.base, self.anchor, self.valid, self.out, self.ws)
+
+    def anchors_np(self):
+        return self.anchor.cpu().numpy().astype("int64")
+
+
+# ----------------------------------------------------------------------------- algorithmic counts
+def kernel_counts(w, anchors):
+    """Algorithmic flops and HBM bytes per launch, and launches per step, for each
+    kernel. GEMMs: 2*M*N*K flops, each operand read once and the output written
+    once. Attention: 4*D flops per (query head, block row, visible key); bytes
+    under the per-block stream model: every (block, KV head) reads the K and V
+    rows of its visible keys (prefix + block) once, plus q in and out."""
+    import numpy as np
+    eb = 4 if w.dtype == "f32" else 2
+    bs, H, D, I = w.block_size, w.hidden, w.head_dim, w.intermediate
+    Hq, Hkv, L = w.num_q_heads, w.num_kv_heads, w.num_layers
+    nb = w.num_blocks
+    R = nb * bs
+    a = np.asarray(anchors, np.int64)
+    live = a >= 0
+    keys = (a[live] + bs).astype(np.float64)
+    c = {}
+
+    def gemm(name, M, N, K, extra_bytes=0.0, launches=1):
+        c[name] = dict(flops=2.0 * M * N * K, bytes=float(eb * (M * K + N * K + M * N) + extra_bytes),
+                       launches=launches, bound="mfma")
+
+    if not w.inference:
+        T = w.batch * w.seq_len
+        Kt = w.num_target_layers * w.target_hidden
+        gemm("ctx_proj", T, H, Kt)
+        gemm("ctx_kv", T, L * 2 * Hkv * D, H)
+    gemm("qkv", R, (Hq + 2 * Hkv) * D, H, launches=L)
+    gemm("o_proj", R, H, Hq * D, extra_bytes=R * H * (8 - eb), launches=L)
+    gemm("gate_up", R, 2 * I, H, extra_bytes=-R * I * eb, launches=L)
+    gemm("down", R, H, I, extra_bytes=R * H * (8 - eb), launches=L)
+    c["attention"] = dict(flops=float(4.0 * D * Hq * bs * keys.sum()),
+                          bytes=float(Hkv * keys.sum() * 2 * D * eb + 2 * R * Hq * D * eb),
+                          launches=L, bound="hbm")
+    c["rmsnorm"] = dict(flops=float(3.0 * R * H), bytes=float(R * H * (4 + eb)), launches=2 * L, bound="hbm")
+    return c
+
+
+def roofline_entry(name, cnt, avg_ms, dtype):
+    t = avg_ms / 1e3
+    if cnt["bound"] == "mfma":
+        ach = cnt["flops"] / t / 1e12
+        peak = PEAK_MFMA_TFLOPS[dtype]
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
+    ach = cnt["bytes"] / t / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4)}
+
+
+def step_roofline_ms(counts, dtype):
+    tot = 0.0
+    for cnt in counts.values():
+        f = cnt["flops"] / (PEAK_MFMA_TFLOPS[dtype] * 1e12)
+        b = cnt["bytes"] / (PEAK_HBM_GBS * 1e9)
+        tot += max(f, b) * cnt["launches"]
+    return tot * 1e3
+
+
+# ----------------------------------------------------------------------------- CPU oracle sample
+def cpu_baseline(w, runner, anchors, budget_rows=None, budget_blocks=None):
+    """The fp64 oracle on a bounded sample of the workload, scaled to block positions/s.
+
+    Training-shaped: the context projection of `rows` target rows and the body of
+    `blocks` blocks (evenly spaced over the plan's anchors, each with its full
+    prefix of context K/V), extrapolated to the step's rows and blocks.
+    Inference-shaped: the body of `blocks` requests over their cached context."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def np64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    inp = runner.inp
+    cfg = dict(block_size=w.block_size, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+               head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps)
+    layers = [{k: np64(v) for k, v in L.items()} for L in inp["layers"]]
+    bs = w.block_size
+    t_ctx = 0.0
+    sample = {}
+    if w.inference:
+        nblk = budget_blocks or 4
+        lens = inp["lengths"].cpu().numpy()
+        offs = inp["offsets"].cpu().numpy()
+        pick = np.linspace(0, w.batch - 1, nblk).round().astype(int)
+        data = []
+        for r in pick:
+            lo, hi = int(offs[r]), int(offs[r + 1])
+            data.append((np64(inp["emb"][r * bs:(r + 1) * bs]), [np64(k[:, lo:hi]) for k in inp["ctx_k"]],
+                         [np64(v[:, lo:hi]) for v in inp["ctx_v"]], int(lens[r])))
+        t0 = time.perf_counter()
+        for e, ck, cv, a in data:
+            oracle.body_forward(e, layers, ck, cv, [0], [a], np.ones(bs, np.uint8), cfg)
+        t_body = time.perf_counter() - t0
+        t_est = t_body * w.num_blocks / nblk
+        sample["what"] = f"body of {nblk} of {w.num_blocks} requests (prefixes {sorted(int(lens[r]) for r in pick)})"
+    else:
+        rows = budget_rows or 1024
+        nblk = budget_blocks or 4
+        w_proj = np64(inp["w_proj"])
+        states = np64(inp["states"][:, :rows])
+        t0 = time.perf_counter()
+        C = oracle.ctx_proj(oracle.concat_target_states(states), w_proj)
+        oracle.ctx_kv(C, layers, np.arange(rows) % w.seq_len, w.num_kv_heads, w.head_dim, w.rope_theta)
+        t_ctx = time.perf_counter() - t0
+        order = np.argsort(anchors, kind="stable")
+        pick = order[np.linspace(0, len(order) - 1, nblk).round().astype(int)]
+        gen = np.random.default_rng(0)
+        data = []
+        for n in pick:
+            a = int(anchors[n])
+            ck = [gen.standard_normal((w.num_kv_heads, max(a, 1), w.head_dim)) for _ in range(w.num_layers)]
+            cv = [gen.standard_normal((w.num_kv_heads, max(a, 1), w.head_dim)) for _ in range(w.num_layers)]
+            data.append((np64(inp["emb"][n * bs:(n + 1) * bs]), ck, cv, a))
+        t0 = time.perf_counter()
+        for e, ck, cv, a in data:
+            oracle.body_forward(e, layers, ck, cv, [0], [a], np.ones(bs, np.uint8), cfg)
+        t_body = time.perf_counter() - t0
+        T = w.batch * w.seq_len
+        t_est = t_ctx * T / rows + t_body * w.num_blocks / nblk
+        sample["what"] = (f"context projection of {rows} of {T} target rows + body of {nblk} of {w.num_blocks} "
+                          f"blocks (anchors {sorted(int(anchors[n]) for n in pick)}), scaled to the whole step")
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    value = w.num_blocks * bs / t_est
+    return {"value": round(value, 3), "unit": "block-positions/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample["what"], "sample_seconds": round(t_ctx + t_body, 2)}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_draft_model_build_amd as d
+    from dflash_synth import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    log(f"workload {w.name}: building inputs")
+    runner = Runner(d, w)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    anchors = runner.anchors_np()
+    counts = kernel_counts(w, anchors)
+    log(f"warmup done ({args.warmup} steps)")
+
+    # Per-kernel time shares: each kernel in turn, over a couple of steps.
+    per_kernel = {}
+    if not args.no_breakdown:
+        for name in counts:
+            launches = counts[name]["launches"]
+            reps = 2
+            d.dflash_profile_start(name, launches * reps)
+            for _ in range(reps):
+                runner.step()
+            times = d.dflash_profile_stop(launches * reps)
+            if times:
+                per_kernel[name] = sum(times) / reps
+        dominant = max(per_kernel, key=per_kernel.get)
+    else:
+        dominant = "ctx_proj" if not w.inference else "attention"
+    log("kernel ms/step: " + ", ".join(f"{k} {v:.3f}" for k, v in per_kernel.items()))
+
+    # Timed region: K steps, with the dominant kernel's launches bracketed by events.
+    n_dom = counts[dominant]["launches"] * args.steps
+    torch.cuda.synchronize()
+    d.dflash_profile_start(dominant, n_dom)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        runner.step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    dom_times = d.dflash_profile_stop(n_dom)
+    dom_avg = sum(dom_times) / len(dom_times)
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; {dominant} avg {dom_avg:.4f} ms over {len(dom_times)} launches")
+
+    positions = w.num_blocks * w.block_size
+    value = positions / (ms / 1e3)
+    roof = roofline_entry(dominant, counts[dominant], dom_avg, w.dtype)
+    roof["traffic"] = None
+    roof["launches_timed"] = len(dom_times)
+    t_roof = step_roofline_ms(counts, w.dtype)
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "block-positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {DESCR[w.name]}", "num_blocks": w.num_blocks,
+                   "block_size": w.block_size, "layers": w.num_layers, "block_positions": positions},
+        "roofline": roof,
+        "step_roofline": {"roofline_ms": round(t_roof, 4), "frac": round(t_roof / ms, 4),
+                          "flops": sum(c["flops"] * c["launches"] for c in counts.values()),
+                          "model": "sum over kernels of max(flops / MFMA peak, bytes / HBM peak)"},
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a CPU sample")
+        budgets = {"c1": (128, 4), "c2": (1024, 8), "c3": (1024, 6), "c4": (1024, 4), "c5": (None, 4)}
+        r, b = budgets[w.name]
+        result["cpu_baseline"] = cpu_baseline(w, runner, anchors, r, b)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

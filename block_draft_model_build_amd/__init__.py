@@ -25,7 +25,12 @@ DFLASH_OK, DFLASH_ERR_INVALID_ARG, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE,
 DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_block_attn", "dflash_body_forward",
-            "dflash_workspace_size", "dflash_check_config", "dflash_status_string")
+            "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
+            "dflash_profile_start", "dflash_profile_stop")
+
+# dflash_kernel ids for the measurement hook
+KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "attention": 5,
+           "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -70,6 +75,10 @@ def _load() -> ctypes.CDLL:
     lib.dflash_workspace_size.restype = ctypes.c_size_t
     lib.dflash_check_config.argtypes = [CFG]
     lib.dflash_check_config.restype = ctypes.c_int
+    lib.dflash_profile_start.argtypes = [I32, I32]
+    lib.dflash_profile_start.restype = ctypes.c_int
+    lib.dflash_profile_stop.argtypes = [P, P]
+    lib.dflash_profile_stop.restype = ctypes.c_int
     lib.dflash_status_string.argtypes = [ctypes.c_int]
     lib.dflash_status_string.restype = ctypes.c_char_p
     return lib
@@ -204,3 +213,17 @@ def dflash_body_forward(cfg: DFlashConfig, num_blocks: int, block_embeds, layers
                                  int(ctx_total), _ptr(block_ctx_base), _ptr(block_anchor),
                                  _ptr(block_valid), _ptr(out), wp, wb, _stream(stream, block_embeds))
     _check("dflash_body_forward", s)
+
+
+def dflash_profile_start(kernel, max_launches: int) -> None:
+    """Time the next max_launches launches of one kernel (name or dflash_kernel id)."""
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check("dflash_profile_start", _lib.dflash_profile_start(kid, int(max_launches)))
+
+
+def dflash_profile_stop(max_launches: int) -> List[float]:
+    """Per-launch durations in milliseconds of the launches recorded since start."""
+    buf = (ctypes.c_float * int(max_launches))()
+    n = ctypes.c_int32(0)
+    _check("dflash_profile_stop", _lib.dflash_profile_stop(buf, ctypes.byref(n)))
+    return [buf[i] for i in range(n.value)]

@@ -1,6 +1,6 @@
 """Builds libdflash.so in-tree with hipcc for gfx950 (cross-compiles without a GPU).
 
-    python -m block_draft_model_build_amd.build      # or build() from Python
+    python block_draft_model_build_amd/build.py      # or build() from Python
 """
 from __future__ import annotations
 
@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["dflash.hip", "plan.hip"]
+SOURCES = ["dflash.hip", "plan.hip", "profile.hip"]
 ARCH = "gfx950"
 
 

@@ -18,7 +18,8 @@ using MidTile = TileCfg<128, 128, 4, 1>;
 static_assert(BigTile::WN == 128 && MidTile::WN == 128, "gate/up interleave and RoPE pairing assume WN = 128");
 
 template <typename T, class AL, class BL, class EP>
-static hipError_t gemm(int M, int N, int K, const AL& al, const BL& bl, const EP& ep, hipStream_t st) {
+static hipError_t gemm(int kid, int M, int N, int K, const AL& al, const BL& bl, const EP& ep, hipStream_t st) {
+    ProfScope prof(kid, st);
     if (M >= 2048 && N % 256 == 0) return launch_gemm<T, BigTile>(M, N, K, al, bl, ep, st);
     return launch_gemm<T, MidTile>(M, N, K, al, bl, ep, st);
 }
@@ -54,10 +55,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in
 template <typename T, int D, int QC>
 static hipError_t attn_launch_t(const dflash_config& c, const AttnArgs<T>& a, int nb, hipStream_t st) {
     const int items_max = c.num_kv_heads * (attn_target_splits(c, nb) + nb);
-    hipLaunchKernelGGL((block_attn_kernel<T, D, QC>), dim3(items_max), dim3(256), 0, st, a);
+    {
+        ProfScope prof(DFLASH_KERNEL_ATTENTION, st);
+        hipLaunchKernelGGL((block_attn_kernel<T, D, QC>), dim3(items_max), dim3(256), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, QC>), dim3(nb, c.num_kv_heads), dim3(256), 0, st, a);
+    {
+        ProfScope prof(DFLASH_KERNEL_ATTN_COMBINE, st);
+        hipLaunchKernelGGL((attn_combine_kernel<T, D, QC>), dim3(nb, c.num_kv_heads), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -106,7 +113,7 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     T* C = reinterpret_cast<T*>(ws + w.c);
     const int H = c.hidden, K = c.num_target_layers * c.target_hidden;
     const int M = (int)rows;
-    hipError_t e = gemm<T>(M, H, K, AStacked<T>{ts, rs, ls, c.target_hidden}, BPlain<T>{w_proj, K},
+    hipError_t e = gemm<T>(DFLASH_KERNEL_CTX_PROJ, M, H, K, AStacked<T>{ts, rs, ls, c.target_hidden}, BPlain<T>{w_proj, K},
                            EpStore<T>{C, H}, st);
     if (e != hipSuccess) return e;
     BCtxKV<T> b{};
@@ -126,6 +133,7 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     ep.rt = make_rope_turns(c);
     const int N = c.num_layers * 2 * c.num_kv_heads * c.head_dim;
     // The RoPE epilogue needs registers the 256x256 tile does not have left.
+    ProfScope prof(DFLASH_KERNEL_CTX_KV, st);
     return launch_gemm<T, MidTile>(M, N, H, APlain<T>{C, H}, b, ep, st);
 }
 
@@ -145,14 +153,17 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
     if (e != hipSuccess) return e;
     for (int l = 0; l < c.num_layers; ++l) {
         const dflash_layer_weights& L = layers[l];
-        if (l == 0)
-            hipLaunchKernelGGL((rmsnorm_kernel<T, T>), dim3(R), dim3(256), 0, st, emb, h,
-                               static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
-        else
-            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
-                               static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
+        {
+            ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
+            if (l == 0)
+                hipLaunchKernelGGL((rmsnorm_kernel<T, T>), dim3(R), dim3(256), 0, st, emb, h,
+                                   static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
+            else
+                hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
+                                   static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = gemm<T>(R, nqkv, H, APlain<T>{x, H},
+        e = gemm<T>(DFLASH_KERNEL_QKV, R, nqkv, H, APlain<T>{x, H},
                     BQKV<T>{static_cast<const T*>(L.wq), static_cast<const T*>(L.wk),
                             static_cast<const T*>(L.wv), nq, nk, H},
                     EpStore<T>{qkv, nqkv}, st);
@@ -161,18 +172,21 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
                                      static_cast<const T*>(ck[l]), static_cast<const T*>(cv[l]), ctx_total,
                                      base, anchor, valid, att, nq, ws, w);
         if ((e = attn_launch<T>(c, a, nb, st)) != hipSuccess) return e;
-        e = gemm<T>(R, H, nq, APlain<T>{att, nq}, BPlain<T>{static_cast<const T*>(L.wo), nq},
+        e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq}, BPlain<T>{static_cast<const T*>(L.wo), nq},
                     EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0}, st);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
-                           static_cast<const T*>(L.mlp_norm), x, H, c.rms_eps);
+        {
+            ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
+            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
+                               static_cast<const T*>(L.mlp_norm), x, H, c.rms_eps);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = gemm<T>(R, 2 * I, H, APlain<T>{x, H},
+        e = gemm<T>(DFLASH_KERNEL_GATE_UP, R, 2 * I, H, APlain<T>{x, H},
                     BGateUp<T, 128>{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), H},
                     EpSwiGLU<T>{u, I}, st);
         if (e != hipSuccess) return e;
         const bool last = l + 1 == c.num_layers;
-        e = gemm<T>(R, H, I, APlain<T>{u, I}, BPlain<T>{static_cast<const T*>(L.w_down), I},
+        e = gemm<T>(DFLASH_KERNEL_DOWN, R, H, I, APlain<T>{u, I}, BPlain<T>{static_cast<const T*>(L.w_down), I},
                     EpResidual<T>{h, H, last ? out : nullptr, valid, anchor, c.block_size}, st);
         if (e != hipSuccess) return e;
     }

@@ -68,4 +68,18 @@ inline RopeTurns make_rope_turns(const dflash_config& c) {
 
 dflash_status check_config(const dflash_config* c);
 
+// Records the measurement hook's events around the launches made in its scope
+// when `kernel` is the kernel being profiled (dflash_profile_start).
+class ProfScope {
+  public:
+    ProfScope(int kernel, hipStream_t st);
+    ~ProfScope();
+    ProfScope(const ProfScope&) = delete;
+    ProfScope& operator=(const ProfScope&) = delete;
+
+  private:
+    hipStream_t stream_;
+    int slot_;
+};
+
 }  // namespace dflash

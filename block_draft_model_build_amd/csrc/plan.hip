@@ -177,6 +177,7 @@ extern "C" dflash_status dflash_build_plan(const uint8_t* mask, int32_t batch, i
         (anchors == nullptr || positions == nullptr || valid == nullptr || loss_mask == nullptr))
         return DFLASH_ERR_INVALID_ARG;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    ProfScope prof(DFLASH_KERNEL_PLAN, st);
     hipLaunchKernelGGL(plan_kernel, dim3(batch), dim3(kPlanThreads), 0, st, mask, seq_len, sample_ids,
                        (uint64_t)step, seed, anchors_per_row, block_size, anchors, positions, valid,
                        loss_mask, num_anchors, block_ctx_base);

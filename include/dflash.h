@@ -21,14 +21,19 @@
  *   - dtype DFLASH_BF16: every tensor argument (activations, weights, caches and
  *     outputs) is bfloat16; arithmetic accumulates in fp32 and the residual
  *     stream of the body is fp32. dtype DFLASH_F32: every tensor is fp32.
- *   - Shape envelope (DFLASH_ERR_UNSUPPORTED outside it): head_dim 64 or 128;
- *     num_q_heads a multiple of num_kv_heads; block_size * (num_q_heads /
- *     num_kv_heads) <= 64; hidden, intermediate and num_q_heads*head_dim
- *     multiples of 256 (bf16) / 128 (fp32)... see dflash_check_config; target
- *     hidden a multiple of 64 elements (bf16) or 32 (fp32); num_layers <= 16.
- *   - Calls on one stream are ordered; the library keeps no state between calls
- *     and is safe to call from several threads on different streams with
- *     different workspaces.
+ *   - Shape envelope (DFLASH_ERR_UNSUPPORTED outside it; dflash_check_config tests
+ *     it): one head row is 256 bytes (head_dim 128 in bf16, 64 in fp32);
+ *     block_size * (num_q_heads / num_kv_heads) <= 64; hidden a multiple of 128;
+ *     intermediate a multiple of 64; (num_q_heads + 2*num_kv_heads)*head_dim a
+ *     multiple of 128; target_hidden a multiple of 64 (bf16) or 32 (fp32);
+ *     num_layers <= 16. num_q_heads must be a multiple of num_kv_heads
+ *     (DFLASH_ERR_INVALID_ARG otherwise).
+ *   - Every device pointer to a tensor must be 16-byte aligned; the workspace
+ *     256-byte aligned.
+ *   - Calls on one stream are ordered. Apart from the measurement hook
+ *     (dflash_profile_start/stop) the library keeps no state between calls and
+ *     may be called from several threads on different streams with different
+ *     workspaces.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -131,7 +136,7 @@ dflash_status dflash_build_plan(const uint8_t *mask, int32_t batch, int32_t seq_
  *                  layer stride H_t) and per-layer slabs [L_t, rows, H_t] (row stride
  *                  H_t, layer stride rows*H_t) are read in place. Strides are in
  *                  elements and must be multiples of 8 (bf16) / 4 (fp32).
- *   positions      device i32 [num_rows]: RoPE position of each row, in [0, ctx_total).
+ *   positions      device i32 [num_rows]: RoPE position of each row.
  *   w_proj         device [H, L_t*H_t]
  *   layers         host array [num_layers]; only wk and wv are read.
  *   ctx_k, ctx_v   host arrays [num_layers] of device caches [Hkv][ctx_total][D]
@@ -206,6 +211,35 @@ dflash_status dflash_body_forward(const dflash_config *cfg, int32_t num_blocks,
                                   const int64_t *block_ctx_base, const int32_t *block_anchor,
                                   const uint8_t *block_valid, void *out, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
+
+/* Kernels that dflash_profile_start can time. */
+typedef enum dflash_kernel {
+    DFLASH_KERNEL_PLAN = 0,          /* anchor plan */
+    DFLASH_KERNEL_CTX_PROJ = 1,      /* GEMM C = X W_proj^T */
+    DFLASH_KERNEL_CTX_KV = 2,        /* GEMM of every layer's context K/V (RoPE, scatter) */
+    DFLASH_KERNEL_RMSNORM = 3,
+    DFLASH_KERNEL_QKV = 4,           /* GEMM x [Wq;Wk;Wv]^T */
+    DFLASH_KERNEL_ATTENTION = 5,     /* dual-source block attention (per split) */
+    DFLASH_KERNEL_ATTN_COMBINE = 6,  /* merge of split prefixes */
+    DFLASH_KERNEL_O_PROJ = 7,        /* GEMM + residual */
+    DFLASH_KERNEL_GATE_UP = 8,       /* GEMM + SiLU(gate) * up */
+    DFLASH_KERNEL_DOWN = 9,          /* GEMM + residual (+ masked output on the last layer) */
+    DFLASH_KERNEL_COUNT = 10
+} dflash_kernel;
+
+/*
+ * Measurement hook (for benchmarks). dflash_profile_start makes the library
+ * bracket each of the next max_launches launches of `kernel` with a pair of
+ * hipEvents recorded on the launch's stream (events created here, on the
+ * current device). dflash_profile_stop waits for those events, writes each
+ * launch's duration in milliseconds to elapsed_ms[0 .. *launches-1] (host array
+ * of max_launches floats) and uninstalls the hook. Process-wide and not
+ * thread-safe: install it only around single-threaded measurement.
+ * Errors: INVALID_ARG for an unknown kernel or max_launches < 1, or a stop without
+ * a start; HIP when creating, recording or reading events fails.
+ */
+dflash_status dflash_profile_start(int32_t kernel, int32_t max_launches);
+dflash_status dflash_profile_stop(float *elapsed_ms, int32_t *launches);
 
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one
