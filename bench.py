@@ -73,7 +73,8 @@ class Runner:
             self.ctx_pos = torch.arange(S, dtype=torch.int32, device=device).repeat(B)
             self.ctx_k = [torch.empty((w.num_kv_heads, self.T, w.head_dim), dtype=w.torch_dtype, device=device)
                           for _ in range(w.num_layers)]
-            self.ctx_v = [torch.empty_like(k) for k in self.ctx_k]
+            self.ctx_v = [torch.empty((w.num_kv_heads, w.head_dim, self.T), dtype=w.torch_dtype, device=device)
+                          for _ in range(w.num_layers)]
             ctx_rows = self.T
         self.out = torch.empty((w.num_blocks * bs, H), dtype=w.torch_dtype, device=device)
         self.ws = torch.empty(d.dflash_workspace_size(self.cfg, w.num_blocks, ctx_rows), dtype=torch.uint8,
@@ -185,7 +186,7 @@ def cpu_baseline(w, runner, anchors, budget_rows=None, budget_blocks=None):
         for r in pick:
             lo, hi = int(offs[r]), int(offs[r + 1])
             data.append((np64(inp["emb"][r * bs:(r + 1) * bs]), [np64(k[:, lo:hi]) for k in inp["ctx_k"]],
-                         [np64(v[:, lo:hi]) for v in inp["ctx_v"]], int(lens[r])))
+                         [np64(v[:, :, lo:hi]).transpose(0, 2, 1) for v in inp["ctx_v"]], int(lens[r])))
         t0 = time.perf_counter()
         for e, ck, cv, a in data:
             oracle.body_forward(e, layers, ck, cv, [0], [a], np.ones(bs, np.uint8), cfg)

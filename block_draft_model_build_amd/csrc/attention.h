@@ -1,52 +1,69 @@
 // Dual-source block attention for gfx950.
 //
-// Work unit ("item"): one block n, one KV head g and one split s of the block's
-// prefix. Its 64 (or 32) query columns are the block's bs positions times the
-// G = Hq/Hkv query heads that share KV head g, so every K/V byte fetched serves
-// all G heads. Keys are the prefix rows [s*chunk, min(a, (s+1)*chunk)) of the
-// projected context plus, for split 0, the block's own bs rows.
+// Work unit ("item"): a group of up to 4 consecutive blocks that read the same
+// sequence (equal context base), one KV head g, and one split s of the group's
+// prefix range. The 4 waves of the workgroup share every K/V tile: with 4
+// blocks in the group each wave serves one block; with fewer, several waves
+// serve one block and divide its keys. A block's query columns are its bs
+// positions times the G = Hq/Hkv query heads of KV head g (<= 64 columns), so a
+// K/V byte fetched once serves every query head of the group.
 //
-// Layout of the math (keys on MFMA rows, queries on MFMA columns):
-//   S^T[key, q] = K[key, :] . Q[q, :]        A = K tile from LDS, B = Q in registers
-//   O^T[d, q]  += V^T[d, key] . P^T[key, q]  A = V^T tile from LDS, B = P in registers
-// Each lane owns one query column, so the row max / row sum of the online
-// softmax are in-lane reductions plus one exchange between the two lane halves,
-// and P goes from the S^T accumulators straight into the B operand of the P.V
-// product without any shuffle: the 8 (bf16) keys a lane holds for one 16-deep
-// MFMA step are matched by reading the same 8 keys of V^T.
+// Keys are the prefix rows [s*chunk, min(a, (s+1)*chunk)) of the projected
+// context plus, for split 0, the block's own bs rows.
 //
-// A workgroup is 4 waves. Per 128-key super-tile, the K rows and the
-// transposed V rows are staged in LDS (next super-tile prefetched into
-// registers meanwhile); wave w consumes keys [32w, 32w+32). The 4 waves' partial
-// softmax states are merged through LDS at the end. When a block's prefix is
-// split over several items, each item writes its partial (max, sum, O) and a
-// combine kernel merges the splits in split order, so results do not depend on
-// timing.
+// Math layout (keys on MFMA rows, queries on MFMA columns):
+//   S^T[key, q] = K[key, :] . Q[q, :]        A = K rows from LDS, B = Q in registers
+//   O^T[d, q]  += V^T[d, key] . P^T[key, q]  A = V^T rows from LDS, B = P in registers
+// Each lane owns one query column: the online-softmax max and sum are in-lane
+// reductions plus one exchange between the two lane halves, and P goes from the
+// S^T accumulators straight into the B operand of the P.V product. The K rows
+// are fed to the S^T product in a permuted order (bits 2 and 3 of the row
+// index swapped inside each 16-row group) so that the 8 P values a lane holds
+// for one 16-key MFMA step belong to 8 consecutive keys; the matching V^T
+// operand is then one 16-byte LDS read. The context V cache is stored
+// transposed ([Hkv][D][T]) so V^T tiles are staged into LDS by plain copies.
+//
+// Per 128-key super-tile the K rows and V^T columns go HBM -> registers -> LDS
+// with two LDS stages and one register stage (two tiles in flight, one barrier
+// per tile). Waves serving the same block merge their softmax states through
+// LDS at the end. When a group's prefix is split over several items, each item
+// writes per-block partial (max, sum, O) and a combine kernel merges the splits
+// in split order, so results do not depend on timing.
 #pragma once
 
 #include "common.h"
 
 namespace dflash {
 
+constexpr int kMaxGroup = 4;
+
 template <typename T> struct AttnArgs {
     const T* q; int64_t q_ld;          // [nb*bs, *] rows; head h at column h*D
     const T* kb; const T* vb; int64_t kv_ld;
-    const T* ck; const T* cv; int64_t ctx_total;
+    const T* ck;                       // [Hkv][ctx_total][D], rotated
+    const T* cvt;                      // [Hkv][D][ctx_total]
+    int64_t ctx_total;
     const int64_t* base; const int32_t* anchor; const uint8_t* valid;
     T* out; int64_t out_ld;
     int nb, bs, hq, hkv;
     float qscale;                      // log2(e) / sqrt(D)
-    const int* item_start;             // [nb + 1] prefix sums of splits per block
-    const int* chunk;                  // keys per split
-    float* part_o;                     // [items][QC][D]
-    float* part_ml;                    // [items][QC][2]
+    const int* group_start;            // [groups + 1]
+    const int* item_start;             // [groups + 1] prefix sums of splits per group
+    const int* sched;                  // [0] keys per split, [1] number of groups
+    float* part_o;                     // [items][kMaxGroup][QC][D]
+    float* part_ml;                    // [items][kMaxGroup][QC][2]
     RopeTurns rt;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Key fed to MFMA row r of a 32-key slice.
+__device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-__device__ __forceinline__ float xor32(float v) {
-    return __shfl_xor(v, 32, 64);
+__device__ __forceinline__ int64_t clamp_base(int64_t b, int64_t total) { return b < 0 ? 0 : (b > total ? total : b); }
+__device__ __forceinline__ int anchor_eff(int a, int64_t base, int64_t total) {
+    if (a < 0) return -1;
+    return (int64_t)a > total - base ? (int)(total - base) : a;
 }
 
 template <typename T, int D, int QC>
@@ -54,24 +71,26 @@ struct AttnTile {
     static constexpr int EB = (int)sizeof(T);
     static constexpr int KSTEP = Mfma<T>::KSTEP, E = Mfma<T>::E;
     static constexpr int QS = QC / 32, DS = D / 32, DK = D / KSTEP, PK = 32 / KSTEP;
-    static constexpr int KROW = D * EB + 16;          // bytes per K row in LDS
     static constexpr int SUPER = 128;                 // keys per super-tile
-    static constexpr int VROW = SUPER * EB + 16;      // bytes per V^T row (prefix)
-    static constexpr int BVROW = 32 * EB + 16;        // bytes per V^T row (block keys)
+    static constexpr int KROW = D * EB + 16;          // bytes per K row in LDS
+    static constexpr int VROW = SUPER * EB + 16;      // bytes per V^T row in LDS
     static constexpr int KS_BYTES = SUPER * KROW;
     static constexpr int VT_BYTES = D * VROW;
-    static constexpr int KB_BYTES = 32 * KROW;
-    static constexpr int VB_BYTES = D * BVROW;
-    static constexpr int MERGE_BYTES = 2 * (DS * QS * 16 * 64 * 4) + 4 * 2 * QS * 64 * 4;
-    static constexpr int MAIN_BYTES = KS_BYTES + VT_BYTES;
-    static constexpr int LDS_BYTES = (MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES) + KB_BYTES + VB_BYTES;
-    static constexpr int ROW_CHUNKS = D * EB / 16;    // 16-byte chunks per K/V row (16)
-    static_assert(ROW_CHUNKS == 16, "a K/V row is 256 bytes");
+    static constexpr int STAGE = KS_BYTES + VT_BYTES;
+    static constexpr int SLOT_FLOATS = DS * QS * 16 * 64;
+    static constexpr int MERGE_BYTES = 2 * SLOT_FLOATS * 4 + 2 * 2 * QS * 64 * 4;
+    static constexpr int LDS_BYTES = 2 * STAGE > MERGE_BYTES ? 2 * STAGE : MERGE_BYTES;
     static constexpr int EC = 16 / EB;                // elements per 16-byte chunk
+    static constexpr int KCH = D * EB / 16;           // 16-byte chunks per K row
+    static constexpr int VCH = SUPER * EB / 16;       // 16-byte chunks per V^T row
+    static_assert(KCH == 16, "a K row is 256 bytes");
+    static_assert((SUPER * KCH) % 256 == 0 && (D * VCH) % 256 == 0, "whole chunks per thread");
+    static constexpr int KLD = SUPER * KCH / 256;     // K chunks per thread per super-tile
+    static constexpr int VLD = D * VCH / 256;         // V^T chunks per thread per super-tile
 };
 
-// One wave: fold a 32-key slice (K rows at ks, V^T at vt with row pitch vrow)
-// with `nvalid` visible keys into the running softmax state.
+// One wave folds a 32-key slice (K rows at ks, V^T at vt, row pitch vrow)
+// with `nvalid` visible keys into its running softmax state.
 template <typename T, int D, int QC>
 __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int vrow, int nvalid,
                                            const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
@@ -86,7 +105,7 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
     for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[qs][e] = 0.f;
-    const char* krow = ks + (lane & 31) * TT::KROW + h * E * EB;
+    const char* krow = ks + key_perm(lane & 31) * TT::KROW + h * E * EB;
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
         frag a = *reinterpret_cast<const frag*>(krow + kk * TT::KSTEP * EB);
@@ -97,11 +116,13 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
         float mx = NEG_INF;
+        if (nvalid < 32) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if (acc_row(e, lane) >= nvalid) s[qs][e] = NEG_INF;
-            mx = fmaxf(mx, s[qs][e]);
+            for (int e = 0; e < 16; ++e)
+                if (key_perm(acc_row(e, lane)) >= nvalid) s[qs][e] = NEG_INF;
         }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qs][e]);
         mx = fmaxf(mx, xor32(mx));
         const float mnew = fmaxf(m[qs], mx);
         const float muse = (mnew == NEG_INF) ? 0.f : mnew;
@@ -134,15 +155,19 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
         }
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-            frag a;
             const char* vr = vbase + ds * 32 * vrow;
+            frag a;
             if constexpr (E == 8) {
-                u32x2 lo = *reinterpret_cast<const u32x2*>(vr + (16 * st + 4 * h) * EB);
-                u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (16 * st + 8 + 4 * h) * EB);
-                u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
-                a = __builtin_bit_cast(frag, both);
+                a = *reinterpret_cast<const frag*>(vr + (16 * st + 8 * h) * EB);
+                if (nvalid < 32) {          // keys past this block's end: exact zeros, even if V is not finite
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (16 * st + 8 * h + i >= nvalid) a[i] = from_f32<T>(0.f);
+                }
             } else {
-                a = *reinterpret_cast<const T*>(vr + acc_row(st, lane) * EB);
+                const int key = key_perm(acc_row(st, lane));
+                a = *reinterpret_cast<const T*>(vr + key * EB);
+                if (key >= nvalid) a = 0.f;
             }
 #pragma unroll
             for (int qs = 0; qs < QS; ++qs) o[ds][qs] = Mfma<T>::mma(a, pf[qs], o[ds][qs]);
@@ -157,79 +182,81 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     constexpr int QS = TT::QS, DS = TT::DS, DK = TT::DK, E = TT::E, EB = TT::EB, EC = TT::EC;
     constexpr int KSTEP = TT::KSTEP, SUPER = TT::SUPER;
     __shared__ __attribute__((aligned(16))) char smem[TT::LDS_BYTES];
-    char* Ks = smem;
-    char* Vt = smem + TT::KS_BYTES;
-    char* Kb = smem + (TT::LDS_BYTES - TT::KB_BYTES - TT::VB_BYTES);
-    char* Vbt = Kb + TT::KB_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     const int hkv = p.hkv, bs = p.bs, G = p.hq / p.hkv;
-    const int total = p.item_start[p.nb] * hkv;
-    const int item = blockIdx.x;
-    if (item >= total) return;
+    const int ngroups = p.sched[1];
+    const int total = p.item_start[ngroups] * hkv;
+    if ((int)blockIdx.x >= total) return;
+    // Items are dispatched last-first: groups come in ascending anchor order,
+    // so the longest prefixes start first and the short ones fill the tail.
+    const int item = total - 1 - (int)blockIdx.x;
     const int sg = item / hkv, g = item - sg * hkv;
-    int lo = 0, hi = p.nb;
+    int lo = 0, hi = ngroups;
     while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
         if (p.item_start[mid] <= sg) lo = mid; else hi = mid;
     }
-    const int n = lo;
-    const int s = sg - p.item_start[n];
-    const int nsplit = p.item_start[n + 1] - p.item_start[n];
+    const int gi = lo;
+    const int s = sg - p.item_start[gi];
+    const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
+    const int n0 = p.group_start[gi];
+    const int ng = p.group_start[gi + 1] - n0;
+    const int wpb = ng == 1 ? 4 : (ng == 2 ? 2 : 1);   // waves per block
+    const int j = wave / wpb;                          // this wave's block in the group
+    const int phase = wave - j * wpb;                  // this wave's share of the block's keys
+    const bool active = j < ng;
     const int qcols = bs * G;
-
-    int64_t base = p.base[n];
-    base = base < 0 ? 0 : (base > p.ctx_total ? p.ctx_total : base);
-    int a = p.anchor[n];
-    if (a < 0) {                                   // empty block: zero rows
-        if (s == 0) {
-            for (int idx = tid; idx < bs * G * D; idx += 256) {
-                int k = idx / (G * D), r = idx - k * G * D;
-                p.out[(int64_t)(n * bs + k) * p.out_ld + (int64_t)g * G * D + r] = from_f32<T>(0.f);
-            }
-        }
-        return;
-    }
-    if ((int64_t)a > p.ctx_total - base) a = (int)(p.ctx_total - base);
-    const int chunk = *p.chunk;
+    const int chunk = p.sched[0];
+    const int64_t base = clamp_base(p.base[n0], p.ctx_total);
     const int kbeg = s * chunk;
+
+    int amax = -1;
+    for (int jj = 0; jj < ng; ++jj) amax = max(amax, anchor_eff(p.anchor[n0 + jj], base, p.ctx_total));
+    const int n = n0 + (active ? j : 0);
+    const int a = active ? anchor_eff(p.anchor[n], base, p.ctx_total) : -1;
+    const int kend_g = min(amax, kbeg + chunk);
     const int kend = min(a, kbeg + chunk);
 
-    // ---- queries: rotate at a + k, scale by log2(e)/sqrt(D), keep as B fragments
+    // ---- queries of this wave's block: rotate at a + k, scale by log2(e)/sqrt(D)
     frag qf[QS][DK];
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
         const int c = qs * 32 + (lane & 31);
-        const bool live = c < qcols;
+        const bool live = a >= 0 && c < qcols;
         const int k = live ? c % bs : 0, hh = live ? c / bs : 0;
         const T* qrow = p.q + (int64_t)(n * bs + k) * p.q_ld + (int64_t)(g * G + hh) * D;
-        const int pos = a + k;
+        const int pos = (a >= 0 ? a : 0) + k;
 #pragma unroll
         for (int kk = 0; kk < DK / 2; ++kk) {
-            float x1[E], x2[E];
             const int d0 = kk * KSTEP + h * E;
+            float x1[E], x2[E];
+            if constexpr (E == 8) {
+                u32x4 r1 = {0, 0, 0, 0}, r2 = {0, 0, 0, 0};
+                if (live) {
+                    r1 = *reinterpret_cast<const u32x4*>(qrow + d0);
+                    r2 = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+                }
+                bf16x8 v1 = __builtin_bit_cast(bf16x8, r1), v2 = __builtin_bit_cast(bf16x8, r2);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                x1[e] = live ? to_f32(qrow[d0 + e]) : 0.f;
-                x2[e] = live ? to_f32(qrow[d0 + D / 2 + e]) : 0.f;
+                for (int e = 0; e < 8; ++e) { x1[e] = to_f32(v1[e]); x2[e] = to_f32(v2[e]); }
+            } else {
+                x1[0] = live ? to_f32(qrow[d0]) : 0.f;
+                x2[0] = live ? to_f32(qrow[d0 + D / 2]) : 0.f;
             }
-            float y1[E], y2[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 float cs, sn;
                 rope_cs(p.rt, d0 + e, pos, cs, sn);
-                y1[e] = (x1[e] * cs - x2[e] * sn) * p.qscale;
-                y2[e] = (x2[e] * cs + x1[e] * sn) * p.qscale;
-            }
-            if constexpr (E == 8) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    qf[qs][kk][e] = from_f32<T>(y1[e]);
-                    qf[qs][kk + DK / 2][e] = from_f32<T>(y2[e]);
+                const float y1 = (x1[e] * cs - x2[e] * sn) * p.qscale;
+                const float y2 = (x2[e] * cs + x1[e] * sn) * p.qscale;
+                if constexpr (E == 8) {
+                    qf[qs][kk][e] = from_f32<T>(y1);
+                    qf[qs][kk + DK / 2][e] = from_f32<T>(y2);
+                } else {
+                    qf[qs][kk] = y1;
+                    qf[qs][kk + DK / 2] = y2;
                 }
-            } else {
-                qf[qs][kk] = y1[0];
-                qf[qs][kk + DK / 2] = y2[0];
             }
         }
     }
@@ -246,136 +273,164 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             for (int e = 0; e < 16; ++e) o[ds][qs][e] = 0.f;
     }
 
-    // ---- the block's own keys (split 0 only): rotate K at a + k', stage K and V^T
+    // ---- split 0: the blocks' own keys. Block jj's rows go to slot jj (32 rows)
+    // of stage 0: K rotated at its anchor + k', V^T transposed; rows >= bs zero.
     if (s == 0) {
-        // K: 32 rows x D (rows >= bs are zero and masked)
-        for (int idx = tid; idx < 32 * (D / 2); idx += 256) {
-            const int k = idx / (D / 2), i = idx - k * (D / 2);
+        char* Ks = smem;
+        char* Vt = smem + TT::KS_BYTES;
+        for (int idx = tid; idx < ng * 32 * (D / 2); idx += 256) {
+            const int jj = idx / (32 * (D / 2)), r = idx - jj * 32 * (D / 2);
+            const int k = r / (D / 2), i = r - k * (D / 2);
+            const int aj = anchor_eff(p.anchor[n0 + jj], base, p.ctx_total);
             float y1 = 0.f, y2 = 0.f;
-            if (k < bs) {
-                const T* kr = p.kb + (int64_t)(n * bs + k) * p.kv_ld + (int64_t)g * D;
-                float x1 = to_f32(kr[i]), x2 = to_f32(kr[i + D / 2]);
+            if (k < bs && aj >= 0) {
+                const T* kr = p.kb + (int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D;
+                const float x1 = to_f32(kr[i]), x2 = to_f32(kr[i + D / 2]);
                 float cs, sn;
-                rope_cs(p.rt, i, a + k, cs, sn);
+                rope_cs(p.rt, i, aj + k, cs, sn);
                 y1 = x1 * cs - x2 * sn;
                 y2 = x2 * cs + x1 * sn;
             }
-            *reinterpret_cast<T*>(Kb + k * TT::KROW + i * EB) = from_f32<T>(y1);
-            *reinterpret_cast<T*>(Kb + k * TT::KROW + (i + D / 2) * EB) = from_f32<T>(y2);
+            char* kd = Ks + (jj * 32 + k) * TT::KROW;
+            *reinterpret_cast<T*>(kd + i * EB) = from_f32<T>(y1);
+            *reinterpret_cast<T*>(kd + (i + D / 2) * EB) = from_f32<T>(y2);
         }
-        for (int idx = tid; idx < 32 * D; idx += 256) {
-            const int k = idx / D, d = idx - k * D;
+        for (int idx = tid; idx < ng * 32 * D; idx += 256) {
+            const int jj = idx / (32 * D), r = idx - jj * 32 * D;
+            const int k = r / D, d = r - k * D;
+            const int aj = p.anchor[n0 + jj];
             T v = from_f32<T>(0.f);
-            if (k < bs) v = p.vb[(int64_t)(n * bs + k) * p.kv_ld + (int64_t)g * D + d];
-            *reinterpret_cast<T*>(Vbt + d * TT::BVROW + k * EB) = v;
+            if (k < bs && aj >= 0) v = p.vb[(int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D + d];
+            *reinterpret_cast<T*>(Vt + d * TT::VROW + (jj * 32 + k) * EB) = v;
         }
         __syncthreads();
-        if (wave == 0) attn_slice<T, D, QC>(Kb, Vbt, TT::BVROW, bs, qf, o, m, l, lane);
+        if (active && phase == 0 && a >= 0)
+            attn_slice<T, D, QC>(Ks + j * 32 * TT::KROW, Vt + j * 32 * EB, TT::VROW, bs, qf, o, m, l, lane);
+        __syncthreads();
     }
 
-    // ---- prefix: 128-key super-tiles, K rows and transposed V staged in LDS
-    const int ntile = kend > kbeg ? (kend - kbeg + SUPER - 1) / SUPER : 0;
-    const T* ckg = p.ck + (int64_t)g * p.ctx_total * D;
-    const T* cvg = p.cv + (int64_t)g * p.ctx_total * D;
-    u32x4 rk[8], rv[8];
+    // ---- prefix super-tiles of the group, staged HBM -> registers -> LDS (2 stages)
+    const int ntile = kend_g > kbeg ? (kend_g - kbeg + SUPER - 1) / SUPER : 0;
+    const T* ckg = p.ck + ((int64_t)g * p.ctx_total + base) * D;
+    const T* cvg = p.cvt + (int64_t)g * D * p.ctx_total + base;
+    u32x4 rk[TT::KLD], rv[TT::VLD];
     auto gload = [&](int t0) {
-        // K: chunk c = tid + 256 i -> key c/16, column chunk c%16
+        // K: chunk c = tid + 256 i -> key c / 16, 16-byte column c % 16
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int key = t0 + (tid >> 4) + 16 * i;
-            key = key < kend ? key : kend - 1;
-            rk[i] = *reinterpret_cast<const u32x4*>(ckg + (base + key) * D + (tid & 15) * EC);
+        for (int i = 0; i < TT::KLD; ++i) {
+            const int c = tid + 256 * i;
+            int key = t0 + c / TT::KCH;
+            key = key < kend_g ? key : kend_g - 1;
+            rk[i] = *reinterpret_cast<const u32x4*>(ckg + (int64_t)key * D + (c % TT::KCH) * EC);
         }
-        // V: two passes of 64 keys; thread owns keys 4*(tid/16)..+3 of a pass, chunk tid%16
+        // V^T: chunk c -> row d = c / VCH, keys t0 + (c % VCH) * EC ..; keys at or past
+        // the group's end are zero (they meet P = 0 and must stay finite).
 #pragma unroll
-        for (int ps = 0; ps < 2; ++ps)
+        for (int i = 0; i < TT::VLD; ++i) {
+            const int c = tid + 256 * i;
+            const int d = c / TT::VCH;
+            const int key = t0 + (c % TT::VCH) * EC;
+            const T* src = cvg + (int64_t)d * p.ctx_total + key;
+            if (key + EC <= kend_g) {
+                rv[i] = *reinterpret_cast<const u32x4*>(src);
+            } else {
+                T tmp[EC];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int key = t0 + ps * 64 + 4 * (tid >> 4) + j;
-                key = key < kend ? key : kend - 1;
-                rv[ps * 4 + j] = *reinterpret_cast<const u32x4*>(cvg + (base + key) * D + (tid & 15) * EC);
+                for (int e = 0; e < EC; ++e) tmp[e] = key + e < kend_g ? src[e] : from_f32<T>(0.f);
+                rv[i] = *reinterpret_cast<const u32x4*>(tmp);
             }
+        }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int stage) {
+        char* Ks = smem + stage * TT::STAGE;
+        char* Vt = Ks + TT::KS_BYTES;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * i) * TT::KROW + (tid & 15) * 16) = rk[i];
+        for (int i = 0; i < TT::KLD; ++i) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<u32x4*>(Ks + (c / TT::KCH) * TT::KROW + (c % TT::KCH) * 16) = rk[i];
+        }
 #pragma unroll
-        for (int ps = 0; ps < 2; ++ps) {
-            const int key0 = ps * 64 + 4 * (tid >> 4);
-            const T* v0 = reinterpret_cast<const T*>(&rv[ps * 4 + 0]);
-            const T* v1 = reinterpret_cast<const T*>(&rv[ps * 4 + 1]);
-            const T* v2 = reinterpret_cast<const T*>(&rv[ps * 4 + 2]);
-            const T* v3 = reinterpret_cast<const T*>(&rv[ps * 4 + 3]);
-#pragma unroll
-            for (int e = 0; e < EC; ++e) {
-                const int d = (tid & 15) * EC + e;
-                T* dst = reinterpret_cast<T*>(Vt + d * TT::VROW + key0 * EB);
-                dst[0] = v0[e]; dst[1] = v1[e]; dst[2] = v2[e]; dst[3] = v3[e];
-            }
+        for (int i = 0; i < TT::VLD; ++i) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<u32x4*>(Vt + (c / TT::VCH) * TT::VROW + (c % TT::VCH) * 16) = rv[i];
         }
     };
 
-    if (ntile > 0) gload(kbeg);
+    if (ntile > 0) {
+        gload(kbeg);
+        lstore(0);
+        if (ntile > 1) gload(kbeg + SUPER);
+    }
     for (int t = 0; t < ntile; ++t) {
         __syncthreads();
-        lstore();
-        __syncthreads();
-        if (t + 1 < ntile) gload(kbeg + (t + 1) * SUPER);
-        const int nvalid = kend - (kbeg + t * SUPER + wave * 32);
-        if (nvalid > 0)
-            attn_slice<T, D, QC>(Ks + wave * 32 * TT::KROW, Vt + wave * 32 * EB, TT::VROW,
-                                 nvalid < 32 ? nvalid : 32, qf, o, m, l, lane);
+        if (t + 1 < ntile) lstore((t + 1) & 1);
+        if (t + 2 < ntile) gload(kbeg + (t + 2) * SUPER);
+        if (active && a >= 0) {
+            const char* Ks = smem + (t & 1) * TT::STAGE;
+            const char* Vt = Ks + TT::KS_BYTES;
+            for (int sl = phase; sl < SUPER / 32; sl += wpb) {
+                const int nvalid = kend - (kbeg + t * SUPER + sl * 32);
+                if (nvalid > 0)
+                    attn_slice<T, D, QC>(Ks + sl * 32 * TT::KROW, Vt + sl * 32 * EB, TT::VROW,
+                                         nvalid < 32 ? nvalid : 32, qf, o, m, l, lane);
+            }
+        }
     }
 
-    // ---- merge the 4 waves: (3 -> 1, 2 -> 0), then (1 -> 0)
+    // ---- merge the waves serving one block (tree over phases), via LDS
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) l[qs] += xor32(l[qs]);
-    float* mo = reinterpret_cast<float*>(smem);                    // [2][DS][QS][16][64]
-    float* mml = mo + 2 * DS * QS * 16 * 64;                       // [2][2][QS][64]
-    auto put = [&](int slot) {
-        float* dst = mo + slot * DS * QS * 16 * 64;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-            for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) dst[((ds * QS + qs) * 16 + e) * 64 + lane] = o[ds][qs][e];
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-            mml[((slot * 2 + 0) * QS + qs) * 64 + lane] = m[qs];
-            mml[((slot * 2 + 1) * QS + qs) * 64 + lane] = l[qs];
-        }
-    };
-    auto take = [&](int slot) {
-        const float* src = mo + slot * DS * QS * 16 * 64;
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs) {
-            const float m2 = mml[((slot * 2 + 0) * QS + qs) * 64 + lane];
-            const float l2 = mml[((slot * 2 + 1) * QS + qs) * 64 + lane];
-            const float mx = fmaxf(m[qs], m2);
-            const float mu = (mx == -__builtin_inff()) ? 0.f : mx;
-            const float f1 = fast_exp2(m[qs] - mu), f2 = fast_exp2(m2 - mu);
-            m[qs] = mx;
-            l[qs] = l[qs] * f1 + l2 * f2;
+    float* mo = reinterpret_cast<float*>(smem);                  // [2 slots][DS][QS][16][64]
+    float* mml = mo + 2 * TT::SLOT_FLOATS;                       // [2 slots][2][QS][64]
+    for (int step = 1; step < 4; step <<= 1) {
+        __syncthreads();
+        if (step < wpb && active && (phase % (2 * step)) == step) {
+            const int slot = wave >> 1;
+            float* dst = mo + slot * TT::SLOT_FLOATS;
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    o[ds][qs][e] = o[ds][qs][e] * f1 + src[((ds * QS + qs) * 16 + e) * 64 + lane] * f2;
+                for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dst[((ds * QS + qs) * 16 + e) * 64 + lane] = o[ds][qs][e];
+#pragma unroll
+            for (int qs = 0; qs < QS; ++qs) {
+                mml[((slot * 2 + 0) * QS + qs) * 64 + lane] = m[qs];
+                mml[((slot * 2 + 1) * QS + qs) * 64 + lane] = l[qs];
+            }
         }
-    };
-    __syncthreads();
-    if (wave >= 2) put(wave - 2);
-    __syncthreads();
-    if (wave < 2) take(wave);
-    __syncthreads();
-    if (wave == 1) put(0);
-    __syncthreads();
-    if (wave != 0) return;
-    take(0);
+        __syncthreads();
+        if (step < wpb && active && (phase % (2 * step)) == 0) {
+            const int slot = (wave + step) >> 1;
+            const float* src = mo + slot * TT::SLOT_FLOATS;
+#pragma unroll
+            for (int qs = 0; qs < QS; ++qs) {
+                const float m2 = mml[((slot * 2 + 0) * QS + qs) * 64 + lane];
+                const float l2 = mml[((slot * 2 + 1) * QS + qs) * 64 + lane];
+                const float mx = fmaxf(m[qs], m2);
+                const float mu = (mx == -__builtin_inff()) ? 0.f : mx;
+                const float f1 = fast_exp2(m[qs] - mu), f2 = fast_exp2(m2 - mu);
+                m[qs] = mx;
+                l[qs] = l[qs] * f1 + l2 * f2;
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        o[ds][qs][e] = o[ds][qs][e] * f1 + src[((ds * QS + qs) * 16 + e) * 64 + lane] * f2;
+            }
+        }
+    }
+    if (!active || phase != 0) return;
 
-    // ---- write: final rows, or this split's partial state
+    // ---- write: final rows of this block, or this split's partial state
+    if (a < 0) {
+        if (s == 0)
+            for (int idx = lane; idx < bs * G * D; idx += 64) {
+                const int k = idx / (G * D), r = idx - k * G * D;
+                p.out[(int64_t)(n * bs + k) * p.out_ld + (int64_t)g * G * D + r] = from_f32<T>(0.f);
+            }
+        return;
+    }
     if (nsplit == 1) {
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
@@ -393,7 +448,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
                     orow[ds * 32 + acc_row(e, lane)] = from_f32<T>(keep ? o[ds][qs][e] * inv : 0.f);
         }
     } else {
-        const int64_t pi = (int64_t)(p.item_start[n] + s) * hkv + g;
+        const int64_t pi = ((int64_t)(p.item_start[gi] + s) * hkv + g) * kMaxGroup + j;
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
             const int c = qs * 32 + (lane & 31);
@@ -410,54 +465,116 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     }
 }
 
-// Merge the splits of every block whose prefix was split, in split order.
+// Merge the splits of every group whose prefix was split, in split order:
+// per query column the global max and 1/sum first, then every output element
+// as one weighted sum over the splits.
 template <typename T, int D, int QC>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
-    const int n = blockIdx.x, g = blockIdx.y;
-    const int nsplit = p.item_start[n + 1] - p.item_start[n];
-    if (nsplit <= 1 || p.anchor[n] < 0) return;
+    constexpr int MAXF = 32;                       // splits whose weights are kept in LDS
+    __shared__ float s_mu[QC], s_inv[QC];
+    __shared__ float s_f[MAXF][QC];
+    const int gi = blockIdx.x, g = blockIdx.y;
+    if (gi >= p.sched[1]) return;
+    const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
+    if (nsplit <= 1) return;
+    const int n0 = p.group_start[gi], ng = p.group_start[gi + 1] - n0;
     const int G = p.hq / p.hkv, bs = p.bs, qcols = bs * G;
-    for (int idx = threadIdx.x; idx < qcols * D; idx += blockDim.x) {
-        const int c = idx / D, d = idx - c * D;
-        float mx = -__builtin_inff();
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t pi = (int64_t)(p.item_start[n] + s) * p.hkv + g;
-            mx = fmaxf(mx, p.part_ml[(pi * QC + c) * 2]);
+    const int tid = threadIdx.x;
+    auto part = [&](int s, int j) -> int64_t {
+        return ((int64_t)(p.item_start[gi] + s) * p.hkv + g) * kMaxGroup + j;
+    };
+    for (int j = 0; j < ng; ++j) {
+        const int n = n0 + j;
+        if (p.anchor[n] < 0) continue;
+        for (int c = tid; c < qcols; c += 256) {
+            float mx = -__builtin_inff();
+            for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.part_ml[(part(s, j) * QC + c) * 2]);
+            const float mu = (mx == -__builtin_inff()) ? 0.f : mx;
+            float L = 0.f;
+            for (int s = 0; s < nsplit; ++s) {
+                const float f = fast_exp2(p.part_ml[(part(s, j) * QC + c) * 2] - mu);
+                if (s < MAXF) s_f[s][c] = f;
+                L += p.part_ml[(part(s, j) * QC + c) * 2 + 1] * f;
+            }
+            s_mu[c] = mu;
+            s_inv[c] = 1.f / L;
         }
-        float L = 0.f, acc = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t pi = (int64_t)(p.item_start[n] + s) * p.hkv + g;
-            const float f = fast_exp2(p.part_ml[(pi * QC + c) * 2] - mx);
-            L += p.part_ml[(pi * QC + c) * 2 + 1] * f;
-            acc += p.part_o[(pi * QC + c) * D + d] * f;
+        __syncthreads();
+        for (int idx = tid; idx < qcols * (D / 4); idx += 256) {
+            const int c = idx / (D / 4), d = (idx - c * (D / 4)) * 4;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < nsplit; ++s) {
+                const float f = s < MAXF ? s_f[s][c] : fast_exp2(p.part_ml[(part(s, j) * QC + c) * 2] - s_mu[c]);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + (part(s, j) * QC + c) * D + d);
+                acc += v * f;
+            }
+            const int k = c % bs, hh = c / bs, row = n * bs + k;
+            const bool keep = p.valid[row] != 0;
+            T* o = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D + d;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(keep ? acc[e] * s_inv[c] : 0.f);
         }
-        const int k = c % bs, hh = c / bs, row = n * bs + k;
-        p.out[(int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D + d] =
-            from_f32<T>(p.valid[row] != 0 ? acc / L : 0.f);
+        __syncthreads();
     }
 }
 
-// Splits per block: chunk = max(512, ceil(sum of prefixes / target) rounded up
-// to a multiple of 128); block n gets max(1, ceil(a_n / chunk)) splits.
-__global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor,
-                                                             int nb, int64_t ctx_total, int target,
-                                                             int* item_start, int* chunk_out) {
-    __shared__ long long red[1024];
+// Groups and splits. A group starts at every block whose index is a multiple
+// of 4 or whose (clamped) context base differs from the previous block's. A
+// group's stream length is its largest (clamped) anchor. chunk = max(256,
+// ceil(sum of group lengths / target) rounded up to 128), so that about
+// target * Hkv items carry the work; a group gets max(1, ceil(length / chunk))
+// splits.
+__global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
+                                                             int64_t ctx_total, int target, int* group_start,
+                                                             int* item_start, int* sched) {
     __shared__ int scan[1024];
-    __shared__ int chunk_s;
+    __shared__ long long red[1024];
+    __shared__ int chunk_s, ngroups_s;
     const int tid = threadIdx.x;
-    auto a_eff = [&](int n) -> int64_t {
-        int64_t b = base[n];
-        b = b < 0 ? 0 : (b > ctx_total ? ctx_total : b);
-        int64_t a = anchor[n];
-        if (a < 0) return -1;
-        return a > ctx_total - b ? ctx_total - b : a;
+    const int per_t = (nb + 1023) / 1024;
+    const int b0 = tid * per_t;
+    auto starts = [&](int n) {
+        return n == 0 || (n & 3) == 0 || clamp_base(base[n], ctx_total) != clamp_base(base[n - 1], ctx_total);
+    };
+    auto block_run = [&](int n) {
+        int64_t b = clamp_base(base[n], ctx_total);
+        return anchor_eff(anchor[n], b, ctx_total);
+    };
+    auto inclusive_scan = [&](int v) {
+        scan[tid] = v;
+        __syncthreads();
+        for (int w = 1; w < 1024; w <<= 1) {
+            int add = tid >= w ? scan[tid - w] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        int r = scan[tid];
+        __syncthreads();
+        return r;
+    };
+    // 1. group starts
+    int cnt = 0;
+    for (int i = 0; i < per_t; ++i) if (b0 + i < nb && starts(b0 + i)) ++cnt;
+    int gidx = inclusive_scan(cnt) - cnt;
+    if (tid == 1023) ngroups_s = gidx + cnt;
+    for (int i = 0; i < per_t; ++i)
+        if (b0 + i < nb && starts(b0 + i)) group_start[gidx++] = b0 + i;
+    __syncthreads();
+    const int ng = ngroups_s;
+    if (tid == 0) group_start[ng] = nb;
+    __threadfence_block();
+    __syncthreads();
+    // 2. group lengths -> chunk
+    const int gper = (ng + 1023) / 1024;
+    const int g0 = tid * gper;
+    auto group_len = [&](int gi) {
+        int mx = -1;
+        for (int n = group_start[gi]; n < group_start[gi + 1]; ++n) mx = max(mx, block_run(n));
+        return mx;
     };
     long long sum = 0;
-    for (int n = tid; n < nb; n += 1024) {
-        int64_t a = a_eff(n);
-        sum += a > 0 ? a : 0;
-    }
+    for (int i = 0; i < gper; ++i) if (g0 + i < ng) sum += max(group_len(g0 + i), 0);
     red[tid] = sum;
     __syncthreads();
     for (int w = 512; w > 0; w >>= 1) {
@@ -465,43 +582,31 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base
         __syncthreads();
     }
     if (tid == 0) {
-        long long per = (red[0] + target - 1) / target;
-        per = (per + 127) / 128 * 128;
-        if (per < 512) per = 512;
-        if (per > (1 << 30)) per = 1 << 30;
-        chunk_s = (int)per;
-        *chunk_out = (int)per;
+        long long c = (red[0] + target - 1) / target;
+        c = (c + 127) / 128 * 128;
+        if (c < 256) c = 256;
+        if (c > (1 << 30)) c = 1 << 30;
+        chunk_s = (int)c;
+        sched[0] = (int)c;
+        sched[1] = ng;
     }
     __syncthreads();
     const int chunk = chunk_s;
-    const int per_t = (nb + 1023) / 1024;
-    const int n0 = tid * per_t;
+    // 3. splits per group -> item_start
     int local = 0;
-    for (int i = 0; i < per_t; ++i) {
-        const int n = n0 + i;
-        if (n < nb) {
-            int64_t a = a_eff(n);
-            local += a <= 0 ? 1 : (int)((a + chunk - 1) / chunk);
+    for (int i = 0; i < gper; ++i)
+        if (g0 + i < ng) {
+            const int len = group_len(g0 + i);
+            local += len <= 0 ? 1 : (len + chunk - 1) / chunk;
         }
-    }
-    scan[tid] = local;
-    __syncthreads();
-    for (int w = 1; w < 1024; w <<= 1) {
-        int v = tid >= w ? scan[tid - w] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    int run = scan[tid] - local;
-    for (int i = 0; i < per_t; ++i) {
-        const int n = n0 + i;
-        if (n < nb) {
-            item_start[n] = run;
-            int64_t a = a_eff(n);
-            run += a <= 0 ? 1 : (int)((a + chunk - 1) / chunk);
+    int run = inclusive_scan(local) - local;
+    for (int i = 0; i < gper; ++i)
+        if (g0 + i < ng) {
+            item_start[g0 + i] = run;
+            const int len = group_len(g0 + i);
+            run += len <= 0 ? 1 : (len + chunk - 1) / chunk;
         }
-    }
-    if (tid == 1023) item_start[nb] = scan[1023];
+    if (tid == 1023) item_start[ng] = run;
 }
 
 }  // namespace dflash

@@ -158,8 +158,9 @@ template <typename T> struct EpSwiGLU {
 
 // Context K/V: virtual column n = l*(2*Hkv*D) + [K heads | V heads]. K columns
 // are rotated (pair d with d + D/2; both live in this wave because WN is a
-// multiple of D and heads start at multiples of D) and both are scattered to
-// the head-major caches [Hkv][ctx_total][D] at cache row row_offset + row.
+// multiple of D and heads start at multiples of D) and written to the
+// head-major cache [Hkv][ctx_total][D]; V columns go to the transposed cache
+// [Hkv][D][ctx_total] (4 consecutive rows per lane -> one vector store).
 template <typename T> struct EpCtxKV {
     T* ck[kMaxLayers];
     T* cv[kMaxLayers];
@@ -173,7 +174,9 @@ template <typename T> struct EpCtxKV {
         constexpr int half = D / 2;
         constexpr int pj = half / 32;             // partner tile distance
         static_assert(NI % (2 * pj) == 0, "a wave covers whole heads");
+        typedef T T4 __attribute__((ext_vector_type(4)));
         const int hkvd = hkv * D;
+        const bool vec_ok = (row_offset & 3) == 0 && (ctx_total & 3) == 0;
 #pragma unroll
         for (int q = 0; q < NI / 2; ++q) {
             const int j = (q / pj) * 2 * pj + q % pj;   // first tile of a (d, d + D/2) pair
@@ -185,25 +188,48 @@ template <typename T> struct EpCtxKV {
             const int rr = is_v ? r - hkvd : r;
             const int g = rr / D;
             const int dd = rr - g * D + (lane & 31);      // in [0, D/2)
-            T* base = (is_v ? cv[l] : ck[l]) + ((int64_t)g * ctx_total + row_offset) * D;
+            if (is_v) {
+                T* v1 = cv[l] + ((int64_t)g * D + dd) * ctx_total + row_offset;
+                T* v2 = v1 + (int64_t)half * ctx_total;
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = mb + i * 32 + acc_row(e, lane);
-                    if (row >= M) continue;
-                    T* o = base + (int64_t)row * D;
-                    const float x1 = acc[i][j][e], x2 = acc[i][jp][e];
-                    if (is_v) {
-                        o[dd] = from_f32<T>(x1);
-                        o[dd + half] = from_f32<T>(x2);
-                    } else {
+                    for (int eg = 0; eg < 4; ++eg) {
+                        const int r0 = mb + i * 32 + acc_row(4 * eg, lane);   // 4 consecutive rows
+                        if (vec_ok && r0 + 3 < M) {
+                            T4 a1, a2;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                a1[t] = from_f32<T>(acc[i][j][4 * eg + t]);
+                                a2[t] = from_f32<T>(acc[i][jp][4 * eg + t]);
+                            }
+                            *reinterpret_cast<T4*>(v1 + r0) = a1;
+                            *reinterpret_cast<T4*>(v2 + r0) = a2;
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                if (r0 + t < M) {
+                                    v1[r0 + t] = from_f32<T>(acc[i][j][4 * eg + t]);
+                                    v2[r0 + t] = from_f32<T>(acc[i][jp][4 * eg + t]);
+                                }
+                        }
+                    }
+            } else {
+                T* kbase = ck[l] + ((int64_t)g * ctx_total + row_offset) * D;
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = mb + i * 32 + acc_row(e, lane);
+                        if (row >= M) continue;
+                        T* o = kbase + (int64_t)row * D;
+                        const float x1 = acc[i][j][e], x2 = acc[i][jp][e];
                         float c, s;
                         rope_cs(rt, dd, positions[row], c, s);
                         o[dd] = from_f32<T>(x1 * c - x2 * s);
                         o[dd + half] = from_f32<T>(x2 * c + x1 * s);
                     }
-                }
+            }
         }
     }
 };

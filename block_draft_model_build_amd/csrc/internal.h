@@ -14,10 +14,13 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int elem_bytes(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
-// Keys per split target for the attention scheduler; see attn_schedule_kernel.
+// The attention scheduler sizes splits so that about kAttnItems work items
+// (group x split x KV head) carry the prefix work: a few per compute unit, so
+// the longest-first dispatch order can balance them.
+constexpr int kAttnItems = 1024;
 inline int attn_target_splits(const dflash_config& c, int nb) {
-    int t = (2048 + c.num_kv_heads - 1) / c.num_kv_heads;
-    return nb > t ? nb : t;
+    (void)nb;
+    return (kAttnItems + c.num_kv_heads - 1) / c.num_kv_heads;
 }
 
 inline int attn_qcols(const dflash_config& c) {
@@ -25,13 +28,17 @@ inline int attn_qcols(const dflash_config& c) {
 }
 
 // Workspace layout (every region 256-byte aligned):
-//   attention scheduler: item_start [nb+1] i32, chunk i32
-//   attention partials:  part_o [items_max][QC][D] f32, part_ml [items_max][QC][2] f32
+//   attention scheduler: group_start [nb+1], item_start [nb+1], sched [2] (i32)
+//   attention partials:  part_o [items_max][4][QC][D] f32, part_ml [items_max][4][QC][2] f32
 //   body: h [R][H] f32, x [R][H], qkv [R][(Hq+2Hkv)D], att [R][Hq D], u [R][I]   (dtype)
 //   ctx_proj: C [ctx_rows][H] (dtype); shares the body's space (calls are stream-ordered).
 struct Workspace {
-    size_t item_start, chunk, part_o, part_ml, h, x, qkv, att, u, c, total;
+    size_t group_start, item_start, sched, part_o, part_ml, h, x, qkv, att, u, c, total;
 };
+
+inline int attn_items_max(const dflash_config& c, int nb) {
+    return c.num_kv_heads * (attn_target_splits(c, nb) + nb);
+}
 
 inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_rows) {
     Workspace w{};
@@ -39,12 +46,13 @@ inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_ro
     const size_t R = (size_t)nb * (size_t)c.block_size;
     const size_t H = (size_t)c.hidden, D = (size_t)c.head_dim;
     const size_t qc = (size_t)attn_qcols(c);
-    const size_t items = (size_t)c.num_kv_heads * (size_t)(attn_target_splits(c, nb) + nb);
+    const size_t parts = (size_t)attn_items_max(c, nb) * 4;
     size_t off = 0;
-    w.item_start = off; off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
-    w.chunk = off;      off = align_up(off + sizeof(int), A);
-    w.part_o = off;     off = align_up(off + sizeof(float) * items * qc * D, A);
-    w.part_ml = off;    off = align_up(off + sizeof(float) * items * qc * 2, A);
+    w.group_start = off; off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
+    w.item_start = off;  off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
+    w.sched = off;       off = align_up(off + sizeof(int) * 2, A);
+    w.part_o = off;      off = align_up(off + sizeof(float) * parts * qc * D, A);
+    w.part_ml = off;     off = align_up(off + sizeof(float) * parts * qc * 2, A);
     const size_t shared0 = off;
     w.h = off;          off = align_up(off + sizeof(float) * R * H, A);
     w.x = off;          off = align_up(off + eb * R * H, A);

@@ -156,8 +156,8 @@ def make_training_inputs(w: Workload, device, plan_seed: int = 0, step: int = 0,
 
 def make_inference_inputs(w: Workload, device) -> Dict[str, object]:
     """Ragged per-request prefixes with precomputed per-layer context K/V caches
-    ([Hkv][total][D] per layer, requests packed back to back), one block of
-    anchor + (block_size - 1) mask-token embeddings per request."""
+    (K [Hkv][total][D], V transposed [Hkv][D][total], requests packed back to
+    back), one block of anchor + (block_size - 1) mask-token embeddings per request."""
     assert w.inference
     rng = Rng(w.seed, device)
     dt = w.torch_dtype
@@ -167,7 +167,7 @@ def make_inference_inputs(w: Workload, device) -> Dict[str, object]:
     total = int(offsets[-1].item())
     ctx_k = [rng.normal(f"L{l}.ctx_k", (w.num_kv_heads, total, w.head_dim), dtype=dt)
              for l in range(w.num_layers)]
-    ctx_v = [rng.normal(f"L{l}.ctx_v", (w.num_kv_heads, total, w.head_dim), dtype=dt)
+    ctx_v = [rng.normal(f"L{l}.ctx_v", (w.num_kv_heads, w.head_dim, total), dtype=dt)
              for l in range(w.num_layers)]
     layers = [layer_weights(w, rng, l) for l in range(w.num_layers)]
     anchor_emb = rng.normal("anchor_embeds", (w.batch, w.hidden), dtype=dt)
@@ -184,11 +184,12 @@ def make_inference_inputs(w: Workload, device) -> Dict[str, object]:
 
 def random_attention_inputs(rng: Rng, num_blocks: int, block_size: int, num_q_heads: int,
                             num_kv_heads: int, head_dim: int, ctx_total: int, dtype):
-    """Free-standing q / block k / block v / context caches for the attention call."""
+    """Free-standing q / block k / block v / context caches for the attention call
+    (context K [Hkv][T][D], context V transposed [Hkv][D][T])."""
     R = num_blocks * block_size
     q = rng.normal("attn.q", (R, num_q_heads * head_dim), dtype=dtype)
     k = rng.normal("attn.k", (R, num_kv_heads * head_dim), dtype=dtype)
     v = rng.normal("attn.v", (R, num_kv_heads * head_dim), dtype=dtype)
     ck = rng.normal("attn.ctx_k", (num_kv_heads, ctx_total, head_dim), dtype=dtype)
-    cv = rng.normal("attn.ctx_v", (num_kv_heads, ctx_total, head_dim), dtype=dtype)
+    cv = rng.normal("attn.ctx_v", (num_kv_heads, head_dim, ctx_total), dtype=dtype)
     return q, k, v, ck, cv

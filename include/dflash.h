@@ -128,7 +128,7 @@ dflash_status dflash_build_plan(const uint8_t *mask, int32_t batch, int32_t seq_
  *
  *   C = X W_proj^T                        X [num_rows, L_t*H_t], C [num_rows, H]
  *   ctx_k[l][g][row_offset + r][:] = RoPE((C Wk_l^T)[r, g*D:(g+1)*D], positions[r])
- *   ctx_v[l][g][row_offset + r][:] = (C Wv_l^T)[r, g*D:(g+1)*D]
+ *   ctx_v[l][g][:][row_offset + r] = (C Wv_l^T)[r, g*D:(g+1)*D]
  *
  *   target_states  device; element (r, k) of X is at
  *                  target_states[r*ts_row_stride + (k / H_t)*ts_layer_stride + k % H_t],
@@ -139,8 +139,10 @@ dflash_status dflash_build_plan(const uint8_t *mask, int32_t batch, int32_t seq_
  *   positions      device i32 [num_rows]: RoPE position of each row.
  *   w_proj         device [H, L_t*H_t]
  *   layers         host array [num_layers]; only wk and wv are read.
- *   ctx_k, ctx_v   host arrays [num_layers] of device caches [Hkv][ctx_total][D]
- *                  (head-major); rows [row_offset, row_offset + num_rows) are written.
+ *   ctx_k, ctx_v   host arrays [num_layers] of device caches: K head-major
+ *                  [Hkv][ctx_total][D], V transposed [Hkv][D][ctx_total] (each head's
+ *                  V is stored dimension by dimension, so attention reads V^T tiles
+ *                  as plain rows); rows [row_offset, row_offset + num_rows) are written.
  * RoPE pairs dimension i with i + D/2 at angle position * rope_theta^(-2i/D).
  * Errors: INVALID_ARG when row_offset + num_rows > ctx_total or a pointer is null;
  * WORKSPACE when workspace_bytes < dflash_workspace_size(cfg, 0, num_rows).
@@ -162,13 +164,14 @@ dflash_status dflash_ctx_proj(const dflash_config *cfg, const void *target_state
  *
  * For block n with anchor a = block_anchor[n] and base = block_ctx_base[n], query
  * row k (position a + k) of head h attends, with softmax(q k^T / sqrt(D)), to
- *   ctx_k/ctx_v[g][base + j] for 0 <= j < a        (prefix, strictly before the anchor)
+ *   ctx K/V row base + j of KV head g, 0 <= j < a   (prefix, strictly before the anchor)
  *   k_blk/v_blk rows n*bs + k', k' = 0..bs-1        (its whole block, both directions)
  * where g = h / (Hq/Hkv). q and k_blk arrive un-rotated and are rotated at a + k.
  *
  *   q              device [nb*bs, Hq*D]
  *   k_blk, v_blk   device [nb*bs, Hkv*D]
- *   ctx_k, ctx_v   device [Hkv][ctx_total][D], K already rotated at its positions
+ *   ctx_k          device [Hkv][ctx_total][D], already rotated at its positions
+ *   ctx_v          device [Hkv][D][ctx_total] (transposed, as dflash_ctx_proj writes it)
  *   block_ctx_base device i64 [nb]; block_anchor device i32 [nb] (-1: empty block)
  *   block_valid    device u8 [nb*bs]
  *   out            device [nb*bs, Hq*D]; rows with block_valid == 0 and all rows of
@@ -201,7 +204,8 @@ dflash_status dflash_block_attn(const dflash_config *cfg, int32_t num_blocks, co
  *
  *   block_embeds   device [nb*bs, H] (caller-supplied embedding per block position)
  *   layers         host array [num_layers]
- *   ctx_k, ctx_v   host arrays [num_layers] of device [Hkv][ctx_total][D]
+ *   ctx_k, ctx_v   host arrays [num_layers] of device caches in dflash_ctx_proj's
+ *                  layouts (K [Hkv][ctx_total][D], V [Hkv][D][ctx_total])
  *   out            device [nb*bs, H]
  * Errors: as dflash_block_attn; WORKSPACE below dflash_workspace_size(cfg, nb, 0).
  */

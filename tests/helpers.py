@@ -69,7 +69,8 @@ class TrainingRun:
         self.ctx_pos = torch.arange(S, dtype=torch.int32, device=d).repeat(B)
         self.ctx_k = [torch.empty((w.num_kv_heads, T, w.head_dim), dtype=w.torch_dtype, device=d)
                       for _ in range(w.num_layers)]
-        self.ctx_v = [torch.empty_like(k) for k in self.ctx_k]
+        self.ctx_v = [torch.empty((w.num_kv_heads, w.head_dim, T), dtype=w.torch_dtype, device=d)
+                      for _ in range(w.num_layers)]
         self.out = torch.empty((w.num_blocks * bs, w.hidden), dtype=w.torch_dtype, device=d)
         self.ws = workspace(lib, self.cfg, w.num_blocks, T, d)
 

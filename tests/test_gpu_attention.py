@@ -36,7 +36,8 @@ def _run(w, bases, anchors, valid, ctx_total, seed, check_blocks=None):
         b0 = int(bases[n])
         lo, hi = (b0, b0 + max(a, 0))
         ref = oracle.block_attn_call(np64(q[rows]), np64(k[rows]), np64(v[rows]), np64(ck[:, lo:hi]),
-                                     np64(cv[:, lo:hi]), [0], [a], val[n], bs, w.num_q_heads,
+                                     np64(cv[:, :, lo:hi]).transpose(0, 2, 1), [0], [a], val[n], bs,
+                                     w.num_q_heads,
                                      w.num_kv_heads, w.head_dim, w.rope_theta)
         got = out[rows]
         compare(got, ref, tol, f"block {n} (anchor {a})")
@@ -124,8 +125,9 @@ def test_deterministic_and_information_boundary():
     assert torch.equal(ref, run(q, k, v, ck, cv))
     ck2, cv2, k2, v2 = ck.clone(), cv.clone(), k.clone(), v.clone()
     ck2[:, 1500:S] += 3.0                # block 0 (base 0, anchor 1500) may not read these
-    cv2[:, 1500:S] -= 2.0
+    cv2[:, :, 1500:S] -= 2.0
     ck2[:, S:] = float("nan")            # another sequence
+    cv2[:, :, S:] = float("nan")
     k2[bs:] = float("nan")               # other blocks
     v2[bs:] = float("nan")
     out = run(q, k2, v2, ck2, cv2)

@@ -44,7 +44,7 @@ def _check_ctx(run, rows):
     tol = tol_for(w)
     for l in range(w.num_layers):
         compare(run.ctx_k[l][:, rows], ck[l], tol, f"ctx_k layer {l}")
-        compare(run.ctx_v[l][:, rows], cv[l], tol, f"ctx_v layer {l}")
+        compare(run.ctx_v[l][:, :, rows], cv[l].transpose(0, 2, 1), tol, f"ctx_v layer {l}")
 
 
 def test_tiny_fp32_end_to_end():
@@ -140,7 +140,7 @@ def test_ragged_cache_body_sampled():
     for r in [int(np.argmin(lens)), int(np.argmax(lens)), 7]:
         lo, hi = int(offs[r]), int(offs[r + 1])
         ck = [np64(k[:, lo:hi]) for k in inp["ctx_k"]]
-        cv = [np64(v[:, lo:hi]) for v in inp["ctx_v"]]
+        cv = [np64(v[:, :, lo:hi]).transpose(0, 2, 1) for v in inp["ctx_v"]]
         ref = oracle.body_forward(np64(inp["emb"][r * bs:(r + 1) * bs]), layers, ck, cv, [0],
                                   [int(lens[r])], np.ones(bs, np.uint8), oracle_cfg(w))
         compare(out[r * bs:(r + 1) * bs], ref, tol_for(w), f"request {r} (prefix {lens[r]})")
@@ -161,7 +161,7 @@ def test_body_invariants_bit_exact():
     S, bs = w.seq_len, w.block_size
     for l in range(w.num_layers):                                 # context at or after the anchor
         run.ctx_k[l][:, b * S + a: (b + 1) * S] += 5.0
-        run.ctx_v[l][:, b * S + a: (b + 1) * S] = float("nan")
+        run.ctx_v[l][:, :, b * S + a: (b + 1) * S] = float("nan")
     emb = inp["emb"]
     saved = emb.clone()
     emb[: n * bs] = float("nan")                                  # every other block's embeddings
