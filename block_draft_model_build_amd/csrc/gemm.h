@@ -4,10 +4,8 @@
 // [out, in]), so every 16-byte global load and every MFMA operand fragment is a
 // contiguous K slice. One workgroup = 4 waves (256 threads) computes a BM x BN
 // tile; each wave owns a WM x WN sub-tile made of 32x32 MFMA tiles. The K loop
-// moves 128-byte-deep slabs (64 bf16 / 32 fp32) of A and B through LDS, double
-// buffered, with the next slab prefetched into registers while the current one
-// feeds the matrix cores. LDS rows are padded by 16 bytes so the 32 rows one
-// fragment load touches fall on distinct banks.
+// streams 64-byte-deep slabs of A and B straight into a 4-stage LDS ring (see
+// gemm_nt_kernel).
 //
 // Operand "loaders" resolve row pointers, which lets a single GEMM read
 // several weight matrices as one virtual B (Q|K|V, interleaved gate/up, every
@@ -19,13 +17,21 @@
 
 namespace dflash {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+// BM x BN tile, WAVES_M x WAVES_N waves, K slabs of ROWB bytes per row, NST
+// LDS stages.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int ROWB_ = 64, int NST_ = 4>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int ROWB = ROWB_, NST = NST_;
+    static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte slabs");
+    static_assert(NST >= 2 && NST <= 4, "2 to 4 stages");
+    static constexpr int NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int MI = WM / 32, NI = WN / 32;
-    static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
+    static constexpr int RUN = 1024 / ROWB;            // rows one 1 KB DMA instruction fills
+    static_assert(BM % (RUN * NW) == 0 && BN % (RUN * NW) == 0, "whole DMA runs per wave");
 };
 
 // ---------------------------------------------------------------- A loaders
@@ -235,29 +241,60 @@ template <typename T> struct EpCtxKV {
 };
 
 // ---------------------------------------------------------------- kernel
+#define DFLASH_GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define DFLASH_LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (LDS and export counters left unconstrained).
+template <int n> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16-byte chunk swizzle of the LDS rows: row r keeps logical chunk c at
+// physical chunk c ^ swz(r). Chosen by measuring LDS bank conflicts of the
+// fragment read pattern (32 rows x one chunk per half-wave) on gfx950: these
+// read conflict-free for 64- and 128-byte rows. swz(r + 32) == swz(r).
+template <int ROWB> __device__ __forceinline__ int swz(int r) {
+    return ROWB == 64 ? (r >> 2) & 3 : (r >> 1) & 7;
+}
+
+// Main loop: 64-byte-deep K slabs (32 bf16 / 16 fp32) of A and B move from
+// global memory straight into LDS (global_load_lds_dwordx4: lane i of a wave
+// writes LDS bytes [16i, 16i + 16) of a 1 KB run, i.e. 16 rows x 64 bytes), in
+// a ring of 4 stages with 3 slabs in flight. One barrier per slab; MFMA
+// fragments of the next k-step are read while the current one multiplies.
 template <typename T, class Cfg, class AL, class BL, class EP>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, AL al, BL bl, EP ep) {
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int K, AL al, BL bl, EP ep) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MI = Cfg::MI, NI = Cfg::NI;
-    constexpr int ROWB = 128 + 16;                 // bytes per padded LDS row
     constexpr int EB = (int)sizeof(T);
-    constexpr int BK = 128 / EB;
-    constexpr int ACH = BM / 32, BCH = BN / 32;    // 16-byte chunks per thread per slab
-    constexpr int KSTEP = Mfma<T>::KSTEP, E = Mfma<T>::E;
+    constexpr int ROWB = Cfg::ROWB;                // bytes per LDS row (one K slab)
+    constexpr int BK = ROWB / EB;
+    constexpr int NST = Cfg::NST;                  // LDS stages
+    constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+    constexpr int NW = Cfg::NW, RUN = Cfg::RUN, CPR = ROWB / 16;
+    constexpr int A_INST = BM / (RUN * NW), B_INST = BN / (RUN * NW);   // DMA runs per wave per slab
+    constexpr int LPS = A_INST + B_INST;                // DMA instructions per wave per slab
+    constexpr int KSTEP = Mfma<T>::KSTEP, E = Mfma<T>::E, KK = BK / KSTEP;
     typedef typename Mfma<T>::frag frag;
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
-    auto sA = [&](int buf) { return smem + buf * (BM + BN) * ROWB; };
-    auto sB = [&](int buf) { return smem + buf * (BM + BN) * ROWB + BM * ROWB; };
+    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
-    // Tile order: consecutive workgroups walk down M inside groups of 8 row
-    // tiles so the B slab they share stays hot in L2.
+    // Tile order: consecutive tiles walk down M inside groups of 8 row tiles
+    // so the B slab they share stays hot in L2.
     const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
     int tm, tn;
     {
-        const int id = blockIdx.x;
+        // Workgroups are dealt round-robin to the 8 XCDs (each with its own
+        // L2); renumber so that each XCD gets a contiguous run of tiles.
+        int id = blockIdx.x;
+        {
+            const int G = tiles_m * tiles_n, G8 = G / 8 * 8;
+            if (id < G8) id = (id % 8) * (G / 8) + id / 8;
+        }
         const int group = 8;
         const int per_group = group * tiles_n;
         const int gi = id / per_group;
@@ -269,31 +306,47 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, AL al
     }
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const T* ap[ACH];
-    const T* bp[BCH];
+    // DMA sources: wave w fills A rows [w*BM/NW, (w+1)*BM/NW) and B rows
+    // [w*BN/NW, ...) in runs of RUN rows; lane -> (row lane/CPR, physical chunk lane%CPR).
+    const T* ap[A_INST];
+    const T* bp[B_INST];
+    const int rr = lane / CPR, pc = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        int r = m0 + (tid >> 3) + 32 * i;
-        ap[i] = al.row(r < M ? r : M - 1);
+    for (int i = 0; i < A_INST; ++i) {
+        const int r = wave * (BM / NW) + i * RUN + rr;
+        const int gr = m0 + r < M ? m0 + r : M - 1;
+        ap[i] = al.row(gr) + ((pc ^ swz<ROWB>(r)) * (16 / EB));
     }
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) bp[i] = bl.row(n0 + (tid >> 3) + 32 * i);
-    const int kofs = (tid & 7) * (16 / EB);
-    const int lds_w = (tid >> 3) * ROWB + (tid & 7) * 16;
+    for (int i = 0; i < B_INST; ++i) {
+        const int r = wave * (BN / NW) + i * RUN + rr;
+        bp[i] = bl.row(n0 + r) + ((pc ^ swz<ROWB>(r)) * (16 / EB));
+    }
+    auto issue = [&](int kt) {
+        char* st = smem + (kt % NST) * STAGE;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i)
+            __builtin_amdgcn_global_load_lds(DFLASH_GPTR(al.at(ap[i], k0)),
+                                             DFLASH_LPTR(st + (wave * (BM / NW) + i * RUN) * ROWB), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B_INST; ++i)
+            __builtin_amdgcn_global_load_lds(DFLASH_GPTR(bp[i] + k0),
+                                             DFLASH_LPTR(st + A_BYTES + (wave * (BN / NW) + i * RUN) * ROWB), 16,
+                                             0, 0);
+    };
 
-    u32x4 ra[ACH], rb[BCH];
-    auto gload = [&](int k0) {
+    // Fragment addresses: lane reads row (lane % 32) of each 32-row sub-tile at
+    // byte offset (kk*KSTEP + h*E)*EB of the row, through the swizzle.
+    int foff[KK];
+    {
+        const int r = lane & 31;                  // swz(r + 32j) == swz(r)
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(al.at(ap[i], k0) + kofs);
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0 + kofs);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(sA(buf) + lds_w + 32 * i * ROWB) = ra[i];
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) *reinterpret_cast<u32x4*>(sB(buf) + lds_w + 32 * i * ROWB) = rb[i];
-    };
+        for (int kk = 0; kk < KK; ++kk) {
+            const int fb = (kk * KSTEP + h * E) * EB;
+            foff[kk] = r * ROWB + (((fb >> 4) ^ swz<ROWB>(r)) << 4) + (fb & 15);
+        }
+    }
 
     f32x16 acc[MI][NI];
 #pragma unroll
@@ -304,33 +357,71 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, AL al
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int KT = K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+        if (t < KT) issue(t);
 
-    const int frag_off = (lane & 31) * ROWB + (lane >> 5) * E * EB;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload((kt + 1) * BK);
-        const char* a_base = sA(cur) + (wm * Cfg::WM) * ROWB + frag_off;
-        const char* b_base = sB(cur) + (wn * Cfg::WN) * ROWB + frag_off;
-#pragma unroll
-        for (int kk = 0; kk < BK / KSTEP; ++kk) {
-            frag af[MI], bf[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const frag*>(a_base + i * 32 * ROWB + kk * KSTEP * EB);
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                bf[j] = *reinterpret_cast<const frag*>(b_base + j * 32 * ROWB + kk * KSTEP * EB);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = Mfma<T>::mma(af[i], bf[j], acc[i][j]);
+    // Slab t is complete (for every wave) once this wave has at most the
+    // later slabs' DMAs outstanding and all waves have met at the barrier.
+    auto wait_slab = [&](int t) {
+        const int later = min(NST - 2, KT - 1 - t);
+        if constexpr (NST >= 4) {
+            if (later >= 2) wait_vmcnt<2 * LPS>();
+            else if (later == 1) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+        } else if constexpr (NST == 3) {
+            if (later >= 1) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
         }
-        if (kt + 1 < KT) lstore(cur ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    frag af[2][MI], bf[2][NI];
+    auto read_frags = [&](int t, int kk, int buf) {
+        const char* st = smem + (t % NST) * STAGE;
+        const char* a_base = st + (wm * Cfg::WM) * ROWB + foff[kk];
+        const char* b_base = st + A_BYTES + (wn * Cfg::WN) * ROWB + foff[kk];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[buf][i] = *reinterpret_cast<const frag*>(a_base + i * 32 * ROWB);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) bf[buf][j] = *reinterpret_cast<const frag*>(b_base + j * 32 * ROWB);
+    };
+
+    wait_slab(0);
+    read_frags(0, 0, 0);
+    for (int t = 0; t < KT; ++t) {
+        // The stage slab t + NST - 1 lands in was last read in iteration t - 1,
+        // whose reads all completed before this wave's previous barrier.
+        if (t + NST - 1 < KT) issue(t + NST - 1);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < KK) read_frags(t, kk + 1, cur ^ 1);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[i][j] = Mfma<T>::mma(af[cur][i], bf[cur][j], acc[i][j]);
+            // Interleave the next k-step's fragment reads with these MFMAs.
+            if (kk + 1 < KK) {
+#pragma unroll
+                for (int q = 0; q < MI + NI; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
+            }
+        }
+        // The last k-step's MFMAs are in flight: meet the other waves on the
+        // next slab and start reading it meanwhile.
+        if (t + 1 < KT) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_slab(t + 1);
+            read_frags(t + 1, 0, KK & 1);
+        }
     }
+    static_assert(KK % 2 == 0, "fragment buffers alternate within a slab");
 
     ep.template apply<MI, NI, Cfg::WN>(m0 + wm * Cfg::WM, n0 + wn * Cfg::WN, acc, lane, M);
 }
@@ -340,7 +431,7 @@ hipError_t launch_gemm(int M, int N, int K, const AL& al, const BL& bl, const EP
                        hipStream_t stream) {
     if (M <= 0) return hipSuccess;
     const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
-    hipLaunchKernelGGL((gemm_nt_kernel<T, Cfg, AL, BL, EP>), dim3(tiles), dim3(256), 0, stream, M, N,
+    hipLaunchKernelGGL((gemm_nt_kernel<T, Cfg, AL, BL, EP>), dim3(tiles), dim3(Cfg::THREADS), 0, stream, M, N,
                        K, al, bl, ep);
     return hipGetLastError();
 }
