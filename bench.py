@@ -299,7 +299,8 @@ def main():
     positions = w.num_blocks * w.block_size
     value = positions / (ms / 1e3)
     roof = roofline_entry(dominant, counts[dominant], dom_avg, w.dtype)
-    roof["traffic"] = None
+    from bench_traffic import load as load_traffic
+    roof["traffic"] = load_traffic(w.name, dominant)
     roof["launches_timed"] = len(dom_times)
     t_roof = step_roofline_ms(counts, w.dtype)
     result = {
@@ -316,7 +317,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")
-        budgets = {"c1": (128, 4), "c2": (1024, 8), "c3": (1024, 6), "c4": (1024, 4), "c5": (None, 4)}
+        budgets = {"c1": (128, 4), "c2": (8192, 32), "c3": (8192, 48), "c4": (4096, 12), "c5": (None, 24)}
         r, b = budgets[w.name]
         result["cpu_baseline"] = cpu_baseline(w, runner, anchors, r, b)
     print(json.dumps(result), flush=True)

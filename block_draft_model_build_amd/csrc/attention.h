@@ -89,29 +89,44 @@ struct AttnTile {
     static constexpr int VLD = D * VCH / 256;         // V^T chunks per thread per super-tile
 };
 
-// One wave folds a 32-key slice (K rows at ks, V^T at vt, row pitch vrow)
-// with `nvalid` visible keys into its running softmax state.
-template <typename T, int D, int QC>
-__device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int vrow, int nvalid,
-                                           const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
-                                           f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
-                                           float (&l)[QC / 32], int lane) {
+// One wave folds a 32-key slice into its running softmax state, given the
+// slice's K fragments (kf[kk]: row key_perm(lane % 32), d-slice kk) and V^T
+// fragments (vf[st][ds]: row d = 32 ds + lane % 32, keys 16 st + 8 (lane / 32)
+// .. + 7 for bf16) of which the first `nvalid` keys are visible.
+// S^T of a 32-key slice; getk(kk) returns the K fragment of d-step kk.
+template <typename T, int D, int QC, class GetK>
+__device__ __forceinline__ void attn_scores(const GetK& getk,
+                                            const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
+                                            f32x16 (&s)[QC / 32]) {
     using TT = AttnTile<T, D, QC>;
-    typedef typename Mfma<T>::frag frag;
-    constexpr int QS = TT::QS, DS = TT::DS, DK = TT::DK, PK = TT::PK, E = TT::E, EB = TT::EB;
-    const int h = lane >> 5;
-    f32x16 s[QS];
+    constexpr int QS = TT::QS, DK = TT::DK;
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[qs][e] = 0.f;
-    const char* krow = ks + key_perm(lane & 31) * TT::KROW + h * E * EB;
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
-        frag a = *reinterpret_cast<const frag*>(krow + kk * TT::KSTEP * EB);
+        const typename Mfma<T>::frag a = getk(kk);
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) s[qs] = Mfma<T>::mma(a, qf[qs][kk], s[qs]);
     }
+}
+
+// getv(st, ds) returns the V^T fragment of MFMA step st, d-tile ds.
+template <typename T, int D, int QC, class GetV>
+__device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& getv, int nvalid,
+                                            f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
+                                            float (&l)[QC / 32], int lane) {
+    using TT = AttnTile<T, D, QC>;
+    typedef typename Mfma<T>::frag frag;
+    constexpr int QS = TT::QS, DS = TT::DS, PK = TT::PK, E = TT::E;
+    const int h = lane >> 5;
+    // Online softmax with a lazily moved reference max m: P = 2^(s - m) is
+    // allowed to grow up to 2^kLazy, and O and l are rescaled only when some
+    // column's scores exceed its reference by more than that (rare after the
+    // first keys), which keeps the DS*16 rescaling multiplies per column off the
+    // common path. The result is the same softmax: O and l share the reference.
+    constexpr float kLazy = 8.f;
     const float NEG_INF = -__builtin_inff();
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
@@ -124,23 +139,26 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qs][e]);
         mx = fmaxf(mx, xor32(mx));
-        const float mnew = fmaxf(m[qs], mx);
-        const float muse = (mnew == NEG_INF) ? 0.f : mnew;
-        const float alpha = fast_exp2(m[qs] - muse);
-        m[qs] = mnew;
+        const bool grow = mx > m[qs] + kLazy;        // also true on the first visible keys
+        if (__any(grow)) {
+            const float mnew = grow ? mx : m[qs];
+            const float alpha = (m[qs] == NEG_INF) ? 0.f : fast_exp2(m[qs] - mnew);
+            m[qs] = mnew;
+            l[qs] *= alpha;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[ds][qs][e] *= alpha;
+        }
+        const float muse = (m[qs] == NEG_INF) ? 0.f : m[qs];
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             s[qs][e] = fast_exp2(s[qs][e] - muse);
             ps += s[qs][e];
         }
-        l[qs] = l[qs] * alpha + ps;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[ds][qs][e] *= alpha;
+        l[qs] += ps;
     }
-    const char* vbase = vt + (lane & 31) * vrow;
 #pragma unroll
     for (int st = 0; st < PK; ++st) {
         frag pf[QS];
@@ -155,19 +173,15 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
         }
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-            const char* vr = vbase + ds * 32 * vrow;
-            frag a;
-            if constexpr (E == 8) {
-                a = *reinterpret_cast<const frag*>(vr + (16 * st + 8 * h) * EB);
-                if (nvalid < 32) {          // keys past this block's end: exact zeros, even if V is not finite
+            frag a = getv(st, ds);
+            if (nvalid < 32) {        // keys past the end: exact zeros, even if V is not finite
+                if constexpr (E == 8) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
                         if (16 * st + 8 * h + i >= nvalid) a[i] = from_f32<T>(0.f);
+                } else {
+                    if (key_perm(acc_row(st, lane)) >= nvalid) a = 0.f;
                 }
-            } else {
-                const int key = key_perm(acc_row(st, lane));
-                a = *reinterpret_cast<const T*>(vr + key * EB);
-                if (key >= nvalid) a = 0.f;
             }
 #pragma unroll
             for (int qs = 0; qs < QS; ++qs) o[ds][qs] = Mfma<T>::mma(a, pf[qs], o[ds][qs]);
@@ -175,7 +189,79 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
     }
 }
 
+// One wave folds a 32-key slice staged in LDS (K rows at ks, V^T at vt with
+// row pitch vrow; `nvalid` visible keys) into its running softmax state.
 template <typename T, int D, int QC>
+__device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int vrow, int nvalid,
+                                           const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
+                                           f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
+                                           float (&l)[QC / 32], int lane) {
+    using TT = AttnTile<T, D, QC>;
+    typedef typename Mfma<T>::frag frag;
+    constexpr int E = TT::E, EB = TT::EB;
+    const int h = lane >> 5;
+    const char* krow = ks + key_perm(lane & 31) * TT::KROW + h * E * EB;
+    f32x16 sc[QC / 32];
+    attn_scores<T, D, QC>([&](int kk) { return *reinterpret_cast<const frag*>(krow + kk * TT::KSTEP * EB); },
+                          qf, sc);
+    const char* vbase = vt + (lane & 31) * vrow;
+    auto getv = [&](int st, int ds) -> frag {
+        const char* vr = vbase + ds * 32 * vrow;
+        if constexpr (E == 8)
+            return *reinterpret_cast<const frag*>(vr + (16 * st + 8 * h) * EB);
+        else
+            return *reinterpret_cast<const T*>(vr + key_perm(acc_row(st, lane)) * EB);
+    };
+    attn_update<T, D, QC>(sc, getv, nvalid, o, m, l, lane);
+}
+
+// Fragments of one 32-key slice straight from the context caches (no LDS):
+// K row key_perm(lane % 32) of the slice, and V^T rows d at the slice's keys.
+// Keys at or past `kend` read the last visible K row, and their V^T elements
+// are loaded one by one as zeros, so nothing outside the caches is touched.
+template <typename T, int D, int QC>
+__device__ __forceinline__ void attn_load_k(const T* ckg, int key0, int kend,
+                                            typename Mfma<T>::frag (&kf)[D / Mfma<T>::KSTEP], int lane) {
+    using TT = AttnTile<T, D, QC>;
+    typedef typename Mfma<T>::frag frag;
+    int key = key0 + key_perm(lane & 31);
+    key = key < kend ? key : kend - 1;
+    const T* kr = ckg + (int64_t)key * D + (lane >> 5) * TT::E;
+#pragma unroll
+    for (int kk = 0; kk < TT::DK; ++kk) kf[kk] = *reinterpret_cast<const frag*>(kr + kk * TT::KSTEP);
+}
+
+template <typename T, int D, int QC>
+__device__ __forceinline__ void attn_load_v(const T* cvg, int64_t ctx_total, int key0, int kend,
+                                            typename Mfma<T>::frag (&vf)[32 / Mfma<T>::KSTEP][D / 32], int lane) {
+    using TT = AttnTile<T, D, QC>;
+    typedef typename Mfma<T>::frag frag;
+    const int h = lane >> 5;
+    const bool full = key0 + 32 <= kend;
+#pragma unroll
+    for (int st = 0; st < TT::PK; ++st)
+#pragma unroll
+        for (int ds = 0; ds < TT::DS; ++ds) {
+            const T* vr = cvg + (int64_t)(ds * 32 + (lane & 31)) * ctx_total + key0;
+            if constexpr (TT::E == 8) {
+                const int k0 = 16 * st + 8 * h;
+                if (full) {
+                    vf[st][ds] = *reinterpret_cast<const frag*>(vr + k0);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) vf[st][ds][i] = key0 + k0 + i < kend ? vr[k0 + i] : from_f32<T>(0.f);
+                }
+            } else {
+                const int kk = key_perm(acc_row(st, lane));
+                vf[st][ds] = key0 + kk < kend ? vr[kk] : 0.f;
+            }
+        }
+}
+
+// STREAM selects the items this instantiation serves: single-block groups
+// (streamed from the caches into registers) or multi-block groups (shared
+// LDS tiles). Both are launched over the same item list.
+template <typename T, int D, int QC, bool STREAM>
 __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     using TT = AttnTile<T, D, QC>;
     typedef typename Mfma<T>::frag frag;
@@ -202,6 +288,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
     const int n0 = p.group_start[gi];
     const int ng = p.group_start[gi + 1] - n0;
+    if ((ng == 1) != STREAM) return;
     const int wpb = ng == 1 ? 4 : (ng == 2 ? 2 : 1);   // waves per block
     const int j = wave / wpb;                          // this wave's block in the group
     const int phase = wave - j * wpb;                  // this wave's share of the block's keys
@@ -356,6 +443,28 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
     };
 
+    if constexpr (STREAM) {
+        // One block: the 4 waves take interleaved 32-key slices and stream them
+        // from the caches into registers. Each buffer is refilled for the next
+        // slice right after its last use (K after the score MFMAs, V^T after
+        // the P.V MFMAs), so loads overlap the rest of the slice's work.
+        const int nsl = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+        if (wave < nsl) {
+            frag kf[DK], vf[TT::PK][DS];
+            attn_load_k<T, D, QC>(ckg, kbeg + 32 * wave, kend, kf, lane);
+            attn_load_v<T, D, QC>(cvg, p.ctx_total, kbeg + 32 * wave, kend, vf, lane);
+            for (int i = wave; i < nsl; i += 4) {
+                const bool more = i + 4 < nsl;
+                f32x16 sc[QS];
+                attn_scores<T, D, QC>([&](int kk) { return kf[kk]; }, qf, sc);
+                if (more) attn_load_k<T, D, QC>(ckg, kbeg + 32 * (i + 4), kend, kf, lane);
+                attn_update<T, D, QC>(sc, [&](int st, int ds) { return vf[st][ds]; },
+                                      min(32, kend - (kbeg + 32 * i)), o, m, l, lane);
+                if (more) attn_load_v<T, D, QC>(cvg, p.ctx_total, kbeg + 32 * (i + 4), kend, vf, lane);
+            }
+        }
+    }
+    if constexpr (!STREAM) {
     if (ntile > 0) {
         gload(kbeg);
         lstore(0);
@@ -376,6 +485,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             }
         }
     }
+
+    }  // !STREAM
 
     // ---- merge the waves serving one block (tree over phases), via LDS
 #pragma unroll

@@ -61,7 +61,8 @@ static hipError_t attn_launch_t(const dflash_config& c, const AttnArgs<T>& a, in
     const int items_max = attn_items_max(c, nb);
     {
         ProfScope prof(DFLASH_KERNEL_ATTENTION, st);
-        hipLaunchKernelGGL((block_attn_kernel<T, D, QC>), dim3(items_max), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((block_attn_kernel<T, D, QC, false>), dim3(items_max), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((block_attn_kernel<T, D, QC, true>), dim3(items_max), dim3(256), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -137,9 +138,7 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     ep.hkv = c.num_kv_heads;
     ep.rt = make_rope_turns(c);
     const int N = c.num_layers * 2 * c.num_kv_heads * c.head_dim;
-    // The RoPE epilogue needs registers the 256x256 tile does not have left.
-    ProfScope prof(DFLASH_KERNEL_CTX_KV, st);
-    return launch_gemm<T, MidTile>(M, N, H, APlain<T>{C, H}, b, ep, st);
+    return gemm<T>(DFLASH_KERNEL_CTX_KV, M, N, H, APlain<T>{C, H}, b, ep, st);
 }
 
 template <typename T>
