@@ -131,6 +131,11 @@ def kernel_counts(w, anchors):
                           bytes=float(Hkv * keys.sum() * 2 * D * eb + 2 * R * Hq * D * eb),
                           launches=L, bound="hbm")
     c["rmsnorm"] = dict(flops=float(3.0 * R * H), bytes=float(R * H * (4 + eb)), launches=2 * L, bound="hbm")
+    # Merge of split prefixes: at most every query row of every head in and out
+    # once in fp32 (an upper bound; no splits -> no work).
+    c["attn_combine"] = dict(flops=0.0, bytes=float(2 * R * Hq * D * 4), launches=L, bound="hbm")
+    if not w.inference:
+        c["plan"] = dict(flops=0.0, bytes=float(w.batch * w.seq_len + 10 * nb * bs), launches=1, bound="hbm")
     return c
 
 

@@ -49,7 +49,8 @@ template <typename T> struct AttnArgs {
     float qscale;                      // log2(e) / sqrt(D)
     const int* group_start;            // [groups + 1]
     const int* item_start;             // [groups + 1] prefix sums of splits per group
-    const int* sched;                  // [0] keys per split, [1] number of groups
+    const int* sched;                  // [0] keys per split of multi-block groups,
+                                       // [1] number of groups, [2] of single-block groups
     float* part_o;                     // [items][kMaxGroup][QC][D]
     float* part_ml;                    // [items][kMaxGroup][QC][2]
     RopeTurns rt;
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     const int phase = wave - j * wpb;                  // this wave's share of the block's keys
     const bool active = j < ng;
     const int qcols = bs * G;
-    const int chunk = p.sched[0];
+    const int chunk = ng == 1 ? p.sched[2] : p.sched[0];
     const int64_t base = clamp_base(p.base[n0], p.ctx_total);
     const int kbeg = s * chunk;
 
@@ -631,16 +632,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
 
 // Groups and splits. A group starts at every block whose index is a multiple
 // of 4 or whose (clamped) context base differs from the previous block's. A
-// group's stream length is its largest (clamped) anchor. chunk = max(256,
-// ceil(sum of group lengths / target) rounded up to 128), so that about
-// target * Hkv items carry the work; a group gets max(1, ceil(length / chunk))
-// splits.
+// group's stream length is its largest (clamped) anchor. Single-block and
+// multi-block groups get separate split sizes: chunk = max(256, ceil(sum of
+// their lengths / target) rounded up to 128), target_stream (single) or
+// target_shared (multi) splits in total; a group gets max(1, ceil(length /
+// chunk)) splits.
 __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
-                                                             int64_t ctx_total, int target, int* group_start,
-                                                             int* item_start, int* sched) {
+                                                             int64_t ctx_total, int target_shared, int target_stream,
+                                                             int* group_start, int* item_start, int* sched) {
     __shared__ int scan[1024];
-    __shared__ long long red[1024];
-    __shared__ int chunk_s, ngroups_s;
+    __shared__ long long red[2][1024];
+    __shared__ int chunk_s[2], ngroups_s;
     const int tid = threadIdx.x;
     const int per_t = (nb + 1023) / 1024;
     const int b0 = tid * per_t;
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base
     if (tid == 0) group_start[ng] = nb;
     __threadfence_block();
     __syncthreads();
-    // 2. group lengths -> chunk
+    // 2. group lengths -> the two split sizes
     const int gper = (ng + 1023) / 1024;
     const int g0 = tid * gper;
     auto group_len = [&](int gi) {
@@ -684,38 +686,45 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base
         for (int n = group_start[gi]; n < group_start[gi + 1]; ++n) mx = max(mx, block_run(n));
         return mx;
     };
-    long long sum = 0;
-    for (int i = 0; i < gper; ++i) if (g0 + i < ng) sum += max(group_len(g0 + i), 0);
-    red[tid] = sum;
+    auto single = [&](int gi) { return group_start[gi + 1] - group_start[gi] == 1; };
+    long long sum[2] = {0, 0};
+    for (int i = 0; i < gper; ++i)
+        if (g0 + i < ng) sum[single(g0 + i) ? 1 : 0] += max(group_len(g0 + i), 0);
+    red[0][tid] = sum[0];
+    red[1][tid] = sum[1];
     __syncthreads();
     for (int w = 512; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
+        if (tid < w) {
+            red[0][tid] += red[0][tid + w];
+            red[1][tid] += red[1][tid + w];
+        }
         __syncthreads();
     }
-    if (tid == 0) {
-        long long c = (red[0] + target - 1) / target;
+    if (tid < 2) {
+        const int target = tid == 0 ? target_shared : target_stream;
+        long long c = (red[tid][0] + target - 1) / target;
         c = (c + 127) / 128 * 128;
         if (c < 256) c = 256;
         if (c > (1 << 30)) c = 1 << 30;
-        chunk_s = (int)c;
-        sched[0] = (int)c;
-        sched[1] = ng;
+        chunk_s[tid] = (int)c;
+        sched[tid == 0 ? 0 : 2] = (int)c;
     }
+    if (tid == 0) sched[1] = ng;
     __syncthreads();
-    const int chunk = chunk_s;
     // 3. splits per group -> item_start
+    auto splits = [&](int gi) {
+        const int len = group_len(gi);
+        const int chunk = chunk_s[single(gi) ? 1 : 0];
+        return len <= 0 ? 1 : (len + chunk - 1) / chunk;
+    };
     int local = 0;
     for (int i = 0; i < gper; ++i)
-        if (g0 + i < ng) {
-            const int len = group_len(g0 + i);
-            local += len <= 0 ? 1 : (len + chunk - 1) / chunk;
-        }
+        if (g0 + i < ng) local += splits(g0 + i);
     int run = inclusive_scan(local) - local;
     for (int i = 0; i < gper; ++i)
         if (g0 + i < ng) {
             item_start[g0 + i] = run;
-            const int len = group_len(g0 + i);
-            run += len <= 0 ? 1 : (len + chunk - 1) / chunk;
+            run += splits(g0 + i);
         }
     if (tid == 1023) item_start[ng] = run;
 }

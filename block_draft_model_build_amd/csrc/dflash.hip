@@ -103,8 +103,10 @@ static AttnArgs<T> attn_args(const dflash_config& c, int nb, const T* q, int64_t
 
 static hipError_t attn_schedule(const dflash_config& c, int nb, const int64_t* base, const int32_t* anchor,
                                 int64_t ctx_total, char* ws, const Workspace& w, hipStream_t st) {
+    const int hkv = c.num_kv_heads;
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, base, anchor, nb, ctx_total,
-                       attn_target_splits(c, nb), reinterpret_cast<int*>(ws + w.group_start),
+                       (kAttnItemsShared + hkv - 1) / hkv, (kAttnItemsStream + hkv - 1) / hkv,
+                       reinterpret_cast<int*>(ws + w.group_start),
                        reinterpret_cast<int*>(ws + w.item_start), reinterpret_cast<int*>(ws + w.sched));
     return hipGetLastError();
 }

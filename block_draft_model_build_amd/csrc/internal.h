@@ -14,13 +14,17 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int elem_bytes(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
-// The attention scheduler sizes splits so that about kAttnItems work items
-// (group x split x KV head) carry the prefix work: a few per compute unit, so
-// the longest-first dispatch order can balance them.
-constexpr int kAttnItems = 1024;
+// The attention scheduler sizes splits so that about kAttnItemsShared work
+// items (group x split x KV head) carry the prefix work of multi-block groups
+// (shared, cache-fed K/V tiles: long items are cheapest) and about
+// kAttnItemsStream that of single-block groups (streamed, latency-bound: more
+// items in flight help). Both were chosen by a sweep over 256..2048 items on
+// the 5-layer, long-context and ragged-cache workloads.
+constexpr int kAttnItemsShared = 256;
+constexpr int kAttnItemsStream = 1024;
 inline int attn_target_splits(const dflash_config& c, int nb) {
     (void)nb;
-    return (kAttnItems + c.num_kv_heads - 1) / c.num_kv_heads;
+    return (kAttnItemsShared + kAttnItemsStream + c.num_kv_heads - 1) / c.num_kv_heads;
 }
 
 inline int attn_qcols(const dflash_config& c) {
@@ -28,7 +32,7 @@ inline int attn_qcols(const dflash_config& c) {
 }
 
 // Workspace layout (every region 256-byte aligned):
-//   attention scheduler: group_start [nb+1], item_start [nb+1], sched [2] (i32)
+//   attention scheduler: group_start [nb+1], item_start [nb+1], sched [4] (i32)
 //   attention partials:  part_o [items_max][4][QC][D] f32, part_ml [items_max][4][QC][2] f32
 //   body: h [R][H] f32, x [R][H], qkv [R][(Hq+2Hkv)D], att [R][Hq D], u [R][I]   (dtype)
 //   ctx_proj: C [ctx_rows][H] (dtype); shares the body's space (calls are stream-ordered).
@@ -50,7 +54,7 @@ inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_ro
     size_t off = 0;
     w.group_start = off; off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
     w.item_start = off;  off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
-    w.sched = off;       off = align_up(off + sizeof(int) * 2, A);
+    w.sched = off;       off = align_up(off + sizeof(int) * 4, A);
     w.part_o = off;      off = align_up(off + sizeof(float) * parts * qc * D, A);
     w.part_ml = off;     off = align_up(off + sizeof(float) * parts * qc * 2, A);
     const size_t shared0 = off;

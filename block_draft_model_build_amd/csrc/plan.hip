@@ -7,13 +7,10 @@
 // the anchor plus gamma draft positions; the loss mask leaves out the anchor
 // and invalid positions.
 //
-// One workgroup (1024 threads) per batch row. Every eligible position gets a
-// 64-bit SplitMix64 key; the N smallest keys are found with an 8-pass radix
-// select (8-bit digits, histogram in LDS), the keys being recomputed in every
-// pass instead of stored, so nothing but a 256-bin histogram lives in LDS at
-// any sequence length. Equal keys are broken by position. A block-wide scan
-// over contiguous position ranges then writes the chosen anchors in ascending
-// order.
+// One workgroup (1024 threads) per batch row; the row's eligibility bitmask
+// lives in LDS (rows up to 524288 positions). Every eligible position gets a
+// 64-bit SplitMix64 key, recomputed where needed instead of stored; see
+// plan_kernel for the selection.
 #include "common.h"
 #include "internal.h"
 
@@ -27,114 +24,176 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 }
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxWords = 16384;      // rows up to 32 * 16384 positions keep their bitmask in LDS
+constexpr int kPlanBins = 4096;           // 12-bit digits
+constexpr int kPlanMaxCand = 2048;        // keys of the threshold bin ranked exactly
 
-// Inclusive block scan of one int per thread.
-__device__ int block_inclusive_scan(int v, int* buf) {
-    const int tid = threadIdx.x;
-    buf[tid] = v;
-    __syncthreads();
-    for (int w = 1; w < kPlanThreads; w <<= 1) {
-        int add = tid >= w ? buf[tid - w] : 0;
-        __syncthreads();
-        buf[tid] += add;
-        __syncthreads();
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & 63;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
     }
-    int r = buf[tid];
-    __syncthreads();
-    return r;
+    return v;
 }
 
+// Inclusive block scan of one int per thread: lane shuffles inside each wave,
+// then a shuffle scan of the 16 wave totals. buf holds >= 32 ints.
+__device__ int block_inclusive_scan(int v, int* buf) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = wave_inclusive_scan(v);
+    if (lane == 63) buf[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < kPlanThreads / 64 ? buf[lane] : 0;
+        t = wave_inclusive_scan(t);
+        if (lane < kPlanThreads / 64) buf[kPlanThreads / 64 + lane] = t;
+    }
+    __syncthreads();
+    if (w > 0) incl += buf[kPlanThreads / 64 + w - 1];
+    __syncthreads();
+    return incl;
+}
+
+// Selection: keys of one row are distinct (the SplitMix64 finaliser is a
+// bijection and row_key ^ a differs for every a), so the anchors are exactly
+// the eligible positions whose key is <= the n-th smallest key. That key's
+// leading bits are found with 12-bit-digit histograms (one sweep when the row
+// is not huge), the keys sharing its bin are ranked exactly, and the chosen
+// positions are compacted in ascending order from a bitmask in LDS.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const uint8_t* __restrict__ mask, int S, const int64_t* __restrict__ sample_ids, uint64_t step,
     uint64_t seed, int N, int bs, int32_t* anchors, int32_t* positions, uint8_t* valid,
     uint8_t* loss_mask, int32_t* num_anchors, int64_t* block_ctx_base) {
-    __shared__ unsigned hist[256];
-    __shared__ int scanbuf[kPlanThreads];
-    __shared__ uint64_t sel_prefix;
-    __shared__ int sel_need;
+    __shared__ uint32_t bits[kPlanMaxWords];          // eligible, then chosen
+    __shared__ unsigned hist[kPlanBins];
+    __shared__ unsigned long long cand_key[kPlanMaxCand];
+    __shared__ int cand_pos[kPlanMaxCand];
+    __shared__ int scanbuf[2 * kPlanThreads / 64];
+    __shared__ int s_int[4];                          // [0] count, [1] need, [2] threshold bin, [3] candidates
 
     const int b = blockIdx.x, tid = threadIdx.x;
     const uint8_t* m = mask + (int64_t)b * S;
     const uint64_t rk = splitmix64(splitmix64(splitmix64(seed) ^ (uint64_t)sample_ids[b]) ^ step);
-    const int P = S > 1 ? S - 1 : 0;                     // candidate positions 0..S-2
-    const int per = (P + kPlanThreads - 1) / kPlanThreads;
-    const int p0 = tid * per, p1 = min(P, p0 + per);
-    auto eligible = [&](int a) { return m[a] != 0 && m[a + 1] != 0; };
+    const int P = S > 1 ? S - 1 : 0;                  // candidate anchors 0..S-2
+    const int words = (P + 31) / 32;
 
+    // 1. Eligibility bits: a is eligible when mask[a] and mask[a + 1] are set.
     int cnt = 0;
-    for (int a = p0; a < p1; ++a) cnt += eligible(a) ? 1 : 0;
-    const int total = block_inclusive_scan(cnt, scanbuf);
-    int elig_count;
-    {
-        if (tid == kPlanThreads - 1) sel_need = total;
-        __syncthreads();
-        elig_count = sel_need;
-        __syncthreads();
+    for (int w = tid; w < words; w += kPlanThreads) {
+        const int a0 = w * 32;
+        uint8_t v[33];
+#pragma unroll
+        for (int i = 0; i < 33; ++i) v[i] = a0 + i < S ? m[a0 + i] : 0;
+        uint32_t x = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x |= (uint32_t)((v[i] != 0) & (v[i + 1] != 0) & (a0 + i < P)) << i;
+        bits[w] = x;
+        cnt += __popc(x);
     }
-    const int n = min(N, elig_count);
+    if (tid == 0) s_int[0] = 0;
+    __syncthreads();
+    atomicAdd(&s_int[0], cnt);
+    __syncthreads();
+    const int n = min(N, s_int[0]);
+    const bool take_all = n == s_int[0];
 
-    // Radix select: the n-th smallest key (when n < #eligible).
-    uint64_t prefix = 0, pmask = 0;
+    // 2. Leading bits of the n-th smallest key (skipped when every eligible
+    //    position is taken or none is asked for).
+    unsigned long long prefix = 0, pmask = 0;
     int need = n;
-    const bool take_all = (n == elig_count);
     if (!take_all && n > 0) {
-        for (int digit = 7; digit >= 0; --digit) {
-            for (int i = tid; i < 256; i += kPlanThreads) hist[i] = 0;
+        const int shifts[6] = {52, 40, 28, 16, 4, 0};
+        const int widths[6] = {12, 12, 12, 12, 12, 4};
+        for (int lvl = 0; lvl < 6; ++lvl) {
+            const int sh = shifts[lvl];
+            const unsigned dm = (1u << widths[lvl]) - 1u;
+            for (int i = tid; i < kPlanBins; i += kPlanThreads) hist[i] = 0;
             __syncthreads();
-            const int sh = digit * 8;
-            for (int a = p0; a < p1; ++a) {
-                if (!eligible(a)) continue;
-                const uint64_t key = splitmix64(rk ^ (uint64_t)a);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & 255u], 1u);
-            }
-            __syncthreads();
-            if (tid == 0) {
-                int before = 0, bk = 0;
-                for (bk = 0; bk < 256; ++bk) {
-                    if (before + (int)hist[bk] >= need) break;
-                    before += hist[bk];
+            for (int w = tid; w < words; w += kPlanThreads) {
+                const uint32_t x = bits[w];
+#pragma unroll 8
+                for (int i = 0; i < 32; ++i) {
+                    const unsigned long long key = splitmix64(rk ^ (uint64_t)(w * 32 + i));
+                    if (((x >> i) & 1u) && (key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
                 }
-                sel_need = need - before;
-                sel_prefix = prefix | ((uint64_t)bk << sh);
             }
             __syncthreads();
-            need = sel_need;
-            prefix = sel_prefix;
-            pmask |= (uint64_t)255 << sh;
+            // Scan of the bins: thread t owns bins [4t, 4t + 4).
+            unsigned hb[4];
+            int own = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { hb[j] = hist[4 * tid + j]; own += (int)hb[j]; }
+            const int incl = block_inclusive_scan(own, scanbuf);
+            int run = incl - own;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < need && run + (int)hb[j] >= need) {
+                    s_int[1] = need - run;
+                    s_int[2] = 4 * tid + j;
+                    s_int[3] = (int)hb[j];
+                }
+                run += (int)hb[j];
+            }
             __syncthreads();
+            need = s_int[1];
+            prefix |= (unsigned long long)s_int[2] << sh;
+            pmask |= (unsigned long long)dm << sh;
+            const int in_bin = s_int[3];
+            __syncthreads();
+            if (in_bin <= kPlanMaxCand) break;
+        }
+        // 3. Keep keys below the bin; collect the bin's keys and rank them exactly.
+        if (tid == 0) s_int[3] = 0;
+        __syncthreads();
+        for (int w = tid; w < words; w += kPlanThreads) {
+            const uint32_t x = bits[w];
+            uint32_t keep = 0;
+#pragma unroll 8
+            for (int i = 0; i < 32; ++i) {
+                if (!((x >> i) & 1u)) continue;
+                const unsigned long long key = splitmix64(rk ^ (uint64_t)(w * 32 + i));
+                const unsigned long long top = key & pmask;
+                if (top < prefix) {
+                    keep |= 1u << i;
+                } else if (top == prefix) {
+                    const int c = atomicAdd(&s_int[3], 1);
+                    if (c < kPlanMaxCand) { cand_key[c] = key; cand_pos[c] = w * 32 + i; }
+                }
+            }
+            bits[w] = keep;
+        }
+        __syncthreads();
+        const int nc = min(s_int[3], kPlanMaxCand);
+        for (int i = tid; i < nc; i += kPlanThreads) {
+            int rank = 0;
+            for (int j = 0; j < nc; ++j)
+                rank += (cand_key[j] < cand_key[i] || (cand_key[j] == cand_key[i] && cand_pos[j] < cand_pos[i])) ? 1 : 0;
+            if (rank < need) atomicOr(&bits[cand_pos[i] >> 5], 1u << (cand_pos[i] & 31));
+        }
+        __syncthreads();
+    } else if (n == 0) {
+        for (int w = tid; w < words; w += kPlanThreads) bits[w] = 0;
+        __syncthreads();
+    }
+
+    // 4. Compaction in ascending position order: thread t owns a contiguous
+    //    run of words.
+    const int wper = (words + kPlanThreads - 1) / kPlanThreads;
+    const int w0 = min(words, tid * wper), w1 = min(words, w0 + wper);
+    int mine = 0;
+    for (int w = w0; w < w1; ++w) mine += __popc(bits[w]);
+    int out_i = block_inclusive_scan(mine, scanbuf) - mine;
+    int32_t* arow = anchors + (int64_t)b * N;
+    for (int w = w0; w < w1; ++w) {
+        uint32_t x = bits[w];
+        while (x) {
+            const int i = __ffs(x) - 1;
+            x &= x - 1;
+            if (out_i < N) arow[out_i] = w * 32 + i;
+            ++out_i;
         }
     }
-    // prefix = threshold key T; `need` keys equal to T are taken, lowest positions first.
-    auto chosen_strict = [&](int a, uint64_t key) { return take_all || key < prefix; };
-
-    int eq_local = 0;
-    if (!take_all && n > 0)
-        for (int a = p0; a < p1; ++a)
-            if (eligible(a) && splitmix64(rk ^ (uint64_t)a) == prefix) ++eq_local;
-    const int eq_incl = block_inclusive_scan(eq_local, scanbuf);
-    int eq_rank = eq_incl - eq_local;
-
-    int sel_local = 0;
-    if (n > 0)
-        for (int a = p0; a < p1; ++a) {
-            if (!eligible(a)) continue;
-            const uint64_t key = take_all ? 0 : splitmix64(rk ^ (uint64_t)a);
-            if (chosen_strict(a, key)) ++sel_local;
-            else if (key == prefix) { if (eq_rank < need) ++sel_local; ++eq_rank; }
-        }
-    const int sel_incl = block_inclusive_scan(sel_local, scanbuf);
-    int out_i = sel_incl - sel_local;
-    eq_rank = eq_incl - eq_local;
-    int32_t* arow = anchors + (int64_t)b * N;
-    if (n > 0)
-        for (int a = p0; a < p1; ++a) {
-            if (!eligible(a)) continue;
-            const uint64_t key = take_all ? 0 : splitmix64(rk ^ (uint64_t)a);
-            bool take = false;
-            if (chosen_strict(a, key)) take = true;
-            else if (key == prefix) { take = eq_rank < need; ++eq_rank; }
-            if (take) arow[out_i++] = a;
-        }
     for (int i = n + tid; i < N; i += kPlanThreads) arow[i] = -1;
     if (tid == 0) num_anchors[b] = n;
     if (block_ctx_base != nullptr)
@@ -170,6 +229,7 @@ extern "C" dflash_status dflash_build_plan(const uint8_t* mask, int32_t batch, i
                                            int64_t* block_ctx_base, void* hip_stream) {
     if (batch < 0 || seq_len < 0 || anchors_per_row < 0 || block_size < 1) return DFLASH_ERR_INVALID_ARG;
     if ((int64_t)seq_len + block_size > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if (seq_len > 32 * kPlanMaxWords) return DFLASH_ERR_UNSUPPORTED;
     if (batch == 0) return DFLASH_OK;
     if (sample_ids == nullptr || num_anchors == nullptr || (seq_len > 0 && mask == nullptr))
         return DFLASH_ERR_INVALID_ARG;
