@@ -60,6 +60,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 // Key fed to MFMA row r of a 32-key slice.
 __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// Key held by accumulator element e of a lane in half h of the wave:
+// key_perm(acc_row(e, lane)) = (e & 7) + 16 (e >> 3) + 8 h. The e-dependent
+// part is a compile-time constant, so masks compare against nvalid - 8 h.
+__device__ __forceinline__ constexpr int acc_key(int e) { return (e & 7) + 16 * (e >> 3); }
 
 __device__ __forceinline__ int64_t clamp_base(int64_t b, int64_t total) { return b < 0 ? 0 : (b > total ? total : b); }
 __device__ __forceinline__ int anchor_eff(int a, int64_t base, int64_t total) {
@@ -73,8 +77,22 @@ struct AttnTile {
     static constexpr int KSTEP = Mfma<T>::KSTEP, E = Mfma<T>::E;
     static constexpr int QS = QC / 32, DS = D / 32, DK = D / KSTEP, PK = 32 / KSTEP;
     static constexpr int SUPER = 128;                 // keys per super-tile
-    static constexpr int KROW = D * EB + 16;          // bytes per K row in LDS
-    static constexpr int VROW = SUPER * EB + 16;      // bytes per V^T row in LDS
+    // bf16: unpadded 256-byte K and V^T rows whose 16-byte chunks are XOR-
+    // swizzled by (row & 15), which reads both fragment patterns without LDS
+    // bank conflicts and lets whole rows arrive by direct-to-LDS loads. fp32:
+    // rows padded by 16 bytes.
+    static constexpr bool SWZ = EB == 2;
+    static constexpr int KROW = SWZ ? D * EB : D * EB + 16;          // bytes per K row in LDS
+    static constexpr int VROW = SWZ ? SUPER * EB : SUPER * EB + 16;  // bytes per V^T row in LDS
+    static_assert(!SWZ || (D * EB == 256 && SUPER * EB == 256 && D == SUPER), "swizzled rows are 256 bytes");
+    // Byte offset of byte b of K row r, and of key `key` in V^T row d.
+    __device__ static __forceinline__ int koff(int r, int b) {
+        return r * KROW + (SWZ ? ((((b >> 4) ^ (r & 15)) << 4) | (b & 15)) : b);
+    }
+    __device__ static __forceinline__ int voff(int d, int key) {
+        const int b = key * EB;
+        return d * VROW + (SWZ ? ((((b >> 4) ^ (d & 15)) << 4) | (b & 15)) : b);
+    }
     static constexpr int KS_BYTES = SUPER * KROW;
     static constexpr int VT_BYTES = D * VROW;
     static constexpr int STAGE = KS_BYTES + VT_BYTES;
@@ -133,9 +151,10 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
     for (int qs = 0; qs < QS; ++qs) {
         float mx = NEG_INF;
         if (nvalid < 32) {
+            const int nv = nvalid - 8 * h;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                if (key_perm(acc_row(e, lane)) >= nvalid) s[qs][e] = NEG_INF;
+                if (acc_key(e) >= nv) s[qs][e] = NEG_INF;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qs][e]);
@@ -176,12 +195,13 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
         for (int ds = 0; ds < DS; ++ds) {
             frag a = getv(st, ds);
             if (nvalid < 32) {        // keys past the end: exact zeros, even if V is not finite
+                const int nv = nvalid - 8 * h;
                 if constexpr (E == 8) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        if (16 * st + 8 * h + i >= nvalid) a[i] = from_f32<T>(0.f);
+                        if (16 * st + i >= nv) a[i] = from_f32<T>(0.f);
                 } else {
-                    if (key_perm(acc_row(st, lane)) >= nvalid) a = 0.f;
+                    if (acc_key(st) >= nv) a = 0.f;
                 }
             }
 #pragma unroll
@@ -190,10 +210,11 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
     }
 }
 
-// One wave folds a 32-key slice staged in LDS (K rows at ks, V^T at vt with
-// row pitch vrow; `nvalid` visible keys) into its running softmax state.
+// One wave folds the 32-key slice starting at key0 of a tile staged in LDS
+// (K rows at ks, V^T rows at vt; `nvalid` visible keys) into its running
+// softmax state.
 template <typename T, int D, int QC>
-__device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int vrow, int nvalid,
+__device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int key0, int nvalid,
                                            const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
                                            f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
                                            float (&l)[QC / 32], int lane) {
@@ -201,17 +222,17 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int v
     typedef typename Mfma<T>::frag frag;
     constexpr int E = TT::E, EB = TT::EB;
     const int h = lane >> 5;
-    const char* krow = ks + key_perm(lane & 31) * TT::KROW + h * E * EB;
+    const int kr = key0 + key_perm(lane & 31);
     f32x16 sc[QC / 32];
-    attn_scores<T, D, QC>([&](int kk) { return *reinterpret_cast<const frag*>(krow + kk * TT::KSTEP * EB); },
-                          qf, sc);
-    const char* vbase = vt + (lane & 31) * vrow;
+    attn_scores<T, D, QC>(
+        [&](int kk) { return *reinterpret_cast<const frag*>(ks + TT::koff(kr, (kk * TT::KSTEP + h * E) * EB)); },
+        qf, sc);
     auto getv = [&](int st, int ds) -> frag {
-        const char* vr = vbase + ds * 32 * vrow;
+        const int d = ds * 32 + (lane & 31);
         if constexpr (E == 8)
-            return *reinterpret_cast<const frag*>(vr + (16 * st + 8 * h) * EB);
+            return *reinterpret_cast<const frag*>(vt + TT::voff(d, key0 + 16 * st + 8 * h));
         else
-            return *reinterpret_cast<const T*>(vr + key_perm(acc_row(st, lane)) * EB);
+            return *reinterpret_cast<const T*>(vt + TT::voff(d, key0 + acc_key(st) + 8 * h));
     };
     attn_update<T, D, QC>(sc, getv, nvalid, o, m, l, lane);
 }
@@ -253,7 +274,7 @@ __device__ __forceinline__ void attn_load_v(const T* cvg, int64_t ctx_total, int
                     for (int i = 0; i < 8; ++i) vf[st][ds][i] = key0 + k0 + i < kend ? vr[k0 + i] : from_f32<T>(0.f);
                 }
             } else {
-                const int kk = key_perm(acc_row(st, lane));
+                const int kk = acc_key(st) + 8 * h;
                 vf[st][ds] = key0 + kk < kend ? vr[kk] : 0.f;
             }
         }
@@ -361,47 +382,15 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             for (int e = 0; e < 16; ++e) o[ds][qs][e] = 0.f;
     }
 
-    // ---- split 0: the blocks' own keys. Block jj's rows go to slot jj (32 rows)
-    // of stage 0: K rotated at its anchor + k', V^T transposed; rows >= bs zero.
-    if (s == 0) {
-        char* Ks = smem;
-        char* Vt = smem + TT::KS_BYTES;
-        for (int idx = tid; idx < ng * 32 * (D / 2); idx += 256) {
-            const int jj = idx / (32 * (D / 2)), r = idx - jj * 32 * (D / 2);
-            const int k = r / (D / 2), i = r - k * (D / 2);
-            const int aj = anchor_eff(p.anchor[n0 + jj], base, p.ctx_total);
-            float y1 = 0.f, y2 = 0.f;
-            if (k < bs && aj >= 0) {
-                const T* kr = p.kb + (int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D;
-                const float x1 = to_f32(kr[i]), x2 = to_f32(kr[i + D / 2]);
-                float cs, sn;
-                rope_cs(p.rt, i, aj + k, cs, sn);
-                y1 = x1 * cs - x2 * sn;
-                y2 = x2 * cs + x1 * sn;
-            }
-            char* kd = Ks + (jj * 32 + k) * TT::KROW;
-            *reinterpret_cast<T*>(kd + i * EB) = from_f32<T>(y1);
-            *reinterpret_cast<T*>(kd + (i + D / 2) * EB) = from_f32<T>(y2);
-        }
-        for (int idx = tid; idx < ng * 32 * D; idx += 256) {
-            const int jj = idx / (32 * D), r = idx - jj * 32 * D;
-            const int k = r / D, d = r - k * D;
-            const int aj = p.anchor[n0 + jj];
-            T v = from_f32<T>(0.f);
-            if (k < bs && aj >= 0) v = p.vb[(int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D + d];
-            *reinterpret_cast<T*>(Vt + d * TT::VROW + (jj * 32 + k) * EB) = v;
-        }
-        __syncthreads();
-        if (active && phase == 0 && a >= 0)
-            attn_slice<T, D, QC>(Ks + j * 32 * TT::KROW, Vt + j * 32 * EB, TT::VROW, bs, qf, o, m, l, lane);
-        __syncthreads();
-    }
-
-    // ---- prefix super-tiles of the group, staged HBM -> registers -> LDS (2 stages)
+    // ---- context rows of the group: K rows and V^T columns [kbeg, kend_g) of the
+    // sequence's range of the caches, in 128-key super-tiles through 2 LDS stages.
     const int ntile = kend_g > kbeg ? (kend_g - kbeg + SUPER - 1) / SUPER : 0;
     const T* ckg = p.ck + ((int64_t)g * p.ctx_total + base) * D;
     const T* cvg = p.cvt + (int64_t)g * D * p.ctx_total + base;
+    const int64_t lim = p.ctx_total - base;          // keys of this range present in the caches
     u32x4 rk[TT::KLD], rv[TT::VLD];
+    // Register path: K rows past the group's end repeat its last row, V^T keys
+    // past it are zero, so nothing outside [0, kend_g) is read.
     auto gload = [&](int t0) {
         // K: chunk c = tid + 256 i -> key c / 16, 16-byte column c % 16
 #pragma unroll
@@ -411,8 +400,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             key = key < kend_g ? key : kend_g - 1;
             rk[i] = *reinterpret_cast<const u32x4*>(ckg + (int64_t)key * D + (c % TT::KCH) * EC);
         }
-        // V^T: chunk c -> row d = c / VCH, keys t0 + (c % VCH) * EC ..; keys at or past
-        // the group's end are zero (they meet P = 0 and must stay finite).
+        // V^T: chunk c -> row d = c / VCH, keys t0 + (c % VCH) * EC ..
 #pragma unroll
         for (int i = 0; i < TT::VLD; ++i) {
             const int c = tid + 256 * i;
@@ -435,14 +423,80 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
 #pragma unroll
         for (int i = 0; i < TT::KLD; ++i) {
             const int c = tid + 256 * i;
-            *reinterpret_cast<u32x4*>(Ks + (c / TT::KCH) * TT::KROW + (c % TT::KCH) * 16) = rk[i];
+            *reinterpret_cast<u32x4*>(Ks + TT::koff(c / TT::KCH, (c % TT::KCH) * 16)) = rk[i];
         }
 #pragma unroll
         for (int i = 0; i < TT::VLD; ++i) {
             const int c = tid + 256 * i;
-            *reinterpret_cast<u32x4*>(Vt + (c / TT::VCH) * TT::VROW + (c % TT::VCH) * 16) = rv[i];
+            *reinterpret_cast<u32x4*>(Vt + TT::voff(c / TT::VCH, (c % TT::VCH) * EC)) = rv[i];
         }
     };
+    // Direct-to-LDS path (bf16, tiles inside the cache range): each wave moves
+    // 32 K rows and 32 V^T rows, 4 rows of 256 bytes per instruction; lane i
+    // lands at physical chunk i % 16 of row i / 16, so it fetches the logical
+    // chunk (i % 16) ^ (row & 15). Keys past the group's end are read as they
+    // are: scores there are masked and V there is zeroed before use.
+    auto tile_dma_ok = [&](int t0) { return TT::SWZ && (int64_t)t0 + SUPER <= lim; };
+    auto issue_dma = [&](int t0, int stage) {
+        if constexpr (TT::SWZ) {
+            char* Ks = smem + stage * TT::STAGE;
+            char* Vt = Ks + TT::KS_BYTES;
+            const int rsub = lane >> 4, pc = lane & 15;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int R = wave * 32 + i * 4, r = R + rsub;
+                const T* src = ckg + (int64_t)(t0 + r) * D + (pc ^ (r & 15)) * EC;
+                __builtin_amdgcn_global_load_lds(DFLASH_GPTR(src), DFLASH_LPTR(Ks + R * TT::KROW), 16, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int R = wave * 32 + i * 4, d = R + rsub;
+                const T* src = cvg + (int64_t)d * p.ctx_total + t0 + (pc ^ (d & 15)) * EC;
+                __builtin_amdgcn_global_load_lds(DFLASH_GPTR(src), DFLASH_LPTR(Vt + R * TT::VROW), 16, 0, 0);
+            }
+        }
+    };
+
+    // bf16 stages the first tile while the blocks' own keys are processed
+    // (they use stage 1); fp32 stages its tiles from registers below.
+    constexpr int OWN = TT::SWZ ? 1 : 0;
+    if constexpr (!STREAM && TT::SWZ) {
+        if (ntile > 0 && tile_dma_ok(kbeg)) issue_dma(kbeg, 0);
+    }
+
+    // ---- split 0: the blocks' own keys. Block jj's rows go to slot jj (32 rows)
+    // of stage OWN: K rotated at its anchor + k', V^T transposed; rows >= bs zero.
+    if (s == 0) {
+        char* Ks = smem + OWN * TT::STAGE;
+        char* Vt = Ks + TT::KS_BYTES;
+        for (int idx = tid; idx < ng * 32 * (D / 2); idx += 256) {
+            const int jj = idx / (32 * (D / 2)), r = idx - jj * 32 * (D / 2);
+            const int k = r / (D / 2), i = r - k * (D / 2);
+            const int aj = anchor_eff(p.anchor[n0 + jj], base, p.ctx_total);
+            float y1 = 0.f, y2 = 0.f;
+            if (k < bs && aj >= 0) {
+                const T* kr = p.kb + (int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D;
+                const float x1 = to_f32(kr[i]), x2 = to_f32(kr[i + D / 2]);
+                float cs, sn;
+                rope_cs(p.rt, i, aj + k, cs, sn);
+                y1 = x1 * cs - x2 * sn;
+                y2 = x2 * cs + x1 * sn;
+            }
+            *reinterpret_cast<T*>(Ks + TT::koff(jj * 32 + k, i * EB)) = from_f32<T>(y1);
+            *reinterpret_cast<T*>(Ks + TT::koff(jj * 32 + k, (i + D / 2) * EB)) = from_f32<T>(y2);
+        }
+        for (int idx = tid; idx < ng * 32 * D; idx += 256) {
+            const int jj = idx / (32 * D), r = idx - jj * 32 * D;
+            const int k = r / D, d = r - k * D;
+            const int aj = p.anchor[n0 + jj];
+            T v = from_f32<T>(0.f);
+            if (k < bs && aj >= 0) v = p.vb[(int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D + d];
+            *reinterpret_cast<T*>(Vt + TT::voff(d, jj * 32 + k)) = v;
+        }
+        __syncthreads();
+        if (active && phase == 0 && a >= 0) attn_slice<T, D, QC>(Ks, Vt, j * 32, bs, qf, o, m, l, lane);
+        __syncthreads();
+    }
 
     if constexpr (STREAM) {
         // One block: the 4 waves take interleaved 32-key slices and stream them
@@ -465,29 +519,55 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             }
         }
     }
-    if constexpr (!STREAM) {
-    if (ntile > 0) {
-        gload(kbeg);
-        lstore(0);
-        if (ntile > 1) gload(kbeg + SUPER);
-    }
-    for (int t = 0; t < ntile; ++t) {
-        __syncthreads();
-        if (t + 1 < ntile) lstore((t + 1) & 1);
-        if (t + 2 < ntile) gload(kbeg + (t + 2) * SUPER);
+    // One tile of this wave's block: its slices phase, phase + wpb, ...
+    auto tile_compute = [&](int t) {
         if (active && a >= 0) {
             const char* Ks = smem + (t & 1) * TT::STAGE;
             const char* Vt = Ks + TT::KS_BYTES;
             for (int sl = phase; sl < SUPER / 32; sl += wpb) {
                 const int nvalid = kend - (kbeg + t * SUPER + sl * 32);
                 if (nvalid > 0)
-                    attn_slice<T, D, QC>(Ks + sl * 32 * TT::KROW, Vt + sl * 32 * EB, TT::VROW,
-                                         nvalid < 32 ? nvalid : 32, qf, o, m, l, lane);
+                    attn_slice<T, D, QC>(Ks, Vt, sl * 32, nvalid < 32 ? nvalid : 32, qf, o, m, l, lane);
             }
         }
+    };
+    if constexpr (!STREAM && TT::SWZ) {
+        // Tile t + 1 is staged into the other stage while tile t is computed:
+        // by DMA when it lies inside the cache range, else (a tile crossing the
+        // end of the caches) through registers after this tile's work.
+        if (ntile > 0 && !tile_dma_ok(kbeg)) {
+            gload(kbeg);
+            lstore(0);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int t = 0; t < ntile; ++t) {
+            const int t1 = kbeg + (t + 1) * SUPER;
+            const bool next = t + 1 < ntile;
+            const bool dma = next && tile_dma_ok(t1);
+            if (dma) issue_dma(t1, (t + 1) & 1);
+            tile_compute(t);
+            if (next && !dma) {
+                gload(t1);
+                lstore((t + 1) & 1);
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
     }
-
-    }  // !STREAM
+    if constexpr (!STREAM && !TT::SWZ) {
+        if (ntile > 0) {
+            gload(kbeg);
+            lstore(0);
+            if (ntile > 1) gload(kbeg + SUPER);
+        }
+        for (int t = 0; t < ntile; ++t) {
+            __syncthreads();
+            if (t + 1 < ntile) lstore((t + 1) & 1);
+            if (t + 2 < ntile) gload(kbeg + (t + 2) * SUPER);
+            tile_compute(t);
+        }
+    }
 
     // ---- merge the waves serving one block (tree over phases), via LDS
 #pragma unroll
@@ -577,56 +657,58 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     }
 }
 
-// Merge the splits of every group whose prefix was split, in split order:
+// Merge the splits of a block whose group's prefix was split, in split order:
 // per query column the global max and 1/sum first, then every output element
-// as one weighted sum over the splits.
+// as one weighted sum over the splits. One workgroup per (block, KV head).
 template <typename T, int D, int QC>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
     constexpr int MAXF = 32;                       // splits whose weights are kept in LDS
     __shared__ float s_mu[QC], s_inv[QC];
     __shared__ float s_f[MAXF][QC];
-    const int gi = blockIdx.x, g = blockIdx.y;
-    if (gi >= p.sched[1]) return;
+    // One workgroup per (block, KV head): locate the block's group.
+    const int n = blockIdx.x, g = blockIdx.y;
+    const int ngroups = p.sched[1];
+    int lo = 0, hi = ngroups;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.group_start[mid] <= n) lo = mid; else hi = mid;
+    }
+    const int gi = lo;
     const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
-    if (nsplit <= 1) return;
-    const int n0 = p.group_start[gi], ng = p.group_start[gi + 1] - n0;
+    if (nsplit <= 1 || p.anchor[n] < 0) return;
+    const int j = n - p.group_start[gi];
     const int G = p.hq / p.hkv, bs = p.bs, qcols = bs * G;
     const int tid = threadIdx.x;
-    auto part = [&](int s, int j) -> int64_t {
+    auto part = [&](int s) -> int64_t {
         return ((int64_t)(p.item_start[gi] + s) * p.hkv + g) * kMaxGroup + j;
     };
-    for (int j = 0; j < ng; ++j) {
-        const int n = n0 + j;
-        if (p.anchor[n] < 0) continue;
-        for (int c = tid; c < qcols; c += 256) {
-            float mx = -__builtin_inff();
-            for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.part_ml[(part(s, j) * QC + c) * 2]);
-            const float mu = (mx == -__builtin_inff()) ? 0.f : mx;
-            float L = 0.f;
-            for (int s = 0; s < nsplit; ++s) {
-                const float f = fast_exp2(p.part_ml[(part(s, j) * QC + c) * 2] - mu);
-                if (s < MAXF) s_f[s][c] = f;
-                L += p.part_ml[(part(s, j) * QC + c) * 2 + 1] * f;
-            }
-            s_mu[c] = mu;
-            s_inv[c] = 1.f / L;
+    for (int c = tid; c < qcols; c += 256) {
+        float mx = -__builtin_inff();
+        for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.part_ml[(part(s) * QC + c) * 2]);
+        const float mu = (mx == -__builtin_inff()) ? 0.f : mx;
+        float L = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const float f = fast_exp2(p.part_ml[(part(s) * QC + c) * 2] - mu);
+            if (s < MAXF) s_f[s][c] = f;
+            L += p.part_ml[(part(s) * QC + c) * 2 + 1] * f;
         }
-        __syncthreads();
-        for (int idx = tid; idx < qcols * (D / 4); idx += 256) {
-            const int c = idx / (D / 4), d = (idx - c * (D / 4)) * 4;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < nsplit; ++s) {
-                const float f = s < MAXF ? s_f[s][c] : fast_exp2(p.part_ml[(part(s, j) * QC + c) * 2] - s_mu[c]);
-                const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + (part(s, j) * QC + c) * D + d);
-                acc += v * f;
-            }
-            const int k = c % bs, hh = c / bs, row = n * bs + k;
-            const bool keep = p.valid[row] != 0;
-            T* o = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D + d;
+        s_mu[c] = mu;
+        s_inv[c] = 1.f / L;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < qcols * (D / 4); idx += 256) {
+        const int c = idx / (D / 4), d = (idx - c * (D / 4)) * 4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nsplit; ++s) {
+            const float f = s < MAXF ? s_f[s][c] : fast_exp2(p.part_ml[(part(s) * QC + c) * 2] - s_mu[c]);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + (part(s) * QC + c) * D + d);
+            acc += v * f;
+        }
+        const int k = c % bs, hh = c / bs, row = n * bs + k;
+        const bool keep = p.valid[row] != 0;
+        T* o = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D + d;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(keep ? acc[e] * s_inv[c] : 0.f);
-        }
-        __syncthreads();
+        for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(keep ? acc[e] * s_inv[c] : 0.f);
     }
 }
 

@@ -16,6 +16,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+
+// Address-space casts for the direct-to-LDS loads (global_load_lds_dwordx4:
+// lane i of the wave writes its 16 bytes to LDS at M0 base + 16 i).
+#define DFLASH_GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define DFLASH_LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (LDS and export counters left unconstrained).
+template <int n> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 constexpr int kMaxLayers = 16;
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -241,15 +241,7 @@ template <typename T> struct EpCtxKV {
 };
 
 // ---------------------------------------------------------------- kernel
-#define DFLASH_GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
-#define DFLASH_LPTR(p) ((void __attribute__((address_space(3)))*)(p))
 
-// s_waitcnt immediate that waits until at most n vector-memory operations are
-// outstanding (LDS and export counters left unconstrained).
-template <int n> __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // 16-byte chunk swizzle of the LDS rows: row r keeps logical chunk c at
 // physical chunk c ^ swz(r). Chosen by measuring LDS bank conflicts of the
