@@ -160,6 +160,57 @@ def step_roofline_ms(counts, dtype):
     return tot * 1e3
 
 
+# ----------------------------------------------------------------------------- steps next to the path
+def time_call(torch, fn, reps=10):
+    fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def next_rows(d, torch, device="cuda"):
+    """Time the steps around the body at the inference shape (64 requests,
+    gamma + 1 = 16 verified positions each, the 5-layer dimensions):
+    ctx_append = one cycle's projection of 1024 newly verified target states into
+    every layer's context cache (scattered rows), with its MFMA roofline."""
+    import math as _m
+    from dflash_synth import WORKLOADS, Rng, layer_weights
+    w = WORKLOADS["c5"]
+    cfg = d.config_from_workload(w)
+    out = {}
+    R, g1, cap = w.batch, w.block_size, 2048
+    rows = R * g1
+    K = w.num_target_layers * w.target_hidden
+    rng = Rng(2024, device)
+    X = rng.normal("append.states", (rows, K))
+    w_proj = rng.normal("append.w_proj", (w.hidden, K), std=1 / _m.sqrt(K))
+    layers = [layer_weights(w, rng, l) for l in range(w.num_layers)]
+    total = R * cap
+    ck = [torch.empty((w.num_kv_heads, total, w.head_dim), dtype=torch.bfloat16, device=device)
+          for _ in range(w.num_layers)]
+    cv = [torch.empty((w.num_kv_heads, w.head_dim, total), dtype=torch.bfloat16, device=device)
+          for _ in range(w.num_layers)]
+    lens = rng.integers("append.len", 0, cap - g1, (R,))
+    j = torch.arange(g1, device=device)
+    pos = (lens[:, None] + j[None, :]).reshape(-1).to(torch.int32)
+    dst = (torch.arange(R, device=device)[:, None] * cap + lens[:, None] + j[None, :]).reshape(-1)
+    ws = torch.empty(d.dflash_workspace_size(cfg, 0, rows), dtype=torch.uint8, device=device)
+    ms = time_call(torch, lambda: d.dflash_ctx_append(cfg, X, K, w.target_hidden, rows, pos, dst, w_proj,
+                                                      layers, ck, cv, total, ws))
+    flops = 2.0 * rows * w.hidden * K + 2.0 * rows * (w.num_layers * 2 * w.num_kv_heads * w.head_dim) * w.hidden
+    ach = flops / (ms / 1e3) / 1e12
+    out["ctx_append"] = {"rows": rows, "ms": round(ms, 4), "rows_per_s": round(rows / (ms / 1e3), 1),
+                         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_TFLOPS["bf16"],
+                                      "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
+    del ck, cv
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU oracle sample
 def cpu_baseline(w, runner, anchors, budget_rows=None, budget_blocks=None):
     """The fp64 oracle on a bounded sample of the workload, scaled to block positions/s.
@@ -243,6 +294,7 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the steps next to the path")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}).",
@@ -320,6 +372,9 @@ def main():
                           "model": "sum over kernels of max(flops / MFMA peak, bytes / HBM peak)"},
         "kernel_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
     }
+    if not args.no_next:
+        log("timing the steps next to the path (inference shape)")
+        result["next_rows"] = next_rows(d, torch)
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")
         budgets = {"c1": (128, 4), "c2": (8192, 32), "c3": (8192, 48), "c4": (4096, 12), "c5": (None, 24)}

@@ -6,8 +6,9 @@ are torch tensors used as device buffers (their data pointers are passed);
 the stream defaults to torch's current stream on the tensor's device.
 
 The names mirror the C entry points:
-  dflash_build_plan, dflash_ctx_proj, dflash_block_attn, dflash_body_forward,
-  dflash_workspace_size, dflash_check_config, dflash_status_string.
+  dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_truncate,
+  dflash_block_attn, dflash_body_forward, dflash_workspace_size,
+  dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
 that fails, importing this package raises ImportError. There is no fallback.
@@ -24,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 DFLASH_OK, DFLASH_ERR_INVALID_ARG, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP = range(5)
 DFLASH_F32, DFLASH_BF16 = 0, 1
 
-EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_block_attn", "dflash_body_forward",
+EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_truncate",
+            "dflash_block_attn", "dflash_body_forward",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
@@ -67,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.dflash_build_plan.restype = ctypes.c_int
     lib.dflash_ctx_proj.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, I64, I64, P, SZ, P]
     lib.dflash_ctx_proj.restype = ctypes.c_int
+    lib.dflash_ctx_append.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, P, I64, P, SZ, P]
+    lib.dflash_ctx_append.restype = ctypes.c_int
+    lib.dflash_ctx_truncate.argtypes = [P, P, I32, P]
+    lib.dflash_ctx_truncate.restype = ctypes.c_int
     lib.dflash_block_attn.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, SZ, P]
     lib.dflash_block_attn.restype = ctypes.c_int
     lib.dflash_body_forward.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, SZ, P]
@@ -190,6 +196,25 @@ def dflash_ctx_proj(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_lay
                              ck, cv, int(ctx_total), int(row_offset), wp, wb,
                              _stream(stream, target_states))
     _check("dflash_ctx_proj", s)
+
+
+def dflash_ctx_append(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
+                      num_rows: int, positions, dst_rows, w_proj, layers, ctx_k: List, ctx_v: List,
+                      ctx_total: int, workspace, stream=None) -> None:
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_ctx_append(ctypes.byref(cfg), _ptr(target_states), int(ts_row_stride),
+                               int(ts_layer_stride), int(num_rows), _ptr(positions), _ptr(dst_rows),
+                               _ptr(w_proj), lw, ck, cv, int(ctx_total), wp, wb,
+                               _stream(stream, target_states))
+    _check("dflash_ctx_append", s)
+
+
+def dflash_ctx_truncate(lengths, keep, n: int = None, stream=None) -> None:
+    n = lengths.numel() if n is None else n
+    s = _lib.dflash_ctx_truncate(_ptr(lengths), _ptr(keep), int(n), _stream(stream, lengths))
+    _check("dflash_ctx_truncate", s)
 
 
 def dflash_block_attn(cfg: DFlashConfig, num_blocks: int, q, k_blk, v_blk, ctx_k, ctx_v,

@@ -116,7 +116,7 @@ template <typename T>
 static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, int64_t ls, int64_t rows,
                              const int32_t* positions, const T* w_proj, const dflash_layer_weights* layers,
                              void* const* ck, void* const* cv, int64_t ctx_total, int64_t row_offset,
-                             char* ws, hipStream_t st) {
+                             const int64_t* dst_rows, char* ws, hipStream_t st) {
     const Workspace w = workspace_layout(c, 0, rows);
     T* C = reinterpret_cast<T*>(ws + w.c);
     const int H = c.hidden, K = c.num_target_layers * c.target_hidden;
@@ -135,6 +135,7 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     b.hkvd = c.num_kv_heads * c.head_dim;
     b.ld = H;
     ep.positions = positions;
+    ep.dst_rows = dst_rows;
     ep.ctx_total = ctx_total;
     ep.row_offset = row_offset;
     ep.hkv = c.num_kv_heads;
@@ -276,12 +277,65 @@ extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* t
     if (cfg->dtype == DFLASH_BF16)
         e = ctx_proj_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
                                num_rows, positions, static_cast<const __bf16*>(w_proj), layers, ctx_k, ctx_v,
-                               ctx_total, row_offset, ws, st);
+                               ctx_total, row_offset, nullptr, ws, st);
     else
         e = ctx_proj_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
                               num_rows, positions, static_cast<const float*>(w_proj), layers, ctx_k, ctx_v,
-                              ctx_total, row_offset, ws, st);
+                              ctx_total, row_offset, nullptr, ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_ctx_append(const dflash_config* cfg, const void* target_states,
+                                           int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                           const int32_t* positions, const int64_t* dst_rows, const void* w_proj,
+                                           const dflash_layer_weights* layers, void* const* ctx_k,
+                                           void* const* ctx_v, int64_t ctx_total, void* workspace,
+                                           size_t workspace_bytes, void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (num_rows < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
+    if (num_rows > INT32_MAX / 2) return DFLASH_ERR_UNSUPPORTED;
+    if (num_rows == 0) return DFLASH_OK;
+    const int64_t vec = 16 / elem_bytes(*cfg);
+    if (target_states == nullptr || positions == nullptr || dst_rows == nullptr || w_proj == nullptr ||
+        layers == nullptr || ctx_k == nullptr || ctx_v == nullptr || !aligned16(target_states) ||
+        !aligned16(w_proj) || ts_row_stride <= 0 || ts_layer_stride < 0 || ts_row_stride % vec != 0 ||
+        ts_layer_stride % vec != 0)
+        return DFLASH_ERR_INVALID_ARG;
+    for (int l = 0; l < cfg->num_layers; ++l)
+        if (layers[l].wk == nullptr || layers[l].wv == nullptr || ctx_k[l] == nullptr || ctx_v[l] == nullptr ||
+            !aligned16(layers[l].wk) || !aligned16(layers[l].wv))
+            return DFLASH_ERR_INVALID_ARG;
+    if ((s = ws_check(cfg, 0, num_rows, workspace, workspace_bytes)) != DFLASH_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e;
+    if (cfg->dtype == DFLASH_BF16)
+        e = ctx_proj_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
+                               num_rows, positions, static_cast<const __bf16*>(w_proj), layers, ctx_k, ctx_v,
+                               ctx_total, 0, dst_rows, ws, st);
+    else
+        e = ctx_proj_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
+                              num_rows, positions, static_cast<const float*>(w_proj), layers, ctx_k, ctx_v,
+                              ctx_total, 0, dst_rows, ws, st);
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+// lengths[i] = min(lengths[i], max(keep[i], 0)).
+__global__ __launch_bounds__(256) void ctx_truncate_kernel(int64_t* lengths, const int64_t* keep, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t k = keep[i] > 0 ? keep[i] : 0;
+    if (k < lengths[i]) lengths[i] = k;
+}
+
+extern "C" dflash_status dflash_ctx_truncate(int64_t* lengths, const int64_t* keep, int32_t n, void* hip_stream) {
+    if (n < 0) return DFLASH_ERR_INVALID_ARG;
+    if (n == 0) return DFLASH_OK;
+    if (lengths == nullptr || keep == nullptr) return DFLASH_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(ctx_truncate_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(hip_stream), lengths, keep, (int)n);
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
 extern "C" dflash_status dflash_block_attn(const dflash_config* cfg, int32_t num_blocks, const void* q,

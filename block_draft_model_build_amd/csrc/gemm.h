@@ -171,9 +171,16 @@ template <typename T> struct EpCtxKV {
     T* ck[kMaxLayers];
     T* cv[kMaxLayers];
     const int* positions;
+    const int64_t* dst_rows;      // cache row per GEMM row (scatter), or null: row_offset + row
     int64_t ctx_total, row_offset;
     int hkv;
     RopeTurns rt;
+    // Cache row of GEMM row `row`, or -1 when it is not to be written.
+    __device__ int64_t dst(int row) const {
+        if (dst_rows == nullptr) return row_offset + row;
+        const int64_t d = dst_rows[row];
+        return d >= 0 && d < ctx_total ? d : -1;
+    }
     template <int MI, int NI, int WN>
     __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
         constexpr int D = 256 / (int)sizeof(T);   // head rows are 256 bytes
@@ -182,7 +189,7 @@ template <typename T> struct EpCtxKV {
         static_assert(NI % (2 * pj) == 0, "a wave covers whole heads");
         typedef T T4 __attribute__((ext_vector_type(4)));
         const int hkvd = hkv * D;
-        const bool vec_ok = (row_offset & 3) == 0 && (ctx_total & 3) == 0;
+        const bool vec_ok = dst_rows == nullptr && (row_offset & 3) == 0 && (ctx_total & 3) == 0;
 #pragma unroll
         for (int q = 0; q < NI / 2; ++q) {
             const int j = (q / pj) * 2 * pj + q % pj;   // first tile of a (d, d + D/2) pair
@@ -195,7 +202,7 @@ template <typename T> struct EpCtxKV {
             const int g = rr / D;
             const int dd = rr - g * D + (lane & 31);      // in [0, D/2)
             if (is_v) {
-                T* v1 = cv[l] + ((int64_t)g * D + dd) * ctx_total + row_offset;
+                T* v1 = cv[l] + ((int64_t)g * D + dd) * ctx_total;
                 T* v2 = v1 + (int64_t)half * ctx_total;
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
@@ -209,26 +216,30 @@ template <typename T> struct EpCtxKV {
                                 a1[t] = from_f32<T>(acc[i][j][4 * eg + t]);
                                 a2[t] = from_f32<T>(acc[i][jp][4 * eg + t]);
                             }
-                            *reinterpret_cast<T4*>(v1 + r0) = a1;
-                            *reinterpret_cast<T4*>(v2 + r0) = a2;
+                            *reinterpret_cast<T4*>(v1 + row_offset + r0) = a1;
+                            *reinterpret_cast<T4*>(v2 + row_offset + r0) = a2;
                         } else {
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                if (r0 + t < M) {
-                                    v1[r0 + t] = from_f32<T>(acc[i][j][4 * eg + t]);
-                                    v2[r0 + t] = from_f32<T>(acc[i][jp][4 * eg + t]);
+                            for (int t = 0; t < 4; ++t) {
+                                const int64_t crow = r0 + t < M ? dst(r0 + t) : -1;
+                                if (crow >= 0) {
+                                    v1[crow] = from_f32<T>(acc[i][j][4 * eg + t]);
+                                    v2[crow] = from_f32<T>(acc[i][jp][4 * eg + t]);
                                 }
+                            }
                         }
                     }
             } else {
-                T* kbase = ck[l] + ((int64_t)g * ctx_total + row_offset) * D;
+                T* kbase = ck[l] + (int64_t)g * ctx_total * D;
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int row = mb + i * 32 + acc_row(e, lane);
                         if (row >= M) continue;
-                        T* o = kbase + (int64_t)row * D;
+                        const int64_t crow = dst(row);
+                        if (crow < 0) continue;
+                        T* o = kbase + crow * D;
                         const float x1 = acc[i][j][e], x2 = acc[i][jp][e];
                         float c, s;
                         rope_cs(rt, dd, positions[row], c, s);

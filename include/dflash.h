@@ -155,6 +155,53 @@ dflash_status dflash_ctx_proj(const dflash_config *cfg, const void *target_state
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * dflash_ctx_append -- incremental form of dflash_ctx_proj for multi-cycle
+ * drafting: newly verified target hidden states are projected exactly as in
+ * dflash_ctx_proj and scattered into the caches at caller-chosen rows, so
+ * requests packed in one cache can each grow by a different number of rows.
+ * [P2] "How It Works" (the context is the target's states before the anchor);
+ * [P3] "One DFlash generation cycle", cache rollback and alignment: only the
+ * verified prefix may stay in the cache, and the draft's context must stay
+ * aligned with the target's.
+ *
+ * Row r of X (same addressing as dflash_ctx_proj) goes to cache row dst_rows[r]:
+ *   ctx_k[l][g][dst_rows[r]][:] = RoPE((C Wk_l^T)[r, g*D:(g+1)*D], positions[r])
+ *   ctx_v[l][g][:][dst_rows[r]] = (C Wv_l^T)[r, g*D:(g+1)*D]
+ * Each row's values do not depend on the other rows of the call, so appending a
+ * prefix piece by piece gives the same bytes as one dflash_ctx_proj over it.
+ *
+ *   positions      device i32 [num_rows]: RoPE position of each row
+ *   dst_rows       device i64 [num_rows]: cache row of each row; rows whose
+ *                  destination lies outside [0, ctx_total) are not written
+ *                  (negative values mark padding rows). Two rows of one call
+ *                  must not share a destination.
+ *   other arguments as dflash_ctx_proj (workspace: dflash_workspace_size(cfg, 0, num_rows)).
+ * Errors: as dflash_ctx_proj; INVALID_ARG also for a null dst_rows.
+ */
+dflash_status dflash_ctx_append(const dflash_config *cfg, const void *target_states,
+                                int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                const int32_t *positions, const int64_t *dst_rows, const void *w_proj,
+                                const dflash_layer_weights *layers, void *const *ctx_k,
+                                void *const *ctx_v, int64_t ctx_total, void *workspace,
+                                size_t workspace_bytes, void *hip_stream);
+
+/*
+ * dflash_ctx_truncate -- roll per-request context lengths back after
+ * verification ([P3] "One DFlash generation cycle", cache rollback: rows of
+ * rejected positions must leave the context). Attention reads only the rows
+ * before a block's anchor, so rolling back is a change of length; the rows
+ * past the new length stay in memory unread and are overwritten by the next
+ * dflash_ctx_append.
+ *
+ *   lengths[i] = min(lengths[i], max(keep[i], 0))      for 0 <= i < n
+ *
+ *   lengths        device i64 [n], updated in place (e.g. the requests' anchors)
+ *   keep           device i64 [n]
+ * Errors: INVALID_ARG for n < 0 or null pointers (n > 0).
+ */
+dflash_status dflash_ctx_truncate(int64_t *lengths, const int64_t *keep, int32_t n, void *hip_stream);
+
+/*
  * dflash_block_attn -- one layer's dual-source block attention.
  * [P2] step 3: a block reads the target prefix before its anchor and all
  * positions of its own block, never another block; outputs are produced for

@@ -1,0 +1,185 @@
+"""Incremental context cache for multi-cycle drafting (dflash_ctx_append,
+dflash_ctx_truncate) vs a one-shot dflash_ctx_proj and vs the oracle.
+
+Pages: NeMo RL "DFlash Draft Body", How It Works (the context of a block is
+the target's projected states before its anchor); cooking-agi deep dive,
+"One DFlash generation cycle" (only the verified prefix may stay in the
+cache, and the draft's context stays aligned with the target's).
+
+Each cycle appends the target states of all gamma + 1 verified positions of
+every request in one call, then rolls each request back to its accepted
+length. Rows of rejected positions are appended with different states, so a
+row that is not overwritten later would be caught: after the last cycle
+every row below each request's length must hold exactly the bytes a one-shot
+projection of the final prefix writes (each row's values depend only on that
+row, and the GEMM's K order does not depend on the M tiling)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_draft_model_build_amd as d
+import oracle
+from dflash_synth import WORKLOADS, Rng, layer_weights, scaled
+from tests.helpers import compare, layers64, np64, oracle_cfg, tol_for, workspace
+
+pytestmark = pytest.mark.gpu
+
+SMALL = scaled(WORKLOADS["c5"], batch=3, num_target_layers=2, target_hidden=128, hidden=256,
+               num_q_heads=4, num_kv_heads=2, intermediate=512, num_layers=2, seed=91)
+TINY_F32 = scaled(WORKLOADS["c1"], seed=92)
+
+
+def _setup(w, cap, dev="cuda"):
+    rng = Rng(w.seed, dev)
+    dt = w.torch_dtype
+    K = w.num_target_layers * w.target_hidden
+    R = w.batch
+    true_states = rng.normal("true", (R, cap, K), dtype=dt)          # states of verified positions
+    wrong_states = rng.normal("wrong", (R, cap, K), dtype=dt)        # states of rejected positions
+    w_proj = rng.normal("w_proj", (w.hidden, K), std=1 / math.sqrt(K), dtype=dt)
+    layers = [layer_weights(w, rng, l) for l in range(w.num_layers)]
+    total = R * cap
+    mk = lambda: ([torch.full((w.num_kv_heads, total, w.head_dim), 7.0, dtype=dt, device=dev)
+                   for _ in range(w.num_layers)],
+                  [torch.full((w.num_kv_heads, w.head_dim, total), 7.0, dtype=dt, device=dev)
+                   for _ in range(w.num_layers)])
+    return true_states, wrong_states, w_proj, layers, total, mk
+
+
+def _run_cycles(w, cap, init, gamma, cycles, seed):
+    dev = "cuda"
+    cfg = d.config_from_workload(w)
+    true_states, wrong_states, w_proj, layers, total, mk = _setup(w, cap)
+    K = w.num_target_layers * w.target_hidden
+    R = w.batch
+    ck, cv = mk()
+    ws = workspace(d, cfg, 0, max(cap, R * (gamma + 1)), dev)
+    rng = np.random.default_rng(seed)
+    lengths = list(init)
+    # Initial prefixes with the one-shot projection.
+    for r in range(R):
+        if lengths[r] > 0:
+            pos = torch.arange(lengths[r], dtype=torch.int32, device=dev)
+            d.dflash_ctx_proj(cfg, true_states[r], K, w.target_hidden, lengths[r], pos, w_proj, layers, ck, cv, total,
+                              r * cap, ws)
+    lens_dev = torch.tensor(lengths, dtype=torch.int64, device=dev)
+    for _ in range(cycles):
+        acc = [int(x) for x in rng.integers(0, gamma + 1, size=R)]   # accepted drafts per request
+        rows, pos, dst = [], [], []
+        for r in range(R):
+            for j in range(gamma + 1):
+                p = lengths[r] + j
+                keep = j <= acc[r]                                    # verified (anchor + accepted)
+                src = true_states if keep else wrong_states
+                rows.append(src[r, min(p, cap - 1)])
+                pos.append(p)
+                dst.append(r * cap + p if p < cap else -1)            # past the capacity: dropped
+        X = torch.stack(rows).contiguous()
+        pos_t = torch.tensor(pos, dtype=torch.int32, device=dev)
+        dst_t = torch.tensor(dst, dtype=torch.int64, device=dev)
+        d.dflash_ctx_append(cfg, X, K, w.target_hidden, X.shape[0], pos_t, dst_t, w_proj, layers, ck, cv, total, ws)
+        opt = torch.tensor([min(lengths[r] + gamma + 1, cap) for r in range(R)], dtype=torch.int64,
+                           device=dev)
+        lens_dev.copy_(opt)                                           # optimistic length after append
+        keep_t = torch.tensor([lengths[r] + acc[r] + 1 for r in range(R)], dtype=torch.int64, device=dev)
+        d.dflash_ctx_truncate(lens_dev, keep_t)
+        lengths = [min(lengths[r] + acc[r] + 1, cap) for r in range(R)]
+    torch.cuda.synchronize()
+    assert lens_dev.cpu().tolist() == lengths
+    # One-shot reference over the final prefixes.
+    rk, rv = mk()
+    for r in range(R):
+        if lengths[r] > 0:
+            p = torch.arange(lengths[r], dtype=torch.int32, device=dev)
+            d.dflash_ctx_proj(cfg, true_states[r], K, w.target_hidden, lengths[r], p, w_proj, layers, rk, rv, total,
+                              r * cap, ws)
+    torch.cuda.synchronize()
+    return dict(cfg=cfg, ck=ck, cv=cv, rk=rk, rv=rv, lengths=lengths, cap=cap, total=total, layers=layers,
+                w_proj=w_proj, true_states=true_states)
+
+
+@pytest.mark.parametrize("w,cap,init,gamma,cycles", [
+    (SMALL, 300, [100, 250, 1], 15, 6),
+    (TINY_F32, 96, [3], 7, 9),
+])
+def test_append_and_truncate_equal_one_shot_projection(w, cap, init, gamma, cycles):
+    s = _run_cycles(w, cap, init, gamma, cycles, seed=cap)
+    for r, L in enumerate(s["lengths"]):
+        lo, hi = r * s["cap"], r * s["cap"] + L
+        for l in range(w.num_layers):
+            assert torch.equal(s["ck"][l][:, lo:hi], s["rk"][l][:, lo:hi]), f"K layer {l} request {r}"
+            assert torch.equal(s["cv"][l][:, :, lo:hi], s["rv"][l][:, :, lo:hi]), f"V layer {l} request {r}"
+
+
+def test_appended_rows_match_oracle_and_body_reads_them():
+    w = SMALL
+    s = _run_cycles(w, 300, [100, 250, 1], 15, 4, seed=5)
+    layers = layers64(s["layers"])
+    tol = tol_for(w)
+    for r, L in enumerate(s["lengths"]):
+        X = np64(s["true_states"][r, :L])
+        C = oracle.ctx_proj(X, np64(s["w_proj"]))
+        ok, ov = oracle.ctx_kv(C, layers, np.arange(L), w.num_kv_heads, w.head_dim, w.rope_theta)
+        lo = r * s["cap"]
+        for l in range(w.num_layers):
+            compare(s["ck"][l][:, lo:lo + L], ok[l], tol, f"ctx_k layer {l} request {r}")
+            compare(s["cv"][l][:, :, lo:lo + L], ov[l].transpose(0, 2, 1), tol, f"ctx_v layer {l} request {r}")
+    # The body reads the appended cache like a one-shot one (anchor = length).
+    dev = "cuda"
+    bs = w.block_size
+    emb = Rng(7, dev).normal("emb", (w.batch * bs, w.hidden), dtype=w.torch_dtype)
+    base = torch.tensor([r * s["cap"] for r in range(w.batch)], dtype=torch.int64, device=dev)
+    anc = torch.tensor(s["lengths"], dtype=torch.int32, device=dev)
+    valid = torch.ones(w.batch * bs, dtype=torch.uint8, device=dev)
+    ws = workspace(d, s["cfg"], w.batch, 0, dev)
+    outs = []
+    for ck, cv in ((s["ck"], s["cv"]), (s["rk"], s["rv"])):
+        out = torch.empty((w.batch * bs, w.hidden), dtype=w.torch_dtype, device=dev)
+        d.dflash_body_forward(s["cfg"], w.batch, emb, s["layers"], ck, cv, s["total"], base, anc, valid, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    r = 1
+    L = s["lengths"][r]
+    lo = r * s["cap"]
+    ck = [np64(k[:, lo:lo + L]) for k in s["ck"]]
+    cv = [np64(v[:, :, lo:lo + L]).transpose(0, 2, 1) for v in s["cv"]]
+    ref = oracle.body_forward(np64(emb[r * bs:(r + 1) * bs]), layers, ck, cv, [0], [L], np.ones(bs, np.uint8),
+                              oracle_cfg(w))
+    compare(outs[0][r * bs:(r + 1) * bs], ref, tol, f"body over the appended cache, request {r}")
+
+
+def test_append_drops_rows_outside_the_cache():
+    w = SMALL
+    dev = "cuda"
+    cfg = d.config_from_workload(w)
+    true_states, _, w_proj, layers, total, mk = _setup(w, 64)
+    K = w.num_target_layers * w.target_hidden
+    ck, cv = mk()
+    ws = workspace(d, cfg, 0, 8, dev)
+    X = true_states[0, :8].contiguous()
+    pos = torch.arange(8, dtype=torch.int32, device=dev)
+    dst = torch.tensor([-1, 5, total, -7, 9, total + 100, 0, -1], dtype=torch.int64, device=dev)
+    d.dflash_ctx_append(cfg, X, K, w.target_hidden, 8, pos, dst, w_proj, layers, ck, cv, total, ws)
+    rk, rv = mk()
+    d.dflash_ctx_proj(cfg, X, K, w.target_hidden, 8, pos, w_proj, layers, rk, rv, total, 0, ws)  # rows 0..7
+    torch.cuda.synchronize()
+    written = {5: 1, 9: 4, 0: 6}                                   # cache row -> source row
+    for l in range(w.num_layers):
+        for row in range(total):
+            if row in written:
+                sr = written[row]
+                assert torch.equal(ck[l][:, row], rk[l][:, sr]) and torch.equal(cv[l][:, :, row], rv[l][:, :, sr])
+        untouched = [r for r in range(total) if r not in written]
+        assert (ck[l][:, untouched] == 7.0).all() and (cv[l][:, :, untouched] == 7.0).all()
+
+
+def test_truncate_only_shortens():
+    dev = "cuda"
+    lengths = torch.tensor([10, 0, 5, 7, 100], dtype=torch.int64, device=dev)
+    keep = torch.tensor([3, 4, -2, 7, 1000], dtype=torch.int64, device=dev)
+    d.dflash_ctx_truncate(lengths, keep)
+    torch.cuda.synchronize()
+    assert lengths.cpu().tolist() == [3, 0, 0, 7, 100]

@@ -99,6 +99,18 @@ def test_rejects_bad_arguments_before_launch():
                                ptrs, ptrs, 50, 0, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_proj(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), P(fake), lw,
                                ptrs, ptrs, 50, 0, P(fake), 1024, None) == d.DFLASH_ERR_WORKSPACE
+    # incremental append: null scatter rows, bad stride, small workspace; truncate: bad sizes
+    assert lib.dflash_ctx_append(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), None, P(fake), lw,
+                                 ptrs, ptrs, 50, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_append(ctypes.byref(cfg), P(fake), 20481, 4096, 10, P(fake), P(fake), P(fake), lw,
+                                 ptrs, ptrs, 50, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_append(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), P(fake), P(fake), lw,
+                                 ptrs, ptrs, 50, P(fake), 1024, None) == d.DFLASH_ERR_WORKSPACE
+    assert lib.dflash_ctx_append(ctypes.byref(cfg), None, 0, 0, 0, None, None, None, None, None, None, 0,
+                                 None, 0, None) == d.DFLASH_OK                     # nothing to append
+    assert lib.dflash_ctx_truncate(P(fake), P(fake), -1, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_truncate(None, P(fake), 3, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_truncate(None, None, 0, None) == d.DFLASH_OK
     # body: a null weight
     lw[0].w_up = None
     assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
