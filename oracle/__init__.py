@@ -7,6 +7,7 @@ Contents:
   plan.py  -- the seeded anchor plan (integer; bit-exact spec).
   body.py  -- context projection, dual-source block attention, the draft body,
               and a brute-force dense-mask attention used to pin the gathered form.
+  verify.py -- greedy and speculative-sampling verification of a drafted block.
 
 Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
   build_plan             pinned by invariants the pages fix (determinism, equal
@@ -21,8 +22,17 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   body_forward           pinned by composition of the above plus the pages'
                          invariants; whole-body values beyond that are
                          "parity unpinned" (the pages print no worked example).
+  verify_greedy          pinned by the pages' worked example and by brute force
+                         over all short blocks.
+  verify_sample          pinned by the speculative-sampling guarantee (emitted
+                         tokens are distributed as p, chi-square over many
+                         draws) and by its closed-form special cases.
 """
 from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
+from .verify import (
+    verify_greedy_block, verify_greedy, target_choices_from_logits, verify_sample_block, verify_sample,
+    inverse_cdf_draw, residual_weights, accept_proposal,
+)
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
     dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
@@ -34,4 +44,6 @@ __all__ = [
     "rms_norm", "silu", "rope", "rope_inv_freq", "ctx_proj", "ctx_kv", "block_attention",
     "dense_mask_attention", "block_attn_call", "body_forward", "body_forward_dense",
     "concat_target_states",
+    "verify_greedy_block", "verify_greedy", "target_choices_from_logits", "verify_sample_block",
+    "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
 ]
