@@ -161,23 +161,28 @@ def step_roofline_ms(counts, dtype):
 
 
 # ----------------------------------------------------------------------------- steps next to the path
-def time_call(torch, fn, reps=10):
+def hook_ms(d, torch, kernels, fn, reps=10):
+    """Device time per call of fn, summed over the given library kernels, from
+    the library's own HIP events on the launch stream (host overhead excluded)."""
     fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        fn()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / reps
+    total = 0.0
+    for name, per_call in kernels:
+        d.dflash_profile_start(name, per_call * reps)
+        for _ in range(reps):
+            fn()
+        times = d.dflash_profile_stop(per_call * reps)
+        total += sum(times) / reps
+    return total
 
 
 def next_rows(d, torch, device="cuda"):
     """Time the steps around the body at the inference shape (64 requests,
     gamma + 1 = 16 verified positions each, the 5-layer dimensions):
     ctx_append = one cycle's projection of 1024 newly verified target states into
-    every layer's context cache (scattered rows), with its MFMA roofline."""
+    every layer's context cache (scattered rows), with its MFMA roofline;
+    verify_greedy / verify_sample = verification of the 64 drafted blocks over a
+    151936-token vocabulary, with their HBM rooflines."""
     import math as _m
     from dflash_synth import WORKLOADS, Rng, layer_weights
     w = WORKLOADS["c5"]
@@ -200,14 +205,43 @@ def next_rows(d, torch, device="cuda"):
     pos = (lens[:, None] + j[None, :]).reshape(-1).to(torch.int32)
     dst = (torch.arange(R, device=device)[:, None] * cap + lens[:, None] + j[None, :]).reshape(-1)
     ws = torch.empty(d.dflash_workspace_size(cfg, 0, rows), dtype=torch.uint8, device=device)
-    ms = time_call(torch, lambda: d.dflash_ctx_append(cfg, X, K, w.target_hidden, rows, pos, dst, w_proj,
-                                                      layers, ck, cv, total, ws))
+    ms = hook_ms(d, torch, [("ctx_proj", 1), ("ctx_kv", 1)],
+                 lambda: d.dflash_ctx_append(cfg, X, K, w.target_hidden, rows, pos, dst, w_proj, layers, ck, cv,
+                                             total, ws))
     flops = 2.0 * rows * w.hidden * K + 2.0 * rows * (w.num_layers * 2 * w.num_kv_heads * w.head_dim) * w.hidden
     ach = flops / (ms / 1e3) / 1e12
     out["ctx_append"] = {"rows": rows, "ms": round(ms, 4), "rows_per_s": round(rows / (ms / 1e3), 1),
                          "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_TFLOPS["bf16"],
                                       "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
     del ck, cv
+
+    # Verification of one cycle's blocks (64 requests, gamma 15, vocabulary 151936).
+    B, g, V = R, g1 - 1, 151936
+    gen = torch.Generator(device=device).manual_seed(7)
+    draft = torch.randint(0, V, (B, g), generator=gen, device=device, dtype=torch.int32)
+    em = torch.empty((B, g + 1), dtype=torch.int32, device=device)
+    num = torch.empty((B,), dtype=torch.int32, device=device)
+    acc = torch.empty((B,), dtype=torch.int32, device=device)
+    logits = torch.randn((B, g + 1, V), generator=gen, device=device).to(torch.bfloat16)
+    ms = hook_ms(d, torch, [("verify", 1)], lambda: d.dflash_verify_greedy(draft, logits, em, num, acc))
+    byt = logits.numel() * 2.0
+    out["verify_greedy"] = {"blocks": B, "gamma": g, "vocab": V, "ms": round(ms, 4),
+                            "roofline": {"bound": "hbm", "achieved": round(byt / (ms / 1e3) / 1e9, 1),
+                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                         "frac": round(byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    del logits
+    p = torch.softmax(torch.randn((B, g + 1, V), generator=gen, device=device) * 3.0, dim=-1)
+    q = torch.softmax(torch.randn((B, g, V), generator=gen, device=device) * 3.0, dim=-1)
+    ua = torch.rand((B, g), generator=gen, device=device)
+    ud = torch.rand((B,), generator=gen, device=device)
+    ms = hook_ms(d, torch, [("verify", 1)], lambda: d.dflash_verify_sample(draft, p, q, ua, ud, em, num, acc))
+    # Algorithmic bytes: the accept lookups, then one p row and one q row per
+    # request (the draw position), read twice (sum, then the crossing walk).
+    byt = B * g * 8.0 + B * 2 * 2 * V * 4.0
+    out["verify_sample"] = {"blocks": B, "gamma": g, "vocab": V, "ms": round(ms, 4),
+                            "roofline": {"bound": "hbm", "achieved": round(byt / (ms / 1e3) / 1e9, 1),
+                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                         "frac": round(byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}
     return out
 
 

@@ -7,8 +7,9 @@ the stream defaults to torch's current stream on the tensor's device.
 
 The names mirror the C entry points:
   dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_truncate,
-  dflash_block_attn, dflash_body_forward, dflash_workspace_size,
-  dflash_check_config, dflash_status_string.
+  dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
+  dflash_verify_sample, dflash_workspace_size, dflash_check_config,
+  dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
 that fails, importing this package raises ImportError. There is no fallback.
@@ -26,13 +27,13 @@ DFLASH_OK, DFLASH_ERR_INVALID_ARG, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE,
 DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_truncate",
-            "dflash_block_attn", "dflash_body_forward",
+            "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
 # dflash_kernel ids for the measurement hook
 KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "attention": 5,
-           "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9}
+           "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -77,6 +78,10 @@ def _load() -> ctypes.CDLL:
     lib.dflash_block_attn.restype = ctypes.c_int
     lib.dflash_body_forward.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, SZ, P]
     lib.dflash_body_forward.restype = ctypes.c_int
+    lib.dflash_verify_greedy.argtypes = [P, P, I32, I32, I32, I32, I32, P, P, P, P]
+    lib.dflash_verify_greedy.restype = ctypes.c_int
+    lib.dflash_verify_sample.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P, P, P, P]
+    lib.dflash_verify_sample.restype = ctypes.c_int
     lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
     lib.dflash_workspace_size.restype = ctypes.c_size_t
     lib.dflash_check_config.argtypes = [CFG]
@@ -238,6 +243,30 @@ def dflash_body_forward(cfg: DFlashConfig, num_blocks: int, block_embeds, layers
                                  int(ctx_total), _ptr(block_ctx_base), _ptr(block_anchor),
                                  _ptr(block_valid), _ptr(out), wp, wb, _stream(stream, block_embeds))
     _check("dflash_body_forward", s)
+
+
+def dflash_verify_greedy(draft, target_logits, emitted, num_emitted, accepted, eos_token: int = -1,
+                         stream=None) -> None:
+    """draft [B, gamma] i32, target_logits [B, gamma + 1, V] bf16/f32 -> emitted [B, gamma + 1],
+    num_emitted [B], accepted [B] (i32)."""
+    import torch
+    B, g1, V = target_logits.shape
+    dt = DFLASH_BF16 if target_logits.dtype == torch.bfloat16 else DFLASH_F32
+    s = _lib.dflash_verify_greedy(_ptr(draft), _ptr(target_logits), dt, int(B), int(g1 - 1), int(V),
+                                  int(eos_token), _ptr(emitted), _ptr(num_emitted), _ptr(accepted),
+                                  _stream(stream, target_logits))
+    _check("dflash_verify_greedy", s)
+
+
+def dflash_verify_sample(draft, p, q, u_accept, u_draw, emitted, num_emitted, accepted, eos_token: int = -1,
+                         stream=None) -> None:
+    """draft [B, gamma] i32, p [B, gamma + 1, V] f32, q [B, gamma, V] f32, u_accept [B, gamma] f32,
+    u_draw [B] f32 -> emitted [B, gamma + 1], num_emitted [B], accepted [B] (i32)."""
+    B, g1, V = p.shape
+    s = _lib.dflash_verify_sample(_ptr(draft), _ptr(p), _ptr(q), _ptr(u_accept), _ptr(u_draw), int(B),
+                                  int(g1 - 1), int(V), int(eos_token), _ptr(emitted), _ptr(num_emitted),
+                                  _ptr(accepted), _stream(stream, p))
+    _check("dflash_verify_sample", s)
 
 
 def dflash_profile_start(kernel, max_launches: int) -> None:

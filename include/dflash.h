@@ -5,7 +5,8 @@
  *   [P1] angelspec documentation, "DFlash" (sections "How it works", "Configuration");
  *   [P2] NeMo RL design docs, "DFlash Draft Body" (section "How It Works", steps 1-4, "Scope");
  *   [P3] cooking-agi deep dive, "DFlash: drafting, verification, and speed"
- *        (section "One DFlash generation cycle").
+ *        (sections "One DFlash generation cycle", "Why can't later correct guesses
+ *        simply stay?", "Sampling with temperature is not argmax matching").
  *
  * Conventions shared by every entry point
  *   - Pointers marked "device" are HIP device pointers; "host" pointers are read
@@ -275,7 +276,8 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_O_PROJ = 7,        /* GEMM + residual */
     DFLASH_KERNEL_GATE_UP = 8,       /* GEMM + SiLU(gate) * up */
     DFLASH_KERNEL_DOWN = 9,          /* GEMM + residual (+ masked output on the last layer) */
-    DFLASH_KERNEL_COUNT = 10
+    DFLASH_KERNEL_VERIFY = 10,       /* dflash_verify_greedy / dflash_verify_sample (whole call) */
+    DFLASH_KERNEL_COUNT = 11
 } dflash_kernel;
 
 /*
@@ -291,6 +293,61 @@ typedef enum dflash_kernel {
  */
 dflash_status dflash_profile_start(int32_t kernel, int32_t max_launches);
 dflash_status dflash_profile_stop(float *elapsed_ms, int32_t *launches);
+
+/*
+ * dflash_verify_greedy -- greedy verification of a batch of drafted blocks.
+ * [P3] "Why can't later correct guesses simply stay?": only a continuous
+ * accepted prefix survives; at the first proposal that differs from the
+ * target's choice the target's choice is emitted instead and the block ends;
+ * if all proposals agree, the target's choice after the block (the bonus) is
+ * emitted too; an accepted end-of-sequence token ends the block with nothing
+ * after it. Worked example there: draft [10, 20, 99, 40] against choices
+ * [10, 20, 30, 40, 50] emits [10, 20, 30] with 2 accepted.
+ *
+ * The target's choice at position i is the argmax over the vocabulary of
+ * target_logits[b][i] (equal maxima: the smallest token id; logits must be
+ * finite). Position gamma is the bonus position.
+ *
+ *   draft          device i32 [batch][gamma]
+ *   target_logits  device [batch][gamma + 1][vocab], logits_dtype DFLASH_BF16 or DFLASH_F32
+ *   eos_token      end-of-sequence id, or -1 for none
+ *   emitted        device i32 [batch][gamma + 1]: emitted tokens, then -1
+ *   num_emitted    device i32 [batch]; accepted: device i32 [batch] (kept proposals)
+ * Errors: INVALID_ARG for negative sizes, vocab < 1, an unknown dtype or null
+ * pointers; UNSUPPORTED when batch*(gamma + 1) exceeds INT32_MAX.
+ */
+dflash_status dflash_verify_greedy(const int32_t *draft, const void *target_logits, int32_t logits_dtype,
+                                   int32_t batch, int32_t gamma, int32_t vocab, int32_t eos_token,
+                                   int32_t *emitted, int32_t *num_emitted, int32_t *accepted,
+                                   void *hip_stream);
+
+/*
+ * dflash_verify_sample -- speculative-sampling verification of a batch of
+ * drafted blocks. [P3] "Sampling with temperature is not argmax matching": a
+ * proposal y drawn from the proposal distribution q is accepted with
+ * probability min(1, p(y)/q(y)) under the target distribution p; at the first
+ * rejection a replacement is drawn from [p - q]_+ renormalised, and the block
+ * ends. If every proposal is accepted, a bonus token is drawn from p at the
+ * position after the block. An accepted end-of-sequence token ends the block.
+ *
+ * The random numbers are inputs. Proposal i is accepted iff
+ * fp32(u_accept[b][i] * q[b][i][y]) < p[b][i][y] (a proposal outside the
+ * vocabulary is rejected). The block's one draw takes the smallest token t
+ * whose running fp64 sum of weights exceeds u_draw[b] times their total; if
+ * [p - q]_+ sums to zero the replacement is drawn from p.
+ *
+ *   draft          device i32 [batch][gamma]
+ *   p              device f32 [batch][gamma + 1][vocab] target probabilities
+ *   q              device f32 [batch][gamma][vocab] proposal probabilities
+ *   u_accept       device f32 [batch][gamma] in [0, 1); u_draw: device f32 [batch] in [0, 1)
+ *   eos_token, emitted, num_emitted, accepted: as dflash_verify_greedy
+ * Errors: INVALID_ARG for negative sizes, vocab < 1 or null pointers;
+ * UNSUPPORTED when (gamma + 1)*vocab exceeds INT32_MAX.
+ */
+dflash_status dflash_verify_sample(const int32_t *draft, const float *p, const float *q,
+                                   const float *u_accept, const float *u_draw, int32_t batch,
+                                   int32_t gamma, int32_t vocab, int32_t eos_token, int32_t *emitted,
+                                   int32_t *num_emitted, int32_t *accepted, void *hip_stream);
 
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one

@@ -24,7 +24,8 @@ the same readings, written separately there):
     whose running sum of w exceeds u_draw * sum(w) (inverse CDF); when
     [p - q]_+ sums to zero the replacement is drawn from p;
   * the bonus token after a fully accepted block is drawn from p at the
-    position after the block.
+    position after the block;
+  * a proposal outside the vocabulary is rejected.
 """
 from __future__ import annotations
 
@@ -102,9 +103,10 @@ def verify_sample_block(draft: Sequence[int], p: np.ndarray, q: np.ndarray, u_ac
     info names the distribution the last token came from (for the tests)."""
     emitted: List[int] = []
     g = len(draft)
+    V = p.shape[-1]
     for i in range(g):
         y = int(draft[i])
-        if accept_proposal(u_accept[i], p[i, y], q[i, y]):
+        if 0 <= y < V and accept_proposal(u_accept[i], p[i, y], q[i, y]):
             emitted.append(y)
             if eos_token is not None and y == eos_token:
                 return emitted, i + 1, {"kind": "eos", "position": i}

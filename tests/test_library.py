@@ -111,6 +111,22 @@ def test_rejects_bad_arguments_before_launch():
     assert lib.dflash_ctx_truncate(P(fake), P(fake), -1, None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_truncate(None, P(fake), 3, None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_truncate(None, None, 0, None) == d.DFLASH_OK
+    # verification: bad sizes, unknown dtype, missing outputs; empty batch is a no-op
+    assert lib.dflash_verify_greedy(P(fake), P(fake), 1, -1, 3, 10, -1, P(fake), P(fake), P(fake),
+                                    None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_verify_greedy(P(fake), P(fake), 7, 2, 3, 10, -1, P(fake), P(fake), P(fake),
+                                    None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_verify_greedy(P(fake), P(fake), 1, 2, 3, 0, -1, P(fake), P(fake), P(fake),
+                                    None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_verify_greedy(None, P(fake), 1, 2, 3, 10, -1, P(fake), P(fake), P(fake),
+                                    None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_verify_greedy(None, None, 1, 0, 3, 10, -1, None, None, None, None) == d.DFLASH_OK
+    assert lib.dflash_verify_sample(P(fake), P(fake), None, P(fake), P(fake), 2, 3, 10, -1, P(fake),
+                                    P(fake), P(fake), None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_verify_sample(P(fake), P(fake), P(fake), P(fake), P(fake), 2, 3, 1 << 30, -1,
+                                    P(fake), P(fake), P(fake), None) == d.DFLASH_ERR_UNSUPPORTED
+    assert lib.dflash_verify_sample(None, None, None, None, None, 0, 3, 10, -1, None, None, None,
+                                    None) == d.DFLASH_OK
     # body: a null weight
     lw[0].w_up = None
     assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
