@@ -8,6 +8,7 @@ Contents:
   body.py  -- context projection, dual-source block attention, the draft body,
               and a brute-force dense-mask attention used to pin the gathered form.
   verify.py -- greedy and speculative-sampling verification of a drafted block.
+  loss.py  -- block LM head and positionally decayed cross-entropy.
 
 Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
   build_plan             pinned by invariants the pages fix (determinism, equal
@@ -27,12 +28,16 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   verify_sample          pinned by the speculative-sampling guarantee (emitted
                          tokens are distributed as p, chi-square over many
                          draws) and by its closed-form special cases.
+  lm_head_ce             pinned by closed forms (uniform logits, two-token
+                         vocabulary, shift invariance, the two-row decayed mean,
+                         the undecayed limit).
 """
 from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
 from .verify import (
     verify_greedy_block, verify_greedy, target_choices_from_logits, verify_sample_block, verify_sample,
     inverse_cdf_draw, residual_weights, accept_proposal,
 )
+from .loss import lm_head_ce, lm_head_ce_rows, token_ce, logsumexp_rows, position_weights
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
     dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
@@ -46,4 +51,5 @@ __all__ = [
     "concat_target_states",
     "verify_greedy_block", "verify_greedy", "target_choices_from_logits", "verify_sample_block",
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
+    "lm_head_ce", "lm_head_ce_rows", "token_ce", "logsumexp_rows", "position_weights",
 ]
