@@ -182,7 +182,9 @@ def next_rows(d, torch, device="cuda"):
     ctx_append = one cycle's projection of 1024 newly verified target states into
     every layer's context cache (scattered rows), with its MFMA roofline;
     verify_greedy / verify_sample = verification of the 64 drafted blocks over a
-    151936-token vocabulary, with their HBM rooflines."""
+    151936-token vocabulary, with their HBM rooflines; and, on the training
+    side, lm_head_ce = LM head + decayed cross-entropy over the 5-layer body's
+    4096 block rows (151936 x 4096 head), with its MFMA roofline."""
     import math as _m
     from dflash_synth import WORKLOADS, Rng, layer_weights
     w = WORKLOADS["c5"]
@@ -242,6 +244,27 @@ def next_rows(d, torch, device="cuda"):
                             "roofline": {"bound": "hbm", "achieved": round(byt / (ms / 1e3) / 1e9, 1),
                                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                          "frac": round(byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    del p, q
+    # Training side: LM head + decayed CE over the 5-layer body's 4096 block rows.
+    wt = WORKLOADS["c3"]
+    cfg3 = d.config_from_workload(wt)
+    rows = wt.num_blocks * wt.block_size
+    hid = torch.randn((rows, wt.hidden), generator=gen, device=device).to(torch.bfloat16)
+    W = (torch.randn((V, wt.hidden), generator=gen, device=device) / _m.sqrt(wt.hidden)).to(torch.bfloat16)
+    tg = torch.randint(0, V, (rows,), generator=gen, device=device, dtype=torch.int32)
+    lm = (torch.arange(rows, device=device) % wt.block_size != 0).to(torch.uint8)
+    ce = torch.empty((rows,), dtype=torch.float32, device=device)
+    loss = torch.empty((1,), dtype=torch.float64, device=device)
+    ws2 = torch.empty(d.dflash_lm_head_ce_workspace_size(rows, V), dtype=torch.uint8, device=device)
+    call = lambda: d.dflash_lm_head_ce(cfg3, hid, W, tg, lm, 7.0, ce, loss, ws2)
+    ms_gemm = hook_ms(d, torch, [("lm_head", 1)], call)
+    ms = ms_gemm + hook_ms(d, torch, [("lm_ce", 1)], call)
+    flops = 2.0 * rows * V * wt.hidden
+    out["lm_head_ce"] = {"rows": rows, "vocab": V, "hidden": wt.hidden, "ms": round(ms, 4),
+                         "lm_head_gemm_ms": round(ms_gemm, 4),
+                         "roofline": {"bound": "mfma", "achieved": round(flops / (ms / 1e3) / 1e12, 2),
+                                      "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+                                      "frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"], 4)}}
     return out
 
 

@@ -8,8 +8,8 @@ the stream defaults to torch's current stream on the tensor's device.
 The names mirror the C entry points:
   dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_truncate,
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
-  dflash_verify_sample, dflash_workspace_size, dflash_check_config,
-  dflash_status_string.
+  dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
+  dflash_workspace_size, dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
 that fails, importing this package raises ImportError. There is no fallback.
@@ -28,12 +28,14 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_truncate",
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
+            "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
 # dflash_kernel ids for the measurement hook
 KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "attention": 5,
-           "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10}
+           "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10,
+           "lm_head": 11, "lm_ce": 12}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -82,6 +84,10 @@ def _load() -> ctypes.CDLL:
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_sample.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P, P, P, P]
     lib.dflash_verify_sample.restype = ctypes.c_int
+    lib.dflash_lm_head_ce.argtypes = [CFG, I32, P, P, I32, P, P, ctypes.c_double, P, P, P, SZ, P]
+    lib.dflash_lm_head_ce.restype = ctypes.c_int
+    lib.dflash_lm_head_ce_workspace_size.argtypes = [I32, I32]
+    lib.dflash_lm_head_ce_workspace_size.restype = ctypes.c_size_t
     lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
     lib.dflash_workspace_size.restype = ctypes.c_size_t
     lib.dflash_check_config.argtypes = [CFG]
@@ -267,6 +273,23 @@ def dflash_verify_sample(draft, p, q, u_accept, u_draw, emitted, num_emitted, ac
                                   int(g1 - 1), int(V), int(eos_token), _ptr(emitted), _ptr(num_emitted),
                                   _ptr(accepted), _stream(stream, p))
     _check("dflash_verify_sample", s)
+
+
+def dflash_lm_head_ce_workspace_size(rows: int, vocab: int) -> int:
+    return _lib.dflash_lm_head_ce_workspace_size(int(rows), int(vocab))
+
+
+def dflash_lm_head_ce(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, decay_tau: float, row_ce, loss,
+                      workspace, stream=None) -> None:
+    """hidden [rows, H], lm_head [V, H] (config dtype), targets [rows] i32, loss_mask [rows] u8
+    -> row_ce [rows] f32, loss [1] f64."""
+    rows = hidden.shape[0]
+    vocab = lm_head.shape[0]
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_lm_head_ce(ctypes.byref(cfg), int(rows), _ptr(hidden), _ptr(lm_head), int(vocab), _ptr(targets),
+                               _ptr(loss_mask), float(decay_tau), _ptr(row_ce), _ptr(loss), wp, wb,
+                               _stream(stream, lm_head))
+    _check("dflash_lm_head_ce", s)
 
 
 def dflash_profile_start(kernel, max_launches: int) -> None:

@@ -321,6 +321,137 @@ extern "C" dflash_status dflash_ctx_append(const dflash_config* cfg, const void*
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
+// ------------------------------------------------------------------ LM head + decayed CE
+// Per row: logsumexp from the per-group (max, sum) statistics in a fixed
+// order (thread-strided groups, then a fixed tree), CE = lse - z[target];
+// rows whose loss mask is 0 or whose target is outside the vocabulary get 0.
+__global__ __launch_bounds__(256) void lm_ce_row_kernel(const float* part, int groups, const float* target_logit,
+                                                        const int32_t* targets, const uint8_t* loss_mask, int vocab,
+                                                        float* row_ce) {
+    const int row = blockIdx.x, tid = threadIdx.x;
+    __shared__ float s_m[4];
+    __shared__ float s_s[4];
+    const float* pr = part + (int64_t)row * groups * 2;
+    float mx = -__builtin_inff();
+    for (int g = tid; g < groups; g += 256) mx = fmaxf(mx, pr[2 * g]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0) s_m[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float s = 0.f;
+    for (int g = tid; g < groups; g += 256) s += pr[2 * g + 1] * __expf(pr[2 * g] - mx);
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if ((tid & 63) == 0) s_s[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) {
+        const float tot = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
+        const int t = targets[row];
+        const bool use = loss_mask[row] != 0 && t >= 0 && t < vocab;
+        row_ce[row] = use ? (mx + logf(tot)) - target_logit[row] : 0.f;
+    }
+}
+
+// loss = sum(m w CE) / sum(m w), w = exp(-(k - 1) / tau), k = row % block_size,
+// in fp64 with a fixed order; 0 when no row is selected.
+__global__ __launch_bounds__(1024) void lm_ce_loss_kernel(const float* row_ce, const int32_t* targets,
+                                                          const uint8_t* loss_mask, int rows, int vocab, int bs,
+                                                          double tau, double* loss) {
+    const int tid = threadIdx.x;
+    __shared__ double s_n[1024], s_d[1024];
+    double num = 0.0, den = 0.0;
+    for (int r = tid; r < rows; r += 1024) {
+        const int t = targets[r];
+        if (loss_mask[r] == 0 || t < 0 || t >= vocab) continue;
+        const double w = exp(-((double)(r % bs) - 1.0) / tau);
+        num += w * (double)row_ce[r];
+        den += w;
+    }
+    s_n[tid] = num;
+    s_d[tid] = den;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if (tid < o) {
+            s_n[tid] += s_n[tid + o];
+            s_d[tid] += s_d[tid + o];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *loss = s_d[0] > 0.0 ? s_n[0] / s_d[0] : 0.0;
+}
+
+static int lm_groups(int vocab) { return (vocab + 127) / 128; }   // WN = 128 in both tile shapes
+
+extern "C" size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab) {
+    if (rows < 0 || vocab < 1) return 0;
+    const size_t part = align_up((size_t)rows * lm_groups(vocab) * 2 * sizeof(float), 256);
+    const size_t tl = align_up((size_t)rows * sizeof(float), 256);
+    return part + tl + 256;
+}
+
+template <typename T>
+static hipError_t lm_head_ce_t(const dflash_config& c, int rows, const T* hidden, const T* lm_head, int vocab,
+                               const int32_t* targets, const uint8_t* loss_mask, double tau, float* row_ce,
+                               double* loss, char* ws, hipStream_t st) {
+    const int groups = lm_groups(vocab);
+    float* part = reinterpret_cast<float*>(ws);
+    float* tl = reinterpret_cast<float*>(ws + align_up((size_t)rows * groups * 2 * sizeof(float), 256));
+    EpLseCE<T> ep{part, tl, targets, groups, vocab};
+    hipError_t e;
+    {
+        ProfScope prof(DFLASH_KERNEL_LM_HEAD, st);
+        const int big_tiles = ((rows + 255) / 256) * ((vocab + 255) / 256);
+        if (big_tiles >= 256)
+            e = launch_gemm<T, BigTile>(rows, vocab, c.hidden, APlain<T>{hidden, c.hidden},
+                                        BClamp<T>{lm_head, c.hidden, vocab}, ep, st);
+        else
+            e = launch_gemm<T, MidTile>(rows, vocab, c.hidden, APlain<T>{hidden, c.hidden},
+                                        BClamp<T>{lm_head, c.hidden, vocab}, ep, st);
+    }
+    if (e != hipSuccess) return e;
+    {
+        ProfScope prof(DFLASH_KERNEL_LM_CE, st);
+        hipLaunchKernelGGL(lm_ce_row_kernel, dim3(rows), dim3(256), 0, st, part, groups, tl, targets, loss_mask, vocab,
+                           row_ce);
+        hipLaunchKernelGGL(lm_ce_loss_kernel, dim3(1), dim3(1024), 0, st, row_ce, targets, loss_mask, rows, vocab,
+                           c.block_size, tau, loss);
+    }
+    return hipGetLastError();
+}
+
+extern "C" dflash_status dflash_lm_head_ce(const dflash_config* cfg, int32_t rows, const void* hidden,
+                                           const void* lm_head, int32_t vocab, const int32_t* targets,
+                                           const uint8_t* loss_mask, double decay_tau, float* row_ce,
+                                           double* loss, void* workspace, size_t workspace_bytes,
+                                           void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (rows < 0 || vocab < 1 || !(decay_tau > 0.0)) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)vocab + 255 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if (hidden == nullptr && rows > 0) return DFLASH_ERR_INVALID_ARG;
+    if (lm_head == nullptr || loss == nullptr || (rows > 0 && (targets == nullptr || loss_mask == nullptr ||
+                                                               row_ce == nullptr)) ||
+        !aligned16(hidden) || !aligned16(lm_head))
+        return DFLASH_ERR_INVALID_ARG;
+    const size_t need = dflash_lm_head_ce_workspace_size(rows, vocab);
+    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return DFLASH_ERR_WORKSPACE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    if (rows == 0) {
+        hipLaunchKernelGGL(lm_ce_loss_kernel, dim3(1), dim3(1024), 0, st, row_ce, targets, loss_mask, 0, vocab,
+                           cfg->block_size, decay_tau, loss);
+        return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+    }
+    hipError_t e;
+    if (cfg->dtype == DFLASH_BF16)
+        e = lm_head_ce_t<__bf16>(*cfg, rows, static_cast<const __bf16*>(hidden), static_cast<const __bf16*>(lm_head),
+                                 vocab, targets, loss_mask, decay_tau, row_ce, loss, ws, st);
+    else
+        e = lm_head_ce_t<float>(*cfg, rows, static_cast<const float*>(hidden), static_cast<const float*>(lm_head),
+                                vocab, targets, loss_mask, decay_tau, row_ce, loss, ws, st);
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 // lengths[i] = min(lengths[i], max(keep[i], 0)).
 __global__ __launch_bounds__(256) void ctx_truncate_kernel(int64_t* lengths, const int64_t* keep, int n) {
     const int i = blockIdx.x * 256 + threadIdx.x;

@@ -57,6 +57,12 @@ template <typename T> struct BPlain {
     __device__ const T* row(int n) const { return w + (int64_t)n * ld; }
 };
 
+// Rows past n_rows repeat the last row (a ragged N; the epilogue ignores them).
+template <typename T> struct BClamp {
+    const T* w; int64_t ld; int n_rows;
+    __device__ const T* row(int n) const { return w + (int64_t)(n < n_rows ? n : n_rows - 1) * ld; }
+};
+
 // Rows [0, nq) of Wq, then Wk, then Wv.
 template <typename T> struct BQKV {
     const T *wq, *wk, *wv; int nq, nk; int64_t ld;
@@ -158,6 +164,51 @@ template <typename T> struct EpSwiGLU {
                     float g = acc[i][j][e], up = acc[i][j + NI / 2][e];
                     o[j * 32] = from_f32<T>(g / (1.f + __expf(-g)) * up);
                 }
+            }
+    }
+};
+
+// Block LM head with a fused softmax statistic: for every row, the maximum
+// and sum of exp(z - max) over each WN-column group of logits z (columns past
+// n_cols excluded), written to part[row][group], and the logit of the row's
+// target token. The 32 lanes of a wave half hold 32 consecutive columns of a
+// row, so each statistic is an in-lane pass over the NI column tiles plus a
+// 5-step exchange within the half.
+template <typename T> struct EpLseCE {
+    float* part;                  // [M][groups][2]
+    float* target_logit;          // [M]
+    const int32_t* targets;       // [M]
+    int groups, n_cols;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+        const int grp = nb / WN;
+        if (grp >= groups) return;                  // a whole group past the vocabulary
+        const int col = nb + (lane & 31);
+        const float NEG_INF = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                float mx = NEG_INF;
+#pragma unroll
+                for (int j = 0; j < NI; ++j) mx = fmaxf(mx, col + j * 32 < n_cols ? acc[i][j][e] : NEG_INF);
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < NI; ++j) s += col + j * 32 < n_cols ? __expf(acc[i][j][e] - mx) : 0.f;
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+                if (row >= M) continue;
+                if ((lane & 31) == 0) {
+                    part[((int64_t)row * groups + grp) * 2 + 0] = mx;
+                    part[((int64_t)row * groups + grp) * 2 + 1] = s;
+                }
+                const int t = targets[row];
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    if (col + j * 32 == t) target_logit[row] = acc[i][j][e];
             }
     }
 };
@@ -288,7 +339,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int
 
     // Tile order: consecutive tiles walk down M inside groups of 8 row tiles
     // so the B slab they share stays hot in L2.
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;   // B loaders clamp a ragged N
     int tm, tn;
     {
         // Workgroups are dealt round-robin to the 8 XCDs (each with its own
@@ -433,7 +484,7 @@ template <typename T, class Cfg, class AL, class BL, class EP>
 hipError_t launch_gemm(int M, int N, int K, const AL& al, const BL& bl, const EP& ep,
                        hipStream_t stream) {
     if (M <= 0) return hipSuccess;
-    const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
     hipLaunchKernelGGL((gemm_nt_kernel<T, Cfg, AL, BL, EP>), dim3(tiles), dim3(Cfg::THREADS), 0, stream, M, N,
                        K, al, bl, ep);
     return hipGetLastError();

@@ -277,7 +277,9 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_GATE_UP = 8,       /* GEMM + SiLU(gate) * up */
     DFLASH_KERNEL_DOWN = 9,          /* GEMM + residual (+ masked output on the last layer) */
     DFLASH_KERNEL_VERIFY = 10,       /* dflash_verify_greedy / dflash_verify_sample (whole call) */
-    DFLASH_KERNEL_COUNT = 11
+    DFLASH_KERNEL_LM_HEAD = 11,      /* GEMM h W_lm^T with per-group softmax statistics */
+    DFLASH_KERNEL_LM_CE = 12,        /* per-row CE and the decayed loss */
+    DFLASH_KERNEL_COUNT = 13
 } dflash_kernel;
 
 /*
@@ -348,6 +350,39 @@ dflash_status dflash_verify_sample(const int32_t *draft, const float *p, const f
                                    const float *u_accept, const float *u_draw, int32_t batch,
                                    int32_t gamma, int32_t vocab, int32_t eos_token, int32_t *emitted,
                                    int32_t *num_emitted, int32_t *accepted, void *hip_stream);
+
+/*
+ * dflash_lm_head_ce -- the draft's training loss over block rows: logits of
+ * the (frozen, target-provided) LM head and cross-entropy against the
+ * ground-truth tokens with an exponential positional decay. [P1] "How it
+ * works", Loss: cross-entropy whose positional decay weights earlier
+ * in-block positions more; [P1] "Configuration": embedding and lm_head come
+ * from the target model; [P2] step 4: the loss mask excludes the anchor and
+ * invalid positions.
+ *
+ *   z_r      = hidden[r] W_lm^T                 (fp32 accumulation, never stored)
+ *   CE_r     = logsumexp(z_r) - z_r[targets[r]]
+ *   w_r      = exp(-(k - 1) / decay_tau),  k = r mod block_size   (k = 1: weight 1)
+ *   loss     = sum(m_r w_r CE_r) / sum(m_r w_r), m_r = loss_mask[r]; 0 if no row counts
+ *
+ *   rows           block rows (normally num_blocks * block_size)
+ *   hidden         device [rows, hidden] (e.g. dflash_body_forward's output)
+ *   lm_head        device [vocab, hidden], Linear layout; any vocab >= 1
+ *   targets        device i32 [rows]; a target outside [0, vocab) excludes its row
+ *   loss_mask      device u8 [rows]
+ *   decay_tau      > 0 (the pages give no value)
+ *   row_ce         device f32 [rows]: CE_r, 0 for excluded rows
+ *   loss           device f64 scalar
+ *   workspace      dflash_lm_head_ce_workspace_size(rows, vocab) bytes, 256-byte aligned
+ * Errors: as dflash_ctx_proj for the config; INVALID_ARG for rows < 0, vocab < 1,
+ * decay_tau <= 0 or null pointers; WORKSPACE for a small or misaligned workspace.
+ */
+dflash_status dflash_lm_head_ce(const dflash_config *cfg, int32_t rows, const void *hidden,
+                                const void *lm_head, int32_t vocab, const int32_t *targets,
+                                const uint8_t *loss_mask, double decay_tau, float *row_ce,
+                                double *loss, void *workspace, size_t workspace_bytes,
+                                void *hip_stream);
+size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab);
 
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one

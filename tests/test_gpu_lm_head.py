@@ -1,0 +1,94 @@
+"""dflash_lm_head_ce vs the draft-loss oracle (angelspec "DFlash", How it
+works, Loss: cross-entropy with an exponential positional decay favouring
+early block positions; NeMo RL "DFlash Draft Body", step 4: loss mask).
+
+Tolerance: logits are fp32 sums of exact bf16 (or fp32) products, the
+softmax statistics use fp32 exp/log; the CE of a row is O(log V) ~ 12, and
+the fp32 error of every step is below 1e-6 of that, so CE values must agree
+with the fp64 oracle to rel-L2 1e-5 and max-abs 1e-4 (fp32 inputs: 1e-6 / 1e-5)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_draft_model_build_amd as d
+import oracle
+from dflash_synth import WORKLOADS, Rng, scaled
+from tests.helpers import compare, np64
+
+pytestmark = pytest.mark.gpu
+CE_TOL = dict(rel_l2=1e-5, max_abs=1e-4)
+CE_TOL_F32 = dict(rel_l2=1e-6, max_abs=1e-5)
+
+
+def _inputs(w, rows, vocab, seed, dev="cuda"):
+    rng = Rng(seed, dev)
+    h = rng.normal("lm.hidden", (rows, w.hidden), dtype=w.torch_dtype)
+    W = rng.normal("lm.head", (vocab, w.hidden), std=1 / math.sqrt(w.hidden), dtype=w.torch_dtype)
+    t = rng.integers("lm.targets", 0, vocab - 1, (rows,)).to(torch.int32)
+    k = torch.arange(rows, device=dev) % w.block_size
+    mask = (k != 0).to(torch.uint8)                     # the anchor row of every block is excluded
+    return h, W, t, mask
+
+
+def _run(w, h, W, t, mask, tau):
+    cfg = d.config_from_workload(w)
+    rows, vocab = h.shape[0], W.shape[0]
+    ce = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    loss = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    ws = torch.empty(d.dflash_lm_head_ce_workspace_size(rows, vocab), dtype=torch.uint8, device="cuda")
+    d.dflash_lm_head_ce(cfg, h, W, t, mask, tau, ce, loss, ws)
+    torch.cuda.synchronize()
+    return ce, float(loss.item())
+
+
+SMALL = scaled(WORKLOADS["c3"], hidden=256, num_q_heads=4, num_kv_heads=2, intermediate=512, num_layers=1)
+
+
+@pytest.mark.parametrize("w,rows,vocab,tol", [
+    (SMALL, 48, 1000, CE_TOL),                          # ragged vocabulary (not a multiple of 128)
+    (SMALL, 300, 4099, CE_TOL),                         # ragged rows and vocabulary
+    (WORKLOADS["c1"], 32, 777, CE_TOL_F32),
+])
+def test_all_rows_small(w, rows, vocab, tol):
+    h, W, t, mask = _inputs(w, rows, vocab, seed=rows + vocab)
+    t[5] = -1                                           # targets outside the vocabulary: excluded rows
+    t[9] = vocab
+    tau = 3.0
+    ce, loss = _run(w, h, W, t, mask, tau)
+    keep = mask.clone()
+    keep[5] = 0
+    keep[9] = 0
+    tt = t.clone()
+    tt[5] = 0
+    tt[9] = 0
+    ref_ce, ref_loss = oracle.lm_head_ce(np64(h), np64(W), tt.cpu().numpy(), keep.cpu().numpy(), w.block_size, tau)
+    compare(ce, ref_ce, tol, "row CE")
+    assert (ce.cpu()[keep.cpu() == 0] == 0).all()
+    assert abs(loss - ref_loss) <= tol["max_abs"]
+
+
+def test_full_size_block_rows_sampled():
+    # The 5-layer training shape: 256 blocks of 16 rows, hidden 4096, vocabulary 151936.
+    w = WORKLOADS["c3"]
+    rows, vocab, tau = w.num_blocks * w.block_size, 151936, 7.0
+    h, W, t, mask = _inputs(w, rows, vocab, seed=5)
+    ce, loss = _run(w, h, W, t, mask, tau)
+    ce_h = ce.cpu().numpy().astype(np.float64)
+    m = mask.cpu().numpy().astype(bool)
+    assert np.isfinite(ce_h).all() and (ce_h[~m] == 0).all() and (ce_h[m] > 0).all()
+    sample = np.array([1, 2, 15, 17, 1000, 2049, 4094, 4095])
+    Wd = np64(W)
+    ref = oracle.lm_head_ce_rows(np64(h[torch.from_numpy(sample).cuda()]), Wd, t.cpu().numpy()[sample])
+    compare(torch.from_numpy(ce_h[sample]), ref, CE_TOL, "sampled row CE")
+    # The loss is the decayed weighted mean of the row CEs the kernel produced.
+    wts = oracle.position_weights(rows, w.block_size, tau) * m
+    assert abs(loss - float((wts * ce_h).sum() / wts.sum())) <= 1e-9 * abs(loss)
+
+
+def test_no_selected_rows_gives_zero_loss():
+    w = SMALL
+    h, W, t, mask = _inputs(w, 32, 500, seed=9)
+    ce, loss = _run(w, h, W, t, torch.zeros_like(mask), 2.0)
+    assert loss == 0.0 and (ce.cpu() == 0).all()

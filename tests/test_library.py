@@ -127,6 +127,14 @@ def test_rejects_bad_arguments_before_launch():
                                     P(fake), P(fake), P(fake), None) == d.DFLASH_ERR_UNSUPPORTED
     assert lib.dflash_verify_sample(None, None, None, None, None, 0, 3, 10, -1, None, None, None,
                                     None) == d.DFLASH_OK
+    # LM head + CE: bad tau, bad vocab, small workspace
+    assert lib.dflash_lm_head_ce(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 0.0, P(fake),
+                                 P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce(ctypes.byref(cfg), 16, P(fake), P(fake), 0, P(fake), P(fake), 2.0, P(fake),
+                                 P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
+                                 P(fake), P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+    assert d.dflash_lm_head_ce_workspace_size(16, 100) > 0 and d.dflash_lm_head_ce_workspace_size(-1, 100) == 0
     # body: a null weight
     lw[0].w_up = None
     assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
