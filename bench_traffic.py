@@ -9,8 +9,8 @@ together with a hash of the library sources, so bench.py reports it only while
 the kernels are unchanged.
 
 On the GPU machine (repo root):
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown
-  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/copy_fetch -o c -- python bench_traffic.py --copy
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/copy_write -o c -- python bench_traffic.py --copy
 Then, anywhere:
@@ -86,7 +86,7 @@ def summarize(root, workload, kernel):
         "bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write,
         "source_hash": source_hash(),
         "command": "see bench_traffic.py docstring (FETCH_SIZE and WRITE_SIZE runs of bench.py --workload "
-                   f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown, plus the copy calibration)",
+                   f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next, plus the copy calibration)",
     }
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(path, "w") as f:
