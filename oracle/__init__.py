@@ -9,6 +9,7 @@ Contents:
               and a brute-force dense-mask attention used to pin the gathered form.
   verify.py -- greedy and speculative-sampling verification of a drafted block.
   loss.py  -- block LM head and positionally decayed cross-entropy.
+  backward.py -- gradients of the dual-source block attention.
 
 Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
   build_plan             pinned by invariants the pages fix (determinism, equal
@@ -31,6 +32,8 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   lm_head_ce             pinned by closed forms (uniform logits, two-token
                          vocabulary, shift invariance, the two-row decayed mean,
                          the undecayed limit).
+  block_attn_call_backward  pinned by central finite differences of the
+                         forward oracle over every input component.
 """
 from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
 from .verify import (
@@ -38,6 +41,7 @@ from .verify import (
     inverse_cdf_draw, residual_weights, accept_proposal,
 )
 from .loss import lm_head_ce, lm_head_ce_rows, token_ce, logsumexp_rows, position_weights
+from .backward import block_attention_backward, block_attn_call_backward
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
     dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
@@ -52,4 +56,5 @@ __all__ = [
     "verify_greedy_block", "verify_greedy", "target_choices_from_logits", "verify_sample_block",
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
     "lm_head_ce", "lm_head_ce_rows", "token_ce", "logsumexp_rows", "position_weights",
+    "block_attention_backward", "block_attn_call_backward",
 ]

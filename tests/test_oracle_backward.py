@@ -1,0 +1,75 @@
+"""Pins of the attention-backward oracle against finite differences of the
+forward oracle (NeMo RL "DFlash Draft Body", How It Works, step 3; Scope:
+training runs the body with an optimizer step). Central differences of
+L = sum(d_out * block_attn_call(...)) in fp64 must match every analytic
+gradient component, including context rows read by several blocks and the
+rows of invalid positions (keys for the others, no output of their own)."""
+import numpy as np
+
+import oracle
+from oracle.backward import block_attention_backward, block_attn_call_backward
+
+
+def _case(seed):
+    rng = np.random.default_rng(seed)
+    nb, bs, Hq, Hkv, D, T = 3, 4, 4, 2, 8, 14
+    q = rng.standard_normal((nb * bs, Hq * D))
+    k = rng.standard_normal((nb * bs, Hkv * D))
+    v = rng.standard_normal((nb * bs, Hkv * D))
+    ck = rng.standard_normal((Hkv, T, D))
+    cv = rng.standard_normal((Hkv, T, D))
+    base = [0, 0, 7]
+    anchor = [5, 7, 6]                            # blocks 0 and 1 share context rows 0..4
+    valid = np.ones(nb * bs, np.uint8)
+    valid[6] = 0                                  # an invalid position: its key still counts
+    dO = rng.standard_normal((nb * bs, Hq * D))
+    return q, k, v, ck, cv, base, anchor, valid, dO, (bs, Hq, Hkv, D, 1e4)
+
+
+def _loss(q, k, v, ck, cv, base, anchor, valid, dO, dims):
+    bs, Hq, Hkv, D, theta = dims
+    o = oracle.block_attn_call(q, k, v, ck, cv, base, anchor, valid, bs, Hq, Hkv, D, theta)
+    return float((dO * o).sum())
+
+
+def test_gradients_match_finite_differences():
+    q, k, v, ck, cv, base, anchor, valid, dO, dims = _case(0)
+    bs, Hq, Hkv, D, theta = dims
+    grads = block_attn_call_backward(q, k, v, ck, cv, base, anchor, valid, bs, Hq, Hkv, D, theta, dO)
+    args = [q, k, v, ck, cv]
+    eps = 1e-6
+    for which, (x, g) in enumerate(zip(args, grads)):
+        num = np.zeros_like(x)
+        flat, nflat = x.reshape(-1), num.reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = _loss(*args, base, anchor, valid, dO, dims)
+            flat[i] = old - eps
+            lm = _loss(*args, base, anchor, valid, dO, dims)
+            flat[i] = old
+            nflat[i] = (lp - lm) / (2 * eps)
+        assert np.allclose(g, num, rtol=1e-6, atol=1e-7), (which, np.abs(g - num).max())
+
+
+def test_structure_of_the_gradients():
+    q, k, v, ck, cv, base, anchor, valid, dO, dims = _case(1)
+    bs, Hq, Hkv, D, theta = dims
+    dq, dk, dv, dck, dcv = block_attn_call_backward(q, k, v, ck, cv, base, anchor, valid, bs, Hq, Hkv, D,
+                                                    theta, dO)
+    assert (dq[6] == 0).all()                     # no output at an invalid position -> no dq
+    assert np.abs(dk[6]).sum() > 0 and np.abs(dv[6]).sum() > 0   # but it is a key of its block
+    # rows that no block reads get nothing
+    assert (dck[:, 13:] == 0).all() and (dcv[:, 13:] == 0).all()     # block 2 reads rows 7..12 only
+    # empty block: no gradient anywhere from it
+    anchor2 = [5, -1, 6]
+    g2 = block_attn_call_backward(q, k, v, ck, cv, base, anchor2, valid, bs, Hq, Hkv, D, theta, dO)
+    assert (g2[0][4:8] == 0).all() and (g2[1][4:8] == 0).all() and (g2[2][4:8] == 0).all()
+    # dV sums p over queries: with dO = 1 everywhere, every block's dV rows sum to bs*G per value dim
+    nb = q.shape[0] // bs
+    q4 = oracle.rope(q.reshape(nb, bs, Hq, D), (np.array(anchor)[:, None] + np.arange(bs))[:, :, None], theta)
+    k4 = oracle.rope(k.reshape(nb, bs, Hkv, D), (np.array(anchor)[:, None] + np.arange(bs))[:, :, None], theta)
+    ones = np.ones((nb, bs, Hq, D))
+    _, _, dvb, _, dcv1 = block_attention_backward(q4, k4, v.reshape(nb, bs, Hkv, D), ck, cv, base, anchor, ones)
+    total = dvb.sum(axis=(0, 1)) + dcv1.sum(axis=1)       # [Hkv, D]
+    assert np.allclose(total, nb * bs * (Hq // Hkv))
