@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "draft block-positions/sec for 5-layer DFlash body forward; % bf16 MFMA / HBM roofline"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # dense MI355X matrix peaks
 PEAK_HBM_GBS = 8000.0
+PEAK_VALU_F32_TFLOPS = 157.3                          # fp32 vector units (FMA = 2 flops)
 
 DESCR = {
     "c1": "tiny fp32 single-layer body: batch 1, target seq 128, 2x256 target layers -> 256, 4/2 heads x 64, block 8, 4 anchors",
@@ -265,6 +266,33 @@ def next_rows(d, torch, device="cuda"):
                          "roofline": {"bound": "mfma", "achieved": round(flops / (ms / 1e3) / 1e12, 2),
                                       "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
                                       "frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"], 4)}}
+    del hid, W
+    # Training side: backward of one layer's dual-source attention at the
+    # training shape (8 sequences of 4096, 32 blocks each at random anchors).
+    T = wt.batch * wt.seq_len
+    nb, bs, Hq, Hkv, D = wt.num_blocks, wt.block_size, wt.num_q_heads, wt.num_kv_heads, wt.head_dim
+    anc = torch.cat([torch.randperm(wt.seq_len - bs - 1, generator=gen, device=device)[:wt.anchors_per_row] + 1
+                     for _ in range(wt.batch)]).to(torch.int32)
+    base = (torch.arange(nb, device=device) // wt.anchors_per_row * wt.seq_len).to(torch.int64)
+    val = torch.ones((nb * bs,), dtype=torch.uint8, device=device)
+    mk = lambda *shape: torch.randn(shape, generator=gen, device=device).to(torch.bfloat16)
+    qa, ka, va, oa, doa = mk(nb * bs, Hq * D), mk(nb * bs, Hkv * D), mk(nb * bs, Hkv * D), mk(nb * bs, Hq * D), \
+        mk(nb * bs, Hq * D)
+    cka, cva = mk(Hkv, T, D), mk(Hkv, D, T)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=device)
+    grads = (f32(nb * bs, Hq * D), f32(nb * bs, Hkv * D), f32(nb * bs, Hkv * D), f32(Hkv, T, D), f32(Hkv, D, T))
+    ws3 = torch.empty(d.dflash_block_attn_backward_workspace_size(cfg3, nb), dtype=torch.uint8, device=device)
+    ms = hook_ms(d, torch, [("attn_bwd", 1)],
+                 lambda: d.dflash_block_attn_backward(cfg3, nb, qa, ka, va, cka, cva, T, base, anc, val, oa, doa,
+                                                      *grads, ws3))
+    # Algorithmic flops: five products of bs x keys x D per query head (scores,
+    # dO V^T, dq, dk, dv), keys = anchor + bs.
+    keys = float((anc.to(torch.float64) + bs).sum().item())
+    flops = 10.0 * bs * D * Hq * keys
+    ach = flops / (ms / 1e3) / 1e12
+    out["attn_backward"] = {"blocks": nb, "ctx_total": T, "ms": round(ms, 4),
+                            "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_VALU_F32_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(ach / PEAK_VALU_F32_TFLOPS, 4)}}
     return out
 
 

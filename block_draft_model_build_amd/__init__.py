@@ -9,6 +9,7 @@ The names mirror the C entry points:
   dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_truncate,
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
+  dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_workspace_size, dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
@@ -29,13 +30,14 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_truncate",
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
+            "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
 # dflash_kernel ids for the measurement hook
 KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "attention": 5,
            "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10,
-           "lm_head": 11, "lm_ce": 12}
+           "lm_head": 11, "lm_ce": 12, "attn_bwd": 13}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -88,6 +90,11 @@ def _load() -> ctypes.CDLL:
     lib.dflash_lm_head_ce.restype = ctypes.c_int
     lib.dflash_lm_head_ce_workspace_size.argtypes = [I32, I32]
     lib.dflash_lm_head_ce_workspace_size.restype = ctypes.c_size_t
+    lib.dflash_block_attn_backward.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
+                                               SZ, P]
+    lib.dflash_block_attn_backward.restype = ctypes.c_int
+    lib.dflash_block_attn_backward_workspace_size.argtypes = [CFG, I32]
+    lib.dflash_block_attn_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
     lib.dflash_workspace_size.restype = ctypes.c_size_t
     lib.dflash_check_config.argtypes = [CFG]
@@ -290,6 +297,22 @@ def dflash_lm_head_ce(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, de
                                _ptr(loss_mask), float(decay_tau), _ptr(row_ce), _ptr(loss), wp, wb,
                                _stream(stream, lm_head))
     _check("dflash_lm_head_ce", s)
+
+
+def dflash_block_attn_backward_workspace_size(cfg: DFlashConfig, num_blocks: int) -> int:
+    return _lib.dflash_block_attn_backward_workspace_size(ctypes.byref(cfg), int(num_blocks))
+
+
+def dflash_block_attn_backward(cfg: DFlashConfig, num_blocks: int, q, k_blk, v_blk, ctx_k, ctx_v,
+                               ctx_total: int, block_ctx_base, block_anchor, block_valid, out, d_out,
+                               d_q, d_k_blk, d_v_blk, d_ctx_k, d_ctx_v, workspace, stream=None) -> None:
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_block_attn_backward(ctypes.byref(cfg), int(num_blocks), _ptr(q), _ptr(k_blk), _ptr(v_blk),
+                                        _ptr(ctx_k), _ptr(ctx_v), int(ctx_total), _ptr(block_ctx_base),
+                                        _ptr(block_anchor), _ptr(block_valid), _ptr(out), _ptr(d_out), _ptr(d_q),
+                                        _ptr(d_k_blk), _ptr(d_v_blk), _ptr(d_ctx_k), _ptr(d_ctx_v), wp, wb,
+                                        _stream(stream, q))
+    _check("dflash_block_attn_backward", s)
 
 
 def dflash_profile_start(kernel, max_launches: int) -> None:

@@ -719,7 +719,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
 // their lengths / target) rounded up to 128), target_stream (single) or
 // target_shared (multi) splits in total; a group gets max(1, ceil(length /
 // chunk)) splits.
-__global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
+static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
                                                              int64_t ctx_total, int target_shared, int target_stream,
                                                              int* group_start, int* item_start, int* sched) {
     __shared__ int scan[1024];

@@ -279,7 +279,8 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_VERIFY = 10,       /* dflash_verify_greedy / dflash_verify_sample (whole call) */
     DFLASH_KERNEL_LM_HEAD = 11,      /* GEMM h W_lm^T with per-group softmax statistics */
     DFLASH_KERNEL_LM_CE = 12,        /* per-row CE and the decayed loss */
-    DFLASH_KERNEL_COUNT = 13
+    DFLASH_KERNEL_ATTN_BWD = 13,     /* dflash_block_attn_backward (both kernels) */
+    DFLASH_KERNEL_COUNT = 14
 } dflash_kernel;
 
 /*
@@ -383,6 +384,38 @@ dflash_status dflash_lm_head_ce(const dflash_config *cfg, int32_t rows, const vo
                                 double *loss, void *workspace, size_t workspace_bytes,
                                 void *hip_stream);
 size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab);
+
+/*
+ * dflash_block_attn_backward -- gradients of dflash_block_attn. [P2] "How It
+ * Works", step 3 (the dual-source visibility the forward implements) and
+ * "Scope" (training runs the body with an optimizer step).
+ *
+ * Given the forward's inputs, its output `out` and the gradient d_out of that
+ * output, writes the gradients with respect to q, k_blk, v_blk (before RoPE,
+ * as dflash_block_attn takes them), the context K cache (in the rotated frame
+ * it stores) and the context V cache (transposed like it). Rows whose forward
+ * output is zero (block_valid == 0, empty blocks) pass no gradient back; their
+ * k and v rows still receive the gradients of the other rows that read them.
+ * Context rows no block reads get zero.
+ *
+ *   q, k_blk, v_blk, ctx_k, ctx_v, ctx_total, block_ctx_base, block_anchor,
+ *   block_valid     as dflash_block_attn
+ *   out, d_out      device [nb*bs, Hq*D] in the config dtype
+ *   d_q             device f32 [nb*bs, Hq*D]; d_k_blk, d_v_blk: device f32 [nb*bs, Hkv*D]
+ *   d_ctx_k         device f32 [Hkv][ctx_total][D]; d_ctx_v: device f32 [Hkv][D][ctx_total]
+ *   workspace       dflash_block_attn_backward_workspace_size(cfg, nb) bytes, 256-byte aligned
+ * Every output element is written (no accumulation into the caller's buffers);
+ * results are deterministic. Errors: as dflash_block_attn.
+ */
+dflash_status dflash_block_attn_backward(const dflash_config *cfg, int32_t num_blocks, const void *q,
+                                         const void *k_blk, const void *v_blk, const void *ctx_k,
+                                         const void *ctx_v, int64_t ctx_total,
+                                         const int64_t *block_ctx_base, const int32_t *block_anchor,
+                                         const uint8_t *block_valid, const void *out, const void *d_out,
+                                         float *d_q, float *d_k_blk, float *d_v_blk, float *d_ctx_k,
+                                         float *d_ctx_v, void *workspace, size_t workspace_bytes,
+                                         void *hip_stream);
+size_t dflash_block_attn_backward_workspace_size(const dflash_config *cfg, int32_t num_blocks);
 
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one

@@ -135,6 +135,19 @@ def test_rejects_bad_arguments_before_launch():
     assert lib.dflash_lm_head_ce(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
                                  P(fake), P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
     assert d.dflash_lm_head_ce_workspace_size(16, 100) > 0 and d.dflash_lm_head_ce_workspace_size(-1, 100) == 0
+    # attention backward: negative sizes, a null gradient, a small workspace, nothing to do
+    F = [P(fake)] * 3
+    assert lib.dflash_block_attn_backward(ctypes.byref(cfg), -1, *F, P(fake), P(fake), 64, *F, P(fake), P(fake),
+                                          *F, P(fake), P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_block_attn_backward(ctypes.byref(cfg), 4, *F, P(fake), P(fake), 64, *F, P(fake), P(fake),
+                                          P(fake), None, P(fake), P(fake), P(fake), P(fake), 1 << 40,
+                                          None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_block_attn_backward(ctypes.byref(cfg), 4, *F, P(fake), P(fake), 64, *F, P(fake), P(fake),
+                                          *F, P(fake), P(fake), P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+    assert lib.dflash_block_attn_backward(ctypes.byref(cfg), 0, *([None] * 5), 0, *([None] * 10), None, 0,
+                                          None) == d.DFLASH_OK
+    assert d.dflash_block_attn_backward_workspace_size(cfg, 4) > 0
+    assert d.dflash_block_attn_backward_workspace_size(cfg, -1) == 0
     # body: a null weight
     lw[0].w_up = None
     assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
