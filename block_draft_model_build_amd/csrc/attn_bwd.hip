@@ -392,23 +392,636 @@ __global__ __launch_bounds__(kBwThreads) void attn_bwd_ctx_kernel(BwArgs<T> a) {
     }
 }
 
-template <typename T, int D>
-hipError_t attn_bwd_t(const BwArgs<T>& a, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// bf16 path on the matrix cores (D = 128). Four waves per workgroup; wave w
+// owns column half wm = w / 2 and key half wn = w % 2 of a 64 x 64 tile.
+// Operand fragments follow the MFMA 32x32x16 layout of Mfma<__bf16>: lane l
+// holds 8 consecutive contraction indices 8 (l / 32) + 0..7 of row / column
+// l % 32. Fragments whose contraction index runs down the rows of a row-major
+// LDS tile come from the gfx950 transposed LDS read (lds_tr below). Products
+// whose contraction runs over keys or columns take their left operand
+// straight from a previous product's accumulator: a row permutation of that
+// product (key_perm) makes each lane hold 8 consecutive keys / columns.
+namespace mfb {
+
+constexpr int D = 128;
+constexpr int KT = 64;                // keys per chunk / tile, columns per block
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Row-major tiles of 64 rows x 128 bf16 (K~, Q~, dO): 16-byte chunk c of row r
+// is stored at chunk position c ^ (r & 15).
+__device__ __forceinline__ int koff(int r, int d) { return r * 256 + ((((d >> 3) ^ (r & 15))) << 4) + ((d & 7) << 1); }
+// V^T tiles of 128 rows (d) x 64 keys: chunk c of row d at c ^ (d & 7).
+__device__ __forceinline__ int voff(int d, int j) { return d * 128 + ((((j >> 3) ^ (d & 7))) << 4) + ((j & 7) << 1); }
+
+// Transposed LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane j supplies the address of 4 consecutive 16-bit elements; lane i gets
+// element i % 4 of lane 4 e + i / 4 as its element e. So if lane j of the
+// group points at row r0 + j / 4, column c0 + 4 (j % 4) of a row-major tile,
+// lane i receives column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 lds_tr(const char* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 join(s16x4 a, s16x4 b) {
+    s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x8 lds_frag(const char* base, int off) { return *(const bf16x8*)(base + off); }
+// Group-relative column offset that makes output lane i of a transposed read
+// hold column key_perm(i) (bits 2 and 3 of i swapped).
+__device__ __forceinline__ int perm_col(int r) { return ((r & 1) << 3) | ((r & 2) << 1); }
+
+// Fragment of a 32x32x16 operand whose contraction index k runs down the rows
+// of a row-major tile: rows k0 + 8 (l / 32) + 0..7, column n0 + l % 32.
+__device__ __forceinline__ bf16x8 tr_frag_k(const char* base, int k0, int n0, int lane) {
+    const int i = lane & 15, G = lane >> 4;
+    const int r = k0 + 8 * (G >> 1) + (i >> 2), col = n0 + 16 * (G & 1) + 4 * (i & 3);
+    return join(lds_tr(base + koff(r, col)), lds_tr(base + koff(r + 4, col)));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int half) {
+    bf16x8 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = static_cast<__bf16>(v[8 * half + i]);
+    return f;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+// Renumber a 1-D grid of `total` items so that every XCD gets a contiguous run
+// of items (blocks of one sequence share their context; tiles of one sequence
+// share their blocks); the items past the last multiple of 8 keep their index.
+__device__ __forceinline__ int xcd_item(int id, int total) {
+    const int t8 = total / 8 * 8;
+    return id < t8 ? (id % 8) * (total / 8) + id / 8 : id;
+}
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(DFLASH_GPTR(src), DFLASH_LPTR(lds_base), 16, 0, 0);
+}
+
+// 64 rows of a row-major [rows][128] bf16 array into a swizzled tile; row r of
+// the tile reads source row rowmap(r). Each wave issues 4 loads (1 KB each).
+template <typename RowPtr>
+__device__ __forceinline__ void dma_rows(char* tile, RowPtr rowptr, int wave, int lane) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int u0 = (it * 4 + wave) * 64, u = u0 + lane;
+        const int r = u >> 4, ch = u & 15;
+        dma16(rowptr(r) + ((ch ^ (r & 15)) << 3), tile + u0 * 16);
+    }
+}
+
+struct QueryLds {
+    char k[2][KT * 256];     // K~ chunk (swizzled rows), two stages
+    char vt[2][D * 128];     // V^T chunk, two stages
+    __bf16 q[KT][D];         // Q~ and masked dO of the block (plain rows)
+    __bf16 dout[KT][D];
+    float p[KT][KT + 1];     // own chunk: P^T and dS^T [key][column]
+    float ds[KT][KT + 1];
+    float m[2][KT], l[2][KT];
+};
+
+struct CtxLds {
+    char k[KT * 256];        // K~ tile
+    char vt[D * 128];        // V^T tile
+    char q[2][KT * 256];     // Q~ of the current and the next block
+    char dout[2][KT * 256];  // masked dO of the current and the next block
+    float lse[2][KT], delta[2][KT];
+    int list[256], list_an[256];
+    int64_t list_base[256];
+    int cnt[4];
+};
+
+struct MfArgs {
+    BwArgs<__bf16> a;
+    __bf16 *qt, *dot;        // workspace [nb][Hkv][64][128]: Q~ and masked dO per block
+};
+
+// Query-major kernel: one workgroup per (block, KV head).
+__global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
+    const BwArgs<__bf16>& a = m.a;
+    __shared__ QueryLds L;
+    const int item = xcd_item(blockIdx.x, a.nb * a.hkv);
+    const int n = item % a.nb, g = item / a.nb, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+    const int G = a.hq / a.hkv, bs = a.bs, C = bs * G;
+    const float scale = 1.f / sqrtf((float)D);
+    const int64_t base = clamp_base(a.base[n], a.ctx_total);
+    const int an = anchor_eff(a.anchor[n], base, a.ctx_total);
+    const int64_t slot = (int64_t)n * a.hkv + g;
+    if (an < 0) {
+        // Empty block: nothing is read, nothing passes back.
+        for (int idx = tid; idx < C * D; idx += 256) {
+            const int c = idx / D, d = idx - c * D;
+            a.dq[(int64_t)(n * bs + c % bs) * a.q_ld + (int64_t)(g * G + c / bs) * D + d] = 0.f;
+        }
+        for (int idx = tid; idx < bs * D; idx += 256) {
+            const int r = idx / D, d = idx - r * D;
+            a.dkb[(int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D + d] = 0.f;
+            a.dvb[(int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D + d] = 0.f;
+        }
+        return;
+    }
+    const __bf16* ckg = a.ck + ((int64_t)g * a.ctx_total + base) * D;
+    const __bf16* cvg = a.cvt + (int64_t)g * D * a.ctx_total + base;
+    const int64_t lim = a.ctx_total - base;          // cache rows addressable from this base
+
+    // This lane's column (B operand n index) and its Q~ / dO fragments.
+    const int c = 32 * wm + l32;
+    const bool col_ok = c < C;
+    const int kq = c % bs, hq = c / bs, qrow = n * bs + kq;
+    bf16x8 qf[8], df[8];
+    float delta = 0.f;
+    {
+        const __bf16* qr = a.q + (int64_t)qrow * a.q_ld + (int64_t)(g * G + hq) * D;
+        const __bf16* orow = a.out + (int64_t)qrow * a.q_ld + (int64_t)(g * G + hq) * D;
+        const __bf16* dr = a.dout + (int64_t)qrow * a.q_ld + (int64_t)(g * G + hq) * D;
+        const bool live_row = col_ok && a.valid[qrow] != 0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 lo = {}, hi = {}, dlo = {}, dhi = {};
+            if (col_ok) {
+                lo = *(const bf16x8*)(qr + 16 * ks + 8 * h);
+                hi = *(const bf16x8*)(qr + 64 + 16 * ks + 8 * h);
+            }
+            if (live_row) {
+                dlo = *(const bf16x8*)(dr + 16 * ks + 8 * h);
+                dhi = *(const bf16x8*)(dr + 64 + 16 * ks + 8 * h);
+                const bf16x8 olo = *(const bf16x8*)(orow + 16 * ks + 8 * h);
+                const bf16x8 ohi = *(const bf16x8*)(orow + 64 + 16 * ks + 8 * h);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    delta += (float)dlo[i] * (float)olo[i] + (float)dhi[i] * (float)ohi[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float cs, sn;
+                rope_cs(a.rt, 16 * ks + 8 * h + i, an + kq, cs, sn);
+                const float x1 = (float)lo[i], x2 = (float)hi[i];
+                qf[ks][i] = static_cast<__bf16>((x1 * cs - x2 * sn) * scale);
+                qf[ks + 4][i] = static_cast<__bf16>((x2 * cs + x1 * sn) * scale);
+            }
+            df[ks] = dlo;
+            df[ks + 4] = dhi;
+        }
+        delta += __shfl_xor(delta, 32, 64);
+        if (!col_ok) delta = 0.f;
+    }
+    if (wn == 0) {
+        // Q~ and masked dO for the context kernel (workspace) and for the own keys (LDS).
+        __bf16* qt = m.qt + slot * KT * D + (int64_t)c * D;
+        __bf16* dt = m.dot + slot * KT * D + (int64_t)c * D;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int d0 = 16 * ks + 8 * h;
+            *(bf16x8*)(qt + d0) = qf[ks];
+            *(bf16x8*)(dt + d0) = df[ks];
+            *(bf16x8*)(&L.q[c][d0]) = qf[ks];
+            *(bf16x8*)(&L.dout[c][d0]) = df[ks];
+        }
+        if (h == 0) a.delta[slot * KT + c] = delta;
+    }
+
+    // Chunks: context keys [0, an) in 64-key chunks, then the block's own keys.
+    const int nctx = (an + KT - 1) / KT;
+    const int nchunks = nctx + 1;
+    auto stage = [&](int ch, bool with_v) {
+        char* Lk = L.k[ch & 1];
+        char* Lvt = L.vt[ch & 1];
+        if (ch < nctx) {
+            const int j0 = ch * KT;
+            dma_rows(Lk, [&](int r) { return ckg + (int64_t)min(j0 + r, an - 1) * D; }, w, lane);
+            if (with_v) {
+                if ((int64_t)j0 + KT <= lim) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int u0 = (it * 4 + w) * 64, u = u0 + lane;
+                        const int d = u >> 3, cc = u & 7;
+                        dma16(cvg + (int64_t)d * a.ctx_total + j0 + ((cc ^ (d & 7)) << 3), Lvt + u0 * 16);
+                    }
+                } else {
+                    // Chunk reaching the end of the cache: element loads, keys clamped.
+                    for (int idx = tid; idx < D * KT; idx += 256) {
+                        const int d = idx / KT, j = idx - d * KT;
+                        const int64_t jj = min((int64_t)(j0 + j), lim - 1);
+                        *(__bf16*)(Lvt + voff(d, j)) = cvg[(int64_t)d * a.ctx_total + jj];
+                    }
+                }
+            }
+        } else {
+            // Own keys: row r of the block rotated at an + r; zero past the block.
+            for (int idx = tid; idx < KT * (D / 2); idx += 256) {
+                const int r = idx / (D / 2), i = idx - r * (D / 2);
+                float y1 = 0.f, y2 = 0.f;
+                if (r < bs) {
+                    const __bf16* kr = a.kb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
+                    const float x1 = (float)kr[i], x2 = (float)kr[i + D / 2];
+                    float cs, sn;
+                    rope_cs(a.rt, i, an + r, cs, sn);
+                    y1 = x1 * cs - x2 * sn;
+                    y2 = x2 * cs + x1 * sn;
+                }
+                *(__bf16*)(Lk + koff(r, i)) = static_cast<__bf16>(y1);
+                *(__bf16*)(Lk + koff(r, i + D / 2)) = static_cast<__bf16>(y2);
+            }
+            if (with_v) {
+                for (int idx = tid; idx < KT * D; idx += 256) {
+                    const int r = idx / D, d = idx - r * D;
+                    __bf16 v = static_cast<__bf16>(0.f);
+                    if (r < bs) v = a.vb[(int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D + d];
+                    *(__bf16*)(Lvt + voff(d, r)) = v;
+                }
+            }
+        }
+    };
+    auto nvalid = [&](int ch) { return ch < nctx ? min(KT, an - ch * KT) : bs; };
+    // S^T tile of this wave: keys 32 wn + key_perm(row), columns 32 wm + l32.
+    auto scores = [&](const char* Lk) {
+        f32x16 s = {};
+        const int kr = 32 * wn + key_perm(l32);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) s = Mfma<__bf16>::mma(lds_frag(Lk, koff(kr, 16 * ks + 8 * h)), qf[ks], s);
+        return s;
+    };
+
+    // One pass over the chunks with a running maximum m per column (online
+    // softmax): p~ = exp(s - m), l = sum p~, dQ~ accumulates dS~ K~ with
+    // dS~ = p~ (dP - delta), and everything is rescaled when m moves. At the
+    // end P = p~ / l and dQ~ = (sum dS~ K~) / l. m only moves when a chunk's
+    // maximum exceeds it by more than 8 (p~ stays below e^8), so rescales are
+    // rare after the first chunk.
+    float mrun = -__builtin_inff(), lrun = 0.f;
+    f32x16 dq[4] = {};
+    f32x16 p_own = {}, ds_own = {};
+    __syncthreads();
+    stage(0, true);
+    for (int ch = 0; ch < nchunks; ++ch) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (ch + 1 < nchunks) stage(ch + 1, true);
+        const char* Lk = L.k[ch & 1];
+        const char* Lvt = L.vt[ch & 1];
+        const f32x16 s = scores(Lk);
+        f32x16 dp = {};
+        {
+            const int i = lane & 15, Gq = lane >> 4;
+            const int kc = 32 * wn + 16 * (Gq & 1) + perm_col(i & 3);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int d0 = 16 * ks + 8 * h + (i >> 2);
+                const bf16x8 va = join(lds_tr(Lvt + voff(d0, kc)), lds_tr(Lvt + voff(d0 + 4, kc)));
+                dp = Mfma<__bf16>::mma(va, df[ks], dp);
+            }
+        }
+        const int nv = nvalid(ch) - 32 * wn - 8 * h;       // keys acc_key(e) < nv are valid
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (acc_key(e) < nv) mx = fmaxf(mx, s[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));            // both key halves of the column
+        const bool move = mx > mrun + 8.f;
+        if (__any(move)) {
+            const float mnew = move ? mx : mrun;
+            const float f = mrun == -__builtin_inff() ? 0.f : __expf(mrun - mnew);
+            mrun = mnew;
+            lrun *= f;
+            // dQ~ accumulator rows are columns: fetch each row's factor from its lane.
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float fe = __shfl(f, acc_row(e, lane), 64);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) dq[dt][e] *= fe;
+            }
+        }
+        f32x16 p, ds;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            p[e] = acc_key(e) < nv ? __expf(s[e] - mrun) : 0.f;
+            lrun += p[e];
+            ds[e] = p[e] * (dp[e] - delta);
+        }
+        if (ch == nctx) {
+            p_own = p;
+            ds_own = ds;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 af = pack8(ds, kk);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                dq[dt] = Mfma<__bf16>::mma(af, tr_frag_k(Lk, 32 * wn + 16 * kk, 32 * dt, lane), dq[dt]);
+        }
+    }
+    // Column statistics: add the lane halves, then merge the two key halves.
+    lrun += __shfl_xor(lrun, 32, 64);
+    if (h == 0) {
+        L.m[wn][c] = mrun;
+        L.l[wn][c] = lrun;
+    }
+    __syncthreads();
+    if (tid < KT) {
+        const int cc = tid;
+        const float m0 = L.m[0][cc], m1 = L.m[1][cc];
+        const float mm = fmaxf(m0, m1);
+        const float f0 = m0 == -__builtin_inff() ? 0.f : __expf(m0 - mm);
+        const float f1 = m1 == -__builtin_inff() ? 0.f : __expf(m1 - mm);
+        const float ll = L.l[0][cc] * f0 + L.l[1][cc] * f1;
+        // Unused columns get lse = +inf: their probabilities are exactly zero.
+        const bool used = cc < C && ll > 0.f;
+        const float lse = used ? mm + __logf(ll) : __builtin_inff();
+        a.lse[slot * KT + cc] = lse;
+        // Factor that turns each key half's p~ into P.
+        L.m[0][cc] = used ? f0 / ll : 0.f;
+        L.m[1][cc] = used ? f1 / ll : 0.f;
+    }
+    __syncthreads();
+    {
+        // The own chunk's P and dS for the own keys' dK / dV.
+        const float f = L.m[wn][c];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int key = 32 * wn + acc_key(e) + 8 * h;
+            L.p[key][c] = p_own[e] * f;
+            L.ds[key][c] = ds_own[e] * f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float fe = L.m[wn][32 * wm + acc_row(e, lane)];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) dq[dt][e] *= fe;
+        }
+    }
+    __syncthreads();
+
+    // Own keys: dK~ = dS^T Q~, dV = P^T dO over the block's columns; dK~ rotated back.
+    for (int idx = tid; idx < bs * (D / 2); idx += 256) {
+        const int r = idx / (D / 2), i = idx - r * (D / 2);
+        float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+        for (int cc = 0; cc < C; ++cc) {
+            const float dsv = L.ds[r][cc], pv = L.p[r][cc];
+            k1 += dsv * (float)L.q[cc][i];
+            k2 += dsv * (float)L.q[cc][i + D / 2];
+            v1 += pv * (float)L.dout[cc][i];
+            v2 += pv * (float)L.dout[cc][i + D / 2];
+        }
+        float cs, sn;
+        rope_cs(a.rt, i, an + r, cs, sn);
+        float* dk = a.dkb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
+        float* dv = a.dvb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
+        dk[i] = k1 * cs + k2 * sn;
+        dk[i + D / 2] = k2 * cs - k1 * sn;
+        dv[i] = v1;
+        dv[i + D / 2] = v2;
+    }
+
+    // dQ~: add the two key halves, rotate back, scale.
+    float* red = reinterpret_cast<float*>(L.k[0]);  // K~ stages: 32 KB
+    if (wn == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[((wm * 4 + dt) * 16 + e) * 64 + lane] = dq[dt][e];
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dq[dt][e] += red[((wm * 4 + dt) * 16 + e) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int cc = 32 * wm + acc_row(e, lane);
+            if (cc >= C) continue;
+            const int k = cc % bs, hh = cc / bs;
+            float* o = a.dq + (int64_t)(n * bs + k) * a.q_ld + (int64_t)(g * G + hh) * D;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const int i = 32 * dt + l32;
+                float cs, sn;
+                rope_cs(a.rt, i, an + k, cs, sn);
+                const float y1 = dq[dt][e], y2 = dq[dt + 2][e];
+                o[i] = (y1 * cs + y2 * sn) * scale;
+                o[i + D / 2] = (y2 * cs - y1 * sn) * scale;
+            }
+        }
+    }
+}
+
+// Key-major kernel over the context: one workgroup per (64-row tile, KV head);
+// the blocks that read the tile are visited in index order, so every dK / dV
+// sum has a fixed order.
+__global__ __launch_bounds__(256) void bwd_ctx_kernel(MfArgs m) {
+    const BwArgs<__bf16>& a = m.a;
+    __shared__ CtxLds L;
+    const int tiles = (int)((a.ctx_total + KT - 1) / KT);
+    const int item = xcd_item(blockIdx.x, tiles * a.hkv);
+    const int g = item / tiles, tid = threadIdx.x;
+    const int64_t t0 = (int64_t)(item % tiles) * KT;
+    const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+    const int64_t T = a.ctx_total;
+    const __bf16* ckg = a.ck + (int64_t)g * T * D;
+    const __bf16* cvg = a.cvt + (int64_t)g * D * T;
+    // The tile's K~ and V^T (rows past the cache clamped to its last row).
+    dma_rows(L.k, [&](int r) { return ckg + min(t0 + r, T - 1) * D; }, w, lane);
+    if (t0 + KT <= T) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int u0 = (it * 4 + w) * 64, u = u0 + lane;
+            const int d = u >> 3, cc = u & 7;
+            dma16(cvg + (int64_t)d * T + t0 + ((cc ^ (d & 7)) << 3), L.vt + u0 * 16);
+        }
+    } else {
+        for (int idx = tid; idx < D * KT; idx += 256) {
+            const int d = idx / KT, j = idx - d * KT;
+            *(__bf16*)(L.vt + voff(d, j)) = cvg[(int64_t)d * T + min(t0 + j, T - 1)];
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // B operands that stay fixed over the blocks: K~ (S) and V (dP) of key column 32 wn + l32.
+    bf16x8 kf[8], vf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        kf[ks] = lds_frag(L.k, koff(32 * wn + l32, 16 * ks + 8 * h));
+        const int i = lane & 15, Gq = lane >> 4;
+        const int d0 = 16 * ks + 8 * h + (i >> 2), kc = 32 * wn + 16 * (Gq & 1) + 4 * (i & 3);
+        vf[ks] = join(lds_tr(L.vt + voff(d0, kc)), lds_tr(L.vt + voff(d0 + 4, kc)));
+    }
+    const int64_t key = t0 + 32 * wn + l32;
+    f32x16 dk[4] = {}, dv[4] = {};
+    auto load_block = [&](int it, int buf) {
+        const int64_t slot = (int64_t)L.list[it] * a.hkv + g;
+        dma_rows(L.q[buf], [&](int r) { return m.qt + (slot * KT + r) * D; }, w, lane);
+        dma_rows(L.dout[buf], [&](int r) { return m.dot + (slot * KT + r) * D; }, w, lane);
+        if (w == 0 && lane < 16) dma16(a.lse + slot * KT + 4 * lane, (char*)L.lse[buf]);
+        if (w == 1 && lane < 16) dma16(a.delta + slot * KT + 4 * lane, (char*)L.delta[buf]);
+    };
+    for (int b0 = 0; b0 < a.nb; b0 += 256) {
+        // The blocks of [b0, b0 + 256) that read this tile, in index order.
+        const int nn = b0 + tid;
+        bool reads = false;
+        int64_t bb = 0;
+        int ba = -1;
+        if (nn < a.nb) {
+            bb = clamp_base(a.base[nn], T);
+            ba = anchor_eff(a.anchor[nn], bb, T);
+            reads = ba > 0 && bb < t0 + KT && bb + ba > t0;
+        }
+        const uint64_t mask = __ballot(reads);
+        if (lane == 0) L.cnt[w] = __popcll(mask);
+        __syncthreads();
+        int off = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            off += i < w ? L.cnt[i] : 0;
+            total += L.cnt[i];
+        }
+        if (reads) {
+            const int at = off + __popcll(mask & ((1ull << lane) - 1));
+            L.list[at] = nn;
+            L.list_base[at] = bb;
+            L.list_an[at] = ba;
+        }
+        __syncthreads();
+        if (total > 0) load_block(0, 0);
+        for (int it = 0; it < total; ++it) {
+            const int buf = it & 1;
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (it + 1 < total) load_block(it + 1, buf ^ 1);
+            const int64_t base = L.list_base[it];
+            const int an = L.list_an[it];
+            const char* Lq = L.q[buf];
+            const char* Ld = L.dout[buf];
+            f32x16 s = {}, dp = {};
+            const int cr = 32 * wm + key_perm(l32);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                s = Mfma<__bf16>::mma(lds_frag(Lq, koff(cr, 16 * ks + 8 * h)), kf[ks], s);
+                dp = Mfma<__bf16>::mma(lds_frag(Ld, koff(cr, 16 * ks + 8 * h)), vf[ks], dp);
+            }
+            const bool seen = key >= base && key < base + an;
+            f32x16 p, ds;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int cc = 32 * wm + acc_key(e) + 8 * h;
+                p[e] = seen ? __expf(s[e] - L.lse[buf][cc]) : 0.f;
+                ds[e] = p[e] * (dp[e] - L.delta[buf][cc]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pa = pack8(p, kk), da = pack8(ds, kk);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    dv[dt] = Mfma<__bf16>::mma(pa, tr_frag_k(Ld, 32 * wm + 16 * kk, 32 * dt, lane), dv[dt]);
+                    dk[dt] = Mfma<__bf16>::mma(da, tr_frag_k(Lq, 32 * wm + 16 * kk, 32 * dt, lane), dk[dt]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // Add the two column halves and write the tile's gradients.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(L.k);     // 64 KB: the K~, V^T and Q~ tiles
+    if (wm == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                red[((wn * 8 + dt) * 16 + e) * 64 + lane] = dk[dt][e];
+                red[((wn * 8 + 4 + dt) * 16 + e) * 64 + lane] = dv[dt][e];
+            }
+    }
+    __syncthreads();
+    if (wm == 0) {
+        const bool vec = (T & 3) == 0;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                dk[dt][e] += red[((wn * 8 + dt) * 16 + e) * 64 + lane];
+                dv[dt][e] += red[((wn * 8 + 4 + dt) * 16 + e) * 64 + lane];
+            }
+            const int d = 32 * dt + l32;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t j = t0 + 32 * wn + acc_row(e, lane);
+                if (j < T) a.dck[((int64_t)g * T + j) * D + d] = dk[dt][e];
+            }
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int64_t j = t0 + 32 * wn + acc_row(4 * e4, lane);     // 4 consecutive rows
+                float* o = a.dcv + ((int64_t)g * D + d) * T + j;
+                if (vec && j + 3 < T) {
+                    *(f32x4*)o = f32x4{dv[dt][4 * e4], dv[dt][4 * e4 + 1], dv[dt][4 * e4 + 2], dv[dt][4 * e4 + 3]};
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (j + q < T) o[q] = dv[dt][4 * e4 + q];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace mfb
+
+// fp32 (D = 64): the vector-unit kernels.
+hipError_t attn_bwd_f32(const BwArgs<float>& a, hipStream_t st) {
     {
         ProfScope prof(DFLASH_KERNEL_ATTN_BWD, st);
-        hipLaunchKernelGGL((attn_bwd_query_kernel<T, D>), dim3(a.nb, a.hkv), dim3(kBwThreads), 0, st, a);
+        hipLaunchKernelGGL((attn_bwd_query_kernel<float, 64>), dim3(a.nb, a.hkv), dim3(kBwThreads), 0, st, a);
         if (a.ctx_total > 0)
-            hipLaunchKernelGGL((attn_bwd_ctx_kernel<T, D>), dim3((unsigned)((a.ctx_total + kBwKeys - 1) / kBwKeys),
-                                                               a.hkv),
-                               dim3(kBwThreads), 0, st, a);
+            hipLaunchKernelGGL((attn_bwd_ctx_kernel<float, 64>),
+                               dim3((unsigned)((a.ctx_total + kBwKeys - 1) / kBwKeys), a.hkv), dim3(kBwThreads), 0,
+                               st, a);
     }
     return hipGetLastError();
 }
 
-size_t bw_workspace(const dflash_config& c, int nb) {
-    const size_t per = (size_t)nb * c.num_kv_heads * 64;
-    return align_up(per * c.head_dim * sizeof(float), 256) + 2 * align_up(per * sizeof(float), 256) + 256;
+// bf16 (D = 128): the matrix-core kernels.
+hipError_t attn_bwd_bf16(const mfb::MfArgs& m, hipStream_t st) {
+    {
+        ProfScope prof(DFLASH_KERNEL_ATTN_BWD, st);
+        hipLaunchKernelGGL(mfb::bwd_query_kernel, dim3(m.a.nb * m.a.hkv), dim3(256), 0, st, m);
+        if (m.a.ctx_total > 0)
+            hipLaunchKernelGGL(mfb::bwd_ctx_kernel,
+                               dim3((unsigned)((m.a.ctx_total + mfb::KT - 1) / mfb::KT * m.a.hkv)), dim3(256), 0, st,
+                               m);
+    }
+    return hipGetLastError();
 }
+
+// Workspace: per (block, KV head) the block's 64 query columns; bf16 keeps
+// Q~ and masked dO (bf16), fp32 keeps Q~ (fp32); both keep lse and
+// rowsum(dO o) per column.
+struct BwLayout {
+    size_t qt, dot, lse, delta, total;
+};
+BwLayout bw_layout(const dflash_config& c, int nb) {
+    const size_t per = (size_t)nb * c.num_kv_heads * 64;
+    BwLayout l{};
+    size_t off = 0;
+    l.qt = off;
+    if (c.dtype == DFLASH_BF16) {
+        off = align_up(off + per * c.head_dim * 2, 256);
+        l.dot = off;
+        off = align_up(off + per * c.head_dim * 2, 256);
+    } else {
+        off = align_up(off + per * c.head_dim * 4, 256);
+        l.dot = off;
+    }
+    l.lse = off;
+    off = align_up(off + per * 4, 256);
+    l.delta = off;
+    off = align_up(off + per * 4, 256);
+    l.total = off + 256;
+    return l;
+}
+size_t bw_workspace(const dflash_config& c, int nb) { return bw_layout(c, nb).total; }
 
 }  // namespace
 
@@ -430,7 +1043,8 @@ extern "C" dflash_status dflash_block_attn_backward(
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
     if (num_blocks < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
-    if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2 || ctx_total > (int64_t)INT32_MAX * 64)
+    if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2 || (int64_t)num_blocks * cfg->num_kv_heads > INT32_MAX ||
+        (ctx_total + 63) / 64 * cfg->num_kv_heads > INT32_MAX)
         return DFLASH_ERR_UNSUPPORTED;
     if (num_blocks == 0 && ctx_total == 0) return DFLASH_OK;
     if ((num_blocks > 0 && (q == nullptr || k_blk == nullptr || v_blk == nullptr || block_ctx_base == nullptr ||
@@ -441,7 +1055,7 @@ extern "C" dflash_status dflash_block_attn_backward(
     const size_t need = bw_workspace(*cfg, num_blocks);
     if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return DFLASH_ERR_WORKSPACE;
-    const size_t per = (size_t)num_blocks * cfg->num_kv_heads * 64;
+    const BwLayout lay = bw_layout(*cfg, num_blocks);
     char* ws = static_cast<char*>(workspace);
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t e;
@@ -466,9 +1080,9 @@ extern "C" dflash_status dflash_block_attn_backward(
         a.dvb = d_v_blk;
         a.dck = d_ctx_k;
         a.dcv = d_ctx_v;
-        a.qt = reinterpret_cast<float*>(ws);
-        a.lse = reinterpret_cast<float*>(ws + align_up(per * cfg->head_dim * sizeof(float), 256));
-        a.delta = a.lse + align_up(per * sizeof(float), 256) / sizeof(float);
+        a.qt = reinterpret_cast<float*>(ws + lay.qt);
+        a.lse = reinterpret_cast<float*>(ws + lay.lse);
+        a.delta = reinterpret_cast<float*>(ws + lay.delta);
         a.nb = num_blocks;
         a.bs = cfg->block_size;
         a.hq = cfg->num_q_heads;
@@ -482,8 +1096,12 @@ extern "C" dflash_status dflash_block_attn_backward(
             hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, st, d_ctx_v, cnt);
             return hipGetLastError();
         }
-        if constexpr (sizeof(T) == 2) return attn_bwd_t<T, 128>(a, st);
-        else return attn_bwd_t<T, 64>(a, st);
+        if constexpr (sizeof(T) == 2) {
+            mfb::MfArgs m{a, reinterpret_cast<__bf16*>(ws + lay.qt), reinterpret_cast<__bf16*>(ws + lay.dot)};
+            return attn_bwd_bf16(m, st);
+        } else {
+            return attn_bwd_f32(a, st);
+        }
     };
     e = cfg->dtype == DFLASH_BF16 ? fill(__bf16{}) : fill(float{});
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
