@@ -34,6 +34,9 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
                          the undecayed limit).
   block_attn_call_backward  pinned by central finite differences of the
                          forward oracle over every input component.
+  ctx_proj_backward      pinned by central differences of the forward context
+                         path (ctx_proj then ctx_kv) along random directions of
+                         W_proj and of C, and entry by entry on a tiny case.
 """
 from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
 from .verify import (
@@ -41,7 +44,7 @@ from .verify import (
     inverse_cdf_draw, residual_weights, accept_proposal,
 )
 from .loss import lm_head_ce, lm_head_ce_rows, token_ce, logsumexp_rows, position_weights
-from .backward import block_attention_backward, block_attn_call_backward
+from .backward import block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_proj_backward
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
     dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
@@ -56,5 +59,5 @@ __all__ = [
     "verify_greedy_block", "verify_greedy", "target_choices_from_logits", "verify_sample_block",
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
     "lm_head_ce", "lm_head_ce_rows", "token_ce", "logsumexp_rows", "position_weights",
-    "block_attention_backward", "block_attn_call_backward",
+    "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_proj_backward",
 ]

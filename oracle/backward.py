@@ -95,3 +95,38 @@ def block_attn_call_backward(q, k_blk, v_blk, ctx_k, ctx_v, base, anchor, valid,
     dq = rope(dqr, -pos[:, :, None], theta)            # transpose of the rotation
     dk = rope(dkr, -pos[:, :, None], theta)
     return (dq.reshape(R, Hq * D), dk.reshape(R, Hkv * D), dvb.reshape(R, Hkv * D), dck, dcv)
+
+
+def ctx_grad_rows(d_ctx_k, d_ctx_v, positions, num_kv_heads: int, head_dim: int, theta: float):
+    """Per-row gradient of every layer's context K and V, back in the
+    un-rotated projection space: for layer l, row t,
+        Gk_l[t] = RoPE^T(dKc_l[:, t, :], positions[t])  (rotation by the opposite angle),
+        Gv_l[t] = dVc_l[:, t, :],
+    each flattened head-major to [Hkv*D]. d_ctx_k / d_ctx_v are lists over layers
+    of [Hkv, T, D]. Returns (Gk, Gv), lists of [T, Hkv*D]."""
+    pos = np.asarray(positions, np.int64)
+    Gk, Gv = [], []
+    for dk, dv in zip(d_ctx_k, d_ctx_v):
+        dk = np.asarray(dk, np.float64).transpose(1, 0, 2)          # [T, Hkv, D]
+        dv = np.asarray(dv, np.float64).transpose(1, 0, 2)
+        T = dk.shape[0]
+        Gk.append(rope(dk, -pos[:, None], theta).reshape(T, num_kv_heads * head_dim))
+        Gv.append(dv.reshape(T, num_kv_heads * head_dim))
+    return Gk, Gv
+
+
+def ctx_proj_backward(X, positions, layers, d_ctx_k, d_ctx_v, num_kv_heads: int, head_dim: int, theta: float):
+    """Gradients through the context path (ctx_proj, then ctx_kv of every layer;
+    NeMo RL "DFlash Draft Body", Scope: training updates W_proj; angelspec
+    "DFlash", How it works: the target's hidden states are projected into every
+    layer's K/V). With C = X W_proj^T, Kc_l = RoPE(C Wk_l^T), Vc_l = C Wv_l^T and
+    upstream gradients dKc_l, dVc_l:
+        dC = sum_l Gk_l Wk_l + Gv_l Wv_l     [T, H]
+        dW_proj = dC^T X                       [H, L_t*H_t]
+    Returns (dC, dW_proj)."""
+    X = np.asarray(X, np.float64)
+    Gk, Gv = ctx_grad_rows(d_ctx_k, d_ctx_v, positions, num_kv_heads, head_dim, theta)
+    dC = np.zeros((X.shape[0], np.asarray(layers[0]["wk"]).shape[1]))
+    for l, W in enumerate(layers):
+        dC += Gk[l] @ np.asarray(W["wk"], np.float64) + Gv[l] @ np.asarray(W["wv"], np.float64)
+    return dC, dC.T @ X

@@ -73,3 +73,72 @@ def test_structure_of_the_gradients():
     _, _, dvb, _, dcv1 = block_attention_backward(q4, k4, v.reshape(nb, bs, Hkv, D), ck, cv, base, anchor, ones)
     total = dvb.sum(axis=(0, 1)) + dcv1.sum(axis=1)       # [Hkv, D]
     assert np.allclose(total, nb * bs * (Hq // Hkv))
+
+
+# ---------------------------------------------------------------- context path
+def _ctx_case(seed):
+    rng = np.random.default_rng(seed)
+    T, K_in, H, Hkv, D, L = 6, 10, 8, 2, 4, 2
+    X = rng.standard_normal((T, K_in))
+    w_proj = rng.standard_normal((H, K_in))
+    layers = [{"wk": rng.standard_normal((Hkv * D, H)), "wv": rng.standard_normal((Hkv * D, H))} for _ in range(L)]
+    pos = rng.integers(0, 50, T)
+    gk = [rng.standard_normal((Hkv, T, D)) for _ in range(L)]
+    gv = [rng.standard_normal((Hkv, T, D)) for _ in range(L)]
+    return X, w_proj, layers, pos, gk, gv, (Hkv, D, 1e4)
+
+
+def _ctx_loss_of_c(C, layers, pos, gk, gv, dims):
+    Hkv, D, theta = dims
+    ks, vs = oracle.ctx_kv(C, layers, pos, Hkv, D, theta)
+    return sum(float((a * b).sum()) for a, b in zip(ks + vs, gk + gv))
+
+
+def _ctx_loss(w_proj, X, layers, pos, gk, gv, dims):
+    return _ctx_loss_of_c(oracle.ctx_proj(X, w_proj), layers, pos, gk, gv, dims)
+
+
+def test_ctx_backward_matches_directional_differences():
+    # The context path is linear in W_proj and in C, so a central difference
+    # along any direction E equals <grad, E> up to rounding.
+    X, w_proj, layers, pos, gk, gv, dims = _ctx_case(2)
+    dC, dW = oracle.ctx_proj_backward(X, pos, layers, gk, gv, *dims)
+    rng = np.random.default_rng(3)
+    for _ in range(3):
+        E = rng.standard_normal(w_proj.shape)
+        h = 1e-3
+        num = (_ctx_loss(w_proj + h * E, X, layers, pos, gk, gv, dims)
+               - _ctx_loss(w_proj - h * E, X, layers, pos, gk, gv, dims)) / (2 * h)
+        assert abs(num - float((dW * E).sum())) <= 1e-9 * max(1.0, abs(num))
+        Ec = rng.standard_normal(dC.shape)
+        C = oracle.ctx_proj(X, w_proj)
+        num_c = (_ctx_loss_of_c(C + h * Ec, layers, pos, gk, gv, dims)
+                 - _ctx_loss_of_c(C - h * Ec, layers, pos, gk, gv, dims)) / (2 * h)
+        assert abs(num_c - float((dC * Ec).sum())) <= 1e-9 * max(1.0, abs(num_c))
+
+
+def test_ctx_backward_entrywise():
+    X, w_proj, layers, pos, gk, gv, dims = _ctx_case(4)
+    _, dW = oracle.ctx_proj_backward(X, pos, layers, gk, gv, *dims)
+    num = np.zeros_like(w_proj)
+    for i in range(w_proj.shape[0]):
+        for j in range(w_proj.shape[1]):
+            E = np.zeros_like(w_proj)
+            E[i, j] = 1.0
+            num[i, j] = (_ctx_loss(w_proj + E, X, layers, pos, gk, gv, dims)
+                         - _ctx_loss(w_proj - E, X, layers, pos, gk, gv, dims)) / 2
+    assert np.allclose(dW, num, rtol=1e-10, atol=1e-9)
+
+
+def test_ctx_grad_rows_undo_the_rotation():
+    # At position 0 RoPE is the identity; at any position the rotated-back
+    # gradient keeps each pair's norm.
+    rng = np.random.default_rng(5)
+    gk = [rng.standard_normal((2, 3, 8))]
+    gv = [rng.standard_normal((2, 3, 8))]
+    Gk, Gv = oracle.ctx_grad_rows(gk, gv, [0, 7, 123], 2, 8, 1e4)
+    assert np.allclose(Gk[0][0], gk[0][:, 0, :].reshape(-1))
+    a = Gk[0].reshape(3, 2, 2, 4)
+    b = gk[0].transpose(1, 0, 2).reshape(3, 2, 2, 4)
+    assert np.allclose((a * a).sum(axis=2), (b * b).sum(axis=2))
+    assert np.allclose(Gv[0], gv[0].transpose(1, 0, 2).reshape(3, -1))
