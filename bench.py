@@ -291,8 +291,30 @@ def next_rows(d, torch, device="cuda"):
     flops = 10.0 * bs * D * Hq * keys
     ach = flops / (ms / 1e3) / 1e12
     out["attn_backward"] = {"blocks": nb, "ctx_total": T, "ms": round(ms, 4),
-                            "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_VALU_F32_TFLOPS,
-                                         "unit": "TFLOP/s", "frac": round(ach / PEAK_VALU_F32_TFLOPS, 4)}}
+                            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_TFLOPS["bf16"],
+                                         "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
+    del qa, ka, va, oa, doa, cka, cva, grads, ws3
+    # Training side: gradient of W_proj through the context path (every layer's
+    # context K/V gradient -> dC -> dW_proj) over the 32768 context rows.
+    Kin = wt.num_target_layers * wt.target_hidden
+    X3 = mk(T, Kin)
+    pos3 = (torch.arange(T, device=device) % wt.seq_len).to(torch.int32)
+    layers3 = [layer_weights(wt, Rng(2025, device), l) for l in range(wt.num_layers)]
+    gk3 = [torch.randn((Hkv, T, D), generator=gen, device=device) for _ in range(wt.num_layers)]
+    gv3 = [torch.randn((Hkv, D, T), generator=gen, device=device) for _ in range(wt.num_layers)]
+    dW3 = torch.empty((wt.hidden, Kin), dtype=torch.float32, device=device)
+    ws4 = torch.empty(d.dflash_ctx_proj_backward_workspace_size(cfg3, T), dtype=torch.uint8, device=device)
+    call = lambda: d.dflash_ctx_proj_backward(cfg3, X3, Kin, wt.target_hidden, T, pos3, layers3, gk3, gv3, T, 0,
+                                              dW3, None, ws4)
+    parts = {k: hook_ms(d, torch, [(k, 1)], call) for k in ("ctx_bwd_pack", "ctx_bwd_dc", "ctx_bwd_dw")}
+    ms = sum(parts.values())
+    kg = 2 * wt.num_layers * Hkv * D
+    flops = 2.0 * T * wt.hidden * kg + 2.0 * wt.hidden * Kin * T
+    ach = flops / (ms / 1e3) / 1e12
+    out["ctx_proj_backward"] = {"rows": T, "ms": round(ms, 4), **{k + "_ms": round(v, 4) for k, v in parts.items()},
+                                "roofline": {"bound": "mfma", "achieved": round(ach, 2),
+                                             "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+                                             "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
     return out
 
 

@@ -10,6 +10,7 @@ The names mirror the C entry points:
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
+  dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
   dflash_workspace_size, dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
@@ -31,13 +32,15 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
+            "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
 # dflash_kernel ids for the measurement hook
 KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "attention": 5,
            "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10,
-           "lm_head": 11, "lm_ce": 12, "attn_bwd": 13}
+           "lm_head": 11, "lm_ce": 12, "attn_bwd": 13,
+           "ctx_bwd_pack": 14, "ctx_bwd_dc": 15, "ctx_bwd_dw": 16}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -95,6 +98,10 @@ def _load() -> ctypes.CDLL:
     lib.dflash_block_attn_backward.restype = ctypes.c_int
     lib.dflash_block_attn_backward_workspace_size.argtypes = [CFG, I32]
     lib.dflash_block_attn_backward_workspace_size.restype = ctypes.c_size_t
+    lib.dflash_ctx_proj_backward.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, I64, I64, P, P, P, SZ, P]
+    lib.dflash_ctx_proj_backward.restype = ctypes.c_int
+    lib.dflash_ctx_proj_backward_workspace_size.argtypes = [CFG, I64]
+    lib.dflash_ctx_proj_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
     lib.dflash_workspace_size.restype = ctypes.c_size_t
     lib.dflash_check_config.argtypes = [CFG]
@@ -313,6 +320,23 @@ def dflash_block_attn_backward(cfg: DFlashConfig, num_blocks: int, q, k_blk, v_b
                                         _ptr(d_k_blk), _ptr(d_v_blk), _ptr(d_ctx_k), _ptr(d_ctx_v), wp, wb,
                                         _stream(stream, q))
     _check("dflash_block_attn_backward", s)
+
+
+def dflash_ctx_proj_backward_workspace_size(cfg: DFlashConfig, num_rows: int) -> int:
+    return _lib.dflash_ctx_proj_backward_workspace_size(ctypes.byref(cfg), int(num_rows))
+
+
+def dflash_ctx_proj_backward(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
+                             num_rows: int, positions, layers, d_ctx_k, d_ctx_v, ctx_total: int, row_offset: int,
+                             d_w_proj, d_ctx_hidden, workspace, stream=None) -> None:
+    lw = _layers(layers)
+    gk, gv = _ptr_array(d_ctx_k), _ptr_array(d_ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_ctx_proj_backward(ctypes.byref(cfg), _ptr(target_states), int(ts_row_stride),
+                                      int(ts_layer_stride), int(num_rows), _ptr(positions), lw, gk, gv,
+                                      int(ctx_total), int(row_offset), _ptr(d_w_proj), _ptr(d_ctx_hidden), wp, wb,
+                                      _stream(stream, d_w_proj))
+    _check("dflash_ctx_proj_backward", s)
 
 
 def dflash_profile_start(kernel, max_launches: int) -> None:

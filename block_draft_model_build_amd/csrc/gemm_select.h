@@ -1,0 +1,26 @@
+// Tile-shape choice shared by every libdflash GEMM call site.
+#pragma once
+
+#include "gemm.h"
+#include "internal.h"
+
+namespace dflash {
+
+// 256x256 tiles with 8 waves (two per SIMD, 64x128 each) and 128-byte K slabs
+// double buffered in LDS (the best of a measured sweep over tile shapes, wave
+// counts, slab depths and stage counts on the context-projection, gate/up and
+// down shapes); 128x128 tiles with 4 waves (one 32-row MFMA strip each) when
+// the big tiles would leave compute units idle.
+using BigTile = TileCfg<256, 256, 4, 2, 128, 2>;
+using MidTile = TileCfg<128, 128, 4, 1>;
+static_assert(BigTile::WN == 128 && MidTile::WN == 128, "gate/up interleave and RoPE pairing assume WN = 128");
+
+template <typename T, class AL, class BL, class EP>
+static hipError_t gemm(int kid, int M, int N, int K, const AL& al, const BL& bl, const EP& ep, hipStream_t st) {
+    ProfScope prof(kid, st);
+    const int big_tiles = ((M + 255) / 256) * (N / 256);
+    if (N % 256 == 0 && big_tiles >= 256) return launch_gemm<T, BigTile>(M, N, K, al, bl, ep, st);
+    return launch_gemm<T, MidTile>(M, N, K, al, bl, ep, st);
+}
+
+}  // namespace dflash

@@ -280,7 +280,10 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_LM_HEAD = 11,      /* GEMM h W_lm^T with per-group softmax statistics */
     DFLASH_KERNEL_LM_CE = 12,        /* per-row CE and the decayed loss */
     DFLASH_KERNEL_ATTN_BWD = 13,     /* dflash_block_attn_backward (both kernels) */
-    DFLASH_KERNEL_COUNT = 14
+    DFLASH_KERNEL_CTX_BWD_PACK = 14, /* dflash_ctx_proj_backward: gradient packing and transposes */
+    DFLASH_KERNEL_CTX_BWD_DC = 15,   /* GEMM dC = G [Wk; Wv] */
+    DFLASH_KERNEL_CTX_BWD_DW = 16,   /* GEMM dW_proj = dC^T X */
+    DFLASH_KERNEL_COUNT = 17
 } dflash_kernel;
 
 /*
@@ -416,6 +419,44 @@ dflash_status dflash_block_attn_backward(const dflash_config *cfg, int32_t num_b
                                          float *d_ctx_v, void *workspace, size_t workspace_bytes,
                                          void *hip_stream);
 size_t dflash_block_attn_backward_workspace_size(const dflash_config *cfg, int32_t num_blocks);
+
+/*
+ * dflash_ctx_proj_backward -- gradient of the projection W_proj through the
+ * context path. [P2] "Scope": training updates the body's weights with an
+ * optimizer step, W_proj among them; [P1] "How it works", dual-source KV
+ * context: the target states reach every layer's K/V through W_proj.
+ *
+ * With the forward of dflash_ctx_proj (C = X W_proj^T, Kc_l = RoPE(C Wk_l^T),
+ * Vc_l = C Wv_l^T) and the gradients of every layer's cache rows
+ * [row_offset, row_offset + num_rows):
+ *   Gk_l[r] = RoPE^T(d_ctx_k[l][g][row_offset + r][:], positions[r])   per head g
+ *   Gv_l[r] = d_ctx_v[l][g][:][row_offset + r]                          per head g
+ *   dC      = sum_l Gk_l Wk_l + Gv_l Wv_l                               [num_rows, H]
+ *   d_w_proj = dC^T X                                                   [H, L_t*H_t]
+ * RoPE^T is the rotation by the opposite angle.
+ *
+ *   target_states, ts_row_stride, ts_layer_stride, positions, layers
+ *                  as dflash_ctx_proj (only wk and wv of the layers are read)
+ *   d_ctx_k, d_ctx_v  host arrays [num_layers] of device f32 gradients in the
+ *                  caches' layouts: K [Hkv][ctx_total][D] (rotated frame, as
+ *                  dflash_block_attn_backward writes it), V [Hkv][D][ctx_total]
+ *   d_w_proj       device f32 [H, L_t*H_t], overwritten (zero when num_rows == 0)
+ *   d_ctx_hidden   optional device f32 [num_rows, H]: dC (NULL: not written)
+ *   workspace      dflash_ctx_proj_backward_workspace_size(cfg, num_rows) bytes,
+ *                  256-byte aligned
+ * G and dC enter their products in the config dtype; the products accumulate in
+ * fp32. Errors: INVALID_ARG as dflash_ctx_proj or for a null d_w_proj;
+ * UNSUPPORTED when L_t*H_t is not a multiple of 128; WORKSPACE when the
+ * workspace is missing, small or misaligned.
+ */
+dflash_status dflash_ctx_proj_backward(const dflash_config *cfg, const void *target_states,
+                                       int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                       const int32_t *positions, const dflash_layer_weights *layers,
+                                       const float *const *d_ctx_k, const float *const *d_ctx_v,
+                                       int64_t ctx_total, int64_t row_offset, float *d_w_proj,
+                                       float *d_ctx_hidden, void *workspace, size_t workspace_bytes,
+                                       void *hip_stream);
+size_t dflash_ctx_proj_backward_workspace_size(const dflash_config *cfg, int64_t num_rows);
 
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one

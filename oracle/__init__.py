@@ -44,7 +44,9 @@ from .verify import (
     inverse_cdf_draw, residual_weights, accept_proposal,
 )
 from .loss import lm_head_ce, lm_head_ce_rows, token_ce, logsumexp_rows, position_weights
-from .backward import block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_proj_backward
+from .backward import (
+    block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_hidden_grad, ctx_proj_backward,
+)
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
     dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
@@ -59,5 +61,5 @@ __all__ = [
     "verify_greedy_block", "verify_greedy", "target_choices_from_logits", "verify_sample_block",
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
     "lm_head_ce", "lm_head_ce_rows", "token_ce", "logsumexp_rows", "position_weights",
-    "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_proj_backward",
+    "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_hidden_grad", "ctx_proj_backward",
 ]

@@ -115,6 +115,17 @@ def ctx_grad_rows(d_ctx_k, d_ctx_v, positions, num_kv_heads: int, head_dim: int,
     return Gk, Gv
 
 
+def ctx_hidden_grad(d_ctx_k, d_ctx_v, positions, layers, num_kv_heads: int, head_dim: int, theta: float):
+    """dC = sum_l Gk_l Wk_l + Gv_l Wv_l [T, H] (the rows of C are independent, so
+    any subset of rows with their positions gives those rows of dC; any subset
+    of the weights' columns gives those columns)."""
+    Gk, Gv = ctx_grad_rows(d_ctx_k, d_ctx_v, positions, num_kv_heads, head_dim, theta)
+    dC = 0.0
+    for l, W in enumerate(layers):
+        dC = dC + Gk[l] @ np.asarray(W["wk"], np.float64) + Gv[l] @ np.asarray(W["wv"], np.float64)
+    return dC
+
+
 def ctx_proj_backward(X, positions, layers, d_ctx_k, d_ctx_v, num_kv_heads: int, head_dim: int, theta: float):
     """Gradients through the context path (ctx_proj, then ctx_kv of every layer;
     NeMo RL "DFlash Draft Body", Scope: training updates W_proj; angelspec
@@ -125,8 +136,5 @@ def ctx_proj_backward(X, positions, layers, d_ctx_k, d_ctx_v, num_kv_heads: int,
         dW_proj = dC^T X                       [H, L_t*H_t]
     Returns (dC, dW_proj)."""
     X = np.asarray(X, np.float64)
-    Gk, Gv = ctx_grad_rows(d_ctx_k, d_ctx_v, positions, num_kv_heads, head_dim, theta)
-    dC = np.zeros((X.shape[0], np.asarray(layers[0]["wk"]).shape[1]))
-    for l, W in enumerate(layers):
-        dC += Gk[l] @ np.asarray(W["wk"], np.float64) + Gv[l] @ np.asarray(W["wv"], np.float64)
+    dC = ctx_hidden_grad(d_ctx_k, d_ctx_v, positions, layers, num_kv_heads, head_dim, theta)
     return dC, dC.T @ X

@@ -148,6 +148,18 @@ def test_rejects_bad_arguments_before_launch():
                                           None) == d.DFLASH_OK
     assert d.dflash_block_attn_backward_workspace_size(cfg, 4) > 0
     assert d.dflash_block_attn_backward_workspace_size(cfg, -1) == 0
+    # context-path backward: rows past the cache, null output, unsupported width, small workspace
+    G = (ctypes.c_void_p * cfg.num_layers)(*([fake] * cfg.num_layers))
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 100, P(fake), lw, G, G, 50, 0,
+                                        P(fake), None, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
+                                        None, None, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
+                                        P(fake), None, P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+    odd = d.config_from_workload(scaled(WORKLOADS["c2"], target_hidden=4032))
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(odd), P(fake), 5 * 4032, 4032, 10, P(fake), lw, G, G, 50, 0,
+                                        P(fake), None, P(fake), 1 << 40, None) == d.DFLASH_ERR_UNSUPPORTED
+    assert d.dflash_ctx_proj_backward_workspace_size(cfg, 100) > d.dflash_ctx_proj_backward_workspace_size(cfg, 10)
     # body: a null weight
     lw[0].w_up = None
     assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
