@@ -9,7 +9,7 @@
 //   dW_proj = dC^T X                                                            [H, L_t H_t]
 // Both products run on the K-contiguous MFMA GEMM of gemm.h; the operands
 // whose contraction runs down their rows (the stacked K/V weights, dC and X)
-// are first transposed through LDS tiles.
+// are transposed on the way (LDS tiles; dC in the first product's epilogue).
 #include "gemm_select.h"
 #include "internal.h"
 
@@ -72,33 +72,46 @@ __global__ __launch_bounds__(256) void grad_pack_v_kernel(GradPtrs gp, int64_t r
 
 template <typename T> struct SrcPlain {
     const T* p; int64_t ld;
-    __device__ float operator()(int64_t r, int64_t c) const { return to_f32(p[r * ld + c]); }
+    __device__ const T* at(int64_t r, int64_t c) const { return p + r * ld + c; }
 };
 // Element (r, k) of the concatenated target states, as dflash_ctx_proj reads them.
 template <typename T> struct SrcStacked {
     const T* p; int64_t rs, ls; int ht;
-    __device__ float operator()(int64_t r, int64_t c) const {
+    __device__ const T* at(int64_t r, int64_t c) const {
         const int64_t layer = c / ht;
-        return to_f32(p[r * rs + layer * ls + (c - layer * ht)]);
+        return p + r * rs + layer * ls + (c - layer * ht);
     }
 };
 
-// dst[c * ldd + r] = src(r, c) for r < rows_pad (zero past rows), c < cols.
+// dst[c * ldd + r] = src(r, c) for r < rows_pad (zero past rows), c < cols, in
+// 64 x 64 tiles through LDS with 16-byte loads along c and 16-byte stores
+// along r. cols is a multiple of 64; src rows hold 16-byte aligned runs of
+// V = 16 / sizeof(T) elements (a run never straddles two target layers);
+// ldd and the column offset of dst keep 16-byte alignment.
 template <typename T, class Src>
 __global__ __launch_bounds__(256) void transpose_kernel(Src src, int64_t rows, int64_t rows_pad, int64_t cols, T* dst,
                                                         int64_t ldd) {
+    constexpr int V = 16 / (int)sizeof(T);
+    typedef T vec __attribute__((ext_vector_type(V)));
     __shared__ float tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-        const int rr = idx >> 6, cc = idx & 63;
-        const int64_t r = r0 + rr, c = c0 + cc;
-        tile[rr][cc] = (r < rows && c < cols) ? src(r, c) : 0.f;
+    for (int idx = threadIdx.x; idx < 64 * (64 / V); idx += 256) {
+        const int rr = idx / (64 / V), cv = (idx - rr * (64 / V)) * V;
+        const int64_t r = r0 + rr;
+        vec v = {};
+        if (r < rows) v = *reinterpret_cast<const vec*>(src.at(r, c0 + cv));
+#pragma unroll
+        for (int q = 0; q < V; ++q) tile[rr][cv + q] = to_f32(v[q]);
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-        const int cc = idx >> 6, rr = idx & 63;
-        const int64_t r = r0 + rr, c = c0 + cc;
-        if (r < rows_pad && c < cols) dst[c * ldd + r] = from_f32<T>(tile[rr][cc]);
+    for (int idx = threadIdx.x; idx < 64 * (64 / V); idx += 256) {
+        const int cc = idx / (64 / V), rv = (idx - cc * (64 / V)) * V;
+        const int64_t r = r0 + rv;
+        if (r >= rows_pad) continue;
+        vec v;
+#pragma unroll
+        for (int q = 0; q < V; ++q) v[q] = from_f32<T>(tile[rv + q][cc]);
+        *reinterpret_cast<vec*>(dst + (c0 + cc) * ldd + r) = v;
     }
 }
 
@@ -254,7 +267,8 @@ extern "C" dflash_status dflash_ctx_proj_backward(const dflash_config* cfg, cons
         return DFLASH_ERR_INVALID_ARG;
     GradPtrs gp{};
     for (int l = 0; l < cfg->num_layers; ++l) {
-        if (layers[l].wk == nullptr || layers[l].wv == nullptr || d_ctx_k[l] == nullptr || d_ctx_v[l] == nullptr)
+        if (layers[l].wk == nullptr || layers[l].wv == nullptr || d_ctx_k[l] == nullptr || d_ctx_v[l] == nullptr ||
+            !aligned16(layers[l].wk) || !aligned16(layers[l].wv))
             return DFLASH_ERR_INVALID_ARG;
         gp.dk[l] = d_ctx_k[l];
         gp.dv[l] = d_ctx_v[l];
