@@ -185,7 +185,10 @@ def next_rows(d, torch, device="cuda"):
     verify_greedy / verify_sample = verification of the 64 drafted blocks over a
     151936-token vocabulary, with their HBM rooflines; and, on the training
     side, lm_head_ce = LM head + decayed cross-entropy over the 5-layer body's
-    4096 block rows (151936 x 4096 head), with its MFMA roofline."""
+    4096 block rows (151936 x 4096 head), attn_backward = one layer's
+    dual-source attention backward at the training shape, and
+    ctx_proj_backward = dW_proj through every layer's context K/V over the
+    32768 context rows, each with its MFMA roofline."""
     import math as _m
     from dflash_synth import WORKLOADS, Rng, layer_weights
     w = WORKLOADS["c5"]
