@@ -477,19 +477,15 @@ __device__ __forceinline__ void dma_rows(char* tile, RowPtr rowptr, int wave, in
 struct QueryLds {
     char k[2][KT * 256];     // K~ chunk (swizzled rows), two stages
     char vt[2][D * 128];     // V^T chunk, two stages
-    __bf16 q[KT][D];         // Q~ and masked dO of the block (plain rows)
-    __bf16 dout[KT][D];
-    float p[KT][KT + 1];     // own chunk: P^T and dS^T [key][column]
-    float ds[KT][KT + 1];
     float m[2][KT], l[2][KT];
 };
 
 struct CtxLds {
     char k[KT * 256];        // K~ tile
     char vt[D * 128];        // V^T tile
-    char q[2][KT * 256];     // Q~ of the current and the next block
-    char dout[2][KT * 256];  // masked dO of the current and the next block
-    float lse[2][KT], delta[2][KT];
+    char q[KT * 256];        // Q~ of the current block
+    char dout[KT * 256];     // masked dO of the current block
+    float lse[KT], delta[KT];
     int list[256], list_an[256];
     int64_t list_base[256];
     int cnt[4];
@@ -500,8 +496,10 @@ struct MfArgs {
     __bf16 *qt, *dot;        // workspace [nb][Hkv][64][128]: Q~ and masked dO per block
 };
 
-// Query-major kernel: one workgroup per (block, KV head).
-__global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
+// Query-major kernel: one workgroup per (block, KV head). Scores are kept in
+// log2 units (Q~ carries log2(e) / sqrt(D)), so every probability is one exp2.
+// Small enough (registers, 64 KB of LDS) for two workgroups per compute unit.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_query_kernel(MfArgs m) {
     const BwArgs<__bf16>& a = m.a;
     __shared__ QueryLds L;
     const int item = xcd_item(blockIdx.x, a.nb * a.hkv);
@@ -509,6 +507,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
     const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
     const int G = a.hq / a.hkv, bs = a.bs, C = bs * G;
     const float scale = 1.f / sqrtf((float)D);
+    const float qscale = 1.4426950408889634f * scale;     // log2(e) / sqrt(D)
     const int64_t base = clamp_base(a.base[n], a.ctx_total);
     const int an = anchor_eff(a.anchor[n], base, a.ctx_total);
     const int64_t slot = (int64_t)n * a.hkv + g;
@@ -561,8 +560,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
                 float cs, sn;
                 rope_cs(a.rt, 16 * ks + 8 * h + i, an + kq, cs, sn);
                 const float x1 = (float)lo[i], x2 = (float)hi[i];
-                qf[ks][i] = static_cast<__bf16>((x1 * cs - x2 * sn) * scale);
-                qf[ks + 4][i] = static_cast<__bf16>((x2 * cs + x1 * sn) * scale);
+                qf[ks][i] = static_cast<__bf16>((x1 * cs - x2 * sn) * qscale);
+                qf[ks + 4][i] = static_cast<__bf16>((x2 * cs + x1 * sn) * qscale);
             }
             df[ks] = dlo;
             df[ks + 4] = dhi;
@@ -571,7 +570,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
         if (!col_ok) delta = 0.f;
     }
     if (wn == 0) {
-        // Q~ and masked dO for the context kernel (workspace) and for the own keys (LDS).
+        // Q~ and masked dO for the context kernel and the own keys (workspace).
         __bf16* qt = m.qt + slot * KT * D + (int64_t)c * D;
         __bf16* dt = m.dot + slot * KT * D + (int64_t)c * D;
 #pragma unroll
@@ -579,113 +578,93 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
             const int d0 = 16 * ks + 8 * h;
             *(bf16x8*)(qt + d0) = qf[ks];
             *(bf16x8*)(dt + d0) = df[ks];
-            *(bf16x8*)(&L.q[c][d0]) = qf[ks];
-            *(bf16x8*)(&L.dout[c][d0]) = df[ks];
         }
         if (h == 0) a.delta[slot * KT + c] = delta;
     }
 
-    // Chunks: context keys [0, an) in 64-key chunks, then the block's own keys.
+    // Context keys [0, an) in 64-key chunks (DMA, K rows clamped to the last
+    // visible one), then the block's own keys (rotated here).
     const int nctx = (an + KT - 1) / KT;
-    const int nchunks = nctx + 1;
-    auto stage = [&](int ch, bool with_v) {
-        char* Lk = L.k[ch & 1];
-        char* Lvt = L.vt[ch & 1];
-        if (ch < nctx) {
-            const int j0 = ch * KT;
-            dma_rows(Lk, [&](int r) { return ckg + (int64_t)min(j0 + r, an - 1) * D; }, w, lane);
-            if (with_v) {
-                if ((int64_t)j0 + KT <= lim) {
+    auto stage_ctx = [&](int ch, int buf) {
+        char* Lk = L.k[buf];
+        char* Lvt = L.vt[buf];
+        const int j0 = ch * KT;
+        dma_rows(Lk, [&](int r) { return ckg + (int64_t)min(j0 + r, an - 1) * D; }, w, lane);
+        if ((int64_t)j0 + KT <= lim) {
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int u0 = (it * 4 + w) * 64, u = u0 + lane;
-                        const int d = u >> 3, cc = u & 7;
-                        dma16(cvg + (int64_t)d * a.ctx_total + j0 + ((cc ^ (d & 7)) << 3), Lvt + u0 * 16);
-                    }
-                } else {
-                    // Chunk reaching the end of the cache: element loads, keys clamped.
-                    for (int idx = tid; idx < D * KT; idx += 256) {
-                        const int d = idx / KT, j = idx - d * KT;
-                        const int64_t jj = min((int64_t)(j0 + j), lim - 1);
-                        *(__bf16*)(Lvt + voff(d, j)) = cvg[(int64_t)d * a.ctx_total + jj];
-                    }
-                }
+            for (int it = 0; it < 4; ++it) {
+                const int u0 = (it * 4 + w) * 64, u = u0 + lane;
+                const int d = u >> 3, cc = u & 7;
+                dma16(cvg + (int64_t)d * a.ctx_total + j0 + ((cc ^ (d & 7)) << 3), Lvt + u0 * 16);
             }
         } else {
-            // Own keys: row r of the block rotated at an + r; zero past the block.
-            for (int idx = tid; idx < KT * (D / 2); idx += 256) {
-                const int r = idx / (D / 2), i = idx - r * (D / 2);
-                float y1 = 0.f, y2 = 0.f;
-                if (r < bs) {
-                    const __bf16* kr = a.kb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
-                    const float x1 = (float)kr[i], x2 = (float)kr[i + D / 2];
-                    float cs, sn;
-                    rope_cs(a.rt, i, an + r, cs, sn);
-                    y1 = x1 * cs - x2 * sn;
-                    y2 = x2 * cs + x1 * sn;
-                }
-                *(__bf16*)(Lk + koff(r, i)) = static_cast<__bf16>(y1);
-                *(__bf16*)(Lk + koff(r, i + D / 2)) = static_cast<__bf16>(y2);
-            }
-            if (with_v) {
-                for (int idx = tid; idx < KT * D; idx += 256) {
-                    const int r = idx / D, d = idx - r * D;
-                    __bf16 v = static_cast<__bf16>(0.f);
-                    if (r < bs) v = a.vb[(int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D + d];
-                    *(__bf16*)(Lvt + voff(d, r)) = v;
-                }
+            // Chunk reaching the end of the cache: element loads, keys clamped.
+            for (int idx = tid; idx < D * KT; idx += 256) {
+                const int d = idx / KT, j = idx - d * KT;
+                const int64_t jj = min((int64_t)(j0 + j), lim - 1);
+                *(__bf16*)(Lvt + voff(d, j)) = cvg[(int64_t)d * a.ctx_total + jj];
             }
         }
     };
-    auto nvalid = [&](int ch) { return ch < nctx ? min(KT, an - ch * KT) : bs; };
-    // S^T tile of this wave: keys 32 wn + key_perm(row), columns 32 wm + l32.
-    auto scores = [&](const char* Lk) {
-        f32x16 s = {};
-        const int kr = 32 * wn + key_perm(l32);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) s = Mfma<__bf16>::mma(lds_frag(Lk, koff(kr, 16 * ks + 8 * h)), qf[ks], s);
-        return s;
+    auto stage_own = [&](int buf) {
+        char* Lk = L.k[buf];
+        char* Lvt = L.vt[buf];
+        for (int idx = tid; idx < KT * (D / 2); idx += 256) {
+            const int r = idx / (D / 2), i = idx - r * (D / 2);
+            float y1 = 0.f, y2 = 0.f;
+            if (r < bs) {
+                const __bf16* kr = a.kb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
+                const float x1 = (float)kr[i], x2 = (float)kr[i + D / 2];
+                float cs, sn;
+                rope_cs(a.rt, i, an + r, cs, sn);
+                y1 = x1 * cs - x2 * sn;
+                y2 = x2 * cs + x1 * sn;
+            }
+            *(__bf16*)(Lk + koff(r, i)) = static_cast<__bf16>(y1);
+            *(__bf16*)(Lk + koff(r, i + D / 2)) = static_cast<__bf16>(y2);
+        }
+        for (int idx = tid; idx < KT * D; idx += 256) {
+            const int r = idx / D, d = idx - r * D;
+            __bf16 v = static_cast<__bf16>(0.f);
+            if (r < bs) v = a.vb[(int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D + d];
+            *(__bf16*)(Lvt + voff(d, r)) = v;
+        }
     };
 
-    // One pass over the chunks with a running maximum m per column (online
-    // softmax): p~ = exp(s - m), l = sum p~, dQ~ accumulates dS~ K~ with
-    // dS~ = p~ (dP - delta), and everything is rescaled when m moves. At the
-    // end P = p~ / l and dQ~ = (sum dS~ K~) / l. m only moves when a chunk's
-    // maximum exceeds it by more than 8 (p~ stays below e^8), so rescales are
-    // rare after the first chunk.
+    // One pass with a running maximum m per column (online softmax):
+    // p~ = 2^(s - m), l = sum p~, dQ~ accumulates dS~ K~ with dS~ = p~ (dP - delta),
+    // rescaled when m moves; at the end P = p~ / l and dQ~ = (sum dS~ K~) / l.
+    // m only moves when a chunk's maximum exceeds it by more than 8 (p~ stays
+    // below 2^8), so rescales are rare after the first chunk.
     float mrun = -__builtin_inff(), lrun = 0.f;
     f32x16 dq[4] = {};
-    f32x16 p_own = {}, ds_own = {};
-    __syncthreads();
-    stage(0, true);
-    for (int ch = 0; ch < nchunks; ++ch) {
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (ch + 1 < nchunks) stage(ch + 1, true);
-        const char* Lk = L.k[ch & 1];
-        const char* Lvt = L.vt[ch & 1];
-        const f32x16 s = scores(Lk);
-        f32x16 dp = {};
-        {
-            const int i = lane & 15, Gq = lane >> 4;
-            const int kc = 32 * wn + 16 * (Gq & 1) + perm_col(i & 3);
+    const int i16 = lane & 15, G16 = lane >> 4;
+    const int kcol = 32 * wn + 16 * (G16 & 1) + perm_col(i16 & 3);   // V^T column (key) of this lane's A rows
+    const int krow = 32 * wn + key_perm(l32);                         // K~ row of this lane's A rows
+    // nv: keys of the chunk that are visible; p and ds come back in p / ds.
+    auto chunk = [&](const char* Lk, const char* Lvt, int nv, f32x16& p, f32x16& ds) {
+        f32x16 s = {}, dp = {};
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int d0 = 16 * ks + 8 * h + (i >> 2);
-                const bf16x8 va = join(lds_tr(Lvt + voff(d0, kc)), lds_tr(Lvt + voff(d0 + 4, kc)));
-                dp = Mfma<__bf16>::mma(va, df[ks], dp);
-            }
+        for (int ks = 0; ks < 8; ++ks) {
+            s = Mfma<__bf16>::mma(lds_frag(Lk, koff(krow, 16 * ks + 8 * h)), qf[ks], s);
+            const int d0 = 16 * ks + 8 * h + (i16 >> 2);
+            const bf16x8 va = join(lds_tr(Lvt + voff(d0, kcol)), lds_tr(Lvt + voff(d0 + 4, kcol)));
+            dp = Mfma<__bf16>::mma(va, df[ks], dp);
         }
-        const int nv = nvalid(ch) - 32 * wn - 8 * h;       // keys acc_key(e) < nv are valid
-        float mx = -__builtin_inff();
+        if (nv < KT) {
+            const int nvl = nv - 32 * wn - 8 * h;       // keys acc_key(e) < nvl are visible
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (acc_key(e) < nv) mx = fmaxf(mx, s[e]);
+            for (int e = 0; e < 16; ++e)
+                if (acc_key(e) >= nvl) s[e] = -__builtin_inff();
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));            // both key halves of the column
         const bool move = mx > mrun + 8.f;
         if (__any(move)) {
             const float mnew = move ? mx : mrun;
-            const float f = mrun == -__builtin_inff() ? 0.f : __expf(mrun - mnew);
+            const float f = mrun == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mrun - mnew);
             mrun = mnew;
             lrun *= f;
             // dQ~ accumulator rows are columns: fetch each row's factor from its lane.
@@ -696,17 +675,15 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
                 for (int dt = 0; dt < 4; ++dt) dq[dt][e] *= fe;
             }
         }
-        f32x16 p, ds;
+        const float muse = mrun == -__builtin_inff() ? 0.f : mrun;
+        float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            p[e] = acc_key(e) < nv ? __expf(s[e] - mrun) : 0.f;
-            lrun += p[e];
+            p[e] = __builtin_amdgcn_exp2f(s[e] - muse);
+            ps += p[e];
             ds[e] = p[e] * (dp[e] - delta);
         }
-        if (ch == nctx) {
-            p_own = p;
-            ds_own = ds;
-        }
+        lrun += ps;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const bf16x8 af = pack8(ds, kk);
@@ -714,7 +691,25 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
             for (int dt = 0; dt < 4; ++dt)
                 dq[dt] = Mfma<__bf16>::mma(af, tr_frag_k(Lk, 32 * wn + 16 * kk, 32 * dt, lane), dq[dt]);
         }
+    };
+
+    __syncthreads();
+    if (nctx > 0) stage_ctx(0, 0);
+    else stage_own(0);
+    for (int ch = 0; ch < nctx; ++ch) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (ch + 1 < nctx) stage_ctx(ch + 1, (ch + 1) & 1);
+        else stage_own((ch + 1) & 1);
+        f32x16 p, ds;
+        chunk(L.k[ch & 1], L.vt[ch & 1], min(KT, an - ch * KT), p, ds);
     }
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int so = nctx & 1;                          // stage holding the own keys
+    f32x16 p_own, ds_own;
+    chunk(L.k[so], L.vt[so], bs, p_own, ds_own);
+
     // Column statistics: add the lane halves, then merge the two key halves.
     lrun += __shfl_xor(lrun, 32, 64);
     if (h == 0) {
@@ -726,26 +721,31 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
         const int cc = tid;
         const float m0 = L.m[0][cc], m1 = L.m[1][cc];
         const float mm = fmaxf(m0, m1);
-        const float f0 = m0 == -__builtin_inff() ? 0.f : __expf(m0 - mm);
-        const float f1 = m1 == -__builtin_inff() ? 0.f : __expf(m1 - mm);
+        const float f0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+        const float f1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
         const float ll = L.l[0][cc] * f0 + L.l[1][cc] * f1;
-        // Unused columns get lse = +inf: their probabilities are exactly zero.
+        // lse in log2 units; unused columns get +inf (their probabilities are exactly zero).
         const bool used = cc < C && ll > 0.f;
-        const float lse = used ? mm + __logf(ll) : __builtin_inff();
+        const float lse = used ? mm + __log2f(ll) : __builtin_inff();
         a.lse[slot * KT + cc] = lse;
         // Factor that turns each key half's p~ into P.
         L.m[0][cc] = used ? f0 / ll : 0.f;
         L.m[1][cc] = used ? f1 / ll : 0.f;
     }
     __syncthreads();
+    // The own chunk's P and dS ([key][column], 16 KB each) go to the free stage;
+    // Q~ and dO (plain [column][d] rows) go over the own keys' stage.
+    float* Pown = reinterpret_cast<float*>(L.k[so ^ 1]);
+    float* Down = reinterpret_cast<float*>(L.vt[so ^ 1]);
+    __bf16* Qs = reinterpret_cast<__bf16*>(L.k[so]);
+    __bf16* Ds = reinterpret_cast<__bf16*>(L.vt[so]);
     {
-        // The own chunk's P and dS for the own keys' dK / dV.
         const float f = L.m[wn][c];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int key = 32 * wn + acc_key(e) + 8 * h;
-            L.p[key][c] = p_own[e] * f;
-            L.ds[key][c] = ds_own[e] * f;
+            Pown[key * KT + c] = p_own[e] * f;
+            Down[key * KT + c] = ds_own[e] * f;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -753,20 +753,31 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) dq[dt][e] *= fe;
         }
+        if (wn == 0) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                *(bf16x8*)(Qs + c * D + 16 * ks + 8 * h) = qf[ks];
+                *(bf16x8*)(Ds + c * D + 16 * ks + 8 * h) = df[ks];
+            }
+        }
     }
     __syncthreads();
 
-    // Own keys: dK~ = dS^T Q~, dV = P^T dO over the block's columns; dK~ rotated back.
+    // Own keys: dK~ = dS^T Q~, dV = P^T dO over the block's columns; dK~ rotated
+    // back (and out of log2 units: Q~ carries log2(e)).
+    constexpr float kLn2 = 0.6931471805599453f;
     for (int idx = tid; idx < bs * (D / 2); idx += 256) {
         const int r = idx / (D / 2), i = idx - r * (D / 2);
         float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
         for (int cc = 0; cc < C; ++cc) {
-            const float dsv = L.ds[r][cc], pv = L.p[r][cc];
-            k1 += dsv * (float)L.q[cc][i];
-            k2 += dsv * (float)L.q[cc][i + D / 2];
-            v1 += pv * (float)L.dout[cc][i];
-            v2 += pv * (float)L.dout[cc][i + D / 2];
+            const float dsv = Down[r * KT + cc], pv = Pown[r * KT + cc];
+            k1 += dsv * (float)Qs[cc * D + i];
+            k2 += dsv * (float)Qs[cc * D + i + D / 2];
+            v1 += pv * (float)Ds[cc * D + i];
+            v2 += pv * (float)Ds[cc * D + i + D / 2];
         }
+        k1 *= kLn2;
+        k2 *= kLn2;
         float cs, sn;
         rope_cs(a.rt, i, an + r, cs, sn);
         float* dk = a.dkb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
@@ -776,9 +787,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
         dv[i] = v1;
         dv[i + D / 2] = v2;
     }
+    __syncthreads();
 
     // dQ~: add the two key halves, rotate back, scale.
-    float* red = reinterpret_cast<float*>(L.k[0]);  // K~ stages: 32 KB
+    float* red = reinterpret_cast<float*>(L.k[0]);  // both K~ stages: 32 KB
     if (wn == 1) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -812,8 +824,9 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(MfArgs m) {
 
 // Key-major kernel over the context: one workgroup per (64-row tile, KV head);
 // the blocks that read the tile are visited in index order, so every dK / dV
-// sum has a fixed order.
-__global__ __launch_bounds__(256) void bwd_ctx_kernel(MfArgs m) {
+// sum has a fixed order. Sized (registers, 67 KB of LDS) for two workgroups
+// per compute unit: one loads a block's Q~ / dO while the other computes.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_ctx_kernel(MfArgs m) {
     const BwArgs<__bf16>& a = m.a;
     __shared__ CtxLds L;
     const int tiles = (int)((a.ctx_total + KT - 1) / KT);
@@ -839,26 +852,11 @@ __global__ __launch_bounds__(256) void bwd_ctx_kernel(MfArgs m) {
             *(__bf16*)(L.vt + voff(d, j)) = cvg[(int64_t)d * T + min(t0 + j, T - 1)];
         }
     }
-    wait_vmcnt<0>();
-    __syncthreads();
-    // B operands that stay fixed over the blocks: K~ (S) and V (dP) of key column 32 wn + l32.
-    bf16x8 kf[8], vf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        kf[ks] = lds_frag(L.k, koff(32 * wn + l32, 16 * ks + 8 * h));
-        const int i = lane & 15, Gq = lane >> 4;
-        const int d0 = 16 * ks + 8 * h + (i >> 2), kc = 32 * wn + 16 * (Gq & 1) + 4 * (i & 3);
-        vf[ks] = join(lds_tr(L.vt + voff(d0, kc)), lds_tr(L.vt + voff(d0 + 4, kc)));
-    }
-    const int64_t key = t0 + 32 * wn + l32;
+    const int64_t key = t0 + 32 * wn + l32;            // key column of this lane in S and dP
+    const int i16 = lane & 15, G16 = lane >> 4;
+    const int vcol = 32 * wn + 16 * (G16 & 1) + 4 * (i16 & 3);
+    const int cr = 32 * wm + key_perm(l32);            // Q~ / dO row of this lane's A operands
     f32x16 dk[4] = {}, dv[4] = {};
-    auto load_block = [&](int it, int buf) {
-        const int64_t slot = (int64_t)L.list[it] * a.hkv + g;
-        dma_rows(L.q[buf], [&](int r) { return m.qt + (slot * KT + r) * D; }, w, lane);
-        dma_rows(L.dout[buf], [&](int r) { return m.dot + (slot * KT + r) * D; }, w, lane);
-        if (w == 0 && lane < 16) dma16(a.lse + slot * KT + 4 * lane, (char*)L.lse[buf]);
-        if (w == 1 && lane < 16) dma16(a.delta + slot * KT + 4 * lane, (char*)L.delta[buf]);
-    };
     for (int b0 = 0; b0 < a.nb; b0 += 256) {
         // The blocks of [b0, b0 + 256) that read this tile, in index order.
         const int nn = b0 + tid;
@@ -885,39 +883,43 @@ __global__ __launch_bounds__(256) void bwd_ctx_kernel(MfArgs m) {
             L.list_base[at] = bb;
             L.list_an[at] = ba;
         }
-        __syncthreads();
-        if (total > 0) load_block(0, 0);
         for (int it = 0; it < total; ++it) {
-            const int buf = it & 1;
-            wait_vmcnt<0>();
-            __syncthreads();
-            if (it + 1 < total) load_block(it + 1, buf ^ 1);
+            __syncthreads();                           // the list, and the previous block's reads
+            const int64_t slot = (int64_t)L.list[it] * a.hkv + g;
+            dma_rows(L.q, [&](int r) { return m.qt + (slot * KT + r) * D; }, w, lane);
+            dma_rows(L.dout, [&](int r) { return m.dot + (slot * KT + r) * D; }, w, lane);
+            if (w == 0 && lane < 16) dma16(a.lse + slot * KT + 4 * lane, (char*)L.lse);
+            if (w == 1 && lane < 16) dma16(a.delta + slot * KT + 4 * lane, (char*)L.delta);
             const int64_t base = L.list_base[it];
             const int an = L.list_an[it];
-            const char* Lq = L.q[buf];
-            const char* Ld = L.dout[buf];
+            wait_vmcnt<0>();
+            __syncthreads();
             f32x16 s = {}, dp = {};
-            const int cr = 32 * wm + key_perm(l32);
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                s = Mfma<__bf16>::mma(lds_frag(Lq, koff(cr, 16 * ks + 8 * h)), kf[ks], s);
-                dp = Mfma<__bf16>::mma(lds_frag(Ld, koff(cr, 16 * ks + 8 * h)), vf[ks], dp);
+                const bf16x8 kf = lds_frag(L.k, koff(32 * wn + l32, 16 * ks + 8 * h));
+                s = Mfma<__bf16>::mma(lds_frag(L.q, koff(cr, 16 * ks + 8 * h)), kf, s);
+                const int d0 = 16 * ks + 8 * h + (i16 >> 2);
+                const bf16x8 vf = join(lds_tr(L.vt + voff(d0, vcol)), lds_tr(L.vt + voff(d0 + 4, vcol)));
+                dp = Mfma<__bf16>::mma(lds_frag(L.dout, koff(cr, 16 * ks + 8 * h)), vf, dp);
             }
-            const bool seen = key >= base && key < base + an;
+            // Scores are in log2 units (Q~ carries log2(e)): P = 2^(s - lse).
+            // Keys outside [base, base + an) get 2^-inf = 0 (no branch per element).
+            const float hide = key >= base && key < base + an ? 0.f : -__builtin_inff();
             f32x16 p, ds;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int cc = 32 * wm + acc_key(e) + 8 * h;
-                p[e] = seen ? __expf(s[e] - L.lse[buf][cc]) : 0.f;
-                ds[e] = p[e] * (dp[e] - L.delta[buf][cc]);
+                p[e] = __builtin_amdgcn_exp2f(s[e] - L.lse[cc] + hide);
+                ds[e] = p[e] * (dp[e] - L.delta[cc]);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 pa = pack8(p, kk), da = pack8(ds, kk);
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    dv[dt] = Mfma<__bf16>::mma(pa, tr_frag_k(Ld, 32 * wm + 16 * kk, 32 * dt, lane), dv[dt]);
-                    dk[dt] = Mfma<__bf16>::mma(da, tr_frag_k(Lq, 32 * wm + 16 * kk, 32 * dt, lane), dk[dt]);
+                    dv[dt] = Mfma<__bf16>::mma(pa, tr_frag_k(L.dout, 32 * wm + 16 * kk, 32 * dt, lane), dv[dt]);
+                    dk[dt] = Mfma<__bf16>::mma(da, tr_frag_k(L.q, 32 * wm + 16 * kk, 32 * dt, lane), dk[dt]);
                 }
             }
         }
@@ -925,7 +927,7 @@ __global__ __launch_bounds__(256) void bwd_ctx_kernel(MfArgs m) {
     }
     // Add the two column halves and write the tile's gradients.
     __syncthreads();
-    float* red = reinterpret_cast<float*>(L.k);     // 64 KB: the K~, V^T and Q~ tiles
+    float* red = reinterpret_cast<float*>(L.k);     // 64 KB: the K~, V^T, Q~ and dO tiles
     if (wm == 1) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -949,7 +951,7 @@ __global__ __launch_bounds__(256) void bwd_ctx_kernel(MfArgs m) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t j = t0 + 32 * wn + acc_row(e, lane);
-                if (j < T) a.dck[((int64_t)g * T + j) * D + d] = dk[dt][e];
+                if (j < T) a.dck[((int64_t)g * T + j) * D + d] = dk[dt][e] * 0.6931471805599453f;   // Q~ carries log2(e)
             }
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
