@@ -37,8 +37,15 @@ KERNEL_MATCH = {
 
 
 def source_hash() -> str:
+    """Hash of the sources the measured forward kernels are built from: the
+    translation unit that instantiates them (dflash.hip), every header, and the
+    public header. The other translation units (plan, verification, backward,
+    profiling hook) cannot change these kernels' code."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "block_draft_model_build_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "block_draft_model_build_amd", "csrc")
+    files = [os.path.join(csrc, "dflash.hip")] + glob.glob(os.path.join(csrc, "*.h")) + \
+        [os.path.join(ROOT, "include", "dflash.h")]
+    for p in sorted(files):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
