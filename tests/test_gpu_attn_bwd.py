@@ -122,6 +122,18 @@ def test_bf16_ragged(hq, hkv):
     _check_all(w, bases, anchors, valid, 2 * S + 37, seed=13)     # 37 trailing rows no block reads
 
 
+def test_bf16_anchor_at_the_end_of_the_cache():
+    # A block whose prefix ends exactly at the last cache row: its last 64-key
+    # chunk reaches past the cache (element loads with clamped keys), and the
+    # last context tile is ragged.
+    w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
+    T = 1000
+    anchors = [1000, 999, 937, 64, 63]
+    valid = np.ones((len(anchors), w.block_size), np.uint8)
+    valid[0, 5:] = 0
+    _check_all(w, [0] * len(anchors), anchors, valid, T, seed=17)
+
+
 def test_bf16_no_blocks_zeroes_context_gradients():
     w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
     ctx_total = 300
