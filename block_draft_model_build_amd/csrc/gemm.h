@@ -337,8 +337,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
-    // Tile order: consecutive tiles walk down M inside groups of 8 row tiles
-    // so the B slab they share stays hot in L2.
+    // Tile order: consecutive tiles walk down M inside groups of 4 row tiles
+    // so the B slab they share stays hot in L2 (4 measured best of 1..32 on the
+    // 5-layer body: the context projection 4-5% faster than with 8).
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;   // B loaders clamp a ragged N
     int tm, tn;
     {
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int
             const int G = tiles_m * tiles_n, G8 = G / 8 * 8;
             if (id < G8) id = (id % 8) * (G / 8) + id / 8;
         }
-        const int group = 8;
+        const int group = 4;
         const int per_group = group * tiles_n;
         const int gi = id / per_group;
         const int first_m = gi * group;
