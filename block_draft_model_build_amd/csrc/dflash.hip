@@ -14,29 +14,61 @@ namespace dflash {
 
 // ------------------------------------------------------------------ RMSNorm
 // out[row] = x / sqrt(mean(x^2) + eps) * w, x read as fp32; optionally copies
-// x into the fp32 residual stream (first layer: embeddings -> h).
+// x into the fp32 residual stream (first layer: embeddings -> h). 16-byte
+// loads; rows of up to 256 * 4 vectors stay in registers between the sum and
+// the scaling (H = 4096 in fp32), longer rows are read twice.
 template <typename TIN, typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in, float* __restrict__ hcopy,
                                                       const T* __restrict__ w, T* __restrict__ out, int H,
                                                       float eps) {
+    constexpr int VI = 16 / (int)sizeof(TIN);     // elements per 16-byte load
+    constexpr int NV = 4;                         // vectors per thread kept in registers
+    typedef TIN vin __attribute__((ext_vector_type(VI)));
+    typedef T vout __attribute__((ext_vector_type(VI)));
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const TIN* x = in + row * H;
+    const int nvec = H / VI;
+    const bool cached = nvec <= 256 * NV;
+    vin v[NV];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        float v = to_f32(x[i]);
-        ss += v * v;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int j = threadIdx.x + 256 * k;
+        if (j < nvec) {
+            v[k] = reinterpret_cast<const vin*>(x)[j];
+#pragma unroll
+            for (int q = 0; q < VI; ++q) ss += to_f32(v[k][q]) * to_f32(v[k][q]);
+        }
     }
+    if (!cached)
+        for (int j = threadIdx.x + 256 * NV; j < nvec; j += 256) {
+            const vin u = reinterpret_cast<const vin*>(x)[j];
+#pragma unroll
+            for (int q = 0; q < VI; ++q) ss += to_f32(u[q]) * to_f32(u[q]);
+        }
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float tot = red[0] + red[1] + red[2] + red[3];
     const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += 256) {
-        float v = to_f32(x[i]);
-        if (hcopy) hcopy[row * H + i] = v;
-        out[row * H + i] = from_f32<T>(v * r * to_f32(w[i]));
+    auto emit = [&](int j, const vin& u) {
+        vout o;
+#pragma unroll
+        for (int q = 0; q < VI; ++q) {
+            const float f = to_f32(u[q]);
+            o[q] = from_f32<T>(f * r * to_f32(w[j * VI + q]));
+            if (hcopy) hcopy[row * H + j * VI + q] = f;
+        }
+        reinterpret_cast<vout*>(out + row * H)[j] = o;
+    };
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int j = threadIdx.x + 256 * k;
+        if (j < nvec) emit(j, v[k]);
     }
+    if (!cached)
+        for (int j = threadIdx.x + 256 * NV; j < nvec; j += 256) emit(j, reinterpret_cast<const vin*>(x)[j]);
 }
 
 // ------------------------------------------------------------------ attention launch
