@@ -22,51 +22,77 @@ struct GradPtrs {
     const float* dv[kMaxLayers];
 };
 
-// Gk: one thread per (row, pair i); the pair's rotation is computed once and
-// applied to every layer and head. RoPE pairs i with i + D/2; its transpose is
-// the rotation by the opposite angle.
+// Gk: one thread per (row, 4 consecutive pairs); the pairs' rotations are
+// computed once and applied to every layer and head. RoPE pairs i with
+// i + D/2; its transpose is the rotation by the opposite angle.
 template <typename T>
 __global__ __launch_bounds__(256) void grad_pack_k_kernel(GradPtrs gp, const int32_t* positions, int64_t rows,
                                                           int64_t ctx_total, int64_t row_offset, int L, int hkv,
                                                           int D, RopeTurns rt, T* G, int64_t ldg) {
-    const int half = D / 2;
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const int half = D / 2, q4 = half / 4;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t r = idx / half;
-    const int i = (int)(idx - r * half);
+    const int64_t r = idx / q4;
+    const int i = (int)(idx - r * q4) * 4;
     if (r >= rows) return;
-    float cs, sn;
-    rope_cs(rt, i, positions[r], cs, sn);
+    float cs[4], sn[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rope_cs(rt, i + q, positions[r], cs[q], sn[q]);
     for (int l = 0; l < L; ++l)
         for (int g = 0; g < hkv; ++g) {
             const float* src = gp.dk[l] + ((int64_t)g * ctx_total + row_offset + r) * D;
-            const float y1 = src[i], y2 = src[i + half];
+            const f32x4 y1 = *reinterpret_cast<const f32x4*>(src + i);
+            const f32x4 y2 = *reinterpret_cast<const f32x4*>(src + i + half);
+            t4 a, b;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[q] = from_f32<T>(y1[q] * cs[q] + y2[q] * sn[q]);
+                b[q] = from_f32<T>(y2[q] * cs[q] - y1[q] * sn[q]);
+            }
             T* dst = G + r * ldg + (int64_t)(l * hkv + g) * D;
-            dst[i] = from_f32<T>(y1 * cs + y2 * sn);
-            dst[i + half] = from_f32<T>(y2 * cs - y1 * sn);
+            *reinterpret_cast<t4*>(dst + i) = a;
+            *reinterpret_cast<t4*>(dst + i + half) = b;
         }
 }
 
 // Gv: the V caches hold each head dimension by dimension ([D][ctx_total]);
-// 64 rows x 64 dimensions per workgroup are transposed through LDS.
+// 64 rows x 64 dimensions per workgroup are transposed through LDS with
+// 16-byte loads along the rows and 16-byte stores along the dimensions.
 template <typename T>
 __global__ __launch_bounds__(256) void grad_pack_v_kernel(GradPtrs gp, int64_t rows, int64_t ctx_total,
                                                           int64_t row_offset, int L, int hkv, int D, T* G,
                                                           int64_t ldg) {
+    constexpr int VO = 16 / (int)sizeof(T);
+    typedef T vout __attribute__((ext_vector_type(VO)));
     __shared__ float tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.x * 64;
     const int lg = blockIdx.y, d0 = blockIdx.z * 64;
     const int l = lg / hkv, g = lg - l * hkv;
     const float* src = gp.dv[l] + (int64_t)g * D * ctx_total + row_offset;
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-        const int dd = idx >> 6, tt = idx & 63;
-        const int64_t r = r0 + tt;
-        tile[dd][tt] = r < rows ? src[(int64_t)(d0 + dd) * ctx_total + r] : 0.f;
+    // Rows r0 .. r0 + 63 of each dimension row; 4 rows per load when the row
+    // start is 16-byte aligned and all 4 rows exist, else one by one.
+    const bool vec = ((row_offset + r0) & 3) == 0 && (ctx_total & 3) == 0;
+    for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
+        const int dd = idx >> 4, t4 = (idx & 15) * 4;
+        const float* srow = src + (int64_t)(d0 + dd) * ctx_total + r0 + t4;
+        if (vec && r0 + t4 + 4 <= rows) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(srow);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tile[dd][t4 + q] = u[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tile[dd][t4 + q] = r0 + t4 + q < rows ? srow[q] : 0.f;
+        }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-        const int tt = idx >> 6, dd = idx & 63;
+    for (int idx = threadIdx.x; idx < 64 * (64 / VO); idx += 256) {
+        const int tt = idx / (64 / VO), dv = (idx - tt * (64 / VO)) * VO;
         const int64_t r = r0 + tt;
-        if (r < rows) G[r * ldg + (int64_t)(L * hkv + lg) * D + d0 + dd] = from_f32<T>(tile[dd][tt]);
+        if (r >= rows) continue;
+        vout o;
+#pragma unroll
+        for (int q = 0; q < VO; ++q) o[q] = from_f32<T>(tile[dv + q][tt]);
+        *reinterpret_cast<vout*>(G + r * ldg + (int64_t)(L * hkv + lg) * D + d0 + dv) = o;
     }
 }
 
@@ -198,8 +224,8 @@ hipError_t ctx_bwd_t(const dflash_config& c, const T* ts, int64_t rs, int64_t ls
     T* xt = reinterpret_cast<T*>(ws + lay.xt);
     {
         ProfScope prof(DFLASH_KERNEL_CTX_BWD_PACK, st);
-        const int64_t pairs = rows * (D / 2);
-        hipLaunchKernelGGL(grad_pack_k_kernel<T>, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st, gp,
+        const int64_t quads = rows * (D / 8);
+        hipLaunchKernelGGL(grad_pack_k_kernel<T>, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, gp,
                            positions, rows, ctx_total, row_offset, L, hkv, D, make_rope_turns(c), G, kg);
         hipLaunchKernelGGL(grad_pack_v_kernel<T>, dim3((unsigned)((rows + 63) / 64), L * hkv, D / 64), dim3(256), 0,
                            st, gp, rows, ctx_total, row_offset, L, hkv, D, G, kg);
@@ -268,7 +294,7 @@ extern "C" dflash_status dflash_ctx_proj_backward(const dflash_config* cfg, cons
     GradPtrs gp{};
     for (int l = 0; l < cfg->num_layers; ++l) {
         if (layers[l].wk == nullptr || layers[l].wv == nullptr || d_ctx_k[l] == nullptr || d_ctx_v[l] == nullptr ||
-            !aligned16(layers[l].wk) || !aligned16(layers[l].wv))
+            !aligned16(layers[l].wk) || !aligned16(layers[l].wv) || !aligned16(d_ctx_k[l]) || !aligned16(d_ctx_v[l]))
             return DFLASH_ERR_INVALID_ARG;
         gp.dk[l] = d_ctx_k[l];
         gp.dv[l] = d_ctx_v[l];

@@ -439,7 +439,8 @@ size_t dflash_block_attn_backward_workspace_size(const dflash_config *cfg, int32
  *                  as dflash_ctx_proj (only wk and wv of the layers are read)
  *   d_ctx_k, d_ctx_v  host arrays [num_layers] of device f32 gradients in the
  *                  caches' layouts: K [Hkv][ctx_total][D] (rotated frame, as
- *                  dflash_block_attn_backward writes it), V [Hkv][D][ctx_total]
+ *                  dflash_block_attn_backward writes it), V [Hkv][D][ctx_total];
+ *                  16-byte aligned
  *   d_w_proj       device f32 [H, L_t*H_t], overwritten (zero when num_rows == 0)
  *   d_ctx_hidden   optional device f32 [num_rows, H]: dC (NULL: not written)
  *   workspace      dflash_ctx_proj_backward_workspace_size(cfg, num_rows) bytes,
