@@ -138,7 +138,7 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     const int H = c.hidden, K = c.num_target_layers * c.target_hidden;
     const int M = (int)rows;
     hipError_t e = gemm<T>(DFLASH_KERNEL_CTX_PROJ, M, H, K, AStacked<T>{ts, rs, ls, c.target_hidden}, BPlain<T>{w_proj, K},
-                           EpStore<T>{C, H}, st);
+                           EpStore<T>{C, H}, st, 4);
     if (e != hipSuccess) return e;
     BCtxKV<T> b{};
     EpCtxKV<T> ep{};

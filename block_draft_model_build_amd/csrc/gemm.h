@@ -319,7 +319,8 @@ template <int ROWB> __device__ __forceinline__ int swz(int r) {
 // a ring of 4 stages with 3 slabs in flight. One barrier per slab; MFMA
 // fragments of the next k-step are read while the current one multiplies.
 template <typename T, class Cfg, class AL, class BL, class EP>
-__global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int K, AL al, BL bl, EP ep) {
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int K, AL al, BL bl, EP ep,
+                                                                int group) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MI = Cfg::MI, NI = Cfg::NI;
     constexpr int EB = (int)sizeof(T);
     constexpr int ROWB = Cfg::ROWB;                // bytes per LDS row (one K slab)
@@ -337,9 +338,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
-    // Tile order: consecutive tiles walk down M inside groups of 4 row tiles
-    // so the B slab they share stays hot in L2 (4 measured best of 1..32 on the
-    // 5-layer body: the context projection 4-5% faster than with 8).
+    // Tile order: consecutive tiles walk down M inside groups of `group` row
+    // tiles so the B slab they share stays hot in L2 (chosen per call site).
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;   // B loaders clamp a ragged N
     int tm, tn;
     {
@@ -350,7 +350,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int
             const int G = tiles_m * tiles_n, G8 = G / 8 * 8;
             if (id < G8) id = (id % 8) * (G / 8) + id / 8;
         }
-        const int group = 4;
         const int per_group = group * tiles_n;
         const int gi = id / per_group;
         const int first_m = gi * group;
@@ -483,11 +482,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_nt_kernel(int M, int N, int
 
 template <typename T, class Cfg, class AL, class BL, class EP>
 hipError_t launch_gemm(int M, int N, int K, const AL& al, const BL& bl, const EP& ep,
-                       hipStream_t stream) {
+                       hipStream_t stream, int group = 8) {
     if (M <= 0) return hipSuccess;
     const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
     hipLaunchKernelGGL((gemm_nt_kernel<T, Cfg, AL, BL, EP>), dim3(tiles), dim3(Cfg::THREADS), 0, stream, M, N,
-                       K, al, bl, ep);
+                       K, al, bl, ep, group);
     return hipGetLastError();
 }
 

@@ -47,12 +47,25 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_argmax_kernel(const T* 
     constexpr int VEC = 16 / (int)sizeof(T);
     const bool vec_ok = (vocab % VEC) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
     if (vec_ok) {
+        // Batches of 8 independent 16-byte loads per thread keep enough bytes
+        // in flight to stream the row near HBM speed; the scan order (and so
+        // the tie rule) is unchanged: each thread still visits its indices in
+        // increasing order.
         typedef T TV __attribute__((ext_vector_type(VEC)));
-#pragma unroll 4
-        for (int v0 = threadIdx.x * VEC; v0 < vocab; v0 += kVerifyThreads * VEC) {
-            const TV t = *reinterpret_cast<const TV*>(x + v0);
+        constexpr int NB = 8, STRIDE = kVerifyThreads * VEC;
+        for (int base = threadIdx.x * VEC; base < vocab; base += NB * STRIDE) {
+            TV t[NB];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) better(bv, bi, to_f32(t[e]), v0 + e);
+            for (int b = 0; b < NB; ++b)
+                if (base + b * STRIDE < vocab) t[b] = *reinterpret_cast<const TV*>(x + base + b * STRIDE);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int v0 = base + b * STRIDE;
+                if (v0 < vocab) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) better(bv, bi, to_f32(t[b][e]), v0 + e);
+                }
+            }
         }
     } else {
         for (int v = threadIdx.x; v < vocab; v += kVerifyThreads) better(bv, bi, logit_f32(x, v), v);
