@@ -5,16 +5,16 @@ rocprofv3 --pmc runs of the bench command; each is scaled by the factor that
 makes the same counter read the known byte count of a plain device-to-device
 copy (1 GiB read + 1 GiB written, run with `python bench_traffic.py --copy`
 under the same counter). The result is written to profiles/traffic_<workload>.json
-together with a hash of the library sources, so bench.py reports it only while
-the kernels are unchanged.
+together with a hash of the forward kernels' sources, so bench.py reports it
+only while those kernels are unchanged.
 
-On the GPU machine (repo root):
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
-  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/copy_fetch -o c -- python bench_traffic.py --copy
-  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/copy_write -o c -- python bench_traffic.py --copy
+On a machine with the GPU, from the repo root (OUT is any output folder):
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/traffic/fetch -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/traffic/write -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/traffic/copy_fetch -o c -- python bench_traffic.py --copy
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/traffic/copy_write -o c -- python bench_traffic.py --copy
 Then, anywhere:
-  python bench_traffic.py --summarize gpurun_out/traffic --workload c3 --kernel ctx_proj
+  python bench_traffic.py --summarize OUT/traffic --workload c3 --kernel ctx_proj
 """
 from __future__ import annotations
 
