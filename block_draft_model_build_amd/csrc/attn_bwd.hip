@@ -442,6 +442,14 @@ __device__ __forceinline__ bf16x8 tr_frag_k(const char* base, int k0, int n0, in
     return join(lds_tr(base + koff(r, col)), lds_tr(base + koff(r + 4, col)));
 }
 
+// The same fragment from a plain (unswizzled) row-major tile with rows of
+// row_bytes bytes.
+__device__ __forceinline__ bf16x8 tr_frag_plain(const char* base, int row_bytes, int k0, int n0, int lane) {
+    const int i = lane & 15, G = lane >> 4;
+    const int r = k0 + 8 * (G >> 1) + (i >> 2), col = n0 + 16 * (G & 1) + 4 * (i & 3);
+    return join(lds_tr(base + r * row_bytes + col * 2), lds_tr(base + (r + 4) * row_bytes + col * 2));
+}
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int half) {
     bf16x8 f;
 #pragma unroll
@@ -474,10 +482,13 @@ __device__ __forceinline__ void dma_rows(char* tile, RowPtr rowptr, int wave, in
     }
 }
 
+constexpr int kRopeRows = 16;   // block rows whose rotations the query kernel tabulates
+
 struct QueryLds {
     char k[2][KT * 256];     // K~ chunk (swizzled rows), two stages
     char vt[2][D * 128];     // V^T chunk, two stages
     float m[2][KT], l[2][KT];
+    float rc[kRopeRows][D / 2], rs[kRopeRows][D / 2];   // cos / sin of block row k, pair i
 };
 
 struct CtxLds {
@@ -528,6 +539,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const __bf16* cvg = a.cvt + (int64_t)g * D * a.ctx_total + base;
     const int64_t lim = a.ctx_total - base;          // cache rows addressable from this base
 
+    // Rotations of the block rows (position an + k), computed once: rows below
+    // kRopeRows from the table, longer blocks' further rows directly.
+    for (int idx = tid; idx < min(bs, kRopeRows) * (D / 2); idx += 256) {
+        const int k = idx / (D / 2), i = idx - k * (D / 2);
+        rope_cs(a.rt, i, an + k, L.rc[k][i], L.rs[k][i]);
+    }
+    __syncthreads();
+    auto rot = [&](int k, int i, float& cs, float& sn) {
+        if (k < kRopeRows) {
+            cs = L.rc[k][i];
+            sn = L.rs[k][i];
+        } else {
+            rope_cs(a.rt, i, an + k, cs, sn);
+        }
+    };
+
     // This lane's column (B operand n index) and its Q~ / dO fragments.
     const int c = 32 * wm + l32;
     const bool col_ok = c < C;
@@ -558,7 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float cs, sn;
-                rope_cs(a.rt, 16 * ks + 8 * h + i, an + kq, cs, sn);
+                rot(kq, 16 * ks + 8 * h + i, cs, sn);
                 const float x1 = (float)lo[i], x2 = (float)hi[i];
                 qf[ks][i] = static_cast<__bf16>((x1 * cs - x2 * sn) * qscale);
                 qf[ks + 4][i] = static_cast<__bf16>((x2 * cs + x1 * sn) * qscale);
@@ -616,7 +643,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const __bf16* kr = a.kb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
                 const float x1 = (float)kr[i], x2 = (float)kr[i + D / 2];
                 float cs, sn;
-                rope_cs(a.rt, i, an + r, cs, sn);
+                rot(r, i, cs, sn);
                 y1 = x1 * cs - x2 * sn;
                 y2 = x2 * cs + x1 * sn;
             }
@@ -763,29 +790,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    // Own keys: dK~ = dS^T Q~, dV = P^T dO over the block's columns; dK~ rotated
-    // back (and out of log2 units: Q~ carries log2(e)).
+    // Own keys: dK~ = dS^T Q~ and dV = P^T dO on the matrix cores (keys x d,
+    // contracting over the block's columns); wave w takes d tile w. dK~ goes
+    // through LDS to be rotated back pairwise (and out of log2 units: Q~
+    // carries log2(e)).
     constexpr float kLn2 = 0.6931471805599453f;
-    for (int idx = tid; idx < bs * (D / 2); idx += 256) {
-        const int r = idx / (D / 2), i = idx - r * (D / 2);
-        float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
-        for (int cc = 0; cc < C; ++cc) {
-            const float dsv = Down[r * KT + cc], pv = Pown[r * KT + cc];
-            k1 += dsv * (float)Qs[cc * D + i];
-            k2 += dsv * (float)Qs[cc * D + i + D / 2];
-            v1 += pv * (float)Ds[cc * D + i];
-            v2 += pv * (float)Ds[cc * D + i + D / 2];
+    {
+        const int ntk = bs > 32 ? 2 : 1;
+        f32x16 ak[2] = {}, av[2] = {};
+        for (int mt = 0; mt < ntk; ++mt) {
+            const int key = 32 * mt + l32;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float* dsr = Down + key * KT + 16 * ks + 8 * h;
+                const float* pr = Pown + key * KT + 16 * ks + 8 * h;
+                bf16x8 a_ds, a_p;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    a_ds[i] = static_cast<__bf16>(dsr[i]);
+                    a_p[i] = static_cast<__bf16>(pr[i]);
+                }
+                const bf16x8 bq = tr_frag_plain(reinterpret_cast<const char*>(Qs), D * 2, 16 * ks, 32 * w, lane);
+                const bf16x8 bd = tr_frag_plain(reinterpret_cast<const char*>(Ds), D * 2, 16 * ks, 32 * w, lane);
+                ak[mt] = Mfma<__bf16>::mma(a_ds, bq, ak[mt]);
+                av[mt] = Mfma<__bf16>::mma(a_p, bd, av[mt]);
+            }
         }
-        k1 *= kLn2;
-        k2 *= kLn2;
-        float cs, sn;
-        rope_cs(a.rt, i, an + r, cs, sn);
-        float* dk = a.dkb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
-        float* dv = a.dvb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
-        dk[i] = k1 * cs + k2 * sn;
-        dk[i + D / 2] = k2 * cs - k1 * sn;
-        dv[i] = v1;
-        dv[i + D / 2] = v2;
+        __syncthreads();                               // P and dS are read: their space takes dK~
+        float* dkst = Pown;   // [key][D] fp32: bs x 512 bytes, past 16 KB over the dead Q~ / dO tiles
+        const int d = 32 * w + l32;
+        for (int mt = 0; mt < ntk; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = 32 * mt + acc_row(e, lane);
+                if (key < bs) {
+                    dkst[key * D + d] = ak[mt][e] * kLn2;
+                    a.dvb[(int64_t)(n * bs + key) * a.kv_ld + (int64_t)g * D + d] = av[mt][e];
+                }
+            }
+    }
+    __syncthreads();
+    {
+        const float* dkst = Pown;
+        for (int idx = tid; idx < bs * (D / 2); idx += 256) {
+            const int r = idx / (D / 2), i = idx - r * (D / 2);
+            const float k1 = dkst[r * D + i], k2 = dkst[r * D + i + D / 2];
+            float cs, sn;
+            rot(r, i, cs, sn);
+            float* dk = a.dkb + (int64_t)(n * bs + r) * a.kv_ld + (int64_t)g * D;
+            dk[i] = k1 * cs + k2 * sn;
+            dk[i + D / 2] = k2 * cs - k1 * sn;
+        }
     }
     __syncthreads();
 
@@ -813,7 +868,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int dt = 0; dt < 2; ++dt) {
                 const int i = 32 * dt + l32;
                 float cs, sn;
-                rope_cs(a.rt, i, an + k, cs, sn);
+                rot(k, i, cs, sn);
                 const float y1 = dq[dt][e], y2 = dq[dt + 2][e];
                 o[i] = (y1 * cs + y2 * sn) * scale;
                 o[i + D / 2] = (y2 * cs - y1 * sn) * scale;
@@ -837,21 +892,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t T = a.ctx_total;
     const __bf16* ckg = a.ck + (int64_t)g * T * D;
     const __bf16* cvg = a.cvt + (int64_t)g * D * T;
-    // The tile's K~ and V^T (rows past the cache clamped to its last row).
-    dma_rows(L.k, [&](int r) { return ckg + min(t0 + r, T - 1) * D; }, w, lane);
-    if (t0 + KT <= T) {
+    // The tile's K~ and V^T (rows past the cache clamped to its last row),
+    // staged once the first block that reads the tile is found.
+    bool staged = false;
+    auto stage_tile = [&]() {
+        dma_rows(L.k, [&](int r) { return ckg + min(t0 + r, T - 1) * D; }, w, lane);
+        if (t0 + KT <= T) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int u0 = (it * 4 + w) * 64, u = u0 + lane;
-            const int d = u >> 3, cc = u & 7;
-            dma16(cvg + (int64_t)d * T + t0 + ((cc ^ (d & 7)) << 3), L.vt + u0 * 16);
+            for (int it = 0; it < 4; ++it) {
+                const int u0 = (it * 4 + w) * 64, u = u0 + lane;
+                const int d = u >> 3, cc = u & 7;
+                dma16(cvg + (int64_t)d * T + t0 + ((cc ^ (d & 7)) << 3), L.vt + u0 * 16);
+            }
+        } else {
+            for (int idx = tid; idx < D * KT; idx += 256) {
+                const int d = idx / KT, j = idx - d * KT;
+                *(__bf16*)(L.vt + voff(d, j)) = cvg[(int64_t)d * T + min(t0 + j, T - 1)];
+            }
         }
-    } else {
-        for (int idx = tid; idx < D * KT; idx += 256) {
-            const int d = idx / KT, j = idx - d * KT;
-            *(__bf16*)(L.vt + voff(d, j)) = cvg[(int64_t)d * T + min(t0 + j, T - 1)];
-        }
-    }
+    };
     const int64_t key = t0 + 32 * wn + l32;            // key column of this lane in S and dP
     const int i16 = lane & 15, G16 = lane >> 4;
     const int vcol = 32 * wn + 16 * (G16 & 1) + 4 * (i16 & 3);
@@ -882,6 +941,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             L.list[at] = nn;
             L.list_base[at] = bb;
             L.list_an[at] = ba;
+        }
+        if (total > 0 && !staged) {
+            stage_tile();                             // completes with the first block's loads below
+            staged = true;
         }
         for (int it = 0; it < total; ++it) {
             __syncthreads();                           // the list, and the previous block's reads
@@ -939,32 +1002,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
     if (wm == 0) {
-        const bool vec = (T & 3) == 0;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 dk[dt][e] += red[((wn * 8 + dt) * 16 + e) * 64 + lane];
                 dv[dt][e] += red[((wn * 8 + 4 + dt) * 16 + e) * 64 + lane];
             }
+    }
+    __syncthreads();
+    // dK rows go out directly (lanes cover consecutive dimensions); dV goes
+    // through LDS as [d][key] so that each dimension's 64 keys leave as one
+    // contiguous 256-byte run of the transposed gradient.
+    constexpr int VP = KT + 4;                        // padded row (floats), 16-byte aligned
+    float* dvt = red;                                 // [D][VP] fp32 = 34 KB of the 64 KB
+    if (wm == 0) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
             const int d = 32 * dt + l32;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t j = t0 + 32 * wn + acc_row(e, lane);
+                const int jj = 32 * wn + acc_row(e, lane);
+                const int64_t j = t0 + jj;
                 if (j < T) a.dck[((int64_t)g * T + j) * D + d] = dk[dt][e] * 0.6931471805599453f;   // Q~ carries log2(e)
+                dvt[d * VP + jj] = dv[dt][e];
             }
+        }
+    }
+    __syncthreads();
+    const bool vec = (T & 3) == 0 && t0 + KT <= T;
+    for (int idx = tid; idx < D * (KT / 4); idx += 256) {
+        const int d = idx / (KT / 4), j4 = (idx - d * (KT / 4)) * 4;
+        float* o = a.dcv + ((int64_t)g * D + d) * T + t0 + j4;
+        const float* src = dvt + d * VP + j4;
+        if (vec) {
+            *(f32x4*)o = *(const f32x4*)src;
+        } else {
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int64_t j = t0 + 32 * wn + acc_row(4 * e4, lane);     // 4 consecutive rows
-                float* o = a.dcv + ((int64_t)g * D + d) * T + j;
-                if (vec && j + 3 < T) {
-                    *(f32x4*)o = f32x4{dv[dt][4 * e4], dv[dt][4 * e4 + 1], dv[dt][4 * e4 + 2], dv[dt][4 * e4 + 3]};
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (j + q < T) o[q] = dv[dt][4 * e4 + q];
-                }
-            }
+            for (int q = 0; q < 4; ++q)
+                if (t0 + j4 + q < T) o[q] = src[q];
         }
     }
 }
