@@ -1130,6 +1130,10 @@ extern "C" dflash_status dflash_block_attn_backward(
                             d_q == nullptr || d_k_blk == nullptr || d_v_blk == nullptr)) ||
         (ctx_total > 0 && (ctx_k == nullptr || ctx_v == nullptr || d_ctx_k == nullptr || d_ctx_v == nullptr)))
         return DFLASH_ERR_INVALID_ARG;
+    // 16-byte vector loads of the inputs and stores of the gradients.
+    for (const void* p : {q, k_blk, v_blk, ctx_k, ctx_v, out, d_out, (const void*)d_q, (const void*)d_k_blk,
+                          (const void*)d_v_blk, (const void*)d_ctx_k, (const void*)d_ctx_v})
+        if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return DFLASH_ERR_INVALID_ARG;
     const size_t need = bw_workspace(*cfg, num_blocks);
     if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return DFLASH_ERR_WORKSPACE;

@@ -408,7 +408,8 @@ size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab);
  *   d_ctx_k         device f32 [Hkv][ctx_total][D]; d_ctx_v: device f32 [Hkv][D][ctx_total]
  *   workspace       dflash_block_attn_backward_workspace_size(cfg, nb) bytes, 256-byte aligned
  * Every output element is written (no accumulation into the caller's buffers);
- * results are deterministic. Errors: as dflash_block_attn.
+ * results are deterministic. All arrays are 16-byte aligned. Errors: as
+ * dflash_block_attn; INVALID_ARG also for a misaligned array.
  */
 dflash_status dflash_block_attn_backward(const dflash_config *cfg, int32_t num_blocks, const void *q,
                                          const void *k_blk, const void *v_blk, const void *ctx_k,
