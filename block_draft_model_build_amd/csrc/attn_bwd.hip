@@ -10,15 +10,19 @@
 // rotation by the opposite angle); context dK stays in the rotated frame the
 // cache holds.
 //
-// First version, fp32 arithmetic on the vector units (no MFMA), deterministic:
-//  * attn_bwd_query_kernel, one workgroup per (block, KV head): softmax
-//    statistics (pass 1), then per 64-key chunk ds and p into LDS and the dq
-//    sums over the chunk (pass 2); the block's own keys get their dk and dv
-//    there (only their own queries read them). Writes q~, lse and
-//    rowsum(dO o) for the second kernel.
-//  * attn_bwd_ctx_kernel, one workgroup per (64-row context tile, KV head):
-//    walks every block that reads the tile, in block order, and accumulates
-//    the tile's dK and dV in registers: no atomics, fixed summation order.
+// Two kernels, deterministic (no atomics, fixed summation orders), in two
+// implementations:
+//  * a query-major kernel, one workgroup per (block, KV head): the softmax
+//    statistics of the block's query columns, dq over all the keys the block
+//    reads, and the block's own keys' dk and dv (only its own queries read
+//    them); it leaves q~, masked dO, the logsumexp and rowsum(dO o) per
+//    column in the workspace for the second kernel;
+//  * a key-major kernel, one workgroup per (64-row context tile, KV head):
+//    visits every block that reads the tile, in block order, and accumulates
+//    the tile's dK and dV.
+// fp32 configs (D = 64) run both on the vector units (attn_bwd_*_kernel, two
+// passes over the keys); bf16 configs (D = 128) on the matrix cores (namespace
+// mfb below: one pass with an online softmax, transposed LDS reads).
 #include "internal.h"
 #include "attention.h"
 
@@ -27,11 +31,11 @@ namespace dflash {
 namespace {
 
 constexpr int kBwKeys = 64;     // keys per chunk (query kernel) and rows per tile (context kernel)
+constexpr int kBwThreads = 256;
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(float* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
-constexpr int kBwThreads = 256;
 
 template <typename T> struct BwArgs {
     const T *q, *kb, *vb;        // [nb*bs, Hq*D], [nb*bs, Hkv*D] x2 (un-rotated q, kb)
