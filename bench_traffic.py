@@ -24,6 +24,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -36,19 +37,24 @@ KERNEL_MATCH = {
 }
 
 
+def _strip_comments(text: str) -> str:
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.sub(r"//[^\n]*", "", text)
+
+
 def source_hash() -> str:
-    """Hash of the sources the measured forward kernels are built from: the
-    translation unit that instantiates them (dflash.hip), every header, and the
-    public header. The other translation units (plan, verification, backward,
-    profiling hook) cannot change these kernels' code."""
+    """Hash of the sources the measured forward kernels are built from, with
+    comments removed: the translation unit that instantiates them (dflash.hip),
+    every header, and the public header. The other translation units (plan,
+    verification, backward, profiling hook) cannot change these kernels' code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_draft_model_build_amd", "csrc")
     files = [os.path.join(csrc, "dflash.hip")] + glob.glob(os.path.join(csrc, "*.h")) + \
         [os.path.join(ROOT, "include", "dflash.h")]
     for p in sorted(files):
-        with open(p, "rb") as f:
+        with open(p) as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
