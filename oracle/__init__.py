@@ -9,7 +9,8 @@ Contents:
               and a brute-force dense-mask attention used to pin the gathered form.
   verify.py -- greedy and speculative-sampling verification of a drafted block.
   loss.py  -- block LM head and positionally decayed cross-entropy.
-  backward.py -- gradients of the dual-source block attention.
+  backward.py -- gradients of the dual-source block attention and of the
+              context path (dW_proj).
 
 Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
   build_plan             pinned by invariants the pages fix (determinism, equal
