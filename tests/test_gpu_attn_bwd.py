@@ -122,6 +122,18 @@ def test_bf16_ragged(hq, hkv):
     _check_all(w, bases, anchors, valid, 2 * S + 37, seed=13)     # 37 trailing rows no block reads
 
 
+@pytest.mark.parametrize("bs,hq,hkv", [(32, 4, 2), (64, 2, 2)])
+def test_bf16_long_blocks(bs, hq, hkv):
+    # Blocks longer than 16 rows (rotations past the tabulated rows) and than
+    # 32 rows (the own keys span two key tiles).
+    w = scaled(WORKLOADS["c2"], num_q_heads=hq, num_kv_heads=hkv, hidden=512, block_size=bs)
+    T = 900
+    anchors = [0, 5, 130, 700, -1, 836]
+    valid = np.ones((len(anchors), bs), np.uint8)
+    valid[2, bs // 2:] = 0
+    _check_all(w, [0] * len(anchors), anchors, valid, T, seed=18 + bs)
+
+
 def test_bf16_anchor_at_the_end_of_the_cache():
     # A block whose prefix ends exactly at the last cache row: its last 64-key
     # chunk reaches past the cache (element loads with clamped keys), and the
