@@ -53,6 +53,7 @@ template <typename T> struct AttnArgs {
                                        // [1] number of groups, [2] of single-block groups
     float* part_o;                     // [items][kMaxGroup][QC][D]
     float* part_ml;                    // [items][kMaxGroup][QC][2]
+    int* redo;                         // [items][4]: a wave's scores outran its reference
     RopeTurns rt;
 };
 
@@ -132,19 +133,25 @@ __device__ __forceinline__ void attn_scores(const GetK& getk,
 }
 
 // getv(st, ds) returns the V^T fragment of MFMA step st, d-tile ds.
-template <typename T, int D, int QC, class GetV>
+//
+// Two ways to keep P = 2^(s - m) in range (O and l always share the reference m,
+// so both give the same softmax):
+// - fixed (LAZY false): m is the maximum of the first visible keys of each query
+//   column and never moves, so O is never rescaled inside the key loop; mt
+//   tracks the true maximum, and the kernel flags its item for a second,
+//   LAZY run when some column's scores rose more than kFixedRange above m;
+// - lazy (LAZY true): m moves when some column's scores pass it by more than
+//   kLazy, and O and l are rescaled then.
+constexpr float kFixedRange = 32.f;
+
+template <typename T, int D, int QC, bool LAZY, class GetV>
 __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& getv, int nvalid,
                                             f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
-                                            float (&l)[QC / 32], int lane) {
+                                            float (&l)[QC / 32], float (&mt)[QC / 32], int lane) {
     using TT = AttnTile<T, D, QC>;
     typedef typename Mfma<T>::frag frag;
     constexpr int QS = TT::QS, DS = TT::DS, PK = TT::PK, E = TT::E;
     const int h = lane >> 5;
-    // Online softmax with a lazily moved reference max m: P = 2^(s - m) is
-    // allowed to grow up to 2^kLazy, and O and l are rescaled only when some
-    // column's scores exceed its reference by more than that (rare after the
-    // first keys), which keeps the DS*16 rescaling multiplies per column off the
-    // common path. The result is the same softmax: O and l share the reference.
     constexpr float kLazy = 8.f;
     const float NEG_INF = -__builtin_inff();
 #pragma unroll
@@ -159,16 +166,21 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qs][e]);
         mx = fmaxf(mx, xor32(mx));
-        const bool grow = mx > m[qs] + kLazy;        // also true on the first visible keys
-        if (__any(grow)) {
-            const float mnew = grow ? mx : m[qs];
-            const float alpha = (m[qs] == NEG_INF) ? 0.f : fast_exp2(m[qs] - mnew);
-            m[qs] = mnew;
-            l[qs] *= alpha;
+        if constexpr (LAZY) {
+            const bool grow = mx > m[qs] + kLazy;    // also true on the first visible keys
+            if (__any(grow)) {
+                const float mnew = grow ? mx : m[qs];
+                const float alpha = (m[qs] == NEG_INF) ? 0.f : fast_exp2(m[qs] - mnew);
+                m[qs] = mnew;
+                l[qs] *= alpha;
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds)
+                for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) o[ds][qs][e] *= alpha;
+                    for (int e = 0; e < 16; ++e) o[ds][qs][e] *= alpha;
+            }
+        } else {
+            if (m[qs] == NEG_INF) m[qs] = mx;
+            mt[qs] = fmaxf(mt[qs], mx);
         }
         const float muse = (m[qs] == NEG_INF) ? 0.f : m[qs];
         float ps = 0.f;
@@ -213,11 +225,11 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
 // One wave folds the 32-key slice starting at key0 of a tile staged in LDS
 // (K rows at ks, V^T rows at vt; `nvalid` visible keys) into its running
 // softmax state.
-template <typename T, int D, int QC>
+template <typename T, int D, int QC, bool LAZY>
 __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int key0, int nvalid,
                                            const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
                                            f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
-                                           float (&l)[QC / 32], int lane) {
+                                           float (&l)[QC / 32], float (&mt)[QC / 32], int lane) {
     using TT = AttnTile<T, D, QC>;
     typedef typename Mfma<T>::frag frag;
     constexpr int E = TT::E, EB = TT::EB;
@@ -234,7 +246,7 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int k
         else
             return *reinterpret_cast<const T*>(vt + TT::voff(d, key0 + acc_key(st) + 8 * h));
     };
-    attn_update<T, D, QC>(sc, getv, nvalid, o, m, l, lane);
+    attn_update<T, D, QC, LAZY>(sc, getv, nvalid, o, m, l, mt, lane);
 }
 
 // Fragments of one 32-key slice straight from the context caches (no LDS):
@@ -282,9 +294,14 @@ __device__ __forceinline__ void attn_load_v(const T* cvg, int64_t ctx_total, int
 
 // STREAM selects the items this instantiation serves: single-block groups
 // (streamed from the caches into registers) or multi-block groups (shared
-// LDS tiles). Both are launched over the same item list.
-template <typename T, int D, int QC, bool STREAM>
+// LDS tiles). Both are launched over the same item list, with the fixed
+// softmax reference, and record per wave whether its scores outran it. The
+// REDO instantiation, launched after them, runs only the items so recorded,
+// through the shared tiles with the lazily moved reference, and overwrites
+// their results.
+template <typename T, int D, int QC, bool STREAM, bool REDO = false>
 __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
+    static_assert(!(STREAM && REDO), "the redo runs through the shared tiles");
     using TT = AttnTile<T, D, QC>;
     typedef typename Mfma<T>::frag frag;
     constexpr int QS = TT::QS, DS = TT::DS, DK = TT::DK, E = TT::E, EB = TT::EB, EC = TT::EC;
@@ -299,6 +316,10 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // Items are dispatched last-first: groups come in ascending anchor order,
     // so the longest prefixes start first and the short ones fill the tail.
     const int item = total - 1 - (int)blockIdx.x;
+    if constexpr (REDO) {
+        const int4 f = *reinterpret_cast<const int4*>(p.redo + 4 * (int64_t)item);
+        if ((f.x | f.y | f.z | f.w) == 0) return;
+    }
     const int sg = item / hkv, g = item - sg * hkv;
     int lo = 0, hi = ngroups;
     while (hi - lo > 1) {
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
     const int n0 = p.group_start[gi];
     const int ng = p.group_start[gi + 1] - n0;
-    if ((ng == 1) != STREAM) return;
+    if (!REDO && (ng == 1) != STREAM) return;
     const int wpb = ng == 1 ? 4 : (ng == 2 ? 2 : 1);   // waves per block
     const int j = wave / wpb;                          // this wave's block in the group
     const int phase = wave - j * wpb;                  // this wave's share of the block's keys
@@ -371,10 +392,10 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     }
 
     f32x16 o[DS][QS];
-    float m[QS], l[QS];
+    float m[QS], l[QS], mt[QS];          // reference, sum, true maximum (attn_update)
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
-        m[qs] = -__builtin_inff();
+        m[qs] = mt[qs] = -__builtin_inff();
         l[qs] = 0.f;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
@@ -494,7 +515,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             *reinterpret_cast<T*>(Vt + TT::voff(d, jj * 32 + k)) = v;
         }
         __syncthreads();
-        if (active && phase == 0 && a >= 0) attn_slice<T, D, QC>(Ks, Vt, j * 32, bs, qf, o, m, l, lane);
+        if (active && phase == 0 && a >= 0) attn_slice<T, D, QC, REDO>(Ks, Vt, j * 32, bs, qf, o, m, l, mt, lane);
         __syncthreads();
     }
 
@@ -513,8 +534,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
                 f32x16 sc[QS];
                 attn_scores<T, D, QC>([&](int kk) { return kf[kk]; }, qf, sc);
                 if (more) attn_load_k<T, D, QC>(ckg, kbeg + 32 * (i + 4), kend, kf, lane);
-                attn_update<T, D, QC>(sc, [&](int st, int ds) { return vf[st][ds]; },
-                                      min(32, kend - (kbeg + 32 * i)), o, m, l, lane);
+                attn_update<T, D, QC, false>(sc, [&](int st, int ds) { return vf[st][ds]; },
+                                             min(32, kend - (kbeg + 32 * i)), o, m, l, mt, lane);
                 if (more) attn_load_v<T, D, QC>(cvg, p.ctx_total, kbeg + 32 * (i + 4), kend, vf, lane);
             }
         }
@@ -527,7 +548,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             for (int sl = phase; sl < SUPER / 32; sl += wpb) {
                 const int nvalid = kend - (kbeg + t * SUPER + sl * 32);
                 if (nvalid > 0)
-                    attn_slice<T, D, QC>(Ks, Vt, sl * 32, nvalid < 32 ? nvalid : 32, qf, o, m, l, lane);
+                    attn_slice<T, D, QC, REDO>(Ks, Vt, sl * 32, nvalid < 32 ? nvalid : 32, qf, o, m, l, mt, lane);
             }
         }
     };
@@ -567,6 +588,14 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             if (t + 2 < ntile) gload(kbeg + (t + 2) * SUPER);
             tile_compute(t);
         }
+    }
+
+    if constexpr (!REDO) {
+        bool over = false;
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) over |= mt[qs] > m[qs] + kFixedRange;
+        over = __any(over);
+        if (lane == 0) p.redo[4 * (int64_t)item + wave] = over ? 1 : 0;
     }
 
     // ---- merge the waves serving one block (tree over phases), via LDS

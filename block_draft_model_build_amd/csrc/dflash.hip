@@ -79,6 +79,7 @@ static hipError_t attn_launch_t(const dflash_config& c, const AttnArgs<T>& a, in
         ProfScope prof(DFLASH_KERNEL_ATTENTION, st);
         hipLaunchKernelGGL((block_attn_kernel<T, D, QC, false>), dim3(items_max), dim3(256), 0, st, a);
         hipLaunchKernelGGL((block_attn_kernel<T, D, QC, true>), dim3(items_max), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((block_attn_kernel<T, D, QC, false, true>), dim3(items_max), dim3(256), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -113,6 +114,7 @@ static AttnArgs<T> attn_args(const dflash_config& c, int nb, const T* q, int64_t
     a.sched = reinterpret_cast<const int*>(ws + w.sched);
     a.part_o = reinterpret_cast<float*>(ws + w.part_o);
     a.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+    a.redo = reinterpret_cast<int*>(ws + w.redo);
     a.rt = make_rope_turns(c);
     return a;
 }

@@ -33,11 +33,12 @@ inline int attn_qcols(const dflash_config& c) {
 
 // Workspace layout (every region 256-byte aligned):
 //   attention scheduler: group_start [nb+1], item_start [nb+1], sched [4] (i32)
-//   attention partials:  part_o [items_max][4][QC][D] f32, part_ml [items_max][4][QC][2] f32
+//   attention partials:  part_o [items_max][4][QC][D] f32, part_ml [items_max][4][QC][2] f32,
+//                        redo [items_max][4] i32
 //   body: h [R][H] f32, x [R][H], qkv [R][(Hq+2Hkv)D], att [R][Hq D], u [R][I]   (dtype)
 //   ctx_proj: C [ctx_rows][H] (dtype); shares the body's space (calls are stream-ordered).
 struct Workspace {
-    size_t group_start, item_start, sched, part_o, part_ml, h, x, qkv, att, u, c, total;
+    size_t group_start, item_start, sched, part_o, part_ml, redo, h, x, qkv, att, u, c, total;
 };
 
 inline int attn_items_max(const dflash_config& c, int nb) {
@@ -57,6 +58,7 @@ inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_ro
     w.sched = off;       off = align_up(off + sizeof(int) * 4, A);
     w.part_o = off;      off = align_up(off + sizeof(float) * parts * qc * D, A);
     w.part_ml = off;     off = align_up(off + sizeof(float) * parts * qc * 2, A);
+    w.redo = off;        off = align_up(off + sizeof(int) * parts, A);
     const size_t shared0 = off;
     w.h = off;          off = align_up(off + sizeof(float) * R * H, A);
     w.x = off;          off = align_up(off + eb * R * H, A);

@@ -13,13 +13,15 @@ from tests.helpers import BF16_TOL, F32_TOL, compare, np64, workspace
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, bases, anchors, valid, ctx_total, seed, check_blocks=None):
+def _run(w, bases, anchors, valid, ctx_total, seed, check_blocks=None, tweak=None):
     dev = "cuda"
     nb, bs = len(anchors), w.block_size
     cfg = d.config_from_workload(w)
     rng = Rng(seed, dev)
     q, k, v, ck, cv = random_attention_inputs(rng, nb, bs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                               ctx_total, w.torch_dtype)
+    if tweak is not None:
+        tweak(q, k, v, ck, cv)
     base_t = torch.tensor(bases, dtype=torch.int64, device=dev)
     anc_t = torch.tensor(anchors, dtype=torch.int32, device=dev)
     val_t = torch.tensor(np.asarray(valid, np.uint8).reshape(-1), dtype=torch.uint8, device=dev)
@@ -101,6 +103,53 @@ def test_long_context_blocks():
     a = anchors[0].tolist()
     check = [0, 1, 255, 510, 511]
     _run(w, [0] * N, a, valid[0], S, seed=6, check_blocks=check)
+
+
+def _spikes(w, ctx_rows, own_rows, scale):
+    """Every query gets +6 on the last rotary pair's first component (rotated by
+    at most 0.02 rad at these positions), and the listed context keys / own keys
+    become scale * e_i on that component: their scores, about
+    6 * scale * log2(e) / sqrt(D) in log2 units, stand far above all others for
+    every query column that can see them."""
+    i = w.head_dim // 2 - 1
+    D = w.head_dim
+
+    def tweak(q, k, v, ck, cv):
+        q.view(q.shape[0], -1, D)[:, :, i] += 6.0
+        for t in ctx_rows:
+            ck[:, t] = 0
+            ck[:, t, i] = scale
+        kk = k.view(k.shape[0], -1, D)
+        for r in own_rows:
+            kk[r] = 0
+            kk[r, :, i] = scale
+    return tweak
+
+
+@pytest.mark.parametrize("scale", [100.0, 300.0])
+def test_bf16_scores_far_above_first_keys(scale):
+    # A few keys score 75 (scale 100) or 230 (scale 300) log2 units above the
+    # rest, far past the first visible keys' maximum that the softmax keeps as
+    # its reference; at 300, 2^(s - reference) is beyond fp32. Covers multi-block
+    # groups (4 and 2 blocks), single-block groups, split prefixes, a spike
+    # among a block's own keys, and blocks that never see a spike.
+    w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
+    S, bs = 6000, w.block_size
+    bases = [0, 0, 0, 0, S, S, 0, S, S, S]
+    anchors = [5999, 3001, 700, 130, 2999, 1000, 4000, 50, 2600, 1200]
+    valid = np.ones((len(anchors), bs), np.uint8)
+    valid[1, 9:] = 0
+    tweak = _spikes(w, ctx_rows=[300, 2900, 5000, S + 1234, S + 2500],
+                    own_rows=[3 * bs + 5, 7 * bs + 2], scale=scale)
+    _run(w, bases, anchors, valid, 2 * S, seed=8, tweak=tweak)
+
+
+def test_fp32_scores_far_above_first_keys():
+    w = WORKLOADS["c1"]
+    anchors = [100, 127, 20, 64]
+    valid = np.ones((4, w.block_size), np.uint8)
+    _run(w, [0] * 4, anchors, valid, 128, seed=9,
+         tweak=_spikes(w, ctx_rows=[40, 90], own_rows=[2 * w.block_size + 1], scale=300.0))
 
 
 def test_deterministic_and_information_boundary():
