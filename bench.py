@@ -96,14 +96,19 @@ class Runner:
     def anchors_np(self):
         return self.anchor.cpu().numpy().astype("int64")
 
+    def bases_np(self):
+        return self.base.cpu().numpy().astype("int64")
+
 
 # ----------------------------------------------------------------------------- algorithmic counts
-def kernel_counts(w, anchors):
+def kernel_counts(w, anchors, bases):
     """Algorithmic flops and HBM bytes per launch, and launches per step, for each
     kernel. GEMMs: 2*M*N*K flops, each operand read once and the output written
-    once. Attention: 4*D flops per (query head, block row, visible key); bytes
-    under the per-block stream model: every (block, KV head) reads the K and V
-    rows of its visible keys (prefix + block) once, plus q in and out."""
+    once. Attention: 4*D flops per (query head, block row, visible key); bytes:
+    every context K and V row that some block can see, once per KV head (blocks
+    of one sequence share their prefix), each block's own K and V, plus q in and
+    out. Its bound is whichever of the two takes longer at peak: the MFMA where
+    many blocks share a sequence's prefix, HBM where each request has its own."""
     import numpy as np
     eb = 4 if w.dtype == "f32" else 2
     bs, H, D, I = w.block_size, w.hidden, w.head_dim, w.intermediate
@@ -128,9 +133,13 @@ def kernel_counts(w, anchors):
     gemm("o_proj", R, H, Hq * D, extra_bytes=R * H * (8 - eb), launches=L)
     gemm("gate_up", R, 2 * I, H, extra_bytes=-R * I * eb, launches=L)
     gemm("down", R, H, I, extra_bytes=R * H * (8 - eb), launches=L)
-    c["attention"] = dict(flops=float(4.0 * D * Hq * bs * keys.sum()),
-                          bytes=float(Hkv * keys.sum() * 2 * D * eb + 2 * R * Hq * D * eb),
-                          launches=L, bound="hbm")
+    b = np.asarray(bases, np.int64)[live]
+    ctx_rows = sum(int(a[live][b == u].max()) for u in np.unique(b))
+    att_flops = float(4.0 * D * Hq * bs * keys.sum())
+    att_bytes = float(Hkv * (ctx_rows + bs * int(live.sum())) * 2 * D * eb + 2 * R * Hq * D * eb)
+    c["attention"] = dict(flops=att_flops, bytes=att_bytes, launches=L,
+                          bound="mfma" if att_flops / (PEAK_MFMA_TFLOPS[w.dtype] * 1e12)
+                          >= att_bytes / (PEAK_HBM_GBS * 1e9) else "hbm")
     c["rmsnorm"] = dict(flops=float(3.0 * R * H), bytes=float(R * H * (4 + eb)), launches=2 * L, bound="hbm")
     # Merge of split prefixes: at most every query row of every head in and out
     # once in fp32 (an upper bound; no splits -> no work).
@@ -427,7 +436,7 @@ def main():
         runner.step()
     torch.cuda.synchronize()
     anchors = runner.anchors_np()
-    counts = kernel_counts(w, anchors)
+    counts = kernel_counts(w, anchors, runner.bases_np())
     log(f"warmup done ({args.warmup} steps)")
 
     # Per-kernel time shares: each kernel in turn, over a couple of steps.

@@ -4,9 +4,12 @@ FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are collected in two separate
 rocprofv3 --pmc runs of the bench command; each is scaled by the factor that
 makes the same counter read the known byte count of a plain device-to-device
 copy (1 GiB read + 1 GiB written, run with `python bench_traffic.py --copy`
-under the same counter). The result is written to profiles/traffic_<workload>.json
-together with a hash of the forward kernels' sources, so bench.py reports it
-only while those kernels are unchanged.
+under the same counter). The result is written to
+profiles/traffic_<workload>_<kernel>.json together with a hash of the forward
+kernels' sources, so bench.py reports it only while those kernels are
+unchanged. A kernel made of several launches per call (attention: the shared
+and streaming instantiations and the redo pass) is counted per call: the bytes
+of all its dispatches divided by the number of calls.
 
 On a machine with the GPU, from the repo root (OUT is any output folder):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/traffic/fetch -o b -- python bench.py --workload c3 --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next
@@ -15,6 +18,7 @@ On a machine with the GPU, from the repo root (OUT is any output folder):
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/traffic/copy_write -o c -- python bench_traffic.py --copy
 Then, anywhere:
   python bench_traffic.py --summarize OUT/traffic --workload c3 --kernel ctx_proj
+  python bench_traffic.py --summarize OUT/traffic --workload c4 --kernel attention
 """
 from __future__ import annotations
 
@@ -35,6 +39,8 @@ KERNEL_MATCH = {
     "ctx_proj": "AStacked", "ctx_kv": "EpCtxKV", "qkv": "BQKV", "gate_up": "EpSwiGLU",
     "attention": "block_attn_kernel", "attn_combine": "attn_combine_kernel", "rmsnorm": "rmsnorm_kernel",
 }
+# Launches per call of the library's kernel (every call makes all of them).
+DISPATCHES_PER_CALL = {"attention": 3}
 
 
 def _strip_comments(text: str) -> str:
@@ -92,16 +98,18 @@ def summarize(root, workload, kernel):
     cw, _ = _per_dispatch(os.path.join(root, "copy_write"), "WRITE_SIZE", is_copy)
     f_fetch = COPY_BYTES / (cf * 1024.0)
     f_write = COPY_BYTES / (cw * 1024.0)
+    per_call = DISPATCHES_PER_CALL.get(kernel, 1)
     out = {
         "workload": workload, "kernel": kernel,
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": [nf, nw],
+        "dispatches_per_call": per_call,
         "copy_factor_fetch": f_fetch, "copy_factor_write": f_write,
-        "bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write,
+        "bytes_per_launch": per_call * (fetch * 1024.0 * f_fetch + write * 1024.0 * f_write),
         "source_hash": source_hash(),
         "command": "see bench_traffic.py docstring (FETCH_SIZE and WRITE_SIZE runs of bench.py --workload "
                    f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --no-breakdown --no-next, plus the copy calibration)",
     }
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -110,7 +118,7 @@ def summarize(root, workload, kernel):
 
 def load(workload, kernel):
     """Traffic per launch in bytes for bench.py, or None when absent or stale."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel}.json")
     try:
         with open(path) as f:
             t = json.load(f)
