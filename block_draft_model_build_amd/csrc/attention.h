@@ -132,8 +132,6 @@ __device__ __forceinline__ void attn_scores(const GetK& getk,
     }
 }
 
-// getv(st, ds) returns the V^T fragment of MFMA step st, d-tile ds.
-//
 // Two ways to keep P = 2^(s - m) in range (O and l always share the reference m,
 // so both give the same softmax):
 // - fixed (LAZY false): m is the maximum of the first visible keys of each query
@@ -144,12 +142,14 @@ __device__ __forceinline__ void attn_scores(const GetK& getk,
 //   kLazy, and O and l are rescaled then.
 constexpr float kFixedRange = 32.f;
 
-template <typename T, int D, int QC, bool LAZY, class GetV>
-__device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& getv, int nvalid,
-                                            f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
-                                            float (&l)[QC / 32], float (&mt)[QC / 32], int lane) {
+// Softmax half of a slice: masks keys at or past `nvalid`, updates the running
+// state (m, l, mt; O is rescaled only in the lazy form) and returns P = 2^(s - m)
+// as the B operand of the P.V product (pf[st][qs]: keys 16 st .. 16 st + 15).
+template <typename T, int D, int QC, bool LAZY>
+__device__ __forceinline__ void attn_softmax(f32x16 (&s)[QC / 32], int nvalid, f32x16 (&o)[D / 32][QC / 32],
+                                             float (&m)[QC / 32], float (&l)[QC / 32], float (&mt)[QC / 32],
+                                             typename Mfma<T>::frag (&pf)[32 / Mfma<T>::KSTEP][QC / 32], int lane) {
     using TT = AttnTile<T, D, QC>;
-    typedef typename Mfma<T>::frag frag;
     constexpr int QS = TT::QS, DS = TT::DS, PK = TT::PK, E = TT::E;
     const int h = lane >> 5;
     constexpr float kLazy = 8.f;
@@ -192,21 +192,34 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
         l[qs] += ps;
     }
 #pragma unroll
-    for (int st = 0; st < PK; ++st) {
-        frag pf[QS];
+    for (int st = 0; st < PK; ++st)
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
             if constexpr (E == 8) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pf[qs][i] = from_f32<T>(s[qs][st * 8 + i]);
+                for (int i = 0; i < 8; ++i) pf[st][qs][i] = from_f32<T>(s[qs][st * 8 + i]);
             } else {
-                pf[qs] = s[qs][st];
+                pf[st][qs] = s[qs][st];
             }
         }
+}
+
+// P.V half of a slice: O^T += V^T P^T; getv(st, ds) returns the V^T fragment of
+// MFMA step st, d-tile ds. Keys at or past `nvalid` enter as exact zeros of V,
+// even where V is not finite.
+template <typename T, int D, int QC, class GetV>
+__device__ __forceinline__ void attn_pv(const typename Mfma<T>::frag (&pf)[32 / Mfma<T>::KSTEP][QC / 32],
+                                        const GetV& getv, int nvalid, f32x16 (&o)[D / 32][QC / 32], int lane) {
+    using TT = AttnTile<T, D, QC>;
+    typedef typename Mfma<T>::frag frag;
+    constexpr int QS = TT::QS, DS = TT::DS, PK = TT::PK, E = TT::E;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int st = 0; st < PK; ++st)
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
             frag a = getv(st, ds);
-            if (nvalid < 32) {        // keys past the end: exact zeros, even if V is not finite
+            if (nvalid < 32) {
                 const int nv = nvalid - 8 * h;
                 if constexpr (E == 8) {
 #pragma unroll
@@ -217,9 +230,17 @@ __device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& ge
                 }
             }
 #pragma unroll
-            for (int qs = 0; qs < QS; ++qs) o[ds][qs] = Mfma<T>::mma(a, pf[qs], o[ds][qs]);
+            for (int qs = 0; qs < QS; ++qs) o[ds][qs] = Mfma<T>::mma(a, pf[st][qs], o[ds][qs]);
         }
-    }
+}
+
+template <typename T, int D, int QC, bool LAZY, class GetV>
+__device__ __forceinline__ void attn_update(f32x16 (&s)[QC / 32], const GetV& getv, int nvalid,
+                                            f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
+                                            float (&l)[QC / 32], float (&mt)[QC / 32], int lane) {
+    typename Mfma<T>::frag pf[32 / Mfma<T>::KSTEP][QC / 32];
+    attn_softmax<T, D, QC, LAZY>(s, nvalid, o, m, l, mt, pf, lane);
+    attn_pv<T, D, QC>(pf, getv, nvalid, o, lane);
 }
 
 // One wave folds the 32-key slice starting at key0 of a tile staged in LDS
@@ -247,6 +268,103 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int k
             return *reinterpret_cast<const T*>(vt + TT::voff(d, key0 + acc_key(st) + 8 * h));
     };
     attn_update<T, D, QC, LAZY>(sc, getv, nvalid, o, m, l, mt, lane);
+}
+
+// Softmax of one query half qs of a slice with every key visible, fixed
+// reference (the state update of attn_softmax for that half alone).
+template <typename T, int D, int QC>
+__device__ __forceinline__ void attn_softmax_half(f32x16& s, int qs, float (&m)[QC / 32], float (&l)[QC / 32],
+                                                  float (&mt)[QC / 32], typename Mfma<T>::frag (&pf)[32 / Mfma<T>::KSTEP]) {
+    constexpr int PK = 32 / Mfma<T>::KSTEP;
+    const float NEG_INF = -__builtin_inff();
+    float mx = NEG_INF;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    mx = fmaxf(mx, xor32(mx));
+    if (m[qs] == NEG_INF) m[qs] = mx;
+    mt[qs] = fmaxf(mt[qs], mx);
+    const float muse = (m[qs] == NEG_INF) ? 0.f : m[qs];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        s[e] = fast_exp2(s[e] - muse);
+        ps += s[e];
+    }
+    l[qs] += ps;
+#pragma unroll
+    for (int st = 0; st < PK; ++st)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pf[st][i] = from_f32<T>(s[st * 8 + i]);
+}
+
+// One wave folds all four 32-key slices of a 128-key bf16 tile staged in LDS,
+// every key visible, with the fixed softmax reference. Work is split into
+// units u = 2 * slice + qs (a slice's scores for one half of the query
+// columns), which are independent in the softmax and in the P.V product. The
+// units are software-pipelined: stage u runs the score MFMAs of unit u + 1
+// and the P.V MFMAs of unit u - 1 on the matrix cores while the vector units
+// run the softmax of unit u (none of the three depends on another, and with
+// the fixed reference the softmax never touches O).
+template <typename T, int D, int QC>
+__device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* vt,
+                                                    const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
+                                                    f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
+                                                    float (&l)[QC / 32], float (&mt)[QC / 32], int lane) {
+    using TT = AttnTile<T, D, QC>;
+    typedef typename Mfma<T>::frag frag;
+    constexpr int QS = TT::QS, PK = TT::PK, E = TT::E, EB = TT::EB, DK = TT::DK, DS = TT::DS;
+    static_assert(E == 8 && TT::SWZ && QS == 2, "bf16 tiles, two query halves");
+    const int h = lane >> 5;
+    const int kr = key_perm(lane & 31);
+    frag kf[DK], vf[PK][DS];
+    f32x16 sc[QS];
+    frag pf[QS][PK];
+    auto load_k = [&](int sl) {
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk)
+            kf[kk] = *reinterpret_cast<const frag*>(ks + TT::koff(sl * 32 + kr, (kk * TT::KSTEP + h * E) * EB));
+    };
+    auto load_v = [&](int sl) {
+#pragma unroll
+        for (int st = 0; st < PK; ++st)
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+                vf[st][ds] = *reinterpret_cast<const frag*>(vt + TT::voff(ds * 32 + (lane & 31), sl * 32 + 16 * st + 8 * h));
+    };
+    auto scores = [&](int qs) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[qs][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) sc[qs] = Mfma<T>::mma(kf[kk], qf[qs][kk], sc[qs]);
+    };
+    auto pv = [&](int qs) {
+#pragma unroll
+        for (int st = 0; st < PK; ++st)
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) o[ds][qs] = Mfma<T>::mma(vf[st][ds], pf[qs][st], o[ds][qs]);
+    };
+    load_k(0);
+    scores(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        // unit u + 1 needs the K fragments of slice (u + 1) / 2, unit u - 1 the
+        // V fragments of slice (u - 1) / 2: both are new on odd u.
+        if (u & 1) {
+            if (u + 1 < 8) load_k((u + 1) >> 1);
+            load_v((u - 1) >> 1);
+        }
+        if (u + 1 < 8) scores((u + 1) & 1);
+        if (u >= 1) pv((u - 1) & 1);
+        attn_softmax_half<T, D, QC>(sc[u & 1], u & 1, m, l, mt, pf[u & 1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    pv(1);
 }
 
 // Fragments of one 32-key slice straight from the context caches (no LDS):
@@ -308,7 +426,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     constexpr int KSTEP = TT::KSTEP, SUPER = TT::SUPER;
     __shared__ __attribute__((aligned(16))) char smem[TT::LDS_BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    // The wave index is uniform across the wave: scalar registers for everything derived from it.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5;
     const int hkv = p.hkv, bs = p.bs, G = p.hq / p.hkv;
     const int ngroups = p.sched[1];
     const int total = p.item_start[ngroups] * hkv;
@@ -391,6 +510,15 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
     }
 
+    // Q is only ever an MFMA operand, which may sit in AGPRs (gfx950): keep it
+    // there and leave the VGPRs to the softmax and the K/V fragments.
+    if constexpr (E == 8) {
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk) asm volatile("" : "+a"(qf[qs][kk]));
+    }
+
     f32x16 o[DS][QS];
     float m[QS], l[QS], mt[QS];          // reference, sum, true maximum (attn_update)
 #pragma unroll
@@ -457,23 +585,36 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // lands at physical chunk i % 16 of row i / 16, so it fetches the logical
     // chunk (i % 16) ^ (row & 15). Keys past the group's end are read as they
     // are: scores there are masked and V there is zeroed before use.
-    auto tile_dma_ok = [&](int t0) { return TT::SWZ && (int64_t)t0 + SUPER <= lim; };
+    auto tile_dma_ok = [&](int t0) { return TT::SWZ && (int64_t)t0 + SUPER <= lim && p.ctx_total < (1 << 28); };
+    // Sources are a wave-uniform base plus a 32-bit lane offset; the swizzle
+    // (row & 15) repeats every 4 instructions, so 4 lane offsets serve all 8
+    // rows of each cache (the V^T offsets stay below 2^32 bytes because
+    // tile_dma_ok limits ctx_total).
+    const int rsub = lane >> 4, pc = lane & 15;
+    uint32_t koff_l[4], voff_l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = i * 4 + rsub;                   // row within a 16-row swizzle period
+        koff_l[i] = (uint32_t)(r * D + (pc ^ r) * EC) * EB;
+        voff_l[i] = (uint32_t)((int64_t)r * p.ctx_total + (pc ^ r) * EC) * EB;
+    }
     auto issue_dma = [&](int t0, int stage) {
         if constexpr (TT::SWZ) {
             char* Ks = smem + stage * TT::STAGE;
             char* Vt = Ks + TT::KS_BYTES;
-            const int rsub = lane >> 4, pc = lane & 15;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int R = wave * 32 + i * 4, r = R + rsub;
-                const T* src = ckg + (int64_t)(t0 + r) * D + (pc ^ (r & 15)) * EC;
-                __builtin_amdgcn_global_load_lds(DFLASH_GPTR(src), DFLASH_LPTR(Ks + R * TT::KROW), 16, 0, 0);
+                const int R = wave * 32 + i * 4;      // first row of this instruction
+                const char* kb = reinterpret_cast<const char*>(ckg + (int64_t)(t0 + R - (i & 3) * 4) * D);
+                __builtin_amdgcn_global_load_lds(DFLASH_GPTR(kb + koff_l[i & 3]), DFLASH_LPTR(Ks + R * TT::KROW), 16,
+                                                 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int R = wave * 32 + i * 4, d = R + rsub;
-                const T* src = cvg + (int64_t)d * p.ctx_total + t0 + (pc ^ (d & 15)) * EC;
-                __builtin_amdgcn_global_load_lds(DFLASH_GPTR(src), DFLASH_LPTR(Vt + R * TT::VROW), 16, 0, 0);
+                const int R = wave * 32 + i * 4;
+                const char* vb = reinterpret_cast<const char*>(cvg + (int64_t)(R - (i & 3) * 4) * p.ctx_total + t0);
+                __builtin_amdgcn_global_load_lds(DFLASH_GPTR(vb + voff_l[i & 3]), DFLASH_LPTR(Vt + R * TT::VROW), 16,
+                                                 0, 0);
             }
         }
     };
@@ -562,19 +703,42 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
         wait_vmcnt<0>();
         __syncthreads();
-        for (int t = 0; t < ntile; ++t) {
+        // Leading tiles that every block of the group sees whole, with one wave
+        // per block: pipelined slices (attn_tile_pipelined). The count is
+        // uniform over the workgroup, so the tile loop splits in two with the
+        // same staging and barriers in both.
+        int nfull = 0;
+        if constexpr (!REDO && QS == 2) {
+            if (wpb == 1) {
+                int kmin = kbeg + chunk;
+                for (int jj = 0; jj < ng; ++jj) kmin = min(kmin, anchor_eff(p.anchor[n0 + jj], base, p.ctx_total));
+                nfull = kmin > kbeg ? min(ntile, (kmin - kbeg) / SUPER) : 0;
+            }
+        }
+        auto stage_next = [&](int t, auto&& compute) {
             const int t1 = kbeg + (t + 1) * SUPER;
             const bool next = t + 1 < ntile;
             const bool dma = next && tile_dma_ok(t1);
             if (dma) issue_dma(t1, (t + 1) & 1);
-            tile_compute(t);
+            compute(t);
             if (next && !dma) {
                 gload(t1);
                 lstore((t + 1) & 1);
             }
             wait_vmcnt<0>();
             __syncthreads();
+        };
+        int t = 0;
+        if constexpr (!REDO && QS == 2) {
+            for (; t < nfull; ++t)
+                stage_next(t, [&](int tt) {
+                    if (active) {
+                        const char* Ks = smem + (tt & 1) * TT::STAGE;
+                        attn_tile_pipelined<T, D, QC>(Ks, Ks + TT::KS_BYTES, qf, o, m, l, mt, lane);
+                    }
+                });
         }
+        for (; t < ntile; ++t) stage_next(t, tile_compute);
     }
     if constexpr (!STREAM && !TT::SWZ) {
         if (ntile > 0) {
