@@ -141,6 +141,10 @@ __device__ __forceinline__ void attn_scores(const GetK& getk,
 // - lazy (LAZY true): m moves when some column's scores pass it by more than
 //   kLazy, and O and l are rescaled then.
 constexpr float kFixedRange = 32.f;
+// Range guard of the pipelined tiles, which track no maximum: a column whose
+// row sum l (relative to m) passes this is flagged for the LAZY run. Every P
+// of the column is then at most l, and |O| at most l * max |V|.
+constexpr float kFixedSum = 1099511627776.f;   // 2^40
 
 // Softmax half of a slice: masks keys at or past `nvalid`, updates the running
 // state (m, l, mt; O is rescaled only in the lazy form) and returns P = 2^(s - m)
@@ -271,23 +275,31 @@ __device__ __forceinline__ void attn_slice(const char* ks, const char* vt, int k
 }
 
 // Softmax of one query half qs of a slice with every key visible, fixed
-// reference (the state update of attn_softmax for that half alone).
-template <typename T, int D, int QC>
+// reference. With SET the scores are raw: their maximum sets the reference m
+// of columns that have none yet (and feeds the true maximum mt). Otherwise
+// the score product started from -m, so P = 2^s directly; mt is not tracked
+// there, and the row sum l guards the range instead (block_attn_kernel flags
+// an item whose l passes kFixedSum).
+template <typename T, int D, int QC, bool SET>
 __device__ __forceinline__ void attn_softmax_half(f32x16& s, int qs, float (&m)[QC / 32], float (&l)[QC / 32],
                                                   float (&mt)[QC / 32], typename Mfma<T>::frag (&pf)[32 / Mfma<T>::KSTEP]) {
     constexpr int PK = 32 / Mfma<T>::KSTEP;
-    const float NEG_INF = -__builtin_inff();
-    float mx = NEG_INF;
+    if constexpr (SET) {
+        const float NEG_INF = -__builtin_inff();
+        float mx = NEG_INF;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    mx = fmaxf(mx, xor32(mx));
-    if (m[qs] == NEG_INF) m[qs] = mx;
-    mt[qs] = fmaxf(mt[qs], mx);
-    const float muse = (m[qs] == NEG_INF) ? 0.f : m[qs];
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        mx = fmaxf(mx, xor32(mx));
+        if (m[qs] == NEG_INF) m[qs] = mx;
+        mt[qs] = fmaxf(mt[qs], mx);
+        const float muse = (m[qs] == NEG_INF) ? 0.f : m[qs];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] -= muse;
+    }
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        s[e] = fast_exp2(s[e] - muse);
+        s[e] = fast_exp2(s[e]);
         ps += s[e];
     }
     l[qs] += ps;
@@ -304,8 +316,9 @@ __device__ __forceinline__ void attn_softmax_half(f32x16& s, int qs, float (&m)[
 // units are software-pipelined: stage u runs the score MFMAs of unit u + 1
 // and the P.V MFMAs of unit u - 1 on the matrix cores while the vector units
 // run the softmax of unit u (none of the three depends on another, and with
-// the fixed reference the softmax never touches O).
-template <typename T, int D, int QC>
+// the fixed reference the softmax never touches O). FIRST: the columns have
+// no reference yet, and units 0 and 1 set it.
+template <typename T, int D, int QC, bool FIRST>
 __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* vt,
                                                     const typename Mfma<T>::frag (&qf)[QC / 32][D / Mfma<T>::KSTEP],
                                                     f32x16 (&o)[D / 32][QC / 32], float (&m)[QC / 32],
@@ -331,9 +344,12 @@ __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* 
             for (int ds = 0; ds < DS; ++ds)
                 vf[st][ds] = *reinterpret_cast<const frag*>(vt + TT::voff(ds * 32 + (lane & 31), sl * 32 + 16 * st + 8 * h));
     };
-    auto scores = [&](int qs) {
+    // Unit u's scores start from -m (0 for the units that set m).
+    auto scores = [&](int u) {
+        const int qs = u & 1;
+        const float init = (FIRST && u < 2) ? 0.f : -m[qs];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[qs][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sc[qs][e] = init;
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) sc[qs] = Mfma<T>::mma(kf[kk], qf[qs][kk], sc[qs]);
     };
@@ -354,13 +370,16 @@ __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* 
             if (u + 1 < 8) load_k((u + 1) >> 1);
             load_v((u - 1) >> 1);
         }
-        if (u + 1 < 8) scores((u + 1) & 1);
+        if (u + 1 < 8) scores(u + 1);
         if (u >= 1) pv((u - 1) & 1);
-        attn_softmax_half<T, D, QC>(sc[u & 1], u & 1, m, l, mt, pf[u & 1]);
+        if (FIRST && u < 2)
+            attn_softmax_half<T, D, QC, true>(sc[u & 1], u & 1, m, l, mt, pf[u & 1]);
+        else
+            attn_softmax_half<T, D, QC, false>(sc[u & 1], u & 1, m, l, mt, pf[u & 1]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -730,11 +749,19 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         };
         int t = 0;
         if constexpr (!REDO && QS == 2) {
+            // Splits after the first have no own keys: their first tile sets
+            // the reference.
+            if (s > 0 && nfull > 0) {
+                stage_next(0, [&](int tt) {
+                    if (active) attn_tile_pipelined<T, D, QC, true>(smem, smem + TT::KS_BYTES, qf, o, m, l, mt, lane);
+                });
+                t = 1;
+            }
             for (; t < nfull; ++t)
                 stage_next(t, [&](int tt) {
                     if (active) {
                         const char* Ks = smem + (tt & 1) * TT::STAGE;
-                        attn_tile_pipelined<T, D, QC>(Ks, Ks + TT::KS_BYTES, qf, o, m, l, mt, lane);
+                        attn_tile_pipelined<T, D, QC, false>(Ks, Ks + TT::KS_BYTES, qf, o, m, l, mt, lane);
                     }
                 });
         }
@@ -757,7 +784,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     if constexpr (!REDO) {
         bool over = false;
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs) over |= mt[qs] > m[qs] + kFixedRange;
+        for (int qs = 0; qs < QS; ++qs) over |= mt[qs] > m[qs] + kFixedRange || !(l[qs] <= kFixedSum);
         over = __any(over);
         if (lane == 0) p.redo[4 * (int64_t)item + wave] = over ? 1 : 0;
     }
