@@ -31,6 +31,8 @@
 // in split order, so results do not depend on timing.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dflash {
@@ -97,6 +99,13 @@ struct AttnTile {
     static constexpr int KS_BYTES = SUPER * KROW;
     static constexpr int VT_BYTES = D * VROW;
     static constexpr int STAGE = KS_BYTES + VT_BYTES;
+    // LDS layout: K stage 0, K stage 1, V^T stage 0, V^T stage 1 (bf16: 32 KB
+    // each), so that with the stage known at compile time every fragment read
+    // of a tile is a base register plus an immediate offset below 64 KB.
+    __device__ static __forceinline__ char* kstage(char* smem, int stage) { return smem + stage * KS_BYTES; }
+    __device__ static __forceinline__ char* vstage(char* smem, int stage) {
+        return smem + 2 * KS_BYTES + stage * VT_BYTES;
+    }
     static constexpr int SLOT_FLOATS = DS * QS * 16 * 64;
     static constexpr int MERGE_BYTES = 2 * SLOT_FLOATS * 4 + 2 * 2 * QS * 64 * 4;
     static constexpr int LDS_BYTES = 2 * STAGE > MERGE_BYTES ? 2 * STAGE : MERGE_BYTES;
@@ -296,17 +305,16 @@ __device__ __forceinline__ void attn_softmax_half(f32x16& s, int qs, float (&m)[
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] -= muse;
     }
-    float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        s[e] = fast_exp2(s[e]);
-        ps += s[e];
-    }
-    l[qs] += ps;
+    for (int e = 0; e < 16; ++e) s[e] = fast_exp2(s[e]);
 #pragma unroll
     for (int st = 0; st < PK; ++st)
 #pragma unroll
         for (int i = 0; i < 8; ++i) pf[st][i] = from_f32<T>(s[st * 8 + i]);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ps += s[e];
+    l[qs] += ps;
 }
 
 // One wave folds all four 32-key slices of a 128-key bf16 tile staged in LDS,
@@ -352,6 +360,7 @@ __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* 
         for (int e = 0; e < 16; ++e) sc[qs][e] = init;
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) sc[qs] = Mfma<T>::mma(kf[kk], qf[qs][kk], sc[qs]);
+        asm volatile("" : "+v"(sc[qs]));      // the softmax reads them: VGPRs
     };
     auto pv = [&](int qs) {
 #pragma unroll
@@ -586,8 +595,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
     };
     auto lstore = [&](int stage) {
-        char* Ks = smem + stage * TT::STAGE;
-        char* Vt = Ks + TT::KS_BYTES;
+        char* Ks = TT::kstage(smem, stage);
+        char* Vt = TT::vstage(smem, stage);
 #pragma unroll
         for (int i = 0; i < TT::KLD; ++i) {
             const int c = tid + 256 * i;
@@ -619,8 +628,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     }
     auto issue_dma = [&](int t0, int stage) {
         if constexpr (TT::SWZ) {
-            char* Ks = smem + stage * TT::STAGE;
-            char* Vt = Ks + TT::KS_BYTES;
+            char* Ks = TT::kstage(smem, stage);
+            char* Vt = TT::vstage(smem, stage);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int R = wave * 32 + i * 4;      // first row of this instruction
@@ -648,8 +657,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // ---- split 0: the blocks' own keys. Block jj's rows go to slot jj (32 rows)
     // of stage OWN: K rotated at its anchor + k', V^T transposed; rows >= bs zero.
     if (s == 0) {
-        char* Ks = smem + OWN * TT::STAGE;
-        char* Vt = Ks + TT::KS_BYTES;
+        char* Ks = TT::kstage(smem, OWN);
+        char* Vt = TT::vstage(smem, OWN);
         for (int idx = tid; idx < ng * 32 * (D / 2); idx += 256) {
             const int jj = idx / (32 * (D / 2)), r = idx - jj * 32 * (D / 2);
             const int k = r / (D / 2), i = r - k * (D / 2);
@@ -703,8 +712,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // One tile of this wave's block: its slices phase, phase + wpb, ...
     auto tile_compute = [&](int t) {
         if (active && a >= 0) {
-            const char* Ks = smem + (t & 1) * TT::STAGE;
-            const char* Vt = Ks + TT::KS_BYTES;
+            const char* Ks = TT::kstage(smem, t & 1);
+            const char* Vt = TT::vstage(smem, t & 1);
             for (int sl = phase; sl < SUPER / 32; sl += wpb) {
                 const int nvalid = kend - (kbeg + t * SUPER + sl * 32);
                 if (nvalid > 0)
@@ -749,21 +758,31 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         };
         int t = 0;
         if constexpr (!REDO && QS == 2) {
+            // The stage of each tile is a compile-time constant (tile t sits
+            // in stage t & 1): pairs of tiles per iteration.
+            auto piped = [&](int tt, auto first, auto stage) {
+                stage_next(tt, [&](int) {
+                    if (active)
+                        attn_tile_pipelined<T, D, QC, decltype(first)::value>(
+                            TT::kstage(smem, decltype(stage)::value), TT::vstage(smem, decltype(stage)::value), qf, o,
+                            m, l, mt, lane);
+                });
+            };
+            using S0 = std::integral_constant<int, 0>;
+            using S1 = std::integral_constant<int, 1>;
+            using F0 = std::integral_constant<bool, false>;
             // Splits after the first have no own keys: their first tile sets
             // the reference.
             if (s > 0 && nfull > 0) {
-                stage_next(0, [&](int tt) {
-                    if (active) attn_tile_pipelined<T, D, QC, true>(smem, smem + TT::KS_BYTES, qf, o, m, l, mt, lane);
-                });
+                piped(0, std::integral_constant<bool, true>(), S0());
                 t = 1;
             }
-            for (; t < nfull; ++t)
-                stage_next(t, [&](int tt) {
-                    if (active) {
-                        const char* Ks = smem + (tt & 1) * TT::STAGE;
-                        attn_tile_pipelined<T, D, QC, false>(Ks, Ks + TT::KS_BYTES, qf, o, m, l, mt, lane);
-                    }
-                });
+            if (t < nfull && (t & 1)) piped(t++, F0(), S1());
+            for (; t + 1 < nfull; t += 2) {
+                piped(t, F0(), S0());
+                piped(t + 1, F0(), S1());
+            }
+            if (t < nfull) piped(t++, F0(), S0());
         }
         for (; t < ntile; ++t) stage_next(t, tile_compute);
     }
