@@ -7,8 +7,8 @@ copy (1 GiB read + 1 GiB written, run with `python bench_traffic.py --copy`
 under the same counter). The result is written to
 profiles/traffic_<workload>_<kernel>.json together with a hash of the forward
 kernels' sources, so bench.py reports it only while those kernels are
-unchanged. A kernel made of several launches per call (attention: the shared
-and streaming instantiations and the redo pass) is counted per call: the bytes
+unchanged. A kernel made of several launches per call (attention: the main
+pass and the redo pass) is counted per call: the bytes
 of all its dispatches divided by the number of calls.
 
 On a machine with the GPU, from the repo root (OUT is any output folder):
@@ -40,7 +40,7 @@ KERNEL_MATCH = {
     "attention": "block_attn_kernel", "attn_combine": "attn_combine_kernel", "rmsnorm": "rmsnorm_kernel",
 }
 # Launches per call of the library's kernel (every call makes all of them).
-DISPATCHES_PER_CALL = {"attention": 3}
+DISPATCHES_PER_CALL = {"attention": 2}
 
 
 def _strip_comments(text: str) -> str:

@@ -23,12 +23,17 @@
 // operand is then one 16-byte LDS read. The context V cache is stored
 // transposed ([Hkv][D][T]) so V^T tiles are staged into LDS by plain copies.
 //
-// Per 128-key super-tile the K rows and V^T columns go HBM -> registers -> LDS
-// with two LDS stages and one register stage (two tiles in flight, one barrier
-// per tile). Waves serving the same block merge their softmax states through
-// LDS at the end. When a group's prefix is split over several items, each item
-// writes per-block partial (max, sum, O) and a combine kernel merges the splits
-// in split order, so results do not depend on timing.
+// Per 128-key super-tile the K rows and V^T columns go into one of two LDS
+// stages (bf16: direct-to-LDS loads, through registers only for a tile that
+// crosses the end of the caches; fp32: through registers), one barrier per
+// tile, the next tile in flight while this one is computed. A wave that owns
+// its block and sees a tile whole runs the tile's slices software-pipelined
+// (attn_tile_pipelined); partial tiles, and blocks shared by several waves (a
+// group of one or two blocks), run slice by slice. Waves serving the same
+// block merge their softmax states through LDS at the end. When a group's
+// prefix is split over several items, each item writes per-block partial
+// (max, sum, O) and a combine kernel merges the splits in split order, so
+// results do not depend on timing.
 #pragma once
 
 #include <type_traits>
@@ -395,59 +400,12 @@ __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* 
     pv(1);
 }
 
-// Fragments of one 32-key slice straight from the context caches (no LDS):
-// K row key_perm(lane % 32) of the slice, and V^T rows d at the slice's keys.
-// Keys at or past `kend` read the last visible K row, and their V^T elements
-// are loaded one by one as zeros, so nothing outside the caches is touched.
-template <typename T, int D, int QC>
-__device__ __forceinline__ void attn_load_k(const T* ckg, int key0, int kend,
-                                            typename Mfma<T>::frag (&kf)[D / Mfma<T>::KSTEP], int lane) {
-    using TT = AttnTile<T, D, QC>;
-    typedef typename Mfma<T>::frag frag;
-    int key = key0 + key_perm(lane & 31);
-    key = key < kend ? key : kend - 1;
-    const T* kr = ckg + (int64_t)key * D + (lane >> 5) * TT::E;
-#pragma unroll
-    for (int kk = 0; kk < TT::DK; ++kk) kf[kk] = *reinterpret_cast<const frag*>(kr + kk * TT::KSTEP);
-}
-
-template <typename T, int D, int QC>
-__device__ __forceinline__ void attn_load_v(const T* cvg, int64_t ctx_total, int key0, int kend,
-                                            typename Mfma<T>::frag (&vf)[32 / Mfma<T>::KSTEP][D / 32], int lane) {
-    using TT = AttnTile<T, D, QC>;
-    typedef typename Mfma<T>::frag frag;
-    const int h = lane >> 5;
-    const bool full = key0 + 32 <= kend;
-#pragma unroll
-    for (int st = 0; st < TT::PK; ++st)
-#pragma unroll
-        for (int ds = 0; ds < TT::DS; ++ds) {
-            const T* vr = cvg + (int64_t)(ds * 32 + (lane & 31)) * ctx_total + key0;
-            if constexpr (TT::E == 8) {
-                const int k0 = 16 * st + 8 * h;
-                if (full) {
-                    vf[st][ds] = *reinterpret_cast<const frag*>(vr + k0);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) vf[st][ds][i] = key0 + k0 + i < kend ? vr[k0 + i] : from_f32<T>(0.f);
-                }
-            } else {
-                const int kk = acc_key(st) + 8 * h;
-                vf[st][ds] = key0 + kk < kend ? vr[kk] : 0.f;
-            }
-        }
-}
-
-// STREAM selects the items this instantiation serves: single-block groups
-// (streamed from the caches into registers) or multi-block groups (shared
-// LDS tiles). Both are launched over the same item list, with the fixed
-// softmax reference, and record per wave whether its scores outran it. The
-// REDO instantiation, launched after them, runs only the items so recorded,
-// through the shared tiles with the lazily moved reference, and overwrites
-// their results.
-template <typename T, int D, int QC, bool STREAM, bool REDO = false>
+// The main instantiation runs every item with the fixed softmax reference
+// and records per wave whether its scores outran it. The REDO instantiation,
+// launched after it, runs only the items so recorded, with the lazily moved
+// reference, and overwrites their results.
+template <typename T, int D, int QC, bool REDO = false>
 __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
-    static_assert(!(STREAM && REDO), "the redo runs through the shared tiles");
     using TT = AttnTile<T, D, QC>;
     typedef typename Mfma<T>::frag frag;
     constexpr int QS = TT::QS, DS = TT::DS, DK = TT::DK, E = TT::E, EB = TT::EB, EC = TT::EC;
@@ -478,7 +436,6 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
     const int n0 = p.group_start[gi];
     const int ng = p.group_start[gi + 1] - n0;
-    if (!REDO && (ng == 1) != STREAM) return;
     const int wpb = ng == 1 ? 4 : (ng == 2 ? 2 : 1);   // waves per block
     const int j = wave / wpb;                          // this wave's block in the group
     const int phase = wave - j * wpb;                  // this wave's share of the block's keys
@@ -650,7 +607,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // bf16 stages the first tile while the blocks' own keys are processed
     // (they use stage 1); fp32 stages its tiles from registers below.
     constexpr int OWN = TT::SWZ ? 1 : 0;
-    if constexpr (!STREAM && TT::SWZ) {
+    if constexpr (TT::SWZ) {
         if (ntile > 0 && tile_dma_ok(kbeg)) issue_dma(kbeg, 0);
     }
 
@@ -688,27 +645,6 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         __syncthreads();
     }
 
-    if constexpr (STREAM) {
-        // One block: the 4 waves take interleaved 32-key slices and stream them
-        // from the caches into registers. Each buffer is refilled for the next
-        // slice right after its last use (K after the score MFMAs, V^T after
-        // the P.V MFMAs), so loads overlap the rest of the slice's work.
-        const int nsl = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
-        if (wave < nsl) {
-            frag kf[DK], vf[TT::PK][DS];
-            attn_load_k<T, D, QC>(ckg, kbeg + 32 * wave, kend, kf, lane);
-            attn_load_v<T, D, QC>(cvg, p.ctx_total, kbeg + 32 * wave, kend, vf, lane);
-            for (int i = wave; i < nsl; i += 4) {
-                const bool more = i + 4 < nsl;
-                f32x16 sc[QS];
-                attn_scores<T, D, QC>([&](int kk) { return kf[kk]; }, qf, sc);
-                if (more) attn_load_k<T, D, QC>(ckg, kbeg + 32 * (i + 4), kend, kf, lane);
-                attn_update<T, D, QC, false>(sc, [&](int st, int ds) { return vf[st][ds]; },
-                                             min(32, kend - (kbeg + 32 * i)), o, m, l, mt, lane);
-                if (more) attn_load_v<T, D, QC>(cvg, p.ctx_total, kbeg + 32 * (i + 4), kend, vf, lane);
-            }
-        }
-    }
     // One tile of this wave's block: its slices phase, phase + wpb, ...
     auto tile_compute = [&](int t) {
         if (active && a >= 0) {
@@ -721,7 +657,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             }
         }
     };
-    if constexpr (!STREAM && TT::SWZ) {
+    if constexpr (TT::SWZ) {
         // Tile t + 1 is staged into the other stage while tile t is computed:
         // by DMA when it lies inside the cache range, else (a tile crossing the
         // end of the caches) through registers after this tile's work.
@@ -786,7 +722,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
         for (; t < ntile; ++t) stage_next(t, tile_compute);
     }
-    if constexpr (!STREAM && !TT::SWZ) {
+    if constexpr (!TT::SWZ) {
         if (ntile > 0) {
             gload(kbeg);
             lstore(0);
@@ -955,11 +891,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
 // of 4 or whose (clamped) context base differs from the previous block's. A
 // group's stream length is its largest (clamped) anchor. Single-block and
 // multi-block groups get separate split sizes: chunk = max(256, ceil(sum of
-// their lengths / target) rounded up to 128), target_stream (single) or
+// their lengths / target) rounded up to 128), target_single (single) or
 // target_shared (multi) splits in total; a group gets max(1, ceil(length /
 // chunk)) splits.
 static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
-                                                             int64_t ctx_total, int target_shared, int target_stream,
+                                                             int64_t ctx_total, int target_shared, int target_single,
                                                              int* group_start, int* item_start, int* sched) {
     __shared__ int scan[1024];
     __shared__ long long red[2][1024];
@@ -1022,7 +958,7 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
         __syncthreads();
     }
     if (tid < 2) {
-        const int target = tid == 0 ? target_shared : target_stream;
+        const int target = tid == 0 ? target_shared : target_single;
         long long c = (red[tid][0] + target - 1) / target;
         c = (c + 127) / 128 * 128;
         if (c < 256) c = 256;

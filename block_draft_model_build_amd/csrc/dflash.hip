@@ -77,9 +77,8 @@ static hipError_t attn_launch_t(const dflash_config& c, const AttnArgs<T>& a, in
     const int items_max = attn_items_max(c, nb);
     {
         ProfScope prof(DFLASH_KERNEL_ATTENTION, st);
-        hipLaunchKernelGGL((block_attn_kernel<T, D, QC, false>), dim3(items_max), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((block_attn_kernel<T, D, QC>), dim3(items_max), dim3(256), 0, st, a);
         hipLaunchKernelGGL((block_attn_kernel<T, D, QC, true>), dim3(items_max), dim3(256), 0, st, a);
-        hipLaunchKernelGGL((block_attn_kernel<T, D, QC, false, true>), dim3(items_max), dim3(256), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -123,7 +122,7 @@ static hipError_t attn_schedule(const dflash_config& c, int nb, const int64_t* b
                                 int64_t ctx_total, char* ws, const Workspace& w, hipStream_t st) {
     const int hkv = c.num_kv_heads;
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, base, anchor, nb, ctx_total,
-                       (kAttnItemsShared + hkv - 1) / hkv, (kAttnItemsStream + hkv - 1) / hkv,
+                       (kAttnItemsShared + hkv - 1) / hkv, (kAttnItemsSingle + hkv - 1) / hkv,
                        reinterpret_cast<int*>(ws + w.group_start),
                        reinterpret_cast<int*>(ws + w.item_start), reinterpret_cast<int*>(ws + w.sched));
     return hipGetLastError();

@@ -16,15 +16,15 @@ inline int elem_bytes(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 
 
 // The attention scheduler sizes splits so that about kAttnItemsShared work
 // items (group x split x KV head) carry the prefix work of multi-block groups
-// (shared, cache-fed K/V tiles: long items are cheapest) and about
-// kAttnItemsStream that of single-block groups (streamed, latency-bound: more
-// items in flight help). Both were chosen by a sweep over 256..2048 items on
+// (several blocks share each K/V tile: long items are cheapest) and about
+// kAttnItemsSingle that of single-block groups (each block reads its own
+// prefix: more items in flight help). Chosen by sweeps over 256..2048 items on
 // the 5-layer, long-context and ragged-cache workloads.
 constexpr int kAttnItemsShared = 256;
-constexpr int kAttnItemsStream = 1024;
+constexpr int kAttnItemsSingle = 1024;
 inline int attn_target_splits(const dflash_config& c, int nb) {
     (void)nb;
-    return (kAttnItemsShared + kAttnItemsStream + c.num_kv_heads - 1) / c.num_kv_heads;
+    return (kAttnItemsShared + kAttnItemsSingle + c.num_kv_heads - 1) / c.num_kv_heads;
 }
 
 inline int attn_qcols(const dflash_config& c) {
