@@ -390,11 +390,7 @@ __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* 
             attn_softmax_half<T, D, QC, true>(sc[u & 1], u & 1, m, l, mt, pf[u & 1]);
         else
             attn_softmax_half<T, D, QC, false>(sc[u & 1], u & 1, m, l, mt, pf[u & 1]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
+
         __builtin_amdgcn_sched_barrier(0);
     }
     pv(1);
