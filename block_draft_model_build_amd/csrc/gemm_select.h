@@ -10,10 +10,14 @@ namespace dflash {
 // double buffered in LDS (the best of a measured sweep over tile shapes, wave
 // counts, slab depths and stage counts on the context-projection, gate/up and
 // down shapes); 128x128 tiles with 4 waves (one 32-row MFMA strip each) when
-// the big tiles would leave compute units idle.
+// the big tiles would leave compute units idle. When even the 128x128 grid is
+// at most one tile per compute unit (1024-row o_proj and down), a CU holds one
+// workgroup anyway, so its LDS goes to 128-byte slabs in 4 stages: twice the
+// bytes in flight (inference body 5.56 -> 5.40 ms per step).
 using BigTile = TileCfg<256, 256, 4, 2, 128, 2>;
 using MidTile = TileCfg<128, 128, 4, 1>;
-static_assert(BigTile::WN == 128 && MidTile::WN == 128, "gate/up interleave and RoPE pairing assume WN = 128");
+using MidDeep = TileCfg<128, 128, 4, 1, 128, 4>;
+static_assert(BigTile::WN == 128 && MidTile::WN == 128 && MidDeep::WN == 128, "gate/up interleave and RoPE pairing assume WN = 128");
 
 // `group`: row tiles walked together in the tile order (gemm_nt_kernel). 8 by
 // default; the context projection (K = 20480, A of stacked target states) is
@@ -25,6 +29,8 @@ static hipError_t gemm(int kid, int M, int N, int K, const AL& al, const BL& bl,
     ProfScope prof(kid, st);
     const int big_tiles = ((M + 255) / 256) * (N / 256);
     if (N % 256 == 0 && big_tiles >= 256) return launch_gemm<T, BigTile>(M, N, K, al, bl, ep, st, group);
+    const int mid_tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (mid_tiles <= 256) return launch_gemm<T, MidDeep>(M, N, K, al, bl, ep, st, group);
     return launch_gemm<T, MidTile>(M, N, K, al, bl, ep, st, group);
 }
 
