@@ -612,29 +612,69 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     if (s == 0) {
         char* Ks = TT::kstage(smem, OWN);
         char* Vt = TT::vstage(smem, OWN);
-        for (int idx = tid; idx < ng * 32 * (D / 2); idx += 256) {
-            const int jj = idx / (32 * (D / 2)), r = idx - jj * 32 * (D / 2);
-            const int k = r / (D / 2), i = r - k * (D / 2);
-            const int aj = anchor_eff(p.anchor[n0 + jj], base, p.ctx_total);
-            float y1 = 0.f, y2 = 0.f;
-            if (k < bs && aj >= 0) {
+        // Every 16-byte chunk of the group's K and V rows is requested before
+        // any is used (one round trip to memory, not one per element). K row
+        // chunks c and c + KCH/2 hold the rotation partners (i, i + D/2).
+        constexpr int HC = TT::KCH / 2;
+        constexpr int KIT = (kMaxGroup * 32 * HC + 255) / 256;
+        constexpr int VIT = (kMaxGroup * 32 * TT::KCH + 255) / 256;
+        const int nrows = ng * bs;
+        u32x4 k1[KIT], k2[KIT], vv[VIT];
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int w = tid + 256 * it, row = w / HC, c = w - row * HC;
+            k1[it] = k2[it] = u32x4{0, 0, 0, 0};
+            if (row < nrows) {
+                const int jj = row / bs, k = row - jj * bs;
                 const T* kr = p.kb + (int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D;
-                const float x1 = to_f32(kr[i]), x2 = to_f32(kr[i + D / 2]);
-                float cs, sn;
-                rope_cs(p.rt, i, aj + k, cs, sn);
-                y1 = x1 * cs - x2 * sn;
-                y2 = x2 * cs + x1 * sn;
+                k1[it] = *reinterpret_cast<const u32x4*>(kr + c * EC);
+                k2[it] = *reinterpret_cast<const u32x4*>(kr + (c + HC) * EC);
             }
-            *reinterpret_cast<T*>(Ks + TT::koff(jj * 32 + k, i * EB)) = from_f32<T>(y1);
-            *reinterpret_cast<T*>(Ks + TT::koff(jj * 32 + k, (i + D / 2) * EB)) = from_f32<T>(y2);
         }
-        for (int idx = tid; idx < ng * 32 * D; idx += 256) {
-            const int jj = idx / (32 * D), r = idx - jj * 32 * D;
-            const int k = r / D, d = r - k * D;
-            const int aj = p.anchor[n0 + jj];
-            T v = from_f32<T>(0.f);
-            if (k < bs && aj >= 0) v = p.vb[(int64_t)((n0 + jj) * bs + k) * p.kv_ld + (int64_t)g * D + d];
-            *reinterpret_cast<T*>(Vt + TT::voff(d, jj * 32 + k)) = v;
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int w = tid + 256 * it, row = w / TT::KCH, c = w - row * TT::KCH;
+            vv[it] = u32x4{0, 0, 0, 0};
+            if (row < nrows) {
+                const int jj = row / bs, k = row - jj * bs;
+                vv[it] = *reinterpret_cast<const u32x4*>(p.vb + (int64_t)((n0 + jj) * bs + k) * p.kv_ld +
+                                                         (int64_t)g * D + c * EC);
+            }
+        }
+        // Block jj's rows go to slot jj (32 rows) of stage OWN: K rotated at its
+        // anchor + k, V^T transposed. Rows bs..31 of a slot are never read
+        // unmasked (the own-key slice masks keys past bs), nor are empty blocks'.
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int w = tid + 256 * it, row = w / HC, c = w - row * HC;
+            if (row < nrows) {
+                const int jj = row / bs, k = row - jj * bs;
+                const int aj = anchor_eff(p.anchor[n0 + jj], base, p.ctx_total);
+                T x1[EC], x2[EC], y1[EC], y2[EC];
+                *reinterpret_cast<u32x4*>(x1) = k1[it];
+                *reinterpret_cast<u32x4*>(x2) = k2[it];
+#pragma unroll
+                for (int e = 0; e < EC; ++e) {
+                    float cs, sn;
+                    rope_cs(p.rt, c * EC + e, (aj >= 0 ? aj : 0) + k, cs, sn);
+                    const float f1 = to_f32(x1[e]), f2 = to_f32(x2[e]);
+                    y1[e] = from_f32<T>(f1 * cs - f2 * sn);
+                    y2[e] = from_f32<T>(f2 * cs + f1 * sn);
+                }
+                *reinterpret_cast<u32x4*>(Ks + TT::koff(jj * 32 + k, c * 16)) = *reinterpret_cast<u32x4*>(y1);
+                *reinterpret_cast<u32x4*>(Ks + TT::koff(jj * 32 + k, (c + HC) * 16)) = *reinterpret_cast<u32x4*>(y2);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int w = tid + 256 * it, row = w / TT::KCH, c = w - row * TT::KCH;
+            if (row < nrows) {
+                const int jj = row / bs, k = row - jj * bs;
+                T v[EC];
+                *reinterpret_cast<u32x4*>(v) = vv[it];
+#pragma unroll
+                for (int e = 0; e < EC; ++e) *reinterpret_cast<T*>(Vt + TT::voff(c * EC + e, jj * 32 + k)) = v[e];
+            }
         }
         __syncthreads();
         if (active && phase == 0 && a >= 0) attn_slice<T, D, QC, REDO>(Ks, Vt, j * 32, bs, qf, o, m, l, mt, lane);

@@ -225,8 +225,10 @@ dflash_status dflash_ctx_truncate(int64_t *lengths, const int64_t *keep, int32_t
  *   out            device [nb*bs, Hq*D]; rows with block_valid == 0 and all rows of
  *                  empty blocks are written as exact zeros.
  * Anchors and bases are clamped on the device so that base + a <= ctx_total.
- * Errors: INVALID_ARG for null pointers or nb < 0; WORKSPACE when workspace_bytes <
- * dflash_workspace_size(cfg, nb, 0).
+ * q, k_blk, v_blk, ctx_k and ctx_v are read with 16-byte accesses and must be
+ * 16-byte aligned.
+ * Errors: INVALID_ARG for null pointers, misaligned arrays or nb < 0; WORKSPACE when
+ * workspace_bytes < dflash_workspace_size(cfg, nb, 0).
  */
 dflash_status dflash_block_attn(const dflash_config *cfg, int32_t num_blocks, const void *q,
                                 const void *k_blk, const void *v_blk, const void *ctx_k,
