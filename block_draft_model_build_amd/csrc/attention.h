@@ -842,13 +842,19 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             const int k = c % bs, hh = c / bs;
             const int row = n * bs + k;
             const bool keep = p.valid[row] != 0;
-            const float inv = 1.f / l[qs];
+            const float inv = keep ? 1.f / l[qs] : 0.f;
             T* orow = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D;
+            // Accumulator elements 4i..4i+3 are 4 consecutive d: one 4-element store.
+            typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    orow[ds * 32 + acc_row(e, lane)] = from_f32<T>(keep ? o[ds][qs][e] * inv : 0.f);
+                for (int eg = 0; eg < 4; ++eg) {
+                    T4 v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = from_f32<T>(o[ds][qs][4 * eg + t] * inv);
+                    *reinterpret_cast<T4*>(orow + ds * 32 + acc_row(4 * eg, lane)) = v;
+                }
         }
     } else {
         const int64_t pi = ((int64_t)(p.item_start[gi] + s) * hkv + g) * kMaxGroup + j;
@@ -859,7 +865,12 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) po[ds * 32 + acc_row(e, lane)] = o[ds][qs][e];
+                for (int eg = 0; eg < 4; ++eg) {
+                    f32x4 v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = o[ds][qs][4 * eg + t];
+                    *reinterpret_cast<f32x4*>(po + ds * 32 + acc_row(4 * eg, lane)) = v;
+                }
             if (h == 0) {
                 p.part_ml[(pi * QC + c) * 2 + 0] = m[qs];
                 p.part_ml[(pi * QC + c) * 2 + 1] = l[qs];

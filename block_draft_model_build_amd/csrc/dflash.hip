@@ -499,7 +499,7 @@ extern "C" dflash_status dflash_block_attn(const dflash_config* cfg, int32_t num
     if (q == nullptr || k_blk == nullptr || v_blk == nullptr || block_ctx_base == nullptr ||
         block_anchor == nullptr || block_valid == nullptr || out == nullptr ||
         (ctx_total > 0 && (ctx_k == nullptr || ctx_v == nullptr)) || !aligned16(ctx_k) || !aligned16(ctx_v) ||
-        !aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk))
+        !aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out))
         return DFLASH_ERR_INVALID_ARG;
     if ((s = ws_check(cfg, num_blocks, 0, workspace, workspace_bytes)) != DFLASH_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);

@@ -225,8 +225,8 @@ dflash_status dflash_ctx_truncate(int64_t *lengths, const int64_t *keep, int32_t
  *   out            device [nb*bs, Hq*D]; rows with block_valid == 0 and all rows of
  *                  empty blocks are written as exact zeros.
  * Anchors and bases are clamped on the device so that base + a <= ctx_total.
- * q, k_blk, v_blk, ctx_k and ctx_v are read with 16-byte accesses and must be
- * 16-byte aligned.
+ * q, k_blk, v_blk, ctx_k and ctx_v are read, and out written, with vector
+ * accesses: all must be 16-byte aligned.
  * Errors: INVALID_ARG for null pointers, misaligned arrays or nb < 0; WORKSPACE when
  * workspace_bytes < dflash_workspace_size(cfg, nb, 0).
  */
