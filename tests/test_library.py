@@ -88,6 +88,12 @@ def test_rejects_bad_arguments_before_launch():
     misaligned = [ctypes.byref(cfg), 4, P(fake), P(fake), P(fake), P(fake + 2), P(fake), 100,
                   P(fake), P(fake), P(fake)]
     assert lib.dflash_block_attn(*misaligned, P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    # q, k_blk, v_blk (positions 2-4) and out are read and written with 16-byte accesses
+    for pos in (2, 3, 4):
+        bad = list(args)
+        bad[pos] = P(fake + 8)
+        assert lib.dflash_block_attn(*bad, P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_block_attn(*args, P(fake + 8), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
     # ctx projection: rows past the cache, bad strides
     lw = (d.DFlashLayerWeights * 1)()
     for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
