@@ -144,6 +144,26 @@ def test_bf16_scores_far_above_first_keys(scale):
     _run(w, bases, anchors, valid, 2 * S, seed=8, tweak=tweak)
 
 
+@pytest.mark.parametrize("scale", [None, 100.0, 300.0])
+def test_bf16_pipelined_tiles(scale):
+    # Groups of 4 and 3 blocks of one 3000-row sequence (64 query columns per
+    # block, one wave each): their prefixes are split into 256-key items, so
+    # whole tiles run software-pipelined, including the first tile of later
+    # splits (which sets the softmax reference), a group with an idle wave,
+    # partial tiles after whole ones, and a last tile that crosses the end of
+    # the caches (staged through registers after a pipelined tile). With a
+    # spike at context row 1000, inside whole tiles of both groups, scores rise
+    # 75 or 230 log2 units above the reference where no maximum is tracked, and
+    # the row-sum guard must send those items to the second run.
+    w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
+    S, bs = 3000, w.block_size
+    anchors = [2999, 2995, 2990, 2960, 1500, 1400, 1300]
+    valid = np.ones((len(anchors), bs), np.uint8)
+    valid[2, 11:] = 0
+    tweak = None if scale is None else _spikes(w, ctx_rows=[1000], own_rows=[], scale=scale)
+    _run(w, [0] * len(anchors), anchors, valid, S, seed=10, tweak=tweak)
+
+
 def test_fp32_scores_far_above_first_keys():
     w = WORKLOADS["c1"]
     anchors = [100, 127, 20, 64]
