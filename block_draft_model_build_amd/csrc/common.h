@@ -70,7 +70,9 @@ __device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 
 // Fraction-of-a-turn rotary frequencies, computed on the host in fp64:
 // turns[i] = rope_theta^(-2i/D) / (2*pi). The angle of pair i at position p is
 // 2*pi*frac(p * turns[i]); taking the fractional part in fp64 keeps the angle
-// exact to ~1e-12 rad at any position before the fp32 sin/cos.
+// exact to ~1e-12 rad at any position. The hardware sine and cosine
+// (v_sin_f32, v_cos_f32) take their argument in turns, so the reduced
+// fraction goes to them directly.
 struct RopeTurns {
     double turns[64];
 };
@@ -78,8 +80,9 @@ struct RopeTurns {
 __device__ __forceinline__ void rope_cs(const RopeTurns& rt, int i, int pos, float& c, float& s) {
     double t = (double)pos * rt.turns[i];
     t -= floor(t);
-    float r = (float)(2.0 * t);          // angle / pi in [0, 2)
-    sincospif(r, &s, &c);
+    const float f = (float)t;            // turns, in [0, 1]
+    s = __builtin_amdgcn_sinf(f);
+    c = __builtin_amdgcn_cosf(f);
 }
 
 }  // namespace dflash
