@@ -365,7 +365,6 @@ __device__ __forceinline__ void attn_tile_pipelined(const char* ks, const char* 
         for (int e = 0; e < 16; ++e) sc[qs][e] = init;
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) sc[qs] = Mfma<T>::mma(kf[kk], qf[qs][kk], sc[qs]);
-        asm volatile("" : "+v"(sc[qs]));      // the softmax reads them: VGPRs
     };
     auto pv = [&](int qs) {
 #pragma unroll
