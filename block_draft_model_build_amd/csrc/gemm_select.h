@@ -25,6 +25,10 @@ using MidDeep = TileCfg<128, 128, 4, 1, 128, 4>;
 // not depend on 128-column waves. 4096-row QKV product (6144 columns): 384 big
 // tiles in 1.5 rounds -> 512 tiles in 2 rounds, 1.06 -> 0.92 ms per step.
 using WideTile = TileCfg<256, 192, 4, 2, 128, 2>;
+// The same deep 128x128 tiles with 8 waves (32x64 each: two waves per SIMD hide
+// each other's fragment-read latency) for plain-store and residual epilogues
+// (1024-row o_proj and down: 1.02 -> 0.94 ms per inference step).
+using MidDeep8 = TileCfg<128, 128, 4, 2, 128, 4>;
 // 128x192 tiles with 128-byte slabs in 4 stages (160 KB of LDS) when they make
 // at most one tile per compute unit where the 128x128 grid makes more (1024-row
 // QKV product: 384 -> 256 tiles, 0.43 -> 0.31 ms per inference step).
@@ -54,6 +58,9 @@ static hipError_t gemm(int kid, int M, int N, int K, const AL& al, const BL& bl,
         const int t192 = ((M + 127) / 128) * (N / 192);
         if (N % 192 == 0 && mid_tiles > 256 && t192 <= 256)
             return launch_gemm<T, MidWideDeep>(M, N, K, al, bl, ep, st, group);
+    }
+    if constexpr (AnyWaveWidth<EP>::value) {
+        if (mid_tiles <= 256) return launch_gemm<T, MidDeep8>(M, N, K, al, bl, ep, st, group);
     }
     if (mid_tiles <= 256) return launch_gemm<T, MidDeep>(M, N, K, al, bl, ep, st, group);
     return launch_gemm<T, MidTile>(M, N, K, al, bl, ep, st, group);
