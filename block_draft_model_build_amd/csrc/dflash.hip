@@ -16,7 +16,9 @@ namespace dflash {
 // out[row] = x / sqrt(mean(x^2) + eps) * w, x read as fp32; optionally copies
 // x into the fp32 residual stream (first layer: embeddings -> h). 16-byte
 // loads; rows of up to 256 * 4 vectors stay in registers between the sum and
-// the scaling (H = 4096 in fp32), longer rows are read twice.
+// the scaling (H = 4096 in fp32), together with their weights, which are read
+// before the reduction so that a row costs one memory round trip; longer rows
+// are read twice.
 template <typename TIN, typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in, float* __restrict__ hcopy,
                                                       const T* __restrict__ w, T* __restrict__ out, int H,
@@ -25,18 +27,27 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in
     constexpr int NV = 4;                         // vectors per thread kept in registers
     typedef TIN vin __attribute__((ext_vector_type(VI)));
     typedef T vout __attribute__((ext_vector_type(VI)));
+    typedef float vf32 __attribute__((ext_vector_type(VI)));
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const TIN* x = in + row * H;
     const int nvec = H / VI;
     const bool cached = nvec <= 256 * NV;
     vin v[NV];
+    vout wv[NV];
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         const int j = threadIdx.x + 256 * k;
         if (j < nvec) {
             v[k] = reinterpret_cast<const vin*>(x)[j];
+            wv[k] = reinterpret_cast<const vout*>(w)[j];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int j = threadIdx.x + 256 * k;
+        if (j < nvec) {
 #pragma unroll
             for (int q = 0; q < VI; ++q) ss += to_f32(v[k][q]) * to_f32(v[k][q]);
         }
@@ -52,23 +63,26 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in
     __syncthreads();
     const float tot = red[0] + red[1] + red[2] + red[3];
     const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    auto emit = [&](int j, const vin& u) {
+    auto emit = [&](int j, const vin& u, const vout& ww) {
         vout o;
+        vf32 hc;
 #pragma unroll
         for (int q = 0; q < VI; ++q) {
             const float f = to_f32(u[q]);
-            o[q] = from_f32<T>(f * r * to_f32(w[j * VI + q]));
-            if (hcopy) hcopy[row * H + j * VI + q] = f;
+            o[q] = from_f32<T>(f * r * to_f32(ww[q]));
+            hc[q] = f;
         }
+        if (hcopy) reinterpret_cast<vf32*>(hcopy + row * H)[j] = hc;
         reinterpret_cast<vout*>(out + row * H)[j] = o;
     };
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         const int j = threadIdx.x + 256 * k;
-        if (j < nvec) emit(j, v[k]);
+        if (j < nvec) emit(j, v[k], wv[k]);
     }
     if (!cached)
-        for (int j = threadIdx.x + 256 * NV; j < nvec; j += 256) emit(j, reinterpret_cast<const vin*>(x)[j]);
+        for (int j = threadIdx.x + 256 * NV; j < nvec; j += 256)
+            emit(j, reinterpret_cast<const vin*>(x)[j], reinterpret_cast<const vout*>(w)[j]);
 }
 
 // ------------------------------------------------------------------ attention launch
@@ -540,7 +554,8 @@ extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t n
     if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2) return DFLASH_ERR_UNSUPPORTED;
     if (num_blocks == 0) return DFLASH_OK;
     if (block_embeds == nullptr || layers == nullptr || ctx_k == nullptr || ctx_v == nullptr ||
-        block_ctx_base == nullptr || block_anchor == nullptr || block_valid == nullptr || out == nullptr)
+        block_ctx_base == nullptr || block_anchor == nullptr || block_valid == nullptr || out == nullptr ||
+        !aligned16(block_embeds))
         return DFLASH_ERR_INVALID_ARG;
     for (int l = 0; l < cfg->num_layers; ++l) {
         const dflash_layer_weights& L = layers[l];

@@ -257,7 +257,10 @@ dflash_status dflash_block_attn(const dflash_config *cfg, int32_t num_blocks, co
  *   ctx_k, ctx_v   host arrays [num_layers] of device caches in dflash_ctx_proj's
  *                  layouts (K [Hkv][ctx_total][D], V [Hkv][D][ctx_total])
  *   out            device [nb*bs, H]
- * Errors: as dflash_block_attn; WORKSPACE below dflash_workspace_size(cfg, nb, 0).
+ * block_embeds, every layer weight and the caches are read with 16-byte
+ * accesses and must be 16-byte aligned.
+ * Errors: INVALID_ARG for null pointers, misaligned arrays or nb < 0; WORKSPACE
+ * below dflash_workspace_size(cfg, nb, 0).
  */
 dflash_status dflash_body_forward(const dflash_config *cfg, int32_t num_blocks,
                                   const void *block_embeds, const dflash_layer_weights *layers,
