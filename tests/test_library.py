@@ -166,10 +166,14 @@ def test_rejects_bad_arguments_before_launch():
     assert lib.dflash_ctx_proj_backward(ctypes.byref(odd), P(fake), 5 * 4032, 4032, 10, P(fake), lw, G, G, 50, 0,
                                         P(fake), None, P(fake), 1 << 40, None) == d.DFLASH_ERR_UNSUPPORTED
     assert d.dflash_ctx_proj_backward_workspace_size(cfg, 100) > d.dflash_ctx_proj_backward_workspace_size(cfg, 10)
-    # body: a null weight
+    # body: misaligned embeddings (16-byte reads), a null weight
+    w_up = lw[0].w_up
+    assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake + 8), lw, ptrs, ptrs, 100, P(fake),
+                                   P(fake), P(fake), P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
     lw[0].w_up = None
     assert lib.dflash_body_forward(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
                                    P(fake), P(fake), P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    lw[0].w_up = w_up
     # unsupported config is reported before anything else
     bad = d.config_from_workload(scaled(WORKLOADS["c2"], head_dim=64))
     assert lib.dflash_body_forward(ctypes.byref(bad), 4, P(fake), lw, ptrs, ptrs, 100, P(fake),
