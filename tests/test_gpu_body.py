@@ -151,6 +151,36 @@ def test_ragged_cache_body_sampled():
         compare(out[r * bs:(r + 1) * bs], ref, tol_for(w), f"request {r} (prefix {lens[r]})")
 
 
+
+@pytest.mark.parametrize("batch", [7, 45, 170])
+def test_full_width_ragged_rows(batch):
+    # One full-width layer (hidden 4096, 32/8 heads, intermediate 12288) over
+    # 112, 720 and 2720 block rows: row counts that end inside a tile of every
+    # GEMM shape the body picks at this width (128x128 with 8 waves, 128x192,
+    # 256x192, 256x256 and plain 128x128), so the last request's rows sit in a
+    # ragged tail of each product.
+    w = scaled(WORKLOADS["c5"], batch=batch, num_layers=1, min_prefix=1, max_prefix=600, seed=2000 + batch)
+    inp = make_inference_inputs(w, "cuda")
+    cfg = d.config_from_workload(w)
+    out = torch.full((w.num_blocks * w.block_size, w.hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = workspace(d, cfg, w.num_blocks, 0, "cuda")
+    d.dflash_body_forward(cfg, w.num_blocks, inp["emb"], inp["layers"], inp["ctx_k"], inp["ctx_v"],
+                          inp["total"], inp["block_ctx_base"], inp["block_anchor"], inp["block_valid"],
+                          out, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    lens = inp["lengths"].cpu().numpy()
+    offs = inp["offsets"].cpu().numpy()
+    layers = layers64(inp["layers"])
+    bs = w.block_size
+    for r in sorted({0, int(np.argmax(lens)), batch - 2, batch - 1}):
+        lo, hi = int(offs[r]), int(offs[r + 1])
+        ck = [np64(k[:, lo:hi]) for k in inp["ctx_k"]]
+        cv = [np64(v[:, :, lo:hi]).transpose(0, 2, 1) for v in inp["ctx_v"]]
+        ref = oracle.body_forward(np64(inp["emb"][r * bs:(r + 1) * bs]), layers, ck, cv, [0],
+                                  [int(lens[r])], np.ones(bs, np.uint8), oracle_cfg(w))
+        compare(out[r * bs:(r + 1) * bs], ref, tol_for(w), f"{batch} requests: request {r} (prefix {lens[r]})")
+
 def test_body_invariants_bit_exact():
     w = SMALL_BF16
     inp = make_training_inputs(w, "cuda", plan_seed=5)
