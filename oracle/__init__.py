@@ -16,9 +16,10 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   build_plan             pinned by invariants the pages fix (determinism, equal
                          sample id -> equal anchors, anchors from valid windows,
                          loss mask excludes the anchor and invalid positions) and
-                         by brute-force top-N selection; the exact SplitMix64
-                         constants are "parity unpinned" (the pages print no
-                         known-answer vector).
+                         by brute-force top-N selection; SplitMix64's increment
+                         is pinned by its golden-ratio definition, its
+                         finaliser's shifts and multipliers are "parity
+                         unpinned" (the pages print no known-answer vector).
   rms_norm, silu, rope   pinned by closed forms and identities.
   block_attention        pinned by the brute-force dense-mask attention and by
                          closed-form special cases.

@@ -1,8 +1,10 @@
 """Pins of the plan oracle against what the pages fix (NeMo RL "DFlash Draft
 Body", How It Works, steps 1, 2 and 4) and against brute force. The exact
-SplitMix64 constants are parity unpinned: the pages print no known-answer
-vector; here the mixer is pinned only as a bijection with full avalanche."""
+SplitMix64 finaliser constants are parity unpinned: the pages print no
+known-answer vector; the finaliser is pinned only as a bijection with full
+avalanche, and the increment by its definition from the golden ratio."""
 import random
+from math import isqrt
 
 import numpy as np
 import pytest
@@ -50,6 +52,22 @@ def test_mixer_avalanche():
     mean = sum(flips) / len(flips)
     assert 31.0 < mean < 33.0
     assert min(flips) >= 8
+
+
+def test_mixer_increment_is_the_golden_gamma():
+    # SplitMix64's increment is the odd integer nearest 2^64 / phi (phi the golden
+    # ratio), derived here with exact integer square roots. The xor-shift-multiply
+    # finaliser is a bijection that maps 0 to 0, so the oracle's output is 0 for
+    # exactly one state: the negated increment.
+    S = isqrt(5 << 256)                          # floor(sqrt(5) * 2^128)
+    num = S - (1 << 128)                         # 2^64 / phi = (sqrt(5) - 1) / 2 * 2^64 = num / 2^65
+    lo = num >> 65
+    frac2 = num - (lo << 65)                     # fractional part, times 2^65
+    cands = [c for c in (lo - 1, lo, lo + 1, lo + 2) if c & 1]
+    gamma = min(cands, key=lambda c: abs((c << 65) - num))
+    assert lo < gamma + 2 and 0 < frac2
+    assert splitmix64((-gamma) & MASK64) == 0
+    assert splitmix64((-gamma + 1) & MASK64) != 0 and splitmix64((-gamma - 1) & MASK64) != 0
 
 
 def _rand_mask(rng, B, S, p_one):
