@@ -44,13 +44,16 @@ DISPATCHES_PER_CALL = {"attention": 2}
 
 
 def _strip_comments(text: str) -> str:
+    """The code without comments or whitespace: editing a comment or the layout
+    leaves the hash unchanged."""
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "".join(text.split())
 
 
 def source_hash() -> str:
     """Hash of the sources the measured forward kernels are built from, with
-    comments removed: the translation unit that instantiates them (dflash.hip),
+    comments and whitespace removed: the translation unit that instantiates them (dflash.hip),
     every header, and the public header. The other translation units (plan,
     verification, backward, profiling hook) cannot change these kernels' code."""
     h = hashlib.sha256()

@@ -9,7 +9,11 @@
 // K/V byte fetched once serves every query head of the group.
 //
 // Keys are the prefix rows [s*chunk, min(a, (s+1)*chunk)) of the projected
-// context plus, for split 0, the block's own bs rows.
+// context plus, for split 0, the block's own bs rows. A single-block group (bf16)
+// split nsplit ways gives split s the 128-key tiles s, s + nsplit, ... of its
+// prefix instead: its items run side by side and read neighbouring 256-byte
+// pieces of each V^T row at about the same time (the transposed cache's rows are
+// a whole context apart).
 //
 // Math layout (keys on MFMA rows, queries on MFMA columns):
 //   S^T[key, q] = K[key, :] . Q[q, :]        A = K rows from LDS, B = Q in registers
@@ -446,6 +450,13 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     const int a = active ? anchor_eff(p.anchor[n], base, p.ctx_total) : -1;
     const int kend_g = min(amax, kbeg + chunk);
     const int kend = min(a, kbeg + chunk);
+    // Single-block groups split over several items take interleaved tiles
+    // (split s of nsplit: tiles s, s + nsplit, ...), so the items of one group,
+    // dispatched together, read neighbouring pieces of the V^T rows together.
+    const bool ilv = TT::SWZ && ng == 1 && nsplit > 1;
+    const int tfirst = ilv ? s * SUPER : kbeg, tstep = ilv ? nsplit * SUPER : SUPER;
+    const int kclamp = ilv ? amax : kend_g;       // end of the keys this item may read
+    const int kvalid = ilv ? a : kend;            // end of this wave's block's visible keys
 
     // ---- queries of this wave's block: rotate at a + k, scale by log2(e)/sqrt(D)
     frag qf[QS][DK];
@@ -513,20 +524,21 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
 
     // ---- context rows of the group: K rows and V^T columns [kbeg, kend_g) of the
     // sequence's range of the caches, in 128-key super-tiles through 2 LDS stages.
-    const int ntile = kend_g > kbeg ? (kend_g - kbeg + SUPER - 1) / SUPER : 0;
+    const int ntile = ilv ? (amax > tfirst ? (amax - tfirst + tstep - 1) / tstep : 0)
+                          : (kend_g > kbeg ? (kend_g - kbeg + SUPER - 1) / SUPER : 0);
     const T* ckg = p.ck + ((int64_t)g * p.ctx_total + base) * D;
     const T* cvg = p.cvt + (int64_t)g * D * p.ctx_total + base;
     const int64_t lim = p.ctx_total - base;          // keys of this range present in the caches
     u32x4 rk[TT::KLD], rv[TT::VLD];
     // Register path: K rows past the group's end repeat its last row, V^T keys
-    // past it are zero, so nothing outside [0, kend_g) is read.
+    // past it are zero, so nothing outside [0, kclamp) is read.
     auto gload = [&](int t0) {
         // K: chunk c = tid + 256 i -> key c / 16, 16-byte column c % 16
 #pragma unroll
         for (int i = 0; i < TT::KLD; ++i) {
             const int c = tid + 256 * i;
             int key = t0 + c / TT::KCH;
-            key = key < kend_g ? key : kend_g - 1;
+            key = key < kclamp ? key : kclamp - 1;
             rk[i] = *reinterpret_cast<const u32x4*>(ckg + (int64_t)key * D + (c % TT::KCH) * EC);
         }
         // V^T: chunk c -> row d = c / VCH, keys t0 + (c % VCH) * EC ..
@@ -536,12 +548,12 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             const int d = c / TT::VCH;
             const int key = t0 + (c % TT::VCH) * EC;
             const T* src = cvg + (int64_t)d * p.ctx_total + key;
-            if (key + EC <= kend_g) {
+            if (key + EC <= kclamp) {
                 rv[i] = *reinterpret_cast<const u32x4*>(src);
             } else {
                 T tmp[EC];
 #pragma unroll
-                for (int e = 0; e < EC; ++e) tmp[e] = key + e < kend_g ? src[e] : from_f32<T>(0.f);
+                for (int e = 0; e < EC; ++e) tmp[e] = key + e < kclamp ? src[e] : from_f32<T>(0.f);
                 rv[i] = *reinterpret_cast<const u32x4*>(tmp);
             }
         }
@@ -603,7 +615,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // (they use stage 1); fp32 stages its tiles from registers below.
     constexpr int OWN = TT::SWZ ? 1 : 0;
     if constexpr (TT::SWZ) {
-        if (ntile > 0 && tile_dma_ok(kbeg)) issue_dma(kbeg, 0);
+        if (ntile > 0 && tile_dma_ok(tfirst)) issue_dma(tfirst, 0);
     }
 
     // ---- split 0: the blocks' own keys. Block jj's rows go to slot jj (32 rows)
@@ -686,7 +698,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             const char* Ks = TT::kstage(smem, t & 1);
             const char* Vt = TT::vstage(smem, t & 1);
             for (int sl = phase; sl < SUPER / 32; sl += wpb) {
-                const int nvalid = kend - (kbeg + t * SUPER + sl * 32);
+                const int nvalid = kvalid - (tfirst + t * tstep + sl * 32);
                 if (nvalid > 0)
                     attn_slice<T, D, QC, REDO>(Ks, Vt, sl * 32, nvalid < 32 ? nvalid : 32, qf, o, m, l, mt, lane);
             }
@@ -696,8 +708,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         // Tile t + 1 is staged into the other stage while tile t is computed:
         // by DMA when it lies inside the cache range, else (a tile crossing the
         // end of the caches) through registers after this tile's work.
-        if (ntile > 0 && !tile_dma_ok(kbeg)) {
-            gload(kbeg);
+        if (ntile > 0 && !tile_dma_ok(tfirst)) {
+            gload(tfirst);
             lstore(0);
         }
         wait_vmcnt<0>();
@@ -715,7 +727,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             }
         }
         auto stage_next = [&](int t, auto&& compute) {
-            const int t1 = kbeg + (t + 1) * SUPER;
+            const int t1 = tfirst + (t + 1) * tstep;
             const bool next = t + 1 < ntile;
             const bool dma = next && tile_dma_ok(t1);
             if (dma) issue_dma(t1, (t + 1) & 1);

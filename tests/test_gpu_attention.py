@@ -77,11 +77,13 @@ def test_bf16_ragged(hq, hkv):
 
 
 def test_bf16_split_prefixes():
-    # Few blocks with long prefixes: each prefix is split over several work items
-    # and merged by the combine step.
+    # Few blocks with long prefixes, each a group of its own: each prefix is split
+    # over several work items that take interleaved 128-key tiles, merged by the
+    # combine step. The last block's prefix ends 1 row before the end of the
+    # caches, so one split's last tile is staged through registers.
     w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
     S = 6000
-    _run(w, [0, S, 0], [5999, 3001, 700], np.ones((3, 16), np.uint8), 2 * S, seed=4)
+    _run(w, [0, S, 0, S], [5999, 3001, 700, 5999], np.ones((4, 16), np.uint8), 2 * S, seed=4)
 
 
 def test_ragged_cache_requests():
