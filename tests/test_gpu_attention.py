@@ -174,14 +174,19 @@ def test_fp32_scores_far_above_first_keys():
          tweak=_spikes(w, ctx_rows=[40, 90], own_rows=[2 * w.block_size + 1], scale=300.0))
 
 
-def test_deterministic_and_information_boundary():
+@pytest.mark.parametrize("layout", ["two-block groups", "single-block groups"])
+def test_deterministic_and_information_boundary(layout):
+    # Two-block groups share their tiles; with the sequences alternating, every
+    # block is a group of its own and its prefix is split into items that take
+    # interleaved tiles.
     w = scaled(WORKLOADS["c2"], num_q_heads=8, num_kv_heads=2, hidden=1024)
     dev = "cuda"
     cfg = d.config_from_workload(w)
     S, nb, bs = 3000, 4, 16
     rng = Rng(7, dev)
     q, k, v, ck, cv = random_attention_inputs(rng, nb, bs, 8, 2, 128, 2 * S, torch.bfloat16)
-    bases = torch.tensor([0, 0, S, S], dtype=torch.int64, device=dev)
+    order = [0, 0, S, S] if layout == "two-block groups" else [0, S, 0, S]
+    bases = torch.tensor(order, dtype=torch.int64, device=dev)
     anchors = torch.tensor([1500, 2999, 700, 2500], dtype=torch.int32, device=dev)
     valid = torch.ones(nb * bs, dtype=torch.uint8, device=dev)
     ws = workspace(d, cfg, nb, 0, dev)
