@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dma_limits.h"
 
 namespace dflash {
 
@@ -577,11 +578,15 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // lands at physical chunk i % 16 of row i / 16, so it fetches the logical
     // chunk (i % 16) ^ (row & 15). Keys past the group's end are read as they
     // are: scores there are masked and V there is zeroed before use.
-    auto tile_dma_ok = [&](int t0) { return TT::SWZ && (int64_t)t0 + SUPER <= lim && p.ctx_total < (1 << 28); };
+    auto tile_dma_ok = [&](int t0) {
+        return TT::SWZ && (int64_t)t0 + SUPER <= lim && p.ctx_total <= vt_dma_max_ctx(EB, TT::EC);
+    };
     // Sources are a wave-uniform base plus a 32-bit lane offset; the swizzle
     // (row & 15) repeats every 4 instructions, so 4 lane offsets serve all 8
-    // rows of each cache (the V^T offsets stay below 2^32 bytes because
-    // tile_dma_ok limits ctx_total).
+    // rows of each cache. The largest V^T lane offset, (15 * ctx_total +
+    // 15 * EC) * EB bytes, fits in 32 bits only up to vt_dma_max_ctx rows
+    // (143,165,568 for bf16); tile_dma_ok sends longer caches down the
+    // register-staged path, so no offset below wraps.
     const int rsub = lane >> 4, pc = lane & 15;
     uint32_t koff_l[4], voff_l[4];
 #pragma unroll

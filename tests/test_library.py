@@ -187,3 +187,31 @@ def test_product_path_does_not_reach_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_vt_dma_offset_limit(tmp_path):
+    # The attention kernel's direct-to-LDS V^T loads form a 32-bit lane offset
+    # (15 * ctx_total + 15 * elems_per_chunk) * elem_bytes; the helper's limit
+    # must be the largest cache length for which that offset still fits.
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++") or shutil.which("c++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "lim.cpp"
+    src.write_text('#include <stdio.h>\n#include "dma_limits.h"\n'
+                   'int main() { printf("%lld %lld\\n", (long long)dflash::vt_dma_max_ctx(2, 8),'
+                   ' (long long)dflash::vt_dma_max_ctx(4, 4)); return 0; }\n')
+    exe = tmp_path / "lim"
+    subprocess.run([gxx, "-std=c++17", "-I", os.path.join(ROOT, "block_draft_model_build_amd", "csrc"),
+                    str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    for lim, (eb, ec) in zip(got, ((2, 8), (4, 4))):
+        off = lambda t: (15 * t + 15 * ec) * eb            # largest lane offset, in bytes
+        assert off(lim) <= 2**32 - 1 < off(lim + 1)
+    assert got[0] == 143_165_568
+    # The kernel's guard uses the helper (and no other bound on ctx_total).
+    att = open(os.path.join(ROOT, "block_draft_model_build_amd", "csrc", "attention.h")).read()
+    guard = re.search(r"auto tile_dma_ok = \[&\]\(int t0\) \{(.*?)\};", att, flags=re.S).group(1)
+    assert "vt_dma_max_ctx(EB, TT::EC)" in guard and "1 << 28" not in guard
