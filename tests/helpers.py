@@ -101,26 +101,39 @@ class TrainingRun:
         return self
 
 
+def oracle_row_context(w: Workload, inputs, b: int, rows: int, layers=None):
+    """Oracle context K/V (per layer, [Hkv, rows, D], K rotated) of the first
+    `rows` positions of training sequence b, projected from the target states."""
+    S = w.seq_len
+    layers = layers64(inputs["layers"]) if layers is None else layers
+    rows = max(int(rows), 1)
+    states = np64(inputs["states"][:, b * S: b * S + rows])
+    C = oracle.ctx_proj(oracle.concat_target_states(states), np64(inputs["w_proj"]))
+    del states
+    return oracle.ctx_kv(C, layers, np.arange(rows), w.num_kv_heads, w.head_dim, w.rope_theta)
+
+
 def oracle_training_blocks(w: Workload, inputs, anchors: np.ndarray, valid: np.ndarray,
-                           blocks: Sequence[int]) -> np.ndarray:
+                           blocks: Sequence[int], contexts: Optional[Dict[int, tuple]] = None,
+                           layers=None) -> np.ndarray:
     """Oracle body outputs [len(blocks)*bs, H] for the chosen blocks of a
     training-shaped workload. Only the context rows each block can read are
-    projected (rows [0, max anchor) of the rows involved)."""
-    bs, N, S = w.block_size, w.anchors_per_row, w.seq_len
-    layers = layers64(inputs["layers"])
-    w_proj = np64(inputs["w_proj"])
+    projected (rows [0, max anchor) of the rows involved), unless `contexts`
+    already holds sequence b's oracle context K/V (from oracle_row_context)
+    covering those rows."""
+    bs, N = w.block_size, w.anchors_per_row
+    layers = layers64(inputs["layers"]) if layers is None else layers
     emb = inputs["emb"]
-    outs = []
     by_row: Dict[int, List[int]] = {}
     for n in blocks:
         by_row.setdefault(n // N, []).append(n)
     result = {}
     for b, ns in by_row.items():
         amax = max(int(anchors.reshape(-1)[n]) for n in ns)
-        rows = max(amax, 1)
-        states = np64(inputs["states"][:, b * S: b * S + rows])
-        C = oracle.ctx_proj(oracle.concat_target_states(states), w_proj)
-        ck, cv = oracle.ctx_kv(C, layers, np.arange(rows), w.num_kv_heads, w.head_dim, w.rope_theta)
+        if contexts is not None and b in contexts and contexts[b][0][0].shape[1] >= amax:
+            ck, cv = contexts[b]
+        else:
+            ck, cv = oracle_row_context(w, inputs, b, amax, layers)
         e = np.concatenate([np64(emb[n * bs:(n + 1) * bs]) for n in ns])
         a = np.array([int(anchors.reshape(-1)[n]) for n in ns])
         v = np.concatenate([valid.reshape(-1)[n * bs:(n + 1) * bs] for n in ns])

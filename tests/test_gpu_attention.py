@@ -208,3 +208,22 @@ def test_deterministic_and_information_boundary(layout):
     v2[bs:] = float("nan")
     out = run(q, k2, v2, ck2, cv2)
     assert torch.equal(out[:bs], ref[:bs])
+
+
+@pytest.mark.parametrize("bs,hq,hkv", [(1, 32, 8), (1, 8, 8), (32, 8, 4), (32, 4, 4), (4, 16, 2)])
+def test_bf16_block_sizes(bs, hq, hkv):
+    # The block size is a parameter (one anchor plus gamma draft positions;
+    # NeMo RL "DFlash Draft Body", How It Works, step 2). Block size 1 is the
+    # causal special case: each block is one query attending to its prefix and
+    # itself. Block size 32 fills the 64 query columns with two query heads per
+    # KV head (or one). Groups of several blocks of one sequence (shared tiles,
+    # pipelined when they run whole), single-block groups whose prefixes are
+    # split, anchors at 0, at tile edges and at the end of a sequence.
+    w = scaled(WORKLOADS["c2"], num_q_heads=hq, num_kv_heads=hkv, hidden=hq * 128, block_size=bs)
+    S = 3000
+    anchors = [0, 1, 127, 128, 129, 1000, 2999, 2500, 2501, 2502, 300, 1777, 2990, 2991]
+    bases = [0, 0, 0, 0, 0, 0, 0, S, S, S, 0, S, 0, 0]
+    valid = np.ones((len(anchors), bs), np.uint8)
+    if bs > 1:
+        valid[6, bs // 2:] = 0
+    _run(w, bases, anchors, valid, 2 * S, seed=11 + bs)
