@@ -12,7 +12,12 @@ the step time, timed live with HIP events recorded by the library around each
 of its launches on the launch stream; the cpu_baseline object is the fp64
 oracle timed on this host on a bounded sample of the same workload.
 
-    python bench.py [--workload c3] [--steps 10] [--warmup 3] [--gpus 1]
+    python bench.py [--workload c3] [--steps 20] [--warmup 5] [--gpus 1]
+
+The JSON line also carries `configs`: the one-layer, 5-layer, long-context and
+ragged-cache workloads each timed the same way (step time with median, p10 and
+p90 over per-step events, the step's roofline and MFMA fractions, the dominant
+kernel's fraction), so every workload's bar is on record in one run.
 """
 from __future__ import annotations
 
@@ -394,26 +399,135 @@ def cpu_baseline(w, runner, anchors, budget_rows=None, budget_blocks=None):
         t_est = t_ctx * T / rows + t_body * w.num_blocks / nblk
         sample["what"] = (f"context projection of {rows} of {T} target rows + body of {nblk} of {w.num_blocks} "
                           f"blocks (anchors {sorted(int(anchors[n]) for n in pick)}), scaled to the whole step")
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max([p.get("num_threads", 1) for p in libs] or [1])
+        if libs:
+            blas = ", ".join(f"{p.get('internal_api', '?')} {p.get('version', '?')}" for p in libs)
     except Exception:  # noqa: BLE001
         cores = len(os.sched_getaffinity(0))
     value = w.num_blocks * bs / t_est
     return {"value": round(value, 3), "unit": "block-positions/s", "cores": int(cores), "kind": "oracle",
+            "blas": blas, "numpy": np.__version__, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": sample["what"], "sample_seconds": round(t_ctx + t_body, 2)}
+
+
+# ----------------------------------------------------------------------------- timing
+def _pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def measure(d, torch, w, steps, warmup, breakdown=True):
+    """Build one workload's inputs, warm up, then time `steps` steps: HIP events
+    around the whole loop (the step time the driver checks) and around each step
+    (median, p10, p90), with the dominant kernel's launches timed by the
+    library's own events over the same region. Returns the figures and the runner."""
+    runner = Runner(d, w)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    anchors = runner.anchors_np()
+    counts = kernel_counts(w, anchors, runner.bases_np())
+
+    # Per-kernel time shares: each kernel in turn, over a couple of steps.
+    per_kernel = {}
+    if breakdown:
+        for name in counts:
+            launches = counts[name]["launches"]
+            reps = 2
+            d.dflash_profile_start(name, launches * reps)
+            for _ in range(reps):
+                runner.step()
+            times = d.dflash_profile_stop(launches * reps)
+            if times:
+                per_kernel[name] = sum(times) / reps
+        dominant = max(per_kernel, key=per_kernel.get)
+    else:
+        dominant = "ctx_proj" if not w.inference else "attention"
+
+    n_dom = counts[dominant]["launches"] * steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    d.dflash_profile_start(dominant, n_dom)
+    ev[0].record()
+    for i in range(steps):
+        runner.step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    dom_times = d.dflash_profile_stop(n_dom)
+    dom_avg = sum(dom_times) / len(dom_times)
+
+    positions = w.num_blocks * w.block_size
+    roof = roofline_entry(dominant, counts[dominant], dom_avg, w.dtype)
+    t_roof = step_roofline_ms(counts, w.dtype)
+    flops = sum(c["flops"] * c["launches"] for c in counts.values())
+    med = _pct(per_step, 50)
+    res = {
+        "ms_per_step": ms, "ms_median": med, "ms_p10": _pct(per_step, 10), "ms_p90": _pct(per_step, 90),
+        "value": positions / (ms / 1e3), "positions": positions, "dominant": dominant, "dom_avg_ms": dom_avg,
+        "dom_launches": len(dom_times), "roofline": roof, "roofline_ms": t_roof, "flops": flops,
+        "counts": counts, "per_kernel": per_kernel, "anchors": anchors,
+    }
+    return res, runner
+
+
+def long_context_views(w, res):
+    """Three labelled figures for the long-context workload. (i) The per-block
+    prefix-stream model: every block streams its own prefix of context K and V
+    from HBM in every layer (the bytes a kernel without shared tiles would
+    move), as a fraction of HBM peak over the step and over attention alone;
+    (ii) the algorithmic MFMA fraction of the step; (iii) the attention kernel's
+    measured DRAM traffic rate, from the committed rocprofv3 counter file when
+    it matches the current sources."""
+    import numpy as np
+    a = np.asarray(res["anchors"], np.int64)
+    eb = 2 if w.dtype == "bf16" else 4
+    stream = float(a[a >= 0].sum()) * w.num_kv_heads * 2 * w.head_dim * eb * w.num_layers
+    att_ms = res["per_kernel"].get("attention")
+    views = {
+        "per_block_stream_bytes": stream,
+        "per_block_stream_hbm_frac_step": round(stream / (PEAK_HBM_GBS * 1e9) / (res["ms_per_step"] / 1e3), 4),
+        "algorithmic_mfma_frac_step": round(res["flops"] / (PEAK_MFMA_TFLOPS[w.dtype] * 1e12)
+                                            / (res["ms_per_step"] / 1e3), 4),
+    }
+    if att_ms:
+        views["per_block_stream_hbm_frac_attention"] = round(
+            stream / (PEAK_HBM_GBS * 1e9) / (att_ms / 1e3), 4)
+    return views
+
+
+def config_summary(w, res):
+    out = {"workload": w.name, "ms_per_step": round(res["ms_per_step"], 4),
+           "ms_median": round(res["ms_median"], 4), "ms_p10": round(res["ms_p10"], 4),
+           "ms_p90": round(res["ms_p90"], 4), "block_positions_per_s": round(res["value"], 1),
+           "step_roofline_frac": round(res["roofline_ms"] / res["ms_per_step"], 4),
+           "step_mfma_frac": round(res["flops"] / (PEAK_MFMA_TFLOPS[w.dtype] * 1e12)
+                                   / (res["ms_per_step"] / 1e3), 4),
+           "dominant_kernel": res["dominant"], "dominant_frac": res["roofline"]["frac"],
+           "dominant_bound": res["roofline"]["bound"],
+           "kernel_ms_per_step": {k: round(v, 4) for k, v in res["per_kernel"].items()}}
+    if w.name == "c4":
+        out["long_context_views"] = long_context_views(w, res)
+    return out
 
 
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the steps next to the path")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' summaries")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}).",
@@ -430,75 +544,62 @@ def main():
     torch.cuda.set_device(0)
     w = WORKLOADS[args.workload]
     log(f"workload {w.name}: building inputs")
-    runner = Runner(d, w)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        runner.step()
-    torch.cuda.synchronize()
-    anchors = runner.anchors_np()
-    counts = kernel_counts(w, anchors, runner.bases_np())
-    log(f"warmup done ({args.warmup} steps)")
+    res, runner = measure(d, torch, w, args.steps, args.warmup, breakdown=not args.no_breakdown)
+    ms = res["ms_per_step"]
+    log("kernel ms/step: " + ", ".join(f"{k} {v:.3f}" for k, v in res["per_kernel"].items()))
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {res['ms_median']:.3f}, p10 {res['ms_p10']:.3f}, "
+        f"p90 {res['ms_p90']:.3f}); {res['dominant']} avg {res['dom_avg_ms']:.4f} ms over "
+        f"{res['dom_launches']} launches")
 
-    # Per-kernel time shares: each kernel in turn, over a couple of steps.
-    per_kernel = {}
-    if not args.no_breakdown:
-        for name in counts:
-            launches = counts[name]["launches"]
-            reps = 2
-            d.dflash_profile_start(name, launches * reps)
-            for _ in range(reps):
-                runner.step()
-            times = d.dflash_profile_stop(launches * reps)
-            if times:
-                per_kernel[name] = sum(times) / reps
-        dominant = max(per_kernel, key=per_kernel.get)
-    else:
-        dominant = "ctx_proj" if not w.inference else "attention"
-    log("kernel ms/step: " + ", ".join(f"{k} {v:.3f}" for k, v in per_kernel.items()))
-
-    # Timed region: K steps, with the dominant kernel's launches bracketed by events.
-    n_dom = counts[dominant]["launches"] * args.steps
-    torch.cuda.synchronize()
-    d.dflash_profile_start(dominant, n_dom)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        runner.step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    dom_times = d.dflash_profile_stop(n_dom)
-    dom_avg = sum(dom_times) / len(dom_times)
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step; {dominant} avg {dom_avg:.4f} ms over {len(dom_times)} launches")
-
-    positions = w.num_blocks * w.block_size
-    value = positions / (ms / 1e3)
-    roof = roofline_entry(dominant, counts[dominant], dom_avg, w.dtype)
+    roof = dict(res["roofline"])
     from bench_traffic import load as load_traffic
-    roof["traffic"] = load_traffic(w.name, dominant)
-    roof["launches_timed"] = len(dom_times)
-    t_roof = step_roofline_ms(counts, w.dtype)
+    roof["traffic"] = load_traffic(w.name, res["dominant"])
+    roof["launches_timed"] = res["dom_launches"]
+    t_roof = res["roofline_ms"]
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "block-positions/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(res["value"], 1), "unit": "block-positions/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: {DESCR[w.name]}", "num_blocks": w.num_blocks,
-                   "block_size": w.block_size, "layers": w.num_layers, "block_positions": positions},
+                   "block_size": w.block_size, "layers": w.num_layers, "block_positions": res["positions"]},
         "roofline": roof,
+        "ms_per_step_stats": {"median": round(res["ms_median"], 4), "p10": round(res["ms_p10"], 4),
+                              "p90": round(res["ms_p90"], 4), "events": "one HIP event pair per step"},
         "step_roofline": {"roofline_ms": round(t_roof, 4), "frac": round(t_roof / ms, 4),
-                          "flops": sum(c["flops"] * c["launches"] for c in counts.values()),
+                          "flops": res["flops"],
                           "model": "sum over kernels of max(flops / MFMA peak, bytes / HBM peak)"},
-        "kernel_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in res["per_kernel"].items()},
     }
-    if not args.no_next:
-        log("timing the steps next to the path (inference shape)")
-        result["next_rows"] = next_rows(d, torch)
+    if w.name == "c4":
+        result["long_context_views"] = long_context_views(w, res)
+    cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")
         budgets = {"c1": (128, 4), "c2": (8192, 32), "c3": (8192, 48), "c4": (4096, 12), "c5": (None, 24)}
         r, b = budgets[w.name]
-        result["cpu_baseline"] = cpu_baseline(w, runner, anchors, r, b)
+        cpu = cpu_baseline(w, runner, res["anchors"], r, b)
+    del runner
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        # The other bf16 workloads (one-layer, long-context, ragged-cache), each
+        # measured the same way, so the per-workload bars are on record.
+        configs = {}
+        for name in ("c2", "c3", "c4", "c5"):
+            if name == w.name:
+                configs[name] = config_summary(w, res)
+                continue
+            log(f"workload {name}: building inputs")
+            r2, run2 = measure(d, torch, WORKLOADS[name], args.steps, args.warmup)
+            configs[name] = config_summary(WORKLOADS[name], r2)
+            log(f"workload {name}: {r2['ms_per_step']:.3f} ms/step (median {r2['ms_median']:.3f})")
+            del run2
+            torch.cuda.empty_cache()
+        result["configs"] = configs
+    if not args.no_next:
+        log("timing the steps next to the path (inference shape)")
+        result["next_rows"] = next_rows(d, torch)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
