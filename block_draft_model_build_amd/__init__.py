@@ -6,7 +6,8 @@ are torch tensors used as device buffers (their data pointers are passed);
 the stream defaults to torch's current stream on the tensor's device.
 
 The names mirror the C entry points:
-  dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_truncate,
+  dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_append_noalloc,
+  dflash_ctx_truncate,
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
@@ -25,10 +26,13 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdflash.so")
 
-DFLASH_OK, DFLASH_ERR_INVALID_ARG, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP = range(5)
+(DFLASH_OK, DFLASH_ERR_INVALID_ARG, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE, DFLASH_ERR_HIP,
+ DFLASH_ERR_SCRATCH_LIMIT) = range(6)
+DFLASH_NOALLOC_SCRATCH_BYTES = 32 << 20
 DFLASH_F32, DFLASH_BF16 = 0, 1
 
-EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_truncate",
+EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_append_noalloc",
+            "dflash_ctx_truncate",
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
@@ -79,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.dflash_ctx_proj.restype = ctypes.c_int
     lib.dflash_ctx_append.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, P, I64, P, SZ, P]
     lib.dflash_ctx_append.restype = ctypes.c_int
+    lib.dflash_ctx_append_noalloc.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, P, I64, P]
+    lib.dflash_ctx_append_noalloc.restype = ctypes.c_int
     lib.dflash_ctx_truncate.argtypes = [P, P, I32, P]
     lib.dflash_ctx_truncate.restype = ctypes.c_int
     lib.dflash_block_attn.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, SZ, P]
@@ -234,6 +240,17 @@ def dflash_ctx_append(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_l
                                _ptr(w_proj), lw, ck, cv, int(ctx_total), wp, wb,
                                _stream(stream, target_states))
     _check("dflash_ctx_append", s)
+
+
+def dflash_ctx_append_noalloc(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
+                              num_rows: int, positions, dst_rows, w_proj, layers, ctx_k: List, ctx_v: List,
+                              ctx_total: int, stream=None) -> None:
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    s = _lib.dflash_ctx_append_noalloc(ctypes.byref(cfg), _ptr(target_states), int(ts_row_stride),
+                                       int(ts_layer_stride), int(num_rows), _ptr(positions), _ptr(dst_rows),
+                                       _ptr(w_proj), lw, ck, cv, int(ctx_total), _stream(stream, target_states))
+    _check("dflash_ctx_append_noalloc", s)
 
 
 def dflash_ctx_truncate(lengths, keep, n: int = None, stream=None) -> None:

@@ -4,6 +4,8 @@
 // attention.h and the RMSNorm kernel below.
 #include <string.h>
 
+#include <mutex>
+
 #include "attention.h"
 #include "common.h"
 #include "gemm.h"
@@ -147,9 +149,7 @@ template <typename T>
 static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, int64_t ls, int64_t rows,
                              const int32_t* positions, const T* w_proj, const dflash_layer_weights* layers,
                              void* const* ck, void* const* cv, int64_t ctx_total, int64_t row_offset,
-                             const int64_t* dst_rows, char* ws, hipStream_t st) {
-    const Workspace w = workspace_layout(c, 0, rows);
-    T* C = reinterpret_cast<T*>(ws + w.c);
+                             const int64_t* dst_rows, T* C, hipStream_t st) {
     const int H = c.hidden, K = c.num_target_layers * c.target_hidden;
     const int M = (int)rows;
     hipError_t e = gemm<T>(DFLASH_KERNEL_CTX_PROJ, M, H, K, AStacked<T>{ts, rs, ls, c.target_hidden}, BPlain<T>{w_proj, K},
@@ -265,6 +265,8 @@ extern "C" const char* dflash_status_string(dflash_status s) {
         case DFLASH_ERR_UNSUPPORTED: return "unsupported shape or dtype";
         case DFLASH_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case DFLASH_ERR_HIP: return "HIP launch or runtime error";
+        case DFLASH_ERR_SCRATCH_LIMIT:
+            return "input larger than the allocation-free entry point's static scratch (32 MiB)";
     }
     return "unknown status";
 }
@@ -304,24 +306,25 @@ extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* t
     if ((s = ws_check(cfg, 0, num_rows, workspace, workspace_bytes)) != DFLASH_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     char* ws = static_cast<char*>(workspace);
+    char* C = ws + workspace_layout(*cfg, 0, num_rows).c;
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = ctx_proj_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
                                num_rows, positions, static_cast<const __bf16*>(w_proj), layers, ctx_k, ctx_v,
-                               ctx_total, row_offset, nullptr, ws, st);
+                               ctx_total, row_offset, nullptr, reinterpret_cast<__bf16*>(C), st);
     else
         e = ctx_proj_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
                               num_rows, positions, static_cast<const float*>(w_proj), layers, ctx_k, ctx_v,
-                              ctx_total, row_offset, nullptr, ws, st);
+                              ctx_total, row_offset, nullptr, reinterpret_cast<float*>(C), st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
-extern "C" dflash_status dflash_ctx_append(const dflash_config* cfg, const void* target_states,
-                                           int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
-                                           const int32_t* positions, const int64_t* dst_rows, const void* w_proj,
-                                           const dflash_layer_weights* layers, void* const* ctx_k,
-                                           void* const* ctx_v, int64_t ctx_total, void* workspace,
-                                           size_t workspace_bytes, void* hip_stream) {
+// Host-side checks shared by dflash_ctx_append and its allocation-free variant.
+static dflash_status ctx_append_check(const dflash_config* cfg, const void* target_states, int64_t ts_row_stride,
+                                      int64_t ts_layer_stride, int64_t num_rows, const int32_t* positions,
+                                      const int64_t* dst_rows, const void* w_proj,
+                                      const dflash_layer_weights* layers, void* const* ctx_k, void* const* ctx_v,
+                                      int64_t ctx_total) {
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
     if (num_rows < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
@@ -337,19 +340,84 @@ extern "C" dflash_status dflash_ctx_append(const dflash_config* cfg, const void*
         if (layers[l].wk == nullptr || layers[l].wv == nullptr || ctx_k[l] == nullptr || ctx_v[l] == nullptr ||
             !aligned16(layers[l].wk) || !aligned16(layers[l].wv))
             return DFLASH_ERR_INVALID_ARG;
-    if ((s = ws_check(cfg, 0, num_rows, workspace, workspace_bytes)) != DFLASH_OK) return s;
-    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    char* ws = static_cast<char*>(workspace);
+    return DFLASH_OK;
+}
+
+static dflash_status ctx_append_run(const dflash_config* cfg, const void* target_states, int64_t ts_row_stride,
+                                    int64_t ts_layer_stride, int64_t num_rows, const int32_t* positions,
+                                    const int64_t* dst_rows, const void* w_proj, const dflash_layer_weights* layers,
+                                    void* const* ctx_k, void* const* ctx_v, int64_t ctx_total, void* C,
+                                    hipStream_t st) {
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = ctx_proj_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
                                num_rows, positions, static_cast<const __bf16*>(w_proj), layers, ctx_k, ctx_v,
-                               ctx_total, 0, dst_rows, ws, st);
+                               ctx_total, 0, dst_rows, static_cast<__bf16*>(C), st);
     else
         e = ctx_proj_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
                               num_rows, positions, static_cast<const float*>(w_proj), layers, ctx_k, ctx_v,
-                              ctx_total, 0, dst_rows, ws, st);
+                              ctx_total, 0, dst_rows, static_cast<float*>(C), st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_ctx_append(const dflash_config* cfg, const void* target_states,
+                                           int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                           const int32_t* positions, const int64_t* dst_rows, const void* w_proj,
+                                           const dflash_layer_weights* layers, void* const* ctx_k,
+                                           void* const* ctx_v, int64_t ctx_total, void* workspace,
+                                           size_t workspace_bytes, void* hip_stream) {
+    dflash_status s = ctx_append_check(cfg, target_states, ts_row_stride, ts_layer_stride, num_rows, positions,
+                                       dst_rows, w_proj, layers, ctx_k, ctx_v, ctx_total);
+    if (s != DFLASH_OK || num_rows == 0) return s;
+    if ((s = ws_check(cfg, 0, num_rows, workspace, workspace_bytes)) != DFLASH_OK) return s;
+    char* C = static_cast<char*>(workspace) + workspace_layout(*cfg, 0, num_rows).c;
+    return ctx_append_run(cfg, target_states, ts_row_stride, ts_layer_stride, num_rows, positions, dst_rows, w_proj,
+                          layers, ctx_k, ctx_v, ctx_total, C, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+// ------------------------------------------------------------------ allocation-free context append
+// The projected rows C of dflash_ctx_append_noalloc live in this array. In
+// host code its name is only a host-side stand-in: the device address comes
+// from hipGetSymbolAddress, looked up once per device (each GPU holds its own
+// copy of the array at its own address) and kept in noalloc_scratch_ptr.
+static __device__ __attribute__((aligned(256))) char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current device's scratch array.
+static dflash_status noalloc_scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DFLASH_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DFLASH_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return DFLASH_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DFLASH_OK;
+}
+
+extern "C" dflash_status dflash_ctx_append_noalloc(const dflash_config* cfg, const void* target_states,
+                                                   int64_t ts_row_stride, int64_t ts_layer_stride,
+                                                   int64_t num_rows, const int32_t* positions,
+                                                   const int64_t* dst_rows, const void* w_proj,
+                                                   const dflash_layer_weights* layers, void* const* ctx_k,
+                                                   void* const* ctx_v, int64_t ctx_total, void* hip_stream) {
+    dflash_status s = ctx_append_check(cfg, target_states, ts_row_stride, ts_layer_stride, num_rows, positions,
+                                       dst_rows, w_proj, layers, ctx_k, ctx_v, ctx_total);
+    if (s != DFLASH_OK || num_rows == 0) return s;
+    if ((uint64_t)num_rows * (uint64_t)cfg->hidden * (uint64_t)elem_bytes(*cfg) > DFLASH_NOALLOC_SCRATCH_BYTES)
+        return DFLASH_ERR_SCRATCH_LIMIT;
+    void* C = nullptr;
+    if ((s = noalloc_scratch_ptr(&C)) != DFLASH_OK) return s;
+    return ctx_append_run(cfg, target_states, ts_row_stride, ts_layer_stride, num_rows, positions, dst_rows, w_proj,
+                          layers, ctx_k, ctx_v, ctx_total, C, reinterpret_cast<hipStream_t>(hip_stream));
 }
 
 // ------------------------------------------------------------------ LM head + decayed CE

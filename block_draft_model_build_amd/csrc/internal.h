@@ -42,6 +42,7 @@ struct Workspace {
 };
 
 inline int attn_items_max(const dflash_config& c, int nb) {
+    if (nb <= 0) return 0;                 // context projection only: no attention partials
     return c.num_kv_heads * (attn_target_splits(c, nb) + nb);
 }
 

@@ -51,7 +51,8 @@ typedef enum dflash_status {
     DFLASH_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shape */
     DFLASH_ERR_UNSUPPORTED = 2,   /* valid, but outside the shapes the kernels implement */
     DFLASH_ERR_WORKSPACE = 3,     /* workspace missing, too small or misaligned */
-    DFLASH_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+    DFLASH_ERR_HIP = 4,           /* a HIP launch or runtime call failed */
+    DFLASH_ERR_SCRATCH_LIMIT = 5  /* input larger than an allocation-free entry point's static scratch */
 } dflash_status;
 
 typedef enum dflash_dtype { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -185,6 +186,38 @@ dflash_status dflash_ctx_append(const dflash_config *cfg, const void *target_sta
                                 const dflash_layer_weights *layers, void *const *ctx_k,
                                 void *const *ctx_v, int64_t ctx_total, void *workspace,
                                 size_t workspace_bytes, void *hip_stream);
+
+/*
+ * dflash_ctx_append_noalloc -- dflash_ctx_append for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, semantics and results as
+ * dflash_ctx_append, minus the workspace: the projected rows C live in a static
+ * device array of DFLASH_NOALLOC_SCRATCH_BYTES (32 MiB) that each GPU the
+ * library runs on holds until the process ends. Nothing is allocated or freed
+ * by this call.
+ *
+ *   Limit: num_rows * hidden * element size <= 32 MiB, i.e. up to
+ *   32 MiB / (hidden * 2) rows in bf16 (4096 rows at hidden 4096) and half that
+ *   in fp32; larger calls return DFLASH_ERR_SCRATCH_LIMIT before anything is
+ *   enqueued.
+ *   Device: the array of the current device is used, so hip_stream must belong
+ *   to the current device. Its address is looked up once per device, on that
+ *   device's first call.
+ *   Sharing: every call on one GPU uses the same array. C is fully rewritten by
+ *   each call before it is read, so nothing carries over between calls, but two
+ *   calls that overlap on one GPU (different streams, or different host threads
+ *   without stream order between them) race on the array and give undefined
+ *   results; serialise them.
+ * Errors: as dflash_ctx_append (no WORKSPACE error); SCRATCH_LIMIT as above;
+ * HIP when the scratch address cannot be obtained.
+ */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dflash_status dflash_ctx_append_noalloc(const dflash_config *cfg, const void *target_states,
+                                        int64_t ts_row_stride, int64_t ts_layer_stride,
+                                        int64_t num_rows, const int32_t *positions,
+                                        const int64_t *dst_rows, const void *w_proj,
+                                        const dflash_layer_weights *layers, void *const *ctx_k,
+                                        void *const *ctx_v, int64_t ctx_total, void *hip_stream);
 
 /*
  * dflash_ctx_truncate -- roll per-request context lengths back after

@@ -55,8 +55,9 @@ def test_workspace_size_grows_with_work():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert d.dflash_status_string(s)
+    assert "scratch" in d.dflash_status_string(d.DFLASH_ERR_SCRATCH_LIMIT)
     assert "workspace" in d.dflash_status_string(d.DFLASH_ERR_WORKSPACE)
 
 
@@ -114,6 +115,16 @@ def test_rejects_bad_arguments_before_launch():
                                  ptrs, ptrs, 50, P(fake), 1024, None) == d.DFLASH_ERR_WORKSPACE
     assert lib.dflash_ctx_append(ctypes.byref(cfg), None, 0, 0, 0, None, None, None, None, None, None, 0,
                                  None, 0, None) == d.DFLASH_OK                     # nothing to append
+    # allocation-free append: same checks; inputs past the static scratch are
+    # refused before anything touches the device (hidden 4096 bf16: 4096 rows fit)
+    assert lib.dflash_ctx_append_noalloc(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), None, P(fake),
+                                         lw, ptrs, ptrs, 50, None) == d.DFLASH_ERR_INVALID_ARG
+    limit = d.DFLASH_NOALLOC_SCRATCH_BYTES // (cfg.hidden * 2)
+    assert limit == 4096
+    assert lib.dflash_ctx_append_noalloc(ctypes.byref(cfg), P(fake), 20480, 4096, limit + 1, P(fake), P(fake),
+                                         P(fake), lw, ptrs, ptrs, 50, None) == d.DFLASH_ERR_SCRATCH_LIMIT
+    assert lib.dflash_ctx_append_noalloc(ctypes.byref(cfg), None, 0, 0, 0, None, None, None, None, None, None,
+                                         0, None) == d.DFLASH_OK                   # nothing to append
     assert lib.dflash_ctx_truncate(P(fake), P(fake), -1, None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_truncate(None, P(fake), 3, None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_truncate(None, None, 0, None) == d.DFLASH_OK
