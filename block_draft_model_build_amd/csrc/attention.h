@@ -62,12 +62,33 @@ template <typename T> struct AttnArgs {
     const int* group_start;            // [groups + 1]
     const int* item_start;             // [groups + 1] prefix sums of splits per group
     const int* sched;                  // [0] keys per split of multi-block groups,
-                                       // [1] number of groups, [2] of single-block groups
+                                       // [1] number of groups, [2] of single-block groups,
+                                       // [3] number of group-splits
+    const int* meta;                   // [group-splits][16] item records in dispatch order (AttnMeta)
+    const int4* bmeta;                 // [nb] block records (AttnBlockMeta)
     float* part_o;                     // [items][kMaxGroup][QC][D]
     float* part_ml;                    // [items][kMaxGroup][QC][2]
     int* redo;                         // [items][4]: a wave's scores outran its reference
     RopeTurns rt;
 };
+
+// Item record (16 int32 per group-split), written by the scheduler in
+// dispatch order so that a workgroup fetches everything it needs to start in
+// one scalar load instead of a chain of dependent ones.
+enum AttnMeta {
+    kMetaN0 = 0,        // first block of the group
+    kMetaNg = 1,        // blocks in the group (1..4)
+    kMetaS = 2,         // split index
+    kMetaNsplit = 3,    // splits of the group
+    kMetaChunk = 4,     // keys per split
+    kMetaSg = 5,        // group-split index (item_start[group] + s)
+    kMetaBaseLo = 6,    // clamped context base, low and high words
+    kMetaBaseHi = 7,
+    kMetaAnchor = 8,    // 8..11: effective anchors of the group's blocks (-1: absent or empty)
+    kMetaAmax = 12,     // largest of them
+};
+// Block record: {first group-split of its group, splits, position in its group, effective anchor}.
+enum AttnBlockMeta { kBmSg0 = 0, kBmNsplit = 1, kBmJ = 2, kBmAnchor = 3 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
@@ -415,40 +436,33 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     // The wave index is uniform across the wave: scalar registers for everything derived from it.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5;
     const int hkv = p.hkv, bs = p.bs, G = p.hq / p.hkv;
-    const int ngroups = p.sched[1];
-    const int total = p.item_start[ngroups] * hkv;
-    if ((int)blockIdx.x >= total) return;
-    // Items are dispatched last-first: groups come in ascending anchor order,
-    // so the longest prefixes start first and the short ones fill the tail.
-    const int item = total - 1 - (int)blockIdx.x;
+    // Item records are stored in dispatch order (longest work first):
+    // workgroup b runs record b / hkv for KV head hkv - 1 - b % hkv.
+    const int slot = (int)blockIdx.x / hkv;
+    if (slot >= p.sched[3]) return;
+    const int g = hkv - 1 - ((int)blockIdx.x - slot * hkv);
+    const int* rec = p.meta + 16 * (int64_t)slot;
+    const int n0 = rec[kMetaN0], ng = rec[kMetaNg], s = rec[kMetaS], nsplit = rec[kMetaNsplit];
+    const int chunk = rec[kMetaChunk], sg = rec[kMetaSg], amax = rec[kMetaAmax];
+    const int64_t base = (int64_t)(uint32_t)rec[kMetaBaseLo] | ((int64_t)rec[kMetaBaseHi] << 32);
+    const int anc[kMaxGroup] = {rec[kMetaAnchor], rec[kMetaAnchor + 1], rec[kMetaAnchor + 2], rec[kMetaAnchor + 3]};
+    auto anchor_of = [&](int jj) {                    // jj < ng
+        return jj == 0 ? anc[0] : (jj == 1 ? anc[1] : (jj == 2 ? anc[2] : anc[3]));
+    };
+    const int item = sg * hkv + g;                    // index of this item's partials and redo flags
     if constexpr (REDO) {
         const int4 f = *reinterpret_cast<const int4*>(p.redo + 4 * (int64_t)item);
         if ((f.x | f.y | f.z | f.w) == 0) return;
     }
-    const int sg = item / hkv, g = item - sg * hkv;
-    int lo = 0, hi = ngroups;
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (p.item_start[mid] <= sg) lo = mid; else hi = mid;
-    }
-    const int gi = lo;
-    const int s = sg - p.item_start[gi];
-    const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
-    const int n0 = p.group_start[gi];
-    const int ng = p.group_start[gi + 1] - n0;
     const int wpb = ng == 1 ? 4 : (ng == 2 ? 2 : 1);   // waves per block
     const int j = wave / wpb;                          // this wave's block in the group
     const int phase = wave - j * wpb;                  // this wave's share of the block's keys
     const bool active = j < ng;
     const int qcols = bs * G;
-    const int chunk = ng == 1 ? p.sched[2] : p.sched[0];
-    const int64_t base = clamp_base(p.base[n0], p.ctx_total);
     const int kbeg = s * chunk;
 
-    int amax = -1;
-    for (int jj = 0; jj < ng; ++jj) amax = max(amax, anchor_eff(p.anchor[n0 + jj], base, p.ctx_total));
     const int n = n0 + (active ? j : 0);
-    const int a = active ? anchor_eff(p.anchor[n], base, p.ctx_total) : -1;
+    const int a = active ? anchor_of(j) : -1;
     const int kend_g = min(amax, kbeg + chunk);
     const int kend = min(a, kbeg + chunk);
     // Single-block groups split over several items take interleaved tiles
@@ -459,57 +473,79 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
     const int kclamp = ilv ? amax : kend_g;       // end of the keys this item may read
     const int kvalid = ilv ? a : kend;            // end of this wave's block's visible keys
 
-    // ---- queries of this wave's block: rotate at a + k, scale by log2(e)/sqrt(D)
+    // ---- queries of this wave's block, rotated at a + k and scaled by
+    // log2(e)/sqrt(D). Their loads are issued here, with the own keys' loads,
+    // before the first context tile's DMA; the rotation comes after it, so the
+    // tile streams in while both are processed (loads complete in issue order).
     frag qf[QS][DK];
+    u32x4 qraw[QS][DK / 2][2];
+    float qraw1[QS][DK / 2][2];
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
         const int c = qs * 32 + (lane & 31);
         const bool live = a >= 0 && c < qcols;
         const int k = live ? c % bs : 0, hh = live ? c / bs : 0;
         const T* qrow = p.q + (int64_t)(n * bs + k) * p.q_ld + (int64_t)(g * G + hh) * D;
-        const int pos = (a >= 0 ? a : 0) + k;
 #pragma unroll
         for (int kk = 0; kk < DK / 2; ++kk) {
             const int d0 = kk * KSTEP + h * E;
-            float x1[E], x2[E];
             if constexpr (E == 8) {
-                u32x4 r1 = {0, 0, 0, 0}, r2 = {0, 0, 0, 0};
+                qraw[qs][kk][0] = qraw[qs][kk][1] = u32x4{0, 0, 0, 0};
                 if (live) {
-                    r1 = *reinterpret_cast<const u32x4*>(qrow + d0);
-                    r2 = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
+                    qraw[qs][kk][0] = *reinterpret_cast<const u32x4*>(qrow + d0);
+                    qraw[qs][kk][1] = *reinterpret_cast<const u32x4*>(qrow + d0 + D / 2);
                 }
-                bf16x8 v1 = __builtin_bit_cast(bf16x8, r1), v2 = __builtin_bit_cast(bf16x8, r2);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { x1[e] = to_f32(v1[e]); x2[e] = to_f32(v2[e]); }
             } else {
-                x1[0] = live ? to_f32(qrow[d0]) : 0.f;
-                x2[0] = live ? to_f32(qrow[d0 + D / 2]) : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float cs, sn;
-                rope_cs(p.rt, d0 + e, pos, cs, sn);
-                const float y1 = (x1[e] * cs - x2[e] * sn) * p.qscale;
-                const float y2 = (x2[e] * cs + x1[e] * sn) * p.qscale;
-                if constexpr (E == 8) {
-                    qf[qs][kk][e] = from_f32<T>(y1);
-                    qf[qs][kk + DK / 2][e] = from_f32<T>(y2);
-                } else {
-                    qf[qs][kk] = y1;
-                    qf[qs][kk + DK / 2] = y2;
-                }
+                qraw1[qs][kk][0] = live ? to_f32(qrow[d0]) : 0.f;
+                qraw1[qs][kk][1] = live ? to_f32(qrow[d0 + D / 2]) : 0.f;
             }
         }
     }
-
-    // Q is only ever an MFMA operand, which may sit in AGPRs (gfx950): keep it
-    // there and leave the VGPRs to the softmax and the K/V fragments.
-    if constexpr (E == 8) {
+    auto rotate_q = [&]() {
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs)
+        for (int qs = 0; qs < QS; ++qs) {
+            const int c = qs * 32 + (lane & 31);
+            const bool live = a >= 0 && c < qcols;
+            const int k = live ? c % bs : 0;
+            const int pos = (a >= 0 ? a : 0) + k;
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) asm volatile("" : "+a"(qf[qs][kk]));
-    }
+            for (int kk = 0; kk < DK / 2; ++kk) {
+                const int d0 = kk * KSTEP + h * E;
+                float x1[E], x2[E];
+                if constexpr (E == 8) {
+                    bf16x8 v1 = __builtin_bit_cast(bf16x8, qraw[qs][kk][0]);
+                    bf16x8 v2 = __builtin_bit_cast(bf16x8, qraw[qs][kk][1]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) { x1[e] = to_f32(v1[e]); x2[e] = to_f32(v2[e]); }
+                } else {
+                    x1[0] = qraw1[qs][kk][0];
+                    x2[0] = qraw1[qs][kk][1];
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float cs, sn;
+                    rope_cs(p.rt, d0 + e, pos, cs, sn);
+                    const float y1 = (x1[e] * cs - x2[e] * sn) * p.qscale;
+                    const float y2 = (x2[e] * cs + x1[e] * sn) * p.qscale;
+                    if constexpr (E == 8) {
+                        qf[qs][kk][e] = from_f32<T>(y1);
+                        qf[qs][kk + DK / 2][e] = from_f32<T>(y2);
+                    } else {
+                        qf[qs][kk] = y1;
+                        qf[qs][kk + DK / 2] = y2;
+                    }
+                }
+            }
+        }
+        // Q is only ever an MFMA operand, which may sit in AGPRs (gfx950): keep
+        // it there and leave the VGPRs to the softmax and the K/V fragments.
+        if constexpr (E == 8) {
+#pragma unroll
+            for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+                for (int kk = 0; kk < DK; ++kk) asm volatile("" : "+a"(qf[qs][kk]));
+        }
+    };
 
     f32x16 o[DS][QS];
     float m[QS], l[QS], mt[QS];          // reference, sum, true maximum (attn_update)
@@ -616,26 +652,20 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
     };
 
-    // bf16 stages the first tile while the blocks' own keys are processed
-    // (they use stage 1); fp32 stages its tiles from registers below.
     constexpr int OWN = TT::SWZ ? 1 : 0;
-    if constexpr (TT::SWZ) {
-        if (ntile > 0 && tile_dma_ok(tfirst)) issue_dma(tfirst, 0);
-    }
 
     // ---- split 0: the blocks' own keys. Block jj's rows go to slot jj (32 rows)
     // of stage OWN: K rotated at its anchor + k', V^T transposed; rows >= bs zero.
+    // Every 16-byte chunk of the group's K and V rows is requested before any
+    // is used (one round trip to memory, not one per element), and before the
+    // first context tile's DMA. K row chunks c and c + KCH/2 hold the rotation
+    // partners (i, i + D/2).
+    constexpr int HC = TT::KCH / 2;
+    constexpr int KIT = (kMaxGroup * 32 * HC + 255) / 256;
+    constexpr int VIT = (kMaxGroup * 32 * TT::KCH + 255) / 256;
+    const int nrows = ng * bs;
+    u32x4 k1[KIT], k2[KIT], vv[VIT];
     if (s == 0) {
-        char* Ks = TT::kstage(smem, OWN);
-        char* Vt = TT::vstage(smem, OWN);
-        // Every 16-byte chunk of the group's K and V rows is requested before
-        // any is used (one round trip to memory, not one per element). K row
-        // chunks c and c + KCH/2 hold the rotation partners (i, i + D/2).
-        constexpr int HC = TT::KCH / 2;
-        constexpr int KIT = (kMaxGroup * 32 * HC + 255) / 256;
-        constexpr int VIT = (kMaxGroup * 32 * TT::KCH + 255) / 256;
-        const int nrows = ng * bs;
-        u32x4 k1[KIT], k2[KIT], vv[VIT];
 #pragma unroll
         for (int it = 0; it < KIT; ++it) {
             const int w = tid + 256 * it, row = w / HC, c = w - row * HC;
@@ -657,6 +687,16 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
                                                          (int64_t)g * D + c * EC);
             }
         }
+    }
+    // bf16 stages the first tile while the queries and the blocks' own keys are
+    // processed (they use stage 1); fp32 stages its tiles from registers below.
+    if constexpr (TT::SWZ) {
+        if (ntile > 0 && tile_dma_ok(tfirst)) issue_dma(tfirst, 0);
+    }
+    rotate_q();
+    if (s == 0) {
+        char* Ks = TT::kstage(smem, OWN);
+        char* Vt = TT::vstage(smem, OWN);
         // Block jj's rows go to slot jj (32 rows) of stage OWN: K rotated at its
         // anchor + k, V^T transposed. Rows bs..31 of a slot are never read
         // unmasked (the own-key slice masks keys past bs), nor are empty blocks'.
@@ -665,7 +705,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             const int w = tid + 256 * it, row = w / HC, c = w - row * HC;
             if (row < nrows) {
                 const int jj = row / bs, k = row - jj * bs;
-                const int aj = anchor_eff(p.anchor[n0 + jj], base, p.ctx_total);
+                const int aj = anchor_of(jj);
                 T x1[EC], x2[EC], y1[EC], y2[EC];
                 *reinterpret_cast<u32x4*>(x1) = k1[it];
                 *reinterpret_cast<u32x4*>(x2) = k2[it];
@@ -727,7 +767,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         if constexpr (!REDO && QS == 2) {
             if (wpb == 1) {
                 int kmin = kbeg + chunk;
-                for (int jj = 0; jj < ng; ++jj) kmin = min(kmin, anchor_eff(p.anchor[n0 + jj], base, p.ctx_total));
+                for (int jj = 0; jj < ng; ++jj) kmin = min(kmin, anchor_of(jj));
                 nfull = kmin > kbeg ? min(ntile, (kmin - kbeg) / SUPER) : 0;
             }
         }
@@ -873,7 +913,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
                 }
         }
     } else {
-        const int64_t pi = ((int64_t)(p.item_start[gi] + s) * hkv + g) * kMaxGroup + j;
+        const int64_t pi = ((int64_t)sg * hkv + g) * kMaxGroup + j;
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
             const int c = qs * 32 + (lane & 31);
@@ -903,23 +943,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
     constexpr int MAXF = 32;                       // splits whose weights are kept in LDS
     __shared__ float s_mu[QC], s_inv[QC];
     __shared__ float s_f[MAXF][QC];
-    // One workgroup per (block, KV head): locate the block's group.
+    // One workgroup per (block, KV head); the block's record says where its
+    // group's splits are.
     const int n = blockIdx.x, g = blockIdx.y;
-    const int ngroups = p.sched[1];
-    int lo = 0, hi = ngroups;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.group_start[mid] <= n) lo = mid; else hi = mid;
-    }
-    const int gi = lo;
-    const int nsplit = p.item_start[gi + 1] - p.item_start[gi];
-    if (nsplit <= 1 || p.anchor[n] < 0) return;
-    const int j = n - p.group_start[gi];
+    const int4 bm = p.bmeta[n];
+    const int nsplit = bm[kBmNsplit];
+    if (nsplit <= 1 || bm[kBmAnchor] < 0) return;
+    const int j = bm[kBmJ], sg0 = bm[kBmSg0];
     const int G = p.hq / p.hkv, bs = p.bs, qcols = bs * G;
     const int tid = threadIdx.x;
-    auto part = [&](int s) -> int64_t {
-        return ((int64_t)(p.item_start[gi] + s) * p.hkv + g) * kMaxGroup + j;
-    };
+    auto part = [&](int s) -> int64_t { return ((int64_t)(sg0 + s) * p.hkv + g) * kMaxGroup + j; };
     for (int c = tid; c < qcols; c += 256) {
         float mx = -__builtin_inff();
         for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.part_ml[(part(s) * QC + c) * 2]);
@@ -956,13 +989,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
 // multi-block groups get separate split sizes: chunk = max(256, ceil(sum of
 // their lengths / target) rounded up to 128), target_single (single) or
 // target_shared (multi) splits in total; a group gets max(1, ceil(length /
-// chunk)) splits.
+// chunk)) splits. The multi-block chunk then grows in 128-key steps until its
+// groups' splits (each rounded up) fit the target. The item records are
+// written longest work first.
 static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
                                                              int64_t ctx_total, int target_shared, int target_single,
-                                                             int* group_start, int* item_start, int* sched) {
+                                                             int* group_start, int* item_start, int* sched, int* meta,
+                                                             int4* bmeta) {
     __shared__ int scan[1024];
     __shared__ long long red[2][1024];
-    __shared__ int chunk_s[2], ngroups_s;
+    __shared__ int chunk_s[2], ngroups_s, nsg_s;
     const int tid = threadIdx.x;
     const int per_t = (nb + 1023) / 1024;
     const int b0 = tid * per_t;
@@ -1020,15 +1056,57 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
         }
         __syncthreads();
     }
+    __shared__ long long sum_s[2], cnt_s;
     if (tid < 2) {
         const int target = tid == 0 ? target_shared : target_single;
+        sum_s[tid] = red[tid][0];
         long long c = (red[tid][0] + target - 1) / target;
         c = (c + 127) / 128 * 128;
         if (c < 256) c = 256;
         if (c > (1 << 30)) c = 1 << 30;
         chunk_s[tid] = (int)c;
-        sched[tid == 0 ? 0 : 2] = (int)c;
     }
+    __syncthreads();
+    // Multi-block groups: rounding each group's split count up can exceed the
+    // target. When there are fewer such groups than the target, binary-search
+    // (in 128-key steps) the smallest chunk whose total split count fits,
+    // between the chunk above and sum / (target - groups), which always fits;
+    // their items then fill one round of workgroups as evenly as it allows.
+    auto count_multi = [&](long long c) {            // called by every thread
+        long long local_cnt = 0;
+        for (int i = 0; i < gper; ++i)
+            if (g0 + i < ng && !single(g0 + i)) {
+                const int len = group_len(g0 + i);
+                local_cnt += len <= 0 ? 1 : (len + c - 1) / c;
+            }
+        __syncthreads();
+        red[0][tid] = local_cnt;
+        __syncthreads();
+        for (int w = 512; w > 0; w >>= 1) {
+            if (tid < w) red[0][tid] += red[0][tid + w];
+            __syncthreads();
+        }
+        if (tid == 0) cnt_s = red[0][0];
+        __syncthreads();
+        return cnt_s;
+    };
+    {
+        const long long n_multi = count_multi(1LL << 30);
+        long long lo = chunk_s[0];
+        if (n_multi > 0 && n_multi < target_shared && count_multi(lo) > target_shared) {
+            long long hi = (sum_s[0] + (target_shared - n_multi) - 1) / (target_shared - n_multi);
+            hi = (hi + 127) / 128 * 128;
+            if (hi > (1 << 30)) hi = 1 << 30;
+            while (hi - lo > 128) {                   // count(lo) > target >= count(hi)
+                long long mid = (lo + hi) / 2 / 128 * 128;
+                if (mid <= lo) mid = lo + 128;
+                if (count_multi(mid) <= target_shared) hi = mid; else lo = mid;
+            }
+            if (tid == 0) chunk_s[0] = (int)hi;
+        }
+        __syncthreads();
+    }
+    if (tid < 2) sched[tid == 0 ? 0 : 2] = chunk_s[tid];
     if (tid == 0) sched[1] = ng;
     __syncthreads();
     // 3. splits per group -> item_start
@@ -1046,7 +1124,74 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
             item_start[g0 + i] = run;
             run += splits(g0 + i);
         }
-    if (tid == 1023) item_start[ng] = run;
+    if (tid == 1023) {
+        item_start[ng] = run;
+        nsg_s = run;
+        sched[3] = run;
+    }
+    __syncthreads();
+    // 4. dispatch order: longest work first (each item's visible keys plus a
+    //    fixed cost for its start), ties by group-split index, so the longest
+    //    items start together and the short ones fill the tail. Ranks are
+    //    counted by comparison (deterministic). Beyond kSortMax group-splits
+    //    the reverse of block order is used (blocks come in ascending anchor
+    //    order within a sequence).
+    const int nsg = nsg_s;
+    constexpr int kSortMax = 4096;
+    __shared__ int key_s[kSortMax], rank_s[kSortMax];
+    const bool sorted = nsg <= kSortMax;
+    if (sorted) {
+        for (int i = 0; i < gper; ++i) {
+            const int gi = g0 + i;
+            if (gi >= ng) continue;
+            const int len = max(group_len(gi), 0), ns = splits(gi);
+            const int chunk = chunk_s[single(gi) ? 1 : 0];
+            const bool ilv = single(gi) && ns > 1;
+            for (int sp = 0; sp < ns; ++sp) {
+                const int keys = ilv ? (len + ns - 1) / ns : max(0, min(len, (sp + 1) * chunk) - sp * chunk);
+                key_s[item_start[gi] + sp] = keys + (sp == 0 ? 384 : 256);
+            }
+        }
+        __syncthreads();
+        for (int x = tid; x < nsg; x += 1024) {
+            const int kx = key_s[x];
+            int r = 0;
+            for (int y = 0; y < nsg; ++y) {
+                const int ky = key_s[y];
+                r += ky > kx || (ky == kx && y < x);
+            }
+            rank_s[x] = r;
+        }
+        __syncthreads();
+    }
+    for (int i = 0; i < gper; ++i) {
+        const int gi = g0 + i;
+        if (gi >= ng) continue;
+        const int n0 = group_start[gi], cnt_g = group_start[gi + 1] - n0;
+        const int ns = splits(gi), sg0 = item_start[gi];
+        const int chunk = chunk_s[single(gi) ? 1 : 0];
+        const int64_t b = clamp_base(base[n0], ctx_total);
+        int a[kMaxGroup], amax = -1;
+        for (int jj = 0; jj < kMaxGroup; ++jj) {
+            a[jj] = jj < cnt_g ? block_run(n0 + jj) : -1;
+            amax = max(amax, a[jj]);
+        }
+        for (int jj = 0; jj < cnt_g; ++jj) bmeta[n0 + jj] = make_int4(sg0, ns, jj, a[jj]);
+        for (int s = 0; s < ns; ++s) {
+            int* m = meta + 16 * (int64_t)(sorted ? rank_s[sg0 + s] : nsg - 1 - (sg0 + s));
+            m[kMetaN0] = n0;
+            m[kMetaNg] = cnt_g;
+            m[kMetaS] = s;
+            m[kMetaNsplit] = ns;
+            m[kMetaChunk] = chunk;
+            m[kMetaSg] = sg0 + s;
+            m[kMetaBaseLo] = (int)(uint32_t)(uint64_t)b;
+            m[kMetaBaseHi] = (int)((uint64_t)b >> 32);
+            for (int jj = 0; jj < kMaxGroup; ++jj) m[kMetaAnchor + jj] = a[jj];
+            m[kMetaAmax] = amax;
+            m[13] = m[14] = m[15] = 0;
+        }
+    }
 }
 
 }  // namespace dflash

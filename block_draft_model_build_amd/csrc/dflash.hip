@@ -127,6 +127,8 @@ static AttnArgs<T> attn_args(const dflash_config& c, int nb, const T* q, int64_t
     a.group_start = reinterpret_cast<const int*>(ws + w.group_start);
     a.item_start = reinterpret_cast<const int*>(ws + w.item_start);
     a.sched = reinterpret_cast<const int*>(ws + w.sched);
+    a.meta = reinterpret_cast<const int*>(ws + w.meta);
+    a.bmeta = reinterpret_cast<const int4*>(ws + w.bmeta);
     a.part_o = reinterpret_cast<float*>(ws + w.part_o);
     a.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
     a.redo = reinterpret_cast<int*>(ws + w.redo);
@@ -140,7 +142,8 @@ static hipError_t attn_schedule(const dflash_config& c, int nb, const int64_t* b
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, base, anchor, nb, ctx_total,
                        (kAttnItemsShared + hkv - 1) / hkv, (kAttnItemsSingle + hkv - 1) / hkv,
                        reinterpret_cast<int*>(ws + w.group_start),
-                       reinterpret_cast<int*>(ws + w.item_start), reinterpret_cast<int*>(ws + w.sched));
+                       reinterpret_cast<int*>(ws + w.item_start), reinterpret_cast<int*>(ws + w.sched),
+                       reinterpret_cast<int*>(ws + w.meta), reinterpret_cast<int4*>(ws + w.bmeta));
     return hipGetLastError();
 }
 

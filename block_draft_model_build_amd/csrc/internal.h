@@ -32,18 +32,23 @@ inline int attn_qcols(const dflash_config& c) {
 }
 
 // Workspace layout (every region 256-byte aligned):
-//   attention scheduler: group_start [nb+1], item_start [nb+1], sched [4] (i32)
+//   attention scheduler: group_start [nb+1], item_start [nb+1], sched [4] (i32),
+//                        item records [splits_max][16] and block records [nb][4] (i32)
 //   attention partials:  part_o [items_max][4][QC][D] f32, part_ml [items_max][4][QC][2] f32,
 //                        redo [items_max][4] i32
 //   body: h [R][H] f32, x [R][H], qkv [R][(Hq+2Hkv)D], att [R][Hq D], u [R][I]   (dtype)
 //   ctx_proj: C [ctx_rows][H] (dtype); shares the body's space (calls are stream-ordered).
 struct Workspace {
-    size_t group_start, item_start, sched, part_o, part_ml, redo, h, x, qkv, att, u, c, total;
+    size_t group_start, item_start, sched, meta, bmeta, part_o, part_ml, redo, h, x, qkv, att, u, c, total;
 };
 
+// Group-splits (work items per KV head) the scheduler can form for nb blocks.
+inline int attn_splits_max(const dflash_config& c, int nb) {
+    return nb <= 0 ? 0 : attn_target_splits(c, nb) + nb;
+}
+
 inline int attn_items_max(const dflash_config& c, int nb) {
-    if (nb <= 0) return 0;                 // context projection only: no attention partials
-    return c.num_kv_heads * (attn_target_splits(c, nb) + nb);
+    return c.num_kv_heads * attn_splits_max(c, nb);   // none for the context projection alone
 }
 
 inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_rows) {
@@ -57,6 +62,8 @@ inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_ro
     w.group_start = off; off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
     w.item_start = off;  off = align_up(off + sizeof(int) * ((size_t)nb + 1), A);
     w.sched = off;       off = align_up(off + sizeof(int) * 4, A);
+    w.meta = off;        off = align_up(off + sizeof(int) * 16 * (size_t)attn_splits_max(c, nb), A);
+    w.bmeta = off;       off = align_up(off + sizeof(int) * 4 * (size_t)nb, A);
     w.part_o = off;      off = align_up(off + sizeof(float) * parts * qc * D, A);
     w.part_ml = off;     off = align_up(off + sizeof(float) * parts * qc * 2, A);
     w.redo = off;        off = align_up(off + sizeof(int) * parts, A);
