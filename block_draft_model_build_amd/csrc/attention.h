@@ -55,7 +55,8 @@ template <typename T> struct AttnArgs {
     const T* ck;                       // [Hkv][ctx_total][D], rotated
     const T* cvt;                      // [Hkv][D][ctx_total]
     int64_t ctx_total;
-    const int64_t* base; const int32_t* anchor; const uint8_t* valid;
+    const int64_t* base; const int32_t* anchor;
+    const uint8_t* valid;              // rows written as zero where 0; null: every row kept
     T* out; int64_t out_ld;
     int nb, bs, hq, hkv;
     float qscale;                      // log2(e) / sqrt(D)
@@ -897,7 +898,7 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             if (c >= qcols) continue;
             const int k = c % bs, hh = c / bs;
             const int row = n * bs + k;
-            const bool keep = p.valid[row] != 0;
+            const bool keep = p.valid == nullptr || p.valid[row] != 0;
             const float inv = keep ? 1.f / l[qs] : 0.f;
             T* orow = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D;
             // Accumulator elements 4i..4i+3 are 4 consecutive d: one 4-element store.
@@ -976,7 +977,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
             acc += v * f;
         }
         const int k = c % bs, hh = c / bs, row = n * bs + k;
-        const bool keep = p.valid[row] != 0;
+        const bool keep = p.valid == nullptr || p.valid[row] != 0;
         T* o = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D + d;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(keep ? acc[e] * s_inv[c] : 0.f);

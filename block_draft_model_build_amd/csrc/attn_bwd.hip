@@ -44,7 +44,7 @@ template <typename T> struct BwArgs {
     int64_t ctx_total;
     const int64_t* base;
     const int32_t* anchor;
-    const uint8_t* valid;
+    const uint8_t* valid;        // rows whose forward output is zero where 0; null: none
     const T *out, *dout;         // forward output and its gradient [nb*bs, Hq*D]
     float *dq, *dkb, *dvb;       // [nb*bs, Hq*D], [nb*bs, Hkv*D] x2
     float *dck, *dcv;            // [Hkv][ctx_total][D], [Hkv][D][ctx_total]
@@ -95,7 +95,8 @@ __device__ __forceinline__ void load_block_dout(const BwArgs<T>& a, int n, int g
         float v = 0.f;
         if (c < C && live) {
             const int k = c % a.bs, hh = c / a.bs, row = n * a.bs + k;
-            if (a.valid[row] != 0) v = to_f32(a.dout[(int64_t)row * a.q_ld + (int64_t)(g * G + hh) * D + d]);
+            if (a.valid == nullptr || a.valid[row] != 0)
+                v = to_f32(a.dout[(int64_t)row * a.q_ld + (int64_t)(g * G + hh) * D + d]);
         }
         L.dout[c][d] = v;
     }
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const __bf16* qr = a.q + (int64_t)qrow * a.q_ld + (int64_t)(g * G + hq) * D;
         const __bf16* orow = a.out + (int64_t)qrow * a.q_ld + (int64_t)(g * G + hq) * D;
         const __bf16* dr = a.dout + (int64_t)qrow * a.q_ld + (int64_t)(g * G + hq) * D;
-        const bool live_row = col_ok && a.valid[qrow] != 0;
+        const bool live_row = col_ok && (a.valid == nullptr || a.valid[qrow] != 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 lo = {}, hi = {}, dlo = {}, dhi = {};

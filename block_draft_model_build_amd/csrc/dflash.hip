@@ -209,9 +209,11 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
                             static_cast<const T*>(L.wv), nq, nk, H},
                     EpStore<T>{qkv, nqkv}, st);
         if (e != hipSuccess) return e;
+        // Inside the body every row keeps its attention output (invalid rows
+        // evolve like the others); only the returned rows are zeroed.
         AttnArgs<T> a = attn_args<T>(c, nb, qkv, nqkv, qkv + nq, qkv + nq + nk, nqkv,
                                      static_cast<const T*>(ck[l]), static_cast<const T*>(cv[l]), ctx_total,
-                                     base, anchor, valid, att, nq, ws, w);
+                                     base, anchor, nullptr, att, nq, ws, w);
         if ((e = attn_launch<T>(c, a, nb, st)) != hipSuccess) return e;
         e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq}, BPlain<T>{static_cast<const T*>(L.wo), nq},
                     EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0}, st);

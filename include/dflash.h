@@ -279,11 +279,14 @@ dflash_status dflash_block_attn(const dflash_config *cfg, int32_t num_blocks, co
  *
  * Per layer l, with h the fp32 residual stream (h = block_embeds at the start):
  *   x = RMSNorm(h) * attn_norm;  q, k, v = x Wq^T, x Wk^T, x Wv^T
- *   h += DualSourceAttention(q, k, v, ctx_k[l], ctx_v[l]) Wo^T   (as dflash_block_attn)
+ *   h += DualSourceAttention(q, k, v, ctx_k[l], ctx_v[l]) Wo^T
  *   y = RMSNorm(h) * mlp_norm;   h += (SiLU(y Wg^T) * (y Wu^T)) Wd^T
- * out = h (cast to the config dtype) on valid rows, exact zero on rows with
- * block_valid == 0 and on every row of an empty block (anchor -1). Invalid rows
- * still take part in their block's attention in every layer.
+ * The attention is dflash_block_attn's, except that no row's output is zeroed
+ * for block_valid == 0: inside the body invalid rows evolve like the others and
+ * take part in their block's attention in every layer (rows of empty blocks
+ * get a zero attention output). out = h (cast to the config dtype) on valid
+ * rows, exact zero on rows with block_valid == 0 and on every row of an empty
+ * block (anchor -1).
  *
  *   block_embeds   device [nb*bs, H] (caller-supplied embedding per block position)
  *   layers         host array [num_layers]

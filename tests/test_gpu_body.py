@@ -78,6 +78,67 @@ def test_small_bf16_multilayer_ragged():
     compare(run.out, ref, tol_for(w), "body")
 
 
+def _invalid_rows_case(w):
+    """Blocks with short prefixes and invalid rows inside them: 3 blocks per
+    sequence at anchors near the start, each with invalid positions spread over
+    the block (including its last row). Empty blocks fill the rest."""
+    B, N, bs = w.batch, w.anchors_per_row, w.block_size
+    anchors = np.full((B, N), -1, np.int32)
+    valid = np.zeros((B, N, bs), np.uint8)
+    for b in range(B):
+        for i, a in enumerate([1 + b, 6 + 3 * b, 19 + b][:N]):
+            anchors[b, i] = a
+            valid[b, i] = 1
+            valid[b, i, [2 + i, 5, bs - 1]] = 0
+    return anchors, valid
+
+
+def _attention_zeroing_invalid(valid, bs):
+    keep = np.asarray(valid, bool).reshape(-1, bs)[:, :, None, None]
+
+    def att(q, k, v, ck, cv, base, anchor):
+        return np.where(keep, oracle.block_attention(q, k, v, ck, cv, base, anchor), 0.0)
+    return att
+
+
+@pytest.mark.parametrize("name", ["c1x2", "small_bf16"])
+def test_multilayer_invalid_rows_keep_evolving(name):
+    # Inside a multi-layer body an invalid row keeps its attention output and
+    # evolves like any other row; only the returned rows are zeroed. With short
+    # prefixes the block's own rows carry much of each query's attention, so
+    # the reading where attention zeroes invalid rows in every layer differs
+    # far beyond the tolerance (checked on the oracle here).
+    w = scaled(WORKLOADS["c1"], num_layers=2, anchors_per_row=4) if name == "c1x2" else SMALL_BF16
+    inp = make_training_inputs(w, "cuda")
+    run = TrainingRun(d, w, inp)
+    run.plan()
+    anchors, valid = _invalid_rows_case(w)
+    run.anchors.copy_(torch.from_numpy(anchors))
+    run.valid.copy_(torch.from_numpy(valid))
+    run.ctx_proj()
+    run.body()
+    torch.cuda.synchronize()
+    blocks = [n for n in range(w.num_blocks) if anchors.reshape(-1)[n] >= 0]
+    ref = oracle_training_blocks(w, inp, anchors, valid, blocks)
+    rows = torch.from_numpy(np.concatenate([np.arange(n * w.block_size, (n + 1) * w.block_size)
+                                            for n in blocks])).cuda()
+    compare(run.out[rows], ref, tol_for(w), "body with invalid rows")
+    empty = torch.from_numpy(np.repeat(anchors.reshape(-1) < 0, w.block_size)).cuda()
+    assert (run.out[empty] == 0).all()
+    # The rejected reading, on the oracle: the first sequence's blocks.
+    b0 = [n for n in blocks if n < w.anchors_per_row]
+    bs = w.block_size
+    layers = layers64(inp["layers"])
+    ck, cv = oracle_row_context(w, inp, 0, int(anchors.max()), layers)
+    e = np.concatenate([np64(inp["emb"][n * bs:(n + 1) * bs]) for n in b0])
+    a = anchors.reshape(-1)[b0]
+    v = np.concatenate([valid.reshape(-1)[n * bs:(n + 1) * bs] for n in b0])
+    alt = oracle.body._body(e, layers, ck, cv, np.zeros(len(b0), np.int64), a, v, oracle_cfg(w),
+                            _attention_zeroing_invalid(v, bs), False)
+    mine = ref[: len(b0) * bs]
+    assert np.linalg.norm(alt - mine) > 4 * tol_for(w)["rel_l2"] * np.linalg.norm(mine)
+
+
 def test_concat_and_stacked_layouts_agree():
     w = SMALL_BF16
     inp = make_training_inputs(w, "cuda")
