@@ -9,8 +9,9 @@ Contents:
               and a brute-force dense-mask attention used to pin the gathered form.
   verify.py -- greedy and speculative-sampling verification of a drafted block.
   loss.py  -- block LM head and positionally decayed cross-entropy.
-  backward.py -- gradients of the dual-source block attention and of the
-              context path (dW_proj).
+  backward.py -- gradients of the dual-source block attention, of the
+              context path (dW_proj) and of the whole body (every layer
+              weight, the block embeddings and the context caches).
 
 Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
   build_plan             pinned by invariants the pages fix (determinism, equal
@@ -39,6 +40,17 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   ctx_proj_backward      pinned by central differences of the forward context
                          path (ctx_proj then ctx_kv) along random directions of
                          W_proj and of C, and entry by entry on a tiny case.
+  rms_norm_backward, swiglu_backward
+                         pinned by central differences of rms_norm and of
+                         SiLU(g) * up, entry by entry.
+  layer_forward, body_forward_layers
+                         pinned to body_forward (an independent loop) to
+                         rounding.
+  layer_backward, body_backward
+                         pinned by central differences of body_forward over
+                         every weight of every layer, the block embeddings and
+                         both context caches of a two-layer case with invalid
+                         rows and an empty block.
 """
 from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
 from .verify import (
@@ -48,6 +60,7 @@ from .verify import (
 from .loss import lm_head_ce, lm_head_ce_rows, token_ce, logsumexp_rows, position_weights
 from .backward import (
     block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_hidden_grad, ctx_proj_backward,
+    rms_norm_backward, swiglu_backward, layer_forward, layer_backward, body_forward_layers, body_backward,
 )
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
@@ -64,4 +77,6 @@ __all__ = [
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
     "lm_head_ce", "lm_head_ce_rows", "token_ce", "logsumexp_rows", "position_weights",
     "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_hidden_grad", "ctx_proj_backward",
+    "rms_norm_backward", "swiglu_backward", "layer_forward", "layer_backward", "body_forward_layers",
+    "body_backward",
 ]

@@ -27,7 +27,7 @@ import math
 
 import numpy as np
 
-from .body import rope
+from .body import block_attn_call, rms_norm, rope, silu
 
 
 def block_attention_backward(q, kb, vb, ctx_k, ctx_v, base, anchor, d_out):
@@ -138,3 +138,161 @@ def ctx_proj_backward(X, positions, layers, d_ctx_k, d_ctx_v, num_kv_heads: int,
     X = np.asarray(X, np.float64)
     dC = ctx_hidden_grad(d_ctx_k, d_ctx_v, positions, layers, num_kv_heads, head_dim, theta)
     return dC, dC.T @ X
+
+
+# ---------------------------------------------------------------------------
+# The draft body's backward: every layer weight, the block embeddings and the
+# context caches (NeMo RL "DFlash Draft Body", How It Works, step 1 and Scope:
+# the body is trained with an optimizer step; step 3: the layers the body runs).
+# The forward differentiated is body_forward (body.py): per layer, with the
+# same readings as there (pre-norm decoder layer, no biases, invalid rows evolve
+# like the others inside the body, only the returned rows are zeroed):
+#     x = RMSNorm(h) w_a;  q, k, v = x Wq^T, x Wk^T, x Wv^T
+#     h1 = h + Attn(q, k, v) Wo^T
+#     y = RMSNorm(h1) w_m;  g = y Wg^T, u_p = y Wu^T,  u = SiLU(g) u_p
+#     h' = h1 + u Wd^T
+# and out = h_L on kept rows (valid, non-empty block), zero elsewhere.
+
+
+def rms_norm_backward(x, w, eps: float, dy):
+    """Gradients of y = x * r * w, r = (mean(x^2) + eps)^(-1/2) per row, given dy:
+        dx = r (dy w) - x r^3 (sum_j dy_j w_j x_j) / H
+        dw = sum over rows of dy x r
+    Returns (dx, dw)."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    dy = np.asarray(dy, np.float64)
+    H = x.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    dyw = dy * w
+    dot = np.sum(dyw * x, axis=-1, keepdims=True)
+    dx = r * dyw - x * (r ** 3) * dot / H
+    dw = np.sum(dy * x * r, axis=0)
+    return dx, dw
+
+
+def swiglu_backward(g, up, du):
+    """Gradients of u = SiLU(g) * up, SiLU(g) = g * s, s = sigmoid(g):
+        dg = du * up * s (1 + g (1 - s)),   dup = du * SiLU(g).
+    Returns (dg, dup)."""
+    g = np.asarray(g, np.float64)
+    up = np.asarray(up, np.float64)
+    du = np.asarray(du, np.float64)
+    s = 1.0 / (1.0 + np.exp(-g))
+    return du * up * s * (1.0 + g * (1.0 - s)), du * g * s
+
+
+def _f64(W):
+    return {k: np.asarray(v, np.float64) for k, v in W.items()}
+
+
+def _layer_attention(x, W, ctx_k, ctx_v, base, anchor, cfg):
+    bs = int(cfg["block_size"])
+    R = x.shape[0]
+    q, k, v = x @ W["wq"].T, x @ W["wk"].T, x @ W["wv"].T
+    every_row = np.ones(R, np.uint8)          # inside the body no row's output is zeroed
+    o = block_attn_call(q, k, v, ctx_k, ctx_v, base, anchor, every_row, bs, int(cfg["num_q_heads"]),
+                        int(cfg["num_kv_heads"]), int(cfg["head_dim"]), float(cfg["rope_theta"]))
+    return q, k, v, o
+
+
+def layer_forward(h, W, ctx_k, ctx_v, base, anchor, cfg):
+    """One draft layer on the residual stream h [R, H] -> h' [R, H] (the loop body
+    of body_forward, written out with its intermediates). ctx_k / ctx_v: this
+    layer's caches [Hkv, T, D] (K rotated)."""
+    W = _f64(W)
+    eps = float(cfg["rms_eps"])
+    h = np.asarray(h, np.float64)
+    x = rms_norm(h, W["attn_norm"], eps)
+    q, k, v, o = _layer_attention(x, W, np.asarray(ctx_k, np.float64), np.asarray(ctx_v, np.float64),
+                                  base, anchor, cfg)
+    h1 = h + o @ W["wo"].T
+    y = rms_norm(h1, W["mlp_norm"], eps)
+    g, up = y @ W["w_gate"].T, y @ W["w_up"].T
+    u = silu(g) * up
+    return h1 + u @ W["w_down"].T
+
+
+def layer_backward(h, W, ctx_k, ctx_v, base, anchor, cfg, dh_out):
+    """Backward of layer_forward given dh_out = dL/dh'. Recomputes the layer's
+    intermediates from its input h, then applies the chain rule from the output
+    back to the input:
+        d_w_down = dh'^T u,            du = dh' Wd
+        dg, dup  = swiglu_backward(g, up, du)
+        d_w_gate = dg^T y, d_w_up = dup^T y,   dy = dg Wg + dup Wu
+        dh1      = dh' + RMSNorm backward of (h1, w_m) at dy      (-> d_mlp_norm)
+        d_wo     = dh1^T o,            do = dh1 Wo
+        dq, dk, dv, dKc, dVc = block_attn_call_backward(..., do)  (every row kept)
+        d_wq = dq^T x, d_wk = dk^T x, d_wv = dv^T x,   dx = dq Wq + dk Wk + dv Wv
+        dh       = dh1 + RMSNorm backward of (h, w_a) at dx       (-> d_attn_norm)
+    Returns (dh, grads, d_ctx_k, d_ctx_v): grads holds d_<name> for every weight
+    of the layer in its own shape; d_ctx_k (rotated frame) and d_ctx_v are
+    [Hkv, T, D] like the caches."""
+    W = _f64(W)
+    eps = float(cfg["rms_eps"])
+    bs, Hq, Hkv, D = (int(cfg["block_size"]), int(cfg["num_q_heads"]), int(cfg["num_kv_heads"]),
+                      int(cfg["head_dim"]))
+    h = np.asarray(h, np.float64)
+    ctx_k = np.asarray(ctx_k, np.float64)
+    ctx_v = np.asarray(ctx_v, np.float64)
+    dh2 = np.asarray(dh_out, np.float64)
+    # Forward, keeping what the backward reads.
+    x = rms_norm(h, W["attn_norm"], eps)
+    q, k, v, o = _layer_attention(x, W, ctx_k, ctx_v, base, anchor, cfg)
+    h1 = h + o @ W["wo"].T
+    y = rms_norm(h1, W["mlp_norm"], eps)
+    g, up = y @ W["w_gate"].T, y @ W["w_up"].T
+    u = silu(g) * up
+    # MLP.
+    d_w_down = dh2.T @ u
+    du = dh2 @ W["w_down"]
+    dg, dup = swiglu_backward(g, up, du)
+    d_w_gate, d_w_up = dg.T @ y, dup.T @ y
+    dy = dg @ W["w_gate"] + dup @ W["w_up"]
+    dh1_norm, d_mlp_norm = rms_norm_backward(h1, W["mlp_norm"], eps, dy)
+    dh1 = dh2 + dh1_norm
+    # Attention.
+    d_wo = dh1.T @ o
+    do = dh1 @ W["wo"]
+    every_row = np.ones(h.shape[0], np.uint8)
+    dq, dk, dv, dck, dcv = block_attn_call_backward(q, k, v, ctx_k, ctx_v, base, anchor, every_row, bs, Hq,
+                                                    Hkv, D, float(cfg["rope_theta"]), do)
+    d_wq, d_wk, d_wv = dq.T @ x, dk.T @ x, dv.T @ x
+    dx = dq @ W["wq"] + dk @ W["wk"] + dv @ W["wv"]
+    dh_norm, d_attn_norm = rms_norm_backward(h, W["attn_norm"], eps, dx)
+    grads = dict(attn_norm=d_attn_norm, wq=d_wq, wk=d_wk, wv=d_wv, wo=d_wo, mlp_norm=d_mlp_norm,
+                 w_gate=d_w_gate, w_up=d_w_up, w_down=d_w_down)
+    return dh1 + dh_norm, grads, dck, dcv
+
+
+def _kept_rows(anchor, valid, bs: int):
+    anchor = np.asarray(anchor, np.int64)
+    return np.asarray(valid, bool).reshape(-1) & np.repeat(anchor >= 0, bs)
+
+
+def body_forward_layers(emb, layers, ctx_k, ctx_v, base, anchor, valid, cfg):
+    """body_forward as a chain of layer_forward calls. Returns (out, hs) with
+    hs[l] the residual stream entering layer l (hs[0] = emb)."""
+    h = np.asarray(emb, np.float64)
+    hs = []
+    for l, W in enumerate(layers):
+        hs.append(h)
+        h = layer_forward(h, W, ctx_k[l], ctx_v[l], base, anchor, cfg)
+    keep = _kept_rows(anchor, valid, int(cfg["block_size"]))
+    return np.where(keep[:, None], h, 0.0), hs
+
+
+def body_backward(emb, layers, ctx_k, ctx_v, base, anchor, valid, cfg, d_out):
+    """Gradients of body_forward given d_out = dL/dout [R, H]: the returned rows'
+    mask passes d_out to the last layer's output (zero rows pass nothing), then
+    layer_backward runs from the last layer to the first. Returns
+    (d_emb, grads, d_ctx_k, d_ctx_v), the last three lists over layers."""
+    _, hs = body_forward_layers(emb, layers, ctx_k, ctx_v, base, anchor, valid, cfg)
+    keep = _kept_rows(anchor, valid, int(cfg["block_size"]))
+    dh = np.where(keep[:, None], np.asarray(d_out, np.float64), 0.0)
+    L = len(layers)
+    grads, dcks, dcvs = [None] * L, [None] * L, [None] * L
+    for l in reversed(range(L)):
+        dh, grads[l], dcks[l], dcvs[l] = layer_backward(hs[l], layers[l], ctx_k[l], ctx_v[l], base, anchor,
+                                                        cfg, dh)
+    return dh, grads, dcks, dcvs
