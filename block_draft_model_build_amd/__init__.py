@@ -12,6 +12,7 @@ The names mirror the C entry points:
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
+  dflash_body_forward_train, dflash_body_backward, dflash_body_backward_workspace_size,
   dflash_workspace_size, dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
@@ -37,6 +38,7 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
+            "dflash_body_forward_train", "dflash_body_backward", "dflash_body_backward_workspace_size",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
@@ -44,7 +46,8 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
 KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "attention": 5,
            "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10,
            "lm_head": 11, "lm_ce": 12, "attn_bwd": 13,
-           "ctx_bwd_pack": 14, "ctx_bwd_dc": 15, "ctx_bwd_dw": 16}
+           "ctx_bwd_pack": 14, "ctx_bwd_dc": 15, "ctx_bwd_dw": 16,
+           "bwd_pack": 17, "bwd_data": 18, "bwd_weight": 19, "bwd_norm": 20}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -60,6 +63,10 @@ _LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_u
 
 
 class DFlashLayerWeights(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in _LAYER_FIELDS]
+
+
+class DFlashLayerGrads(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in _LAYER_FIELDS]
 
 
@@ -106,6 +113,12 @@ def _load() -> ctypes.CDLL:
     lib.dflash_block_attn_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_ctx_proj_backward.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, I64, I64, P, P, P, SZ, P]
     lib.dflash_ctx_proj_backward.restype = ctypes.c_int
+    lib.dflash_body_forward_train.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, P, SZ, P]
+    lib.dflash_body_forward_train.restype = ctypes.c_int
+    lib.dflash_body_backward.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.dflash_body_backward.restype = ctypes.c_int
+    lib.dflash_body_backward_workspace_size.argtypes = [CFG, I32]
+    lib.dflash_body_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_ctx_proj_backward_workspace_size.argtypes = [CFG, I64]
     lib.dflash_ctx_proj_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
@@ -354,6 +367,46 @@ def dflash_ctx_proj_backward(cfg: DFlashConfig, target_states, ts_row_stride: in
                                       int(ctx_total), int(row_offset), _ptr(d_w_proj), _ptr(d_ctx_hidden), wp, wb,
                                       _stream(stream, d_w_proj))
     _check("dflash_ctx_proj_backward", s)
+
+
+def dflash_body_forward_train(cfg: DFlashConfig, num_blocks: int, block_embeds, layers, ctx_k: List,
+                              ctx_v: List, ctx_total: int, block_ctx_base, block_anchor, block_valid, out,
+                              h_saved, workspace, stream=None) -> None:
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_body_forward_train(ctypes.byref(cfg), int(num_blocks), _ptr(block_embeds), lw, ck, cv,
+                                       int(ctx_total), _ptr(block_ctx_base), _ptr(block_anchor),
+                                       _ptr(block_valid), _ptr(out), _ptr(h_saved), wp, wb,
+                                       _stream(stream, block_embeds))
+    _check("dflash_body_forward_train", s)
+
+
+def _grads(grads: Sequence[Dict[str, object]]):
+    arr = (DFlashLayerGrads * len(grads))()
+    for i, G in enumerate(grads):
+        for f in _LAYER_FIELDS:
+            setattr(arr[i], f, _ptr(G.get(f)))
+    return arr
+
+
+def dflash_body_backward_workspace_size(cfg: DFlashConfig, num_blocks: int) -> int:
+    return _lib.dflash_body_backward_workspace_size(ctypes.byref(cfg), int(num_blocks))
+
+
+def dflash_body_backward(cfg: DFlashConfig, num_blocks: int, h_saved, layers, ctx_k: List, ctx_v: List,
+                         ctx_total: int, block_ctx_base, block_anchor, block_valid, d_out, d_block_embeds,
+                         grads: Sequence[Dict[str, object]], d_ctx_k: List, d_ctx_v: List, workspace,
+                         stream=None) -> None:
+    """grads: one dict per layer with an fp32 tensor per weight name (as the layers' dicts)."""
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    gk, gv = _ptr_array(d_ctx_k), _ptr_array(d_ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_body_backward(ctypes.byref(cfg), int(num_blocks), _ptr(h_saved), lw, ck, cv, int(ctx_total),
+                                  _ptr(block_ctx_base), _ptr(block_anchor), _ptr(block_valid), _ptr(d_out),
+                                  _ptr(d_block_embeds), _grads(grads), gk, gv, wp, wb, _stream(stream, d_out))
+    _check("dflash_body_backward", s)
 
 
 def dflash_profile_start(kernel, max_launches: int) -> None:

@@ -1108,44 +1108,13 @@ size_t bw_workspace(const dflash_config& c, int nb) { return bw_layout(c, nb).to
 
 }  // namespace
 
-}  // namespace dflash
-
-using namespace dflash;
-
-extern "C" size_t dflash_block_attn_backward_workspace_size(const dflash_config* cfg, int32_t num_blocks) {
-    if (check_config(cfg) != DFLASH_OK || num_blocks < 0) return 0;
-    return bw_workspace(*cfg, num_blocks);
-}
-
-extern "C" dflash_status dflash_block_attn_backward(
-    const dflash_config* cfg, int32_t num_blocks, const void* q, const void* k_blk, const void* v_blk,
-    const void* ctx_k, const void* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
-    const int32_t* block_anchor, const uint8_t* block_valid, const void* out, const void* d_out, float* d_q,
-    float* d_k_blk, float* d_v_blk, float* d_ctx_k, float* d_ctx_v, void* workspace, size_t workspace_bytes,
-    void* hip_stream) {
-    dflash_status s = check_config(cfg);
-    if (s != DFLASH_OK) return s;
-    if (num_blocks < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
-    if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2 || (int64_t)num_blocks * cfg->num_kv_heads > INT32_MAX ||
-        (ctx_total + 63) / 64 * cfg->num_kv_heads > INT32_MAX)
-        return DFLASH_ERR_UNSUPPORTED;
-    if (num_blocks == 0 && ctx_total == 0) return DFLASH_OK;
-    if ((num_blocks > 0 && (q == nullptr || k_blk == nullptr || v_blk == nullptr || block_ctx_base == nullptr ||
-                            block_anchor == nullptr || block_valid == nullptr || out == nullptr || d_out == nullptr ||
-                            d_q == nullptr || d_k_blk == nullptr || d_v_blk == nullptr)) ||
-        (ctx_total > 0 && (ctx_k == nullptr || ctx_v == nullptr || d_ctx_k == nullptr || d_ctx_v == nullptr)))
-        return DFLASH_ERR_INVALID_ARG;
-    // 16-byte vector loads of the inputs and stores of the gradients.
-    for (const void* p : {q, k_blk, v_blk, ctx_k, ctx_v, out, d_out, (const void*)d_q, (const void*)d_k_blk,
-                          (const void*)d_v_blk, (const void*)d_ctx_k, (const void*)d_ctx_v})
-        if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return DFLASH_ERR_INVALID_ARG;
-    const size_t need = bw_workspace(*cfg, num_blocks);
-    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return DFLASH_ERR_WORKSPACE;
+// The whole attention backward on the stream, arguments checked by the caller.
+hipError_t attn_backward_run(const dflash_config* cfg, int num_blocks, const void* q, const void* k_blk,
+                             const void* v_blk, const void* ctx_k, const void* ctx_v, int64_t ctx_total,
+                             const int64_t* block_ctx_base, const int32_t* block_anchor, const uint8_t* block_valid,
+                             const void* out, const void* d_out, float* d_q, float* d_k_blk, float* d_v_blk,
+                             float* d_ctx_k, float* d_ctx_v, char* ws, hipStream_t st) {
     const BwLayout lay = bw_layout(*cfg, num_blocks);
-    char* ws = static_cast<char*>(workspace);
-    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    hipError_t e;
     auto fill = [&](auto tag) -> hipError_t {
         using T = decltype(tag);
         BwArgs<T> a{};
@@ -1190,6 +1159,47 @@ extern "C" dflash_status dflash_block_attn_backward(
             return attn_bwd_f32(a, st);
         }
     };
-    e = cfg->dtype == DFLASH_BF16 ? fill(__bf16{}) : fill(float{});
+    return cfg->dtype == DFLASH_BF16 ? fill(__bf16{}) : fill(float{});
+}
+
+size_t attn_backward_workspace(const dflash_config& c, int nb) { return bw_layout(c, nb).total; }
+
+}  // namespace dflash
+
+using namespace dflash;
+
+extern "C" size_t dflash_block_attn_backward_workspace_size(const dflash_config* cfg, int32_t num_blocks) {
+    if (check_config(cfg) != DFLASH_OK || num_blocks < 0) return 0;
+    return bw_workspace(*cfg, num_blocks);
+}
+
+extern "C" dflash_status dflash_block_attn_backward(
+    const dflash_config* cfg, int32_t num_blocks, const void* q, const void* k_blk, const void* v_blk,
+    const void* ctx_k, const void* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
+    const int32_t* block_anchor, const uint8_t* block_valid, const void* out, const void* d_out, float* d_q,
+    float* d_k_blk, float* d_v_blk, float* d_ctx_k, float* d_ctx_v, void* workspace, size_t workspace_bytes,
+    void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (num_blocks < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)num_blocks * cfg->block_size > INT32_MAX / 2 || (int64_t)num_blocks * cfg->num_kv_heads > INT32_MAX ||
+        (ctx_total + 63) / 64 * cfg->num_kv_heads > INT32_MAX)
+        return DFLASH_ERR_UNSUPPORTED;
+    if (num_blocks == 0 && ctx_total == 0) return DFLASH_OK;
+    if ((num_blocks > 0 && (q == nullptr || k_blk == nullptr || v_blk == nullptr || block_ctx_base == nullptr ||
+                            block_anchor == nullptr || block_valid == nullptr || out == nullptr || d_out == nullptr ||
+                            d_q == nullptr || d_k_blk == nullptr || d_v_blk == nullptr)) ||
+        (ctx_total > 0 && (ctx_k == nullptr || ctx_v == nullptr || d_ctx_k == nullptr || d_ctx_v == nullptr)))
+        return DFLASH_ERR_INVALID_ARG;
+    // 16-byte vector loads of the inputs and stores of the gradients.
+    for (const void* p : {q, k_blk, v_blk, ctx_k, ctx_v, out, d_out, (const void*)d_q, (const void*)d_k_blk,
+                          (const void*)d_v_blk, (const void*)d_ctx_k, (const void*)d_ctx_v})
+        if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return DFLASH_ERR_INVALID_ARG;
+    const size_t need = bw_workspace(*cfg, num_blocks);
+    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return DFLASH_ERR_WORKSPACE;
+    hipError_t e = attn_backward_run(cfg, num_blocks, q, k_blk, v_blk, ctx_k, ctx_v, ctx_total, block_ctx_base,
+                                     block_anchor, block_valid, out, d_out, d_q, d_k_blk, d_v_blk, d_ctx_k, d_ctx_v,
+                                     static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }

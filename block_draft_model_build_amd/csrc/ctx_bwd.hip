@@ -12,6 +12,7 @@
 // are transposed on the way (LDS tiles; dC in the first product's epilogue).
 #include "gemm_select.h"
 #include "internal.h"
+#include "transpose.h"
 
 namespace dflash {
 
@@ -96,60 +97,6 @@ __global__ __launch_bounds__(256) void grad_pack_v_kernel(GradPtrs gp, int64_t r
     }
 }
 
-template <typename T> struct SrcPlain {
-    const T* p; int64_t ld;
-    __device__ const T* at(int64_t r, int64_t c) const { return p + r * ld + c; }
-};
-// Element (r, k) of the concatenated target states, as dflash_ctx_proj reads them.
-template <typename T> struct SrcStacked {
-    const T* p; int64_t rs, ls; int ht;
-    __device__ const T* at(int64_t r, int64_t c) const {
-        const int64_t layer = c / ht;
-        return p + r * rs + layer * ls + (c - layer * ht);
-    }
-};
-
-// dst[c * ldd + r] = src(r, c) for r < rows_pad (zero past rows), c < cols, in
-// 64 x 64 tiles through LDS with 16-byte loads along c and 16-byte stores
-// along r. cols is a multiple of 64; src rows hold 16-byte aligned runs of
-// V = 16 / sizeof(T) elements (a run never straddles two target layers);
-// ldd and the column offset of dst keep 16-byte alignment.
-template <typename T, class Src>
-__global__ __launch_bounds__(256) void transpose_kernel(Src src, int64_t rows, int64_t rows_pad, int64_t cols, T* dst,
-                                                        int64_t ldd) {
-    constexpr int V = 16 / (int)sizeof(T);
-    typedef T vec __attribute__((ext_vector_type(V)));
-    __shared__ float tile[64][65];
-    const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-    for (int idx = threadIdx.x; idx < 64 * (64 / V); idx += 256) {
-        const int rr = idx / (64 / V), cv = (idx - rr * (64 / V)) * V;
-        const int64_t r = r0 + rr;
-        vec v = {};
-        if (r < rows) v = *reinterpret_cast<const vec*>(src.at(r, c0 + cv));
-#pragma unroll
-        for (int q = 0; q < V; ++q) tile[rr][cv + q] = to_f32(v[q]);
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * (64 / V); idx += 256) {
-        const int cc = idx / (64 / V), rv = (idx - cc * (64 / V)) * V;
-        const int64_t r = r0 + rv;
-        if (r >= rows_pad) continue;
-        vec v;
-#pragma unroll
-        for (int q = 0; q < V; ++q) v[q] = from_f32<T>(tile[rv + q][cc]);
-        *reinterpret_cast<vec*>(dst + (c0 + cc) * ldd + r) = v;
-    }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void fill_cols_kernel(T* p, int64_t ld, int64_t nrows, int64_t c0, int64_t c1) {
-    const int64_t w = c1 - c0, n = nrows * w;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int64_t r = i / w;
-        p[r * ld + c0 + (i - r * w)] = from_f32<T>(0.f);
-    }
-}
-
 // dC: transposed store (dC^T [H][ldt], the A operand of dW_proj) and, when
 // asked for, the fp32 gradient itself [T][H].
 template <typename T> struct EpDCT {
@@ -168,23 +115,6 @@ template <typename T> struct EpDCT {
                     dct[(int64_t)col * ldt + row] = from_f32<T>(acc[i][j][e]);
                     if (dch) dch[(int64_t)row * ldh + col] = acc[i][j][e];
                 }
-            }
-    }
-};
-
-struct EpStoreF32 {
-    float* out; int64_t ldo;
-    template <int MI, int NI, int WN>
-    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = mb + i * 32 + acc_row(e, lane);
-                if (row >= M) continue;
-                float* o = out + (int64_t)row * ldo + nb + (lane & 31);
-#pragma unroll
-                for (int j = 0; j < NI; ++j) o[j * 32] = acc[i][j][e];
             }
     }
 };

@@ -6,146 +6,14 @@
 
 #include <mutex>
 
-#include "attention.h"
+#include "attn_launch.h"
 #include "common.h"
 #include "gemm.h"
 #include "gemm_select.h"
 #include "internal.h"
+#include "norm.h"
 
 namespace dflash {
-
-// ------------------------------------------------------------------ RMSNorm
-// out[row] = x / sqrt(mean(x^2) + eps) * w, x read as fp32; optionally copies
-// x into the fp32 residual stream (first layer: embeddings -> h). 16-byte
-// loads; rows of up to 256 * 4 vectors stay in registers between the sum and
-// the scaling (H = 4096 in fp32), together with their weights, which are read
-// before the reduction so that a row costs one memory round trip; longer rows
-// are read twice.
-template <typename TIN, typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in, float* __restrict__ hcopy,
-                                                      const T* __restrict__ w, T* __restrict__ out, int H,
-                                                      float eps) {
-    constexpr int VI = 16 / (int)sizeof(TIN);     // elements per 16-byte load
-    constexpr int NV = 4;                         // vectors per thread kept in registers
-    typedef TIN vin __attribute__((ext_vector_type(VI)));
-    typedef T vout __attribute__((ext_vector_type(VI)));
-    typedef float vf32 __attribute__((ext_vector_type(VI)));
-    __shared__ float red[4];
-    const int64_t row = blockIdx.x;
-    const TIN* x = in + row * H;
-    const int nvec = H / VI;
-    const bool cached = nvec <= 256 * NV;
-    vin v[NV];
-    vout wv[NV];
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int j = threadIdx.x + 256 * k;
-        if (j < nvec) {
-            v[k] = reinterpret_cast<const vin*>(x)[j];
-            wv[k] = reinterpret_cast<const vout*>(w)[j];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int j = threadIdx.x + 256 * k;
-        if (j < nvec) {
-#pragma unroll
-            for (int q = 0; q < VI; ++q) ss += to_f32(v[k][q]) * to_f32(v[k][q]);
-        }
-    }
-    if (!cached)
-        for (int j = threadIdx.x + 256 * NV; j < nvec; j += 256) {
-            const vin u = reinterpret_cast<const vin*>(x)[j];
-#pragma unroll
-            for (int q = 0; q < VI; ++q) ss += to_f32(u[q]) * to_f32(u[q]);
-        }
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
-    const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    auto emit = [&](int j, const vin& u, const vout& ww) {
-        vout o;
-        vf32 hc;
-#pragma unroll
-        for (int q = 0; q < VI; ++q) {
-            const float f = to_f32(u[q]);
-            o[q] = from_f32<T>(f * r * to_f32(ww[q]));
-            hc[q] = f;
-        }
-        if (hcopy) reinterpret_cast<vf32*>(hcopy + row * H)[j] = hc;
-        reinterpret_cast<vout*>(out + row * H)[j] = o;
-    };
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int j = threadIdx.x + 256 * k;
-        if (j < nvec) emit(j, v[k], wv[k]);
-    }
-    if (!cached)
-        for (int j = threadIdx.x + 256 * NV; j < nvec; j += 256)
-            emit(j, reinterpret_cast<const vin*>(x)[j], reinterpret_cast<const vout*>(w)[j]);
-}
-
-// ------------------------------------------------------------------ attention launch
-template <typename T, int D, int QC>
-static hipError_t attn_launch_t(const dflash_config& c, const AttnArgs<T>& a, int nb, hipStream_t st) {
-    const int items_max = attn_items_max(c, nb);
-    {
-        ProfScope prof(DFLASH_KERNEL_ATTENTION, st);
-        hipLaunchKernelGGL((block_attn_kernel<T, D, QC>), dim3(items_max), dim3(256), 0, st, a);
-        hipLaunchKernelGGL((block_attn_kernel<T, D, QC, true>), dim3(items_max), dim3(256), 0, st, a);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    {
-        ProfScope prof(DFLASH_KERNEL_ATTN_COMBINE, st);
-        hipLaunchKernelGGL((attn_combine_kernel<T, D, QC>), dim3(nb, c.num_kv_heads), dim3(256), 0, st, a);
-    }
-    return hipGetLastError();
-}
-
-template <typename T>
-static hipError_t attn_launch(const dflash_config& c, const AttnArgs<T>& a, int nb, hipStream_t st) {
-    constexpr int D = 256 / (int)sizeof(T);
-    if (attn_qcols(c) == 32) return attn_launch_t<T, D, 32>(c, a, nb, st);
-    return attn_launch_t<T, D, 64>(c, a, nb, st);
-}
-
-template <typename T>
-static AttnArgs<T> attn_args(const dflash_config& c, int nb, const T* q, int64_t q_ld, const T* kb,
-                             const T* vb, int64_t kv_ld, const T* ck, const T* cvt, int64_t ctx_total,
-                             const int64_t* base, const int32_t* anchor, const uint8_t* valid, T* out,
-                             int64_t out_ld, char* ws, const Workspace& w) {
-    AttnArgs<T> a;
-    a.q = q; a.q_ld = q_ld; a.kb = kb; a.vb = vb; a.kv_ld = kv_ld;
-    a.ck = ck; a.cvt = cvt; a.ctx_total = ctx_total;
-    a.base = base; a.anchor = anchor; a.valid = valid;
-    a.out = out; a.out_ld = out_ld;
-    a.nb = nb; a.bs = c.block_size; a.hq = c.num_q_heads; a.hkv = c.num_kv_heads;
-    a.qscale = (float)(1.4426950408889634 / sqrt((double)c.head_dim));
-    a.group_start = reinterpret_cast<const int*>(ws + w.group_start);
-    a.item_start = reinterpret_cast<const int*>(ws + w.item_start);
-    a.sched = reinterpret_cast<const int*>(ws + w.sched);
-    a.meta = reinterpret_cast<const int*>(ws + w.meta);
-    a.bmeta = reinterpret_cast<const int4*>(ws + w.bmeta);
-    a.part_o = reinterpret_cast<float*>(ws + w.part_o);
-    a.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
-    a.redo = reinterpret_cast<int*>(ws + w.redo);
-    a.rt = make_rope_turns(c);
-    return a;
-}
-
-static hipError_t attn_schedule(const dflash_config& c, int nb, const int64_t* base, const int32_t* anchor,
-                                int64_t ctx_total, char* ws, const Workspace& w, hipStream_t st) {
-    const int hkv = c.num_kv_heads;
-    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, base, anchor, nb, ctx_total,
-                       (kAttnItemsShared + hkv - 1) / hkv, (kAttnItemsSingle + hkv - 1) / hkv,
-                       reinterpret_cast<int*>(ws + w.group_start),
-                       reinterpret_cast<int*>(ws + w.item_start), reinterpret_cast<int*>(ws + w.sched),
-                       reinterpret_cast<int*>(ws + w.meta), reinterpret_cast<int4*>(ws + w.bmeta));
-    return hipGetLastError();
-}
 
 // ------------------------------------------------------------------ typed bodies
 template <typename T>
@@ -178,10 +46,14 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     return gemm<T>(DFLASH_KERNEL_CTX_KV, M, N, H, APlain<T>{C, H}, b, ep, st);
 }
 
+// hs (optional): [num_layers][R][H] fp32; when given, layer l reads its input
+// residual from hs[l] and writes its output to hs[l + 1] (the workspace's h for
+// the last layer), so every layer's input survives for the backward.
 template <typename T>
 static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dflash_layer_weights* layers,
                          void* const* ck, void* const* cv, int64_t ctx_total, const int64_t* base,
-                         const int32_t* anchor, const uint8_t* valid, T* out, char* ws, hipStream_t st) {
+                         const int32_t* anchor, const uint8_t* valid, T* out, float* hs, char* ws,
+                         hipStream_t st) {
     const Workspace w = workspace_layout(c, nb, 0);
     const int R = nb * c.block_size, H = c.hidden, D = c.head_dim;
     const int nq = c.num_q_heads * D, nk = c.num_kv_heads * D, nqkv = nq + 2 * nk, I = c.intermediate;
@@ -192,15 +64,18 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
     T* u = reinterpret_cast<T*>(ws + w.u);
     hipError_t e = attn_schedule(c, nb, base, anchor, ctx_total, ws, w, st);
     if (e != hipSuccess) return e;
+    const int64_t RH = (int64_t)R * H;
     for (int l = 0; l < c.num_layers; ++l) {
         const dflash_layer_weights& L = layers[l];
+        float* hin = hs ? hs + l * RH : h;                                  // residual entering layer l
+        float* hout = hs && l + 1 < c.num_layers ? hs + (l + 1) * RH : h;   // ... and leaving it
         {
             ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
             if (l == 0)
-                hipLaunchKernelGGL((rmsnorm_kernel<T, T>), dim3(R), dim3(256), 0, st, emb, h,
+                hipLaunchKernelGGL((rmsnorm_kernel<T, T>), dim3(R), dim3(256), 0, st, emb, hin,
                                    static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
             else
-                hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
+                hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, hin, (float*)nullptr,
                                    static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -215,12 +90,17 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
                                      static_cast<const T*>(ck[l]), static_cast<const T*>(cv[l]), ctx_total,
                                      base, anchor, nullptr, att, nq, ws, w);
         if ((e = attn_launch<T>(c, a, nb, st)) != hipSuccess) return e;
-        e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq}, BPlain<T>{static_cast<const T*>(L.wo), nq},
-                    EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0}, st);
+        if (hin == hout)
+            e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq},
+                        BPlain<T>{static_cast<const T*>(L.wo), nq}, EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0},
+                        st);
+        else
+            e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq},
+                        BPlain<T>{static_cast<const T*>(L.wo), nq}, EpAddF32{hin, hout, H}, st);
         if (e != hipSuccess) return e;
         {
             ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
-            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h, (float*)nullptr,
+            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, hout, (float*)nullptr,
                                static_cast<const T*>(L.mlp_norm), x, H, c.rms_eps);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -230,7 +110,7 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
         if (e != hipSuccess) return e;
         const bool last = l + 1 == c.num_layers;
         e = gemm<T>(DFLASH_KERNEL_DOWN, R, H, I, APlain<T>{u, I}, BPlain<T>{static_cast<const T*>(L.w_down), I},
-                    EpResidual<T>{h, H, last ? out : nullptr, valid, anchor, c.block_size}, st);
+                    EpResidual<T>{hout, H, last ? out : nullptr, valid, anchor, c.block_size}, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -616,11 +496,11 @@ extern "C" dflash_status dflash_block_attn(const dflash_config* cfg, int32_t num
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
-extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t num_blocks, const void* block_embeds,
-                                             const dflash_layer_weights* layers, void* const* ctx_k,
-                                             void* const* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
-                                             const int32_t* block_anchor, const uint8_t* block_valid, void* out,
-                                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+static dflash_status body_entry(const dflash_config* cfg, int32_t num_blocks, const void* block_embeds,
+                                const dflash_layer_weights* layers, void* const* ctx_k, void* const* ctx_v,
+                                int64_t ctx_total, const int64_t* block_ctx_base, const int32_t* block_anchor,
+                                const uint8_t* block_valid, void* out, float* h_saved, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
     if (num_blocks < 0 || ctx_total < 0) return DFLASH_ERR_INVALID_ARG;
@@ -628,7 +508,7 @@ extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t n
     if (num_blocks == 0) return DFLASH_OK;
     if (block_embeds == nullptr || layers == nullptr || ctx_k == nullptr || ctx_v == nullptr ||
         block_ctx_base == nullptr || block_anchor == nullptr || block_valid == nullptr || out == nullptr ||
-        !aligned16(block_embeds))
+        !aligned16(block_embeds) || !aligned16(h_saved))
         return DFLASH_ERR_INVALID_ARG;
     for (int l = 0; l < cfg->num_layers; ++l) {
         const dflash_layer_weights& L = layers[l];
@@ -645,9 +525,31 @@ extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t n
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = body_t<__bf16>(*cfg, num_blocks, static_cast<const __bf16*>(block_embeds), layers, ctx_k, ctx_v,
-                           ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<__bf16*>(out), ws, st);
+                           ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<__bf16*>(out), h_saved,
+                           ws, st);
     else
         e = body_t<float>(*cfg, num_blocks, static_cast<const float*>(block_embeds), layers, ctx_k, ctx_v,
-                          ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<float*>(out), ws, st);
+                          ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<float*>(out), h_saved,
+                          ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t num_blocks, const void* block_embeds,
+                                             const dflash_layer_weights* layers, void* const* ctx_k,
+                                             void* const* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
+                                             const int32_t* block_anchor, const uint8_t* block_valid, void* out,
+                                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return body_entry(cfg, num_blocks, block_embeds, layers, ctx_k, ctx_v, ctx_total, block_ctx_base, block_anchor,
+                      block_valid, out, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" dflash_status dflash_body_forward_train(const dflash_config* cfg, int32_t num_blocks,
+                                                   const void* block_embeds, const dflash_layer_weights* layers,
+                                                   void* const* ctx_k, void* const* ctx_v, int64_t ctx_total,
+                                                   const int64_t* block_ctx_base, const int32_t* block_anchor,
+                                                   const uint8_t* block_valid, void* out, float* h_saved,
+                                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (h_saved == nullptr && num_blocks > 0) return DFLASH_ERR_INVALID_ARG;
+    return body_entry(cfg, num_blocks, block_embeds, layers, ctx_k, ctx_v, ctx_total, block_ctx_base, block_anchor,
+                      block_valid, out, h_saved, workspace, workspace_bytes, hip_stream);
 }

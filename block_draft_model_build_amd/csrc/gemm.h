@@ -168,6 +168,146 @@ template <typename T> struct EpSwiGLU {
     }
 };
 
+// dst[row, col] = src[row, col] + acc (fp32 residual stream written to a new
+// buffer: the layer's input stays intact for the backward).
+struct EpAddF32 {
+    const float* src; float* dst; int64_t ld;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                const int64_t o = (int64_t)row * ld + nb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) dst[o + j * 32] = src[o + j * 32] + acc[i][j][e];
+            }
+    }
+};
+
+// The Q|K|V product (BQKV column order) stored as three packed matrices
+// q [rows][nq], k [rows][nk], v [rows][nk]. nq and nk are multiples of 32, so a
+// 32-column tile lies in one of them.
+template <typename T> struct EpSplitQKV {
+    T *q, *k, *v; int nq, nk;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int c = nb + j * 32;
+            T* base;
+            int64_t ld;
+            if (c < nq) { base = q + c; ld = nq; }
+            else if (c < nq + nk) { base = k + (c - nq); ld = nk; }
+            else { base = v + (c - nq - nk); ld = nk; }
+            base += lane & 31;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = mb + i * 32 + acc_row(e, lane);
+                    if (row < M) base[(int64_t)row * ld] = from_f32<T>(acc[i][j][e]);
+                }
+        }
+    }
+};
+
+// EpSwiGLU that also keeps the fp32 pre-activations gate[row, c] and
+// up[row, c] (ld ldu) for the backward.
+template <typename T> struct EpSwiGLUSave {
+    T* u; float* gate; float* up; int64_t ldu;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+        static_assert(NI % 2 == 0, "gate and up halves");
+        const int c0 = (nb / WN) * (WN / 2) + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                const int64_t o = (int64_t)row * ldu + c0;
+#pragma unroll
+                for (int j = 0; j < NI / 2; ++j) {
+                    float g = acc[i][j][e], p = acc[i][j + NI / 2][e];
+                    u[o + j * 32] = from_f32<T>(g / (1.f + __expf(-g)) * p);
+                    gate[o + j * 32] = g;
+                    up[o + j * 32] = p;
+                }
+            }
+    }
+};
+
+// Backward of u = SiLU(g) * up through the product du = dh W_down (acc = du at
+// [row, c], c < I): with s = sigmoid(g),
+//   dg = du * up * s * (1 + g (1 - s)),  dup = du * g * s,
+// stored side by side, dgu[row, c] = dg and dgu[row, I + c] = dup (ld 2I).
+template <typename T> struct EpSwiGLUBwd {
+    const float* gate; const float* up; T* dgu; int I;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                const int c = nb + (lane & 31);
+                const float* gp = gate + (int64_t)row * I + c;
+                const float* up_ = up + (int64_t)row * I + c;
+                T* o = dgu + (int64_t)row * 2 * I + c;
+#pragma unroll
+                for (int j = 0; j < NI; ++j) {
+                    const float g = gp[j * 32], p = up_[j * 32], du = acc[i][j][e];
+                    const float s = 1.f / (1.f + __expf(-g));
+                    o[j * 32] = from_f32<T>(du * p * s * (1.f + g * (1.f - s)));
+                    o[I + j * 32] = from_f32<T>(du * g * s);
+                }
+            }
+    }
+};
+
+// fp32 rows split over up to three outputs: rows [0, s1) -> out0, [s1, s2) ->
+// out1, [s2, M) -> out2, each [rows][ld] (stacked weight gradients).
+struct EpStoreF32Rows3 {
+    float* out0; float* out1; float* out2; int s1, s2; int64_t ld;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                float* o = row < s1 ? out0 + (int64_t)row * ld
+                                    : row < s2 ? out1 + (int64_t)(row - s1) * ld : out2 + (int64_t)(row - s2) * ld;
+                o += nb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) o[j * 32] = acc[i][j][e];
+            }
+    }
+};
+
+// out[row, col] = acc in fp32.
+struct EpStoreF32 {
+    float* out; int64_t ldo;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                float* o = out + (int64_t)row * ldo + nb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) o[j * 32] = acc[i][j][e];
+            }
+    }
+};
+
 // Block LM head with a fused softmax statistic: for every row, the maximum
 // and sum of exp(z - max) over each WN-column group of logits z (columns past
 // n_cols excluded), written to part[row][group], and the logit of the row's

@@ -36,6 +36,9 @@ using MidWideDeep = TileCfg<128, 192, 4, 1, 128, 4>;
 template <class EP> struct AnyWaveWidth : std::false_type {};
 template <typename T> struct AnyWaveWidth<EpStore<T>> : std::true_type {};
 template <typename T> struct AnyWaveWidth<EpResidual<T>> : std::true_type {};
+template <> struct AnyWaveWidth<EpAddF32> : std::true_type {};
+template <typename T> struct AnyWaveWidth<EpSplitQKV<T>> : std::true_type {};
+template <typename T> struct AnyWaveWidth<EpSwiGLUBwd<T>> : std::true_type {};
 static_assert(BigTile::WN == 128 && MidTile::WN == 128 && MidDeep::WN == 128, "gate/up interleave and RoPE pairing assume WN = 128");
 
 // `group`: row tiles walked together in the tile order (gemm_nt_kernel). 8 by

@@ -90,6 +90,17 @@ inline RopeTurns make_rope_turns(const dflash_config& c) {
 
 dflash_status check_config(const dflash_config* c);
 
+// The attention backward (attn_bwd.hip) for callers that checked the arguments:
+// the kernels of dflash_block_attn_backward on `st`, with `ws` holding
+// attn_backward_workspace(c, nb) bytes. A null block_valid keeps every row's
+// output gradient (inside the body no row's attention output is zeroed).
+hipError_t attn_backward_run(const dflash_config* cfg, int num_blocks, const void* q, const void* k_blk,
+                             const void* v_blk, const void* ctx_k, const void* ctx_v, int64_t ctx_total,
+                             const int64_t* block_ctx_base, const int32_t* block_anchor, const uint8_t* block_valid,
+                             const void* out, const void* d_out, float* d_q, float* d_k_blk, float* d_v_blk,
+                             float* d_ctx_k, float* d_ctx_v, char* ws, hipStream_t st);
+size_t attn_backward_workspace(const dflash_config& c, int nb);
+
 // Records the measurement hook's events around the launches made in its scope
 // when `kernel` is the kernel being profiled (dflash_profile_start).
 class ProfScope {

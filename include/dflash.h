@@ -324,7 +324,11 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_CTX_BWD_PACK = 14, /* dflash_ctx_proj_backward: gradient packing and transposes */
     DFLASH_KERNEL_CTX_BWD_DC = 15,   /* GEMM dC = G [Wk; Wv] */
     DFLASH_KERNEL_CTX_BWD_DW = 16,   /* GEMM dW_proj = dC^T X */
-    DFLASH_KERNEL_COUNT = 17
+    DFLASH_KERNEL_BWD_PACK = 17,     /* dflash_body_backward: transposes, casts, gradient mask */
+    DFLASH_KERNEL_BWD_DATA = 18,     /* GEMMs of the activation gradients (du, dy, do, dx) */
+    DFLASH_KERNEL_BWD_WEIGHT = 19,   /* GEMMs of the weight gradients (contraction over rows) */
+    DFLASH_KERNEL_BWD_NORM = 20,     /* RMSNorm backward and its weight-gradient column sums */
+    DFLASH_KERNEL_COUNT = 21
 } dflash_kernel;
 
 /*
@@ -500,6 +504,81 @@ dflash_status dflash_ctx_proj_backward(const dflash_config *cfg, const void *tar
                                        float *d_ctx_hidden, void *workspace, size_t workspace_bytes,
                                        void *hip_stream);
 size_t dflash_ctx_proj_backward_workspace_size(const dflash_config *cfg, int64_t num_rows);
+
+/*
+ * dflash_body_forward_train -- dflash_body_forward for a training step: the same
+ * arithmetic and the same `out` (bit for bit), and in addition every layer's
+ * input residual stream, kept for dflash_body_backward.
+ *
+ *   h_saved  device f32 [num_layers][nb*bs, H]: h_saved[l] = the fp32 residual
+ *            stream entering layer l (h_saved[0] = block_embeds as fp32)
+ * Other arguments, errors and workspace as dflash_body_forward; INVALID_ARG
+ * also for a null or misaligned h_saved.
+ */
+dflash_status dflash_body_forward_train(const dflash_config *cfg, int32_t num_blocks,
+                                        const void *block_embeds, const dflash_layer_weights *layers,
+                                        void *const *ctx_k, void *const *ctx_v, int64_t ctx_total,
+                                        const int64_t *block_ctx_base, const int32_t *block_anchor,
+                                        const uint8_t *block_valid, void *out, float *h_saved,
+                                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Gradients of one draft layer's weights (device f32, the shapes of
+ * dflash_layer_weights). */
+typedef struct dflash_layer_grads {
+    float *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} dflash_layer_grads;
+
+/*
+ * dflash_body_backward -- gradients of dflash_body_forward with respect to every
+ * layer weight, the block embeddings and every layer's context caches. [P2]
+ * "How It Works", step 1 and "Scope": the body is trained with an optimizer
+ * step; step 3: the layers it differentiates; step 4: rows returned as zero
+ * pass no gradient.
+ *
+ * d_out is the gradient of `out`. It reaches the last layer's output on the
+ * rows the body returns (valid, non-empty block); then, from the last layer to
+ * the first, each layer recomputes its forward from h_saved[l] and applies
+ *   d_w_down = dh^T u,  du = dh W_down,  (dg, dup) = SwiGLU backward at (g, up)
+ *   d_w_gate = dg^T y,  d_w_up = dup^T y,  dy = dg W_gate + dup W_up
+ *   dh1 = dh + RMSNorm backward (h1, mlp_norm) at dy           -> d_mlp_norm
+ *   d_wo = dh1^T o,  do = dh1 Wo,  (dq, dk, dv, dKc, dVc) = attention backward at do
+ *   d_wq|d_wk|d_wv = [dq|dk|dv]^T x,  dx = dq Wq + dk Wk + dv Wv
+ *   dh_in = dh1 + RMSNorm backward (h, attn_norm) at dx         -> d_attn_norm
+ * where x, y are the normalised inputs, g, up the SwiGLU pre-activations,
+ * u = SiLU(g) up and o the attention output of the forward. RMSNorm backward of
+ * y = x r w (r = (mean(x^2) + eps)^-1/2) at dy is r (dy w) - x r^3 sum(dy w x) / H,
+ * with weight gradient sum over rows of dy x r. The attention backward is
+ * dflash_block_attn_backward's, with no row's output gradient dropped (inside
+ * the body invalid rows keep their attention output).
+ *
+ *   h_saved         device f32 [num_layers][nb*bs, H] from dflash_body_forward_train
+ *   layers, ctx_k, ctx_v, ctx_total, block_ctx_base, block_anchor, block_valid
+ *                   as dflash_body_forward
+ *   d_out           device [nb*bs, H] in the config dtype
+ *   d_block_embeds  device f32 [nb*bs, H], or NULL (not returned)
+ *   grads           host array [num_layers]; every pointer device f32, 16-byte
+ *                   aligned, overwritten
+ *   d_ctx_k, d_ctx_v  host arrays [num_layers] of device f32 gradients in the
+ *                   caches' layouts (K [Hkv][ctx_total][D] rotated frame, V
+ *                   [Hkv][D][ctx_total]), overwritten; dflash_ctx_proj_backward
+ *                   takes them on to W_proj
+ *   workspace       dflash_body_backward_workspace_size(cfg, nb) bytes, 256-byte aligned
+ * GEMM operands are in the config dtype (activation gradients are rounded to it
+ * before their products); products accumulate in fp32; the residual-stream
+ * gradient, the RMSNorm backward and every output are fp32. Deterministic: no
+ * atomics, fixed reduction orders. With nb == 0 every output is zero.
+ * Errors: as dflash_body_forward; INVALID_ARG for null required pointers or
+ * misaligned arrays; UNSUPPORTED when intermediate is not a multiple of 128 or
+ * hidden exceeds 8192; WORKSPACE as usual.
+ */
+dflash_status dflash_body_backward(const dflash_config *cfg, int32_t num_blocks, const float *h_saved,
+                                   const dflash_layer_weights *layers, void *const *ctx_k, void *const *ctx_v,
+                                   int64_t ctx_total, const int64_t *block_ctx_base,
+                                   const int32_t *block_anchor, const uint8_t *block_valid, const void *d_out,
+                                   float *d_block_embeds, const dflash_layer_grads *grads,
+                                   float *const *d_ctx_k, float *const *d_ctx_v, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+size_t dflash_body_backward_workspace_size(const dflash_config *cfg, int32_t num_blocks);
 
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one

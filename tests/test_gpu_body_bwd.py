@@ -1,0 +1,280 @@
+"""dflash_body_forward_train and dflash_body_backward vs the oracle's body
+backward (NeMo RL "DFlash Draft Body", How It Works, steps 1, 3 and 4, and
+Scope: the body is trained with an optimizer step). The oracle's backward is
+pinned by central differences of its forward (tests/test_oracle_body_backward.py).
+
+Context caches come from dflash_ctx_proj on the GPU; the oracle projects its
+own from the target states. Each sequence's blocks are differentiated by the
+oracle on their own (blocks never read each other), so weight gradients are
+the sums of the per-sequence results and context gradients of a sequence sit
+in its own cache rows.
+
+Tolerance. fp32: every product is fp32 with fp32 accumulation, so the bar is
+the forward's fp32 bar relative to each gradient's scale (rel-L2 1e-5). bf16:
+weights and activations enter their products in bf16 as in the forward, and
+each activation gradient (dh, dg|dup, dh1, do, dq|dk|dv) is rounded to bf16
+once before its products. A gradient element is then a sum of products whose
+factors carry a few roundings of unit 2^-9 each, composed through at most two
+layers' chains in these tests, so rel-L2 stays at a few units of 2^-9 x the
+number of rounded factors on the path: rel-L2 3e-2 and max-abs 6e-2 of the
+tensor's largest magnitude bound it with room."""
+import numpy as np
+import pytest
+import torch
+
+import block_draft_model_build_amd as d
+import oracle
+from dflash_synth import WORKLOADS, Rng, make_training_inputs, scaled
+from tests.helpers import TrainingRun, layers64, np64, oracle_cfg, oracle_row_context
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+F32_GRAD = dict(rel_l2=1e-5, max_rel=1e-4)
+BF16_GRAD = dict(rel_l2=3e-2, max_rel=6e-2)
+
+
+def _tol(w):
+    return F32_GRAD if w.dtype == "f32" else BF16_GRAD
+
+
+def _cmp(gpu, ref, tol, what):
+    g = np64(gpu).reshape(ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = g - ref
+    rel = float(np.sqrt((err * err).sum()) / (np.sqrt((ref * ref).sum()) or 1.0))
+    mx = float(np.abs(err).max()) if err.size else 0.0
+    assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3e} > {tol['rel_l2']}"
+    assert mx <= tol["max_rel"] * max(scale, 1e-30), f"{what}: max-abs {mx:.3e} > {tol['max_rel']} x {scale:.3e}"
+    return rel
+
+
+class TrainStep:
+    """Plan + context projection + training forward + body backward on the GPU."""
+
+    def __init__(self, w, inp, anchors=None, valid=None, d_out=None):
+        self.w, self.inp = w, inp
+        self.run = TrainingRun(d, w, inp)
+        self.run.plan()
+        if anchors is not None:
+            self.run.anchors.copy_(torch.from_numpy(anchors))
+            self.run.valid.copy_(torch.from_numpy(valid))
+        self.run.ctx_proj()
+        R = w.num_blocks * w.block_size
+        L, H = w.num_layers, w.hidden
+        dev = "cuda"
+        self.h_saved = torch.full((L, R, H), float("nan"), dtype=torch.float32, device=dev)
+        self.out = torch.empty((R, H), dtype=w.torch_dtype, device=dev)
+        if d_out is None:
+            d_out = Rng(w.seed + 17, dev).normal("body.d_out", (R, H), dtype=w.torch_dtype)
+        self.d_out = d_out
+        nan = float("nan")
+        self.grads = [{k: torch.full(tuple(v.shape), nan, dtype=torch.float32, device=dev) for k, v in Lw.items()}
+                      for Lw in inp["layers"]]
+        T = self.run.T
+        self.dck = [torch.full((w.num_kv_heads, T, w.head_dim), nan, dtype=torch.float32, device=dev)
+                    for _ in range(L)]
+        self.dcv = [torch.full((w.num_kv_heads, w.head_dim, T), nan, dtype=torch.float32, device=dev)
+                    for _ in range(L)]
+        self.demb = torch.full((R, H), nan, dtype=torch.float32, device=dev)
+        self.bws = torch.empty(d.dflash_body_backward_workspace_size(self.run.cfg, w.num_blocks),
+                               dtype=torch.uint8, device=dev)
+
+    def forward(self):
+        r, w = self.run, self.w
+        d.dflash_body_forward_train(r.cfg, w.num_blocks, self.inp["emb"], self.inp["layers"], r.ctx_k, r.ctx_v,
+                                    r.T, r.base, r.anchors.reshape(-1), r.valid.reshape(-1), self.out,
+                                    self.h_saved, r.ws)
+
+    def backward(self):
+        r, w = self.run, self.w
+        d.dflash_body_backward(r.cfg, w.num_blocks, self.h_saved, self.inp["layers"], r.ctx_k, r.ctx_v, r.T,
+                               r.base, r.anchors.reshape(-1), r.valid.reshape(-1), self.d_out, self.demb,
+                               self.grads, self.dck, self.dcv, self.bws)
+
+    def all(self):
+        self.forward()
+        self.backward()
+        torch.cuda.synchronize()
+        return self
+
+
+def oracle_backward(w, inp, anchors, valid, d_out, blocks):
+    """Oracle gradients of the chosen blocks, sequence by sequence: d_emb rows of
+    those blocks, weight gradients summed over the sequences, and per sequence
+    the context gradients of its rows [0, max anchor)."""
+    bs, N = w.block_size, w.anchors_per_row
+    layers = layers64(inp["layers"])
+    by_row = {}
+    for n in blocks:
+        by_row.setdefault(n // N, []).append(n)
+    d_emb, grads, ctx = {}, None, {}
+    for b, ns in by_row.items():
+        a = np.array([int(anchors.reshape(-1)[n]) for n in ns])
+        amax = max(int(a.max()), 1)
+        ck, cv = oracle_row_context(w, inp, b, amax, layers)
+        rows = np.concatenate([np.arange(n * bs, (n + 1) * bs) for n in ns])
+        e = np64(inp["emb"][torch.from_numpy(rows).to(inp["emb"].device)])
+        v = valid.reshape(-1)[rows]
+        de, g, dck, dcv = oracle.body_backward(e, layers, ck, cv, np.zeros(len(ns), np.int64), a, v,
+                                               oracle_cfg(w), np64(d_out[torch.from_numpy(rows).to(d_out.device)]))
+        for i, n in enumerate(ns):
+            d_emb[n] = de[i * bs:(i + 1) * bs]
+        grads = g if grads is None else [{k: grads[l][k] + g[l][k] for k in NAMES} for l in range(len(g))]
+        ctx[b] = (amax, dck, dcv)
+    return d_emb, grads, ctx
+
+
+def _check(step, blocks, d_emb, grads, ctx, tol):
+    w = step.w
+    bs, S = w.block_size, w.seq_len
+    for l in range(w.num_layers):
+        for k in NAMES:
+            _cmp(step.grads[l][k], grads[l][k], tol, f"layer {l} d_{k}")
+    rows = torch.from_numpy(np.concatenate([np.arange(n * bs, (n + 1) * bs) for n in blocks])).cuda()
+    _cmp(step.demb[rows], np.concatenate([d_emb[n] for n in blocks]), tol, "d_block_embeds")
+    for b, (amax, dck, dcv) in ctx.items():
+        for l in range(w.num_layers):
+            _cmp(step.dck[l][:, b * S: b * S + amax], dck[l], tol, f"d_ctx_k layer {l} sequence {b}")
+            _cmp(step.dcv[l][:, :, b * S: b * S + amax], dcv[l].transpose(0, 2, 1), tol,
+                 f"d_ctx_v layer {l} sequence {b}")
+            assert (step.dck[l][:, b * S + amax:(b + 1) * S] == 0).all()
+            assert (step.dcv[l][:, :, b * S + amax:(b + 1) * S] == 0).all()
+
+
+def _invalid_rows_case(w):
+    """Short prefixes with invalid positions inside every live block, one empty block per sequence."""
+    B, N, bs = w.batch, w.anchors_per_row, w.block_size
+    anchors = np.full((B, N), -1, np.int32)
+    valid = np.zeros((B, N, bs), np.uint8)
+    for b in range(B):
+        for i, a in enumerate([1 + b, 6 + 3 * b, 19 + b, 40 + 7 * b, 77][:N - 1]):
+            anchors[b, i] = a
+            valid[b, i] = 1
+            valid[b, i, [2 + i, 5, bs - 1]] = 0
+    return anchors, valid
+
+
+C1X2 = scaled(WORKLOADS["c1"], num_layers=2, anchors_per_row=4)
+SMALL_BF16 = scaled(WORKLOADS["c3"], batch=2, seq_len=300, num_target_layers=2, target_hidden=128,
+                    hidden=256, num_q_heads=4, num_kv_heads=2, intermediate=512, num_layers=2,
+                    block_size=16, anchors_per_row=6, seed=77)
+
+
+def test_training_forward_keeps_layer_inputs():
+    w = C1X2
+    inp = make_training_inputs(w, "cuda")
+    step = TrainStep(w, inp)
+    step.forward()
+    step.run.body()
+    torch.cuda.synchronize()
+    assert torch.equal(step.out, step.run.out)                   # same arithmetic, bit for bit
+    anchors = step.run.anchors.cpu().numpy()
+    valid = step.run.valid.cpu().numpy()
+    layers = layers64(inp["layers"])
+    bs, N = w.block_size, w.anchors_per_row
+    ns = list(range(N))
+    ck, cv = oracle_row_context(w, inp, 0, max(int(anchors.max()), 1), layers)
+    _, hs = oracle.body_forward_layers(np64(inp["emb"]), layers, ck, cv, np.zeros(N, np.int64),
+                                       anchors.reshape(-1)[ns], valid.reshape(-1), oracle_cfg(w))
+    for l in range(w.num_layers):
+        _cmp(step.h_saved[l], hs[l], F32_GRAD, f"h entering layer {l}")
+    assert torch.equal(step.h_saved[0], inp["emb"].float())
+
+
+@pytest.mark.parametrize("name", ["c1x2", "small_bf16"])
+def test_all_gradients_invalid_rows_and_empty_blocks(name):
+    w = C1X2 if name == "c1x2" else SMALL_BF16
+    inp = make_training_inputs(w, "cuda")
+    anchors, valid = _invalid_rows_case(w)
+    step = TrainStep(w, inp, anchors, valid).all()
+    blocks = [n for n in range(w.num_blocks) if anchors.reshape(-1)[n] >= 0]
+    d_emb, grads, ctx = oracle_backward(w, inp, anchors, valid, step.d_out, blocks)
+    _check(step, blocks, d_emb, grads, ctx, _tol(w))
+    empty = torch.from_numpy(np.repeat(anchors.reshape(-1) < 0, w.block_size)).cuda()
+    assert (step.demb[empty] == 0).all()
+
+
+def test_planned_blocks_bf16():
+    # Blocks from the plan (anchors spread over 300-position rows, one row
+    # shorter than the other): longer prefixes than the case above.
+    w = SMALL_BF16
+    mask = torch.ones((2, 300), dtype=torch.uint8, device="cuda")
+    mask[1, 250:] = 0
+    inp = make_training_inputs(w, "cuda", plan_seed=3, mask=mask)
+    step = TrainStep(w, inp).all()
+    anchors = step.run.anchors.cpu().numpy()
+    valid = step.run.valid.cpu().numpy()
+    blocks = list(range(w.num_blocks))
+    d_emb, grads, ctx = oracle_backward(w, inp, anchors, valid, step.d_out, blocks)
+    _check(step, blocks, d_emb, grads, ctx, BF16_GRAD)
+
+
+def test_deterministic():
+    w = SMALL_BF16
+    inp = make_training_inputs(w, "cuda", plan_seed=1)
+    step = TrainStep(w, inp).all()
+    first = [{k: g.clone() for k, g in G.items()} for G in step.grads]
+    demb = step.demb.clone()
+    dck = [t.clone() for t in step.dck]
+    step.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(step.demb, demb)
+    assert all(torch.equal(step.grads[l][k], first[l][k]) for l in range(w.num_layers) for k in NAMES)
+    assert all(torch.equal(a, b) for a, b in zip(step.dck, dck))
+
+
+def test_no_blocks_gives_zero_gradients():
+    w = C1X2
+    inp = make_training_inputs(w, "cuda")
+    step = TrainStep(w, inp)
+    r = step.run
+    d.dflash_body_backward(r.cfg, 0, None, inp["layers"], r.ctx_k, r.ctx_v, r.T, None, None, None, None, None,
+                           step.grads, step.dck, step.dcv, None)
+    torch.cuda.synchronize()
+    for l in range(w.num_layers):
+        assert all((step.grads[l][k] == 0).all() for k in NAMES)
+        assert (step.dck[l] == 0).all() and (step.dcv[l] == 0).all()
+
+
+@pytest.mark.timeout(1200)
+def test_five_layer_full_size_sampled_blocks():
+    # The 5-layer training workload at full size (256 blocks of 16 rows, hidden
+    # 4096, intermediate 12288, 8 sequences of 4096 target positions), every
+    # block computed in the launch configuration the benchmark times. The
+    # output gradient is non-zero on three blocks only (the row-0 block with
+    # the largest anchor, a mid-order block of row 3 and row 7's first block):
+    # the other blocks then contribute nothing to any gradient, so every weight
+    # gradient is compared in full against the oracle's three-block backward,
+    # as are those blocks' embedding gradients and their sequences' context
+    # gradients; every other embedding and context gradient must be zero.
+    w = WORKLOADS["c3"]
+    inp = make_training_inputs(w, "cuda")
+    pre = TrainingRun(d, w, inp)
+    pre.plan()
+    torch.cuda.synchronize()
+    anchors = pre.anchors.cpu().numpy()
+    valid = pre.valid.cpu().numpy()
+    N, bs = w.anchors_per_row, w.block_size
+    row0 = int(np.argmax(anchors[0]))
+    picks = [row0, 3 * N + N // 2, 7 * N]
+    R, H = w.num_blocks * bs, w.hidden
+    d_out = torch.zeros((R, H), dtype=w.torch_dtype, device="cuda")
+    src = Rng(w.seed + 17, "cuda").normal("body.d_out", (R, H), dtype=w.torch_dtype)
+    for n in picks:
+        d_out[n * bs:(n + 1) * bs] = src[n * bs:(n + 1) * bs]
+    del src
+    step = TrainStep(w, inp, d_out=d_out).all()
+    d_emb, grads, ctx = oracle_backward(w, inp, anchors, valid, d_out, picks)
+    _check(step, picks, d_emb, grads, ctx, BF16_GRAD)
+    others = np.ones(w.num_blocks, bool)
+    others[picks] = False
+    assert (step.demb[torch.from_numpy(np.repeat(others, bs)).cuda()] == 0).all()
+    S = w.seq_len
+    for b in range(w.batch):
+        if b in ctx:
+            continue
+        for l in range(w.num_layers):
+            assert (step.dck[l][:, b * S:(b + 1) * S] == 0).all()
+            assert (step.dcv[l][:, :, b * S:(b + 1) * S] == 0).all()

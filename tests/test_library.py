@@ -191,6 +191,56 @@ def test_rejects_bad_arguments_before_launch():
                                    P(fake), P(fake), P(fake), P(fake), 1 << 40, None) == d.DFLASH_ERR_UNSUPPORTED
 
 
+def test_body_training_entry_points_reject_bad_arguments():
+    # Checked on the host before anything is enqueued, so no GPU is needed.
+    lib = d.library()
+    fake = 1 << 20
+    P = ctypes.c_void_p
+    c3 = WORKLOADS["c3"]
+    cfg = d.config_from_workload(c3)
+    L = c3.num_layers
+    lw = (d.DFlashLayerWeights * L)()
+    for i in range(L):
+        for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
+            setattr(lw[i], f, fake)
+    grads = (d.DFlashLayerGrads * L)()
+    for i in range(L):
+        for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
+            setattr(grads[i], f, fake)
+    ptrs = (ctypes.c_void_p * L)(*([fake] * L))
+    big = 1 << 44
+    # training forward: a null or misaligned h_saved
+    assert lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
+                                         P(fake), P(fake), None, P(fake), big, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
+                                         P(fake), P(fake), P(fake + 4), P(fake), big, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
+                                         P(fake), P(fake), P(fake), P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+
+    def bwd(c=cfg, nb=4, hs=P(fake), g=grads, dout=P(fake), demb=None, ws=P(fake), nbytes=big):
+        return lib.dflash_body_backward(ctypes.byref(c), nb, hs, lw, ptrs, ptrs, 100, P(fake), P(fake), P(fake),
+                                        dout, demb, g, ptrs, ptrs, ws, nbytes, None)
+    assert bwd(nb=-1) == d.DFLASH_ERR_INVALID_ARG
+    assert bwd(hs=None) == d.DFLASH_ERR_INVALID_ARG
+    assert bwd(dout=None) == d.DFLASH_ERR_INVALID_ARG
+    assert bwd(demb=P(fake + 8)) == d.DFLASH_ERR_INVALID_ARG
+    assert bwd(g=None) == d.DFLASH_ERR_INVALID_ARG
+    w_up = grads[2].w_up
+    grads[2].w_up = None
+    assert bwd() == d.DFLASH_ERR_INVALID_ARG
+    grads[2].w_up = w_up
+    assert bwd(nbytes=64) == d.DFLASH_ERR_WORKSPACE
+    assert bwd(ws=P(fake + 16)) == d.DFLASH_ERR_WORKSPACE
+    # shapes outside the backward's envelope: intermediate not a multiple of 128, hidden > 8192
+    for change in (dict(intermediate=12288 + 64), dict(hidden=8192 + 128)):
+        odd = d.config_from_workload(scaled(c3, **change))
+        assert d.dflash_check_config(odd) == d.DFLASH_OK, change
+        assert bwd(c=odd) == d.DFLASH_ERR_UNSUPPORTED, change
+        assert d.dflash_body_backward_workspace_size(odd, 4) == 0, change
+    # the workspace grows with the blocks
+    assert 0 < d.dflash_body_backward_workspace_size(cfg, 64) < d.dflash_body_backward_workspace_size(cfg, 256)
+
+
 def test_product_path_does_not_reach_the_oracle():
     pkg = os.path.join(ROOT, "block_draft_model_build_amd")
     for dirpath, _, files in os.walk(pkg):
