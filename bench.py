@@ -332,7 +332,62 @@ def next_rows(d, torch, device="cuda"):
                                 "roofline": {"bound": "mfma", "achieved": round(ach, 2),
                                              "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
                                              "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
+    del X3, dW3, ws4
+    out["body_backward"] = body_backward_row(d, torch, wt, cfg3, layers3, anc, base, val, gk3, gv3, mk, f32)
     return out
+
+
+def body_backward_row(d, torch, wt, cfg, layers, anc, base, val, d_ctx_k, d_ctx_v, mk, f32, reps=5):
+    """The body's training step at the 5-layer training shape (256 blocks at
+    random anchors over 8 sequences of 4096 positions): dflash_body_forward_train
+    (keeping every layer's activations in the reserve space), then
+    dflash_body_backward (every gradient). Wall times from events around the calls on the launch stream;
+    per-class device times from the library's hook. Rooflines: the weight-
+    gradient GEMMs (contraction over the 4096 rows) and the activation-gradient
+    GEMMs, each 2 * R * (H I + 2 I H + H nq + nqkv H) flops per layer."""
+    T = wt.batch * wt.seq_len
+    nb, bs, L = wt.num_blocks, wt.block_size, wt.num_layers
+    R, H, I = nb * bs, wt.hidden, wt.intermediate
+    nq, nk = wt.num_q_heads * wt.head_dim, wt.num_kv_heads * wt.head_dim
+    cks = [mk(wt.num_kv_heads, T, wt.head_dim) for _ in range(L)]
+    cvs = [mk(wt.num_kv_heads, wt.head_dim, T) for _ in range(L)]
+    emb, dout = mk(R, H), mk(R, H)
+    outb = torch.empty_like(emb)
+    demb = f32(R, H)
+    reserve = torch.empty(d.dflash_body_train_reserve_size(cfg, nb), dtype=torch.uint8, device=emb.device)
+    grads = [{k: f32(*v.shape) for k, v in Lw.items()} for Lw in layers]
+    ws = torch.empty(d.dflash_workspace_size(cfg, nb, 0), dtype=torch.uint8, device=emb.device)
+    wsb = torch.empty(d.dflash_body_backward_workspace_size(cfg, nb), dtype=torch.uint8, device=emb.device)
+    fwd = lambda: d.dflash_body_forward_train(cfg, nb, emb, layers, cks, cvs, T, base, anc, val, outb, reserve,
+                                              ws)
+    bwd = lambda: d.dflash_body_backward(cfg, nb, reserve, layers, cks, cvs, T, base, anc, val, dout, demb, grads,
+                                         d_ctx_k, d_ctx_v, wsb)
+
+    def wall(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ms_f, ms_b = wall(fwd), wall(bwd)
+    # Hook scopes per backward call: 4 pack scopes per layer + the output mask,
+    # 4 GEMMs of each gradient kind per layer, 2 norms per layer, the attention backward.
+    per_call = {"bwd_pack": 4 * L + 1, "bwd_data": 4 * L, "bwd_weight": 4 * L, "bwd_norm": 2 * L, "attn_bwd": L}
+    parts = {k: hook_ms(d, torch, [(k, n)], bwd, reps=3) for k, n in per_call.items()}
+    gemm_flops = L * 2.0 * R * (H * I + 2 * I * H + H * nq + (nq + 2 * nk) * H)
+    peak = PEAK_MFMA_TFLOPS["bf16"]
+
+    def roof(ms):
+        ach = gemm_flops / (ms / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
+    return {"blocks": nb, "layers": L, "rows": R, "ctx_total": T, "ms": round(ms_b, 4),
+            "forward_train_ms": round(ms_f, 4), "parts_ms": {k: round(v, 4) for k, v in parts.items()},
+            "roofline": roof(parts["bwd_weight"]), "roofline_data_grads": roof(parts["bwd_data"])}
 
 
 # ----------------------------------------------------------------------------- CPU oracle sample

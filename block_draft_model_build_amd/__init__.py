@@ -12,7 +12,8 @@ The names mirror the C entry points:
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
-  dflash_body_forward_train, dflash_body_backward, dflash_body_backward_workspace_size,
+  dflash_body_forward_train, dflash_body_train_reserve_size, dflash_body_backward,
+  dflash_body_backward_workspace_size,
   dflash_workspace_size, dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
@@ -38,7 +39,8 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
-            "dflash_body_forward_train", "dflash_body_backward", "dflash_body_backward_workspace_size",
+            "dflash_body_forward_train", "dflash_body_train_reserve_size", "dflash_body_backward",
+            "dflash_body_backward_workspace_size",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
@@ -113,9 +115,11 @@ def _load() -> ctypes.CDLL:
     lib.dflash_block_attn_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_ctx_proj_backward.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, I64, I64, P, P, P, SZ, P]
     lib.dflash_ctx_proj_backward.restype = ctypes.c_int
-    lib.dflash_body_forward_train.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, P, SZ, P]
+    lib.dflash_body_forward_train.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, SZ, P, SZ, P]
     lib.dflash_body_forward_train.restype = ctypes.c_int
-    lib.dflash_body_backward.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.dflash_body_train_reserve_size.argtypes = [CFG, I32]
+    lib.dflash_body_train_reserve_size.restype = ctypes.c_size_t
+    lib.dflash_body_backward.argtypes = [CFG, I32, P, SZ, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.dflash_body_backward.restype = ctypes.c_int
     lib.dflash_body_backward_workspace_size.argtypes = [CFG, I32]
     lib.dflash_body_backward_workspace_size.restype = ctypes.c_size_t
@@ -369,17 +373,29 @@ def dflash_ctx_proj_backward(cfg: DFlashConfig, target_states, ts_row_stride: in
     _check("dflash_ctx_proj_backward", s)
 
 
+def dflash_body_train_reserve_size(cfg: DFlashConfig, num_blocks: int) -> int:
+    return _lib.dflash_body_train_reserve_size(ctypes.byref(cfg), int(num_blocks))
+
+
 def dflash_body_forward_train(cfg: DFlashConfig, num_blocks: int, block_embeds, layers, ctx_k: List,
                               ctx_v: List, ctx_total: int, block_ctx_base, block_anchor, block_valid, out,
-                              h_saved, workspace, stream=None) -> None:
+                              reserve, workspace, stream=None) -> None:
+    """reserve: a uint8 device tensor of dflash_body_train_reserve_size bytes (kept for the backward)."""
     lw = _layers(layers)
     ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    rp, rb = _ws(reserve)
     wp, wb = _ws(workspace)
     s = _lib.dflash_body_forward_train(ctypes.byref(cfg), int(num_blocks), _ptr(block_embeds), lw, ck, cv,
                                        int(ctx_total), _ptr(block_ctx_base), _ptr(block_anchor),
-                                       _ptr(block_valid), _ptr(out), _ptr(h_saved), wp, wb,
-                                       _stream(stream, block_embeds))
+                                       _ptr(block_valid), _ptr(out), rp, rb, wp, wb, _stream(stream, block_embeds))
     _check("dflash_body_forward_train", s)
+
+
+def train_reserve_h(reserve, num_layers: int, rows: int, hidden: int):
+    """The fp32 residual streams entering each layer, [num_layers, rows, hidden]: a
+    view of the start of a training reserve space (the documented part of its layout)."""
+    import torch
+    return reserve[: num_layers * rows * hidden * 4].view(torch.float32).view(num_layers, rows, hidden)
 
 
 def _grads(grads: Sequence[Dict[str, object]]):
@@ -394,7 +410,7 @@ def dflash_body_backward_workspace_size(cfg: DFlashConfig, num_blocks: int) -> i
     return _lib.dflash_body_backward_workspace_size(ctypes.byref(cfg), int(num_blocks))
 
 
-def dflash_body_backward(cfg: DFlashConfig, num_blocks: int, h_saved, layers, ctx_k: List, ctx_v: List,
+def dflash_body_backward(cfg: DFlashConfig, num_blocks: int, reserve, layers, ctx_k: List, ctx_v: List,
                          ctx_total: int, block_ctx_base, block_anchor, block_valid, d_out, d_block_embeds,
                          grads: Sequence[Dict[str, object]], d_ctx_k: List, d_ctx_v: List, workspace,
                          stream=None) -> None:
@@ -402,8 +418,9 @@ def dflash_body_backward(cfg: DFlashConfig, num_blocks: int, h_saved, layers, ct
     lw = _layers(layers)
     ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
     gk, gv = _ptr_array(d_ctx_k), _ptr_array(d_ctx_v)
+    rp, rb = _ws(reserve)
     wp, wb = _ws(workspace)
-    s = _lib.dflash_body_backward(ctypes.byref(cfg), int(num_blocks), _ptr(h_saved), lw, ck, cv, int(ctx_total),
+    s = _lib.dflash_body_backward(ctypes.byref(cfg), int(num_blocks), rp, rb, lw, ck, cv, int(ctx_total),
                                   _ptr(block_ctx_base), _ptr(block_anchor), _ptr(block_valid), _ptr(d_out),
                                   _ptr(d_block_embeds), _grads(grads), gk, gv, wp, wb, _stream(stream, d_out))
     _check("dflash_body_backward", s)

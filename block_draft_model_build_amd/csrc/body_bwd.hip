@@ -2,8 +2,8 @@
 // step 1 and Scope: the body is trained with an optimizer step; step 3: the
 // decoder layers it runs; step 4: rows returned as zero pass no gradient).
 //
-// Per layer, from the last to the first, the forward is recomputed from the
-// layer's saved fp32 input h (dflash_body_forward_train keeps it), then
+// Per layer, from the last to the first, with the layer's activations from the
+// training forward's reserve space (h, x, q, k, v, o, h1, y, gate, up, u):
 //   d_w_down = dh^T u          du = dh W_down -> (dg, dup) in the epilogue
 //   d_w_gate | d_w_up = [dg | dup]^T y          dy = [dg | dup] [W_gate; W_up]
 //   dh1 = dh + RMSNorm^T(h1, mlp_norm; dy)
@@ -17,7 +17,6 @@
 // weight on the right take that weight transposed, once per layer. Activation
 // gradients enter their products in the config dtype; the residual-stream
 // gradient and every output stay fp32.
-#include "attn_launch.h"
 #include "gemm_select.h"
 #include "internal.h"
 #include "norm.h"
@@ -29,10 +28,7 @@ namespace {
 
 // Workspace (every region 256-byte aligned; T = config dtype, Rp = rows rounded
 // up to 64):
-//   the attention scheduler and partials of Workspace (before its body regions)
 //   attention backward scratch
-//   forward recompute: x, y [R][H] T; q [R][nq], k, v [R][nk], o [R][nq] T;
-//     h1 [R][H] f32; gate, up [R][I] f32; u [R][I] T
 //   transposes [features][Rp] T: xT, yT, oT, uT, dhT, dguT, dh1T, dqkvT
 //   gradients: dh_b, dh1_b [R][H] T; dgu [R][2I] T; do_b [R][nq] T;
 //     dqkv_b [R][nqkv] T; df (dy, then dx), dh1, dh [R][H] f32;
@@ -40,8 +36,8 @@ namespace {
 //   transposed weights: W_down^T [I][H], [W_gate; W_up]^T [H][2I],
 //     Wo^T [nq][H], [Wq; Wk; Wv]^T [H][nqkv]
 struct BodyBwdLayout {
-    size_t abw, x, xt, q, k, v, o, ot, h1, y, yt, gate, up, u, ut, dhb, dht, dgu, dgut, df, dh1, dh1b, dh1t, dob,
-        dq, dk, dv, dqkv, dqkvt, dh, part, wdt, wgut, wot, wqkvt, total;
+    size_t abw, xt, ot, yt, ut, dhb, dht, dgu, dgut, df, dh1, dh1b, dh1t, dob, dq, dk, dv, dqkv, dqkvt, dh, part,
+        wdt, wgut, wot, wqkvt, total;
     int64_t rp;
 };
 
@@ -53,26 +49,16 @@ BodyBwdLayout body_bwd_layout(const dflash_config& c, int nb) {
     const size_t nqkv = nq + 2 * nk;
     l.rp = (int64_t)((R + 63) / 64 * 64);
     const size_t Rp = (size_t)l.rp;
-    size_t off = align_up(workspace_layout(c, nb, 0).h, A);   // the attention regions come first
+    size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
         off = align_up(off + bytes, A);
         return o;
     };
     l.abw = take(attn_backward_workspace(c, nb));
-    l.x = take(eb * R * H);
     l.xt = take(eb * H * Rp);
-    l.q = take(eb * R * nq);
-    l.k = take(eb * R * nk);
-    l.v = take(eb * R * nk);
-    l.o = take(eb * R * nq);
     l.ot = take(eb * nq * Rp);
-    l.h1 = take(4 * R * H);
-    l.y = take(eb * R * H);
     l.yt = take(eb * H * Rp);
-    l.gate = take(4 * R * I);
-    l.up = take(4 * R * I);
-    l.u = take(eb * R * I);
     l.ut = take(eb * I * Rp);
     l.dhb = take(eb * R * H);
     l.dht = take(eb * H * Rp);
@@ -131,17 +117,20 @@ hipError_t norm_bwd(const float* x, const T* w, const float* dy, const float* re
         if (e_ != hipSuccess) return e_;         \
     } while (0)
 
-// One layer: dh holds dL/d(layer output) on entry and dL/d(layer input) on exit.
+// One layer: dh holds dL/d(layer output) on entry and dL/d(layer input) on exit;
+// lb is the layer's block of the reserve space, hl its input residual.
 template <typename T>
-hipError_t layer_bwd_t(const dflash_config& c, int nb, const float* hl, const dflash_layer_weights& L, const T* ck,
-                       const T* cv, int64_t ctx_total, const int64_t* base, const int32_t* anchor, float* dh,
-                       const dflash_layer_grads& G, float* dck, float* dcv, char* ws, const BodyBwdLayout& lay,
-                       const Workspace& aw, hipStream_t st) {
+hipError_t layer_bwd_t(const dflash_config& c, int nb, const float* hl, const char* lb, const TrainReserve& tr,
+                       const dflash_layer_weights& L, const T* ck, const T* cv, int64_t ctx_total,
+                       const int64_t* base, const int32_t* anchor, float* dh, const dflash_layer_grads& G,
+                       float* dck, float* dcv, char* ws, const BodyBwdLayout& lay, hipStream_t st) {
     const int R = nb * c.block_size, H = c.hidden, I = c.intermediate, D = c.head_dim;
     const int nq = c.num_q_heads * D, nk = c.num_kv_heads * D, nqkv = nq + 2 * nk;
     const int64_t Rp = lay.rp;
     auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    auto SP = [&](size_t off) { return reinterpret_cast<const T*>(lb + off); };
+    auto SF = [&](size_t off) { return reinterpret_cast<const float*>(lb + off); };
     const T* wq = static_cast<const T*>(L.wq);
     const T* wk = static_cast<const T*>(L.wk);
     const T* wv = static_cast<const T*>(L.wv);
@@ -149,10 +138,10 @@ hipError_t layer_bwd_t(const dflash_config& c, int nb, const float* hl, const df
     const T* wg = static_cast<const T*>(L.w_gate);
     const T* wu = static_cast<const T*>(L.w_up);
     const T* wd = static_cast<const T*>(L.w_down);
-    T *x = P(lay.x), *q = P(lay.q), *k = P(lay.k), *v = P(lay.v), *o = P(lay.o), *y = P(lay.y), *u = P(lay.u);
-    float *h1 = F(lay.h1), *gate = F(lay.gate), *up = F(lay.up);
+    const T *x = SP(tr.x), *q = SP(tr.q), *k = SP(tr.k), *v = SP(tr.v), *o = SP(tr.o), *y = SP(tr.y), *u = SP(tr.u);
+    const float *h1 = SF(tr.h1), *gate = SF(tr.gate), *up = SF(tr.up);
 
-    // ---- transposed weights and the forward recompute
+    // ---- transposed weights and activations
     {
         ProfScope prof(DFLASH_KERNEL_BWD_PACK, st);
         transpose_to<T>(wd, I, H, H, I, P(lay.wdt), H, st);                       // [I][H]
@@ -162,31 +151,6 @@ hipError_t layer_bwd_t(const dflash_config& c, int nb, const float* hl, const df
         transpose_to<T>(wq, H, nq, nq, H, P(lay.wqkvt), nqkv, st);                // [H][nqkv]
         transpose_to<T>(wk, H, nk, nk, H, P(lay.wqkvt) + nq, nqkv, st);
         transpose_to<T>(wv, H, nk, nk, H, P(lay.wqkvt) + nq + nk, nqkv, st);
-    }
-    DFLASH_TRY(hipGetLastError());
-    {
-        ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
-        hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, hl, (float*)nullptr,
-                           static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
-    }
-    DFLASH_TRY(hipGetLastError());
-    DFLASH_TRY(gemm<T>(DFLASH_KERNEL_QKV, R, nqkv, H, APlain<T>{x, H}, BQKV<T>{wq, wk, wv, nq, nk, H},
-                       EpSplitQKV<T>{q, k, v, nq, nk}, st));
-    DFLASH_TRY(attn_launch<T>(c,
-                              attn_args<T>(c, nb, q, nq, k, v, nk, ck, cv, ctx_total, base, anchor, nullptr, o, nq,
-                                           ws, aw),
-                              nb, st));
-    DFLASH_TRY(gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{o, nq}, BPlain<T>{wo, nq}, EpAddF32{hl, h1, H}, st));
-    {
-        ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
-        hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h1, (float*)nullptr,
-                           static_cast<const T*>(L.mlp_norm), y, H, c.rms_eps);
-    }
-    DFLASH_TRY(hipGetLastError());
-    DFLASH_TRY(gemm<T>(DFLASH_KERNEL_GATE_UP, R, 2 * I, H, APlain<T>{y, H}, BGateUp<T, 128>{wg, wu, H},
-                       EpSwiGLUSave<T>{u, gate, up, I}, st));
-    {
-        ProfScope prof(DFLASH_KERNEL_BWD_PACK, st);
         transpose_to<T>(x, H, R, Rp, H, P(lay.xt), Rp, st);
         transpose_to<T>(y, H, R, Rp, H, P(lay.yt), Rp, st);
         transpose_to<T>(o, nq, R, Rp, nq, P(lay.ot), Rp, st);
@@ -242,12 +206,12 @@ hipError_t layer_bwd_t(const dflash_config& c, int nb, const float* hl, const df
 }
 
 template <typename T>
-hipError_t body_bwd_t(const dflash_config& c, int nb, const float* hs, const dflash_layer_weights* layers,
+hipError_t body_bwd_t(const dflash_config& c, int nb, const char* reserve, const dflash_layer_weights* layers,
                       void* const* ck, void* const* cv, int64_t ctx_total, const int64_t* base, const int32_t* anchor,
                       const uint8_t* valid, const T* dout, float* demb, const dflash_layer_grads* grads,
                       float* const* dck, float* const* dcv, char* ws, hipStream_t st) {
     const BodyBwdLayout lay = body_bwd_layout(c, nb);
-    const Workspace aw = workspace_layout(c, nb, 0);
+    const TrainReserve tr = train_reserve_layout(c, nb);
     const int R = nb * c.block_size, H = c.hidden;
     float* dh = demb ? demb : reinterpret_cast<float*>(ws + lay.dh);
     {
@@ -258,12 +222,12 @@ hipError_t body_bwd_t(const dflash_config& c, int nb, const float* hs, const dfl
                            (int64_t)R, H, dh);
     }
     DFLASH_TRY(hipGetLastError());
-    // One attention schedule serves every layer's recompute (same blocks).
-    DFLASH_TRY(attn_schedule(c, nb, base, anchor, ctx_total, ws, aw, st));
+    const float* hs = reinterpret_cast<const float*>(reserve);
     for (int l = c.num_layers - 1; l >= 0; --l)
-        DFLASH_TRY(layer_bwd_t<T>(c, nb, hs + (int64_t)l * R * H, layers[l], static_cast<const T*>(ck[l]),
-                                  static_cast<const T*>(cv[l]), ctx_total, base, anchor, dh, grads[l],
-                                  dck ? dck[l] : nullptr, dcv ? dcv[l] : nullptr, ws, lay, aw, st));
+        DFLASH_TRY(layer_bwd_t<T>(c, nb, hs + (int64_t)l * R * H, reserve + tr.layer0 + (size_t)l * tr.per_layer, tr,
+                                  layers[l], static_cast<const T*>(ck[l]), static_cast<const T*>(cv[l]), ctx_total,
+                                  base, anchor, dh, grads[l], dck ? dck[l] : nullptr, dcv ? dcv[l] : nullptr, ws,
+                                  lay, st));
     return hipSuccess;
 }
 
@@ -302,8 +266,8 @@ extern "C" size_t dflash_body_backward_workspace_size(const dflash_config* cfg, 
     return body_bwd_layout(*cfg, num_blocks).total;
 }
 
-extern "C" dflash_status dflash_body_backward(const dflash_config* cfg, int32_t num_blocks, const float* h_saved,
-                                              const dflash_layer_weights* layers, void* const* ctx_k,
+extern "C" dflash_status dflash_body_backward(const dflash_config* cfg, int32_t num_blocks, const void* reserve,
+                                              size_t reserve_bytes, const dflash_layer_weights* layers, void* const* ctx_k,
                                               void* const* ctx_v, int64_t ctx_total, const int64_t* block_ctx_base,
                                               const int32_t* block_anchor, const uint8_t* block_valid,
                                               const void* d_out, float* d_block_embeds,
@@ -350,9 +314,9 @@ extern "C" dflash_status dflash_body_backward(const dflash_config* cfg, int32_t 
         }
         return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
     }
-    if (h_saved == nullptr || ctx_k == nullptr || ctx_v == nullptr || block_ctx_base == nullptr ||
-        block_anchor == nullptr || block_valid == nullptr || d_out == nullptr || !aligned16(h_saved) ||
-        !aligned16(d_out) || !aligned16(d_block_embeds))
+    if (reserve == nullptr || ctx_k == nullptr || ctx_v == nullptr || block_ctx_base == nullptr ||
+        block_anchor == nullptr || block_valid == nullptr || d_out == nullptr || !aligned16(d_out) ||
+        !aligned16(d_block_embeds))
         return DFLASH_ERR_INVALID_ARG;
     for (int l = 0; l < L; ++l) {
         const dflash_layer_weights& W = layers[l];
@@ -364,16 +328,17 @@ extern "C" dflash_status dflash_body_backward(const dflash_config* cfg, int32_t 
             return DFLASH_ERR_INVALID_ARG;
     }
     const size_t need = body_bwd_layout(*cfg, num_blocks).total;
-    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        reserve_bytes < train_reserve_layout(*cfg, num_blocks).total || (reinterpret_cast<uintptr_t>(reserve) & 255u) != 0)
         return DFLASH_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
-        e = body_bwd_t<__bf16>(*cfg, num_blocks, h_saved, layers, ctx_k, ctx_v, ctx_total, block_ctx_base,
+        e = body_bwd_t<__bf16>(*cfg, num_blocks, static_cast<const char*>(reserve), layers, ctx_k, ctx_v, ctx_total, block_ctx_base,
                                block_anchor, block_valid, static_cast<const __bf16*>(d_out), d_block_embeds, grads,
                                d_ctx_k, d_ctx_v, ws, st);
     else
-        e = body_bwd_t<float>(*cfg, num_blocks, h_saved, layers, ctx_k, ctx_v, ctx_total, block_ctx_base,
+        e = body_bwd_t<float>(*cfg, num_blocks, static_cast<const char*>(reserve), layers, ctx_k, ctx_v, ctx_total, block_ctx_base,
                               block_anchor, block_valid, static_cast<const float*>(d_out), d_block_embeds, grads,
                               d_ctx_k, d_ctx_v, ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;

@@ -46,29 +46,40 @@ static hipError_t ctx_proj_t(const dflash_config& c, const T* ts, int64_t rs, in
     return gemm<T>(DFLASH_KERNEL_CTX_KV, M, N, H, APlain<T>{C, H}, b, ep, st);
 }
 
-// hs (optional): [num_layers][R][H] fp32; when given, layer l reads its input
-// residual from hs[l] and writes its output to hs[l + 1] (the workspace's h for
-// the last layer), so every layer's input survives for the backward.
+// reserve (optional): the training reserve space (train_reserve_layout). With
+// it, every layer's input residual and activations are written there and kept:
+// layer l reads h_l, writes h1_l = h_l + attention and h_{l+1} = h1_l + MLP to
+// new buffers, keeps the SwiGLU pre-activations, and stores q, k, v unpacked.
+// The arithmetic is the same either way, so `out` is bit-identical.
 template <typename T>
 static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dflash_layer_weights* layers,
                          void* const* ck, void* const* cv, int64_t ctx_total, const int64_t* base,
-                         const int32_t* anchor, const uint8_t* valid, T* out, float* hs, char* ws,
+                         const int32_t* anchor, const uint8_t* valid, T* out, char* reserve, char* ws,
                          hipStream_t st) {
     const Workspace w = workspace_layout(c, nb, 0);
+    const TrainReserve tr = train_reserve_layout(c, nb);
     const int R = nb * c.block_size, H = c.hidden, D = c.head_dim;
     const int nq = c.num_q_heads * D, nk = c.num_kv_heads * D, nqkv = nq + 2 * nk, I = c.intermediate;
     float* h = reinterpret_cast<float*>(ws + w.h);
-    T* x = reinterpret_cast<T*>(ws + w.x);
-    T* qkv = reinterpret_cast<T*>(ws + w.qkv);
-    T* att = reinterpret_cast<T*>(ws + w.att);
-    T* u = reinterpret_cast<T*>(ws + w.u);
     hipError_t e = attn_schedule(c, nb, base, anchor, ctx_total, ws, w, st);
     if (e != hipSuccess) return e;
     const int64_t RH = (int64_t)R * H;
     for (int l = 0; l < c.num_layers; ++l) {
         const dflash_layer_weights& L = layers[l];
-        float* hin = hs ? hs + l * RH : h;                                  // residual entering layer l
-        float* hout = hs && l + 1 < c.num_layers ? hs + (l + 1) * RH : h;   // ... and leaving it
+        const bool last = l + 1 == c.num_layers;
+        char* lb = reserve ? reserve + tr.layer0 + (size_t)l * tr.per_layer : nullptr;
+        auto at = [&](size_t off_r, size_t off_w) { return reserve ? lb + off_r : ws + off_w; };
+        float* hin = reserve ? reinterpret_cast<float*>(reserve) + l * RH : h;     // residual entering layer l
+        float* h1 = reserve ? reinterpret_cast<float*>(lb + tr.h1) : h;             // ... after attention
+        float* hout = reserve && !last ? reinterpret_cast<float*>(reserve) + (l + 1) * RH : h;
+        T* x = reinterpret_cast<T*>(at(tr.x, w.x));
+        T* y = reinterpret_cast<T*>(at(tr.y, w.x));
+        T* q = reinterpret_cast<T*>(at(tr.q, w.qkv));
+        T* k = reserve ? reinterpret_cast<T*>(lb + tr.k) : q + nq;
+        T* v = reserve ? reinterpret_cast<T*>(lb + tr.v) : q + nq + nk;
+        const int q_ld = reserve ? nq : nqkv, kv_ld = reserve ? nk : nqkv;
+        T* att = reinterpret_cast<T*>(at(tr.o, w.att));
+        T* u = reinterpret_cast<T*>(at(tr.u, w.u));
         {
             ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
             if (l == 0)
@@ -79,38 +90,43 @@ static hipError_t body_t(const dflash_config& c, int nb, const T* emb, const dfl
                                    static_cast<const T*>(L.attn_norm), x, H, c.rms_eps);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = gemm<T>(DFLASH_KERNEL_QKV, R, nqkv, H, APlain<T>{x, H},
-                    BQKV<T>{static_cast<const T*>(L.wq), static_cast<const T*>(L.wk),
-                            static_cast<const T*>(L.wv), nq, nk, H},
-                    EpStore<T>{qkv, nqkv}, st);
+        const BQKV<T> bqkv{static_cast<const T*>(L.wq), static_cast<const T*>(L.wk), static_cast<const T*>(L.wv),
+                           nq, nk, H};
+        e = reserve ? gemm<T>(DFLASH_KERNEL_QKV, R, nqkv, H, APlain<T>{x, H}, bqkv, EpSplitQKV<T>{q, k, v, nq, nk}, st)
+                    : gemm<T>(DFLASH_KERNEL_QKV, R, nqkv, H, APlain<T>{x, H}, bqkv, EpStore<T>{q, nqkv}, st);
         if (e != hipSuccess) return e;
         // Inside the body every row keeps its attention output (invalid rows
         // evolve like the others); only the returned rows are zeroed.
-        AttnArgs<T> a = attn_args<T>(c, nb, qkv, nqkv, qkv + nq, qkv + nq + nk, nqkv,
-                                     static_cast<const T*>(ck[l]), static_cast<const T*>(cv[l]), ctx_total,
-                                     base, anchor, nullptr, att, nq, ws, w);
+        AttnArgs<T> a = attn_args<T>(c, nb, q, q_ld, k, v, kv_ld, static_cast<const T*>(ck[l]),
+                                     static_cast<const T*>(cv[l]), ctx_total, base, anchor, nullptr, att, nq, ws, w);
         if ((e = attn_launch<T>(c, a, nb, st)) != hipSuccess) return e;
-        if (hin == hout)
-            e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq},
-                        BPlain<T>{static_cast<const T*>(L.wo), nq}, EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0},
-                        st);
-        else
-            e = gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq},
-                        BPlain<T>{static_cast<const T*>(L.wo), nq}, EpAddF32{hin, hout, H}, st);
+        const BPlain<T> bo{static_cast<const T*>(L.wo), nq};
+        e = reserve ? gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq}, bo, EpAddF32{hin, h1, H}, st)
+                    : gemm<T>(DFLASH_KERNEL_O_PROJ, R, H, nq, APlain<T>{att, nq}, bo,
+                              EpResidual<T>{h, H, nullptr, nullptr, nullptr, 0}, st);
         if (e != hipSuccess) return e;
         {
             ProfScope prof(DFLASH_KERNEL_RMSNORM, st);
-            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, hout, (float*)nullptr,
-                               static_cast<const T*>(L.mlp_norm), x, H, c.rms_eps);
+            hipLaunchKernelGGL((rmsnorm_kernel<float, T>), dim3(R), dim3(256), 0, st, h1, (float*)nullptr,
+                               static_cast<const T*>(L.mlp_norm), y, H, c.rms_eps);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = gemm<T>(DFLASH_KERNEL_GATE_UP, R, 2 * I, H, APlain<T>{x, H},
-                    BGateUp<T, 128>{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), H},
-                    EpSwiGLU<T>{u, I}, st);
+        const BGateUp<T, 128> bgu{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), H};
+        e = reserve ? gemm<T>(DFLASH_KERNEL_GATE_UP, R, 2 * I, H, APlain<T>{y, H}, bgu,
+                              EpSwiGLUSave<T>{u, reinterpret_cast<float*>(lb + tr.gate),
+                                              reinterpret_cast<float*>(lb + tr.up), I},
+                              st)
+                    : gemm<T>(DFLASH_KERNEL_GATE_UP, R, 2 * I, H, APlain<T>{y, H}, bgu, EpSwiGLU<T>{u, I}, st);
         if (e != hipSuccess) return e;
-        const bool last = l + 1 == c.num_layers;
-        e = gemm<T>(DFLASH_KERNEL_DOWN, R, H, I, APlain<T>{u, I}, BPlain<T>{static_cast<const T*>(L.w_down), I},
-                    EpResidual<T>{hout, H, last ? out : nullptr, valid, anchor, c.block_size}, st);
+        const BPlain<T> bd{static_cast<const T*>(L.w_down), I};
+        if (last)   // out = h1 + MLP on the returned rows; h1 is only read
+            e = gemm<T>(DFLASH_KERNEL_DOWN, R, H, I, APlain<T>{u, I}, bd,
+                        EpResidual<T>{h1, H, out, valid, anchor, c.block_size}, st);
+        else if (reserve)
+            e = gemm<T>(DFLASH_KERNEL_DOWN, R, H, I, APlain<T>{u, I}, bd, EpAddF32{h1, hout, H}, st);
+        else
+            e = gemm<T>(DFLASH_KERNEL_DOWN, R, H, I, APlain<T>{u, I}, bd,
+                        EpResidual<T>{h, H, nullptr, valid, anchor, c.block_size}, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -499,7 +515,7 @@ extern "C" dflash_status dflash_block_attn(const dflash_config* cfg, int32_t num
 static dflash_status body_entry(const dflash_config* cfg, int32_t num_blocks, const void* block_embeds,
                                 const dflash_layer_weights* layers, void* const* ctx_k, void* const* ctx_v,
                                 int64_t ctx_total, const int64_t* block_ctx_base, const int32_t* block_anchor,
-                                const uint8_t* block_valid, void* out, float* h_saved, void* workspace,
+                                const uint8_t* block_valid, void* out, void* reserve, void* workspace,
                                 size_t workspace_bytes, void* hip_stream) {
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
@@ -508,7 +524,7 @@ static dflash_status body_entry(const dflash_config* cfg, int32_t num_blocks, co
     if (num_blocks == 0) return DFLASH_OK;
     if (block_embeds == nullptr || layers == nullptr || ctx_k == nullptr || ctx_v == nullptr ||
         block_ctx_base == nullptr || block_anchor == nullptr || block_valid == nullptr || out == nullptr ||
-        !aligned16(block_embeds) || !aligned16(h_saved))
+        !aligned16(block_embeds))
         return DFLASH_ERR_INVALID_ARG;
     for (int l = 0; l < cfg->num_layers; ++l) {
         const dflash_layer_weights& L = layers[l];
@@ -525,12 +541,12 @@ static dflash_status body_entry(const dflash_config* cfg, int32_t num_blocks, co
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = body_t<__bf16>(*cfg, num_blocks, static_cast<const __bf16*>(block_embeds), layers, ctx_k, ctx_v,
-                           ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<__bf16*>(out), h_saved,
-                           ws, st);
+                           ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<__bf16*>(out),
+                           static_cast<char*>(reserve), ws, st);
     else
         e = body_t<float>(*cfg, num_blocks, static_cast<const float*>(block_embeds), layers, ctx_k, ctx_v,
-                          ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<float*>(out), h_saved,
-                          ws, st);
+                          ctx_total, block_ctx_base, block_anchor, block_valid, static_cast<float*>(out),
+                          static_cast<char*>(reserve), ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
@@ -543,13 +559,27 @@ extern "C" dflash_status dflash_body_forward(const dflash_config* cfg, int32_t n
                       block_valid, out, nullptr, workspace, workspace_bytes, hip_stream);
 }
 
+extern "C" size_t dflash_body_train_reserve_size(const dflash_config* cfg, int32_t num_blocks) {
+    if (check_config(cfg) != DFLASH_OK || num_blocks < 0 || (int64_t)num_blocks * cfg->block_size > INT32_MAX / 2)
+        return 0;
+    return train_reserve_layout(*cfg, num_blocks).total;
+}
+
 extern "C" dflash_status dflash_body_forward_train(const dflash_config* cfg, int32_t num_blocks,
                                                    const void* block_embeds, const dflash_layer_weights* layers,
                                                    void* const* ctx_k, void* const* ctx_v, int64_t ctx_total,
                                                    const int64_t* block_ctx_base, const int32_t* block_anchor,
-                                                   const uint8_t* block_valid, void* out, float* h_saved,
-                                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
-    if (h_saved == nullptr && num_blocks > 0) return DFLASH_ERR_INVALID_ARG;
+                                                   const uint8_t* block_valid, void* out, void* reserve,
+                                                   size_t reserve_bytes, void* workspace, size_t workspace_bytes,
+                                                   void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (num_blocks > 0 && (int64_t)num_blocks * cfg->block_size <= INT32_MAX / 2) {
+        if (reserve == nullptr) return DFLASH_ERR_INVALID_ARG;
+        if (reserve_bytes < train_reserve_layout(*cfg, num_blocks).total ||
+            (reinterpret_cast<uintptr_t>(reserve) & 255u) != 0)
+            return DFLASH_ERR_WORKSPACE;
+    }
     return body_entry(cfg, num_blocks, block_embeds, layers, ctx_k, ctx_v, ctx_total, block_ctx_base, block_anchor,
-                      block_valid, out, h_saved, workspace, workspace_bytes, hip_stream);
+                      block_valid, out, reserve, workspace, workspace_bytes, hip_stream);
 }

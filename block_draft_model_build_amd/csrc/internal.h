@@ -80,6 +80,44 @@ inline Workspace workspace_layout(const dflash_config& c, int nb, int64_t ctx_ro
     return w;
 }
 
+// Reserve space of a training step (dflash_body_forward_train writes it,
+// dflash_body_backward reads it): first every layer's fp32 input residual
+// h [L][R][H] (offset 0, part of the documented interface), then one block per
+// layer (offset layer0 + l * per_layer) holding that layer's activations:
+//   h1 [R][H], gate [R][I], up [R][I] (fp32);  x [R][H], y [R][H], q [R][nq],
+//   k [R][nk], v [R][nk], o [R][nq], u [R][I] (config dtype)
+// at the offsets below, relative to the layer's block (each 256-byte aligned).
+struct TrainReserve {
+    size_t layer0, per_layer, h1, gate, up, x, y, q, k, v, o, u, total;
+};
+
+inline TrainReserve train_reserve_layout(const dflash_config& c, int nb) {
+    TrainReserve t{};
+    const size_t A = 256, eb = (size_t)elem_bytes(c);
+    const size_t R = (size_t)nb * (size_t)c.block_size, H = (size_t)c.hidden, I = (size_t)c.intermediate;
+    const size_t nq = (size_t)c.num_q_heads * c.head_dim, nk = (size_t)c.num_kv_heads * c.head_dim;
+    t.layer0 = align_up(sizeof(float) * (size_t)c.num_layers * R * H, A);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, A);
+        return o;
+    };
+    t.h1 = take(sizeof(float) * R * H);
+    t.gate = take(sizeof(float) * R * I);
+    t.up = take(sizeof(float) * R * I);
+    t.x = take(eb * R * H);
+    t.y = take(eb * R * H);
+    t.q = take(eb * R * nq);
+    t.k = take(eb * R * nk);
+    t.v = take(eb * R * nk);
+    t.o = take(eb * R * nq);
+    t.u = take(eb * R * I);
+    t.per_layer = off;
+    t.total = t.layer0 + (size_t)c.num_layers * t.per_layer;
+    return t;
+}
+
 inline RopeTurns make_rope_turns(const dflash_config& c) {
     RopeTurns rt{};
     const int half = c.head_dim / 2;

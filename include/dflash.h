@@ -508,19 +508,29 @@ size_t dflash_ctx_proj_backward_workspace_size(const dflash_config *cfg, int64_t
 /*
  * dflash_body_forward_train -- dflash_body_forward for a training step: the same
  * arithmetic and the same `out` (bit for bit), and in addition every layer's
- * input residual stream, kept for dflash_body_backward.
+ * input residual stream and activations, kept in a reserve space that
+ * dflash_body_backward reads.
  *
- *   h_saved  device f32 [num_layers][nb*bs, H]: h_saved[l] = the fp32 residual
- *            stream entering layer l (h_saved[0] = block_embeds as fp32)
- * Other arguments, errors and workspace as dflash_body_forward; INVALID_ARG
- * also for a null or misaligned h_saved.
+ *   reserve        device, dflash_body_train_reserve_size(cfg, nb) bytes, 256-byte
+ *                  aligned; owned by the caller and left untouched until the
+ *                  backward. It begins with h [num_layers][nb*bs, H] fp32, h[l] the
+ *                  residual stream entering layer l (h[0] = block_embeds as fp32);
+ *                  the rest holds, per layer, the normalised inputs, q/k/v, the
+ *                  attention output, the residual after attention, the SwiGLU
+ *                  pre-activations (fp32) and SiLU(g) * up, in an internal layout.
+ * Other arguments, errors and workspace as dflash_body_forward; INVALID_ARG for a
+ * null reserve, WORKSPACE for a small or misaligned one.
  */
 dflash_status dflash_body_forward_train(const dflash_config *cfg, int32_t num_blocks,
                                         const void *block_embeds, const dflash_layer_weights *layers,
                                         void *const *ctx_k, void *const *ctx_v, int64_t ctx_total,
                                         const int64_t *block_ctx_base, const int32_t *block_anchor,
-                                        const uint8_t *block_valid, void *out, float *h_saved,
-                                        void *workspace, size_t workspace_bytes, void *hip_stream);
+                                        const uint8_t *block_valid, void *out, void *reserve,
+                                        size_t reserve_bytes, void *workspace, size_t workspace_bytes,
+                                        void *hip_stream);
+/* Bytes of a training step's reserve space for num_blocks blocks (0 for an
+ * invalid config). */
+size_t dflash_body_train_reserve_size(const dflash_config *cfg, int32_t num_blocks);
 
 /* Gradients of one draft layer's weights (device f32, the shapes of
  * dflash_layer_weights). */
@@ -537,7 +547,8 @@ typedef struct dflash_layer_grads {
  *
  * d_out is the gradient of `out`. It reaches the last layer's output on the
  * rows the body returns (valid, non-empty block); then, from the last layer to
- * the first, each layer recomputes its forward from h_saved[l] and applies
+ * the first, each layer takes its forward activations from the reserve space and
+ * applies
  *   d_w_down = dh^T u,  du = dh W_down,  (dg, dup) = SwiGLU backward at (g, up)
  *   d_w_gate = dg^T y,  d_w_up = dup^T y,  dy = dg W_gate + dup W_up
  *   dh1 = dh + RMSNorm backward (h1, mlp_norm) at dy           -> d_mlp_norm
@@ -551,7 +562,8 @@ typedef struct dflash_layer_grads {
  * dflash_block_attn_backward's, with no row's output gradient dropped (inside
  * the body invalid rows keep their attention output).
  *
- *   h_saved         device f32 [num_layers][nb*bs, H] from dflash_body_forward_train
+ *   reserve         the reserve space dflash_body_forward_train filled for the same
+ *                   blocks, weights and caches (read only)
  *   layers, ctx_k, ctx_v, ctx_total, block_ctx_base, block_anchor, block_valid
  *                   as dflash_body_forward
  *   d_out           device [nb*bs, H] in the config dtype
@@ -569,10 +581,12 @@ typedef struct dflash_layer_grads {
  * atomics, fixed reduction orders. With nb == 0 every output is zero.
  * Errors: as dflash_body_forward; INVALID_ARG for null required pointers or
  * misaligned arrays; UNSUPPORTED when intermediate is not a multiple of 128 or
- * hidden exceeds 8192; WORKSPACE as usual.
+ * hidden exceeds 8192; WORKSPACE when the workspace or the reserve is missing
+ * (for nb > 0), small or misaligned.
  */
-dflash_status dflash_body_backward(const dflash_config *cfg, int32_t num_blocks, const float *h_saved,
-                                   const dflash_layer_weights *layers, void *const *ctx_k, void *const *ctx_v,
+dflash_status dflash_body_backward(const dflash_config *cfg, int32_t num_blocks, const void *reserve,
+                                   size_t reserve_bytes, const dflash_layer_weights *layers,
+                                   void *const *ctx_k, void *const *ctx_v,
                                    int64_t ctx_total, const int64_t *block_ctx_base,
                                    const int32_t *block_anchor, const uint8_t *block_valid, const void *d_out,
                                    float *d_block_embeds, const dflash_layer_grads *grads,

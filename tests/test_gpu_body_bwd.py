@@ -1,4 +1,4 @@
-"""dflash_body_forward_train and dflash_body_backward vs the oracle's body
+"""dflash_body_forward_train (with its reserve space) and dflash_body_backward vs the oracle's body
 backward (NeMo RL "DFlash Draft Body", How It Works, steps 1, 3 and 4, and
 Scope: the body is trained with an optimizer step). The oracle's backward is
 pinned by central differences of its forward (tests/test_oracle_body_backward.py).
@@ -64,7 +64,9 @@ class TrainStep:
         R = w.num_blocks * w.block_size
         L, H = w.num_layers, w.hidden
         dev = "cuda"
-        self.h_saved = torch.full((L, R, H), float("nan"), dtype=torch.float32, device=dev)
+        self.reserve = torch.full((d.dflash_body_train_reserve_size(self.run.cfg, w.num_blocks),), 0xFF,
+                                  dtype=torch.uint8, device=dev)     # NaN patterns until written
+        self.h_saved = d.train_reserve_h(self.reserve, L, R, H)
         self.out = torch.empty((R, H), dtype=w.torch_dtype, device=dev)
         if d_out is None:
             d_out = Rng(w.seed + 17, dev).normal("body.d_out", (R, H), dtype=w.torch_dtype)
@@ -85,11 +87,11 @@ class TrainStep:
         r, w = self.run, self.w
         d.dflash_body_forward_train(r.cfg, w.num_blocks, self.inp["emb"], self.inp["layers"], r.ctx_k, r.ctx_v,
                                     r.T, r.base, r.anchors.reshape(-1), r.valid.reshape(-1), self.out,
-                                    self.h_saved, r.ws)
+                                    self.reserve, r.ws)
 
     def backward(self):
         r, w = self.run, self.w
-        d.dflash_body_backward(r.cfg, w.num_blocks, self.h_saved, self.inp["layers"], r.ctx_k, r.ctx_v, r.T,
+        d.dflash_body_backward(r.cfg, w.num_blocks, self.reserve, self.inp["layers"], r.ctx_k, r.ctx_v, r.T,
                                r.base, r.anchors.reshape(-1), r.valid.reshape(-1), self.d_out, self.demb,
                                self.grads, self.dck, self.dcv, self.bws)
 

@@ -209,16 +209,20 @@ def test_body_training_entry_points_reject_bad_arguments():
             setattr(grads[i], f, fake)
     ptrs = (ctypes.c_void_p * L)(*([fake] * L))
     big = 1 << 44
-    # training forward: a null or misaligned h_saved
-    assert lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
-                                         P(fake), P(fake), None, P(fake), big, None) == d.DFLASH_ERR_INVALID_ARG
-    assert lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
-                                         P(fake), P(fake), P(fake + 4), P(fake), big, None) == d.DFLASH_ERR_INVALID_ARG
-    assert lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
-                                         P(fake), P(fake), P(fake), P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+    # training forward: a null, small or misaligned reserve
+    need = d.dflash_body_train_reserve_size(cfg, 4)
+    assert need > 0 and d.dflash_body_train_reserve_size(cfg, -1) == 0
 
-    def bwd(c=cfg, nb=4, hs=P(fake), g=grads, dout=P(fake), demb=None, ws=P(fake), nbytes=big):
-        return lib.dflash_body_backward(ctypes.byref(c), nb, hs, lw, ptrs, ptrs, 100, P(fake), P(fake), P(fake),
+    def fwd(res=P(fake), nbytes=need, nbw=big):
+        return lib.dflash_body_forward_train(ctypes.byref(cfg), 4, P(fake), lw, ptrs, ptrs, 100, P(fake), P(fake),
+                                             P(fake), P(fake), res, nbytes, P(fake), nbw, None)
+    assert fwd(res=None) == d.DFLASH_ERR_INVALID_ARG
+    assert fwd(nbytes=need - 1) == d.DFLASH_ERR_WORKSPACE
+    assert fwd(res=P(fake + 16)) == d.DFLASH_ERR_WORKSPACE
+    assert fwd(nbw=64) == d.DFLASH_ERR_WORKSPACE
+
+    def bwd(c=cfg, nb=4, hs=P(fake), rb=big, g=grads, dout=P(fake), demb=None, ws=P(fake), nbytes=big):
+        return lib.dflash_body_backward(ctypes.byref(c), nb, hs, rb, lw, ptrs, ptrs, 100, P(fake), P(fake), P(fake),
                                         dout, demb, g, ptrs, ptrs, ws, nbytes, None)
     assert bwd(nb=-1) == d.DFLASH_ERR_INVALID_ARG
     assert bwd(hs=None) == d.DFLASH_ERR_INVALID_ARG
@@ -230,6 +234,7 @@ def test_body_training_entry_points_reject_bad_arguments():
     assert bwd() == d.DFLASH_ERR_INVALID_ARG
     grads[2].w_up = w_up
     assert bwd(nbytes=64) == d.DFLASH_ERR_WORKSPACE
+    assert bwd(rb=need - 1) == d.DFLASH_ERR_WORKSPACE
     assert bwd(ws=P(fake + 16)) == d.DFLASH_ERR_WORKSPACE
     # shapes outside the backward's envelope: intermediate not a multiple of 128, hidden > 8192
     for change in (dict(intermediate=12288 + 64), dict(hidden=8192 + 128)):
