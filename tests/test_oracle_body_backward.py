@@ -140,3 +140,42 @@ def test_single_layer_backward_is_linear_in_dh():
     b = layer_backward(emb, layers[0], ck[0], cv[0], base, anchor, CFG, 2.5 * d_out)
     assert np.allclose(b[0], 2.5 * a[0], rtol=1e-12, atol=1e-12)
     assert all(np.allclose(b[1][k], 2.5 * a[1][k], rtol=1e-12, atol=1e-12) for k in a[1])
+
+
+# Plausible mistakes, planted in a copy of the backward oracle: each must make
+# its gradients disagree with the central differences somewhere.
+MUTATIONS = [
+    ("    dx = r * dyw - x * (r ** 3) * dot / H", "    dx = r * dyw"),                      # RMSNorm term dropped
+    ("    dh1 = dh2 + dh1_norm", "    dh1 = dh1_norm"),                                    # residual path dropped
+    ('    dy = dg @ W["w_gate"] + dup @ W["w_up"]', '    dy = dg @ W["w_gate"]'),          # up branch dropped
+    ("    d_wq, d_wk, d_wv = dq.T @ x, dk.T @ x, dv.T @ x",
+     "    d_wq, d_wk, d_wv = dq.T @ x, dv.T @ x, dk.T @ x"),                              # operands swapped
+    ("    return du * up * s * (1.0 + g * (1.0 - s)), du * g * s",
+     "    return du * up * s, du * g * s"),                                                # SiLU' incomplete
+    ("    return dh1 + dh_norm, grads, dck, dcv", "    return dh1 - dh_norm, grads, dck, dcv"),   # sign
+    ("    d_w_down = dh2.T @ u", "    d_w_down = dh2.T @ (g * up)"),                        # wrong activation
+]
+
+
+@pytest.mark.parametrize("k", range(len(MUTATIONS)))
+def test_planted_mistakes_are_caught(k):
+    import types
+    import oracle.backward as ob
+    old, new = MUTATIONS[k]
+    src = open(ob.__file__).read()
+    assert old in src
+    mod = types.ModuleType("oracle._planted")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new, 1), "planted", "exec"), mod.__dict__)
+    layers, ck, cv, emb, base, anchor, valid, d_out = _case(3)
+    d_emb, grads, dck, dcv = mod.body_backward(emb, layers, ck, cv, base, anchor, valid, CFG, d_out)
+    f = lambda: float((d_out * oracle.body_forward(emb, layers, ck, cv, base, anchor, valid, CFG)).sum())
+    checks = [(emb, d_emb)] + [(layers[l][n], grads[l][n]) for l in (1, 0) for n in
+                               ("w_down", "w_gate", "w_up", "wo", "wq", "wk", "wv", "attn_norm", "mlp_norm")]
+    rng = np.random.default_rng(9)
+    for x, g in checks:
+        scale = max(float(np.abs(g).max()), 1e-3)
+        for i in rng.choice(x.size, min(x.size, 12), replace=False):
+            if abs(_central(f, x, int(i)) - g.reshape(-1)[int(i)]) > 1e-6 * scale + 1e-8:
+                return
+    pytest.fail(f"planted mistake not caught: {new.strip()}")
