@@ -8,7 +8,8 @@ Contents:
   body.py  -- context projection, dual-source block attention, the draft body,
               and a brute-force dense-mask attention used to pin the gathered form.
   verify.py -- greedy and speculative-sampling verification of a drafted block.
-  loss.py  -- block LM head and positionally decayed cross-entropy.
+  loss.py  -- block LM head and positionally decayed cross-entropy, and its
+              gradient with respect to the hidden rows (the head is frozen).
   backward.py -- gradients of the dual-source block attention, of the
               context path (dW_proj) and of the whole body (every layer
               weight, the block embeddings and the context caches).
@@ -35,6 +36,9 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   lm_head_ce             pinned by closed forms (uniform logits, two-token
                          vocabulary, shift invariance, the two-row decayed mean,
                          the undecayed limit).
+  lm_head_ce_backward    pinned by central differences of lm_head_ce's loss over
+                         every hidden entry (rows that do not count included),
+                         and by closed forms (a one-hot head, linearity in d_loss).
   block_attn_call_backward  pinned by central finite differences of the
                          forward oracle over every input component.
   ctx_proj_backward      pinned by central differences of the forward context
@@ -57,7 +61,7 @@ from .verify import (
     verify_greedy_block, verify_greedy, target_choices_from_logits, verify_sample_block, verify_sample,
     inverse_cdf_draw, residual_weights, accept_proposal,
 )
-from .loss import lm_head_ce, lm_head_ce_rows, token_ce, logsumexp_rows, position_weights
+from .loss import lm_head_ce, lm_head_ce_rows, lm_head_ce_backward, token_ce, logsumexp_rows, position_weights
 from .backward import (
     block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_hidden_grad, ctx_proj_backward,
     rms_norm_backward, swiglu_backward, layer_forward, layer_backward, body_forward_layers, body_backward,
@@ -75,7 +79,7 @@ __all__ = [
     "concat_target_states",
     "verify_greedy_block", "verify_greedy", "target_choices_from_logits", "verify_sample_block",
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
-    "lm_head_ce", "lm_head_ce_rows", "token_ce", "logsumexp_rows", "position_weights",
+    "lm_head_ce", "lm_head_ce_rows", "lm_head_ce_backward", "token_ce", "logsumexp_rows", "position_weights",
     "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_hidden_grad", "ctx_proj_backward",
     "rms_norm_backward", "swiglu_backward", "layer_forward", "layer_backward", "body_forward_layers",
     "body_backward",

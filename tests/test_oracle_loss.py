@@ -58,3 +58,47 @@ def test_decayed_mean_two_rows_and_limits():
     assert abs(plain - ce_all[1:].mean()) < 1e-12
     ce0, zero = oracle.lm_head_ce(h, W, t, np.zeros(bs), bs, tau)
     assert zero == 0.0 and (ce0 == 0).all()
+
+
+def _ce_case(seed):
+    rng = np.random.default_rng(seed)
+    rows, H, V, bs = 12, 6, 9, 4
+    h = rng.standard_normal((rows, H))
+    W = rng.standard_normal((V, H))
+    t = rng.integers(0, V, rows)
+    t[5] = V + 3                                 # a target outside the vocabulary: the row does not count
+    m = np.ones(rows, np.uint8)
+    m[[0, 4, 8]] = 0                             # the anchors of the three blocks
+    return h, W, t, m, bs, 2.5
+
+
+def test_ce_backward_matches_finite_differences():
+    h, W, t, m, bs, tau = _ce_case(0)
+    g = oracle.lm_head_ce_backward(h, W, t, m, bs, tau)
+    eps = 1e-6
+    for i in range(h.size):
+        flat = h.reshape(-1)
+        old = flat[i]
+        flat[i] = old + eps
+        lp = oracle.lm_head_ce(h, W, t, m, bs, tau)[1]
+        flat[i] = old - eps
+        lm = oracle.lm_head_ce(h, W, t, m, bs, tau)[1]
+        flat[i] = old
+        assert abs((lp - lm) / (2 * eps) - g.reshape(-1)[i]) < 1e-8, i
+    assert (g[[0, 4, 5, 8]] == 0).all()          # rows that do not count pass nothing back
+
+
+def test_ce_backward_closed_forms():
+    h, W, t, m, bs, tau = _ce_case(1)
+    g = oracle.lm_head_ce_backward(h, W, t, m, bs, tau)
+    assert np.allclose(oracle.lm_head_ce_backward(h, W, t, m, bs, tau, d_loss=-3.0), -3.0 * g, rtol=1e-13, atol=0)
+    # One selected row, identity head (vocabulary = hidden): dL/dh = p - onehot(t), exactly the softmax
+    # gradient, since z = h.
+    H = 5
+    hh = np.array([[0.2, -1.0, 0.7, 0.0, 1.5]])
+    gi = oracle.lm_head_ce_backward(hh, np.eye(H), np.array([2]), np.array([1]), 4, 1.0)
+    p = np.exp(hh[0]) / np.exp(hh[0]).sum()
+    p[2] -= 1.0
+    assert np.allclose(gi[0], p, rtol=0, atol=1e-15)
+    # Nothing selected: zero gradient.
+    assert (oracle.lm_head_ce_backward(h, W, t, np.zeros_like(m), bs, tau) == 0).all()
