@@ -10,6 +10,7 @@ The names mirror the C entry points:
   dflash_ctx_truncate,
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
+  dflash_lm_head_ce_backward, dflash_lm_head_ce_backward_workspace_size,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
   dflash_body_forward_train, dflash_body_train_reserve_size, dflash_body_backward,
@@ -37,6 +38,7 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
             "dflash_ctx_truncate",
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
+            "dflash_lm_head_ce_backward", "dflash_lm_head_ce_backward_workspace_size",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
             "dflash_body_forward_train", "dflash_body_train_reserve_size", "dflash_body_backward",
@@ -49,7 +51,8 @@ KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "atten
            "attn_combine": 6, "o_proj": 7, "gate_up": 8, "down": 9, "verify": 10,
            "lm_head": 11, "lm_ce": 12, "attn_bwd": 13,
            "ctx_bwd_pack": 14, "ctx_bwd_dc": 15, "ctx_bwd_dw": 16,
-           "bwd_pack": 17, "bwd_data": 18, "bwd_weight": 19, "bwd_norm": 20}
+           "bwd_pack": 17, "bwd_data": 18, "bwd_weight": 19, "bwd_norm": 20,
+           "lm_bwd_prep": 21, "lm_bwd_dz": 22, "lm_bwd_dh": 23}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -106,6 +109,11 @@ def _load() -> ctypes.CDLL:
     lib.dflash_verify_sample.restype = ctypes.c_int
     lib.dflash_lm_head_ce.argtypes = [CFG, I32, P, P, I32, P, P, ctypes.c_double, P, P, P, SZ, P]
     lib.dflash_lm_head_ce.restype = ctypes.c_int
+    lib.dflash_lm_head_ce_backward.argtypes = [CFG, I32, P, P, I32, P, P, ctypes.c_double, P, ctypes.c_double, P,
+                                               P, SZ, P]
+    lib.dflash_lm_head_ce_backward.restype = ctypes.c_int
+    lib.dflash_lm_head_ce_backward_workspace_size.argtypes = [CFG, I32, I32]
+    lib.dflash_lm_head_ce_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_lm_head_ce_workspace_size.argtypes = [I32, I32]
     lib.dflash_lm_head_ce_workspace_size.restype = ctypes.c_size_t
     lib.dflash_block_attn_backward.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
@@ -338,6 +346,22 @@ def dflash_lm_head_ce(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, de
                                _ptr(loss_mask), float(decay_tau), _ptr(row_ce), _ptr(loss), wp, wb,
                                _stream(stream, lm_head))
     _check("dflash_lm_head_ce", s)
+
+
+def dflash_lm_head_ce_backward_workspace_size(cfg: DFlashConfig, rows: int, vocab: int) -> int:
+    return _lib.dflash_lm_head_ce_backward_workspace_size(ctypes.byref(cfg), int(rows), int(vocab))
+
+
+def dflash_lm_head_ce_backward(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, decay_tau: float, row_ce,
+                               d_loss: float, d_hidden, workspace, stream=None) -> None:
+    """hidden [rows, H], lm_head [vocab, H] (config dtype), targets i32 / loss_mask u8 [rows], row_ce f32 [rows]
+    from dflash_lm_head_ce -> d_hidden [rows, H] (config dtype)."""
+    rows, vocab = int(hidden.shape[0]), int(lm_head.shape[0])
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_lm_head_ce_backward(ctypes.byref(cfg), rows, _ptr(hidden), _ptr(lm_head), vocab, _ptr(targets),
+                                        _ptr(loss_mask), float(decay_tau), _ptr(row_ce), float(d_loss),
+                                        _ptr(d_hidden), wp, wb, _stream(stream, hidden))
+    _check("dflash_lm_head_ce_backward", s)
 
 
 def dflash_block_attn_backward_workspace_size(cfg: DFlashConfig, num_blocks: int) -> int:

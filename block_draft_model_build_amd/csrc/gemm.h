@@ -353,6 +353,35 @@ template <typename T> struct EpLseCE {
     }
 };
 
+// Gradient of the decayed CE with respect to the logits z = acc:
+// dz[row, col] = coef[row] * (exp(z - lse[row]) - [col == targets[row]]) for
+// col < vocab, exact zero for vocab <= col < ldz (the padding the next product
+// contracts over) and on rows whose coef is 0 (rows that do not count).
+template <typename T> struct EpCEGrad {
+    T* dz; int64_t ldz; const float* coef; const float* lse; const int32_t* targets; int vocab;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                const float c = coef[row], L = lse[row];
+                const int t = targets[row];
+                T* o = dz + (int64_t)row * ldz;
+#pragma unroll
+                for (int j = 0; j < NI; ++j) {
+                    const int col = nb + j * 32 + (lane & 31);
+                    if (col >= ldz) continue;
+                    float v = 0.f;
+                    if (col < vocab && c != 0.f) v = c * (__expf(acc[i][j][e] - L) - (col == t ? 1.f : 0.f));
+                    o[col] = from_f32<T>(v);
+                }
+            }
+    }
+};
+
 // Context K/V: virtual column n = l*(2*Hkv*D) + [K heads | V heads]. K columns
 // are rotated (pair d with d + D/2; both live in this wave because WN is a
 // multiple of D and heads start at multiples of D) and written to the

@@ -328,7 +328,10 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_BWD_DATA = 18,     /* GEMMs of the activation gradients (du, dy, do, dx) */
     DFLASH_KERNEL_BWD_WEIGHT = 19,   /* GEMMs of the weight gradients (contraction over rows) */
     DFLASH_KERNEL_BWD_NORM = 20,     /* RMSNorm backward and its weight-gradient column sums */
-    DFLASH_KERNEL_COUNT = 21
+    DFLASH_KERNEL_LM_BWD_PREP = 21,  /* dflash_lm_head_ce_backward: row statistics, LM head transpose */
+    DFLASH_KERNEL_LM_BWD_DZ = 22,    /* GEMM of the logits with the CE gradient epilogue */
+    DFLASH_KERNEL_LM_BWD_DH = 23,    /* GEMM d_hidden = dz W_lm */
+    DFLASH_KERNEL_COUNT = 24
 } dflash_kernel;
 
 /*
@@ -432,6 +435,40 @@ dflash_status dflash_lm_head_ce(const dflash_config *cfg, int32_t rows, const vo
                                 double *loss, void *workspace, size_t workspace_bytes,
                                 void *hip_stream);
 size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab);
+
+/*
+ * dflash_lm_head_ce_backward -- gradient of dflash_lm_head_ce's loss with
+ * respect to the hidden rows: the d_out that dflash_body_backward takes.
+ * [P1] "Configuration": the LM head comes from the target model and stays
+ * frozen, so it has no gradient here; [P1] "How it works", Loss: the decayed
+ * cross-entropy being differentiated.
+ *
+ * With D = sum(m_r w_r) over the rows that count (loss_mask set, target inside
+ * the vocabulary), c_r = d_loss m_r w_r / D (0 for the others) and
+ * p_r = softmax(z_r), z_r = hidden[r] W_lm^T:
+ *   dz_r        = c_r (p_r - onehot(targets[r]))
+ *   d_hidden[r] = dz_r W_lm
+ * The softmax uses logsumexp(z_r) = row_ce[r] + z_r[targets[r]], the second
+ * term recomputed as a dot product.
+ *
+ *   hidden, lm_head, vocab, targets, loss_mask, decay_tau, rows
+ *                  as dflash_lm_head_ce
+ *   row_ce         device f32 [rows]: dflash_lm_head_ce's output for the same inputs
+ *   d_loss         the upstream gradient of the loss (1 for the loss itself)
+ *   d_hidden       device [rows, hidden] in the config dtype, overwritten (rows
+ *                  that do not count get exact zeros)
+ *   workspace      dflash_lm_head_ce_backward_workspace_size(cfg, rows, vocab)
+ *                  bytes, 256-byte aligned
+ * dz enters the second product in the config dtype; both products accumulate
+ * in fp32. Errors: as dflash_lm_head_ce (INVALID_ARG also for a null row_ce or
+ * d_hidden when rows > 0).
+ */
+dflash_status dflash_lm_head_ce_backward(const dflash_config *cfg, int32_t rows, const void *hidden,
+                                         const void *lm_head, int32_t vocab, const int32_t *targets,
+                                         const uint8_t *loss_mask, double decay_tau, const float *row_ce,
+                                         double d_loss, void *d_hidden, void *workspace, size_t workspace_bytes,
+                                         void *hip_stream);
+size_t dflash_lm_head_ce_backward_workspace_size(const dflash_config *cfg, int32_t rows, int32_t vocab);
 
 /*
  * dflash_block_attn_backward -- gradients of dflash_block_attn. [P2] "How It

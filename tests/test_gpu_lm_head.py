@@ -89,3 +89,78 @@ def test_no_selected_rows_gives_zero_loss():
     h, W, t, mask = _inputs(w, 32, 500, seed=9)
     ce, loss = _run(w, h, W, t, torch.zeros_like(mask), 2.0)
     assert loss == 0.0 and (ce.cpu() == 0).all()
+
+
+# ---------------------------------------------------------------- backward
+# dflash_lm_head_ce_backward vs oracle.lm_head_ce_backward (pinned by central
+# differences of the loss). fp32: every step is fp32, so the forward's fp32 bar
+# relative to the gradient's scale. bf16: dz is rounded to bf16 once before its
+# product with W_lm and d_hidden once on output, each a relative 2^-9; the
+# softmax and both accumulations are fp32: rel-L2 1e-2 and max-abs 2e-2 of the
+# largest magnitude hold that with room.
+GRAD_TOL = dict(rel_l2=1e-2, max_rel=2e-2)
+GRAD_TOL_F32 = dict(rel_l2=1e-5, max_rel=1e-4)
+
+
+def _cmp_rel(gpu, ref, tol, what):
+    g = np64(gpu).reshape(ref.shape)
+    assert np.isfinite(g).all(), what
+    err = g - ref
+    rel = float(np.sqrt((err * err).sum()) / (np.sqrt((ref * ref).sum()) or 1.0))
+    scale = float(np.abs(ref).max())
+    assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3e}"
+    assert float(np.abs(err).max()) <= tol["max_rel"] * scale, f"{what}: max-abs {np.abs(err).max():.3e} vs {scale:.3e}"
+
+
+def _run_bwd(w, h, W, t, mask, tau, ce, d_loss=1.0):
+    cfg = d.config_from_workload(w)
+    rows, vocab = h.shape[0], W.shape[0]
+    dh = torch.full_like(h, float("nan"))
+    ws = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg, rows, vocab), dtype=torch.uint8, device="cuda")
+    d.dflash_lm_head_ce_backward(cfg, h, W, t, mask, tau, ce, d_loss, dh, ws)
+    torch.cuda.synchronize()
+    return dh
+
+
+@pytest.mark.parametrize("w,rows,vocab,tol", [
+    (SMALL, 48, 1000, GRAD_TOL),
+    (SMALL, 300, 4099, GRAD_TOL),
+    (WORKLOADS["c1"], 32, 777, GRAD_TOL_F32),
+])
+def test_backward_all_rows_small(w, rows, vocab, tol):
+    h, W, t, mask = _inputs(w, rows, vocab, seed=rows + vocab + 1)
+    t[5] = -1
+    t[9] = vocab
+    tau = 3.0
+    ce, _ = _run(w, h, W, t, mask, tau)
+    dh = _run_bwd(w, h, W, t, mask, tau, ce)
+    ref = oracle.lm_head_ce_backward(np64(h), np64(W), t.cpu().numpy(), mask.cpu().numpy(), w.block_size, tau)
+    _cmp_rel(dh, ref, tol, "d_hidden")
+    skip = (mask == 0).cpu().numpy()
+    skip[[5, 9]] = True
+    assert (dh.cpu()[torch.from_numpy(skip)] == 0).all()
+    # Linear in d_loss: doubling it doubles every element exactly; zero gives zeros.
+    assert torch.equal(_run_bwd(w, h, W, t, mask, tau, ce, 2.0), 2 * dh)
+    assert (_run_bwd(w, h, W, t, mask, tau, ce, 0.0) == 0).all()
+
+
+def test_backward_full_size_sampled_blocks():
+    # 4096 block rows x vocabulary 151936 x hidden 4096. The oracle differentiates
+    # three whole blocks (so each row keeps its in-block position); its
+    # normaliser covers only those rows, so its result is rescaled by the ratio
+    # of that normaliser to the one over all rows.
+    w = WORKLOADS["c3"]
+    rows, vocab, tau = w.num_blocks * w.block_size, 151936, 7.0
+    h, W, t, mask = _inputs(w, rows, vocab, seed=6)
+    ce, _ = _run(w, h, W, t, mask, tau)
+    dh = _run_bwd(w, h, W, t, mask, tau, ce)
+    bs = w.block_size
+    blocks = [0, 131, 255]
+    idx = np.concatenate([np.arange(n * bs, (n + 1) * bs) for n in blocks])
+    m_all = mask.cpu().numpy()
+    wts = oracle.position_weights(rows, bs, tau) * (m_all != 0)
+    sub = torch.from_numpy(idx).cuda()
+    ref = oracle.lm_head_ce_backward(np64(h[sub]), np64(W), t.cpu().numpy()[idx], m_all[idx], bs, tau)
+    ref *= wts[idx].sum() / wts.sum()
+    _cmp_rel(dh[sub], ref, GRAD_TOL, "sampled d_hidden")
+    assert torch.isfinite(dh.float()).all()
