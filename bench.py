@@ -200,9 +200,12 @@ def next_rows(d, torch, device="cuda"):
     151936-token vocabulary, with their HBM rooflines; and, on the training
     side, lm_head_ce = LM head + decayed cross-entropy over the 5-layer body's
     4096 block rows (151936 x 4096 head), attn_backward = one layer's
-    dual-source attention backward at the training shape, and
+    dual-source attention backward at the training shape,
     ctx_proj_backward = dW_proj through every layer's context K/V over the
-    32768 context rows, each with its MFMA roofline."""
+    32768 context rows, lm_head_ce_backward = the loss gradient with respect to
+    the 4096 block rows, body_backward = the body's training forward and
+    backward, each with its MFMA roofline; and train_step = one whole training
+    step of the 5-layer workload, end to end."""
     import math as _m
     from dflash_synth import WORKLOADS, Rng, layer_weights
     w = WORKLOADS["c5"]
@@ -283,7 +286,20 @@ def next_rows(d, torch, device="cuda"):
                          "roofline": {"bound": "mfma", "achieved": round(flops / (ms / 1e3) / 1e12, 2),
                                       "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
                                       "frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"], 4)}}
-    del hid, W
+    # Its backward (the gradient of the loss with respect to the hidden rows):
+    # two products of 2 * rows * V * H flops each (logits again, then dz W_lm).
+    dh = torch.empty_like(hid)
+    ws5 = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg3, rows, V), dtype=torch.uint8, device=device)
+    call = lambda: d.dflash_lm_head_ce_backward(cfg3, hid, W, tg, lm, 7.0, ce, 1.0, dh, ws5)
+    parts = {k: hook_ms(d, torch, [(k, 1)], call) for k in ("lm_bwd_prep", "lm_bwd_dz", "lm_bwd_dh")}
+    ms = sum(parts.values())
+    ach = 2 * flops / (ms / 1e3) / 1e12
+    out["lm_head_ce_backward"] = {"rows": rows, "vocab": V, "hidden": wt.hidden, "ms": round(ms, 4),
+                                  **{k + "_ms": round(v, 4) for k, v in parts.items()},
+                                  "roofline": {"bound": "mfma", "achieved": round(ach, 2),
+                                               "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+                                               "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
+    del hid, W, dh, ws5
     # Training side: backward of one layer's dual-source attention at the
     # training shape (8 sequences of 4096, 32 blocks each at random anchors).
     T = wt.batch * wt.seq_len
@@ -334,7 +350,111 @@ def next_rows(d, torch, device="cuda"):
                                              "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
     del X3, dW3, ws4
     out["body_backward"] = body_backward_row(d, torch, wt, cfg3, layers3, anc, base, val, gk3, gv3, mk, f32)
+    del gk3, gv3, layers3
+    torch.cuda.empty_cache()
+    out["train_step"] = train_step_row(d, torch, wt, V, device)
     return out
+
+
+class TrainingBuffers:
+    """Inputs, outputs and workspaces of one training step of a training-shaped
+    workload, and the step itself as the library's calls in order. The targets
+    (the caller's ground-truth tokens at each block position) are gathered with
+    torch from a synthetic token sequence, as a caller would."""
+
+    def __init__(self, d, torch, w, vocab, device):
+        import math as _m
+        from dflash_synth import Rng, make_training_inputs
+        self.d, self.torch, self.w, self.vocab = d, torch, w, vocab
+        B, S, N, bs, L = w.batch, w.seq_len, w.anchors_per_row, w.block_size, w.num_layers
+        self.inp = inp = make_training_inputs(w, device)
+        self.cfg = cfg = d.config_from_workload(w)
+        rng = Rng(4321, device)
+        self.tokens = rng.integers("train.tokens", 0, vocab - 1, (B, S)).to(torch.int32)
+        self.lm_head = rng.normal("train.lm_head", (vocab, w.hidden), std=1 / _m.sqrt(w.hidden),
+                                  dtype=w.torch_dtype)
+        nb, R, T, H = w.num_blocks, w.num_blocks * bs, B * S, w.hidden
+        e = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device=device)
+        u8 = lambda n: torch.empty(n, dtype=torch.uint8, device=device)
+        self.anchors, self.positions = e(B, N, dt=torch.int32), e(B, N, bs, dt=torch.int32)
+        self.valid, self.loss_mask = e(B, N, bs, dt=torch.uint8), e(B, N, bs, dt=torch.uint8)
+        self.num, self.base = e(B, dt=torch.int32), e(nb, dt=torch.int64)
+        self.ctx_pos = (torch.arange(T, device=device) % S).to(torch.int32)
+        self.ck = [e(w.num_kv_heads, T, w.head_dim, dt=w.torch_dtype) for _ in range(L)]
+        self.cv = [e(w.num_kv_heads, w.head_dim, T, dt=w.torch_dtype) for _ in range(L)]
+        self.out, self.d_out = e(R, H, dt=w.torch_dtype), e(R, H, dt=w.torch_dtype)
+        self.ws = u8(d.dflash_workspace_size(cfg, nb, T))
+        self.reserve = u8(d.dflash_body_train_reserve_size(cfg, nb))
+        self.ce, self.loss = e(R), e(1, dt=torch.float64)
+        self.ws_lm = u8(d.dflash_lm_head_ce_workspace_size(R, vocab))
+        self.ws_lmb = u8(d.dflash_lm_head_ce_backward_workspace_size(cfg, R, vocab))
+        self.grads = [{k: e(*v.shape) for k, v in Lw.items()} for Lw in inp["layers"]]
+        self.dck = [e(w.num_kv_heads, T, w.head_dim) for _ in range(L)]
+        self.dcv = [e(w.num_kv_heads, w.head_dim, T) for _ in range(L)]
+        self.demb = e(R, H)
+        self.ws_bb = u8(d.dflash_body_backward_workspace_size(cfg, nb))
+        self.Kt = w.num_target_layers * w.target_hidden
+        self.dW = e(H, self.Kt)
+        self.ws_cb = u8(d.dflash_ctx_proj_backward_workspace_size(cfg, T))
+        self.row_of = torch.arange(R, device=device) // (bs * N)
+
+    def step(self):
+        """Runs the step; returns events recorded before and after each stage."""
+        d, torch, w, i = self.d, self.torch, self.w, self.inp
+        cfg, T, nb, V = self.cfg, self.w.batch * self.w.seq_len, self.w.num_blocks, self.vocab
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        ev[0].record()
+        d.dflash_build_plan(i["mask"], i["sample_ids"], i["step"], i["plan_seed"], w.anchors_per_row, w.block_size,
+                            self.anchors, self.positions, self.valid, self.loss_mask, self.num, self.base)
+        ev[1].record()
+        d.dflash_ctx_proj(cfg, i["states"], w.target_hidden, T * w.target_hidden, T, self.ctx_pos, i["w_proj"],
+                          i["layers"], self.ck, self.cv, T, 0, self.ws)
+        ev[2].record()
+        anc, val = self.anchors.reshape(-1), self.valid.reshape(-1)
+        d.dflash_body_forward_train(cfg, nb, i["emb"], i["layers"], self.ck, self.cv, T, self.base, anc, val, self.out,
+                                    self.reserve, self.ws)
+        ev[3].record()
+        pos = self.positions.reshape(-1).long().clamp(0, w.seq_len - 1)
+        targets = self.tokens[self.row_of, pos].contiguous()
+        lm = self.loss_mask.reshape(-1)
+        d.dflash_lm_head_ce(cfg, self.out, self.lm_head, targets, lm, 7.0, self.ce, self.loss, self.ws_lm)
+        ev[4].record()
+        d.dflash_lm_head_ce_backward(cfg, self.out, self.lm_head, targets, lm, 7.0, self.ce, 1.0, self.d_out,
+                                     self.ws_lmb)
+        ev[5].record()
+        d.dflash_body_backward(cfg, nb, self.reserve, i["layers"], self.ck, self.cv, T, self.base, anc, val,
+                               self.d_out, self.demb, self.grads, self.dck, self.dcv, self.ws_bb)
+        ev[6].record()
+        d.dflash_ctx_proj_backward(cfg, i["states"], w.target_hidden, T * w.target_hidden, T, self.ctx_pos,
+                                   i["layers"], self.dck, self.dcv, T, 0, self.dW, None, self.ws_cb)
+        ev[7].record()
+        return ev
+
+
+def train_step_row(d, torch, w, vocab, device, reps=3):
+    """One whole training step of the 5-layer training workload through the
+    library, timed end to end with events on the launch stream: plan, context
+    projection, training forward (reserve space), LM head + decayed CE, its
+    backward, body backward, W_proj backward. Synthetic inputs of the workload's
+    shapes; targets are random tokens at the block positions; frozen synthetic
+    LM head of the given vocabulary. Also the events between the stages."""
+    bufs = TrainingBuffers(d, torch, w, vocab, device)
+    marks = bufs.step()                       # warm-up
+    torch.cuda.synchronize()
+    names = ["plan", "ctx_proj", "forward_train", "lm_head_ce", "lm_head_ce_backward", "body_backward",
+             "ctx_proj_backward"]
+    acc = [0.0] * len(names)
+    total = 0.0
+    for _ in range(reps):
+        marks = bufs.step()
+        torch.cuda.synchronize()
+        ts = [marks[i].elapsed_time(marks[i + 1]) for i in range(len(names))]
+        acc = [a + t for a, t in zip(acc, ts)]
+        total += marks[0].elapsed_time(marks[-1])
+    ms = total / reps
+    return {"blocks": w.num_blocks, "layers": w.num_layers, "vocab": vocab, "ms": round(ms, 3),
+            "stages_ms": {n: round(a / reps, 3) for n, a in zip(names, acc)},
+            "block_positions_per_s": round(w.num_blocks * w.block_size / (ms / 1e3), 1)}
 
 
 def body_backward_row(d, torch, wt, cfg, layers, anc, base, val, d_ctx_k, d_ctx_v, mk, f32, reps=5):
