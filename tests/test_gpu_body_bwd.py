@@ -280,3 +280,25 @@ def test_five_layer_full_size_sampled_blocks():
         for l in range(w.num_layers):
             assert (step.dck[l][:, b * S:(b + 1) * S] == 0).all()
             assert (step.dcv[l][:, :, b * S:(b + 1) * S] == 0).all()
+
+
+@pytest.mark.parametrize("dims", [
+    # bf16: 8 query heads on one KV head (G = 8), blocks of 8, three layers, 5 blocks (40 rows: ragged in 64)
+    dict(dtype="bf16", hidden=384, num_q_heads=8, num_kv_heads=1, head_dim=128, intermediate=384,
+         num_layers=3, block_size=8, anchors_per_row=5, batch=1, seq_len=96),
+    # bf16: blocks of 32 with G = 2 (64 query columns), two layers
+    dict(dtype="bf16", hidden=256, num_q_heads=2, num_kv_heads=1, head_dim=128, intermediate=256,
+         num_layers=2, block_size=32, anchors_per_row=3, batch=2, seq_len=160),
+    # fp32: blocks of 2, G = 4, two layers
+    dict(dtype="f32", hidden=128, num_q_heads=4, num_kv_heads=1, head_dim=64, intermediate=256,
+         num_layers=2, block_size=2, anchors_per_row=6, batch=2, seq_len=40),
+], ids=["bf16-G8-bs8-3layers", "bf16-G2-bs32", "f32-G4-bs2"])
+def test_other_shapes(dims):
+    w = scaled(WORKLOADS["c1"], num_target_layers=2, target_hidden=128, seed=55, **dims)
+    inp = make_training_inputs(w, "cuda", plan_seed=2)
+    step = TrainStep(w, inp).all()
+    anchors = step.run.anchors.cpu().numpy()
+    valid = step.run.valid.cpu().numpy()
+    blocks = list(range(w.num_blocks))
+    d_emb, grads, ctx = oracle_backward(w, inp, anchors, valid, step.d_out, blocks)
+    _check(step, blocks, d_emb, grads, ctx, _tol(w))
