@@ -1,5 +1,7 @@
 /*
- * libdflash -- the DFlash draft-body forward pass on AMD Instinct MI355X (gfx950).
+ * libdflash -- the DFlash draft-body forward pass on AMD Instinct MI355X (gfx950),
+ * with the steps around it: context-cache append, verification, the draft loss
+ * and a whole training step's backward.
  *
  * What the library computes is stated on three pages:
  *   [P1] angelspec documentation, "DFlash" (sections "How it works", "Configuration");
@@ -11,8 +13,11 @@
  * Conventions shared by every entry point
  *   - Pointers marked "device" are HIP device pointers; "host" pointers are read
  *     during the call only. The library never allocates device memory and never
- *     frees caller memory; scratch space comes from the caller's workspace
- *     (size: dflash_workspace_size).
+ *     frees caller memory; scratch space comes from the caller's workspace (size:
+ *     dflash_workspace_size and the per-call *_workspace_size functions), and a
+ *     training step's forward activations live in a caller-owned reserve space
+ *     (dflash_body_train_reserve_size). The one exception is the static scratch
+ *     array of dflash_ctx_append_noalloc, held for the life of the process.
  *   - Asynchronous calls enqueue kernels on `hip_stream` (a hipStream_t; NULL is
  *     the null stream) and return before they finish. Every argument that can be
  *     checked on the host is checked before anything is enqueued: a call that
