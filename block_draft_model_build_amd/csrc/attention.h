@@ -760,16 +760,17 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         }
         wait_vmcnt<0>();
         __syncthreads();
-        // Leading tiles that every block of the group sees whole, with one wave
-        // per block: pipelined slices (attn_tile_pipelined). The count is
-        // uniform over the workgroup, so the tile loop splits in two with the
-        // same staging and barriers in both.
+        // Leading tiles that this wave's block sees whole, with one wave per
+        // block: pipelined slices (attn_tile_pipelined); the tiles after them
+        // slice by slice. The count is per wave (uniform within it): both
+        // loops stage each tile the same way and meet the workgroup at one
+        // barrier per tile, so the waves of a group whose anchors lie in
+        // different tiles switch loops at different tiles.
         int nfull = 0;
         if constexpr (!REDO && QS == 2) {
-            if (wpb == 1) {
-                int kmin = kbeg + chunk;
-                for (int jj = 0; jj < ng; ++jj) kmin = min(kmin, anchor_of(jj));
-                nfull = kmin > kbeg ? min(ntile, (kmin - kbeg) / SUPER) : 0;
+            if (wpb == 1 && active && a >= 0) {
+                const int kv = min(a, kbeg + chunk);
+                nfull = kv > kbeg ? min(ntile, (kv - kbeg) / SUPER) : 0;
             }
         }
         auto stage_next = [&](int t, auto&& compute) {
