@@ -106,7 +106,12 @@ hipError_t norm_bwd(const float* x, const T* w, const float* dy, const float* re
                     float* dw, int R, int H, float eps, hipStream_t st) {
     ProfScope prof(DFLASH_KERNEL_BWD_NORM, st);
     const int nparts = (R + kNormBwdRows - 1) / kNormBwdRows;
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(nparts), dim3(256), 0, st, x, w, dy, res, out, part, R, H, eps);
+    // float4 columns per thread: the fewest that cover the row
+    const int nv = (H / 4 + 255) / 256;
+    auto kern = nv <= 1 ? rmsnorm_bwd_kernel<T, 1>
+              : nv <= 2 ? rmsnorm_bwd_kernel<T, 2>
+              : nv <= 4 ? rmsnorm_bwd_kernel<T, 4> : rmsnorm_bwd_kernel<T, 8>;
+    hipLaunchKernelGGL(kern, dim3(nparts), dim3(256), 0, st, x, w, dy, res, out, part, R, H, eps);
     hipLaunchKernelGGL(norm_colsum_kernel, dim3((H + 63) / 64), dim3(256), 0, st, part, nparts, H, dw);
     return hipGetLastError();
 }
@@ -248,7 +253,7 @@ dflash_status body_bwd_supported(const dflash_config* cfg) {
     if (s != DFLASH_OK) return s;
     // (Hq * D is a multiple of 128 whenever the config is valid: (Hq + 2 Hkv) D is,
     // and D = 64 forces Hq even.)
-    if (cfg->intermediate % 128 != 0 || cfg->hidden > 256 * 4 * kNormBwdVec)
+    if (cfg->intermediate % 128 != 0 || cfg->hidden > kNormBwdMaxH)
         return DFLASH_ERR_UNSUPPORTED;
     return DFLASH_OK;
 }

@@ -82,23 +82,26 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIN* __restrict__ in
 //   out = res + r (dy w) - x r^3 (sum_j dy_j w_j x_j) / H
 // (res: the residual path's gradient, added here), and per workgroup the
 // partial column sums of dy x r over its kNormBwdRows rows; dw is their sum
-// over workgroups (norm_colsum_kernel, fixed order). A thread keeps up to
-// kNormBwdVec float4 columns of a row and its accumulators in registers:
-// H <= 256 * 4 * kNormBwdVec.
-constexpr int kNormBwdRows = 16;
-constexpr int kNormBwdVec = 8;
+// over workgroups (norm_colsum_kernel, fixed order). A thread keeps NV float4
+// columns of a row (H <= 1024 NV) and its accumulators in registers. Few rows
+// per workgroup and few registers per thread let several workgroups share a
+// compute unit, so several rows are in flight there while one waits at its
+// row reduction: with one 16-row workgroup per compute unit the kernel moved
+// 3.1 TB/s.
+constexpr int kNormBwdRows = 4;
+constexpr int kNormBwdMaxH = 8192;
 
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ x, const T* __restrict__ w,
                                                           const float* __restrict__ dy,
                                                           const float* __restrict__ res, float* __restrict__ out,
                                                           float* __restrict__ part, int rows, int H, float eps) {
     typedef T t4 __attribute__((ext_vector_type(4)));
-    __shared__ float red[2][4];
+    __shared__ float red[2][2][4];
     const int nvec = H / 4, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    f32x4 wv[kNormBwdVec], acc[kNormBwdVec];
+    f32x4 wv[NV], acc[NV];
 #pragma unroll
-    for (int k = 0; k < kNormBwdVec; ++k) {
+    for (int k = 0; k < NV; ++k) {
         const int j = tid + 256 * k;
         acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         wv[k] = acc[k];
@@ -114,72 +117,82 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
         if (row >= rows) break;                       // the same for the whole workgroup
         const f32x4* xr = reinterpret_cast<const f32x4*>(x + row * H);
         const f32x4* gr = reinterpret_cast<const f32x4*>(dy + row * H);
-        f32x4 xv[kNormBwdVec], gv[kNormBwdVec];
+        const f32x4* rs = reinterpret_cast<const f32x4*>(res + row * H);
+        f32x4 xv[NV], gv[NV], rv[NV];
         float ss = 0.f, dot = 0.f;
 #pragma unroll
-        for (int k = 0; k < kNormBwdVec; ++k) {
+        for (int k = 0; k < NV; ++k) {
             const int j = tid + 256 * k;
             xv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            gv[k] = xv[k];
+            gv[k] = rv[k] = xv[k];
             if (j < nvec) {
                 xv[k] = xr[j];
                 gv[k] = gr[j];
+                rv[k] = rs[j];
             }
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 ss += xv[k][q] * xv[k][q];
                 dot += gv[k][q] * wv[k][q] * xv[k][q];
             }
-        }
         for (int o = 32; o > 0; o >>= 1) {
             ss += __shfl_xor(ss, o, 64);
             dot += __shfl_xor(dot, o, 64);
         }
+        // Two copies of the reduction slots (by row parity): a wave can only
+        // rewrite a copy after every wave has read it, one barrier later.
         if (lane == 0) {
-            red[0][wave] = ss;
-            red[1][wave] = dot;
+            red[rr & 1][0][wave] = ss;
+            red[rr & 1][1][wave] = dot;
         }
         __syncthreads();
-        const float tss = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-        const float tdot = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-        __syncthreads();                              // red is rewritten for the next row
+        const float tss = red[rr & 1][0][0] + red[rr & 1][0][1] + red[rr & 1][0][2] + red[rr & 1][0][3];
+        const float tdot = red[rr & 1][1][0] + red[rr & 1][1][1] + red[rr & 1][1][2] + red[rr & 1][1][3];
         const float r = 1.0f / sqrtf(tss / (float)H + eps);
         const float coef = r * r * r * tdot / (float)H;
-        const f32x4* rs = reinterpret_cast<const f32x4*>(res + row * H);
         f32x4* orow = reinterpret_cast<f32x4*>(out + row * H);
 #pragma unroll
-        for (int k = 0; k < kNormBwdVec; ++k) {
+        for (int k = 0; k < NV; ++k) {
             const int j = tid + 256 * k;
             if (j < nvec) {
-                orow[j] = rs[j] + r * gv[k] * wv[k] - xv[k] * coef;
+                orow[j] = rv[k] + r * gv[k] * wv[k] - xv[k] * coef;
                 acc[k] += gv[k] * xv[k] * r;
             }
         }
     }
     f32x4* pr = reinterpret_cast<f32x4*>(part + (int64_t)blockIdx.x * H);
 #pragma unroll
-    for (int k = 0; k < kNormBwdVec; ++k) {
+    for (int k = 0; k < NV; ++k) {
         const int j = tid + 256 * k;
         if (j < nvec) pr[j] = acc[k];
     }
 }
 
-// dw[j] = sum over p < nparts of part[p][j]. A workgroup takes 64 columns;
-// its 4 waves sum the parts p = s (mod 4), then wave 0 adds the four slices in
-// order.
+// dw[j] = sum over p < nparts of part[p][j]. A workgroup takes 64 columns as
+// 16 float4 lanes x 16 slices; slice s sums the parts p = s (mod 16), then
+// slice 0 adds the 16 slice sums in order. H is a multiple of 4.
 static __global__ __launch_bounds__(256) void norm_colsum_kernel(const float* __restrict__ part, int nparts, int H,
-                                                          float* __restrict__ dw) {
-    __shared__ float sl[4][64];
-    const int c = threadIdx.x & 63, s = threadIdx.x >> 6;
-    const int j = blockIdx.x * 64 + c;
-    float a = 0.f;
+                                                                 float* __restrict__ dw) {
+    __shared__ f32x4 sl[16][16];
+    const int c4 = threadIdx.x & 15, s = threadIdx.x >> 4;
+    const int j = blockIdx.x * 64 + c4 * 4;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
     if (j < H) {
 #pragma unroll 8
-        for (int p = s; p < nparts; p += 4) a += part[(int64_t)p * H + j];
+        for (int p = s; p < nparts; p += 16) a += *reinterpret_cast<const f32x4*>(part + (int64_t)p * H + j);
     }
-    sl[s][c] = a;
+    sl[s][c4] = a;
     __syncthreads();
-    if (s == 0 && j < H) dw[j] = ((sl[0][c] + sl[1][c]) + sl[2][c]) + sl[3][c];
+    if (s == 0 && j < H) {
+        f32x4 t = sl[0][c4];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) t += sl[q][c4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dw[j + q] = t[q];   // dw: caller's buffer, 4-byte aligned
+    }
 }
 
 }  // namespace dflash
