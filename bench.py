@@ -299,7 +299,28 @@ def next_rows(d, torch, device="cuda"):
                                   "roofline": {"bound": "mfma", "achieved": round(ach, 2),
                                                "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
                                                "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
-    del hid, W, dh, ws5
+    # The training pair that keeps the fp32 logits: the forward's GEMM also
+    # stores them, and the backward takes dz from them in one elementwise pass
+    # (rows x V fp32 read, rows x V bf16 written), then the one product dz W_lm.
+    logits = torch.empty(d.dflash_lm_head_ce_logits_size(rows, V), dtype=torch.uint8, device=device)
+    call = lambda: d.dflash_lm_head_ce_train(cfg3, hid, W, tg, lm, 7.0, ce, loss, logits, ws2)
+    ms_gemm = hook_ms(d, torch, [("lm_head", 1)], call)
+    ms = ms_gemm + hook_ms(d, torch, [("lm_ce", 1)], call)
+    out["lm_head_ce_train"] = {"ms": round(ms, 4), "lm_head_gemm_ms": round(ms_gemm, 4),
+                               "logits_bytes": logits.numel()}
+    call = lambda: d.dflash_lm_head_ce_backward_saved(cfg3, rows, logits, W, tg, lm, 7.0, ce, 1.0, dh, ws5)
+    parts = {k: hook_ms(d, torch, [(k, 1)], call) for k in ("lm_bwd_prep", "lm_bwd_dz", "lm_bwd_dh")}
+    ms = sum(parts.values())
+    dz_bytes = rows * ((V + 63) // 64 * 64) * (4 + 2)
+    out["lm_head_ce_backward_saved"] = {
+        "ms": round(ms, 4), **{k + "_ms": round(v, 4) for k, v in parts.items()},
+        "dz_pass": {"bound": "hbm", "achieved": round(dz_bytes / (parts["lm_bwd_dz"] / 1e3) / 1e9, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(dz_bytes / (parts["lm_bwd_dz"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (ms / 1e3) / 1e12, 2),
+                     "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"], 4)}}
+    del hid, W, dh, ws5, logits
     # Training side: backward of one layer's dual-source attention at the
     # training shape (8 sequences of 4096, 32 blocks each at random anchors).
     T = wt.batch * wt.seq_len
@@ -388,6 +409,7 @@ class TrainingBuffers:
         self.ce, self.loss = e(R), e(1, dt=torch.float64)
         self.ws_lm = u8(d.dflash_lm_head_ce_workspace_size(R, vocab))
         self.ws_lmb = u8(d.dflash_lm_head_ce_backward_workspace_size(cfg, R, vocab))
+        self.logits = u8(d.dflash_lm_head_ce_logits_size(R, vocab))
         self.grads = [{k: e(*v.shape) for k, v in Lw.items()} for Lw in inp["layers"]]
         self.dck = [e(w.num_kv_heads, T, w.head_dim) for _ in range(L)]
         self.dcv = [e(w.num_kv_heads, w.head_dim, T) for _ in range(L)]
@@ -417,10 +439,11 @@ class TrainingBuffers:
         pos = self.positions.reshape(-1).long().clamp(0, w.seq_len - 1)
         targets = self.tokens[self.row_of, pos].contiguous()
         lm = self.loss_mask.reshape(-1)
-        d.dflash_lm_head_ce(cfg, self.out, self.lm_head, targets, lm, 7.0, self.ce, self.loss, self.ws_lm)
+        d.dflash_lm_head_ce_train(cfg, self.out, self.lm_head, targets, lm, 7.0, self.ce, self.loss, self.logits,
+                                  self.ws_lm)
         ev[4].record()
-        d.dflash_lm_head_ce_backward(cfg, self.out, self.lm_head, targets, lm, 7.0, self.ce, 1.0, self.d_out,
-                                     self.ws_lmb)
+        d.dflash_lm_head_ce_backward_saved(cfg, self.out.shape[0], self.logits, self.lm_head, targets, lm, 7.0,
+                                           self.ce, 1.0, self.d_out, self.ws_lmb)
         ev[5].record()
         d.dflash_body_backward(cfg, nb, self.reserve, i["layers"], self.ck, self.cv, T, self.base, anc, val,
                                self.d_out, self.demb, self.grads, self.dck, self.dcv, self.ws_bb)
@@ -434,8 +457,8 @@ class TrainingBuffers:
 def train_step_row(d, torch, w, vocab, device, reps=3):
     """One whole training step of the 5-layer training workload through the
     library, timed end to end with events on the launch stream: plan, context
-    projection, training forward (reserve space), LM head + decayed CE, its
-    backward, body backward, W_proj backward. Synthetic inputs of the workload's
+    projection, training forward (reserve space), LM head + decayed CE keeping
+    its logits, its backward from them, body backward, W_proj backward. Synthetic inputs of the workload's
     shapes; targets are random tokens at the block positions; frozen synthetic
     LM head of the given vocabulary. Also the events between the stages."""
     bufs = TrainingBuffers(d, torch, w, vocab, device)

@@ -11,6 +11,7 @@ The names mirror the C entry points:
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
   dflash_lm_head_ce_backward, dflash_lm_head_ce_backward_workspace_size,
+  dflash_lm_head_ce_train, dflash_lm_head_ce_logits_size, dflash_lm_head_ce_backward_saved,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
   dflash_body_forward_train, dflash_body_train_reserve_size, dflash_body_backward,
@@ -39,6 +40,7 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_lm_head_ce_backward", "dflash_lm_head_ce_backward_workspace_size",
+            "dflash_lm_head_ce_train", "dflash_lm_head_ce_logits_size", "dflash_lm_head_ce_backward_saved",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
             "dflash_body_forward_train", "dflash_body_train_reserve_size", "dflash_body_backward",
@@ -116,6 +118,13 @@ def _load() -> ctypes.CDLL:
     lib.dflash_lm_head_ce_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_lm_head_ce_workspace_size.argtypes = [I32, I32]
     lib.dflash_lm_head_ce_workspace_size.restype = ctypes.c_size_t
+    lib.dflash_lm_head_ce_train.argtypes = [CFG, I32, P, P, I32, P, P, ctypes.c_double, P, P, P, SZ, P, SZ, P]
+    lib.dflash_lm_head_ce_train.restype = ctypes.c_int
+    lib.dflash_lm_head_ce_logits_size.argtypes = [I32, I32]
+    lib.dflash_lm_head_ce_logits_size.restype = ctypes.c_size_t
+    lib.dflash_lm_head_ce_backward_saved.argtypes = [CFG, I32, P, SZ, P, I32, P, P, ctypes.c_double, P,
+                                                     ctypes.c_double, P, P, SZ, P]
+    lib.dflash_lm_head_ce_backward_saved.restype = ctypes.c_int
     lib.dflash_block_attn_backward.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
                                                SZ, P]
     lib.dflash_block_attn_backward.restype = ctypes.c_int
@@ -346,6 +355,37 @@ def dflash_lm_head_ce(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, de
                                _ptr(loss_mask), float(decay_tau), _ptr(row_ce), _ptr(loss), wp, wb,
                                _stream(stream, lm_head))
     _check("dflash_lm_head_ce", s)
+
+
+def dflash_lm_head_ce_logits_size(rows: int, vocab: int) -> int:
+    return _lib.dflash_lm_head_ce_logits_size(int(rows), int(vocab))
+
+
+def dflash_lm_head_ce_train(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, decay_tau: float, row_ce, loss,
+                            logits, workspace, stream=None) -> None:
+    """dflash_lm_head_ce that also writes the fp32 logits into `logits` (a device buffer of
+    dflash_lm_head_ce_logits_size(rows, vocab) bytes or more; rows of vocab rounded up to 64)."""
+    rows = hidden.shape[0]
+    vocab = lm_head.shape[0]
+    wp, wb = _ws(workspace)
+    lp, lb = _ws(logits)
+    s = _lib.dflash_lm_head_ce_train(ctypes.byref(cfg), int(rows), _ptr(hidden), _ptr(lm_head), int(vocab),
+                                     _ptr(targets), _ptr(loss_mask), float(decay_tau), _ptr(row_ce), _ptr(loss),
+                                     lp, lb, wp, wb, _stream(stream, lm_head))
+    _check("dflash_lm_head_ce_train", s)
+
+
+def dflash_lm_head_ce_backward_saved(cfg: DFlashConfig, rows: int, logits, lm_head, targets, loss_mask,
+                                     decay_tau: float, row_ce, d_loss: float, d_hidden, workspace,
+                                     stream=None) -> None:
+    """dflash_lm_head_ce_backward from the logits dflash_lm_head_ce_train kept -> d_hidden [rows, H]."""
+    vocab = int(lm_head.shape[0])
+    wp, wb = _ws(workspace)
+    lp, lb = _ws(logits)
+    s = _lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), int(rows), lp, lb, _ptr(lm_head), vocab,
+                                              _ptr(targets), _ptr(loss_mask), float(decay_tau), _ptr(row_ce),
+                                              float(d_loss), _ptr(d_hidden), wp, wb, _stream(stream, lm_head))
+    _check("dflash_lm_head_ce_backward_saved", s)
 
 
 def dflash_lm_head_ce_backward_workspace_size(cfg: DFlashConfig, rows: int, vocab: int) -> int:

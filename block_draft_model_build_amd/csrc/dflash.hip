@@ -388,14 +388,19 @@ extern "C" size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab) 
     return part + tl + 256;
 }
 
+extern "C" size_t dflash_lm_head_ce_logits_size(int32_t rows, int32_t vocab) {
+    if (rows < 0 || vocab < 1 || (int64_t)vocab + 255 > INT32_MAX) return 0;
+    return (size_t)rows * (size_t)lm_logits_ld(vocab) * sizeof(float);
+}
+
 template <typename T>
 static hipError_t lm_head_ce_t(const dflash_config& c, int rows, const T* hidden, const T* lm_head, int vocab,
                                const int32_t* targets, const uint8_t* loss_mask, double tau, float* row_ce,
-                               double* loss, char* ws, hipStream_t st) {
+                               double* loss, float* logits, char* ws, hipStream_t st) {
     const int groups = lm_groups(vocab);
     float* part = reinterpret_cast<float*>(ws);
     float* tl = reinterpret_cast<float*>(ws + align_up((size_t)rows * groups * 2 * sizeof(float), 256));
-    EpLseCE<T> ep{part, tl, targets, groups, vocab};
+    EpLseCE<T> ep{part, tl, targets, groups, vocab, logits, lm_logits_ld(vocab)};
     hipError_t e;
     {
         ProfScope prof(DFLASH_KERNEL_LM_HEAD, st);
@@ -418,20 +423,10 @@ static hipError_t lm_head_ce_t(const dflash_config& c, int rows, const T* hidden
     return hipGetLastError();
 }
 
-extern "C" dflash_status dflash_lm_head_ce(const dflash_config* cfg, int32_t rows, const void* hidden,
-                                           const void* lm_head, int32_t vocab, const int32_t* targets,
-                                           const uint8_t* loss_mask, double decay_tau, float* row_ce,
-                                           double* loss, void* workspace, size_t workspace_bytes,
-                                           void* hip_stream) {
-    dflash_status s = check_config(cfg);
-    if (s != DFLASH_OK) return s;
-    if (rows < 0 || vocab < 1 || !(decay_tau > 0.0)) return DFLASH_ERR_INVALID_ARG;
-    if ((int64_t)vocab + 255 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
-    if (hidden == nullptr && rows > 0) return DFLASH_ERR_INVALID_ARG;
-    if (lm_head == nullptr || loss == nullptr || (rows > 0 && (targets == nullptr || loss_mask == nullptr ||
-                                                               row_ce == nullptr)) ||
-        !aligned16(hidden) || !aligned16(lm_head))
-        return DFLASH_ERR_INVALID_ARG;
+static dflash_status lm_head_ce_entry(const dflash_config* cfg, int32_t rows, const void* hidden,
+                                      const void* lm_head, int32_t vocab, const int32_t* targets,
+                                      const uint8_t* loss_mask, double decay_tau, float* row_ce, double* loss,
+                                      float* logits, void* workspace, size_t workspace_bytes, void* hip_stream) {
     const size_t need = dflash_lm_head_ce_workspace_size(rows, vocab);
     if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return DFLASH_ERR_WORKSPACE;
@@ -445,11 +440,54 @@ extern "C" dflash_status dflash_lm_head_ce(const dflash_config* cfg, int32_t row
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = lm_head_ce_t<__bf16>(*cfg, rows, static_cast<const __bf16*>(hidden), static_cast<const __bf16*>(lm_head),
-                                 vocab, targets, loss_mask, decay_tau, row_ce, loss, ws, st);
+                                 vocab, targets, loss_mask, decay_tau, row_ce, loss, logits, ws, st);
     else
         e = lm_head_ce_t<float>(*cfg, rows, static_cast<const float*>(hidden), static_cast<const float*>(lm_head),
-                                vocab, targets, loss_mask, decay_tau, row_ce, loss, ws, st);
+                                vocab, targets, loss_mask, decay_tau, row_ce, loss, logits, ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+static dflash_status lm_head_ce_check(const dflash_config* cfg, int32_t rows, const void* hidden,
+                                      const void* lm_head, int32_t vocab, const int32_t* targets,
+                                      const uint8_t* loss_mask, double decay_tau, const float* row_ce,
+                                      const double* loss) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (rows < 0 || vocab < 1 || !(decay_tau > 0.0)) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)vocab + 255 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if (hidden == nullptr && rows > 0) return DFLASH_ERR_INVALID_ARG;
+    if (lm_head == nullptr || loss == nullptr || (rows > 0 && (targets == nullptr || loss_mask == nullptr ||
+                                                               row_ce == nullptr)) ||
+        !aligned16(hidden) || !aligned16(lm_head))
+        return DFLASH_ERR_INVALID_ARG;
+    return DFLASH_OK;
+}
+
+extern "C" dflash_status dflash_lm_head_ce(const dflash_config* cfg, int32_t rows, const void* hidden,
+                                           const void* lm_head, int32_t vocab, const int32_t* targets,
+                                           const uint8_t* loss_mask, double decay_tau, float* row_ce,
+                                           double* loss, void* workspace, size_t workspace_bytes,
+                                           void* hip_stream) {
+    const dflash_status s = lm_head_ce_check(cfg, rows, hidden, lm_head, vocab, targets, loss_mask, decay_tau,
+                                             row_ce, loss);
+    if (s != DFLASH_OK) return s;
+    return lm_head_ce_entry(cfg, rows, hidden, lm_head, vocab, targets, loss_mask, decay_tau, row_ce, loss, nullptr,
+                            workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" dflash_status dflash_lm_head_ce_train(const dflash_config* cfg, int32_t rows, const void* hidden,
+                                                 const void* lm_head, int32_t vocab, const int32_t* targets,
+                                                 const uint8_t* loss_mask, double decay_tau, float* row_ce,
+                                                 double* loss, float* logits, size_t logits_bytes, void* workspace,
+                                                 size_t workspace_bytes, void* hip_stream) {
+    const dflash_status s = lm_head_ce_check(cfg, rows, hidden, lm_head, vocab, targets, loss_mask, decay_tau,
+                                             row_ce, loss);
+    if (s != DFLASH_OK) return s;
+    if (rows > 0 && (logits == nullptr || logits_bytes < dflash_lm_head_ce_logits_size(rows, vocab) ||
+                     !aligned16(logits)))
+        return DFLASH_ERR_INVALID_ARG;
+    return lm_head_ce_entry(cfg, rows, hidden, lm_head, vocab, targets, loss_mask, decay_tau, row_ce, loss, logits,
+                            workspace, workspace_bytes, hip_stream);
 }
 
 // lengths[i] = min(lengths[i], max(keep[i], 0)).

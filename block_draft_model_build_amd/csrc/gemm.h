@@ -313,12 +313,15 @@ struct EpStoreF32 {
 // n_cols excluded), written to part[row][group], and the logit of the row's
 // target token. The 32 lanes of a wave half hold 32 consecutive columns of a
 // row, so each statistic is an in-lane pass over the NI column tiles plus a
-// 5-step exchange within the half.
+// 5-step exchange within the half. With `logits` set the fp32 logits are kept
+// too (logits[row * ldl + col], col < n_cols).
 template <typename T> struct EpLseCE {
     float* part;                  // [M][groups][2]
     float* target_logit;          // [M]
     const int32_t* targets;       // [M]
     int groups, n_cols;
+    float* logits = nullptr;      // optional [M][ldl]
+    int64_t ldl = 0;
     template <int MI, int NI, int WN>
     __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
         const int grp = nb / WN;
@@ -349,6 +352,12 @@ template <typename T> struct EpLseCE {
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
                     if (col + j * 32 == t) target_logit[row] = acc[i][j][e];
+                if (logits != nullptr) {
+                    float* lr = logits + (int64_t)row * ldl;
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        if (col + j * 32 < n_cols) lr[col + j * 32] = acc[i][j][e];
+                }
             }
     }
 };

@@ -128,6 +128,10 @@ inline RopeTurns make_rope_turns(const dflash_config& c) {
 
 dflash_status check_config(const dflash_config* c);
 
+// Row stride of the fp32 logits dflash_lm_head_ce_train keeps (and of the
+// backward's dz): the vocabulary rounded up to 64 columns.
+inline int64_t lm_logits_ld(int vocab) { return ((int64_t)vocab + 63) / 64 * 64; }
+
 // The attention backward (attn_bwd.hip) for callers that checked the arguments:
 // the kernels of dflash_block_attn_backward on `st`, with `ws` holding
 // attn_backward_workspace(c, nb) bytes. A null block_valid keeps every row's

@@ -41,6 +41,64 @@ __global__ __launch_bounds__(256) void target_logit_kernel(const T* hidden, cons
     if (threadIdx.x == 0) zt[row] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// zt[r] = logits[r][targets[r]] from the logits the training forward kept (0
+// for a target outside the vocabulary).
+__global__ __launch_bounds__(256) void saved_target_logit_kernel(const float* logits, int64_t ldl,
+                                                                 const int32_t* targets, int rows, int vocab,
+                                                                 float* zt) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const int t = targets[r];
+    zt[r] = (t >= 0 && t < vocab) ? logits[(int64_t)r * ldl + t] : 0.f;
+}
+
+// dz from the kept logits, the same arithmetic as EpCEGrad: 8 consecutive
+// columns per thread (two 16-byte loads), exact zeros past the vocabulary up
+// to ld and on rows whose coef is 0 (their logits are not read).
+template <typename T>
+__device__ __forceinline__ void ce_grad_saved_run(const float* __restrict__ logits, int64_t ld,
+                                                  const float* __restrict__ coef, const float* __restrict__ lse,
+                                                  const int32_t* __restrict__ targets, int vocab,
+                                                  T* __restrict__ dz, int64_t row, int64_t c0) {
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    const float c = coef[row], L = lse[row];
+    const int t = targets[row];
+    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c != 0.f) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(logits + row * ld + c0);
+        const f32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            z[q] = a[q];
+            z[4 + q] = b[q];
+        }
+    }
+    t8 o;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int64_t col = c0 + q;
+        float v = 0.f;
+        if (col < vocab && c != 0.f) v = c * (__expf(z[q] - L) - (col == t ? 1.f : 0.f));
+        o[q] = from_f32<T>(v);
+    }
+    *reinterpret_cast<t8*>(dz + row * ld + c0) = o;
+}
+
+// A workgroup takes 2048 columns of one row per item, items row-major.
+template <typename T>
+__global__ __launch_bounds__(256) void ce_grad_saved_kernel(const float* __restrict__ logits, int64_t ld, int rows,
+                                                            const float* __restrict__ coef,
+                                                            const float* __restrict__ lse,
+                                                            const int32_t* __restrict__ targets, int vocab,
+                                                            T* __restrict__ dz) {
+    const int64_t chunks = (ld + 2047) / 2048, items = (int64_t)rows * chunks;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const int64_t row = item / chunks;
+        const int64_t c0 = (item - row * chunks) * 2048 + (int64_t)threadIdx.x * 8;
+        if (c0 < ld) ce_grad_saved_run<T>(logits, ld, coef, lse, targets, vocab, dz, row, c0);
+    }
+}
+
 // D = sum of m w over the rows that count (fp64, fixed order as the forward's
 // loss), then per row coef = d_loss m w / D and lse = row_ce + zt.
 __global__ __launch_bounds__(1024) void ce_grad_rows_kernel(const float* row_ce, const float* zt,
@@ -79,7 +137,7 @@ struct LmBwdLayout {
 LmBwdLayout lm_bwd_layout(const dflash_config& c, int64_t rows, int64_t vocab) {
     LmBwdLayout l{};
     const size_t A = 256, eb = (size_t)elem_bytes(c);
-    l.vp = (vocab + 63) / 64 * 64;
+    l.vp = lm_logits_ld((int)vocab);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -132,6 +190,44 @@ hipError_t lm_bwd_t(const dflash_config& c, int rows, const T* hidden, const T* 
                    EpStore<T>{d_hidden, H}, st);
 }
 
+// The same gradient from the logits dflash_lm_head_ce_train kept: the row
+// statistics read the target logit from them, dz is one elementwise pass, and
+// only the second product remains.
+template <typename T>
+hipError_t lm_bwd_saved_t(const dflash_config& c, int rows, const float* logits, const T* W, int vocab,
+                          const int32_t* targets, const uint8_t* loss_mask, double tau, const float* row_ce,
+                          double d_loss, T* d_hidden, char* ws, hipStream_t st) {
+    const LmBwdLayout lay = lm_bwd_layout(c, rows, vocab);
+    const int H = c.hidden;
+    const int64_t Vp = lay.vp;
+    float* zt = reinterpret_cast<float*>(ws + lay.zt);
+    float* coef = reinterpret_cast<float*>(ws + lay.coef);
+    float* lse = reinterpret_cast<float*>(ws + lay.lse);
+    T* dz = reinterpret_cast<T*>(ws + lay.dz);
+    T* wt = reinterpret_cast<T*>(ws + lay.wt);
+    {
+        ProfScope prof(DFLASH_KERNEL_LM_BWD_PREP, st);
+        hipLaunchKernelGGL(saved_target_logit_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, logits,
+                           Vp, targets, rows, vocab, zt);
+        hipLaunchKernelGGL(ce_grad_rows_kernel, dim3(1), dim3(1024), 0, st, row_ce, zt, targets, loss_mask, rows, vocab,
+                           c.block_size, tau, d_loss, coef, lse);
+        hipLaunchKernelGGL((transpose_kernel<T, SrcPlain<T>>), dim3((unsigned)(Vp / 64), (unsigned)(H / 64)), dim3(256),
+                           0, st, SrcPlain<T>{W, H}, (int64_t)vocab, Vp, (int64_t)H, wt, Vp);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    {
+        ProfScope prof(DFLASH_KERNEL_LM_BWD_DZ, st);
+        const int64_t items = (int64_t)rows * ((Vp + 2047) / 2048);
+        hipLaunchKernelGGL(ce_grad_saved_kernel<T>, dim3((unsigned)(items < (1 << 20) ? items : (1 << 20))), dim3(256),
+                           0, st, logits, Vp, rows, coef, lse, targets, vocab, dz);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    return gemm<T>(DFLASH_KERNEL_LM_BWD_DH, rows, H, (int)Vp, APlain<T>{dz, Vp}, BPlain<T>{wt, Vp},
+                   EpStore<T>{d_hidden, H}, st);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -170,5 +266,35 @@ extern "C" dflash_status dflash_lm_head_ce_backward(const dflash_config* cfg, in
     else
         e = lm_bwd_t<float>(*cfg, rows, static_cast<const float*>(hidden), static_cast<const float*>(lm_head), vocab,
                             targets, loss_mask, decay_tau, row_ce, d_loss, static_cast<float*>(d_hidden), ws, st);
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_lm_head_ce_backward_saved(const dflash_config* cfg, int32_t rows, const float* logits,
+                                                          size_t logits_bytes, const void* lm_head, int32_t vocab,
+                                                          const int32_t* targets, const uint8_t* loss_mask,
+                                                          double decay_tau, const float* row_ce, double d_loss,
+                                                          void* d_hidden, void* workspace, size_t workspace_bytes,
+                                                          void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (rows < 0 || vocab < 1 || !(decay_tau > 0.0)) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)vocab + 255 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if (rows == 0) return DFLASH_OK;
+    if (logits == nullptr || logits_bytes < (size_t)rows * (size_t)lm_logits_ld(vocab) * sizeof(float) ||
+        lm_head == nullptr || targets == nullptr || loss_mask == nullptr || row_ce == nullptr || d_hidden == nullptr ||
+        !aligned16(logits) || !aligned16(lm_head) || !aligned16(d_hidden))
+        return DFLASH_ERR_INVALID_ARG;
+    const size_t need = lm_bwd_layout(*cfg, rows, vocab).total;
+    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return DFLASH_ERR_WORKSPACE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e;
+    if (cfg->dtype == DFLASH_BF16)
+        e = lm_bwd_saved_t<__bf16>(*cfg, rows, logits, static_cast<const __bf16*>(lm_head), vocab, targets, loss_mask,
+                                   decay_tau, row_ce, d_loss, static_cast<__bf16*>(d_hidden), ws, st);
+    else
+        e = lm_bwd_saved_t<float>(*cfg, rows, logits, static_cast<const float*>(lm_head), vocab, targets, loss_mask,
+                                  decay_tau, row_ce, d_loss, static_cast<float*>(d_hidden), ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }

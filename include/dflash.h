@@ -333,8 +333,9 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_BWD_DATA = 18,     /* GEMMs of the activation gradients (du, dy, do, dx) */
     DFLASH_KERNEL_BWD_WEIGHT = 19,   /* GEMMs of the weight gradients (contraction over rows) */
     DFLASH_KERNEL_BWD_NORM = 20,     /* RMSNorm backward and its weight-gradient column sums */
-    DFLASH_KERNEL_LM_BWD_PREP = 21,  /* dflash_lm_head_ce_backward: row statistics, LM head transpose */
-    DFLASH_KERNEL_LM_BWD_DZ = 22,    /* GEMM of the logits with the CE gradient epilogue */
+    DFLASH_KERNEL_LM_BWD_PREP = 21,  /* dflash_lm_head_ce_backward(_saved): row statistics, LM head transpose */
+    DFLASH_KERNEL_LM_BWD_DZ = 22,    /* dz: GEMM of the logits with the CE gradient epilogue, or (_saved)
+                                        the elementwise pass over the kept logits */
     DFLASH_KERNEL_LM_BWD_DH = 23,    /* GEMM d_hidden = dz W_lm */
     DFLASH_KERNEL_COUNT = 24
 } dflash_kernel;
@@ -417,7 +418,7 @@ dflash_status dflash_verify_sample(const int32_t *draft, const float *p, const f
  * from the target model; [P2] step 4: the loss mask excludes the anchor and
  * invalid positions.
  *
- *   z_r      = hidden[r] W_lm^T                 (fp32 accumulation, never stored)
+ *   z_r      = hidden[r] W_lm^T                 (fp32 accumulation; not stored here)
  *   CE_r     = logsumexp(z_r) - z_r[targets[r]]
  *   w_r      = exp(-(k - 1) / decay_tau),  k = r mod block_size   (k = 1: weight 1)
  *   loss     = sum(m_r w_r CE_r) / sum(m_r w_r), m_r = loss_mask[r]; 0 if no row counts
@@ -440,6 +441,29 @@ dflash_status dflash_lm_head_ce(const dflash_config *cfg, int32_t rows, const vo
                                 double *loss, void *workspace, size_t workspace_bytes,
                                 void *hip_stream);
 size_t dflash_lm_head_ce_workspace_size(int32_t rows, int32_t vocab);
+
+/*
+ * dflash_lm_head_ce_train -- dflash_lm_head_ce that also keeps the fp32 logits
+ * z for the backward (dflash_lm_head_ce_backward_saved), the way a training
+ * forward keeps its activations, so that the gradient does not recompute the
+ * product with the LM head. Same loss as dflash_lm_head_ce ([P1] "How it
+ * works", Loss); row_ce and loss are bit-identical to its outputs.
+ *
+ *   logits        device f32 [rows][ldl], ldl = vocab rounded up to a multiple of
+ *                 64; z_r[v] at logits[r * ldl + v] for v < vocab (columns past
+ *                 the vocabulary are not written). 16-byte aligned, caller-owned,
+ *                 logits_bytes >= dflash_lm_head_ce_logits_size(rows, vocab).
+ *   other arguments as dflash_lm_head_ce (same workspace size).
+ * Errors: as dflash_lm_head_ce; INVALID_ARG also for a null, small or
+ * misaligned logits buffer when rows > 0.
+ */
+dflash_status dflash_lm_head_ce_train(const dflash_config *cfg, int32_t rows, const void *hidden,
+                                      const void *lm_head, int32_t vocab, const int32_t *targets,
+                                      const uint8_t *loss_mask, double decay_tau, float *row_ce, double *loss,
+                                      float *logits, size_t logits_bytes, void *workspace,
+                                      size_t workspace_bytes, void *hip_stream);
+/* rows * ldl * 4 bytes (0 for invalid sizes). */
+size_t dflash_lm_head_ce_logits_size(int32_t rows, int32_t vocab);
 
 /*
  * dflash_lm_head_ce_backward -- gradient of dflash_lm_head_ce's loss with
@@ -474,6 +498,27 @@ dflash_status dflash_lm_head_ce_backward(const dflash_config *cfg, int32_t rows,
                                          double d_loss, void *d_hidden, void *workspace, size_t workspace_bytes,
                                          void *hip_stream);
 size_t dflash_lm_head_ce_backward_workspace_size(const dflash_config *cfg, int32_t rows, int32_t vocab);
+
+/*
+ * dflash_lm_head_ce_backward_saved -- dflash_lm_head_ce_backward from the
+ * logits dflash_lm_head_ce_train kept for the same rows, targets and mask:
+ * lse_r = row_ce[r] + logits[r][targets[r]], dz_r = c_r (softmax(z_r) -
+ * onehot) in one elementwise pass over the logits, d_hidden = dz W_lm. The
+ * hidden rows are not read. Same arithmetic as dflash_lm_head_ce_backward per
+ * element of dz, except that the target logit in lse is the forward's own value
+ * rather than a recomputed dot product; the same workspace size.
+ *
+ *   logits, logits_bytes   as dflash_lm_head_ce_train wrote them
+ *   other arguments        as dflash_lm_head_ce_backward
+ * Errors: as dflash_lm_head_ce_backward; INVALID_ARG also for a null, small or
+ * misaligned logits buffer when rows > 0.
+ */
+dflash_status dflash_lm_head_ce_backward_saved(const dflash_config *cfg, int32_t rows, const float *logits,
+                                               size_t logits_bytes, const void *lm_head, int32_t vocab,
+                                               const int32_t *targets, const uint8_t *loss_mask,
+                                               double decay_tau, const float *row_ce, double d_loss,
+                                               void *d_hidden, void *workspace, size_t workspace_bytes,
+                                               void *hip_stream);
 
 /*
  * dflash_block_attn_backward -- gradients of dflash_block_attn. [P2] "How It

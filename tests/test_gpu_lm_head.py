@@ -164,3 +164,83 @@ def test_backward_full_size_sampled_blocks():
     ref *= wts[idx].sum() / wts.sum()
     _cmp_rel(dh[sub], ref, GRAD_TOL, "sampled d_hidden")
     assert torch.isfinite(dh.float()).all()
+
+
+# ---------------------------------------------------------------- kept logits
+# dflash_lm_head_ce_train keeps the fp32 logits; dflash_lm_head_ce_backward_saved
+# takes the gradient from them. The forward runs the same GEMM and reductions as
+# dflash_lm_head_ce, so the row CEs and the loss are bit-identical; the logits are
+# fp32 sums of exact products, within the forward's bar of hidden W^T in fp64.
+# The saved backward recovers lse = row_ce + z_target with the forward's own
+# target logit, where the recomputing backward recomputes that logit as a dot
+# product (a different fp32 summation order, ~1e-6 apart): the two d_hidden agree
+# to that, i.e. up to a bf16 rounding of dz flipping now and then (rel-L2 1e-3),
+# and each meets the oracle's bar.
+SAVED_VS_RECOMPUTE = dict(rel_l2=1e-3, max_rel=1e-2)
+
+
+def _run_train(w, h, W, t, mask, tau):
+    cfg = d.config_from_workload(w)
+    rows, vocab = h.shape[0], W.shape[0]
+    ce = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    loss = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    ws = torch.empty(d.dflash_lm_head_ce_workspace_size(rows, vocab), dtype=torch.uint8, device="cuda")
+    nbytes = d.dflash_lm_head_ce_logits_size(rows, vocab)
+    ldl = (vocab + 63) // 64 * 64
+    assert nbytes == rows * ldl * 4
+    logits = torch.full((rows, ldl), float("nan"), dtype=torch.float32, device="cuda")
+    d.dflash_lm_head_ce_train(cfg, h, W, t, mask, tau, ce, loss, logits, ws)
+    torch.cuda.synchronize()
+    return ce, float(loss.item()), logits
+
+
+def _run_bwd_saved(w, rows, logits, W, t, mask, tau, ce, d_loss=1.0):
+    cfg = d.config_from_workload(w)
+    vocab, H = W.shape
+    dh = torch.full((rows, H), float("nan"), dtype=W.dtype, device="cuda")
+    ws = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg, rows, vocab), dtype=torch.uint8, device="cuda")
+    d.dflash_lm_head_ce_backward_saved(cfg, rows, logits, W, t, mask, tau, ce, d_loss, dh, ws)
+    torch.cuda.synchronize()
+    return dh
+
+
+@pytest.mark.parametrize("w,rows,vocab,tol", [
+    (SMALL, 48, 1000, GRAD_TOL),
+    (SMALL, 300, 4099, GRAD_TOL),
+    (WORKLOADS["c1"], 32, 777, GRAD_TOL_F32),
+])
+def test_kept_logits_small(w, rows, vocab, tol):
+    h, W, t, mask = _inputs(w, rows, vocab, seed=rows + vocab + 2)
+    t[5] = -1
+    t[9] = vocab
+    tau = 3.0
+    ce, loss = _run(w, h, W, t, mask, tau)
+    ce2, loss2, logits = _run_train(w, h, W, t, mask, tau)
+    assert torch.equal(ce, ce2) and loss == loss2
+    ref_z = np64(h) @ np64(W).T
+    compare(logits[:, :vocab], ref_z, dict(rel_l2=1e-5, max_abs=1e-4) if w.dtype == "bf16" else CE_TOL_F32,
+            "kept logits")
+    dh = _run_bwd(w, h, W, t, mask, tau, ce)
+    dh2 = _run_bwd_saved(w, rows, logits, W, t, mask, tau, ce)
+    _cmp_rel(dh2, np64(dh), SAVED_VS_RECOMPUTE if w.dtype == "bf16" else GRAD_TOL_F32, "saved vs recomputed")
+    skip = (mask == 0).cpu().numpy()
+    skip[[5, 9]] = True
+    assert (dh2.cpu()[torch.from_numpy(skip)] == 0).all()
+    ref = oracle.lm_head_ce_backward(np64(h), np64(W), t.cpu().numpy(), mask.cpu().numpy(), w.block_size, tau)
+    _cmp_rel(dh2, ref, tol, "d_hidden from kept logits")
+    assert torch.equal(_run_bwd_saved(w, rows, logits, W, t, mask, tau, ce, 2.0), 2 * dh2)
+
+
+def test_kept_logits_full_size():
+    # The training shape: 4096 block rows x vocabulary 151936 x hidden 4096.
+    w = WORKLOADS["c3"]
+    rows, vocab, tau = w.num_blocks * w.block_size, 151936, 7.0
+    h, W, t, mask = _inputs(w, rows, vocab, seed=8)
+    ce, loss = _run(w, h, W, t, mask, tau)
+    ce2, loss2, logits = _run_train(w, h, W, t, mask, tau)
+    assert torch.equal(ce, ce2) and loss == loss2
+    sample = torch.tensor([0, 1, 2047, 4095], device="cuda")
+    compare(logits[sample, :vocab], np64(h[sample]) @ np64(W).T, dict(rel_l2=1e-5, max_abs=1e-4), "kept logits rows")
+    dh = _run_bwd(w, h, W, t, mask, tau, ce)
+    dh2 = _run_bwd_saved(w, rows, logits, W, t, mask, tau, ce)
+    _cmp_rel(dh2, np64(dh), SAVED_VS_RECOMPUTE, "saved vs recomputed")

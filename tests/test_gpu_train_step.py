@@ -4,8 +4,9 @@ trained with an optimizer step; angelspec "DFlash", How it works, Loss, and
 Configuration: the LM head is the target's, frozen).
 
 GPU: dflash_build_plan -> dflash_ctx_proj -> dflash_body_forward_train ->
-dflash_lm_head_ce -> dflash_lm_head_ce_backward -> dflash_body_backward ->
-dflash_ctx_proj_backward. Oracle: build_plan, ctx_proj/ctx_kv, body_forward,
+dflash_lm_head_ce_train (keeps the logits) -> dflash_lm_head_ce_backward_saved
+-> dflash_body_backward -> dflash_ctx_proj_backward, the chain the benchmark's
+training step runs. Oracle: build_plan, ctx_proj/ctx_kv, body_forward,
 lm_head_ce, lm_head_ce_backward, body_backward, ctx_proj_backward, each pinned
 on its own. Targets are the sequence's own tokens at each block position.
 
@@ -59,10 +60,11 @@ def _step(w, vocab, tau, seed):
     ce = torch.empty(R, dtype=torch.float32, device=dev)
     loss = torch.empty(1, dtype=torch.float64, device=dev)
     ws = torch.empty(d.dflash_lm_head_ce_workspace_size(R, vocab), dtype=torch.uint8, device=dev)
-    d.dflash_lm_head_ce(cfg, run.out, W_lm, targets, loss_mask, tau, ce, loss, ws)
+    logits = torch.empty(d.dflash_lm_head_ce_logits_size(R, vocab), dtype=torch.uint8, device=dev)
+    d.dflash_lm_head_ce_train(cfg, run.out, W_lm, targets, loss_mask, tau, ce, loss, logits, ws)
     d_out = torch.empty_like(run.out)
     ws = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg, R, vocab), dtype=torch.uint8, device=dev)
-    d.dflash_lm_head_ce_backward(cfg, run.out, W_lm, targets, loss_mask, tau, ce, 1.0, d_out, ws)
+    d.dflash_lm_head_ce_backward_saved(cfg, R, logits, W_lm, targets, loss_mask, tau, ce, 1.0, d_out, ws)
     grads = [{k: torch.empty(tuple(v.shape), dtype=torch.float32, device=dev) for k, v in Lw.items()}
              for Lw in inp["layers"]]
     dck = [torch.empty((w.num_kv_heads, run.T, w.head_dim), dtype=torch.float32, device=dev) for _ in range(L)]

@@ -152,6 +152,27 @@ def test_rejects_bad_arguments_before_launch():
     assert lib.dflash_lm_head_ce(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
                                  P(fake), P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
     assert d.dflash_lm_head_ce_workspace_size(16, 100) > 0 and d.dflash_lm_head_ce_workspace_size(-1, 100) == 0
+    # kept logits: null or small buffer; their size; the saved backward's checks
+    assert d.dflash_lm_head_ce_logits_size(16, 100) == 16 * 128 * 4
+    assert d.dflash_lm_head_ce_logits_size(-1, 100) == 0 and d.dflash_lm_head_ce_logits_size(16, 0) == 0
+    assert lib.dflash_lm_head_ce_train(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
+                                       P(fake), None, 1 << 40, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce_train(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
+                                       P(fake), P(fake), 16 * 128 * 4 - 1, P(fake), 1 << 40,
+                                       None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce_train(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
+                                       P(fake), P(fake), 1 << 40, P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 16, None, 1 << 40, P(fake), 100, P(fake), P(fake),
+                                                2.0, P(fake), 1.0, P(fake), P(fake), 1 << 40,
+                                                None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 16, P(fake), 1 << 40, P(fake), 100, P(fake),
+                                                P(fake), 0.0, P(fake), 1.0, P(fake), P(fake), 1 << 40,
+                                                None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 16, P(fake), 1 << 40, P(fake), 100, P(fake),
+                                                P(fake), 2.0, P(fake), 1.0, P(fake), P(fake), 64,
+                                                None) == d.DFLASH_ERR_WORKSPACE
+    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 0, None, 0, P(fake), 100, None, None, 2.0, None,
+                                                1.0, None, None, 0, None) == d.DFLASH_OK
     # attention backward: negative sizes, a null gradient, a small workspace, nothing to do
     F = [P(fake)] * 3
     assert lib.dflash_block_attn_backward(ctypes.byref(cfg), -1, *F, P(fake), P(fake), 64, *F, P(fake), P(fake),
