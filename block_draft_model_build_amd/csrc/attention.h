@@ -881,9 +881,23 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
             }
         }
     }
+    // The merge's last LDS reads are done: the LDS now stages the outputs.
+    __syncthreads();
     if (!active || phase != 0) return;
 
-    // ---- write: final rows of this block, or this split's partial state
+    // ---- write: final rows of this block, or this split's partial state.
+    // A lane holds 4 consecutive d of one column (32 qs + lane % 32), so
+    // direct stores scatter 8-byte pieces over 32 rows per instruction. The
+    // final rows go through this wave's LDS region instead (16-byte chunks
+    // XOR-swizzled by the row), then out as 16-byte lanes, 256 contiguous
+    // bytes per row (writes then reads by the same wave: a wave-level fence
+    // between them). The fp32 partial state keeps its direct 16-byte stores:
+    // staged the same way it measured no faster.
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
     if (a < 0) {
         if (s == 0)
             for (int idx = lane; idx < bs * G * D; idx += 64) {
@@ -893,17 +907,16 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
         return;
     }
     if (nsplit == 1) {
+        constexpr int RB = D * EB, NCH = RB / 16;      // bytes and 16-byte chunks per row
+        static_assert(4 * QC * RB <= TT::LDS_BYTES, "four waves' rows fit in the LDS");
+        char* st = smem + wave * QC * RB;
+        typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
             const int c = qs * 32 + (lane & 31);
-            if (c >= qcols) continue;
-            const int k = c % bs, hh = c / bs;
-            const int row = n * bs + k;
-            const bool keep = p.valid == nullptr || p.valid[row] != 0;
+            const int row = n * bs + (c < qcols ? c % bs : 0);
+            const bool keep = c < qcols && (p.valid == nullptr || p.valid[row] != 0);
             const float inv = keep ? 1.f / l[qs] : 0.f;
-            T* orow = p.out + (int64_t)row * p.out_ld + (int64_t)(g * G + hh) * D;
-            // Accumulator elements 4i..4i+3 are 4 consecutive d: one 4-element store.
-            typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
@@ -911,8 +924,18 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs<T> p) {
                     T4 v;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = from_f32<T>(o[ds][qs][4 * eg + t] * inv);
-                    *reinterpret_cast<T4*>(orow + ds * 32 + acc_row(4 * eg, lane)) = v;
+                    const int b = (ds * 32 + acc_row(4 * eg, lane)) * EB;
+                    *reinterpret_cast<T4*>(st + c * RB + ((((b >> 4) ^ (c & (NCH - 1)))) << 4) + (b & 15)) = v;
                 }
+        }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < QC * NCH / 64; ++i) {
+            const int idx = i * 64 + lane, c = idx / NCH, ch = idx % NCH;
+            if (c >= qcols) continue;
+            const int k = c % bs, hh = c / bs;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(st + c * RB + ((ch ^ (c & (NCH - 1))) << 4));
+            *reinterpret_cast<u32x4*>(p.out + (int64_t)(n * bs + k) * p.out_ld + (int64_t)(g * G + hh) * D + ch * EC) = v;
         }
     } else {
         const int64_t pi = ((int64_t)sg * hkv + g) * kMaxGroup + j;
