@@ -32,7 +32,7 @@ namespace {
 //   transposes [features][Rp] T: xT, yT, oT, uT, dhT, dguT, dh1T, dqkvT
 //   gradients: dh_b, dh1_b [R][H] T; dgu [R][2I] T; do_b [R][nq] T;
 //     dqkv_b [R][nqkv] T; df (dy, then dx), dh1, dh [R][H] f32;
-//     dq [R][nq], dk, dv [R][nk] f32; RMSNorm partial sums [R/16][H] f32
+//     dq [R][nq], dk, dv [R][nk] f32; RMSNorm partial sums [R / kNormBwdRows][H] f32
 //   transposed weights: W_down^T [I][H], [W_gate; W_up]^T [H][2I],
 //     Wo^T [nq][H], [Wq; Wk; Wv]^T [H][nqkv]
 struct BodyBwdLayout {
