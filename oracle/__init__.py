@@ -13,6 +13,8 @@ Contents:
   backward.py -- gradients of the dual-source block attention, of the
               context path (dW_proj) and of the whole body (every layer
               weight, the block embeddings and the context caches).
+  optim.py -- the AdamW step that follows the backward (the reading taken
+              for the optimizer the pages leave unnamed).
 
 Parity status of each function (what pins it is listed in tests/test_oracle_*.py):
   build_plan             pinned by invariants the pages fix (determinism, equal
@@ -55,6 +57,10 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
                          every weight of every layer, the block embeddings and
                          both context caches of a two-layer case with invalid
                          rows and an empty block.
+  adamw_step             pinned by closed forms: the first step's normalised
+                         sign step, decay alone, a constant gradient under the
+                         bias correction, two steps' rate-weighted gradients,
+                         decay before the step.
 """
 from .plan import splitmix64, build_plan, eligible_anchors, row_key, position_key
 from .verify import (
@@ -66,6 +72,7 @@ from .backward import (
     block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_hidden_grad, ctx_proj_backward,
     rms_norm_backward, swiglu_backward, layer_forward, layer_backward, body_forward_layers, body_backward,
 )
+from .optim import adamw_step
 from .body import (
     rms_norm, silu, rope, rope_inv_freq, ctx_proj, ctx_kv, block_attention,
     dense_mask_attention, block_attn_call, body_forward, body_forward_dense,
@@ -82,5 +89,5 @@ __all__ = [
     "lm_head_ce", "lm_head_ce_rows", "lm_head_ce_backward", "token_ce", "logsumexp_rows", "position_weights",
     "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_hidden_grad", "ctx_proj_backward",
     "rms_norm_backward", "swiglu_backward", "layer_forward", "layer_backward", "body_forward_layers",
-    "body_backward",
+    "body_backward", "adamw_step",
 ]
