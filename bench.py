@@ -419,12 +419,25 @@ class TrainingBuffers:
         self.dW = e(H, self.Kt)
         self.ws_cb = u8(d.dflash_ctx_proj_backward_workspace_size(cfg, T))
         self.row_of = torch.arange(R, device=device) // (bs * N)
+        # Optimizer state of every trainable tensor (each layer's weights and
+        # W_proj): fp32 master copies and moments; the working copies are the
+        # config-dtype weights the forward reads.
+        pairs = [(Lw[k], G[k]) for Lw, G in zip(inp["layers"], self.grads) for k in Lw]
+        pairs.append((inp["w_proj"], self.dW))
+        self.opt = [{"master": wt.float().reshape(-1).clone(), "exp_avg": e(wt.numel()),
+                     "exp_avg_sq": e(wt.numel()), "grad": gr.reshape(-1), "weight": wt.reshape(-1)}
+                    for wt, gr in pairs]
+        for t in self.opt:
+            t["exp_avg"].zero_()
+            t["exp_avg_sq"].zero_()
+        self.params = sum(t["master"].numel() for t in self.opt)
+        self.opt_step = 0
 
     def step(self):
         """Runs the step; returns events recorded before and after each stage."""
         d, torch, w, i = self.d, self.torch, self.w, self.inp
         cfg, T, nb, V = self.cfg, self.w.batch * self.w.seq_len, self.w.num_blocks, self.vocab
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
         ev[0].record()
         d.dflash_build_plan(i["mask"], i["sample_ids"], i["step"], i["plan_seed"], w.anchors_per_row, w.block_size,
                             self.anchors, self.positions, self.valid, self.loss_mask, self.num, self.base)
@@ -451,6 +464,10 @@ class TrainingBuffers:
         d.dflash_ctx_proj_backward(cfg, i["states"], w.target_hidden, T * w.target_hidden, T, self.ctx_pos,
                                    i["layers"], self.dck, self.dcv, T, 0, self.dW, None, self.ws_cb)
         ev[7].record()
+        self.opt_step += 1
+        d.dflash_adamw_step(cfg.dtype, self.opt, lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.01,
+                            step=self.opt_step)
+        ev[8].record()
         return ev
 
 
@@ -458,14 +475,16 @@ def train_step_row(d, torch, w, vocab, device, reps=3):
     """One whole training step of the 5-layer training workload through the
     library, timed end to end with events on the launch stream: plan, context
     projection, training forward (reserve space), LM head + decayed CE keeping
-    its logits, its backward from them, body backward, W_proj backward. Synthetic inputs of the workload's
+    its logits, its backward from them, body backward, W_proj backward, and the
+    AdamW step over every layer weight and W_proj (fp32 master copies and
+    moments; it writes the bf16 weights the next step's forward reads). Synthetic inputs of the workload's
     shapes; targets are random tokens at the block positions; frozen synthetic
     LM head of the given vocabulary. Also the events between the stages."""
     bufs = TrainingBuffers(d, torch, w, vocab, device)
     marks = bufs.step()                       # warm-up
     torch.cuda.synchronize()
     names = ["plan", "ctx_proj", "forward_train", "lm_head_ce", "lm_head_ce_backward", "body_backward",
-             "ctx_proj_backward"]
+             "ctx_proj_backward", "optimizer"]
     acc = [0.0] * len(names)
     total = 0.0
     for _ in range(reps):
@@ -475,9 +494,15 @@ def train_step_row(d, torch, w, vocab, device, reps=3):
         acc = [a + t for a, t in zip(acc, ts)]
         total += marks[0].elapsed_time(marks[-1])
     ms = total / reps
+    opt_ms = acc[-1] / reps
+    opt_bytes = bufs.params * (4 + 3 * 4 + 3 * 4 + (2 if w.dtype == "bf16" else 4))
     return {"blocks": w.num_blocks, "layers": w.num_layers, "vocab": vocab, "ms": round(ms, 3),
             "stages_ms": {n: round(a / reps, 3) for n, a in zip(names, acc)},
-            "block_positions_per_s": round(w.num_blocks * w.block_size / (ms / 1e3), 1)}
+            "block_positions_per_s": round(w.num_blocks * w.block_size / (ms / 1e3), 1),
+            "optimizer": {"params": bufs.params, "bytes": opt_bytes,
+                          "roofline": {"bound": "hbm", "achieved": round(opt_bytes / (opt_ms / 1e3) / 1e9, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(opt_bytes / (opt_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}}
 
 
 def body_backward_row(d, torch, wt, cfg, layers, anc, base, val, d_ctx_k, d_ctx_v, mk, f32, reps=5):

@@ -15,7 +15,7 @@ The names mirror the C entry points:
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
   dflash_body_forward_train, dflash_body_train_reserve_size, dflash_body_backward,
-  dflash_body_backward_workspace_size,
+  dflash_body_backward_workspace_size, dflash_adamw_step,
   dflash_workspace_size, dflash_check_config, dflash_status_string.
 
 If libdflash.so is missing it is built in-tree with hipcc on first import; if
@@ -44,7 +44,7 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
             "dflash_body_forward_train", "dflash_body_train_reserve_size", "dflash_body_backward",
-            "dflash_body_backward_workspace_size",
+            "dflash_body_backward_workspace_size", "dflash_adamw_step",
             "dflash_workspace_size", "dflash_check_config", "dflash_status_string",
             "dflash_profile_start", "dflash_profile_stop")
 
@@ -75,6 +75,11 @@ class DFlashLayerWeights(ctypes.Structure):
 
 class DFlashLayerGrads(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in _LAYER_FIELDS]
+
+
+class DFlashAdamWTensor(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("numel", ctypes.c_int64)]
 
 
 class DFlashError(RuntimeError):
@@ -140,6 +145,9 @@ def _load() -> ctypes.CDLL:
     lib.dflash_body_backward.restype = ctypes.c_int
     lib.dflash_body_backward_workspace_size.argtypes = [CFG, I32]
     lib.dflash_body_backward_workspace_size.restype = ctypes.c_size_t
+    lib.dflash_adamw_step.argtypes = [I32, I32, P, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                      ctypes.c_double, ctypes.c_double, I64, P]
+    lib.dflash_adamw_step.restype = ctypes.c_int
     lib.dflash_ctx_proj_backward_workspace_size.argtypes = [CFG, I64]
     lib.dflash_ctx_proj_backward_workspace_size.restype = ctypes.c_size_t
     lib.dflash_workspace_size.argtypes = [CFG, I32, I64]
@@ -502,3 +510,21 @@ def dflash_profile_stop(max_launches: int) -> List[float]:
     n = ctypes.c_int32(0)
     _check("dflash_profile_stop", _lib.dflash_profile_stop(buf, ctypes.byref(n)))
     return [buf[i] for i in range(n.value)]
+
+
+def dflash_adamw_step(dtype: int, tensors, lr: float, beta1: float, beta2: float, eps: float,
+                      weight_decay: float, step: int, stream=None) -> None:
+    """tensors: sequence of dicts with f32 `grad`, `master`, `exp_avg`, `exp_avg_sq` of equal numel
+    and an optional `weight` (the working copy, DFLASH_BF16 or DFLASH_F32 per dtype)."""
+    arr = (DFlashAdamWTensor * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i].grad = _ptr(t["grad"])
+        arr[i].master = _ptr(t["master"])
+        arr[i].exp_avg = _ptr(t["exp_avg"])
+        arr[i].exp_avg_sq = _ptr(t["exp_avg_sq"])
+        arr[i].weight = _ptr(t.get("weight"))
+        arr[i].numel = int(t["master"].numel())
+    first = tensors[0]["master"] if len(tensors) else None
+    s = _lib.dflash_adamw_step(int(dtype), len(tensors), ctypes.addressof(arr), float(lr), float(beta1),
+                               float(beta2), float(eps), float(weight_decay), int(step), _stream(stream, first))
+    _check("dflash_adamw_step", s)

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["dflash.hip", "plan.hip", "profile.hip", "verify.hip", "attn_bwd.hip", "ctx_bwd.hip", "body_bwd.hip", "lm_bwd.hip"]
+SOURCES = ["dflash.hip", "plan.hip", "profile.hip", "verify.hip", "attn_bwd.hip", "ctx_bwd.hip", "body_bwd.hip", "lm_bwd.hip", "optim.hip"]
 ARCH = "gfx950"
 
 

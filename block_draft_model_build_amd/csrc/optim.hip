@@ -1,0 +1,172 @@
+// The optimizer step after the body's backward (NeMo RL "DFlash Draft Body",
+// How It Works, step 1, and Scope: the draft body is trained with an optimizer
+// step). The pages name no optimizer; this is AdamW: Adam's bias-corrected
+// moment estimates (Kingma and Ba, ICLR 2015) with weight decay decoupled from
+// the gradient (Loshchilov and Hutter, ICLR 2019), decay first, then the
+// moments, then the step:
+//   w <- w (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+//   w <- w - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+// in fp32 on fp32 master weights and moments, optionally writing the config-
+// dtype working copy the next forward reads. Purely elementwise and HBM-bound
+// (30 bytes per bf16 parameter): several tensors per launch, a workgroup per
+// 4096 elements of one tensor, 16-byte accesses, 16 elements per thread.
+#include "internal.h"
+
+namespace dflash {
+
+namespace {
+
+constexpr int kAdamTensors = 8;          // tensors per launch
+constexpr int kAdamSegs = 4;             // segments of 1024 elements per workgroup
+constexpr int kAdamChunk = 1024 * kAdamSegs;   // elements per workgroup
+
+struct AdamBatch {
+    const float* g[kAdamTensors];
+    float* w[kAdamTensors];
+    float* m[kAdamTensors];
+    float* v[kAdamTensors];
+    void* out[kAdamTensors];
+    int64_t n[kAdamTensors];
+    int64_t first_block[kAdamTensors + 1];   // workgroups before each tensor
+    int count;
+    float decay, beta1, beta2, omb1, omb2, step_size, rsqrt_bc2, eps;
+};
+
+__device__ __forceinline__ void adam_elem(const AdamBatch& b, float g, float& w, float& m, float& v) {
+    w *= b.decay;
+    m = b.beta1 * m + b.omb1 * g;
+    v = b.beta2 * v + b.omb2 * g * g;
+    w -= b.step_size * m / (sqrtf(v) * b.rsqrt_bc2 + b.eps);
+}
+
+// Thread t of a workgroup takes elements 4t .. 4t + 3 of each of the chunk's
+// kAdamSegs segments of 1024: every load of a thread is issued before any
+// arithmetic (16 independent 16-byte loads in flight), then the updates and
+// the stores. Only the last workgroup of a tensor meets its tail, element by
+// element.
+template <typename T>
+__global__ __launch_bounds__(256) void adamw_kernel(AdamBatch b) {
+    int i = 0;
+    while (i + 1 < b.count && (int64_t)blockIdx.x >= b.first_block[i + 1]) ++i;   // wave-uniform
+    const int64_t n = b.n[i];
+    const int64_t e0 = ((int64_t)blockIdx.x - b.first_block[i]) * kAdamChunk + (int64_t)threadIdx.x * 4;
+    const float* gp = b.g[i];
+    float* wp = b.w[i];
+    float* mp = b.m[i];
+    float* vp = b.v[i];
+    T* op = static_cast<T*>(b.out[i]);
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    if (e0 + (kAdamSegs - 1) * 1024 + 4 <= n) {
+        f32x4 g[kAdamSegs], w[kAdamSegs], m[kAdamSegs], v[kAdamSegs];
+#pragma unroll
+        for (int k = 0; k < kAdamSegs; ++k) {
+            const int64_t e = e0 + k * 1024;
+            g[k] = *reinterpret_cast<const f32x4*>(gp + e);
+            w[k] = *reinterpret_cast<const f32x4*>(wp + e);
+            m[k] = *reinterpret_cast<const f32x4*>(mp + e);
+            v[k] = *reinterpret_cast<const f32x4*>(vp + e);
+        }
+#pragma unroll
+        for (int k = 0; k < kAdamSegs; ++k) {
+            const int64_t e = e0 + k * 1024;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float wq = w[k][q], mq = m[k][q], vq = v[k][q];
+                adam_elem(b, g[k][q], wq, mq, vq);
+                w[k][q] = wq;
+                m[k][q] = mq;
+                v[k][q] = vq;
+            }
+            *reinterpret_cast<f32x4*>(wp + e) = w[k];
+            *reinterpret_cast<f32x4*>(mp + e) = m[k];
+            *reinterpret_cast<f32x4*>(vp + e) = v[k];
+            if (op != nullptr) {
+                T4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = from_f32<T>(w[k][q]);
+                *reinterpret_cast<T4*>(op + e) = o;
+            }
+        }
+    } else {
+        for (int k = 0; k < kAdamSegs; ++k)
+            for (int64_t e = e0 + k * 1024; e < n && e < e0 + k * 1024 + 4; ++e) {
+                float w = wp[e], m = mp[e], v = vp[e];
+                adam_elem(b, gp[e], w, m, v);
+                wp[e] = w;
+                mp[e] = m;
+                vp[e] = v;
+                if (op != nullptr) op[e] = from_f32<T>(w);
+            }
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+}  // namespace dflash
+
+using namespace dflash;
+
+extern "C" dflash_status dflash_adamw_step(int32_t dtype, int32_t num_tensors, const dflash_adamw_tensor* tensors,
+                                           double lr, double beta1, double beta2, double eps, double weight_decay,
+                                           int64_t step, void* hip_stream) {
+    if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return DFLASH_ERR_INVALID_ARG;
+    if (num_tensors < 0 || (num_tensors > 0 && tensors == nullptr) || step < 1 || !(lr >= 0.0) ||
+        !(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps > 0.0) || !(weight_decay >= 0.0))
+        return DFLASH_ERR_INVALID_ARG;
+    for (int t = 0; t < num_tensors; ++t) {
+        const dflash_adamw_tensor& x = tensors[t];
+        if (x.numel < 0) return DFLASH_ERR_INVALID_ARG;
+        if (x.numel == 0) continue;
+        if (x.grad == nullptr || x.master == nullptr || x.exp_avg == nullptr || x.exp_avg_sq == nullptr ||
+            !aligned16(x.grad) || !aligned16(x.master) || !aligned16(x.exp_avg) || !aligned16(x.exp_avg_sq) ||
+            !aligned16(x.weight))
+            return DFLASH_ERR_INVALID_ARG;
+    }
+    AdamBatch b{};
+    const double bc1 = 1.0 - pow(beta1, (double)step), bc2 = 1.0 - pow(beta2, (double)step);
+    b.decay = (float)(1.0 - lr * weight_decay);
+    b.beta1 = (float)beta1;
+    b.beta2 = (float)beta2;
+    b.omb1 = (float)(1.0 - beta1);
+    b.omb2 = (float)(1.0 - beta2);
+    b.step_size = (float)(lr / bc1);
+    b.rsqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    b.eps = (float)eps;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    auto flush = [&]() -> hipError_t {
+        if (b.count == 0) return hipSuccess;
+        const int64_t blocks = b.first_block[b.count];
+        if (dtype == DFLASH_BF16)
+            hipLaunchKernelGGL(adamw_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st, b);
+        else
+            hipLaunchKernelGGL(adamw_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, b);
+        b.count = 0;
+        b.first_block[0] = 0;
+        return hipGetLastError();
+    };
+    for (int t = 0; t < num_tensors; ++t) {
+        const dflash_adamw_tensor& x = tensors[t];
+        for (int64_t done = 0; done < x.numel;) {
+            // A launch covers at most 2^30 workgroups of the same batch.
+            const int64_t room = ((int64_t)1 << 30) - b.first_block[b.count];
+            int64_t len = x.numel - done;
+            if ((len + kAdamChunk - 1) / kAdamChunk > room) len = room * kAdamChunk;
+            const int k = b.count;
+            b.g[k] = x.grad + done;
+            b.w[k] = x.master + done;
+            b.m[k] = x.exp_avg + done;
+            b.v[k] = x.exp_avg_sq + done;
+            b.out[k] = x.weight == nullptr ? nullptr
+                                           : static_cast<char*>(x.weight) + done * (dtype == DFLASH_BF16 ? 2 : 4);
+            b.n[k] = len;
+            b.first_block[k + 1] = b.first_block[k] + (len + kAdamChunk - 1) / kAdamChunk;
+            b.count = k + 1;
+            done += len;
+            if (b.count == kAdamTensors || b.first_block[b.count] >= ((int64_t)1 << 30))
+                if (flush() != hipSuccess) return DFLASH_ERR_HIP;
+        }
+    }
+    return flush() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}

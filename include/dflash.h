@@ -681,6 +681,46 @@ dflash_status dflash_body_backward(const dflash_config *cfg, int32_t num_blocks,
                                    size_t workspace_bytes, void *hip_stream);
 size_t dflash_body_backward_workspace_size(const dflash_config *cfg, int32_t num_blocks);
 
+/*
+ * dflash_adamw_step -- the optimizer step after the backward, over any set of
+ * trainable tensors (the draft layers' weights, W_proj). [P2] "How It Works",
+ * step 1, and "Scope": the draft body is trained with an optimizer step; the
+ * pages name no optimizer, and this is AdamW (Adam's bias-corrected moments,
+ * Kingma and Ba 2015; weight decay decoupled from the gradient, Loshchilov and
+ * Hutter 2019), applied decay first, then the moments, then the step:
+ *
+ *   w <- w (1 - lr weight_decay)
+ *   m <- beta1 m + (1 - beta1) g,    v <- beta2 v + (1 - beta2) g^2
+ *   w <- w - (lr / (1 - beta1^step)) m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ *
+ * elementwise in fp32; then weight = w rounded to `dtype` (the working copy the
+ * next forward reads) where a weight pointer is given.
+ *
+ *   dtype          DFLASH_BF16 or DFLASH_F32: element type of the working copies
+ *   tensors        host array of num_tensors descriptors; per tensor, device arrays
+ *                  of numel elements: grad (f32, read), master weights, exp_avg and
+ *                  exp_avg_sq (f32, updated in place; start the moments at zero),
+ *                  weight (dtype, written; null: no working copy). All 16-byte
+ *                  aligned; tensors must not overlap.
+ *   step           the step number, 1 for the first update
+ * Every element is independent, so results do not depend on the launch split.
+ * Errors: INVALID_ARG for an unknown dtype, num_tensors < 0, step < 1, lr < 0,
+ * beta outside [0, 1), eps <= 0, weight_decay < 0, negative numel, or a null or
+ * misaligned array of a non-empty tensor.
+ */
+typedef struct dflash_adamw_tensor {
+    const float *grad;
+    float *master;
+    float *exp_avg;
+    float *exp_avg_sq;
+    void *weight;
+    int64_t numel;
+} dflash_adamw_tensor;
+
+dflash_status dflash_adamw_step(int32_t dtype, int32_t num_tensors, const dflash_adamw_tensor *tensors,
+                                double lr, double beta1, double beta2, double eps, double weight_decay,
+                                int64_t step, void *hip_stream);
+
 /* Bytes of workspace that dflash_ctx_proj over ctx_rows rows and
  * dflash_block_attn / dflash_body_forward over num_blocks blocks need (one
  * buffer of this size serves all of them; 256-byte aligned). Returns 0 for an

@@ -173,6 +173,23 @@ def test_rejects_bad_arguments_before_launch():
                                                 None) == d.DFLASH_ERR_WORKSPACE
     assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 0, None, 0, P(fake), 100, None, None, 2.0, None,
                                                 1.0, None, None, 0, None) == d.DFLASH_OK
+    # optimizer step: dtype, step, rates, eps, sizes, null or misaligned arrays; empty calls
+    T = d.DFlashAdamWTensor
+    good = (T * 1)(T(fake, fake, fake, fake, fake, 100))
+    args = lambda **k: dict(dict(dt=d.DFLASH_BF16, n=1, t=good, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0,
+                                 step=1), **k)
+    def adam(a):
+        return lib.dflash_adamw_step(a["dt"], a["n"], a["t"], a["lr"], a["b1"], a["b2"], a["eps"], a["wd"],
+                                     a["step"], None)
+    for bad in (dict(dt=7), dict(n=-1), dict(step=0), dict(lr=-1.0), dict(b1=1.0), dict(b2=-0.1),
+                dict(eps=0.0), dict(wd=-1.0), dict(t=None)):
+        assert adam(args(**bad)) == d.DFLASH_ERR_INVALID_ARG, bad
+    assert adam(args(t=(T * 1)(T(fake, fake, fake, fake, fake, -1)))) == d.DFLASH_ERR_INVALID_ARG
+    assert adam(args(t=(T * 1)(T(None, fake, fake, fake, fake, 4)))) == d.DFLASH_ERR_INVALID_ARG
+    assert adam(args(t=(T * 1)(T(fake, fake + 4, fake, fake, fake, 4)))) == d.DFLASH_ERR_INVALID_ARG
+    assert adam(args(t=(T * 1)(T(fake, fake, fake, fake, fake + 8, 4)))) == d.DFLASH_ERR_INVALID_ARG
+    assert adam(args(n=0, t=None)) == d.DFLASH_OK
+    assert adam(args(t=(T * 1)(T(None, None, None, None, None, 0)))) == d.DFLASH_OK
     # attention backward: negative sizes, a null gradient, a small workspace, nothing to do
     F = [P(fake)] * 3
     assert lib.dflash_block_attn_backward(ctypes.byref(cfg), -1, *F, P(fake), P(fake), 64, *F, P(fake), P(fake),
