@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256) void saved_target_logit_kernel(const float* lo
 
 // dz from the kept logits, the same arithmetic as EpCEGrad: 8 consecutive
 // columns per thread (two 16-byte loads), exact zeros past the vocabulary up
-// to ld and on rows whose coef is 0 (their logits are not read).
+// to ld and on rows whose coef is 0 (their logits are not read). Logits and dz
+// (GBs, each touched once here) use non-temporal accesses: 0.65 -> 0.61 ms at
+// 4096 rows x 151936.
 template <typename T>
 __device__ __forceinline__ void ce_grad_saved_run(const float* __restrict__ logits, int64_t ld,
                                                   const float* __restrict__ coef, const float* __restrict__ lse,
@@ -66,7 +68,7 @@ __device__ __forceinline__ void ce_grad_saved_run(const float* __restrict__ logi
     float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (c != 0.f) {
         const f32x4* p = reinterpret_cast<const f32x4*>(logits + row * ld + c0);
-        const f32x4 a = p[0], b = p[1];
+        const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             z[q] = a[q];
@@ -81,7 +83,7 @@ __device__ __forceinline__ void ce_grad_saved_run(const float* __restrict__ logi
         if (col < vocab && c != 0.f) v = c * (__expf(z[q] - L) - (col == t ? 1.f : 0.f));
         o[q] = from_f32<T>(v);
     }
-    *reinterpret_cast<t8*>(dz + row * ld + c0) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<t8*>(dz + row * ld + c0));
 }
 
 // A workgroup takes 2048 columns of one row per item, items row-major.

@@ -42,8 +42,10 @@ __device__ __forceinline__ void adam_elem(const AdamBatch& b, float g, float& w,
 // Thread t of a workgroup takes elements 4t .. 4t + 3 of each of the chunk's
 // kAdamSegs segments of 1024: every load of a thread is issued before any
 // arithmetic (16 independent 16-byte loads in flight), then the updates and
-// the stores. Only the last workgroup of a tensor meets its tail, element by
-// element.
+// the stores. Every byte is touched once, so the vector accesses are
+// non-temporal (5.34 -> 5.64 TB/s on 512 M parameters, where torch's own
+// device copy moves 5.0-5.15 TB/s). Only the last workgroup of a tensor meets
+// its tail, element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void adamw_kernel(AdamBatch b) {
     int i = 0;
@@ -61,10 +63,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamBatch b) {
 #pragma unroll
         for (int k = 0; k < kAdamSegs; ++k) {
             const int64_t e = e0 + k * 1024;
-            g[k] = *reinterpret_cast<const f32x4*>(gp + e);
-            w[k] = *reinterpret_cast<const f32x4*>(wp + e);
-            m[k] = *reinterpret_cast<const f32x4*>(mp + e);
-            v[k] = *reinterpret_cast<const f32x4*>(vp + e);
+            g[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gp + e));
+            w[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wp + e));
+            m[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(mp + e));
+            v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vp + e));
         }
 #pragma unroll
         for (int k = 0; k < kAdamSegs; ++k) {
@@ -77,14 +79,14 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamBatch b) {
                 m[k][q] = mq;
                 v[k][q] = vq;
             }
-            *reinterpret_cast<f32x4*>(wp + e) = w[k];
-            *reinterpret_cast<f32x4*>(mp + e) = m[k];
-            *reinterpret_cast<f32x4*>(vp + e) = v[k];
+            __builtin_nontemporal_store(w[k], reinterpret_cast<f32x4*>(wp + e));
+            __builtin_nontemporal_store(m[k], reinterpret_cast<f32x4*>(mp + e));
+            __builtin_nontemporal_store(v[k], reinterpret_cast<f32x4*>(vp + e));
             if (op != nullptr) {
                 T4 o;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = from_f32<T>(w[k][q]);
-                *reinterpret_cast<T4*>(op + e) = o;
+                __builtin_nontemporal_store(o, reinterpret_cast<T4*>(op + e));
             }
         }
     } else {

@@ -48,16 +48,16 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_argmax_kernel(const T* 
     const bool vec_ok = (vocab % VEC) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
     if (vec_ok) {
         // Batches of 8 independent 16-byte loads per thread keep enough bytes
-        // in flight to stream the row near HBM speed; the scan order (and so
-        // the tie rule) is unchanged: each thread still visits its indices in
-        // increasing order.
+        // in flight to stream the row near HBM speed (non-temporal: each logit
+        // is read once); the scan order (and so the tie rule) is unchanged:
+        // each thread still visits its indices in increasing order.
         typedef T TV __attribute__((ext_vector_type(VEC)));
         constexpr int NB = 8, STRIDE = kVerifyThreads * VEC;
         for (int base = threadIdx.x * VEC; base < vocab; base += NB * STRIDE) {
             TV t[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                if (base + b * STRIDE < vocab) t[b] = *reinterpret_cast<const TV*>(x + base + b * STRIDE);
+                if (base + b * STRIDE < vocab) t[b] = __builtin_nontemporal_load(reinterpret_cast<const TV*>(x + base + b * STRIDE));
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int v0 = base + b * STRIDE;
