@@ -645,7 +645,7 @@ def _pct(xs, q):
 
 def measure(d, torch, w, steps, warmup, breakdown=True):
     """Build one workload's inputs, warm up, then time `steps` steps: HIP events
-    around the whole loop (the step time the driver checks) and around each step
+    around the whole loop (the reported step time) and around each step
     (median, p10, p90), with the dominant kernel's launches timed by the
     library's own events over the same region. Returns the figures and the runner."""
     runner = Runner(d, w)
