@@ -46,6 +46,10 @@ Parity status of each function (what pins it is listed in tests/test_oracle_*.py
   ctx_proj_backward      pinned by central differences of the forward context
                          path (ctx_proj then ctx_kv) along random directions of
                          W_proj and of C, and entry by entry on a tiny case.
+  ctx_kv_weight_grads    pinned by central differences of the context path
+                         (ctx_proj then ctx_kv) over every entry of Wk and Wv,
+                         and, with body_backward, by central differences of a
+                         whole training step's loss (tests/test_oracle_train_chain.py).
   rms_norm_backward, swiglu_backward
                          pinned by central differences of rms_norm and of
                          SiLU(g) * up, entry by entry.
@@ -70,6 +74,7 @@ from .verify import (
 from .loss import lm_head_ce, lm_head_ce_rows, lm_head_ce_backward, token_ce, logsumexp_rows, position_weights
 from .backward import (
     block_attention_backward, block_attn_call_backward, ctx_grad_rows, ctx_hidden_grad, ctx_proj_backward,
+    ctx_kv_weight_grads,
     rms_norm_backward, swiglu_backward, layer_forward, layer_backward, body_forward_layers, body_backward,
 )
 from .optim import adamw_step
@@ -88,6 +93,7 @@ __all__ = [
     "verify_sample", "inverse_cdf_draw", "residual_weights", "accept_proposal",
     "lm_head_ce", "lm_head_ce_rows", "lm_head_ce_backward", "token_ce", "logsumexp_rows", "position_weights",
     "block_attention_backward", "block_attn_call_backward", "ctx_grad_rows", "ctx_hidden_grad", "ctx_proj_backward",
+    "ctx_kv_weight_grads",
     "rms_norm_backward", "swiglu_backward", "layer_forward", "layer_backward", "body_forward_layers",
     "body_backward", "adamw_step",
 ]

@@ -126,6 +126,19 @@ def ctx_hidden_grad(d_ctx_k, d_ctx_v, positions, layers, num_kv_heads: int, head
     return dC
 
 
+def ctx_kv_weight_grads(C, positions, d_ctx_k, d_ctx_v, num_kv_heads: int, head_dim: int, theta: float):
+    """The context path's share of every layer's Wk and Wv gradient (angelspec
+    "DFlash", How it works: the projected target context enters each draft
+    layer's K/V through that layer's own projections). With Kc_l = RoPE(C Wk_l^T)
+    and Vc_l = C Wv_l^T:
+        dWk_l = Gk_l^T C,   dWv_l = Gv_l^T C      [Hkv*D, H]
+    with Gk_l, Gv_l as in ctx_grad_rows. The block rows' share comes from
+    body_backward; a training step adds the two. Returns (dWk list, dWv list)."""
+    C = np.asarray(C, np.float64)
+    Gk, Gv = ctx_grad_rows(d_ctx_k, d_ctx_v, positions, num_kv_heads, head_dim, theta)
+    return [g.T @ C for g in Gk], [g.T @ C for g in Gv]
+
+
 def ctx_proj_backward(X, positions, layers, d_ctx_k, d_ctx_v, num_kv_heads: int, head_dim: int, theta: float):
     """Gradients through the context path (ctx_proj, then ctx_kv of every layer;
     NeMo RL "DFlash Draft Body", Scope: training updates W_proj; angelspec

@@ -142,3 +142,25 @@ def test_ctx_grad_rows_undo_the_rotation():
     b = gk[0].transpose(1, 0, 2).reshape(3, 2, 2, 4)
     assert np.allclose((a * a).sum(axis=2), (b * b).sum(axis=2))
     assert np.allclose(Gv[0], gv[0].transpose(1, 0, 2).reshape(3, -1))
+
+
+def test_ctx_kv_weight_grads_entrywise():
+    # The context path is linear in each Wk_l and Wv_l: a central difference of
+    # step 1 over one entry is that entry's gradient exactly (up to rounding).
+    X, w_proj, layers, pos, gk, gv, dims = _ctx_case(6)
+    C = oracle.ctx_proj(X, w_proj)
+    dWk, dWv = oracle.ctx_kv_weight_grads(C, pos, gk, gv, *dims)
+    for l in range(len(layers)):
+        for kind, grad in (("wk", dWk[l]), ("wv", dWv[l])):
+            num = np.zeros_like(grad)
+            for i in range(grad.shape[0]):
+                for j in range(grad.shape[1]):
+                    plus = [dict(L) for L in layers]
+                    minus = [dict(L) for L in layers]
+                    E = np.zeros_like(layers[l][kind])
+                    E[i, j] = 1.0
+                    plus[l][kind] = layers[l][kind] + E
+                    minus[l][kind] = layers[l][kind] - E
+                    num[i, j] = (_ctx_loss_of_c(C, plus, pos, gk, gv, dims)
+                                 - _ctx_loss_of_c(C, minus, pos, gk, gv, dims)) / 2
+            assert np.allclose(grad, num, rtol=1e-10, atol=1e-9), f"layer {l} {kind}"
