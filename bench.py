@@ -201,8 +201,9 @@ def next_rows(d, torch, device="cuda"):
     side, lm_head_ce = LM head + decayed cross-entropy over the 5-layer body's
     4096 block rows (151936 x 4096 head), attn_backward = one layer's
     dual-source attention backward at the training shape,
-    ctx_proj_backward = dW_proj through every layer's context K/V over the
-    32768 context rows, lm_head_ce_backward = the loss gradient with respect to
+    ctx_proj_backward = dW_proj and the context path's share of every layer's
+    Wk / Wv gradient through every layer's context K/V over the 32768 context
+    rows, lm_head_ce_backward = the loss gradient with respect to
     the 4096 block rows, body_backward = the body's training forward and
     backward, each with its MFMA roofline; and train_step = one whole training
     step of the 5-layer workload, end to end."""
@@ -349,9 +350,12 @@ def next_rows(d, torch, device="cuda"):
                                          "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
     del qa, ka, va, oa, doa, cka, cva, grads, ws3
     # Training side: gradient of W_proj through the context path (every layer's
-    # context K/V gradient -> dC -> dW_proj) over the 32768 context rows.
+    # context K/V gradient -> dC -> dW_proj) over the 32768 context rows, and
+    # the path's share of every layer's Wk / Wv gradient (G^T C).
     Kin = wt.num_target_layers * wt.target_hidden
     X3 = mk(T, Kin)
+    C3 = mk(T, wt.hidden)
+    dkv3 = [f32(Hkv * D, wt.hidden).zero_() for _ in range(2 * wt.num_layers)]
     pos3 = (torch.arange(T, device=device) % wt.seq_len).to(torch.int32)
     layers3 = [layer_weights(wt, Rng(2025, device), l) for l in range(wt.num_layers)]
     gk3 = [torch.randn((Hkv, T, D), generator=gen, device=device) for _ in range(wt.num_layers)]
@@ -359,17 +363,19 @@ def next_rows(d, torch, device="cuda"):
     dW3 = torch.empty((wt.hidden, Kin), dtype=torch.float32, device=device)
     ws4 = torch.empty(d.dflash_ctx_proj_backward_workspace_size(cfg3, T), dtype=torch.uint8, device=device)
     call = lambda: d.dflash_ctx_proj_backward(cfg3, X3, Kin, wt.target_hidden, T, pos3, layers3, gk3, gv3, T, 0,
-                                              dW3, None, ws4)
-    parts = {k: hook_ms(d, torch, [(k, 1)], call) for k in ("ctx_bwd_pack", "ctx_bwd_dc", "ctx_bwd_dw")}
+                                              dW3, None, ws4, ctx_hidden=C3, d_wk=dkv3[:wt.num_layers],
+                                              d_wv=dkv3[wt.num_layers:])
+    parts = {k: hook_ms(d, torch, [(k, n)], call)
+             for k, n in (("ctx_bwd_pack", 2), ("ctx_bwd_dc", 1), ("ctx_bwd_dw", 1), ("ctx_bwd_dkv", 1))}
     ms = sum(parts.values())
     kg = 2 * wt.num_layers * Hkv * D
-    flops = 2.0 * T * wt.hidden * kg + 2.0 * wt.hidden * Kin * T
+    flops = 2.0 * T * wt.hidden * kg + 2.0 * wt.hidden * Kin * T + 2.0 * kg * wt.hidden * T
     ach = flops / (ms / 1e3) / 1e12
     out["ctx_proj_backward"] = {"rows": T, "ms": round(ms, 4), **{k + "_ms": round(v, 4) for k, v in parts.items()},
                                 "roofline": {"bound": "mfma", "achieved": round(ach, 2),
                                              "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
                                              "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4)}}
-    del X3, dW3, ws4
+    del X3, dW3, ws4, C3, dkv3
     out["body_backward"] = body_backward_row(d, torch, wt, cfg3, layers3, anc, base, val, gk3, gv3, mk, f32)
     del gk3, gv3, layers3
     torch.cuda.empty_cache()
@@ -404,6 +410,7 @@ class TrainingBuffers:
         self.ck = [e(w.num_kv_heads, T, w.head_dim, dt=w.torch_dtype) for _ in range(L)]
         self.cv = [e(w.num_kv_heads, w.head_dim, T, dt=w.torch_dtype) for _ in range(L)]
         self.out, self.d_out = e(R, H, dt=w.torch_dtype), e(R, H, dt=w.torch_dtype)
+        self.C = e(T, H, dt=w.torch_dtype)          # C = X W_proj^T, kept for the Wk / Wv gradients
         self.ws = u8(d.dflash_workspace_size(cfg, nb, T))
         self.reserve = u8(d.dflash_body_train_reserve_size(cfg, nb))
         self.ce, self.loss = e(R), e(1, dt=torch.float64)
@@ -442,8 +449,8 @@ class TrainingBuffers:
         d.dflash_build_plan(i["mask"], i["sample_ids"], i["step"], i["plan_seed"], w.anchors_per_row, w.block_size,
                             self.anchors, self.positions, self.valid, self.loss_mask, self.num, self.base)
         ev[1].record()
-        d.dflash_ctx_proj(cfg, i["states"], w.target_hidden, T * w.target_hidden, T, self.ctx_pos, i["w_proj"],
-                          i["layers"], self.ck, self.cv, T, 0, self.ws)
+        d.dflash_ctx_proj_train(cfg, i["states"], w.target_hidden, T * w.target_hidden, T, self.ctx_pos,
+                                i["w_proj"], i["layers"], self.ck, self.cv, T, 0, self.C, self.ws)
         ev[2].record()
         anc, val = self.anchors.reshape(-1), self.valid.reshape(-1)
         d.dflash_body_forward_train(cfg, nb, i["emb"], i["layers"], self.ck, self.cv, T, self.base, anc, val, self.out,
@@ -462,7 +469,9 @@ class TrainingBuffers:
                                self.d_out, self.demb, self.grads, self.dck, self.dcv, self.ws_bb)
         ev[6].record()
         d.dflash_ctx_proj_backward(cfg, i["states"], w.target_hidden, T * w.target_hidden, T, self.ctx_pos,
-                                   i["layers"], self.dck, self.dcv, T, 0, self.dW, None, self.ws_cb)
+                                   i["layers"], self.dck, self.dcv, T, 0, self.dW, None, self.ws_cb,
+                                   ctx_hidden=self.C, d_wk=[g["wk"] for g in self.grads],
+                                   d_wv=[g["wv"] for g in self.grads])
         ev[7].record()
         self.opt_step += 1
         d.dflash_adamw_step(cfg.dtype, self.opt, lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.01,
@@ -474,8 +483,9 @@ class TrainingBuffers:
 def train_step_row(d, torch, w, vocab, device, reps=3):
     """One whole training step of the 5-layer training workload through the
     library, timed end to end with events on the launch stream: plan, context
-    projection, training forward (reserve space), LM head + decayed CE keeping
-    its logits, its backward from them, body backward, W_proj backward, and the
+    projection (keeping C), training forward (reserve space), LM head + decayed
+    CE keeping its logits, its backward from them, body backward, the context
+    path's backward (W_proj, and its share of every Wk / Wv gradient), and the
     AdamW step over every layer weight and W_proj (fp32 master copies and
     moments; it writes the bf16 weights the next step's forward reads). Synthetic inputs of the workload's
     shapes; targets are random tokens at the block positions; frozen synthetic

@@ -6,7 +6,7 @@ are torch tensors used as device buffers (their data pointers are passed);
 the stream defaults to torch's current stream on the tensor's device.
 
 The names mirror the C entry points:
-  dflash_build_plan, dflash_ctx_proj, dflash_ctx_append, dflash_ctx_append_noalloc,
+  dflash_build_plan, dflash_ctx_proj, dflash_ctx_proj_train, dflash_ctx_append, dflash_ctx_append_noalloc,
   dflash_ctx_truncate,
   dflash_block_attn, dflash_body_forward, dflash_verify_greedy,
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
@@ -35,7 +35,8 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 DFLASH_NOALLOC_SCRATCH_BYTES = 32 << 20
 DFLASH_F32, DFLASH_BF16 = 0, 1
 
-EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_append", "dflash_ctx_append_noalloc",
+EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_proj_train", "dflash_ctx_append",
+            "dflash_ctx_append_noalloc",
             "dflash_ctx_truncate",
             "dflash_block_attn", "dflash_body_forward", "dflash_verify_greedy", "dflash_verify_sample",
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
@@ -54,7 +55,7 @@ KERNELS = {"plan": 0, "ctx_proj": 1, "ctx_kv": 2, "rmsnorm": 3, "qkv": 4, "atten
            "lm_head": 11, "lm_ce": 12, "attn_bwd": 13,
            "ctx_bwd_pack": 14, "ctx_bwd_dc": 15, "ctx_bwd_dw": 16,
            "bwd_pack": 17, "bwd_data": 18, "bwd_weight": 19, "bwd_norm": 20,
-           "lm_bwd_prep": 21, "lm_bwd_dz": 22, "lm_bwd_dh": 23}
+           "lm_bwd_prep": 21, "lm_bwd_dz": 22, "lm_bwd_dh": 23, "ctx_bwd_dkv": 24}
 
 
 class DFlashConfig(ctypes.Structure):
@@ -100,6 +101,8 @@ def _load() -> ctypes.CDLL:
     lib.dflash_build_plan.restype = ctypes.c_int
     lib.dflash_ctx_proj.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, I64, I64, P, SZ, P]
     lib.dflash_ctx_proj.restype = ctypes.c_int
+    lib.dflash_ctx_proj_train.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, I64, I64, P, P, SZ, P]
+    lib.dflash_ctx_proj_train.restype = ctypes.c_int
     lib.dflash_ctx_append.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, P, I64, P, SZ, P]
     lib.dflash_ctx_append.restype = ctypes.c_int
     lib.dflash_ctx_append_noalloc.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, P, P, I64, P]
@@ -135,7 +138,8 @@ def _load() -> ctypes.CDLL:
     lib.dflash_block_attn_backward.restype = ctypes.c_int
     lib.dflash_block_attn_backward_workspace_size.argtypes = [CFG, I32]
     lib.dflash_block_attn_backward_workspace_size.restype = ctypes.c_size_t
-    lib.dflash_ctx_proj_backward.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, I64, I64, P, P, P, SZ, P]
+    lib.dflash_ctx_proj_backward.argtypes = [CFG, P, I64, I64, I64, P, P, P, P, I64, I64, P, P, P, P, P, P, SZ,
+                                             P]
     lib.dflash_ctx_proj_backward.restype = ctypes.c_int
     lib.dflash_body_forward_train.argtypes = [CFG, I32, P, P, P, P, I64, P, P, P, P, P, SZ, P, SZ, P]
     lib.dflash_body_forward_train.restype = ctypes.c_int
@@ -269,6 +273,20 @@ def dflash_ctx_proj(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_lay
                              ck, cv, int(ctx_total), int(row_offset), wp, wb,
                              _stream(stream, target_states))
     _check("dflash_ctx_proj", s)
+
+
+def dflash_ctx_proj_train(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
+                          num_rows: int, positions, w_proj, layers, ctx_k: List, ctx_v: List,
+                          ctx_total: int, row_offset: int, ctx_hidden, workspace, stream=None) -> None:
+    """dflash_ctx_proj that also writes C = X W_proj^T into ctx_hidden [num_rows, H] (config dtype)."""
+    lw = _layers(layers)
+    ck, cv = _ptr_array(ctx_k), _ptr_array(ctx_v)
+    wp, wb = _ws(workspace)
+    s = _lib.dflash_ctx_proj_train(ctypes.byref(cfg), _ptr(target_states), int(ts_row_stride),
+                                   int(ts_layer_stride), int(num_rows), _ptr(positions), _ptr(w_proj), lw,
+                                   ck, cv, int(ctx_total), int(row_offset), _ptr(ctx_hidden), wp, wb,
+                                   _stream(stream, target_states))
+    _check("dflash_ctx_proj_train", s)
 
 
 def dflash_ctx_append(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
@@ -434,14 +452,19 @@ def dflash_ctx_proj_backward_workspace_size(cfg: DFlashConfig, num_rows: int) ->
 
 def dflash_ctx_proj_backward(cfg: DFlashConfig, target_states, ts_row_stride: int, ts_layer_stride: int,
                              num_rows: int, positions, layers, d_ctx_k, d_ctx_v, ctx_total: int, row_offset: int,
-                             d_w_proj, d_ctx_hidden, workspace, stream=None) -> None:
+                             d_w_proj, d_ctx_hidden, workspace, stream=None, ctx_hidden=None, d_wk=None,
+                             d_wv=None) -> None:
+    """With ctx_hidden (C from dflash_ctx_proj_train), the context path's share of each layer's
+    Wk / Wv gradient is added into d_wk[l] / d_wv[l] (f32 [Hkv*D, H])."""
     lw = _layers(layers)
     gk, gv = _ptr_array(d_ctx_k), _ptr_array(d_ctx_v)
+    dk = _ptr_array(d_wk) if d_wk is not None else None
+    dv = _ptr_array(d_wv) if d_wv is not None else None
     wp, wb = _ws(workspace)
     s = _lib.dflash_ctx_proj_backward(ctypes.byref(cfg), _ptr(target_states), int(ts_row_stride),
                                       int(ts_layer_stride), int(num_rows), _ptr(positions), lw, gk, gv,
-                                      int(ctx_total), int(row_offset), _ptr(d_w_proj), _ptr(d_ctx_hidden), wp, wb,
-                                      _stream(stream, d_w_proj))
+                                      int(ctx_total), int(row_offset), _ptr(d_w_proj), _ptr(d_ctx_hidden),
+                                      _ptr(ctx_hidden), dk, dv, wp, wb, _stream(stream, d_w_proj))
     _check("dflash_ctx_proj_backward", s)
 
 

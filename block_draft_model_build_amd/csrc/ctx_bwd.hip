@@ -7,9 +7,13 @@
 //   G = [Gk_1 .. Gk_L | Gv_1 .. Gv_L]     Gk_l = RoPE^T(dKc_l), Gv_l = dVc_l   [T, 2 L Hkv D]
 //   dC = G [Wk_1; ..; Wk_L; Wv_1; ..; Wv_L]                                      [T, H]
 //   dW_proj = dC^T X                                                            [H, L_t H_t]
-// Both products run on the K-contiguous MFMA GEMM of gemm.h; the operands
-// whose contraction runs down their rows (the stacked K/V weights, dC and X)
-// are transposed on the way (LDS tiles; dC in the first product's epilogue).
+// and, given C from the training forward, the context path's share of every
+// layer's K/V projection gradient (each layer's Wk, Wv map C into its K/V):
+//   d[Wk_1; ..; Wk_L; Wv_1; ..; Wv_L] += G^T C                                  [2 L Hkv D, H]
+// The products run on the K-contiguous MFMA GEMM of gemm.h; the operands
+// whose contraction runs down their rows (the stacked K/V weights, dC, X, G
+// and C) are transposed on the way (LDS tiles; dC in the first product's
+// epilogue).
 #include "gemm_select.h"
 #include "internal.h"
 #include "transpose.h"
@@ -119,10 +123,32 @@ template <typename T> struct EpDCT {
     }
 };
 
+// d[Wk; Wv] += acc: row r of the product is row r % (Hkv D) of layer
+// (r / (Hkv D)) % L's Wk (r < L Hkv D) or Wv (after), added in fp32.
+struct EpKVGradAdd {
+    float* dst[2 * kMaxLayers];        // Wk of every layer, then Wv of every layer
+    int kvd, H;
+    template <int MI, int NI, int WN>
+    __device__ void apply(int mb, int nb, f32x16 (&acc)[MI][NI], int lane, int M) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = mb + i * 32 + acc_row(e, lane);
+                if (row >= M) continue;
+                const int t = row / kvd;
+                float* o = dst[t] + (int64_t)(row - t * kvd) * H + nb + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) o[j * 32] += acc[i][j][e];
+            }
+    }
+};
+
 // Workspace (256-byte aligned regions, config dtype):
-//   G [T][Kg], WkvT [H][Kg], dCT [H][Tp], XT [L_t H_t][Tp];  Kg = 2 L Hkv D, Tp = T rounded up to 64.
+//   G [T][Kg], WkvT [H][Kg], dCT [H][Tp], XT [L_t H_t][Tp], and for the K/V weight
+//   gradients GT [Kg][Tp], CT [H][Tp];  Kg = 2 L Hkv D, Tp = T rounded up to 64.
 struct CtxBwdLayout {
-    size_t g, wkvt, dct, xt, total;
+    size_t g, wkvt, dct, xt, gt, ct, total;
     int64_t kg, tp;
 };
 CtxBwdLayout ctx_bwd_layout(const dflash_config& c, int64_t rows) {
@@ -136,6 +162,8 @@ CtxBwdLayout ctx_bwd_layout(const dflash_config& c, int64_t rows) {
     l.wkvt = off; off = align_up(off + eb * (size_t)c.hidden * l.kg, A);
     l.dct = off;  off = align_up(off + eb * (size_t)c.hidden * l.tp, A);
     l.xt = off;   off = align_up(off + eb * (size_t)kin * l.tp, A);
+    l.gt = off;   off = align_up(off + eb * (size_t)l.kg * l.tp, A);
+    l.ct = off;   off = align_up(off + eb * (size_t)c.hidden * l.tp, A);
     l.total = off + A;
     return l;
 }
@@ -143,8 +171,8 @@ CtxBwdLayout ctx_bwd_layout(const dflash_config& c, int64_t rows) {
 template <typename T>
 hipError_t ctx_bwd_t(const dflash_config& c, const T* ts, int64_t rs, int64_t ls, int64_t rows,
                      const int32_t* positions, const dflash_layer_weights* layers, const GradPtrs& gp,
-                     int64_t ctx_total, int64_t row_offset, float* d_w_proj, float* d_ctx_hidden, char* ws,
-                     hipStream_t st) {
+                     int64_t ctx_total, int64_t row_offset, float* d_w_proj, float* d_ctx_hidden, const T* C,
+                     const EpKVGradAdd& dkv, char* ws, hipStream_t st) {
     const CtxBwdLayout lay = ctx_bwd_layout(c, rows);
     const int H = c.hidden, L = c.num_layers, hkv = c.num_kv_heads, D = c.head_dim;
     const int64_t kin = (int64_t)c.num_target_layers * c.target_hidden, kg = lay.kg, tp = lay.tp;
@@ -179,8 +207,21 @@ hipError_t ctx_bwd_t(const dflash_config& c, const T* ts, int64_t rs, int64_t ls
     e = gemm<T>(DFLASH_KERNEL_CTX_BWD_DC, (int)rows, H, (int)kg, APlain<T>{G, kg}, BPlain<T>{wkvt, kg},
                 EpDCT<T>{dct, tp, d_ctx_hidden, H}, st);
     if (e != hipSuccess) return e;
-    return gemm<T>(DFLASH_KERNEL_CTX_BWD_DW, H, (int)kin, (int)tp, APlain<T>{dct, tp}, BPlain<T>{xt, tp},
-                   EpStoreF32{d_w_proj, kin}, st);
+    e = gemm<T>(DFLASH_KERNEL_CTX_BWD_DW, H, (int)kin, (int)tp, APlain<T>{dct, tp}, BPlain<T>{xt, tp},
+                EpStoreF32{d_w_proj, kin}, st);
+    if (e != hipSuccess || C == nullptr) return e;
+    // d[Wk; Wv] += G^T C: both operands transposed to [features][Tp] (zero past the last row).
+    T* gt = reinterpret_cast<T*>(ws + lay.gt);
+    T* ct = reinterpret_cast<T*>(ws + lay.ct);
+    {
+        ProfScope prof(DFLASH_KERNEL_CTX_BWD_PACK, st);
+        hipLaunchKernelGGL((transpose_kernel<T, SrcPlain<T>>), dim3((unsigned)(tp / 64), (unsigned)(kg / 64)),
+                           dim3(256), 0, st, SrcPlain<T>{G, kg}, rows, tp, kg, gt, tp);
+        hipLaunchKernelGGL((transpose_kernel<T, SrcPlain<T>>), dim3((unsigned)(tp / 64), (unsigned)(H / 64)),
+                           dim3(256), 0, st, SrcPlain<T>{C, H}, rows, tp, (int64_t)H, ct, tp);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return gemm<T>(DFLASH_KERNEL_CTX_BWD_DKV, (int)kg, H, (int)tp, APlain<T>{gt, tp}, BPlain<T>{ct, tp}, dkv, st);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -201,8 +242,9 @@ extern "C" dflash_status dflash_ctx_proj_backward(const dflash_config* cfg, cons
                                                   const int32_t* positions, const dflash_layer_weights* layers,
                                                   const float* const* d_ctx_k, const float* const* d_ctx_v,
                                                   int64_t ctx_total, int64_t row_offset, float* d_w_proj,
-                                                  float* d_ctx_hidden, void* workspace, size_t workspace_bytes,
-                                                  void* hip_stream) {
+                                                  float* d_ctx_hidden, const void* ctx_hidden,
+                                                  float* const* d_wk, float* const* d_wv, void* workspace,
+                                                  size_t workspace_bytes, void* hip_stream) {
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
     if (num_rows < 0 || ctx_total < 0 || row_offset < 0 || row_offset + num_rows > ctx_total || d_w_proj == nullptr)
@@ -229,6 +271,18 @@ extern "C" dflash_status dflash_ctx_proj_backward(const dflash_config* cfg, cons
         gp.dk[l] = d_ctx_k[l];
         gp.dv[l] = d_ctx_v[l];
     }
+    EpKVGradAdd dkv{};
+    if (ctx_hidden != nullptr) {
+        if (!aligned16(ctx_hidden) || d_wk == nullptr || d_wv == nullptr) return DFLASH_ERR_INVALID_ARG;
+        for (int l = 0; l < cfg->num_layers; ++l) {
+            if (d_wk[l] == nullptr || d_wv[l] == nullptr || !aligned16(d_wk[l]) || !aligned16(d_wv[l]))
+                return DFLASH_ERR_INVALID_ARG;
+            dkv.dst[l] = d_wk[l];
+            dkv.dst[cfg->num_layers + l] = d_wv[l];
+        }
+        dkv.kvd = cfg->num_kv_heads * cfg->head_dim;
+        dkv.H = cfg->hidden;
+    }
     const size_t need = ctx_bwd_layout(*cfg, num_rows).total;
     if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return DFLASH_ERR_WORKSPACE;
@@ -236,9 +290,11 @@ extern "C" dflash_status dflash_ctx_proj_backward(const dflash_config* cfg, cons
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = ctx_bwd_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
-                              num_rows, positions, layers, gp, ctx_total, row_offset, d_w_proj, d_ctx_hidden, ws, st);
+                              num_rows, positions, layers, gp, ctx_total, row_offset, d_w_proj, d_ctx_hidden,
+                              static_cast<const __bf16*>(ctx_hidden), dkv, ws, st);
     else
         e = ctx_bwd_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
-                             num_rows, positions, layers, gp, ctx_total, row_offset, d_w_proj, d_ctx_hidden, ws, st);
+                             num_rows, positions, layers, gp, ctx_total, row_offset, d_w_proj, d_ctx_hidden,
+                             static_cast<const float*>(ctx_hidden), dkv, ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }

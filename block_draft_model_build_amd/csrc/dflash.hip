@@ -183,12 +183,11 @@ static dflash_status ws_check(const dflash_config* c, int nb, int64_t rows, void
     return DFLASH_OK;
 }
 
-extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* target_states,
-                                         int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
-                                         const int32_t* positions, const void* w_proj,
-                                         const dflash_layer_weights* layers, void* const* ctx_k,
-                                         void* const* ctx_v, int64_t ctx_total, int64_t row_offset,
-                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+static dflash_status ctx_proj_entry(const dflash_config* cfg, const void* target_states, int64_t ts_row_stride,
+                                    int64_t ts_layer_stride, int64_t num_rows, const int32_t* positions,
+                                    const void* w_proj, const dflash_layer_weights* layers, void* const* ctx_k,
+                                    void* const* ctx_v, int64_t ctx_total, int64_t row_offset, void* keep_c,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream) {
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
     if (num_rows < 0 || ctx_total < 0 || row_offset < 0 || row_offset + num_rows > ctx_total)
@@ -198,7 +197,8 @@ extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* t
     const int64_t vec = 16 / elem_bytes(*cfg);
     if (target_states == nullptr || positions == nullptr || w_proj == nullptr || layers == nullptr ||
         ctx_k == nullptr || ctx_v == nullptr || !aligned16(target_states) || !aligned16(w_proj) ||
-        ts_row_stride <= 0 || ts_layer_stride < 0 || ts_row_stride % vec != 0 || ts_layer_stride % vec != 0)
+        !aligned16(keep_c) || ts_row_stride <= 0 || ts_layer_stride < 0 || ts_row_stride % vec != 0 ||
+        ts_layer_stride % vec != 0)
         return DFLASH_ERR_INVALID_ARG;
     for (int l = 0; l < cfg->num_layers; ++l)
         if (layers[l].wk == nullptr || layers[l].wv == nullptr || ctx_k[l] == nullptr || ctx_v[l] == nullptr ||
@@ -207,17 +207,39 @@ extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* t
     if ((s = ws_check(cfg, 0, num_rows, workspace, workspace_bytes)) != DFLASH_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     char* ws = static_cast<char*>(workspace);
-    char* C = ws + workspace_layout(*cfg, 0, num_rows).c;
+    void* C = keep_c != nullptr ? keep_c : ws + workspace_layout(*cfg, 0, num_rows).c;
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
         e = ctx_proj_t<__bf16>(*cfg, static_cast<const __bf16*>(target_states), ts_row_stride, ts_layer_stride,
                                num_rows, positions, static_cast<const __bf16*>(w_proj), layers, ctx_k, ctx_v,
-                               ctx_total, row_offset, nullptr, reinterpret_cast<__bf16*>(C), st);
+                               ctx_total, row_offset, nullptr, static_cast<__bf16*>(C), st);
     else
         e = ctx_proj_t<float>(*cfg, static_cast<const float*>(target_states), ts_row_stride, ts_layer_stride,
                               num_rows, positions, static_cast<const float*>(w_proj), layers, ctx_k, ctx_v,
-                              ctx_total, row_offset, nullptr, reinterpret_cast<float*>(C), st);
+                              ctx_total, row_offset, nullptr, static_cast<float*>(C), st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+extern "C" dflash_status dflash_ctx_proj(const dflash_config* cfg, const void* target_states,
+                                         int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                         const int32_t* positions, const void* w_proj,
+                                         const dflash_layer_weights* layers, void* const* ctx_k,
+                                         void* const* ctx_v, int64_t ctx_total, int64_t row_offset,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return ctx_proj_entry(cfg, target_states, ts_row_stride, ts_layer_stride, num_rows, positions, w_proj, layers,
+                          ctx_k, ctx_v, ctx_total, row_offset, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" dflash_status dflash_ctx_proj_train(const dflash_config* cfg, const void* target_states,
+                                               int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                               const int32_t* positions, const void* w_proj,
+                                               const dflash_layer_weights* layers, void* const* ctx_k,
+                                               void* const* ctx_v, int64_t ctx_total, int64_t row_offset,
+                                               void* ctx_hidden, void* workspace, size_t workspace_bytes,
+                                               void* hip_stream) {
+    if (num_rows > 0 && ctx_hidden == nullptr) return DFLASH_ERR_INVALID_ARG;
+    return ctx_proj_entry(cfg, target_states, ts_row_stride, ts_layer_stride, num_rows, positions, w_proj, layers,
+                          ctx_k, ctx_v, ctx_total, row_offset, ctx_hidden, workspace, workspace_bytes, hip_stream);
 }
 
 // Host-side checks shared by dflash_ctx_append and its allocation-free variant.

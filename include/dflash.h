@@ -162,6 +162,26 @@ dflash_status dflash_ctx_proj(const dflash_config *cfg, const void *target_state
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * dflash_ctx_proj_train -- dflash_ctx_proj that also keeps C = X W_proj^T for
+ * the backward (the way dflash_body_forward_train keeps the body's
+ * activations): the context path's share of the Wk / Wv gradients is G^T C
+ * (dflash_ctx_proj_backward). Same caches, bit for bit.
+ *
+ *   ctx_hidden     device [num_rows, H] in the config dtype, 16-byte aligned,
+ *                  caller-owned: written with C (row r = target row r)
+ *   other arguments as dflash_ctx_proj (same workspace size).
+ * Errors: as dflash_ctx_proj; INVALID_ARG also for a null or misaligned
+ * ctx_hidden when num_rows > 0.
+ */
+dflash_status dflash_ctx_proj_train(const dflash_config *cfg, const void *target_states,
+                                    int64_t ts_row_stride, int64_t ts_layer_stride, int64_t num_rows,
+                                    const int32_t *positions, const void *w_proj,
+                                    const dflash_layer_weights *layers, void *const *ctx_k,
+                                    void *const *ctx_v, int64_t ctx_total, int64_t row_offset,
+                                    void *ctx_hidden, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream);
+
+/*
  * dflash_ctx_append -- incremental form of dflash_ctx_proj for multi-cycle
  * drafting: newly verified target hidden states are projected exactly as in
  * dflash_ctx_proj and scattered into the caches at caller-chosen rows, so
@@ -337,7 +357,8 @@ typedef enum dflash_kernel {
     DFLASH_KERNEL_LM_BWD_DZ = 22,    /* dz: GEMM of the logits with the CE gradient epilogue, or (_saved)
                                         the elementwise pass over the kept logits */
     DFLASH_KERNEL_LM_BWD_DH = 23,    /* GEMM d_hidden = dz W_lm */
-    DFLASH_KERNEL_COUNT = 24
+    DFLASH_KERNEL_CTX_BWD_DKV = 24,  /* dflash_ctx_proj_backward: GEMM d[Wk; Wv] += G^T C */
+    DFLASH_KERNEL_COUNT = 25
 } dflash_kernel;
 
 /*
@@ -576,6 +597,15 @@ size_t dflash_block_attn_backward_workspace_size(const dflash_config *cfg, int32
  *                  16-byte aligned
  *   d_w_proj       device f32 [H, L_t*H_t], overwritten (zero when num_rows == 0)
  *   d_ctx_hidden   optional device f32 [num_rows, H]: dC (NULL: not written)
+ *   ctx_hidden     optional device [num_rows, H] in the config dtype: C of these rows,
+ *                  as dflash_ctx_proj_train kept it. With it, the context path's share
+ *                  of every layer's Wk and Wv gradient is ADDED to d_wk[l], d_wv[l]:
+ *                    d_wk[l] += Gk_l^T C,   d_wv[l] += Gv_l^T C        [Hkv*D, H]
+ *                  ([P1] "How it works": the projected context enters each layer's
+ *                  K/V through that layer's own projections; dflash_body_backward
+ *                  writes the block rows' share first). NULL: not computed.
+ *   d_wk, d_wv     host arrays [num_layers] of device f32 [Hkv*D, H] (16-byte
+ *                  aligned), required with ctx_hidden, else ignored
  *   workspace      dflash_ctx_proj_backward_workspace_size(cfg, num_rows) bytes,
  *                  256-byte aligned
  * G and dC enter their products in the config dtype; the products accumulate in
@@ -588,7 +618,8 @@ dflash_status dflash_ctx_proj_backward(const dflash_config *cfg, const void *tar
                                        const int32_t *positions, const dflash_layer_weights *layers,
                                        const float *const *d_ctx_k, const float *const *d_ctx_v,
                                        int64_t ctx_total, int64_t row_offset, float *d_w_proj,
-                                       float *d_ctx_hidden, void *workspace, size_t workspace_bytes,
+                                       float *d_ctx_hidden, const void *ctx_hidden, float *const *d_wk,
+                                       float *const *d_wv, void *workspace, size_t workspace_bytes,
                                        void *hip_stream);
 size_t dflash_ctx_proj_backward_workspace_size(const dflash_config *cfg, int64_t num_rows);
 

@@ -154,6 +154,27 @@ def test_concat_and_stacked_layouts_agree():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["c1", "small_bf16"])
+def test_ctx_proj_train_keeps_c(name):
+    """dflash_ctx_proj_train writes the caches of dflash_ctx_proj bit for bit and
+    keeps C = X W_proj^T (angelspec "DFlash", How it works)."""
+    w = WORKLOADS["c1"] if name == "c1" else SMALL_BF16
+    inp = make_training_inputs(w, "cuda")
+    run = TrainingRun(d, w, inp)
+    run.ctx_proj()
+    k1, v1 = [t.clone() for t in run.ctx_k], [t.clone() for t in run.ctx_v]
+    for t in run.ctx_k + run.ctx_v:
+        t.fill_(7.0)
+    C = torch.full((run.T, w.hidden), float("nan"), dtype=w.torch_dtype, device="cuda")
+    d.dflash_ctx_proj_train(run.cfg, inp["states"], w.target_hidden, run.T * w.target_hidden, run.T, run.ctx_pos,
+                            inp["w_proj"], inp["layers"], run.ctx_k, run.ctx_v, run.T, 0, C, run.ws)
+    torch.cuda.synchronize()
+    for a, b in zip(k1 + v1, run.ctx_k + run.ctx_v):
+        assert torch.equal(a, b)
+    X = oracle.concat_target_states(np64(inp["states"]))
+    compare(C, oracle.ctx_proj(X, np64(inp["w_proj"])), tol_for(w), "kept C")
+
+
 def test_one_layer_bf16_full_size():
     w = WORKLOADS["c2"]
     inp = make_training_inputs(w, "cuda")

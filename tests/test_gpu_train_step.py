@@ -3,12 +3,15 @@
 trained with an optimizer step; angelspec "DFlash", How it works, Loss, and
 Configuration: the LM head is the target's, frozen).
 
-GPU: dflash_build_plan -> dflash_ctx_proj -> dflash_body_forward_train ->
-dflash_lm_head_ce_train (keeps the logits) -> dflash_lm_head_ce_backward_saved
--> dflash_body_backward -> dflash_ctx_proj_backward, the chain the benchmark's
-training step runs. Oracle: build_plan, ctx_proj/ctx_kv, body_forward,
-lm_head_ce, lm_head_ce_backward, body_backward, ctx_proj_backward, each pinned
-on its own. Targets are the sequence's own tokens at each block position.
+GPU: dflash_build_plan -> dflash_ctx_proj_train (keeps C) ->
+dflash_body_forward_train -> dflash_lm_head_ce_train (keeps the logits) ->
+dflash_lm_head_ce_backward_saved -> dflash_body_backward ->
+dflash_ctx_proj_backward (adds the context path's share of every Wk / Wv
+gradient), the chain the benchmark's training step runs. Oracle: build_plan,
+ctx_proj/ctx_kv, body_forward, lm_head_ce, lm_head_ce_backward, body_backward,
+ctx_kv_weight_grads, ctx_proj_backward, each pinned on its own and their sum by
+central differences of a whole step's loss. Targets are the sequence's own
+tokens at each block position.
 
 Tolerance: fp32 chains every fp32 step: rel-L2 1e-5 of each gradient's scale.
 bf16: the tolerance of the body backward (rel-L2 3e-2, max-abs 6e-2 of the
@@ -48,8 +51,10 @@ def _step(w, vocab, tau, seed):
     W_lm = rng.normal("train.lm_head", (vocab, w.hidden), std=1 / math.sqrt(w.hidden), dtype=w.torch_dtype)
     run = TrainingRun(d, w, inp)
     run.plan()
-    run.ctx_proj()
     cfg, bs, R, H, L = run.cfg, w.block_size, w.num_blocks * w.block_size, w.hidden, w.num_layers
+    C = torch.empty((run.T, H), dtype=w.torch_dtype, device=dev)
+    d.dflash_ctx_proj_train(cfg, inp["states"], w.target_hidden, run.T * w.target_hidden, run.T, run.ctx_pos,
+                            inp["w_proj"], inp["layers"], run.ctx_k, run.ctx_v, run.T, 0, C, run.ws)
     pos = run.positions.reshape(-1).long().clamp(0, w.seq_len - 1)
     row = torch.arange(R, device=dev) // (bs * w.anchors_per_row)
     targets = tokens[row, pos].contiguous()
@@ -77,7 +82,8 @@ def _step(w, vocab, tau, seed):
     dW = torch.empty((H, Kt), dtype=torch.float32, device=dev)
     ws = torch.empty(d.dflash_ctx_proj_backward_workspace_size(cfg, run.T), dtype=torch.uint8, device=dev)
     d.dflash_ctx_proj_backward(cfg, inp["states"], w.target_hidden, run.T * w.target_hidden, run.T, run.ctx_pos,
-                               inp["layers"], dck, dcv, run.T, 0, dW, None, ws)
+                               inp["layers"], dck, dcv, run.T, 0, dW, None, ws, ctx_hidden=C,
+                               d_wk=[g["wk"] for g in grads], d_wv=[g["wv"] for g in grads])
     torch.cuda.synchronize()
     return dict(inp=inp, run=run, W_lm=W_lm, targets=targets, loss_mask=loss_mask, loss=float(loss.item()),
                 grads=grads, demb=demb, dW=dW)
@@ -105,6 +111,10 @@ def _oracle(w, s, tau):
     _, loss = oracle.lm_head_ce(out, np64(s["W_lm"]), t, m, bs, tau)
     d_out = oracle.lm_head_ce_backward(out, np64(s["W_lm"]), t, m, bs, tau)
     d_emb, grads, dck, dcv = oracle.body_backward(emb, layers, ck, cv, base, anchors, valid, cfg, d_out)
+    dWk, dWv = oracle.ctx_kv_weight_grads(C, pos, dck, dcv, w.num_kv_heads, w.head_dim, w.rope_theta)
+    for l in range(w.num_layers):
+        grads[l]["wk"] = grads[l]["wk"] + dWk[l]
+        grads[l]["wv"] = grads[l]["wv"] + dWv[l]
     _, dW = oracle.ctx_proj_backward(X, pos, layers, dck, dcv, w.num_kv_heads, w.head_dim, w.rope_theta)
     return loss, d_emb, grads, dW
 

@@ -206,14 +206,34 @@ def test_rejects_bad_arguments_before_launch():
     # context-path backward: rows past the cache, null output, unsupported width, small workspace
     G = (ctypes.c_void_p * cfg.num_layers)(*([fake] * cfg.num_layers))
     assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 100, P(fake), lw, G, G, 50, 0,
-                                        P(fake), None, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+                                        P(fake), None, None, None, None, P(fake), 1 << 40,
+                                        None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
-                                        None, None, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+                                        None, None, None, None, None, P(fake), 1 << 40,
+                                        None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
-                                        P(fake), None, P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
+                                        P(fake), None, None, None, None, P(fake), 64,
+                                        None) == d.DFLASH_ERR_WORKSPACE
+    # with C for the K/V weight gradients: their arrays are required and aligned
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
+                                        P(fake), None, P(fake), None, G, P(fake), 1 << 40,
+                                        None) == d.DFLASH_ERR_INVALID_ARG
+    Gbad = (ctypes.c_void_p * cfg.num_layers)(*([fake + 4] * cfg.num_layers))
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
+                                        P(fake), None, P(fake), G, Gbad, P(fake), 1 << 40,
+                                        None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_proj_backward(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), lw, G, G, 50, 0,
+                                        P(fake), None, P(fake + 8), G, G, P(fake), 1 << 40,
+                                        None) == d.DFLASH_ERR_INVALID_ARG
+    # the training context projection needs its C buffer
+    assert lib.dflash_ctx_proj_train(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), P(fake), lw, G, G, 50,
+                                     0, None, P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_ctx_proj_train(ctypes.byref(cfg), P(fake), 20480, 4096, 10, P(fake), P(fake), lw, G, G, 50,
+                                     0, P(fake + 8), P(fake), 1 << 40, None) == d.DFLASH_ERR_INVALID_ARG
     odd = d.config_from_workload(scaled(WORKLOADS["c2"], target_hidden=4032))
     assert lib.dflash_ctx_proj_backward(ctypes.byref(odd), P(fake), 5 * 4032, 4032, 10, P(fake), lw, G, G, 50, 0,
-                                        P(fake), None, P(fake), 1 << 40, None) == d.DFLASH_ERR_UNSUPPORTED
+                                        P(fake), None, None, None, None, P(fake), 1 << 40,
+                                        None) == d.DFLASH_ERR_UNSUPPORTED
     assert d.dflash_ctx_proj_backward_workspace_size(cfg, 100) > d.dflash_ctx_proj_backward_workspace_size(cfg, 10)
     # body: misaligned embeddings (16-byte reads), a null weight
     w_up = lw[0].w_up
