@@ -1017,14 +1017,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs<T> p) {
 // chunk)) splits. The multi-block chunk then grows in 128-key steps until its
 // groups' splits (each rounded up) fit the target. The item records are
 // written longest work first.
+//
+// One workgroup of 1024 threads. Up to kSchedCache groups, every group's
+// start, length and first item sit in LDS once computed (each later phase
+// would otherwise wait on dependent global loads again), and sums and scans
+// go through wave shuffles with one barrier per step.
+constexpr int kSchedCache = 4096;
 static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_t* base, const int32_t* anchor, int nb,
                                                              int64_t ctx_total, int target_shared, int target_single,
                                                              int* group_start, int* item_start, int* sched, int* meta,
                                                              int4* bmeta) {
-    __shared__ int scan[1024];
-    __shared__ long long red[2][1024];
-    __shared__ int chunk_s[2], ngroups_s, nsg_s;
-    const int tid = threadIdx.x;
+    __shared__ int gs_s[kSchedCache + 1], gl_s[kSchedCache], is_s[kSchedCache + 1];
+    __shared__ int wscan[16];
+    __shared__ long long wred[2][16];
+    __shared__ int chunk_s[2];
+    __shared__ long long sum_s[2];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int per_t = (nb + 1023) / 1024;
     const int b0 = tid * per_t;
     auto starts = [&](int n) {
@@ -1034,64 +1042,100 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
         int64_t b = clamp_base(base[n], ctx_total);
         return anchor_eff(anchor[n], b, ctx_total);
     };
-    auto inclusive_scan = [&](int v) {
-        scan[tid] = v;
-        __syncthreads();
-        for (int w = 1; w < 1024; w <<= 1) {
-            int add = tid >= w ? scan[tid - w] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
+    // Exclusive prefix of v over the threads in index order; *total = the sum.
+    auto exclusive_scan = [&](int v, int* total) {
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += u;
         }
-        int r = scan[tid];
+        if (lane == 63) wscan[wv] = incl;
         __syncthreads();
-        return r;
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int x = wscan[w];
+            before += w < wv ? x : 0;
+            all += x;
+        }
+        __syncthreads();
+        *total = all;
+        return before + incl - v;
+    };
+    // Sums of a and b over all threads (integers: any order gives the same).
+    auto block_sum2 = [&](long long a, long long b, long long* sa, long long* sb) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            a += __shfl_xor(a, o, 64);
+            b += __shfl_xor(b, o, 64);
+        }
+        if (lane == 0) {
+            wred[0][wv] = a;
+            wred[1][wv] = b;
+        }
+        __syncthreads();
+        long long ta = 0, tb = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            ta += wred[0][w];
+            tb += wred[1][w];
+        }
+        __syncthreads();
+        *sa = ta;
+        *sb = tb;
     };
     // 1. group starts
     int cnt = 0;
     for (int i = 0; i < per_t; ++i) if (b0 + i < nb && starts(b0 + i)) ++cnt;
-    int gidx = inclusive_scan(cnt) - cnt;
-    if (tid == 1023) ngroups_s = gidx + cnt;
+    int ng;
+    int gidx = exclusive_scan(cnt, &ng);
     for (int i = 0; i < per_t; ++i)
-        if (b0 + i < nb && starts(b0 + i)) group_start[gidx++] = b0 + i;
-    __syncthreads();
-    const int ng = ngroups_s;
-    if (tid == 0) group_start[ng] = nb;
+        if (b0 + i < nb && starts(b0 + i)) {
+            if (gidx <= kSchedCache) gs_s[gidx] = b0 + i;
+            group_start[gidx++] = b0 + i;
+        }
+    if (tid == 0) {
+        group_start[ng] = nb;
+        if (ng <= kSchedCache) gs_s[ng] = nb;
+    }
     __threadfence_block();
     __syncthreads();
+    const bool cached = ng <= kSchedCache;
+    auto gstart = [&](int gi) { return cached ? gs_s[gi] : group_start[gi]; };
+    auto group_len_of = [&](int gi) {
+        int mx = -1;
+        for (int n = gstart(gi), e = gstart(gi + 1); n < e; ++n) mx = max(mx, block_run(n));
+        return mx;
+    };
     // 2. group lengths -> the two split sizes
     const int gper = (ng + 1023) / 1024;
     const int g0 = tid * gper;
-    auto group_len = [&](int gi) {
-        int mx = -1;
-        for (int n = group_start[gi]; n < group_start[gi + 1]; ++n) mx = max(mx, block_run(n));
-        return mx;
-    };
-    auto single = [&](int gi) { return group_start[gi + 1] - group_start[gi] == 1; };
-    long long sum[2] = {0, 0};
-    for (int i = 0; i < gper; ++i)
-        if (g0 + i < ng) sum[single(g0 + i) ? 1 : 0] += max(group_len(g0 + i), 0);
-    red[0][tid] = sum[0];
-    red[1][tid] = sum[1];
-    __syncthreads();
-    for (int w = 512; w > 0; w >>= 1) {
-        if (tid < w) {
-            red[0][tid] += red[0][tid + w];
-            red[1][tid] += red[1][tid + w];
+    if (cached) {
+        for (int i = 0; i < gper; ++i)
+            if (g0 + i < ng) gl_s[g0 + i] = group_len_of(g0 + i);
+        __syncthreads();
+    }
+    auto group_len = [&](int gi) { return cached ? gl_s[gi] : group_len_of(gi); };
+    auto single = [&](int gi) { return gstart(gi + 1) - gstart(gi) == 1; };
+    {
+        long long sum[2] = {0, 0};
+        for (int i = 0; i < gper; ++i)
+            if (g0 + i < ng) sum[single(g0 + i) ? 1 : 0] += max(group_len(g0 + i), 0);
+        long long t0, t1;
+        block_sum2(sum[0], sum[1], &t0, &t1);
+        if (tid < 2) {
+            const long long tot = tid == 0 ? t0 : t1;
+            const int target = tid == 0 ? target_shared : target_single;
+            sum_s[tid] = tot;
+            long long c = (tot + target - 1) / target;
+            c = (c + 127) / 128 * 128;
+            if (c < 256) c = 256;
+            if (c > (1 << 30)) c = 1 << 30;
+            chunk_s[tid] = (int)c;
         }
         __syncthreads();
     }
-    __shared__ long long sum_s[2], cnt_s;
-    if (tid < 2) {
-        const int target = tid == 0 ? target_shared : target_single;
-        sum_s[tid] = red[tid][0];
-        long long c = (red[tid][0] + target - 1) / target;
-        c = (c + 127) / 128 * 128;
-        if (c < 256) c = 256;
-        if (c > (1 << 30)) c = 1 << 30;
-        chunk_s[tid] = (int)c;
-    }
-    __syncthreads();
     // Multi-block groups: rounding each group's split count up can exceed the
     // target. When there are fewer such groups than the target, binary-search
     // (in 128-key steps) the smallest chunk whose total split count fits,
@@ -1104,16 +1148,9 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
                 const int len = group_len(g0 + i);
                 local_cnt += len <= 0 ? 1 : (len + c - 1) / c;
             }
-        __syncthreads();
-        red[0][tid] = local_cnt;
-        __syncthreads();
-        for (int w = 512; w > 0; w >>= 1) {
-            if (tid < w) red[0][tid] += red[0][tid + w];
-            __syncthreads();
-        }
-        if (tid == 0) cnt_s = red[0][0];
-        __syncthreads();
-        return cnt_s;
+        long long tot, unused;
+        block_sum2(local_cnt, 0, &tot, &unused);
+        return tot;
     };
     {
         const long long n_multi = count_multi(1LL << 30);
@@ -1133,7 +1170,6 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
     }
     if (tid < 2) sched[tid == 0 ? 0 : 2] = chunk_s[tid];
     if (tid == 0) sched[1] = ng;
-    __syncthreads();
     // 3. splits per group -> item_start
     auto splits = [&](int gi) {
         const int len = group_len(gi);
@@ -1143,25 +1179,27 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
     int local = 0;
     for (int i = 0; i < gper; ++i)
         if (g0 + i < ng) local += splits(g0 + i);
-    int run = inclusive_scan(local) - local;
+    int nsg;
+    int run = exclusive_scan(local, &nsg);
     for (int i = 0; i < gper; ++i)
         if (g0 + i < ng) {
+            if (cached) is_s[g0 + i] = run;
             item_start[g0 + i] = run;
             run += splits(g0 + i);
         }
-    if (tid == 1023) {
-        item_start[ng] = run;
-        nsg_s = run;
-        sched[3] = run;
+    if (tid == 0) {
+        item_start[ng] = nsg;
+        if (cached) is_s[ng] = nsg;
+        sched[3] = nsg;
     }
     __syncthreads();
+    auto first_item = [&](int gi) { return cached ? is_s[gi] : item_start[gi]; };
     // 4. dispatch order: longest work first (each item's visible keys plus a
     //    fixed cost for its start), ties by group-split index, so the longest
     //    items start together and the short ones fill the tail. Ranks are
     //    counted by comparison (deterministic). Beyond kSortMax group-splits
     //    the reverse of block order is used (blocks come in ascending anchor
     //    order within a sequence).
-    const int nsg = nsg_s;
     constexpr int kSortMax = 4096;
     __shared__ int key_s[kSortMax], rank_s[kSortMax];
     const bool sorted = nsg <= kSortMax;
@@ -1174,7 +1212,7 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
             const bool ilv = single(gi) && ns > 1;
             for (int sp = 0; sp < ns; ++sp) {
                 const int keys = ilv ? (len + ns - 1) / ns : max(0, min(len, (sp + 1) * chunk) - sp * chunk);
-                key_s[item_start[gi] + sp] = keys + (sp == 0 ? 384 : 256);
+                key_s[first_item(gi) + sp] = keys + (sp == 0 ? 384 : 256);
             }
         }
         __syncthreads();
@@ -1192,8 +1230,8 @@ static __global__ __launch_bounds__(1024) void attn_schedule_kernel(const int64_
     for (int i = 0; i < gper; ++i) {
         const int gi = g0 + i;
         if (gi >= ng) continue;
-        const int n0 = group_start[gi], cnt_g = group_start[gi + 1] - n0;
-        const int ns = splits(gi), sg0 = item_start[gi];
+        const int n0 = gstart(gi), cnt_g = gstart(gi + 1) - n0;
+        const int ns = splits(gi), sg0 = first_item(gi);
         const int chunk = chunk_s[single(gi) ? 1 : 0];
         const int64_t b = clamp_base(base[n0], ctx_total);
         int a[kMaxGroup], amax = -1;
