@@ -41,7 +41,18 @@ def _cmp(gpu, ref, tol, what):
     assert float(np.abs(err).max()) <= tol[1] * float(np.abs(ref).max()), what
 
 
-def _step(w, vocab, tau, seed):
+def _case(name):
+    """(workload, (rel-L2, max-abs fraction), vocabulary) of the two training cases."""
+    if name == "f32":
+        return scaled(WORKLOADS["c1"], batch=2, num_layers=2, anchors_per_row=4), (1e-5, 1e-4), 301
+    w = scaled(WORKLOADS["c3"], batch=2, seq_len=160, num_target_layers=2, target_hidden=128, hidden=256,
+               num_q_heads=4, num_kv_heads=2, intermediate=512, num_layers=2, block_size=16, anchors_per_row=4,
+               seed=91)
+    return w, (3e-2, 6e-2), 999
+
+
+def _setup(w, vocab, seed):
+    """Seeded inputs of a training step: states, embeddings, weights, a shorter last row, tokens, frozen head."""
     dev = "cuda"
     mask = torch.ones((w.batch, w.seq_len), dtype=torch.uint8, device=dev)
     mask[-1, w.seq_len - w.seq_len // 5:] = 0                   # a shorter last row
@@ -49,6 +60,13 @@ def _step(w, vocab, tau, seed):
     rng = Rng(seed + 100, dev)
     tokens = rng.integers("train.tokens", 0, vocab - 1, (w.batch, w.seq_len)).to(torch.int32)
     W_lm = rng.normal("train.lm_head", (vocab, w.hidden), std=1 / math.sqrt(w.hidden), dtype=w.torch_dtype)
+    return dict(inp=inp, tokens=tokens, W_lm=W_lm)
+
+
+def _step(w, vocab, tau, setup):
+    """The GPU chain over the setup's inputs, with the weights its tensors hold now."""
+    dev = "cuda"
+    inp, tokens, W_lm = setup["inp"], setup["tokens"], setup["W_lm"]
     run = TrainingRun(d, w, inp)
     run.plan()
     cfg, bs, R, H, L = run.cfg, w.block_size, w.num_blocks * w.block_size, w.hidden, w.num_layers
@@ -89,7 +107,9 @@ def _step(w, vocab, tau, seed):
                 grads=grads, demb=demb, dW=dW)
 
 
-def _oracle(w, s, tau):
+def _oracle(w, s, tau, layers=None, w_proj=None):
+    """The oracle's chain over the same seeded inputs; layers / w_proj (fp64) replace the
+    weights the inputs were made with (the oracle's own update of them, for a later step)."""
     inp, run = s["inp"], s["run"]
     bs, S, N = w.block_size, w.seq_len, w.anchors_per_row
     plan = oracle.build_plan(inp["mask"].cpu().numpy(), inp["sample_ids"].cpu().numpy(), inp["step"],
@@ -97,10 +117,10 @@ def _oracle(w, s, tau):
     anchors = plan[0].reshape(-1)
     valid = plan[2].reshape(-1)
     assert np.array_equal(run.anchors.cpu().numpy().reshape(-1), anchors)
-    layers = layers64(inp["layers"])
+    layers = layers64(inp["layers"]) if layers is None else layers
     X = oracle.concat_target_states(np64(inp["states"]))
     pos = np.arange(w.batch * S) % S
-    C = oracle.ctx_proj(X, np64(inp["w_proj"]))
+    C = oracle.ctx_proj(X, np64(inp["w_proj"]) if w_proj is None else w_proj)
     ck, cv = oracle.ctx_kv(C, layers, pos, w.num_kv_heads, w.head_dim, w.rope_theta)
     base = np.arange(len(anchors)) // N * S
     cfg = oracle_cfg(w)
@@ -121,16 +141,9 @@ def _oracle(w, s, tau):
 
 @pytest.mark.parametrize("name", ["f32", "bf16"])
 def test_training_step_matches_the_oracle_chain(name):
-    if name == "f32":
-        w = scaled(WORKLOADS["c1"], batch=2, num_layers=2, anchors_per_row=4)
-        tol, vocab = (1e-5, 1e-4), 301
-    else:
-        w = scaled(WORKLOADS["c3"], batch=2, seq_len=160, num_target_layers=2, target_hidden=128, hidden=256,
-                   num_q_heads=4, num_kv_heads=2, intermediate=512, num_layers=2, block_size=16,
-                   anchors_per_row=4, seed=91)
-        tol, vocab = (3e-2, 6e-2), 999
+    w, tol, vocab = _case(name)
     tau = 4.0
-    s = _step(w, vocab, tau, seed=13)
+    s = _step(w, vocab, tau, _setup(w, vocab, 13))
     loss, d_emb, grads, dW = _oracle(w, s, tau)
     assert abs(s["loss"] - loss) <= (1e-5 if name == "f32" else 1e-2) * abs(loss)
     _cmp(s["demb"], d_emb, tol, "d_block_embeds")
@@ -138,3 +151,54 @@ def test_training_step_matches_the_oracle_chain(name):
         for k in NAMES:
             _cmp(s["grads"][l][k], grads[l][k], tol, f"layer {l} d_{k}")
     _cmp(s["dW"], dW, tol, "d_w_proj")
+
+
+def _adam_tensor(weight, grad):
+    return {"master": weight.float().reshape(-1).clone(), "exp_avg": torch.zeros(weight.numel(), device="cuda"),
+            "exp_avg_sq": torch.zeros(weight.numel(), device="cuda"), "grad": grad.reshape(-1),
+            "weight": weight.reshape(-1)}
+
+
+@pytest.mark.parametrize("name", ["f32", "bf16"])
+def test_second_step_after_the_optimizer(name):
+    """Two training steps with the AdamW step between them (NeMo RL "DFlash Draft
+    Body", How It Works, step 1: the body is trained with an optimizer step): the
+    second step's forward reads the working copies the optimizer wrote. The oracle
+    updates its own weights from its own gradients (fp64) and rounds them to the
+    config dtype, as a working copy is; the second step's loss and gradients are
+    compared at the first step's bar. The first step moves an entry by
+    lr * g / (|g| + eps); with eps = lr its derivative in g is at most 1, so the
+    two sides' gradient differences carry over to the weights at most one for
+    one (with eps near zero, an entry whose tiny gradient differs in sign between
+    the two sides would move by +-lr)."""
+    w, tol, vocab = _case(name)
+    tau = 4.0
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.99, eps=1e-3, weight_decay=0.01)
+    setup = _setup(w, vocab, 17)
+    inp = setup["inp"]
+    lay0, wp0 = layers64(inp["layers"]), np64(inp["w_proj"])        # before the update
+    s1 = _step(w, vocab, tau, setup)
+    _, _, g1, dW1 = _oracle(w, s1, tau)
+    tensors = [_adam_tensor(Lw[k], G[k]) for Lw, G in zip(inp["layers"], s1["grads"]) for k in NAMES]
+    tensors.append(_adam_tensor(inp["w_proj"], s1["dW"]))
+    d.dflash_adamw_step(s1["run"].cfg.dtype, tensors, step=1, **hp)
+    torch.cuda.synchronize()
+
+    def update(w0, g):
+        w1, _, _ = oracle.adamw_step(w0, g, np.zeros_like(w0), np.zeros_like(w0), 1, **hp)
+        return np64(torch.from_numpy(w1).to(w.torch_dtype))
+    lay1 = [{k: update(L[k], G[k]) for k in NAMES} for L, G in zip(lay0, g1)]
+    wp1 = update(wp0, dW1)
+    if name == "f32":                                  # the working copies themselves, against the oracle's
+        for l in range(w.num_layers):
+            for k in NAMES:
+                _cmp(inp["layers"][l][k] - torch.from_numpy(lay0[l][k]).cuda(), lay1[l][k] - lay0[l][k],
+                     (1e-4, 1e-3), f"layer {l} {k} update")
+    s2 = _step(w, vocab, tau, setup)
+    loss, d_emb, grads, dW = _oracle(w, s2, tau, layers=lay1, w_proj=wp1)
+    assert abs(s2["loss"] - loss) <= (1e-5 if name == "f32" else 1e-2) * abs(loss)
+    _cmp(s2["demb"], d_emb, tol, "step 2 d_block_embeds")
+    for l in range(w.num_layers):
+        for k in NAMES:
+            _cmp(s2["grads"][l][k], grads[l][k], tol, f"step 2 layer {l} d_{k}")
+    _cmp(s2["dW"], dW, tol, "step 2 d_w_proj")
