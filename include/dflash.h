@@ -605,12 +605,14 @@ size_t dflash_block_attn_backward_workspace_size(const dflash_config *cfg, int32
  *                  K/V through that layer's own projections; dflash_body_backward
  *                  writes the block rows' share first). NULL: not computed.
  *   d_wk, d_wv     host arrays [num_layers] of device f32 [Hkv*D, H] (16-byte
- *                  aligned), required with ctx_hidden, else ignored
+ *                  aligned), required with ctx_hidden, else ignored; left as they
+ *                  are when num_rows == 0 (the share is zero)
  *   workspace      dflash_ctx_proj_backward_workspace_size(cfg, num_rows) bytes,
  *                  256-byte aligned
- * G and dC enter their products in the config dtype; the products accumulate in
- * fp32. Errors: INVALID_ARG as dflash_ctx_proj or for a null d_w_proj;
- * UNSUPPORTED when L_t*H_t is not a multiple of 128; WORKSPACE when the
+ * G, dC and C enter their products in the config dtype; the products accumulate
+ * in fp32. Errors: INVALID_ARG as dflash_ctx_proj, for a null d_w_proj, or, with
+ * ctx_hidden, for a misaligned ctx_hidden or a null or misaligned d_wk / d_wv
+ * entry; UNSUPPORTED when L_t*H_t is not a multiple of 128; WORKSPACE when the
  * workspace is missing, small or misaligned.
  */
 dflash_status dflash_ctx_proj_backward(const dflash_config *cfg, const void *target_states,
