@@ -55,7 +55,10 @@ static hipError_t gemm(int kid, int M, int N, int K, const AL& al, const BL& bl,
         if (N % 192 == 0 && big_tiles >= 256 && 3 * ((t192 + 255) / 256) < 4 * r256)
             return launch_gemm<T, WideTile>(M, N, K, al, bl, ep, st, group);
     }
-    if (N % 256 == 0 && big_tiles >= 256) return launch_gemm<T, BigTile>(M, N, K, al, bl, ep, st, group);
+    // From half a round of big tiles up: 128x128 tiles move about half the flops per compute unit
+    // and would need at least two rounds (1024-row context K/V product of five layers:
+    // 640 tiles in 2.5 rounds against 160 big ones).
+    if (N % 256 == 0 && big_tiles >= 128) return launch_gemm<T, BigTile>(M, N, K, al, bl, ep, st, group);
     const int mid_tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if constexpr (AnyWaveWidth<EP>::value) {
         const int t192 = ((M + 127) / 128) * (N / 192);
