@@ -183,3 +183,50 @@ def test_truncate_only_shortens():
     d.dflash_ctx_truncate(lengths, keep)
     torch.cuda.synchronize()
     assert lengths.cpu().tolist() == [3, 0, 0, 7, 100]
+
+
+def test_inference_shape_append_equals_a_larger_projection():
+    """One cycle at the inference shape (64 requests x 16 rows, 5 layers of 8 KV heads,
+    5 x 4096 target features): the 1024 appended rows, scattered over the requests'
+    cache ranges, hold the bytes a one-shot projection of 4096 rows (those 1024 first)
+    writes, although the two calls tile their products differently; sampled rows match
+    the oracle."""
+    w = WORKLOADS["c5"]
+    dev = "cuda"
+    cfg = d.config_from_workload(w)
+    R, g1, cap = w.batch, w.block_size, 256
+    rows, big = R * g1, 4096
+    K = w.num_target_layers * w.target_hidden
+    rng = Rng(31, dev)
+    X = rng.normal("inf.states", (big, K), dtype=w.torch_dtype)
+    w_proj = rng.normal("inf.w_proj", (w.hidden, K), std=1 / math.sqrt(K), dtype=w.torch_dtype)
+    layers = [layer_weights(w, rng, l) for l in range(w.num_layers)]
+    lens = rng.integers("inf.len", 0, cap - g1, (R,))
+    j = torch.arange(g1, device=dev)
+    pos = torch.cat([(lens[:, None] + j[None, :]).reshape(-1),
+                     rng.integers("inf.pos", 0, 20000, (big - rows,))]).to(torch.int32)
+    dst = (torch.arange(R, device=dev)[:, None] * cap + lens[:, None] + j[None, :]).reshape(-1)
+    total = R * cap
+    mk = lambda n: ([torch.full((w.num_kv_heads, n, w.head_dim), 7.0, dtype=w.torch_dtype, device=dev)
+                     for _ in range(w.num_layers)],
+                    [torch.full((w.num_kv_heads, w.head_dim, n), 7.0, dtype=w.torch_dtype, device=dev)
+                     for _ in range(w.num_layers)])
+    ck, cv = mk(total)
+    ws = workspace(d, cfg, 0, big, dev)
+    d.dflash_ctx_append(cfg, X, K, w.target_hidden, rows, pos, dst, w_proj, layers, ck, cv, total, ws)
+    rk, rv = mk(big)
+    d.dflash_ctx_proj(cfg, X, K, w.target_hidden, big, pos, w_proj, layers, rk, rv, big, 0, ws)
+    torch.cuda.synchronize()
+    for l in range(w.num_layers):
+        assert torch.equal(ck[l][:, dst], rk[l][:, :rows]), f"K layer {l}"
+        assert torch.equal(cv[l][:, :, dst], rv[l][:, :, :rows]), f"V layer {l}"
+    sample = np.array([0, 1, 17, 511, 1000, rows - 1])
+    Xs = np64(X[torch.from_numpy(sample).cuda()])
+    C = oracle.ctx_proj(Xs, np64(w_proj))
+    kv64 = [{"wk": np64(L["wk"]), "wv": np64(L["wv"])} for L in layers]     # only these are read
+    ok, ov = oracle.ctx_kv(C, kv64, pos.cpu().numpy()[sample], w.num_kv_heads, w.head_dim, w.rope_theta)
+    d_s = dst.cpu().numpy()[sample]
+    for l in range(w.num_layers):
+        compare(ck[l][:, torch.from_numpy(d_s).cuda()], ok[l], tol_for(w), f"K layer {l} vs oracle")
+        compare(cv[l][:, :, torch.from_numpy(d_s).cuda()], ov[l].transpose(0, 2, 1), tol_for(w),
+                f"V layer {l} vs oracle")
