@@ -309,7 +309,11 @@ def next_rows(d, torch, device="cuda"):
     ms = ms_gemm + hook_ms(d, torch, [("lm_ce", 1)], call)
     out["lm_head_ce_train"] = {"ms": round(ms, 4), "lm_head_gemm_ms": round(ms_gemm, 4),
                                "logits_bytes": logits.numel()}
-    call = lambda: d.dflash_lm_head_ce_backward_saved(cfg3, rows, logits, W, tg, lm, 7.0, ce, 1.0, dh, ws5)
+    # The head is frozen: its transpose is formed once (dflash_lm_head_transpose) and kept.
+    W_t = torch.empty(d.dflash_lm_head_transpose_size(cfg3, V), dtype=torch.uint8, device=device)
+    d.dflash_lm_head_transpose(cfg3, W, W_t)
+    call = lambda: d.dflash_lm_head_ce_backward_saved(cfg3, rows, logits, W, tg, lm, 7.0, ce, 1.0, dh, ws5,
+                                                      lm_head_t=W_t)
     parts = {k: hook_ms(d, torch, [(k, 1)], call) for k in ("lm_bwd_prep", "lm_bwd_dz", "lm_bwd_dh")}
     ms = sum(parts.values())
     dz_bytes = rows * ((V + 63) // 64 * 64) * (4 + 2)
@@ -321,7 +325,7 @@ def next_rows(d, torch, device="cuda"):
         "roofline": {"bound": "mfma", "achieved": round(flops / (ms / 1e3) / 1e12, 2),
                      "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
                      "frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"], 4)}}
-    del hid, W, dh, ws5, logits
+    del hid, W, dh, ws5, logits, W_t
     # Training side: backward of one layer's dual-source attention at the
     # training shape (8 sequences of 4096, 32 blocks each at random anchors).
     T = wt.batch * wt.seq_len
@@ -417,6 +421,9 @@ class TrainingBuffers:
         self.ws_lm = u8(d.dflash_lm_head_ce_workspace_size(R, vocab))
         self.ws_lmb = u8(d.dflash_lm_head_ce_backward_workspace_size(cfg, R, vocab))
         self.logits = u8(d.dflash_lm_head_ce_logits_size(R, vocab))
+        # The LM head is frozen: its transpose for the loss backward is formed once.
+        self.lm_head_t = u8(d.dflash_lm_head_transpose_size(cfg, vocab))
+        d.dflash_lm_head_transpose(cfg, self.lm_head, self.lm_head_t)
         self.grads = [{k: e(*v.shape) for k, v in Lw.items()} for Lw in inp["layers"]]
         self.dck = [e(w.num_kv_heads, T, w.head_dim) for _ in range(L)]
         self.dcv = [e(w.num_kv_heads, w.head_dim, T) for _ in range(L)]
@@ -463,7 +470,7 @@ class TrainingBuffers:
                                   self.ws_lm)
         ev[4].record()
         d.dflash_lm_head_ce_backward_saved(cfg, self.out.shape[0], self.logits, self.lm_head, targets, lm, 7.0,
-                                           self.ce, 1.0, self.d_out, self.ws_lmb)
+                                           self.ce, 1.0, self.d_out, self.ws_lmb, lm_head_t=self.lm_head_t)
         ev[5].record()
         d.dflash_body_backward(cfg, nb, self.reserve, i["layers"], self.ck, self.cv, T, self.base, anc, val,
                                self.d_out, self.demb, self.grads, self.dck, self.dcv, self.ws_bb)
@@ -484,10 +491,11 @@ def train_step_row(d, torch, w, vocab, device, reps=3):
     """One whole training step of the 5-layer training workload through the
     library, timed end to end with events on the launch stream: plan, context
     projection (keeping C), training forward (reserve space), LM head + decayed
-    CE keeping its logits, its backward from them, body backward, the context
-    path's backward (W_proj, and its share of every Wk / Wv gradient), and the
-    AdamW step over every layer weight and W_proj (fp32 master copies and
-    moments; it writes the bf16 weights the next step's forward reads). Synthetic inputs of the workload's
+    CE keeping its logits, its backward from them (the frozen head transposed
+    once, outside the step), body backward, the context path's backward (W_proj,
+    and its share of every Wk / Wv gradient), and the AdamW step over every
+    layer weight and W_proj (fp32 master copies and moments; it writes the bf16
+    weights the next step's forward reads). Synthetic inputs of the workload's
     shapes; targets are random tokens at the block positions; frozen synthetic
     LM head of the given vocabulary. Also the events between the stages."""
     bufs = TrainingBuffers(d, torch, w, vocab, device)

@@ -12,6 +12,7 @@ The names mirror the C entry points:
   dflash_verify_sample, dflash_lm_head_ce, dflash_lm_head_ce_workspace_size,
   dflash_lm_head_ce_backward, dflash_lm_head_ce_backward_workspace_size,
   dflash_lm_head_ce_train, dflash_lm_head_ce_logits_size, dflash_lm_head_ce_backward_saved,
+  dflash_lm_head_transpose, dflash_lm_head_transpose_size,
   dflash_block_attn_backward, dflash_block_attn_backward_workspace_size,
   dflash_ctx_proj_backward, dflash_ctx_proj_backward_workspace_size,
   dflash_body_forward_train, dflash_body_train_reserve_size, dflash_body_backward,
@@ -42,6 +43,7 @@ EXPORTED = ("dflash_build_plan", "dflash_ctx_proj", "dflash_ctx_proj_train", "df
             "dflash_lm_head_ce", "dflash_lm_head_ce_workspace_size",
             "dflash_lm_head_ce_backward", "dflash_lm_head_ce_backward_workspace_size",
             "dflash_lm_head_ce_train", "dflash_lm_head_ce_logits_size", "dflash_lm_head_ce_backward_saved",
+            "dflash_lm_head_transpose", "dflash_lm_head_transpose_size",
             "dflash_block_attn_backward", "dflash_block_attn_backward_workspace_size",
             "dflash_ctx_proj_backward", "dflash_ctx_proj_backward_workspace_size",
             "dflash_body_forward_train", "dflash_body_train_reserve_size", "dflash_body_backward",
@@ -119,8 +121,12 @@ def _load() -> ctypes.CDLL:
     lib.dflash_verify_sample.restype = ctypes.c_int
     lib.dflash_lm_head_ce.argtypes = [CFG, I32, P, P, I32, P, P, ctypes.c_double, P, P, P, SZ, P]
     lib.dflash_lm_head_ce.restype = ctypes.c_int
-    lib.dflash_lm_head_ce_backward.argtypes = [CFG, I32, P, P, I32, P, P, ctypes.c_double, P, ctypes.c_double, P,
-                                               P, SZ, P]
+    lib.dflash_lm_head_ce_backward.argtypes = [CFG, I32, P, P, P, SZ, I32, P, P, ctypes.c_double, P,
+                                               ctypes.c_double, P, P, SZ, P]
+    lib.dflash_lm_head_transpose.argtypes = [CFG, P, I32, P, SZ, P]
+    lib.dflash_lm_head_transpose.restype = ctypes.c_int
+    lib.dflash_lm_head_transpose_size.argtypes = [CFG, I32]
+    lib.dflash_lm_head_transpose_size.restype = ctypes.c_size_t
     lib.dflash_lm_head_ce_backward.restype = ctypes.c_int
     lib.dflash_lm_head_ce_backward_workspace_size.argtypes = [CFG, I32, I32]
     lib.dflash_lm_head_ce_backward_workspace_size.restype = ctypes.c_size_t
@@ -130,7 +136,7 @@ def _load() -> ctypes.CDLL:
     lib.dflash_lm_head_ce_train.restype = ctypes.c_int
     lib.dflash_lm_head_ce_logits_size.argtypes = [I32, I32]
     lib.dflash_lm_head_ce_logits_size.restype = ctypes.c_size_t
-    lib.dflash_lm_head_ce_backward_saved.argtypes = [CFG, I32, P, SZ, P, I32, P, P, ctypes.c_double, P,
+    lib.dflash_lm_head_ce_backward_saved.argtypes = [CFG, I32, P, SZ, P, P, SZ, I32, P, P, ctypes.c_double, P,
                                                      ctypes.c_double, P, P, SZ, P]
     lib.dflash_lm_head_ce_backward_saved.restype = ctypes.c_int
     lib.dflash_block_attn_backward.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
@@ -403,15 +409,29 @@ def dflash_lm_head_ce_train(cfg: DFlashConfig, hidden, lm_head, targets, loss_ma
 
 def dflash_lm_head_ce_backward_saved(cfg: DFlashConfig, rows: int, logits, lm_head, targets, loss_mask,
                                      decay_tau: float, row_ce, d_loss: float, d_hidden, workspace,
-                                     stream=None) -> None:
-    """dflash_lm_head_ce_backward from the logits dflash_lm_head_ce_train kept -> d_hidden [rows, H]."""
+                                     stream=None, lm_head_t=None) -> None:
+    """dflash_lm_head_ce_backward from the logits dflash_lm_head_ce_train kept -> d_hidden [rows, H];
+    lm_head_t: an optional kept dflash_lm_head_transpose of the head."""
     vocab = int(lm_head.shape[0])
     wp, wb = _ws(workspace)
     lp, lb = _ws(logits)
-    s = _lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), int(rows), lp, lb, _ptr(lm_head), vocab,
+    tp, tb = _ws(lm_head_t)
+    s = _lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), int(rows), lp, lb, _ptr(lm_head), tp, tb, vocab,
                                               _ptr(targets), _ptr(loss_mask), float(decay_tau), _ptr(row_ce),
                                               float(d_loss), _ptr(d_hidden), wp, wb, _stream(stream, lm_head))
     _check("dflash_lm_head_ce_backward_saved", s)
+
+
+def dflash_lm_head_transpose_size(cfg: DFlashConfig, vocab: int) -> int:
+    return _lib.dflash_lm_head_transpose_size(ctypes.byref(cfg), int(vocab))
+
+
+def dflash_lm_head_transpose(cfg: DFlashConfig, lm_head, lm_head_t, stream=None) -> None:
+    """lm_head [vocab, H] -> lm_head_t (a byte buffer of dflash_lm_head_transpose_size bytes): W_lm^T [H][vp]."""
+    tp, tb = _ws(lm_head_t)
+    s = _lib.dflash_lm_head_transpose(ctypes.byref(cfg), _ptr(lm_head), int(lm_head.shape[0]), tp, tb,
+                                      _stream(stream, lm_head))
+    _check("dflash_lm_head_transpose", s)
 
 
 def dflash_lm_head_ce_backward_workspace_size(cfg: DFlashConfig, rows: int, vocab: int) -> int:
@@ -419,14 +439,16 @@ def dflash_lm_head_ce_backward_workspace_size(cfg: DFlashConfig, rows: int, voca
 
 
 def dflash_lm_head_ce_backward(cfg: DFlashConfig, hidden, lm_head, targets, loss_mask, decay_tau: float, row_ce,
-                               d_loss: float, d_hidden, workspace, stream=None) -> None:
+                               d_loss: float, d_hidden, workspace, stream=None, lm_head_t=None) -> None:
     """hidden [rows, H], lm_head [vocab, H] (config dtype), targets i32 / loss_mask u8 [rows], row_ce f32 [rows]
-    from dflash_lm_head_ce -> d_hidden [rows, H] (config dtype)."""
+    from dflash_lm_head_ce -> d_hidden [rows, H] (config dtype); lm_head_t: an optional kept
+    dflash_lm_head_transpose of the head."""
     rows, vocab = int(hidden.shape[0]), int(lm_head.shape[0])
     wp, wb = _ws(workspace)
-    s = _lib.dflash_lm_head_ce_backward(ctypes.byref(cfg), rows, _ptr(hidden), _ptr(lm_head), vocab, _ptr(targets),
-                                        _ptr(loss_mask), float(decay_tau), _ptr(row_ce), float(d_loss),
-                                        _ptr(d_hidden), wp, wb, _stream(stream, hidden))
+    tp, tb = _ws(lm_head_t)
+    s = _lib.dflash_lm_head_ce_backward(ctypes.byref(cfg), rows, _ptr(hidden), _ptr(lm_head), tp, tb, vocab,
+                                        _ptr(targets), _ptr(loss_mask), float(decay_tau), _ptr(row_ce),
+                                        float(d_loss), _ptr(d_hidden), wp, wb, _stream(stream, hidden))
     _check("dflash_lm_head_ce_backward", s)
 
 

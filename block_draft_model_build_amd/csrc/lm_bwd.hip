@@ -155,10 +155,17 @@ LmBwdLayout lm_bwd_layout(const dflash_config& c, int64_t rows, int64_t vocab) {
     return l;
 }
 
+// W_lm^T [H][Vp] with zero columns for the padded vocabulary.
 template <typename T>
-hipError_t lm_bwd_t(const dflash_config& c, int rows, const T* hidden, const T* W, int vocab, const int32_t* targets,
-                    const uint8_t* loss_mask, double tau, const float* row_ce, double d_loss, T* d_hidden, char* ws,
-                    hipStream_t st) {
+void head_transpose(const T* W, int vocab, int H, int64_t Vp, T* wt, hipStream_t st) {
+    hipLaunchKernelGGL((transpose_kernel<T, SrcPlain<T>>), dim3((unsigned)(Vp / 64), (unsigned)(H / 64)), dim3(256), 0,
+                       st, SrcPlain<T>{W, H}, (int64_t)vocab, Vp, (int64_t)H, wt, Vp);
+}
+
+template <typename T>
+hipError_t lm_bwd_t(const dflash_config& c, int rows, const T* hidden, const T* W, const T* W_t, int vocab,
+                    const int32_t* targets, const uint8_t* loss_mask, double tau, const float* row_ce, double d_loss,
+                    T* d_hidden, char* ws, hipStream_t st) {
     const LmBwdLayout lay = lm_bwd_layout(c, rows, vocab);
     const int H = c.hidden;
     const int64_t Vp = lay.vp;
@@ -166,15 +173,13 @@ hipError_t lm_bwd_t(const dflash_config& c, int rows, const T* hidden, const T* 
     float* coef = reinterpret_cast<float*>(ws + lay.coef);
     float* lse = reinterpret_cast<float*>(ws + lay.lse);
     T* dz = reinterpret_cast<T*>(ws + lay.dz);
-    T* wt = reinterpret_cast<T*>(ws + lay.wt);
+    const T* wt = W_t != nullptr ? W_t : reinterpret_cast<T*>(ws + lay.wt);
     {
         ProfScope prof(DFLASH_KERNEL_LM_BWD_PREP, st);
         hipLaunchKernelGGL(target_logit_kernel<T>, dim3(rows), dim3(256), 0, st, hidden, W, targets, H, vocab, zt);
         hipLaunchKernelGGL(ce_grad_rows_kernel, dim3(1), dim3(1024), 0, st, row_ce, zt, targets, loss_mask, rows, vocab,
                            c.block_size, tau, d_loss, coef, lse);
-        // W_lm^T with zero columns for the padded vocabulary.
-        hipLaunchKernelGGL((transpose_kernel<T, SrcPlain<T>>), dim3((unsigned)(Vp / 64), (unsigned)(H / 64)), dim3(256),
-                           0, st, SrcPlain<T>{W, H}, (int64_t)vocab, Vp, (int64_t)H, wt, Vp);
+        if (W_t == nullptr) head_transpose(W, vocab, H, Vp, reinterpret_cast<T*>(ws + lay.wt), st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -196,7 +201,7 @@ hipError_t lm_bwd_t(const dflash_config& c, int rows, const T* hidden, const T* 
 // statistics read the target logit from them, dz is one elementwise pass, and
 // only the second product remains.
 template <typename T>
-hipError_t lm_bwd_saved_t(const dflash_config& c, int rows, const float* logits, const T* W, int vocab,
+hipError_t lm_bwd_saved_t(const dflash_config& c, int rows, const float* logits, const T* W, const T* W_t, int vocab,
                           const int32_t* targets, const uint8_t* loss_mask, double tau, const float* row_ce,
                           double d_loss, T* d_hidden, char* ws, hipStream_t st) {
     const LmBwdLayout lay = lm_bwd_layout(c, rows, vocab);
@@ -206,15 +211,14 @@ hipError_t lm_bwd_saved_t(const dflash_config& c, int rows, const float* logits,
     float* coef = reinterpret_cast<float*>(ws + lay.coef);
     float* lse = reinterpret_cast<float*>(ws + lay.lse);
     T* dz = reinterpret_cast<T*>(ws + lay.dz);
-    T* wt = reinterpret_cast<T*>(ws + lay.wt);
+    const T* wt = W_t != nullptr ? W_t : reinterpret_cast<T*>(ws + lay.wt);
     {
         ProfScope prof(DFLASH_KERNEL_LM_BWD_PREP, st);
         hipLaunchKernelGGL(saved_target_logit_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, logits,
                            Vp, targets, rows, vocab, zt);
         hipLaunchKernelGGL(ce_grad_rows_kernel, dim3(1), dim3(1024), 0, st, row_ce, zt, targets, loss_mask, rows, vocab,
                            c.block_size, tau, d_loss, coef, lse);
-        hipLaunchKernelGGL((transpose_kernel<T, SrcPlain<T>>), dim3((unsigned)(Vp / 64), (unsigned)(H / 64)), dim3(256),
-                           0, st, SrcPlain<T>{W, H}, (int64_t)vocab, Vp, (int64_t)H, wt, Vp);
+        if (W_t == nullptr) head_transpose(W, vocab, H, Vp, reinterpret_cast<T*>(ws + lay.wt), st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -243,8 +247,42 @@ extern "C" size_t dflash_lm_head_ce_backward_workspace_size(const dflash_config*
     return lm_bwd_layout(*cfg, rows, vocab).total;
 }
 
+// A kept transposed head (dflash_lm_head_transpose): null, or 16-byte aligned and large enough.
+static dflash_status head_t_check(const dflash_config* cfg, int32_t vocab, const void* lm_head_t,
+                                  size_t lm_head_t_bytes) {
+    if (lm_head_t == nullptr) return DFLASH_OK;
+    const size_t need = (size_t)elem_bytes(*cfg) * (size_t)cfg->hidden * (size_t)lm_logits_ld(vocab);
+    return aligned16(lm_head_t) && lm_head_t_bytes >= need ? DFLASH_OK : DFLASH_ERR_INVALID_ARG;
+}
+
+extern "C" size_t dflash_lm_head_transpose_size(const dflash_config* cfg, int32_t vocab) {
+    if (check_config(cfg) != DFLASH_OK || vocab < 1 || (int64_t)vocab + 255 > INT32_MAX) return 0;
+    return (size_t)elem_bytes(*cfg) * (size_t)cfg->hidden * (size_t)lm_logits_ld(vocab);
+}
+
+extern "C" dflash_status dflash_lm_head_transpose(const dflash_config* cfg, const void* lm_head, int32_t vocab,
+                                                  void* lm_head_t, size_t lm_head_t_bytes, void* hip_stream) {
+    dflash_status s = check_config(cfg);
+    if (s != DFLASH_OK) return s;
+    if (vocab < 1) return DFLASH_ERR_INVALID_ARG;
+    if ((int64_t)vocab + 255 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
+    if (lm_head == nullptr || lm_head_t == nullptr || !aligned16(lm_head) ||
+        head_t_check(cfg, vocab, lm_head_t, lm_head_t_bytes) != DFLASH_OK)
+        return DFLASH_ERR_INVALID_ARG;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    const int64_t Vp = lm_logits_ld(vocab);
+    ProfScope prof(DFLASH_KERNEL_LM_BWD_PREP, st);
+    if (cfg->dtype == DFLASH_BF16)
+        head_transpose(static_cast<const __bf16*>(lm_head), vocab, cfg->hidden, Vp, static_cast<__bf16*>(lm_head_t),
+                       st);
+    else
+        head_transpose(static_cast<const float*>(lm_head), vocab, cfg->hidden, Vp, static_cast<float*>(lm_head_t), st);
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 extern "C" dflash_status dflash_lm_head_ce_backward(const dflash_config* cfg, int32_t rows, const void* hidden,
-                                                    const void* lm_head, int32_t vocab, const int32_t* targets,
+                                                    const void* lm_head, const void* lm_head_t,
+                                                    size_t lm_head_t_bytes, int32_t vocab, const int32_t* targets,
                                                     const uint8_t* loss_mask, double decay_tau, const float* row_ce,
                                                     double d_loss, void* d_hidden, void* workspace,
                                                     size_t workspace_bytes, void* hip_stream) {
@@ -254,7 +292,8 @@ extern "C" dflash_status dflash_lm_head_ce_backward(const dflash_config* cfg, in
     if ((int64_t)vocab + 255 > INT32_MAX) return DFLASH_ERR_UNSUPPORTED;
     if (rows == 0) return DFLASH_OK;
     if (hidden == nullptr || lm_head == nullptr || targets == nullptr || loss_mask == nullptr || row_ce == nullptr ||
-        d_hidden == nullptr || !aligned16(hidden) || !aligned16(lm_head) || !aligned16(d_hidden))
+        d_hidden == nullptr || !aligned16(hidden) || !aligned16(lm_head) || !aligned16(d_hidden) ||
+        head_t_check(cfg, vocab, lm_head_t, lm_head_t_bytes) != DFLASH_OK)
         return DFLASH_ERR_INVALID_ARG;
     const size_t need = lm_bwd_layout(*cfg, rows, vocab).total;
     if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -263,20 +302,23 @@ extern "C" dflash_status dflash_lm_head_ce_backward(const dflash_config* cfg, in
     char* ws = static_cast<char*>(workspace);
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
-        e = lm_bwd_t<__bf16>(*cfg, rows, static_cast<const __bf16*>(hidden), static_cast<const __bf16*>(lm_head), vocab,
-                             targets, loss_mask, decay_tau, row_ce, d_loss, static_cast<__bf16*>(d_hidden), ws, st);
+        e = lm_bwd_t<__bf16>(*cfg, rows, static_cast<const __bf16*>(hidden), static_cast<const __bf16*>(lm_head),
+                             static_cast<const __bf16*>(lm_head_t), vocab, targets, loss_mask, decay_tau, row_ce,
+                             d_loss, static_cast<__bf16*>(d_hidden), ws, st);
     else
-        e = lm_bwd_t<float>(*cfg, rows, static_cast<const float*>(hidden), static_cast<const float*>(lm_head), vocab,
-                            targets, loss_mask, decay_tau, row_ce, d_loss, static_cast<float*>(d_hidden), ws, st);
+        e = lm_bwd_t<float>(*cfg, rows, static_cast<const float*>(hidden), static_cast<const float*>(lm_head),
+                            static_cast<const float*>(lm_head_t), vocab, targets, loss_mask, decay_tau, row_ce, d_loss,
+                            static_cast<float*>(d_hidden), ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
 extern "C" dflash_status dflash_lm_head_ce_backward_saved(const dflash_config* cfg, int32_t rows, const float* logits,
-                                                          size_t logits_bytes, const void* lm_head, int32_t vocab,
-                                                          const int32_t* targets, const uint8_t* loss_mask,
-                                                          double decay_tau, const float* row_ce, double d_loss,
-                                                          void* d_hidden, void* workspace, size_t workspace_bytes,
-                                                          void* hip_stream) {
+                                                          size_t logits_bytes, const void* lm_head,
+                                                          const void* lm_head_t, size_t lm_head_t_bytes,
+                                                          int32_t vocab, const int32_t* targets,
+                                                          const uint8_t* loss_mask, double decay_tau,
+                                                          const float* row_ce, double d_loss, void* d_hidden,
+                                                          void* workspace, size_t workspace_bytes, void* hip_stream) {
     dflash_status s = check_config(cfg);
     if (s != DFLASH_OK) return s;
     if (rows < 0 || vocab < 1 || !(decay_tau > 0.0)) return DFLASH_ERR_INVALID_ARG;
@@ -284,7 +326,8 @@ extern "C" dflash_status dflash_lm_head_ce_backward_saved(const dflash_config* c
     if (rows == 0) return DFLASH_OK;
     if (logits == nullptr || logits_bytes < (size_t)rows * (size_t)lm_logits_ld(vocab) * sizeof(float) ||
         lm_head == nullptr || targets == nullptr || loss_mask == nullptr || row_ce == nullptr || d_hidden == nullptr ||
-        !aligned16(logits) || !aligned16(lm_head) || !aligned16(d_hidden))
+        !aligned16(logits) || !aligned16(lm_head) || !aligned16(d_hidden) ||
+        head_t_check(cfg, vocab, lm_head_t, lm_head_t_bytes) != DFLASH_OK)
         return DFLASH_ERR_INVALID_ARG;
     const size_t need = lm_bwd_layout(*cfg, rows, vocab).total;
     if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -293,10 +336,12 @@ extern "C" dflash_status dflash_lm_head_ce_backward_saved(const dflash_config* c
     char* ws = static_cast<char*>(workspace);
     hipError_t e;
     if (cfg->dtype == DFLASH_BF16)
-        e = lm_bwd_saved_t<__bf16>(*cfg, rows, logits, static_cast<const __bf16*>(lm_head), vocab, targets, loss_mask,
-                                   decay_tau, row_ce, d_loss, static_cast<__bf16*>(d_hidden), ws, st);
+        e = lm_bwd_saved_t<__bf16>(*cfg, rows, logits, static_cast<const __bf16*>(lm_head),
+                                   static_cast<const __bf16*>(lm_head_t), vocab, targets, loss_mask, decay_tau, row_ce,
+                                   d_loss, static_cast<__bf16*>(d_hidden), ws, st);
     else
-        e = lm_bwd_saved_t<float>(*cfg, rows, logits, static_cast<const float*>(lm_head), vocab, targets, loss_mask,
-                                  decay_tau, row_ce, d_loss, static_cast<float*>(d_hidden), ws, st);
+        e = lm_bwd_saved_t<float>(*cfg, rows, logits, static_cast<const float*>(lm_head),
+                                  static_cast<const float*>(lm_head_t), vocab, targets, loss_mask, decay_tau, row_ce,
+                                  d_loss, static_cast<float*>(d_hidden), ws, st);
     return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }

@@ -503,6 +503,10 @@ size_t dflash_lm_head_ce_logits_size(int32_t rows, int32_t vocab);
  *
  *   hidden, lm_head, vocab, targets, loss_mask, decay_tau, rows
  *                  as dflash_lm_head_ce
+ *   lm_head_t, lm_head_t_bytes
+ *                  optional: dflash_lm_head_transpose's output for this head (the
+ *                  call then skips its own transpose); NULL: the head is
+ *                  transposed into the workspace. The result is the same bit for bit.
  *   row_ce         device f32 [rows]: dflash_lm_head_ce's output for the same inputs
  *   d_loss         the upstream gradient of the loss (1 for the loss itself)
  *   d_hidden       device [rows, hidden] in the config dtype, overwritten (rows
@@ -511,14 +515,33 @@ size_t dflash_lm_head_ce_logits_size(int32_t rows, int32_t vocab);
  *                  bytes, 256-byte aligned
  * dz enters the second product in the config dtype; both products accumulate
  * in fp32. Errors: as dflash_lm_head_ce (INVALID_ARG also for a null row_ce or
- * d_hidden when rows > 0).
+ * d_hidden when rows > 0, or a small or misaligned lm_head_t).
  */
 dflash_status dflash_lm_head_ce_backward(const dflash_config *cfg, int32_t rows, const void *hidden,
-                                         const void *lm_head, int32_t vocab, const int32_t *targets,
-                                         const uint8_t *loss_mask, double decay_tau, const float *row_ce,
-                                         double d_loss, void *d_hidden, void *workspace, size_t workspace_bytes,
-                                         void *hip_stream);
+                                         const void *lm_head, const void *lm_head_t, size_t lm_head_t_bytes,
+                                         int32_t vocab, const int32_t *targets, const uint8_t *loss_mask,
+                                         double decay_tau, const float *row_ce, double d_loss, void *d_hidden,
+                                         void *workspace, size_t workspace_bytes, void *hip_stream);
 size_t dflash_lm_head_ce_backward_workspace_size(const dflash_config *cfg, int32_t rows, int32_t vocab);
+
+/*
+ * dflash_lm_head_transpose -- W_lm^T, the head as the loss backward's second
+ * product reads it. [P1] "Configuration": the LM head comes from the target
+ * and stays frozen, so a training run can form its transpose once and pass it
+ * to every backward call (lm_head_t) instead of having each call transpose it.
+ *
+ *   lm_head        device [vocab, hidden] in the config dtype
+ *   lm_head_t      device [hidden][vp] in the config dtype, vp = vocab rounded
+ *                  up to a multiple of 64; columns >= vocab are written as zero.
+ *                  16-byte aligned, caller-owned,
+ *                  lm_head_t_bytes >= dflash_lm_head_transpose_size(cfg, vocab)
+ * Errors: as dflash_lm_head_ce for the config and the vocabulary; INVALID_ARG
+ * for a null or misaligned lm_head, or a null, small or misaligned lm_head_t.
+ */
+dflash_status dflash_lm_head_transpose(const dflash_config *cfg, const void *lm_head, int32_t vocab,
+                                       void *lm_head_t, size_t lm_head_t_bytes, void *hip_stream);
+/* hidden * vp * element size bytes (0 for invalid sizes). */
+size_t dflash_lm_head_transpose_size(const dflash_config *cfg, int32_t vocab);
 
 /*
  * dflash_lm_head_ce_backward_saved -- dflash_lm_head_ce_backward from the
@@ -535,11 +558,11 @@ size_t dflash_lm_head_ce_backward_workspace_size(const dflash_config *cfg, int32
  * misaligned logits buffer when rows > 0.
  */
 dflash_status dflash_lm_head_ce_backward_saved(const dflash_config *cfg, int32_t rows, const float *logits,
-                                               size_t logits_bytes, const void *lm_head, int32_t vocab,
-                                               const int32_t *targets, const uint8_t *loss_mask,
-                                               double decay_tau, const float *row_ce, double d_loss,
-                                               void *d_hidden, void *workspace, size_t workspace_bytes,
-                                               void *hip_stream);
+                                               size_t logits_bytes, const void *lm_head, const void *lm_head_t,
+                                               size_t lm_head_t_bytes, int32_t vocab, const int32_t *targets,
+                                               const uint8_t *loss_mask, double decay_tau, const float *row_ce,
+                                               double d_loss, void *d_hidden, void *workspace,
+                                               size_t workspace_bytes, void *hip_stream);
 
 /*
  * dflash_block_attn_backward -- gradients of dflash_block_attn. [P2] "How It

@@ -112,12 +112,12 @@ def _cmp_rel(gpu, ref, tol, what):
     assert float(np.abs(err).max()) <= tol["max_rel"] * scale, f"{what}: max-abs {np.abs(err).max():.3e} vs {scale:.3e}"
 
 
-def _run_bwd(w, h, W, t, mask, tau, ce, d_loss=1.0):
+def _run_bwd(w, h, W, t, mask, tau, ce, d_loss=1.0, W_t=None):
     cfg = d.config_from_workload(w)
     rows, vocab = h.shape[0], W.shape[0]
     dh = torch.full_like(h, float("nan"))
     ws = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg, rows, vocab), dtype=torch.uint8, device="cuda")
-    d.dflash_lm_head_ce_backward(cfg, h, W, t, mask, tau, ce, d_loss, dh, ws)
+    d.dflash_lm_head_ce_backward(cfg, h, W, t, mask, tau, ce, d_loss, dh, ws, lm_head_t=W_t)
     torch.cuda.synchronize()
     return dh
 
@@ -194,12 +194,20 @@ def _run_train(w, h, W, t, mask, tau):
     return ce, float(loss.item()), logits
 
 
-def _run_bwd_saved(w, rows, logits, W, t, mask, tau, ce, d_loss=1.0):
+def _transposed_head(w, W):
+    cfg = d.config_from_workload(w)
+    W_t = torch.full((d.dflash_lm_head_transpose_size(cfg, W.shape[0]),), 255, dtype=torch.uint8, device="cuda")
+    d.dflash_lm_head_transpose(cfg, W, W_t)
+    torch.cuda.synchronize()
+    return W_t
+
+
+def _run_bwd_saved(w, rows, logits, W, t, mask, tau, ce, d_loss=1.0, W_t=None):
     cfg = d.config_from_workload(w)
     vocab, H = W.shape
     dh = torch.full((rows, H), float("nan"), dtype=W.dtype, device="cuda")
     ws = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg, rows, vocab), dtype=torch.uint8, device="cuda")
-    d.dflash_lm_head_ce_backward_saved(cfg, rows, logits, W, t, mask, tau, ce, d_loss, dh, ws)
+    d.dflash_lm_head_ce_backward_saved(cfg, rows, logits, W, t, mask, tau, ce, d_loss, dh, ws, lm_head_t=W_t)
     torch.cuda.synchronize()
     return dh
 
@@ -229,6 +237,13 @@ def test_kept_logits_small(w, rows, vocab, tol):
     ref = oracle.lm_head_ce_backward(np64(h), np64(W), t.cpu().numpy(), mask.cpu().numpy(), w.block_size, tau)
     _cmp_rel(dh2, ref, tol, "d_hidden from kept logits")
     assert torch.equal(_run_bwd_saved(w, rows, logits, W, t, mask, tau, ce, 2.0), 2 * dh2)
+    # A kept transposed head gives the same bytes, and holds W_lm^T with zero padding columns.
+    W_t = _transposed_head(w, W)
+    assert torch.equal(_run_bwd_saved(w, rows, logits, W, t, mask, tau, ce, W_t=W_t), dh2)
+    assert torch.equal(_run_bwd(w, h, W, t, mask, tau, ce, W_t=W_t), dh)
+    H, vp = W.shape[1], (vocab + 63) // 64 * 64
+    Wt = W_t.view(W.dtype).reshape(H, vp)
+    assert torch.equal(Wt[:, :vocab], W.t()) and (Wt[:, vocab:] == 0).all()
 
 
 def test_kept_logits_full_size():

@@ -5,7 +5,8 @@ Configuration: the LM head is the target's, frozen).
 
 GPU: dflash_build_plan -> dflash_ctx_proj_train (keeps C) ->
 dflash_body_forward_train -> dflash_lm_head_ce_train (keeps the logits) ->
-dflash_lm_head_ce_backward_saved -> dflash_body_backward ->
+dflash_lm_head_ce_backward_saved (with the head transposed once by
+dflash_lm_head_transpose) -> dflash_body_backward ->
 dflash_ctx_proj_backward (adds the context path's share of every Wk / Wv
 gradient), the chain the benchmark's training step runs. Oracle: build_plan,
 ctx_proj/ctx_kv, body_forward, lm_head_ce, lm_head_ce_backward, body_backward,
@@ -60,7 +61,10 @@ def _setup(w, vocab, seed):
     rng = Rng(seed + 100, dev)
     tokens = rng.integers("train.tokens", 0, vocab - 1, (w.batch, w.seq_len)).to(torch.int32)
     W_lm = rng.normal("train.lm_head", (vocab, w.hidden), std=1 / math.sqrt(w.hidden), dtype=w.torch_dtype)
-    return dict(inp=inp, tokens=tokens, W_lm=W_lm)
+    cfg = d.config_from_workload(w)
+    W_t = torch.empty(d.dflash_lm_head_transpose_size(cfg, vocab), dtype=torch.uint8, device=dev)
+    d.dflash_lm_head_transpose(cfg, W_lm, W_t)                   # the head is frozen: transposed once
+    return dict(inp=inp, tokens=tokens, W_lm=W_lm, W_t=W_t)
 
 
 def _step(w, vocab, tau, setup):
@@ -87,7 +91,8 @@ def _step(w, vocab, tau, setup):
     d.dflash_lm_head_ce_train(cfg, run.out, W_lm, targets, loss_mask, tau, ce, loss, logits, ws)
     d_out = torch.empty_like(run.out)
     ws = torch.empty(d.dflash_lm_head_ce_backward_workspace_size(cfg, R, vocab), dtype=torch.uint8, device=dev)
-    d.dflash_lm_head_ce_backward_saved(cfg, R, logits, W_lm, targets, loss_mask, tau, ce, 1.0, d_out, ws)
+    d.dflash_lm_head_ce_backward_saved(cfg, R, logits, W_lm, targets, loss_mask, tau, ce, 1.0, d_out, ws,
+                                       lm_head_t=setup["W_t"])
     grads = [{k: torch.empty(tuple(v.shape), dtype=torch.float32, device=dev) for k, v in Lw.items()}
              for Lw in inp["layers"]]
     dck = [torch.empty((w.num_kv_heads, run.T, w.head_dim), dtype=torch.float32, device=dev) for _ in range(L)]

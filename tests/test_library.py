@@ -162,17 +162,29 @@ def test_rejects_bad_arguments_before_launch():
                                        None) == d.DFLASH_ERR_INVALID_ARG
     assert lib.dflash_lm_head_ce_train(ctypes.byref(cfg), 16, P(fake), P(fake), 100, P(fake), P(fake), 2.0, P(fake),
                                        P(fake), P(fake), 1 << 40, P(fake), 64, None) == d.DFLASH_ERR_WORKSPACE
-    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 16, None, 1 << 40, P(fake), 100, P(fake), P(fake),
-                                                2.0, P(fake), 1.0, P(fake), P(fake), 1 << 40,
-                                                None) == d.DFLASH_ERR_INVALID_ARG
-    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 16, P(fake), 1 << 40, P(fake), 100, P(fake),
-                                                P(fake), 0.0, P(fake), 1.0, P(fake), P(fake), 1 << 40,
-                                                None) == d.DFLASH_ERR_INVALID_ARG
-    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 16, P(fake), 1 << 40, P(fake), 100, P(fake),
-                                                P(fake), 2.0, P(fake), 1.0, P(fake), P(fake), 64,
-                                                None) == d.DFLASH_ERR_WORKSPACE
-    assert lib.dflash_lm_head_ce_backward_saved(ctypes.byref(cfg), 0, None, 0, P(fake), 100, None, None, 2.0, None,
-                                                1.0, None, None, 0, None) == d.DFLASH_OK
+    saved = lambda logits, head_t, head_t_bytes, tau, ws_bytes, rows=16: lib.dflash_lm_head_ce_backward_saved(
+        ctypes.byref(cfg), rows, logits, 1 << 40, P(fake), head_t, head_t_bytes, 100, P(fake), P(fake), tau,
+        P(fake), 1.0, P(fake), P(fake), ws_bytes, None)
+    assert saved(None, None, 0, 2.0, 1 << 40) == d.DFLASH_ERR_INVALID_ARG
+    assert saved(P(fake), None, 0, 0.0, 1 << 40) == d.DFLASH_ERR_INVALID_ARG
+    assert saved(P(fake), None, 0, 2.0, 64) == d.DFLASH_ERR_WORKSPACE
+    assert saved(None, None, 0, 2.0, 0, rows=0) == d.DFLASH_OK
+    # a kept transposed head: its size; small or misaligned buffers are refused
+    tsize = d.dflash_lm_head_transpose_size(cfg, 100)
+    assert tsize == cfg.hidden * 128 * (2 if cfg.dtype == d.DFLASH_BF16 else 4)
+    assert d.dflash_lm_head_transpose_size(cfg, 0) == 0
+    assert saved(P(fake), P(fake), tsize - 1, 2.0, 1 << 40) == d.DFLASH_ERR_INVALID_ARG
+    assert saved(P(fake), P(fake + 8), tsize, 2.0, 1 << 40) == d.DFLASH_ERR_INVALID_ARG
+    assert lib.dflash_lm_head_ce_backward(ctypes.byref(cfg), 16, P(fake), P(fake), P(fake), tsize - 1, 100, P(fake),
+                                          P(fake), 2.0, P(fake), 1.0, P(fake), P(fake), 1 << 40,
+                                          None) == d.DFLASH_ERR_INVALID_ARG
+    transpose = lambda head, vocab, out, nbytes: lib.dflash_lm_head_transpose(ctypes.byref(cfg), head, vocab, out,
+                                                                             nbytes, None)
+    assert transpose(P(fake), 100, P(fake), tsize - 1) == d.DFLASH_ERR_INVALID_ARG
+    assert transpose(P(fake), 100, None, tsize) == d.DFLASH_ERR_INVALID_ARG
+    assert transpose(None, 100, P(fake), tsize) == d.DFLASH_ERR_INVALID_ARG
+    assert transpose(P(fake), 100, P(fake + 8), tsize) == d.DFLASH_ERR_INVALID_ARG
+    assert transpose(P(fake), 0, P(fake), tsize) == d.DFLASH_ERR_INVALID_ARG
     # optimizer step: dtype, step, rates, eps, sizes, null or misaligned arrays; empty calls
     T = d.DFlashAdamWTensor
     good = (T * 1)(T(fake, fake, fake, fake, fake, 100))
